@@ -1,0 +1,73 @@
+"""The pins are strong enough: each plausible mistake planted in a copy of the
+oracle's C source (compiled here, on the CPU) makes at least one pin fail.
+The shipped oracle is untouched; mutants live in a temporary directory."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")
+
+MUTANTS = {
+    "gate_on_dv_axis": ("row[j] *= alpha[i];", "row[j] *= alpha[j];"),
+    "no_erase_term": ("u[j] = b * (vt[j] - u[j]);", "u[j] = b * vt[j];"),
+    "write_along_q": ("row[j] += kt[i] * u[j];", "row[j] += qt[i] * u[j];"),
+    "conv_taps_reversed": ("p - 3 + j,", "p - j,"),
+    "gate_sign_flipped": ("gate_lower_bound * sigmoid(a)", "gate_lower_bound * sigmoid(-a)"),
+    "k_normalised_by_q_norm": ("kt[c] *= ik;", "kt[c] *= iq;"),
+    "scale_dropped": ("scale * ot[j]", "ot[j]"),
+    "eps_outside_root": ("sqrt(sq + L2_EPS)", "(sqrt(sq) + L2_EPS)"),
+    "beta_dropped": ("u[j] = b * (vt[j] - u[j]);", "u[j] = (vt[j] - u[j]);"),
+}
+
+# the fast pins, by name, from the pin module
+PINS = [
+    "test_short_conv_matches_torch_conv1d",
+    "test_l2_norm_closed_form",
+    "test_gate_sigmoid_values_and_row_axis",
+    "test_beta_zero_is_pure_gated_decay",
+    "test_one_hot_keys_reduce_to_gla",
+    "test_orthonormal_keys_exact_retrieval_and_overwrite",
+    "test_beta_one_self_query_returns_value",
+    "test_brute_force_unrolled_products",
+]
+
+
+def _run_pins():
+    from tests import test_oracle_pins as P
+    failed = []
+    for name in PINS:
+        fn = getattr(P, name)
+        try:
+            if name == "test_short_conv_matches_torch_conv1d":
+                fn(False, True)
+            elif name == "test_brute_force_unrolled_products":
+                fn(5, False)
+            else:
+                fn()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistake_is_caught(mutant, tmp_path, monkeypatch):
+    old, new = MUTANTS[mutant]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation anchor missing: " + old
+    mpath = tmp_path / "mut.c"
+    mpath.write_text(src.replace(old, new))
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                    str(mpath), "-o", str(so), "-lm"], check=True)
+    lib = oracle._bind(ctypes.CDLL(str(so)))
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failed = _run_pins()
+    assert failed, "no pin caught mutant " + mutant
+
+
+def test_unmutated_oracle_passes_the_same_pins():
+    assert _run_pins() == []
