@@ -1,0 +1,223 @@
+// kda_api.hip -- the extern "C" entry points of libkda.so (declared in kda.h).
+//
+// Every argument is checked on the host before anything is enqueued; failures
+// return a status code and leave a message in a thread-local buffer.  The
+// library allocates nothing and never synchronises the stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status fail(kda_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kda_status hip_fail(hipError_t e, const char *what) {
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t esize(kda_dtype d) { return d == KDA_BF16 ? 2 : 4; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+// Checks an optional host copy of cu_seqlens.
+kda_status check_cu_host(const int32_t *cu, int32_t n, int64_t total) {
+    if (!cu) return KDA_OK;
+    if (cu[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    for (int32_t i = 0; i < n; ++i)
+        if (cu[i + 1] < cu[i])
+            return fail(KDA_ERR_INVALID_ARG, "cu_seqlens not monotone at %d (%d > %d)", i, cu[i],
+                        cu[i + 1]);
+    if ((int64_t)cu[n] != total)
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[%d] = %d, expected total_tokens = %lld", n,
+                    cu[n], (long long)total);
+    return KDA_OK;
+}
+
+kda_status check_common(int32_t num_seqs, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                        uint32_t flags, float scale, float lb) {
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs = %d, must be >= 1", num_seqs);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "num_heads = %d, must be >= 1", H);
+    if (dk != 128 || dv != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "head dims %d x %d: only 128 x 128 is supported", dk, dv);
+    if (dt != KDA_F32 && dt != KDA_BF16) return fail(KDA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+    if (flags & ~(uint32_t)KDA_F_ALL) return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    if (!std::isfinite(scale) || scale < 0.f)
+        return fail(KDA_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 = default)");
+    if (!std::isfinite(lb) || !(lb < 0.f))
+        return fail(KDA_ERR_INVALID_ARG, "gate_lower_bound must be finite and < 0");
+    if ((int64_t)num_seqs * H > (int64_t)1 << 26)
+        return fail(KDA_ERR_INVALID_ARG, "num_seqs * num_heads too large");
+    return KDA_OK;
+}
+
+int env_int(const char *name, int dflt) {
+    const char *v = std::getenv(name);
+    return v && *v ? std::atoi(v) : dflt;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_string(int s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+        default: return "KDA_UNKNOWN_STATUS";
+    }
+}
+
+const char *kda_last_error(void) { return g_err; }
+
+kda_status kda_short_conv(const void *x, void *y, int64_t total_tokens, int32_t channels,
+                          const float *weight, const float *bias, const void *conv_state_in,
+                          void *conv_state_out, const int32_t *cu_seqlens,
+                          const int32_t *cu_seqlens_host, int32_t num_seqs, kda_dtype dtype,
+                          uint32_t flags, hipStream_t stream) {
+    g_err[0] = 0;
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs = %d, must be >= 1", num_seqs);
+    if (channels < 1) return fail(KDA_ERR_INVALID_ARG, "channels = %d, must be >= 1", channels);
+    if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens < 0");
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (flags & ~(uint32_t)KDA_F_SILU)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_short_conv accepts only KDA_F_SILU (flags 0x%x)", flags);
+    if (!weight) return fail(KDA_ERR_INVALID_ARG, "weight is NULL");
+    if (total_tokens > 0 && (!x || !y)) return fail(KDA_ERR_INVALID_ARG, "x or y is NULL");
+    if (!cu_seqlens && total_tokens % num_seqs)
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens NULL needs total_tokens %% num_seqs == 0");
+    if (cu_seqlens && cu_seqlens_host == nullptr && num_seqs < 1)
+        return fail(KDA_ERR_INVALID_ARG, "bad cu_seqlens");
+    kda_status st = check_cu_host(cu_seqlens_host, num_seqs, total_tokens);
+    if (st != KDA_OK) return st;
+    const size_t bytes = (size_t)total_tokens * channels * esize(dtype);
+    if (overlap(x, bytes, y, bytes)) return fail(KDA_ERR_INVALID_ARG, "y overlaps x");
+    const size_t csb = (size_t)num_seqs * 3 * channels * esize(dtype);
+    if (conv_state_out && conv_state_out != conv_state_in &&
+        overlap(conv_state_out, csb, conv_state_in, csb))
+        return fail(KDA_ERR_INVALID_ARG, "conv_state_out partially overlaps conv_state_in");
+    if (total_tokens > 0) {
+        hipError_t e = kda::launch_short_conv(dtype, x, y, total_tokens, channels, weight, bias,
+                                              conv_state_in, cu_seqlens, num_seqs,
+                                              (flags & KDA_F_SILU) != 0, stream);
+        if (e != hipSuccess) return hip_fail(e, "short_conv launch");
+    }
+    if (conv_state_out) {
+        const void *src[3] = {x, x, x};
+        const int ch[3] = {channels, 0, 0};
+        hipError_t e = kda::launch_conv_tail(dtype, src, ch, total_tokens, conv_state_in,
+                                             conv_state_out, cu_seqlens, num_seqs, stream);
+        if (e != hipSuccess) return hip_fail(e, "conv tail launch");
+    }
+    return KDA_OK;
+}
+
+kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
+    kda_status st = check_common(a->num_seqs, a->num_heads, a->head_dim_k, a->head_dim_v, a->dtype,
+                                 a->flags, a->scale, a->gate_lower_bound);
+    if (st != KDA_OK) return st;
+    if (a->total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens < 0");
+    int chunk = a->chunk_size;
+    if (chunk == 0) chunk = a->dtype == KDA_BF16 ? 64 : 32;
+    if (chunk != 16 && chunk != 32 && chunk != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d: use 16, 32 or 64", a->chunk_size);
+    if (a->dtype == KDA_F32 && chunk == 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size 64 needs bf16 I/O (fp32 staging exceeds LDS)");
+    if (!a->conv_weight) return fail(KDA_ERR_INVALID_ARG, "conv_weight is NULL");
+    if (a->total_tokens > 0 &&
+        (!a->q || !a->k || !a->v || !a->gate || !a->beta || !a->o))
+        return fail(KDA_ERR_INVALID_ARG, "q, k, v, gate, beta and o must be non-NULL");
+    if (!a->cu_seqlens && a->total_tokens % a->num_seqs)
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens NULL needs total_tokens %% num_seqs == 0");
+    st = check_cu_host(a->cu_seqlens_host, a->num_seqs, a->total_tokens);
+    if (st != KDA_OK) return st;
+    const int64_t T = a->total_tokens, H = a->num_heads;
+    const size_t es = esize(a->dtype);
+    const size_t tok = (size_t)T * H * 128 * es;
+    const void *ins[4] = {a->q, a->k, a->v, a->gate};
+    for (const void *in : ins)
+        if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
+    if (overlap(a->o, tok, a->beta, (size_t)T * H * es))
+        return fail(KDA_ERR_INVALID_ARG, "o overlaps beta");
+    const size_t sb = (size_t)a->num_seqs * H * 128 * 128 * 4;
+    if (a->state_out && (const void *)a->state_out != (const void *)a->state_in &&
+        overlap(a->state_out, sb, a->state_in, sb))
+        return fail(KDA_ERR_INVALID_ARG, "state_out partially overlaps state_in");
+    if (overlap(a->state_out, sb, a->o, tok)) return fail(KDA_ERR_INVALID_ARG, "state_out overlaps o");
+    const size_t csb = (size_t)a->num_seqs * 3 * 3 * H * 128 * es;
+    if (a->conv_state_out && a->conv_state_out != a->conv_state_in &&
+        overlap(a->conv_state_out, csb, a->conv_state_in, csb))
+        return fail(KDA_ERR_INVALID_ARG, "conv_state_out partially overlaps conv_state_in");
+
+    kda_prefill_args args = *a;
+    if (args.scale == 0.f) args.scale = 1.0f / std::sqrt(128.0f);
+    // dv tile per workgroup: enough workgroups for 256 compute units.  The tile
+    // changes only which workgroup computes a column, not the arithmetic.
+    const int64_t pairs = (int64_t)a->num_seqs * H;
+    int dv_tile = pairs >= 256 ? 128 : (pairs >= 128 ? 64 : 32);
+    const int forced = env_int("KDA_PREFILL_DV_TILE", 0);
+    if (forced == 32 || forced == 64 || forced == 128) dv_tile = forced;
+    kda::PrefillLaunch pl{&args, chunk, dv_tile};
+    hipError_t e = kda::launch_prefill(pl, stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    if (a->conv_state_out) {
+        const void *src[3] = {a->q, a->k, a->v};
+        const int c = (int)(H * 128);
+        const int ch[3] = {c, c, c};
+        e = kda::launch_conv_tail(a->dtype, src, ch, T, a->conv_state_in, a->conv_state_out,
+                                  a->cu_seqlens, a->num_seqs, stream);
+        if (e != hipSuccess) return hip_fail(e, "conv tail launch");
+    }
+    return KDA_OK;
+}
+
+kda_status kda_decode(const kda_decode_args *a, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
+    kda_status st = check_common(a->num_seqs, a->num_heads, a->head_dim_k, a->head_dim_v, a->dtype,
+                                 a->flags, a->scale, a->gate_lower_bound);
+    if (st != KDA_OK) return st;
+    if (!a->q || !a->k || !a->v || !a->gate || !a->beta || !a->o || !a->conv_weight ||
+        !a->conv_state || !a->state)
+        return fail(KDA_ERR_INVALID_ARG, "q, k, v, gate, beta, o, conv_weight, conv_state and "
+                                         "state must be non-NULL");
+    const size_t es = esize(a->dtype);
+    const size_t tok = (size_t)a->num_seqs * a->num_heads * 128 * es;
+    const size_t sb = (size_t)a->num_seqs * a->num_heads * 128 * 128 * 4;
+    const void *ins[4] = {a->q, a->k, a->v, a->gate};
+    for (const void *in : ins) {
+        if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
+        if (overlap(a->state, sb, in, tok)) return fail(KDA_ERR_INVALID_ARG, "state overlaps an input");
+    }
+    if (overlap(a->state, sb, a->o, tok)) return fail(KDA_ERR_INVALID_ARG, "state overlaps o");
+    kda_decode_args args = *a;
+    if (args.scale == 0.f) args.scale = 1.0f / std::sqrt(128.0f);
+    hipError_t e = kda::launch_decode(&args, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// kda_internal.h -- host-side launch entry points of the individual kernels.
+// Arguments are validated by the C ABI layer (kda_api.hip) before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+// Conv over packed sequences; x, y: [T][channels].
+hipError_t launch_short_conv(kda_dtype dt, const void *x, void *y, int64_t T, int channels,
+                             const float *w, const float *b, const void *cs_in,
+                             const int32_t *cu, int num_seqs, bool silu, hipStream_t s);
+
+// Last three raw tokens of (conv_state_in ++ sequence) for up to three sources that
+// together form the conv channels: source i has `ch[i]` channels and rows of `ch[i]`
+// elements ([T][ch[i]]).  Writes cs_out [N][3][sum ch]; cs_out may alias cs_in.
+hipError_t launch_conv_tail(kda_dtype dt, const void *const src[3], const int ch[3],
+                            int64_t T, const void *cs_in, void *cs_out, const int32_t *cu,
+                            int num_seqs, hipStream_t s);
+
+struct PrefillLaunch {
+    const kda_prefill_args *a;
+    int chunk;      // 16, 32 or 64
+    int dv_tile;    // dv columns per workgroup: 32, 64 or 128
+};
+hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t s);
+
+hipError_t launch_decode(const kda_decode_args *a, hipStream_t s);
+
+}  // namespace kda

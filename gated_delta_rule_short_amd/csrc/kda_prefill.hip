@@ -1,0 +1,646 @@
+// kda_prefill.hip -- chunk-parallel KDA prefill on gfx950 matrix cores.
+//
+// Source: "GLM-5.3-Flash im Detail" (flozi.net), section "Sequenz-Mixing: 34
+// KDA-Schichten mit festem Zustand": width-4 causal depthwise conv on q, k, v;
+// a channel-wise forget gate (log-decay >= -5) attenuates a 128 x 128 fp32
+// state per head; a scalar beta writes by the delta rule; the query reads the
+// updated state; in prefill the tokens of a chunk are evaluated in parallel and
+// a state is handed from chunk to chunk.
+//
+// Chunked form.  Inside a chunk of C = 16*NB tokens with state S0 on entry and
+// b_r = sum_{t<=r} g_t (per channel, from the chunk start):
+//     A_rs = sum_i k_ri k_si 2^(b_ri - b_si)   (s < r)     decayed key Gram
+//     P_rs = sum_i q_ri k_si 2^(b_ri - b_si)   (s <= r)    decayed query-key Gram
+//     X    = (I + diag(beta) A)^-1                          unit lower triangular
+//     W    = X diag(beta) (K . 2^b),  U0 = X diag(beta) V
+//     U    = U0 - W S0
+//     O    = scale ((Q . 2^b) S0 + P U)
+//     S1   = diag(2^b_last) S0 + (K . 2^(b_last - b))^T U
+// which equals the token recurrence exactly in exact arithmetic.  Log-decays
+// are kept in log2 units.
+//
+// Overflow-safe factoring.  A chunk's cumulative log-decay reaches -5*C (-320
+// for C = 64), far below fp32's exponent range, so the Grams are formed on
+// 16-row blocks with a reference point per block: with bl the cumsum inside
+// a block (>= -80 since g >= -5 and 16 * 5 = 80 < ln(FLT_MAX) = 88.7) and G its
+// total, the left factors k 2^bl, q 2^bl and the right factor k 2^(G - bl) are
+// all <= 1; a diagonal block multiplies the right factor by 2^-G (<= 2^115 in
+// log2 units, finite); an off-diagonal block (R, S) multiplies it by the decay
+// 2^(B_R - B_{S+1}) of the blocks strictly between them (<= 1).
+//
+// Work split.  One workgroup of four waves per (sequence, head, dv tile); the
+// fp32 state slice (128 x DVW) lives in registers in matrix-core accumulator
+// layout for the whole sequence, so no state byte touches HBM between chunks.
+// Per chunk:
+//   1  wave R loads block R (+3 halo rows), convs, L2-normalises q and k, turns
+//      the gate into log2-decays and their block cumsum        -> LDS
+//   1b with the block totals of all waves, writes the MFMA operands -> LDS
+//   2  decayed Grams A, P on 16 x 16 blocks (matrix cores); wave R inverts its
+//      diagonal block of I + diag(beta) A by forward substitution (VALU, fp32)
+//   3  block forward substitution for W (dk tiles spread over the waves) and
+//      U0 (each wave its own dv tiles), chained in accumulator layout
+//   4  per wave and dv tile: U, O, and the state update (matrix cores)
+// Accumulator layout (16 x 16 tile): lane l holds column l % 16 and rows
+// 4 (l / 16) + i.  Such a tile is consumed directly as the B operand of the
+// next product with the K elements in the same slots, and the A operand is
+// read from LDS with the matching K order, so the state, U, W and U0 chain
+// between products in registers.
+#include <mutex>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct PrefillParams {
+    const void *q, *k, *v, *gate, *beta;
+    const float *w, *bias;
+    const void *cs_in;
+    const float *state_in;
+    float *state_out;
+    void *o;
+    const int32_t *cu;
+    int64_t total;
+    int num_seqs, H;
+    float scale, lb;
+    uint32_t flags;
+    int pairs, tiles;
+};
+
+// Shared-memory layout (bytes).  E is the element type of the staged MFMA
+// operands: bf16 for bf16 I/O, fp32 for fp32 I/O.  Row strides are padded so
+// that the 16 rows read by one quarter-wave fall in distinct banks.
+template <typename E, int NB, int DVW> struct Layout {
+    static constexpr int C = 16 * NB;
+    static constexpr int SRM = 128 + (sizeof(E) == 2 ? 4 : 2);  // [C][128]  token-major
+    static constexpr int STR = C + 4;                            // [128][C]  channel-major
+    static constexpr int SCC = C + 4;                            // [C][C]
+    static constexpr int SXD = 20;                               // [16][16]
+    static constexpr int NFO = NB >= 3 ? (NB - 1) * (NB - 2) / 2 : 1;
+    static constexpr size_t RM = (size_t)C * SRM * sizeof(E);
+    static constexpr size_t TR = (size_t)128 * STR * sizeof(E);
+    static constexpr size_t KL = 0, QL = KL + RM, KR = QL + RM, QG = KR + RM;
+    static constexpr size_t KGT = QG + RM, KDT = KGT + TR, VT = KDT + TR;
+    static constexpr size_t LN = VT + (size_t)DVW * STR * sizeof(E);
+    static constexpr size_t PM = LN + (size_t)C * SCC * sizeof(E);
+    static constexpr size_t XD = PM + (size_t)C * SCC * sizeof(E);
+    static constexpr size_t ND = XD + (((size_t)NB * 16 * SXD * sizeof(E) + 15) & ~(size_t)15);
+    static constexpr size_t G2 = ND + (size_t)NB * 256 * 4;
+    static constexpr size_t FD = G2 + (size_t)NB * 128 * 4;
+    static constexpr size_t FO = FD + (size_t)NB * 128 * 4;
+    static constexpr size_t GAM = FO + (size_t)NFO * 128 * 4;
+    static constexpr size_t BET = GAM + 128 * 4;
+    static constexpr size_t TOTAL = BET + (size_t)C * 4;
+};
+
+// Operand helpers per staged element type.
+template <typename E> struct Ops;
+
+template <> struct Ops<__bf16> {
+    typedef bf16x4 B4;  // one 16-row K block of a B operand, this lane's 4 elements
+    static __device__ __forceinline__ B4 pack(f32x4 v) { return pack4(v); }
+    static __device__ __forceinline__ f32x4 load4(const __bf16 *p) {
+        bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+        f32x4 r = {(float)v.x, (float)v.y, (float)v.z, (float)v.w};
+        return r;
+    }
+    static __device__ __forceinline__ void store4(__bf16 *p, float a, float b, float c, float d) {
+        bf16x4 v;
+        v.x = (__bf16)a; v.y = (__bf16)b; v.z = (__bf16)c; v.w = (__bf16)d;
+        *reinterpret_cast<bf16x4 *>(p) = v;
+    }
+    // acc += sum_{kb < kb1} sum_i arow[16 kb + i] * B[kb][i], kb1 <= MAXKB; arow points
+    // at A[row0 + lane%16][col0 + 4 (lane/16)].  kb1 folds to a constant once the
+    // caller's loops are unrolled, so B stays in registers.
+    template <int MAXKB>
+    static __device__ __forceinline__ f32x4 chain(f32x4 acc, const __bf16 *arow, const B4 *B,
+                                                  int kb1) {
+#pragma unroll
+        for (int kb = 0; kb < MAXKB; kb += 2) {
+            if (kb + 1 < kb1) {
+                bf16x4 a0 = *reinterpret_cast<const bf16x4 *>(arow + 16 * kb);
+                bf16x4 a1 = *reinterpret_cast<const bf16x4 *>(arow + 16 * kb + 16);
+                acc = mma_k32(join8(a0, a1), join8(B[kb], B[kb + 1]), acc);
+            } else if (kb < kb1) {
+                acc = mma_k16(*reinterpret_cast<const bf16x4 *>(arow + 16 * kb), B[kb], acc);
+            }
+        }
+        return acc;
+    }
+    // 16x16 Gram over 128 channels: lrow/rrow point at the rows of this lane's
+    // A row / B column; f (nullable) scales the right operand per channel.
+    static __device__ __forceinline__ f32x4 gram(const __bf16 *lrow, const __bf16 *rrow,
+                                                 const float *f, int g4) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k0 = 32 * t + 8 * g4;
+            bf16x8 a = join8(*reinterpret_cast<const bf16x4 *>(lrow + k0),
+                             *reinterpret_cast<const bf16x4 *>(lrow + k0 + 4));
+            bf16x4 b0 = *reinterpret_cast<const bf16x4 *>(rrow + k0);
+            bf16x4 b1 = *reinterpret_cast<const bf16x4 *>(rrow + k0 + 4);
+            if (f) {
+                f32x4 f0 = *reinterpret_cast<const f32x4 *>(f + k0);
+                f32x4 f1 = *reinterpret_cast<const f32x4 *>(f + k0 + 4);
+                f32x4 x0 = {(float)b0.x, (float)b0.y, (float)b0.z, (float)b0.w};
+                f32x4 x1 = {(float)b1.x, (float)b1.y, (float)b1.z, (float)b1.w};
+                b0 = pack4(x0 * f0);
+                b1 = pack4(x1 * f1);
+            }
+            acc = mma_k32(a, join8(b0, b1), acc);
+        }
+        return acc;
+    }
+};
+
+template <> struct Ops<float> {
+    typedef f32x4 B4;
+    static __device__ __forceinline__ B4 pack(f32x4 v) { return v; }
+    static __device__ __forceinline__ f32x4 load4(const float *p) {
+        return *reinterpret_cast<const f32x4 *>(p);
+    }
+    static __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
+        f32x4 v = {a, b, c, d};
+        *reinterpret_cast<f32x4 *>(p) = v;
+    }
+    template <int MAXKB>
+    static __device__ __forceinline__ f32x4 chain(f32x4 acc, const float *arow, const B4 *B,
+                                                  int kb1) {
+#pragma unroll
+        for (int kb = 0; kb < MAXKB; ++kb) {
+            if (kb < kb1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = mma_f32(arow[16 * kb + i], B[kb][i], acc);
+            }
+        }
+        return acc;
+    }
+    static __device__ __forceinline__ f32x4 gram(const float *lrow, const float *rrow,
+                                                 const float *f, int g4) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+            const int k = 4 * t + g4;
+            const float b = f ? rrow[k] * f[k] : rrow[k];
+            acc = mma_f32(lrow[k], b, acc);
+        }
+        return acc;
+    }
+};
+
+// Index of the off-diagonal block pair (R, S), R >= S + 2, in the factor table.
+__device__ __forceinline__ constexpr int fo_index(int R, int S) { return (R - 2) * (R - 1) / 2 + S; }
+
+template <typename T, int NB, int DVW>
+__global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
+    typedef T E;
+    typedef Layout<E, NB, DVW> LY;
+    typedef Ops<E> OP;
+    typedef typename OP::B4 B4;
+    constexpr int D = kHeadDim;
+    constexpr int C = 16 * NB;
+    constexpr int NTWG = DVW / 16;                // dv n-tiles per workgroup
+    constexpr int WST = NTWG < 4 ? NTWG : 4;      // waves owning state columns
+    constexpr int NTW = NTWG / WST;               // dv n-tiles per state wave
+    constexpr int SRM = LY::SRM, STR = LY::STR, SCC = LY::SCC, SXD = LY::SXD;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    E *sKL = reinterpret_cast<E *>(smem + LY::KL);  // also W (negated) after the Grams
+    E *sQL = reinterpret_cast<E *>(smem + LY::QL);
+    E *sKR = reinterpret_cast<E *>(smem + LY::KR);
+    E *sQG = reinterpret_cast<E *>(smem + LY::QG);
+    E *sKGT = reinterpret_cast<E *>(smem + LY::KGT);
+    E *sKDT = reinterpret_cast<E *>(smem + LY::KDT);
+    E *sVT = reinterpret_cast<E *>(smem + LY::VT);
+    E *sLN = reinterpret_cast<E *>(smem + LY::LN);
+    E *sPM = reinterpret_cast<E *>(smem + LY::PM);
+    E *sXD = reinterpret_cast<E *>(smem + LY::XD);
+    float *sND = reinterpret_cast<float *>(smem + LY::ND);
+    float *sG2 = reinterpret_cast<float *>(smem + LY::G2);
+    float *sFD = reinterpret_cast<float *>(smem + LY::FD);
+    float *sFO = reinterpret_cast<float *>(smem + LY::FO);
+    float *sGAM = reinterpret_cast<float *>(smem + LY::GAM);
+    float *sBET = reinterpret_cast<float *>(smem + LY::BET);
+    E *sWN = sKL;
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int m16 = lane & 15, g4 = lane >> 4;
+
+    // All dv tiles of one (sequence, head) share blockIdx % 8, i.e. one XCD and
+    // its L2, so the q/k/gate rows they all read are fetched from HBM once.
+    const int bid = blockIdx.x;
+    const int grp = bid / (8 * p.tiles), rem = bid - grp * 8 * p.tiles;
+    const int tile = rem >> 3, pr = grp * 8 + (rem & 7);
+    if (pr >= p.pairs) return;
+    const int H = p.H;
+    const int n = pr / H, h = pr - n * H;
+    int64_t s0, L;
+    seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
+    const int dvb = tile * DVW;
+    const bool st_wave = w < WST;
+    const int64_t tokstride = (int64_t)H * D;
+    const bool silu = p.flags & KDA_F_SILU;
+    const bool l2 = !(p.flags & KDA_F_NO_QK_L2NORM);
+    const bool glog = p.flags & KDA_F_GATE_IS_LOG;
+    const int CCH = 3 * H * D;
+
+    // fp32 state slice in accumulator layout: tile mt covers dk rows 16 mt..,
+    // tile j the dv columns dvb + 16 (w NTW + j)..
+    f32x4 S[8][NTW];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int col = dvb + 16 * (w * NTW + j) + m16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mt + 4 * g4 + i;
+                S[mt][j][i] = (st_wave && p.state_in)
+                                  ? p.state_in[((size_t)pr * D + row) * D + col] : 0.f;
+            }
+        }
+
+    // the strictly upper blocks of P are never written: zero them once
+    for (int idx = tid; idx < C * SCC; idx += 256) sPM[idx] = from_f32<E>(0.f);
+    __syncthreads();
+
+    const int64_t nchunks = (L + C - 1) / C;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t cbase = c * C;
+        // ------------------------------------------------ phase 1: prologue
+        float qh[16][2], kh[16][2], bl[16][2], vh[16][2], Gw[2] = {0.f, 0.f};
+        const int c0 = 2 * lane;
+        const bool has_v = c0 < DVW;
+        if (w < NB) {
+            const int R = w;
+            const int64_t rowbase = cbase + 16 * R;
+            const T *qg = reinterpret_cast<const T *>(p.q) + (size_t)h * D + c0;
+            const T *kg = reinterpret_cast<const T *>(p.k) + (size_t)h * D + c0;
+            const T *vg = reinterpret_cast<const T *>(p.v) + (size_t)h * D + dvb + c0;
+            const int qch = h * D + c0, kch = H * D + h * D + c0, vch = 2 * H * D + h * D + dvb + c0;
+            const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)n * 3 * CCH
+                                   : nullptr;
+            float xq[19][2], xk[19][2], xv[19][2];
+#pragma unroll
+            for (int r = 0; r < 19; ++r) {
+                const int64_t sp = rowbase + r - 3;
+                xq[r][0] = xq[r][1] = xk[r][0] = xk[r][1] = xv[r][0] = xv[r][1] = 0.f;
+                if (sp >= 0 && sp < L) {
+                    const int64_t off = (s0 + sp) * tokstride;
+                    Pair<T>::load(qg + off, xq[r][0], xq[r][1]);
+                    Pair<T>::load(kg + off, xk[r][0], xk[r][1]);
+                    if (has_v) Pair<T>::load(vg + off, xv[r][0], xv[r][1]);
+                } else if (sp < 0 && csn) {
+                    const T *row = csn + (size_t)(3 + sp) * CCH;
+                    Pair<T>::load(row + qch, xq[r][0], xq[r][1]);
+                    Pair<T>::load(row + kch, xk[r][0], xk[r][1]);
+                    if (has_v) Pair<T>::load(row + vch, xv[r][0], xv[r][1]);
+                }
+            }
+            float wq[2][4], wk[2][4], wv[2][4], bq[2], bk[2], bv[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                f32x4 a = *reinterpret_cast<const f32x4 *>(p.w + 4 * (qch + e));
+                f32x4 b = *reinterpret_cast<const f32x4 *>(p.w + 4 * (kch + e));
+                f32x4 cc = has_v ? *reinterpret_cast<const f32x4 *>(p.w + 4 * (vch + e))
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { wq[e][j] = a[j]; wk[e][j] = b[j]; wv[e][j] = cc[j]; }
+                bq[e] = p.bias ? p.bias[qch + e] : 0.f;
+                bk[e] = p.bias ? p.bias[kch + e] : 0.f;
+                bv[e] = (p.bias && has_v) ? p.bias[vch + e] : 0.f;
+            }
+            const T *ag = reinterpret_cast<const T *>(p.gate) + (size_t)h * D + c0;
+            float run[2] = {0.f, 0.f};
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const bool valid = rowbase + rr < L;
+                float yq[2], yk[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    float a = bq[e] + wq[e][0] * xq[rr][e] + wq[e][1] * xq[rr + 1][e] +
+                              wq[e][2] * xq[rr + 2][e] + wq[e][3] * xq[rr + 3][e];
+                    float b = bk[e] + wk[e][0] * xk[rr][e] + wk[e][1] * xk[rr + 1][e] +
+                              wk[e][2] * xk[rr + 2][e] + wk[e][3] * xk[rr + 3][e];
+                    float cv = bv[e] + wv[e][0] * xv[rr][e] + wv[e][1] * xv[rr + 1][e] +
+                               wv[e][2] * xv[rr + 2][e] + wv[e][3] * xv[rr + 3][e];
+                    if (silu) {
+                        a = a * sigmoidf_dev(a);
+                        b = b * sigmoidf_dev(b);
+                        cv = cv * sigmoidf_dev(cv);
+                    }
+                    yq[e] = valid ? a : 0.f;
+                    yk[e] = valid ? b : 0.f;
+                    vh[rr][e] = (valid && has_v) ? cv : 0.f;
+                }
+                const float sq = wave_sum(yq[0] * yq[0] + yq[1] * yq[1]);
+                const float sk = wave_sum(yk[0] * yk[0] + yk[1] * yk[1]);
+                const float iq = l2 ? rsqrtf(sq + 1e-6f) : 1.f;
+                const float ik = l2 ? rsqrtf(sk + 1e-6f) : 1.f;
+                float ga = 0.f, gb = 0.f;
+                if (valid) Pair<T>::load(ag + (s0 + rowbase + rr) * tokstride, ga, gb);
+                const float gg[2] = {ga, gb};
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    qh[rr][e] = yq[e] * iq;
+                    kh[rr][e] = yk[e] * ik;
+                    const float g = glog ? fmaxf(gg[e], p.lb) : p.lb * sigmoidf_dev(gg[e]);
+                    run[e] += valid ? g * kLog2e : 0.f;
+                    bl[rr][e] = run[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                Gw[e] = run[e];
+                sG2[R * 128 + c0 + e] = run[e];
+                sFD[R * 128 + c0 + e] = exp2f(-run[e]);
+            }
+            if (lane < 16) {
+                const int64_t sp = rowbase + lane;
+                sBET[16 * R + lane] =
+                    sp < L ? to_f32(reinterpret_cast<const T *>(p.beta)[(s0 + sp) * H + h]) : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // ------------------------------------ phase 1b: operands with block offsets
+        if (w < NB) {
+            const int R = w;
+            float B2R[2] = {0.f, 0.f}, Bt[2] = {0.f, 0.f};
+#pragma unroll
+            for (int Rp = 0; Rp < NB; ++Rp)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float gsum = sG2[Rp * 128 + c0 + e];
+                    if (Rp < R) B2R[e] += gsum;
+                    Bt[e] += gsum;
+                }
+            float eB[2], eD[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                eB[e] = exp2f(B2R[e]);
+                eD[e] = exp2f(Bt[e] - B2R[e] - Gw[e]);
+            }
+            float kgt[2][16], kdt[2][16], vtt[2][16];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = 16 * R + rr;
+                const float bt = sBET[row];
+                float kl[2], ql[2], kr[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float eL = exp2f(bl[rr][e]);
+                    const float eR = exp2f(Gw[e] - bl[rr][e]);
+                    kl[e] = kh[rr][e] * eL;
+                    ql[e] = qh[rr][e] * eL;
+                    kr[e] = kh[rr][e] * eR;
+                    kgt[e][rr] = bt * kl[e] * eB[e];
+                    kdt[e][rr] = kr[e] * eD[e];
+                    vtt[e][rr] = bt * vh[rr][e];
+                }
+                Pair<E>::store(sKL + row * SRM + c0, kl[0], kl[1]);
+                Pair<E>::store(sQL + row * SRM + c0, ql[0], ql[1]);
+                Pair<E>::store(sKR + row * SRM + c0, kr[0], kr[1]);
+                Pair<E>::store(sQG + row * SRM + c0, ql[0] * eB[0], ql[1] * eB[1]);
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int o = (c0 + e) * STR + 16 * R + 4 * q4;
+                    OP::store4(sKGT + o, kgt[e][4 * q4], kgt[e][4 * q4 + 1], kgt[e][4 * q4 + 2],
+                               kgt[e][4 * q4 + 3]);
+                    OP::store4(sKDT + o, kdt[e][4 * q4], kdt[e][4 * q4 + 1], kdt[e][4 * q4 + 2],
+                               kdt[e][4 * q4 + 3]);
+                    if (has_v)
+                        OP::store4(sVT + o, vtt[e][4 * q4], vtt[e][4 * q4 + 1], vtt[e][4 * q4 + 2],
+                                   vtt[e][4 * q4 + 3]);
+                }
+            if (R == 0) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    sGAM[c0 + e] = exp2f(Bt[e]);
+#pragma unroll
+                    for (int Ri = 2; Ri < NB; ++Ri)
+#pragma unroll
+                        for (int Si = 0; Si + 2 <= Ri; ++Si) {
+                            float between = 0.f;
+#pragma unroll
+                            for (int Rp = Si + 1; Rp < Ri; ++Rp) between += sG2[Rp * 128 + c0 + e];
+                            sFO[fo_index(Ri, Si) * 128 + c0 + e] = exp2f(between);
+                        }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ----------------------------- phase 2: decayed Grams, diagonal inverses
+        auto gram_tile = [&](int kind, int R, int Sb) {
+            const E *lrow = (kind == 0 ? sKL : sQL) + (16 * R + m16) * SRM;
+            const E *rrow = sKR + (16 * Sb + m16) * SRM;
+            const float *f = (R == Sb) ? sFD + R * 128
+                                       : (R >= Sb + 2 ? sFO + fo_index(R, Sb) * 128 : nullptr);
+            const f32x4 acc = OP::gram(lrow, rrow, f, g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rl = 4 * g4 + i, sl = m16;
+                float val = acc[i];
+                if (kind == 0) {
+                    if (R == Sb && sl >= rl) val = 0.f;
+                    val *= sBET[16 * R + rl];
+                    if (R == Sb) sND[R * 256 + rl * 16 + sl] = val;
+                    else sLN[(16 * R + rl) * SCC + 16 * Sb + sl] = from_f32<E>(-val);
+                } else {
+                    if (R == Sb && sl > rl) val = 0.f;
+                    sPM[(16 * R + rl) * SCC + 16 * Sb + sl] = from_f32<E>(val);
+                }
+            }
+        };
+        if (w < NB) {
+            gram_tile(0, w, w);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < 16) {
+                // column `lane` of (I + N)^-1 with N the strictly lower diagonal block
+                const float *Nd = sND + w * 256;
+                float x[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float acc = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+                    for (int s = 0; s < i; ++s) acc -= Nd[i * 16 + s] * x[s];
+                    x[i] = acc;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sXD[(w * 16 + i) * SXD + lane] = from_f32<E>(x[i]);
+            }
+            gram_tile(1, w, w);
+        }
+        if constexpr (NB > 1) {
+            constexpr int NOFF = NB * (NB - 1) / 2;
+            for (int task = w; task < 2 * NOFF; task += 4) {
+                const int kind = task / NOFF, idx = task - kind * NOFF;
+                int R = 1, acc = 0;
+                while (acc + R <= idx) { acc += R; ++R; }
+                gram_tile(kind, R, idx - acc);
+            }
+        }
+        __syncthreads();
+
+        // ----------------------- phase 3: W and U0 by block forward substitution
+        f32x4 U0[NB][NTW];
+        {
+            B4 Wb[2][NB];
+#pragma unroll
+            for (int R = 0; R < NB; ++R) {
+                const E *lnrow = sLN + (16 * R + m16) * SCC + 4 * g4;
+                const E *xrow = sXD + (R * 16 + m16) * SXD + 4 * g4;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int col = 16 * (2 * w + j) + m16;
+                    f32x4 rhs = OP::load4(sKGT + col * STR + 16 * R + 4 * g4);
+                    rhs = OP::template chain<NB>(rhs, lnrow, Wb[j], R);
+                    B4 rb[1] = {OP::pack(rhs)};
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 wr = OP::template chain<1>(z, xrow, rb, 1);
+                    Wb[j][R] = OP::pack(wr);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sWN[(16 * R + 4 * g4 + i) * SRM + col] = from_f32<E>(-wr[i]);
+                }
+                if (st_wave) {
+                    B4 Ub[NTW][NB];
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) {
+                        const int col = 16 * (w * NTW + j) + m16;
+                        f32x4 rhs = OP::load4(sVT + col * STR + 16 * R + 4 * g4);
+                        // U0 blocks of earlier R are re-packed (cheap; keeps registers flat)
+#pragma unroll
+                        for (int Rp = 0; Rp < R; ++Rp) Ub[j][Rp] = OP::pack(U0[Rp][j]);
+                        rhs = OP::template chain<NB>(rhs, lnrow, Ub[j], R);
+                        B4 rb[1] = {OP::pack(rhs)};
+                        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                        U0[R][j] = OP::template chain<1>(z, xrow, rb, 1);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ----------------------------------------- phase 4: state path (per wave)
+        if (st_wave) {
+            B4 Sb[NTW][8];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) Sb[j][mt] = OP::pack(S[mt][j]);
+            B4 Ub[NTW][NB];
+#pragma unroll
+            for (int R = 0; R < NB; ++R) {
+                const E *wrow = sWN + (16 * R + m16) * SRM + 4 * g4;
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+                    Ub[j][R] = OP::pack(OP::template chain<8>(U0[R][j], wrow, Sb[j], 8));
+            }
+#pragma unroll
+            for (int R = 0; R < NB; ++R) {
+                const E *qrow = sQG + (16 * R + m16) * SRM + 4 * g4;
+                const E *prow = sPM + (16 * R + m16) * SCC + 4 * g4;
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = OP::template chain<8>(acc, qrow, Sb[j], 8);
+                    acc = OP::template chain<NB>(acc, prow, Ub[j], NB);
+                    const int col = dvb + 16 * (w * NTW + j) + m16;
+                    T *op = reinterpret_cast<T *>(p.o) + (size_t)h * D + col;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t sp = cbase + 16 * R + 4 * g4 + i;
+                        if (sp < L) op[(s0 + sp) * tokstride] = from_f32<T>(p.scale * acc[i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const f32x4 gam = *reinterpret_cast<const f32x4 *>(sGAM + 16 * mt + 4 * g4);
+                const E *krow = sKDT + (16 * mt + m16) * STR + 4 * g4;
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+                    S[mt][j] = OP::template chain<NB>(S[mt][j] * gam, krow, Ub[j], NB);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (st_wave && p.state_out) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int col = dvb + 16 * (w * NTW + j) + m16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * mt + 4 * g4 + i;
+                    p.state_out[((size_t)pr * D + row) * D + col] = S[mt][j][i];
+                }
+            }
+    }
+}
+
+template <typename T, int NB, int DVW>
+static hipError_t launch_t(const PrefillParams &pp, hipStream_t s) {
+    typedef Layout<T, NB, DVW> LY;
+    static_assert(LY::TOTAL <= 160 * 1024, "shared memory budget");
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [] {
+        attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<T, NB, DVW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LY::TOTAL);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    const int groups = (pp.pairs + 7) / 8;
+    const unsigned blocks = (unsigned)groups * 8u * (unsigned)pp.tiles;
+    hipLaunchKernelGGL((prefill_kernel<T, NB, DVW>), dim3(blocks), dim3(256), LY::TOTAL, s, pp);
+    return hipGetLastError();
+}
+
+template <typename T, int NB>
+static hipError_t dispatch_dv(const PrefillParams &pp, int dv_tile, hipStream_t s) {
+    switch (dv_tile) {
+        case 32: return launch_t<T, NB, 32>(pp, s);
+        case 64: return launch_t<T, NB, 64>(pp, s);
+        default: return launch_t<T, NB, 128>(pp, s);
+    }
+}
+
+hipError_t launch_prefill(const PrefillLaunch &L, hipStream_t s) {
+    const kda_prefill_args *a = L.a;
+    PrefillParams pp;
+    pp.q = a->q; pp.k = a->k; pp.v = a->v; pp.gate = a->gate; pp.beta = a->beta;
+    pp.w = a->conv_weight; pp.bias = a->conv_bias;
+    pp.cs_in = a->conv_state_in;
+    pp.state_in = a->state_in; pp.state_out = a->state_out;
+    pp.o = a->o;
+    pp.cu = a->cu_seqlens;
+    pp.total = a->total_tokens;
+    pp.num_seqs = a->num_seqs; pp.H = a->num_heads;
+    pp.scale = a->scale; pp.lb = a->gate_lower_bound; pp.flags = a->flags;
+    pp.pairs = a->num_seqs * a->num_heads;
+    pp.tiles = kHeadDim / L.dv_tile;
+    if (a->dtype == KDA_BF16) {
+        switch (L.chunk) {
+            case 16: return dispatch_dv<__bf16, 1>(pp, L.dv_tile, s);
+            case 32: return dispatch_dv<__bf16, 2>(pp, L.dv_tile, s);
+            default: return dispatch_dv<__bf16, 4>(pp, L.dv_tile, s);
+        }
+    }
+    switch (L.chunk) {
+        case 16: return dispatch_dv<float, 1>(pp, L.dv_tile, s);
+        default: return dispatch_dv<float, 2>(pp, L.dv_tile, s);
+    }
+}
+
+}  // namespace kda

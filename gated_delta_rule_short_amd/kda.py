@@ -1,0 +1,224 @@
+"""ctypes binding of libkda.so (the C ABI in include/kda.h).
+
+Argument marshalling only: torch tensors supply device memory and the HIP
+stream; every step of the mixer runs in the library's kernels.  There is no
+fallback: if libkda.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+KDA_F32, KDA_BF16 = 0, 1
+KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG = 1, 2, 4
+
+# every symbol include/kda.h declares
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_short_conv",
+           "kda_prefill", "kda_decode")
+
+_c_i32, _c_i64, _c_u32, _c_f32, _p = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                      ctypes.c_float, ctypes.c_void_p)
+
+
+class KdaPrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", _c_i32), ("num_heads", _c_i32), ("head_dim_k", _c_i32),
+        ("head_dim_v", _c_i32), ("chunk_size", _c_i32), ("total_tokens", _c_i64),
+        ("dtype", ctypes.c_int), ("flags", _c_u32), ("scale", _c_f32),
+        ("gate_lower_bound", _c_f32),
+        ("q", _p), ("k", _p), ("v", _p), ("gate", _p), ("beta", _p),
+        ("conv_weight", _p), ("conv_bias", _p), ("conv_state_in", _p), ("conv_state_out", _p),
+        ("state_in", _p), ("state_out", _p), ("o", _p), ("cu_seqlens", _p),
+        ("cu_seqlens_host", _p),
+    ]
+
+
+class KdaDecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", _c_i32), ("num_heads", _c_i32), ("head_dim_k", _c_i32),
+        ("head_dim_v", _c_i32), ("dtype", ctypes.c_int), ("flags", _c_u32),
+        ("scale", _c_f32), ("gate_lower_bound", _c_f32),
+        ("q", _p), ("k", _p), ("v", _p), ("gate", _p), ("beta", _p),
+        ("conv_weight", _p), ("conv_bias", _p), ("conv_state", _p), ("state", _p), ("o", _p),
+    ]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (status, msg))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (raises if it was not built) and declare its signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None and path == LIB_PATH:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError("libkda.so not found at %s: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`" % path)
+        lib = ctypes.CDLL(path)
+        lib.kda_abi_version.restype = ctypes.c_int
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_status_string.argtypes = [ctypes.c_int]
+        lib.kda_last_error.restype = ctypes.c_char_p
+        lib.kda_short_conv.restype = ctypes.c_int
+        lib.kda_short_conv.argtypes = [_p, _p, _c_i64, _c_i32, _p, _p, _p, _p, _p, _p, _c_i32,
+                                       ctypes.c_int, _c_u32, _p]
+        lib.kda_prefill.restype = ctypes.c_int
+        lib.kda_prefill.argtypes = [ctypes.POINTER(KdaPrefillArgs), _p]
+        lib.kda_decode.restype = ctypes.c_int
+        lib.kda_decode.argtypes = [ctypes.POINTER(KdaDecodeArgs), _p]
+        if path == LIB_PATH:
+            _lib = lib
+        return lib
+
+
+def _check(lib, status):
+    if status != KDA_OK:
+        raise KdaError(lib.kda_status_string(status).decode(), lib.kda_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError("unsupported dtype %s (bf16 or fp32)" % t.dtype)
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+
+
+def abi_version():
+    return load_library().kda_abi_version()
+
+
+def kda_short_conv(x, weight, *, cu_seqlens=None, cu_seqlens_host=None, bias=None,
+                   conv_state_in=None, conv_state_out=None, y=None, num_seqs=None, silu=False,
+                   stream=None):
+    """Causal depthwise conv, width 4.  x: [T, C] bf16/fp32 on the GPU; weight [C, 4] fp32.
+
+    Returns y (allocated when not given).  conv_state_out=True allocates [N, 3, C]."""
+    lib = load_library()
+    dev = x.device
+    T, C = x.shape
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else int(num_seqs or 1)
+    if y is None:
+        y = torch.empty_like(x)
+    if conv_state_out is True:
+        conv_state_out = torch.empty((N, 3, C), dtype=x.dtype, device=dev)
+    for t, nm in ((x, "x"), (y, "y"), (conv_state_in, "conv_state_in"),
+                  (conv_state_out, "conv_state_out")):
+        _need(t, nm, x.dtype, dev)
+    _need(weight, "weight", torch.float32, dev)
+    _need(bias, "bias", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    cuh = None
+    if cu_seqlens_host is not None:
+        cuh = cu_seqlens_host.to(torch.int32).contiguous().cpu()
+    st = lib.kda_short_conv(_ptr(x), _ptr(y), T, C, _ptr(weight), _ptr(bias), _ptr(conv_state_in),
+                            _ptr(conv_state_out), _ptr(cu_seqlens), _ptr(cuh), N, _dtype_code(x),
+                            KDA_F_SILU if silu else 0, _stream(stream, dev))
+    _check(lib, st)
+    if conv_state_out is not None:
+        return y, conv_state_out
+    return y
+
+
+def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens_host=None,
+                num_seqs=None, conv_bias=None, conv_state_in=None, conv_state_out=None,
+                state_in=None, state_out=None, o=None, scale=0.0, gate_lower_bound=-5.0,
+                chunk_size=0, flags=0, stream=None):
+    """Chunked KDA prefill of packed sequences.
+
+    q, k, gate: [T, H, 128]; v: [T, H, 128]; beta: [T, H] (bf16 or fp32, one dtype);
+    conv_weight: [3*H*128, 4] fp32.  state_out / conv_state_out: a tensor, or True
+    to allocate one.  Returns (o, state_out, conv_state_out)."""
+    lib = load_library()
+    dev = q.device
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else int(num_seqs or 1)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    if state_out is True:
+        state_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if conv_state_out is True:
+        conv_state_out = torch.empty((N, 3, 2 * H * dk + H * dv), dtype=q.dtype, device=dev)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (o, "o"),
+                  (conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
+        _need(t, nm, q.dtype, dev)
+    for t, nm in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"),
+                  (state_in, "state_in"), (state_out, "state_out")):
+        _need(t, nm, torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    cuh = None
+    if cu_seqlens_host is not None:
+        cuh = cu_seqlens_host.to(torch.int32).contiguous().cpu()
+    a = KdaPrefillArgs(
+        num_seqs=N, num_heads=H, head_dim_k=dk, head_dim_v=dv, chunk_size=int(chunk_size),
+        total_tokens=T, dtype=_dtype_code(q), flags=int(flags), scale=float(scale),
+        gate_lower_bound=float(gate_lower_bound),
+        q=_ptr(q), k=_ptr(k), v=_ptr(v), gate=_ptr(gate), beta=_ptr(beta),
+        conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias),
+        conv_state_in=_ptr(conv_state_in), conv_state_out=_ptr(conv_state_out),
+        state_in=_ptr(state_in), state_out=_ptr(state_out), o=_ptr(o),
+        cu_seqlens=_ptr(cu_seqlens), cu_seqlens_host=_ptr(cuh))
+    _check(lib, lib.kda_prefill(ctypes.byref(a), _stream(stream, dev)))
+    return o, state_out, conv_state_out
+
+
+def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias=None, o=None,
+               scale=0.0, gate_lower_bound=-5.0, flags=0, stream=None):
+    """One decode step: q, k, gate, v: [N, H, 128]; beta [N, H]; conv_state [N, 3, CC]
+    and state [N, H, 128, 128] fp32 are updated in place.  Returns o [N, H, 128]."""
+    lib = load_library()
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (o, "o"),
+                  (conv_state, "conv_state")):
+        _need(t, nm, q.dtype, dev)
+    for t, nm in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"), (state, "state")):
+        _need(t, nm, torch.float32, dev)
+    a = KdaDecodeArgs(
+        num_seqs=N, num_heads=H, head_dim_k=dk, head_dim_v=dv, dtype=_dtype_code(q),
+        flags=int(flags), scale=float(scale), gate_lower_bound=float(gate_lower_bound),
+        q=_ptr(q), k=_ptr(k), v=_ptr(v), gate=_ptr(gate), beta=_ptr(beta),
+        conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias), conv_state=_ptr(conv_state),
+        state=_ptr(state), o=_ptr(o))
+    _check(lib, lib.kda_decode(ctypes.byref(a), _stream(stream, dev)))
+    return o

@@ -1,0 +1,176 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) implementation of the
+ * Kimi Delta Attention (KDA) sequence mixer.
+ *
+ * The operation (source: "GLM-5.3-Flash im Detail" (flozi.net), section
+ * "Sequenz-Mixing: 34 KDA-Schichten mit festem Zustand"; the dataset card
+ * "GLM-5.3-Flash Internals", section "Anatomy", gives the same shape):
+ * per head (64 heads of dimension 128 in the published model) q, k and v pass
+ * through a causal depthwise convolution of width 4; a channel-wise forget gate
+ * with log-decay bounded below at -5 attenuates a matrix state; a scalar beta
+ * drives a delta-rule write of v along k; the query reads the updated state.
+ * Prefill evaluates tokens inside chunks in parallel and passes a state between
+ * chunks; decode of one token is a recurrent update (same section).  The state
+ * is a dk x dv matrix per head held in fp32 (same section, the state-size
+ * arithmetic), and prefill and decode share one state layout (same page,
+ * section "FP8-Checkpoint und Betriebsgrenzen": identical KDA layouts when
+ * prefill and decode run separately).
+ *
+ * Per token t of a sequence and per head, with conv-ed, L2-normalised q_t, k_t:
+ *     S   <- diag(exp(g_t)) S                 g_t = lb * sigmoid(a_t), lb = -5
+ *     u   =  beta_t * (v_t - S^T k_t)
+ *     S   <- S + k_t u^T
+ *     o_t =  scale * S^T q_t
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every buffer.  The library never allocates,
+ *     frees or synchronises; work is enqueued asynchronously on `stream`.
+ *   - Pointers: all tensor pointers are DEVICE pointers, except the optional
+ *     `cu_seqlens_host`, which is a HOST pointer used only for validation.
+ *   - Layouts are dense row-major with the last index fastest.  T = total
+ *     tokens of all packed sequences, N = number of sequences, H = heads,
+ *     dk = dv = 128, CC = 2*H*dk + H*dv conv channels ordered q, k, v
+ *     (head-major, channel fastest inside each).
+ *   - dtype (kda_dtype) applies to q, k, v, gate, beta, o and conv states;
+ *     conv weights/biases and the recurrent state are always fp32.
+ *   - Errors: every argument check runs on the host before any launch and
+ *     returns KDA_ERR_INVALID_ARG (bad pointer, size, layout) or
+ *     KDA_ERR_UNSUPPORTED (head dim != 128, unknown flag, unsupported chunk).
+ *     A failed launch returns KDA_ERR_HIP.  kda_last_error() gives a message
+ *     for the calling thread's last failure.  No exception crosses the ABI.
+ *   - Thread safety: no global mutable state besides that per-thread message;
+ *     concurrent calls on different buffers are safe.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,
+    KDA_ERR_UNSUPPORTED = 2,
+    KDA_ERR_HIP = 3
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Flags.  The pages do not say whether an activation follows the conv, whether
+ * q/k are L2-normalised, or how the gate is parameterised; these flags select
+ * the alternatives (default: no activation, L2 on, g = lb * sigmoid(a)). */
+enum {
+    KDA_F_SILU = 1u,          /* y <- y * sigmoid(y) after the conv (q, k and v) */
+    KDA_F_NO_QK_L2NORM = 2u,  /* skip q/k L2 normalisation x / sqrt(|x|^2 + 1e-6) */
+    KDA_F_GATE_IS_LOG = 4u    /* gate holds the log-decay: g = max(gate, lb) */
+};
+#define KDA_F_ALL (KDA_F_SILU | KDA_F_NO_QK_L2NORM | KDA_F_GATE_IS_LOG)
+
+/* Version of this ABI (KDA_ABI_VERSION). */
+int kda_abi_version(void);
+
+/* Static string naming a kda_status value. */
+const char *kda_status_string(int status);
+
+/* Message describing the calling thread's most recent failing call ("" if none). */
+const char *kda_last_error(void);
+
+/*
+ * kda_short_conv -- causal depthwise convolution of width 4 over packed
+ * sequences (the conv step of the passage above, on its own).
+ *   x, y            [T][channels] in `dtype`; y must not overlap x.
+ *   weight          [channels][4] fp32; tap 3 multiplies the current token,
+ *                   taps 0..2 the three previous tokens of the same sequence.
+ *   bias            [channels] fp32 or NULL.
+ *   conv_state_in   [N][3][channels] or NULL (zeros): the three raw tokens
+ *                   before each sequence, oldest first.
+ *   conv_state_out  [N][3][channels] or NULL: the last three raw tokens of
+ *                   (conv_state_in ++ sequence); may alias conv_state_in.
+ *   cu_seqlens      [N+1] int32 device prefix sums (cu[0] = 0, cu[N] = T), or
+ *                   NULL for N equal sequences of T/N tokens.
+ *   cu_seqlens_host optional host copy of cu_seqlens; when given it is
+ *                   checked (monotone, cu[0] = 0, cu[N] = T).
+ *   flags           0 or KDA_F_SILU.
+ * A sequence never reads another sequence's tokens.  Empty sequences are
+ * allowed (their conv state passes through).
+ */
+kda_status kda_short_conv(const void *x, void *y, int64_t total_tokens, int32_t channels,
+                          const float *weight, const float *bias,
+                          const void *conv_state_in, void *conv_state_out,
+                          const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                          int32_t num_seqs, kda_dtype dtype, uint32_t flags,
+                          hipStream_t stream);
+
+/*
+ * kda_prefill -- chunk-parallel prefill of packed sequences (the prefill
+ * kernel shape of the passage above): tokens inside a chunk are evaluated in
+ * parallel through the WY/UT form, the fp32 state is carried from chunk to
+ * chunk.
+ */
+typedef struct {
+    int32_t num_seqs;        /* N >= 1 */
+    int32_t num_heads;       /* H >= 1 */
+    int32_t head_dim_k;      /* must be 128 */
+    int32_t head_dim_v;      /* must be 128 */
+    int32_t chunk_size;      /* 0 = default (64 for bf16, 32 for fp32); 16, 32 or 64
+                                (fp32 I/O: 16 or 32) */
+    int64_t total_tokens;    /* T >= 0 */
+    kda_dtype dtype;
+    uint32_t flags;          /* KDA_F_* */
+    float scale;             /* 0 = 1/sqrt(dk) */
+    float gate_lower_bound;  /* lb of the log-decay, -5 in the published model; < 0 */
+    const void *q, *k;       /* [T][H][dk] raw (pre-conv) */
+    const void *v;           /* [T][H][dv] raw (pre-conv) */
+    const void *gate;        /* [T][H][dk] pre-activation a (log-decay if GATE_IS_LOG) */
+    const void *beta;        /* [T][H] write strength in [0, 1] */
+    const float *conv_weight;/* [CC][4] */
+    const float *conv_bias;  /* [CC] or NULL */
+    const void *conv_state_in; /* [N][3][CC] or NULL (zeros) */
+    void *conv_state_out;      /* [N][3][CC] or NULL; may alias conv_state_in */
+    const float *state_in;     /* [N][H][dk][dv] fp32 or NULL (zeros) */
+    float *state_out;          /* [N][H][dk][dv] fp32 or NULL; may alias state_in */
+    void *o;                   /* [T][H][dv] output; must not overlap the inputs */
+    const int32_t *cu_seqlens; /* [N+1] device, or NULL for N equal sequences */
+    const int32_t *cu_seqlens_host; /* optional host copy, validated when given */
+} kda_prefill_args;
+
+kda_status kda_prefill(const kda_prefill_args *args, hipStream_t stream);
+
+/*
+ * kda_decode -- one new token for each of N sequences (the single-token
+ * recurrent update of the passage above).  The conv cache and the state are
+ * updated in place; the state layout is the one kda_prefill writes.
+ */
+typedef struct {
+    int32_t num_seqs;        /* N >= 1 */
+    int32_t num_heads;       /* H >= 1 */
+    int32_t head_dim_k;      /* must be 128 */
+    int32_t head_dim_v;      /* must be 128 */
+    kda_dtype dtype;
+    uint32_t flags;          /* KDA_F_* */
+    float scale;             /* 0 = 1/sqrt(dk) */
+    float gate_lower_bound;  /* < 0 */
+    const void *q, *k;       /* [N][H][dk] raw */
+    const void *v;           /* [N][H][dv] raw */
+    const void *gate;        /* [N][H][dk] */
+    const void *beta;        /* [N][H] */
+    const float *conv_weight;/* [CC][4] */
+    const float *conv_bias;  /* [CC] or NULL */
+    void *conv_state;        /* [N][3][CC] in/out (shifted by one token) */
+    float *state;            /* [N][H][dk][dv] fp32 in/out */
+    void *o;                 /* [N][H][dv] */
+} kda_decode_args;
+
+kda_status kda_decode(const kda_decode_args *args, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

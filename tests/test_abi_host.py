@@ -1,0 +1,175 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every symbol
+include/kda.h declares, and rejects bad arguments on the host before touching a
+device.  The validation paths return before any HIP call, so they run here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_short_amd as pkg
+from gated_delta_rule_short_amd import kda as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.LIB_PATH):
+        from gated_delta_rule_short_amd import _build
+        _build.build()
+    return K.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text))
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == set(K.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.kda_abi_version() == 1
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARG"
+    assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
+    assert lib.kda_status_string(3) == b"KDA_ERR_HIP"
+
+
+def test_struct_layouts_match_header():
+    # offsets of the first pointer fields follow the C layout rules (int64 aligned at 8)
+    assert K.KdaPrefillArgs.total_tokens.offset == 24
+    assert K.KdaPrefillArgs.q.offset == 48
+    assert ctypes.sizeof(K.KdaPrefillArgs) == 48 + 14 * 8
+    assert K.KdaDecodeArgs.q.offset == 32
+    assert ctypes.sizeof(K.KdaDecodeArgs) == 32 + 10 * 8
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def _prefill_args(**kw):
+    a = K.KdaPrefillArgs(num_seqs=1, num_heads=2, head_dim_k=128, head_dim_v=128, chunk_size=0,
+                         total_tokens=64, dtype=K.KDA_BF16, flags=0, scale=0.0,
+                         gate_lower_bound=-5.0)
+    for f in ("q", "k", "v", "gate", "beta", "conv_weight", "o"):
+        setattr(a, f, None)
+    base = 0x100000
+    for i, f in enumerate(("q", "k", "v", "gate", "beta", "conv_weight", "o")):
+        setattr(a, f, ctypes.c_void_p(base + i * 0x1000000))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_seqs", 0, K.KDA_ERR_INVALID_ARG),
+    ("num_heads", 0, K.KDA_ERR_INVALID_ARG),
+    ("head_dim_k", 64, K.KDA_ERR_UNSUPPORTED),
+    ("head_dim_v", 256, K.KDA_ERR_UNSUPPORTED),
+    ("chunk_size", 48, K.KDA_ERR_UNSUPPORTED),
+    ("flags", 8, K.KDA_ERR_UNSUPPORTED),
+    ("dtype", 7, K.KDA_ERR_INVALID_ARG),
+    ("gate_lower_bound", 0.0, K.KDA_ERR_INVALID_ARG),
+    ("gate_lower_bound", float("nan"), K.KDA_ERR_INVALID_ARG),
+    ("scale", -1.0, K.KDA_ERR_INVALID_ARG),
+    ("total_tokens", -1, K.KDA_ERR_INVALID_ARG),
+    ("q", None, K.KDA_ERR_INVALID_ARG),
+    ("conv_weight", None, K.KDA_ERR_INVALID_ARG),
+])
+def test_prefill_rejects_bad_arguments(lib, field, value, status):
+    a = _prefill_args(**{field: value})
+    assert lib.kda_prefill(ctypes.byref(a), None) == status
+    assert lib.kda_last_error() != b""
+
+
+def test_prefill_fp32_chunk64_unsupported(lib):
+    a = _prefill_args(dtype=K.KDA_F32, chunk_size=64)
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_UNSUPPORTED
+
+
+def test_prefill_checks_host_cu_seqlens(lib):
+    for cu in ([1, 64], [0, 30, 20, 64], [0, 63]):
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        a = _prefill_args(num_seqs=len(cu) - 1, cu_seqlens=FAKE,
+                          cu_seqlens_host=ctypes.cast(arr, ctypes.c_void_p))
+        assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG, cu
+
+
+def test_prefill_dense_layout_needs_divisible_tokens(lib):
+    a = _prefill_args(num_seqs=3, total_tokens=64)
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_prefill_rejects_output_overlapping_input(lib):
+    a = _prefill_args()
+    a.o = a.q
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_prefill_rejects_partial_state_alias(lib):
+    a = _prefill_args(state_in=ctypes.c_void_p(0x9000000), state_out=ctypes.c_void_p(0x9000010))
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def _decode_args(**kw):
+    a = K.KdaDecodeArgs(num_seqs=2, num_heads=2, head_dim_k=128, head_dim_v=128,
+                        dtype=K.KDA_BF16, flags=0, scale=0.0, gate_lower_bound=-5.0)
+    base = 0x100000
+    for i, f in enumerate(("q", "k", "v", "gate", "beta", "conv_weight", "conv_state", "state",
+                           "o")):
+        setattr(a, f, ctypes.c_void_p(base + i * 0x1000000))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_seqs", -1, K.KDA_ERR_INVALID_ARG),
+    ("head_dim_k", 32, K.KDA_ERR_UNSUPPORTED),
+    ("flags", 0x10, K.KDA_ERR_UNSUPPORTED),
+    ("state", None, K.KDA_ERR_INVALID_ARG),
+    ("conv_state", None, K.KDA_ERR_INVALID_ARG),
+    ("o", None, K.KDA_ERR_INVALID_ARG),
+    ("gate_lower_bound", 1.0, K.KDA_ERR_INVALID_ARG),
+])
+def test_decode_rejects_bad_arguments(lib, field, value, status):
+    a = _decode_args(**{field: value})
+    assert lib.kda_decode(ctypes.byref(a), None) == status
+
+
+def test_decode_rejects_state_overlapping_output(lib):
+    a = _decode_args()
+    a.state = a.o
+    assert lib.kda_decode(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_short_conv_rejects_bad_arguments(lib):
+    f = lib.kda_short_conv
+    # num_seqs 0
+    assert f(FAKE, ctypes.c_void_p(0x900000), 8, 4, FAKE, None, None, None, None, None, 0, 1, 0,
+             None) == K.KDA_ERR_INVALID_ARG
+    # unknown flag
+    assert f(FAKE, ctypes.c_void_p(0x900000), 8, 4, FAKE, None, None, None, None, None, 1, 1, 2,
+             None) == K.KDA_ERR_UNSUPPORTED
+    # y overlapping x
+    assert f(FAKE, FAKE, 8, 4, FAKE, None, None, None, None, None, 1, 1, 0,
+             None) == K.KDA_ERR_INVALID_ARG
+    # bad host cu_seqlens
+    cu = (ctypes.c_int32 * 3)(0, 5, 7)
+    assert f(FAKE, ctypes.c_void_p(0x900000), 8, 4, FAKE, None, None, None, FAKE,
+             ctypes.cast(cu, ctypes.c_void_p), 2, 1, 0, None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        K.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,330 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element
+by element on the same seeded inputs, plus invariants the chunked method must
+keep.  Bars: fp32 inputs max-abs <= 1e-4; bf16 inputs relative L2 <= 2e-2 per
+(sequence, head) slice, for outputs and final states."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as KI
+import oracle
+import gated_delta_rule_short_amd as kda
+from tests._gpu_common import (BF16_REL, assert_bf16_close, assert_f32_close, head_conv_state,
+                               head_conv_w, slice_rel_errors, state_rel_errors, to_np)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kda.load_library()
+
+
+def _oracle_prefill(inp, **kw):
+    return oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["conv_w"],
+                          inp["cu_seqlens"], state_in=inp.get("state_in"),
+                          conv_state_in=inp.get("conv_state_in"), **kw)
+
+
+def _gpu_prefill(inp, **kw):
+    o, st, cs = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                                inp["conv_w"], cu_seqlens=inp["cu_seqlens"],
+                                state_in=inp.get("state_in"),
+                                conv_state_in=inp.get("conv_state_in"), state_out=True,
+                                conv_state_out=True, **kw)
+    torch.cuda.synchronize()
+    return o, st, cs
+
+
+# ------------------------------------------------------------------ short conv
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("silu", [False, True])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_short_conv_matches_oracle(dtype, silu, with_state):
+    g = torch.Generator(device="cpu").manual_seed(3)
+    lengths = [37, 0, 1, 2, 3, 100, 64, 5]
+    C = 390  # not a multiple of the 512 channels a block covers
+    cu = KI.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    x = torch.randn(T, C, generator=g).to(dtype)
+    w = torch.randn(C, 4, generator=g) * 0.5
+    b = torch.randn(C, generator=g) * 0.1
+    cs = torch.randn(len(lengths), 3, C, generator=g).to(dtype) if with_state else None
+    y, cso = kda.kda_short_conv(x.to(DEV), w.to(DEV), cu_seqlens=cu.to(DEV), cu_seqlens_host=cu,
+                                bias=b.to(DEV), conv_state_in=None if cs is None else cs.to(DEV),
+                                conv_state_out=True, silu=silu)
+    torch.cuda.synchronize()
+    ref, ref_cs = oracle.short_conv(x, w, cu, bias=b, conv_state_in=cs, silu=silu)
+    yn = to_np(y)
+    if dtype == torch.float32:
+        np.testing.assert_allclose(yn, ref, rtol=1e-5, atol=1e-5)
+    else:  # one bf16 rounding of the fp32 result
+        np.testing.assert_allclose(yn, ref, rtol=2 ** -7, atol=1e-6)
+    # the conv state is a copy of raw tokens: exact
+    np.testing.assert_array_equal(to_np(cso), ref_cs)
+
+
+def test_short_conv_dense_odd_channels_and_in_place_state():
+    g = torch.Generator(device="cpu").manual_seed(4)
+    N, L, C = 3, 21, 33
+    x = torch.randn(N * L, C, generator=g)
+    w = torch.randn(C, 4, generator=g)
+    cs = torch.randn(N, 3, C, generator=g)
+    ref, ref_cs = oracle.short_conv(x, w, KI.cu_from_lengths([L] * N), conv_state_in=cs)
+    csd = cs.to(DEV)
+    y = kda.kda_short_conv(x.to(DEV), w.to(DEV), num_seqs=N, conv_state_in=csd,
+                           conv_state_out=csd)[0]
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_np(y), ref, rtol=1e-5, atol=1e-5)
+    np.testing.assert_array_equal(to_np(csd), ref_cs)
+
+
+# ---------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("flags", [0, kda.KDA_F_SILU | kda.KDA_F_GATE_IS_LOG, kda.KDA_F_NO_QK_L2NORM])
+def test_decode_matches_oracle(dtype, flags):
+    d = KI.make_decode(6, 3, dtype=dtype, seed=21, device=DEV)
+    if flags & kda.KDA_F_GATE_IS_LOG:
+        d["gate"] = (-6.0 * torch.rand(d["gate"].shape, device=DEV)).to(dtype)
+    bias = (0.1 * torch.randn(d["conv_w"].shape[0], device=DEV))
+    ref = oracle.decode(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"], d["conv_state"],
+                        d["state"], conv_b=bias, flags=flags)
+    o = kda.kda_decode(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"], d["conv_state"],
+                       d["state"], conv_bias=bias, flags=flags)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(d["conv_state"]), ref["conv_state"])
+    if dtype == torch.float32:
+        assert_f32_close(o, ref["o"], "decode o")
+        assert_f32_close(d["state"], ref["state"], "decode state")
+    else:
+        e = np.linalg.norm((to_np(o) - ref["o"]).reshape(-1, 128), axis=1) / \
+            np.linalg.norm(ref["o"].reshape(-1, 128), axis=1)
+        assert e.max() <= BF16_REL
+        assert state_rel_errors(d["state"], ref["state"]).max() <= BF16_REL
+
+
+def test_decode_full_size_sampled():
+    """The 256-sequence x 64-head decode step as timed; the oracle checks sampled sequences."""
+    d = KI.workload_inputs(2, device=DEV)
+    st0 = d["state"].clone()
+    cs0 = d["conv_state"].clone()
+    o = kda.kda_decode(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"], d["conv_state"],
+                       d["state"])
+    torch.cuda.synchronize()
+    for n in (0, 101, 255):
+        sl = slice(n, n + 1)
+        ref = oracle.decode(d["q"][sl], d["k"][sl], d["v"][sl], d["gate"][sl], d["beta"][sl],
+                            d["conv_w"], cs0[sl], st0[sl])
+        e = np.linalg.norm((to_np(o[sl]) - ref["o"]).reshape(-1, 128), axis=1) / \
+            np.linalg.norm(ref["o"].reshape(-1, 128), axis=1)
+        assert e.max() <= BF16_REL, (n, e.max())
+        assert state_rel_errors(d["state"][sl], ref["state"]).max() <= BF16_REL
+        np.testing.assert_array_equal(to_np(d["conv_state"][sl]), ref["conv_state"])
+
+
+# --------------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_prefill_tiny_fp32_max_abs(chunk):
+    """The tiny fp32 workload (H=1, T=256): max-abs error <= 1e-4."""
+    inp = KI.workload_inputs(0, device=DEV)
+    ref = _oracle_prefill(inp)
+    o, st, cs = _gpu_prefill(inp, chunk_size=chunk)
+    assert_f32_close(o, ref["o"], "o")
+    assert_f32_close(st, ref["state"], "state")
+    np.testing.assert_array_equal(to_np(cs), ref["conv_state"])
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_prefill_bf16_ragged(chunk):
+    lengths = [1, 2, 3, 15, 16, 17, 0, 63, 64, 65, 130, 200]
+    inp = KI.make_prefill(3, lengths, seed=31, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    ref = _oracle_prefill(inp)
+    o, st, cs = _gpu_prefill(inp, chunk_size=chunk, cu_seqlens_host=inp["cu_seqlens"].cpu())
+    assert_bf16_close(o, ref["o"], inp["cu_seqlens"], 3, st, ref["state"], "chunk %d" % chunk)
+    np.testing.assert_array_equal(to_np(cs), ref["conv_state"])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("flags", [kda.KDA_F_SILU, kda.KDA_F_NO_QK_L2NORM, kda.KDA_F_GATE_IS_LOG])
+def test_prefill_flags_and_bias(dtype, flags):
+    inp = KI.make_prefill(2, [40, 77], dtype=dtype, seed=41, device=DEV, state_std=0.1,
+                          conv_cache_std=1.0)
+    if flags & kda.KDA_F_GATE_IS_LOG:
+        inp["gate"] = (-6.0 * torch.rand(inp["gate"].shape, device=DEV)).to(dtype)
+    bias = 0.1 * torch.randn(inp["conv_w"].shape[0], device=DEV)
+    ref = _oracle_prefill(inp, conv_b=bias, flags=flags, scale=0.3, gate_lower_bound=-4.0)
+    o, st, cs = _gpu_prefill(inp, conv_bias=bias, flags=flags, scale=0.3, gate_lower_bound=-4.0)
+    if dtype == torch.float32:
+        assert_f32_close(o, ref["o"], "o")
+        assert_f32_close(st, ref["state"], "state")
+    else:
+        assert_bf16_close(o, ref["o"], inp["cu_seqlens"], 2, st, ref["state"])
+
+
+@pytest.mark.parametrize("dv_tile", ["32", "64", "128"])
+def test_prefill_dv_tiles_agree(dv_tile, monkeypatch):
+    monkeypatch.setenv("KDA_PREFILL_DV_TILE", dv_tile)
+    inp = KI.make_prefill(2, [130, 70], seed=51, device=DEV, state_std=0.1)
+    ref = _oracle_prefill(inp)
+    o, st, _ = _gpu_prefill(inp)
+    assert_bf16_close(o, ref["o"], inp["cu_seqlens"], 2, st, ref["state"], "dv tile " + dv_tile)
+
+
+def test_prefill_workload1_reduced_heads_full_length():
+    """Single-sequence 4096-token prefill with 8 of the 64 heads, checked in full."""
+    inp = KI.workload_inputs(1, device=DEV, H=8)
+    ref = _oracle_prefill(inp)
+    o, st, _ = _gpu_prefill(inp)
+    assert_bf16_close(o, ref["o"], inp["cu_seqlens"], 8, st, ref["state"])
+
+
+def _sampled_check(inp, o, st, heads, seqs=None):
+    H = inp["H"]
+    cu = [int(c) for c in inp["cu_seqlens"]]
+    seqs = range(len(cu) - 1) if seqs is None else seqs
+    for n in seqs:
+        a, b = cu[n], cu[n + 1]
+        sub = {
+            "q": inp["q"][a:b, heads], "k": inp["k"][a:b, heads], "v": inp["v"][a:b, heads],
+            "gate": inp["gate"][a:b, heads], "beta": inp["beta"][a:b, heads],
+            "conv_w": head_conv_w(inp["conv_w"], H, heads),
+            "cu_seqlens": torch.tensor([0, b - a], dtype=torch.int32),
+            "state_in": None if inp["state_in"] is None else inp["state_in"][n:n + 1, heads],
+            "conv_state_in": None,
+        }
+        ref = _oracle_prefill(sub, nthreads=len(heads))
+        assert_bf16_close(o[a:b, heads], ref["o"], sub["cu_seqlens"], len(heads),
+                          st[n:n + 1, heads], ref["state"], "seq %d" % n)
+
+
+def test_prefill_workload1_full_size_sampled_heads():
+    """The timed prefill configuration (H=64, T=4096) with sampled heads checked."""
+    inp = KI.workload_inputs(1, device=DEV)
+    o, st, _ = _gpu_prefill(inp)
+    _sampled_check(inp, o, st, [0, 21, 63])
+    assert torch.isfinite(o).all()
+
+
+def test_prefill_workload3_long_sampled_heads():
+    """T=65536 with gates near the -5 bound: 1024 chunks of carried state."""
+    inp = KI.workload_inputs(3, device=DEV)
+    o, st, _ = _gpu_prefill(inp)
+    assert torch.isfinite(o).all() and torch.isfinite(st).all()
+    _sampled_check(inp, o, st, [5, 40])
+
+
+def test_prefill_workload4_varlen_sampled():
+    """16 packed sequences (lengths 512..16384) with nonzero initial states."""
+    inp = KI.workload_inputs(4, device=DEV)
+    o, st, _ = _gpu_prefill(inp)
+    assert torch.isfinite(o).all()
+    lengths = inp["lengths"]
+    longest = int(np.argmax(lengths))
+    shortest = int(np.argmin(lengths))
+    _sampled_check(inp, o, st, [3, 62], seqs=[longest, shortest, 7])
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_split_prefill_equals_whole():
+    inp = KI.make_prefill(2, [300], seed=61, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    o, st, cs = _gpu_prefill(inp)
+    for cut in (64, 100):
+        a = {k_: (v_[:cut] if k_ in ("q", "k", "v", "gate", "beta") else v_) for k_, v_ in inp.items()}
+        a["cu_seqlens"] = torch.tensor([0, cut], dtype=torch.int32, device=DEV)
+        o1, st1, cs1 = _gpu_prefill(a)
+        b = {k_: (v_[cut:] if k_ in ("q", "k", "v", "gate", "beta") else v_) for k_, v_ in inp.items()}
+        b["cu_seqlens"] = torch.tensor([0, 300 - cut], dtype=torch.int32, device=DEV)
+        b["state_in"], b["conv_state_in"] = st1, cs1
+        o2, st2, cs2 = _gpu_prefill(b)
+        e = slice_rel_errors(torch.cat([o1, o2]), o, [0, 300], 2)
+        assert e.max() <= 1e-2
+        assert state_rel_errors(st2, st).max() <= 1e-2
+        assert torch.equal(cs2, cs)
+        if cut % 64 == 0:  # chunk boundaries coincide: same arithmetic
+            assert torch.equal(torch.cat([o1, o2]), o)
+
+
+def test_prefill_equals_decode_steps():
+    T = 9
+    inp = KI.make_prefill(2, [T], seed=71, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    o, st, cs = _gpu_prefill(inp)
+    state = inp["state_in"].clone()
+    conv = inp["conv_state_in"].clone()
+    outs = []
+    for t in range(T):
+        outs.append(kda.kda_decode(inp["q"][t:t + 1], inp["k"][t:t + 1], inp["v"][t:t + 1],
+                                   inp["gate"][t:t + 1], inp["beta"][t:t + 1], inp["conv_w"], conv,
+                                   state))
+    torch.cuda.synchronize()
+    e = slice_rel_errors(torch.cat(outs), o, [0, T], 2)
+    assert e.max() <= 1e-2
+    assert state_rel_errors(state, st).max() <= 1e-2
+    assert torch.equal(conv, cs)
+
+
+def test_varlen_packed_equals_separate_calls_bitwise():
+    lengths = [70, 0, 129, 5]
+    inp = KI.make_prefill(2, lengths, seed=81, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    o, st, cs = _gpu_prefill(inp)
+    cu = [int(c) for c in inp["cu_seqlens"]]
+    for n, L in enumerate(lengths):
+        a, b = cu[n], cu[n + 1]
+        one = {k_: (v_[a:b] if k_ in ("q", "k", "v", "gate", "beta") else v_) for k_, v_ in inp.items()}
+        one["cu_seqlens"] = torch.tensor([0, L], dtype=torch.int32, device=DEV)
+        one["state_in"] = inp["state_in"][n:n + 1]
+        one["conv_state_in"] = inp["conv_state_in"][n:n + 1]
+        o1, st1, cs1 = _gpu_prefill(one)
+        assert torch.equal(o1, o[a:b])
+        assert torch.equal(st1, st[n:n + 1])
+        assert torch.equal(cs1, cs[n:n + 1])
+    # an empty sequence passes its states through
+    assert torch.equal(st[1], inp["state_in"][1])
+    assert torch.equal(cs[1], inp["conv_state_in"][1])
+
+
+def test_in_place_state_and_conv_state():
+    inp = KI.make_prefill(2, [90, 33], seed=91, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    o, st, cs = _gpu_prefill(inp)
+    s_io = inp["state_in"].clone()
+    c_io = inp["conv_state_in"].clone()
+    o2, _, _ = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                               inp["conv_w"], cu_seqlens=inp["cu_seqlens"], state_in=s_io,
+                               state_out=s_io, conv_state_in=c_io, conv_state_out=c_io)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(s_io, st) and torch.equal(c_io, cs)
+
+
+def test_every_output_written_and_deterministic():
+    inp = KI.make_prefill(3, [200, 1, 64], seed=101, device=DEV, state_std=0.1)
+    T = inp["q"].shape[0]
+    outs = []
+    for _ in range(2):
+        o = torch.full((T, 3, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+        st = torch.full((3, 3, 128, 128), float("nan"), device=DEV)
+        kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["conv_w"],
+                        cu_seqlens=inp["cu_seqlens"], state_in=inp["state_in"], state_out=st, o=o)
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any() and not torch.isnan(st).any()
+        outs.append((o, st))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_chunk_sizes_agree():
+    inp = KI.make_prefill(2, [257], seed=111, device=DEV, state_std=0.1)
+    res = [_gpu_prefill(inp, chunk_size=c) for c in (16, 32, 64)]
+    for o, st, _ in res[1:]:
+        assert slice_rel_errors(o, res[0][0], [0, 257], 2).max() <= 1e-2
+        assert state_rel_errors(st, res[0][1]).max() <= 1e-2
+
+
+def test_empty_batch_and_zero_tokens():
+    inp = KI.make_prefill(1, [0, 0], seed=5, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    o, st, cs = _gpu_prefill(inp)
+    assert o.numel() == 0
+    assert torch.equal(st, inp["state_in"]) and torch.equal(cs, inp["conv_state_in"])
