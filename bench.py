@@ -1,0 +1,214 @@
+"""Benchmark of the KDA mixer on one MI355X.
+
+One step runs every entry point of the hot path once, each on its workload,
+with all inputs already resident in HBM:
+  prefill    : 1 sequence x 4096 tokens, 64 heads of 128, bf16, chunk 64,
+               zero initial state, final fp32 state written   (kda_prefill)
+  decode     : 256 sequences x 1 token, 64 heads, fp32 state 256x64x128x128
+               updated in place, bf16 tokens                  (kda_decode)
+  short_conv : the same 4096-token q|k|v rows as a [4096, 24576] bf16 tensor,
+               conv width 4                                   (kda_short_conv)
+Every call is bracketed by HIP events on the stream it is launched on; `value`
+is prefill tokens per second per layer from the prefill kernel's own time,
+decode reports the state bandwidth (read + write of the fp32 state).
+
+Prints ONE JSON line.  --gpus N > 1 is refused: the mixer runs on one GPU here.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
+METRIC = "KDA prefill tokens/s/layer (H=64,d=128) + decode state GB/s, 1 MI355X"
+
+
+def _source_sha(name):
+    path = os.path.join(ROOT, "gated_delta_rule_short_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic_from_profile(kernel_src, fname):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when
+    the summary is absent or was taken on a different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", fname)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != _source_sha(kernel_src):
+        return None
+    return float(m_b.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "short_conv", "copy"],
+                    default="all", help="run one entry point only (for profiler passes)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: the KDA mixer is built and measured on one GPU; --gpus %d is not "
+              "supported (sharding over heads, sequences or dv columns is described in "
+              "DESIGN.md but not built)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kda_inputs as KI
+    import gated_delta_rule_short_amd as kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kda.load_library()
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- inputs (resident in HBM before the timed region)
+    P = KI.workload_inputs(1, device=dev)
+    T, H = P["q"].shape[0], P["q"].shape[1]
+    o = torch.empty_like(P["v"])
+    st_out = torch.empty((1, H, 128, 128), dtype=torch.float32, device=dev)
+    Dd = KI.workload_inputs(2, device=dev)
+    N_dec = Dd["q"].shape[0]
+    o_dec = torch.empty_like(Dd["v"])
+    X = torch.cat([P["q"].reshape(T, -1), P["k"].reshape(T, -1), P["v"].reshape(T, -1)], 1).contiguous()
+    Y = torch.empty_like(X)
+    cu1 = P["cu_seqlens"]
+    copy_src = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+
+    def run_prefill():
+        kda.kda_prefill(P["q"], P["k"], P["v"], P["gate"], P["beta"], P["conv_w"], cu_seqlens=cu1,
+                        state_out=st_out, o=o)
+
+    def run_decode():
+        kda.kda_decode(Dd["q"], Dd["k"], Dd["v"], Dd["gate"], Dd["beta"], Dd["conv_w"],
+                       Dd["conv_state"], Dd["state"], o=o_dec)
+
+    def run_conv():
+        kda.kda_short_conv(X, P["conv_w"], cu_seqlens=cu1, y=Y)
+
+    def run_copy():
+        copy_dst.copy_(copy_src)
+
+    ops = {"prefill": run_prefill, "decode": run_decode, "short_conv": run_conv, "copy": run_copy}
+    if args.only == "all":
+        names = ["short_conv", "prefill", "decode"]
+    else:
+        names = [args.only]
+
+    for _ in range(args.warmup):
+        for nm in names:
+            ops[nm]()
+    torch.cuda.synchronize()
+
+    ev = {nm: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] for nm in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for nm in names:
+            a, b = ev[nm][s]
+            a.record(stream)
+            ops[nm]()
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {nm: sum(a.elapsed_time(b) for a, b in ev[nm]) / args.steps for nm in names}
+    ms_per_step = wall * 1e3 / args.steps
+
+    if args.only != "all":
+        print(json.dumps({"only": args.only, "ms_per_launch": ms[args.only],
+                          "steps": args.steps}), flush=True)
+        return
+
+    # ---------------- derived figures
+    units = T * H                                   # token-heads per prefill launch
+    pre_bytes = units * KI.bytes_per_token_head() + H * 128 * 128 * 4   # + final state
+    pre_s = ms["prefill"] * 1e-3
+    pre_flops = units * KI.prefill_flops_per_token_head()
+    tok_per_s = T / pre_s                           # one layer = all 64 heads
+    dec_state_bytes = 2 * N_dec * H * 128 * 128 * 4  # fp32 state read + written
+    dec_other = N_dec * H * (KI.bytes_per_token_head() + 2 * 3 * 128 * 2)  # tokens + conv cache
+    dec_s = ms["decode"] * 1e-3
+    conv_bytes = 2 * X.numel() * X.element_size()
+    traffic = _traffic_from_profile("kda_prefill.hip", "prefill_bf16_T4096_H64_pmc.md")
+    dec_traffic = _traffic_from_profile("kda_decode.hip", "decode_bf16_N256_H64_pmc.md")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tok_per_s, 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, distributions of the published workloads)",
+        "config": {"workload": "prefill B=1 T=4096 H=64 d=128 chunk=64 bf16; decode N=256 H=64 "
+                               "fp32 state; short_conv T=4096 C=24576", "global_batch": 1,
+                   "seq_len": T, "heads": H, "head_dim": 128, "parallelism": "none (1 GPU)"},
+        "decode_state_GBps": round(dec_state_bytes / dec_s / 1e9, 1),
+        "per_call_us": {nm: round(ms[nm] * 1e3, 2) for nm in names},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(pre_bytes / pre_s / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(pre_bytes / pre_s / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "prefill_kernel<bf16, chunk 64, dv tile 32>",
+            "algorithmic_bytes_per_launch": pre_bytes,
+            "mfma_util": round(pre_flops / pre_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        },
+        "roofline_decode": {
+            "bound": "hbm",
+            "achieved": round((dec_state_bytes + dec_other) / dec_s / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round((dec_state_bytes + dec_other) / dec_s / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": dec_traffic,
+            "algorithmic_bytes_per_launch": dec_state_bytes + dec_other,
+        },
+        "short_conv_GBps": round(conv_bytes / (ms["short_conv"] * 1e-3) / 1e9, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle  # the CPU baseline leg: the fp64 oracle as it stands
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+        host = {k_: (v_.cpu() if torch.is_tensor(v_) else v_) for k_, v_ in P.items()}
+        t0 = time.perf_counter()
+        oracle.prefill(host["q"], host["k"], host["v"], host["gate"], host["beta"], host["conv_w"],
+                       host["cu_seqlens"], nthreads=threads)
+        cpu_s = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(T / cpu_s, 1), "unit": "tokens/s/layer",
+            "cores": min(threads, H), "kind": "oracle",
+            "sample": "the full prefill workload (1 x 4096 tokens x 64 heads), fp64 token-by-token "
+                      "oracle, OpenMP over heads; %.2f s wall" % cpu_s,
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

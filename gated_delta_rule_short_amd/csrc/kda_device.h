@@ -58,14 +58,64 @@ template <> struct Pair<__bf16> {
     }
 };
 
+// Sum over the 64 lanes of a wave; every lane receives the same value.  DPP
+// moves combine lanes inside each 16-lane row (xor 1, xor 2, half-row mirror,
+// row mirror), then the four row sums are read out as scalars.
+#define KDA_DPP(x, ctrl) \
+    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (x)), (ctrl), 0xf, 0xf, false))
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-    return x;
+    x += KDA_DPP(x, 0xb1);   // quad_perm [1,0,3,2]
+    x += KDA_DPP(x, 0x4e);   // quad_perm [2,3,0,1]
+    x += KDA_DPP(x, 0x141);  // row_half_mirror
+    x += KDA_DPP(x, 0x140);  // row_mirror
+    const int xi = __builtin_bit_cast(int, x);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48)));
 }
 
-// Logistic function on the VALU (exp is the device library's).
-__device__ __forceinline__ float sigmoidf_dev(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// 2^x on the transcendental unit (v_exp_f32); results below 2^-126 flush to 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Logistic function: 1 / (1 + e^-x) with the hardware exp and reciprocal (1 ulp each).
+__device__ __forceinline__ float sigmoidf_dev(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-1.4426950408889634f * x));
+}
+
+// Sums of 16 per-row partials over the 64 lanes of a wave.  p[r] holds this
+// lane's partial for row r.  Two butterfly steps across lane halves (xor 32,
+// then xor 16) halve the row set per lane while doubling the lanes summed; the
+// remaining 16 lanes of each row block are combined with DPP.  On return, every
+// lane of 16-lane block b holds in out[j] the full sum of row 4 b + j.
+// (The gfx950 lane-swap builtins would save the selects, but this compiler
+// folds their two results into one value when both feed an expression.)
+__device__ __forceinline__ void rows16_sum(float p[16], float out[4], int lane) {
+    const bool hi32 = lane & 32, hi16 = lane & 16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float send = hi32 ? p[j] : p[j + 8];
+        const float keep = hi32 ? p[j + 8] : p[j];
+        p[j] = keep + __shfl_xor(send, 32, kWave);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float send = hi16 ? p[j] : p[j + 4];
+        const float keep = hi16 ? p[j + 4] : p[j];
+        float x = keep + __shfl_xor(send, 16, kWave);
+        x += KDA_DPP(x, 0xb1);   // quad_perm [1,0,3,2]
+        x += KDA_DPP(x, 0x4e);   // quad_perm [2,3,0,1]
+        x += KDA_DPP(x, 0x141);  // row_half_mirror
+        x += KDA_DPP(x, 0x140);  // row_mirror
+        out[j] = x;
+    }
+}
+
+// Value of row r (0..15) from rows16_sum's layout, as a wave-uniform scalar.
+__device__ __forceinline__ float row_value(const float v[4], int r) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[r & 3]), 16 * (r >> 2)));
+}
 
 // ---------------------------------------------------------------- MFMA
 // 16x16 output tiles.  For every variant the accumulator (C/D) layout is:

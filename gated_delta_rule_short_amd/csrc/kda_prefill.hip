@@ -276,27 +276,49 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
         if (w < NB) {
             const int R = w;
             const int64_t rowbase = cbase + 16 * R;
+            // rare cases: rows before the sequence (conv state or zeros) or past its end
+            const bool edge = rowbase < 3 || rowbase + 16 > L;
             const T *qg = reinterpret_cast<const T *>(p.q) + (size_t)h * D + c0;
             const T *kg = reinterpret_cast<const T *>(p.k) + (size_t)h * D + c0;
             const T *vg = reinterpret_cast<const T *>(p.v) + (size_t)h * D + dvb + c0;
+            const T *vsrc = has_v ? vg : qg;  // lanes without v columns re-read q (unused)
             const int qch = h * D + c0, kch = H * D + h * D + c0, vch = 2 * H * D + h * D + dvb + c0;
-            const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)n * 3 * CCH
-                                   : nullptr;
-            float xq[19][2], xk[19][2], xv[19][2];
+            // raw rows rowbase-3 .. rowbase+15, clamped into the sequence: no branches,
+            // so all loads of the block are in flight together
+            float xq[19][2], xk[19][2], xv[19][2], ga[16][2];
 #pragma unroll
             for (int r = 0; r < 19; ++r) {
-                const int64_t sp = rowbase + r - 3;
-                xq[r][0] = xq[r][1] = xk[r][0] = xk[r][1] = xv[r][0] = xv[r][1] = 0.f;
-                if (sp >= 0 && sp < L) {
-                    const int64_t off = (s0 + sp) * tokstride;
-                    Pair<T>::load(qg + off, xq[r][0], xq[r][1]);
-                    Pair<T>::load(kg + off, xk[r][0], xk[r][1]);
-                    if (has_v) Pair<T>::load(vg + off, xv[r][0], xv[r][1]);
-                } else if (sp < 0 && csn) {
-                    const T *row = csn + (size_t)(3 + sp) * CCH;
-                    Pair<T>::load(row + qch, xq[r][0], xq[r][1]);
-                    Pair<T>::load(row + kch, xk[r][0], xk[r][1]);
-                    if (has_v) Pair<T>::load(row + vch, xv[r][0], xv[r][1]);
+                int64_t sp = rowbase + r - 3;
+                sp = sp < 0 ? 0 : (sp >= L ? L - 1 : sp);
+                const int64_t off = (s0 + sp) * tokstride;
+                Pair<T>::load(qg + off, xq[r][0], xq[r][1]);
+                Pair<T>::load(kg + off, xk[r][0], xk[r][1]);
+                Pair<T>::load(vsrc + off, xv[r][0], xv[r][1]);
+            }
+            const T *ag = reinterpret_cast<const T *>(p.gate) + (size_t)h * D + c0;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int64_t sp = rowbase + rr < L ? rowbase + rr : L - 1;
+                Pair<T>::load(ag + (s0 + sp) * tokstride, ga[rr][0], ga[rr][1]);
+            }
+            if (edge) {
+                const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)n * 3 * CCH
+                                       : nullptr;
+#pragma unroll
+                for (int r = 0; r < 3; ++r) {
+                    const int64_t sp = rowbase + r - 3;
+                    if (sp < 0) {
+                        float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, v0 = 0.f, v1 = 0.f;
+                        if (csn) {
+                            const T *row = csn + (size_t)(3 + sp) * CCH;
+                            Pair<T>::load(row + qch, a0, a1);
+                            Pair<T>::load(row + kch, b0, b1);
+                            if (has_v) Pair<T>::load(row + vch, v0, v1);
+                        }
+                        xq[r][0] = a0; xq[r][1] = a1;
+                        xk[r][0] = b0; xk[r][1] = b1;
+                        xv[r][0] = v0; xv[r][1] = v1;
+                    }
                 }
             }
             float wq[2][4], wk[2][4], wv[2][4], bq[2], bk[2], bv[2];
@@ -304,58 +326,100 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
             for (int e = 0; e < 2; ++e) {
                 f32x4 a = *reinterpret_cast<const f32x4 *>(p.w + 4 * (qch + e));
                 f32x4 b = *reinterpret_cast<const f32x4 *>(p.w + 4 * (kch + e));
-                f32x4 cc = has_v ? *reinterpret_cast<const f32x4 *>(p.w + 4 * (vch + e))
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 cc = *reinterpret_cast<const f32x4 *>(p.w + 4 * ((has_v ? vch : qch) + e));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) { wq[e][j] = a[j]; wk[e][j] = b[j]; wv[e][j] = cc[j]; }
                 bq[e] = p.bias ? p.bias[qch + e] : 0.f;
                 bk[e] = p.bias ? p.bias[kch + e] : 0.f;
                 bv[e] = (p.bias && has_v) ? p.bias[vch + e] : 0.f;
             }
-            const T *ag = reinterpret_cast<const T *>(p.gate) + (size_t)h * D + c0;
+            // width-4 causal conv (tap 3 = current row)
+            float yq[16][2], yk[16][2];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    yq[rr][e] = bq[e] + wq[e][0] * xq[rr][e] + wq[e][1] * xq[rr + 1][e] +
+                                wq[e][2] * xq[rr + 2][e] + wq[e][3] * xq[rr + 3][e];
+                    yk[rr][e] = bk[e] + wk[e][0] * xk[rr][e] + wk[e][1] * xk[rr + 1][e] +
+                                wk[e][2] * xk[rr + 2][e] + wk[e][3] * xk[rr + 3][e];
+                    vh[rr][e] = bv[e] + wv[e][0] * xv[rr][e] + wv[e][1] * xv[rr + 1][e] +
+                                wv[e][2] * xv[rr + 2][e] + wv[e][3] * xv[rr + 3][e];
+                }
+            if (silu) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        yq[rr][e] *= sigmoidf_dev(yq[rr][e]);
+                        yk[rr][e] *= sigmoidf_dev(yk[rr][e]);
+                        vh[rr][e] *= sigmoidf_dev(vh[rr][e]);
+                    }
+            }
+            // log2-decays of the gate
+            float g2[16][2];
+            if (glog) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) g2[rr][e] = fmaxf(ga[rr][e], p.lb) * kLog2e;
+            } else {
+                const float lb2 = p.lb * kLog2e;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) g2[rr][e] = lb2 * sigmoidf_dev(ga[rr][e]);
+            }
+            if (edge) {  // rows past the end: no input, no decay
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+                    if (rowbase + rr >= L) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            yq[rr][e] = 0.f; yk[rr][e] = 0.f; vh[rr][e] = 0.f; g2[rr][e] = 0.f;
+                        }
+                    }
+            }
+            // L2 norms of q and k: per-row sums over the 128 channels
+            float rq[16], rk[16];
+            if (l2) {
+                float pq[16], pk[16], sq4[4], sk4[4];
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    pq[rr] = yq[rr][0] * yq[rr][0] + yq[rr][1] * yq[rr][1];
+                    pk[rr] = yk[rr][0] * yk[rr][0] + yk[rr][1] * yk[rr][1];
+                }
+                rows16_sum(pq, sq4, lane);
+                rows16_sum(pk, sk4, lane);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sq4[j] = __builtin_amdgcn_rsqf(sq4[j] + 1e-6f);
+                    sk4[j] = __builtin_amdgcn_rsqf(sk4[j] + 1e-6f);
+                }
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    rq[rr] = row_value(sq4, rr);
+                    rk[rr] = row_value(sk4, rr);
+                }
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) { rq[rr] = 1.f; rk[rr] = 1.f; }
+            }
             float run[2] = {0.f, 0.f};
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const bool valid = rowbase + rr < L;
-                float yq[2], yk[2];
+            for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    float a = bq[e] + wq[e][0] * xq[rr][e] + wq[e][1] * xq[rr + 1][e] +
-                              wq[e][2] * xq[rr + 2][e] + wq[e][3] * xq[rr + 3][e];
-                    float b = bk[e] + wk[e][0] * xk[rr][e] + wk[e][1] * xk[rr + 1][e] +
-                              wk[e][2] * xk[rr + 2][e] + wk[e][3] * xk[rr + 3][e];
-                    float cv = bv[e] + wv[e][0] * xv[rr][e] + wv[e][1] * xv[rr + 1][e] +
-                               wv[e][2] * xv[rr + 2][e] + wv[e][3] * xv[rr + 3][e];
-                    if (silu) {
-                        a = a * sigmoidf_dev(a);
-                        b = b * sigmoidf_dev(b);
-                        cv = cv * sigmoidf_dev(cv);
-                    }
-                    yq[e] = valid ? a : 0.f;
-                    yk[e] = valid ? b : 0.f;
-                    vh[rr][e] = (valid && has_v) ? cv : 0.f;
-                }
-                const float sq = wave_sum(yq[0] * yq[0] + yq[1] * yq[1]);
-                const float sk = wave_sum(yk[0] * yk[0] + yk[1] * yk[1]);
-                const float iq = l2 ? rsqrtf(sq + 1e-6f) : 1.f;
-                const float ik = l2 ? rsqrtf(sk + 1e-6f) : 1.f;
-                float ga = 0.f, gb = 0.f;
-                if (valid) Pair<T>::load(ag + (s0 + rowbase + rr) * tokstride, ga, gb);
-                const float gg[2] = {ga, gb};
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    qh[rr][e] = yq[e] * iq;
-                    kh[rr][e] = yk[e] * ik;
-                    const float g = glog ? fmaxf(gg[e], p.lb) : p.lb * sigmoidf_dev(gg[e]);
-                    run[e] += valid ? g * kLog2e : 0.f;
+                    qh[rr][e] = yq[rr][e] * rq[rr];
+                    kh[rr][e] = yk[rr][e] * rk[rr];
+                    run[e] += g2[rr][e];
                     bl[rr][e] = run[e];
                 }
-            }
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 Gw[e] = run[e];
                 sG2[R * 128 + c0 + e] = run[e];
-                sFD[R * 128 + c0 + e] = exp2f(-run[e]);
+                sFD[R * 128 + c0 + e] = exp2_fast(-run[e]);
             }
             if (lane < 16) {
                 const int64_t sp = rowbase + lane;
@@ -380,8 +444,8 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
             float eB[2], eD[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                eB[e] = exp2f(B2R[e]);
-                eD[e] = exp2f(Bt[e] - B2R[e] - Gw[e]);
+                eB[e] = exp2_fast(B2R[e]);
+                eD[e] = exp2_fast(Bt[e] - B2R[e] - Gw[e]);
             }
             float kgt[2][16], kdt[2][16], vtt[2][16];
 #pragma unroll
@@ -391,8 +455,8 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
                 float kl[2], ql[2], kr[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const float eL = exp2f(bl[rr][e]);
-                    const float eR = exp2f(Gw[e] - bl[rr][e]);
+                    const float eL = exp2_fast(bl[rr][e]);
+                    const float eR = exp2_fast(Gw[e] - bl[rr][e]);
                     kl[e] = kh[rr][e] * eL;
                     ql[e] = qh[rr][e] * eL;
                     kr[e] = kh[rr][e] * eR;
@@ -421,7 +485,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
             if (R == 0) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    sGAM[c0 + e] = exp2f(Bt[e]);
+                    sGAM[c0 + e] = exp2_fast(Bt[e]);
 #pragma unroll
                     for (int Ri = 2; Ri < NB; ++Ri)
 #pragma unroll
@@ -429,7 +493,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
                             float between = 0.f;
 #pragma unroll
                             for (int Rp = Si + 1; Rp < Ri; ++Rp) between += sG2[Rp * 128 + c0 + e];
-                            sFO[fo_index(Ri, Si) * 128 + c0 + e] = exp2f(between);
+                            sFO[fo_index(Ri, Si) * 128 + c0 + e] = exp2_fast(between);
                         }
                 }
             }
