@@ -85,6 +85,7 @@ def main():
     T, H = P["q"].shape[0], P["q"].shape[1]
     o = torch.empty_like(P["v"])
     st_out = torch.empty((1, H, 128, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.prefill_workspace_bytes(T, H, 1), dtype=torch.uint8, device=dev)
     Dd = KI.workload_inputs(2, device=dev)
     N_dec = Dd["q"].shape[0]
     o_dec = torch.empty_like(Dd["v"])
@@ -96,7 +97,7 @@ def main():
 
     def run_prefill():
         kda.kda_prefill(P["q"], P["k"], P["v"], P["gate"], P["beta"], P["conv_w"], cu_seqlens=cu1,
-                        state_out=st_out, o=o)
+                        state_out=st_out, o=o, workspace=ws)
 
     def run_decode():
         kda.kda_decode(Dd["q"], Dd["k"], Dd["v"], Dd["gate"], Dd["beta"], Dd["conv_w"],

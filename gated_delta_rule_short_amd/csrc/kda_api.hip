@@ -133,6 +133,12 @@ kda_status kda_short_conv(const void *x, void *y, int64_t total_tokens, int32_t 
     return KDA_OK;
 }
 
+size_t kda_prefill_workspace_size(const kda_prefill_args *a) {
+    if (!a || a->dtype != KDA_BF16 || (a->chunk_size != 0 && a->chunk_size != 16)) return 0;
+    if (a->num_seqs < 1 || a->num_heads < 1 || a->total_tokens < 0) return 0;
+    return kda::split_workspace_bytes(a->total_tokens, a->num_seqs, a->num_heads);
+}
+
 kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
     g_err[0] = 0;
     if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
@@ -174,14 +180,29 @@ kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
 
     kda_prefill_args args = *a;
     if (args.scale == 0.f) args.scale = 1.0f / std::sqrt(128.0f);
+    const int64_t pairs = (int64_t)a->num_seqs * H;
+    const size_t need = kda_prefill_workspace_size(a);
+    const bool two_pass = need > 0 && a->workspace && a->workspace_bytes >= need;
+    if (two_pass) {
+        const size_t wb = a->workspace_bytes;
+        if (overlap(a->workspace, wb, a->o, tok) || overlap(a->workspace, wb, a->state_out, sb))
+            return fail(KDA_ERR_INVALID_ARG, "workspace overlaps an output");
+        for (const void *in : ins)
+            if (overlap(a->workspace, wb, in, tok))
+                return fail(KDA_ERR_INVALID_ARG, "workspace overlaps an input");
+    }
     // dv tile per workgroup: enough workgroups for 256 compute units.  The tile
     // changes only which workgroup computes a column, not the arithmetic.
-    const int64_t pairs = (int64_t)a->num_seqs * H;
     int dv_tile = pairs >= 256 ? 128 : (pairs >= 128 ? 64 : 32);
     const int forced = env_int("KDA_PREFILL_DV_TILE", 0);
-    if (forced == 32 || forced == 64 || forced == 128) dv_tile = forced;
-    kda::PrefillLaunch pl{&args, chunk, dv_tile};
-    hipError_t e = kda::launch_prefill(pl, stream);
+    if (forced == 32 || forced == 64 || forced == 128 || (two_pass && forced == 16)) dv_tile = forced;
+    hipError_t e;
+    if (two_pass) {
+        e = kda::launch_prefill_split(&args, dv_tile, stream);
+    } else {
+        kda::PrefillLaunch pl{&args, chunk, dv_tile};
+        e = kda::launch_prefill(pl, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     if (a->conv_state_out) {
         const void *src[3] = {a->q, a->k, a->v};

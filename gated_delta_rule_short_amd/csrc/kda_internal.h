@@ -30,4 +30,8 @@ hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t s);
 
 hipError_t launch_decode(const kda_decode_args *a, hipStream_t s);
 
+// Two-pass prefill (bf16 I/O, 16-token sub-chunks) and its workspace size.
+size_t split_workspace_bytes(int64_t total_tokens, int num_seqs, int H);
+hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStream_t s);
+
 }  // namespace kda

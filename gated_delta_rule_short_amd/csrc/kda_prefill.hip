@@ -49,6 +49,7 @@
 
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_mma.h"
 
 namespace kda {
 
@@ -92,103 +93,36 @@ template <typename E, int NB, int DVW> struct Layout {
     static constexpr size_t FO = FD + (size_t)NB * 128 * 4;
     static constexpr size_t GAM = FO + (size_t)NFO * 128 * 4;
     static constexpr size_t BET = GAM + 128 * 4;
-    static constexpr size_t TOTAL = BET + (size_t)C * 4;
+    static constexpr int HS = 256 + DVW;  // halo row: q (128), k (128), v (DVW)
+    static constexpr size_t HALO = BET + (((size_t)C * 4 + 15) & ~(size_t)15);
+    static constexpr size_t TOTAL = HALO + (size_t)2 * 3 * HS * sizeof(E);
+    // raw rows of the next chunk, staged by DMA into slots that are dead by then
+    static constexpr size_t RQ = QL, RK = KR, RG = KGT, RV = VT, RB = ND;
+    static_assert((size_t)C * SRM >= (size_t)C * 128 && (size_t)128 * STR >= (size_t)C * 128,
+                  "staging fits");
 };
 
-// Operand helpers per staged element type.
-template <typename E> struct Ops;
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <> struct Ops<__bf16> {
-    typedef bf16x4 B4;  // one 16-row K block of a B operand, this lane's 4 elements
-    static __device__ __forceinline__ B4 pack(f32x4 v) { return pack4(v); }
-    static __device__ __forceinline__ f32x4 load4(const __bf16 *p) {
-        bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
-        f32x4 r = {(float)v.x, (float)v.y, (float)v.z, (float)v.w};
-        return r;
-    }
-    static __device__ __forceinline__ void store4(__bf16 *p, float a, float b, float c, float d) {
-        bf16x4 v;
-        v.x = (__bf16)a; v.y = (__bf16)b; v.z = (__bf16)c; v.w = (__bf16)d;
-        *reinterpret_cast<bf16x4 *>(p) = v;
-    }
-    // acc += sum_{kb < kb1} sum_i arow[16 kb + i] * B[kb][i], kb1 <= MAXKB; arow points
-    // at A[row0 + lane%16][col0 + 4 (lane/16)].  kb1 folds to a constant once the
-    // caller's loops are unrolled, so B stays in registers.
-    template <int MAXKB>
-    static __device__ __forceinline__ f32x4 chain(f32x4 acc, const __bf16 *arow, const B4 *B,
-                                                  int kb1) {
+// DMA of BYTES bytes (a multiple of 1 KiB) of row-gathered global data into
+// contiguous LDS: 16-byte piece i comes from row (16 i) / ROW_BYTES of the
+// source, byte (16 i) % ROW_BYTES.  Rows past `last_row` repeat it.  Each wave
+// moves every fourth KiB; completion is tracked by vmcnt.
+template <int ROW_BYTES, int BYTES>
+__device__ __forceinline__ void dma_rows(unsigned char *lds_dst, const unsigned char *gbase,
+                                         int64_t row_stride, int64_t first_row, int64_t last_row,
+                                         int w, int lane) {
+    static_assert(BYTES % 1024 == 0 && ROW_BYTES % 16 == 0, "DMA granularity");
 #pragma unroll
-        for (int kb = 0; kb < MAXKB; kb += 2) {
-            if (kb + 1 < kb1) {
-                bf16x4 a0 = *reinterpret_cast<const bf16x4 *>(arow + 16 * kb);
-                bf16x4 a1 = *reinterpret_cast<const bf16x4 *>(arow + 16 * kb + 16);
-                acc = mma_k32(join8(a0, a1), join8(B[kb], B[kb + 1]), acc);
-            } else if (kb < kb1) {
-                acc = mma_k16(*reinterpret_cast<const bf16x4 *>(arow + 16 * kb), B[kb], acc);
-            }
-        }
-        return acc;
+    for (int inst = w; inst < BYTES / 1024; inst += 4) {
+        const int piece = inst * 64 + lane;
+        const int row = (piece * 16) / ROW_BYTES, col = (piece * 16) % ROW_BYTES;
+        int64_t gr = first_row + row;
+        gr = gr > last_row ? last_row : gr;
+        __builtin_amdgcn_global_load_lds(gbase + gr * row_stride + col,
+                                         (lds_void *)(lds_dst + inst * 1024), 16, 0, 0);
     }
-    // 16x16 Gram over 128 channels: lrow/rrow point at the rows of this lane's
-    // A row / B column; f (nullable) scales the right operand per channel.
-    static __device__ __forceinline__ f32x4 gram(const __bf16 *lrow, const __bf16 *rrow,
-                                                 const float *f, int g4) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int k0 = 32 * t + 8 * g4;
-            bf16x8 a = join8(*reinterpret_cast<const bf16x4 *>(lrow + k0),
-                             *reinterpret_cast<const bf16x4 *>(lrow + k0 + 4));
-            bf16x4 b0 = *reinterpret_cast<const bf16x4 *>(rrow + k0);
-            bf16x4 b1 = *reinterpret_cast<const bf16x4 *>(rrow + k0 + 4);
-            if (f) {
-                f32x4 f0 = *reinterpret_cast<const f32x4 *>(f + k0);
-                f32x4 f1 = *reinterpret_cast<const f32x4 *>(f + k0 + 4);
-                f32x4 x0 = {(float)b0.x, (float)b0.y, (float)b0.z, (float)b0.w};
-                f32x4 x1 = {(float)b1.x, (float)b1.y, (float)b1.z, (float)b1.w};
-                b0 = pack4(x0 * f0);
-                b1 = pack4(x1 * f1);
-            }
-            acc = mma_k32(a, join8(b0, b1), acc);
-        }
-        return acc;
-    }
-};
-
-template <> struct Ops<float> {
-    typedef f32x4 B4;
-    static __device__ __forceinline__ B4 pack(f32x4 v) { return v; }
-    static __device__ __forceinline__ f32x4 load4(const float *p) {
-        return *reinterpret_cast<const f32x4 *>(p);
-    }
-    static __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
-        f32x4 v = {a, b, c, d};
-        *reinterpret_cast<f32x4 *>(p) = v;
-    }
-    template <int MAXKB>
-    static __device__ __forceinline__ f32x4 chain(f32x4 acc, const float *arow, const B4 *B,
-                                                  int kb1) {
-#pragma unroll
-        for (int kb = 0; kb < MAXKB; ++kb) {
-            if (kb < kb1) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mma_f32(arow[16 * kb + i], B[kb][i], acc);
-            }
-        }
-        return acc;
-    }
-    static __device__ __forceinline__ f32x4 gram(const float *lrow, const float *rrow,
-                                                 const float *f, int g4) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 32; ++t) {
-            const int k = 4 * t + g4;
-            const float b = f ? rrow[k] * f[k] : rrow[k];
-            acc = mma_f32(lrow[k], b, acc);
-        }
-        return acc;
-    }
-};
+}
 
 // Index of the off-diagonal block pair (R, S), R >= S + 2, in the factor table.
 __device__ __forceinline__ constexpr int fo_index(int R, int S) { return (R - 2) * (R - 1) / 2 + S; }
@@ -204,7 +138,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
     constexpr int NTWG = DVW / 16;                // dv n-tiles per workgroup
     constexpr int WST = NTWG < 4 ? NTWG : 4;      // waves owning state columns
     constexpr int NTW = NTWG / WST;               // dv n-tiles per state wave
-    constexpr int SRM = LY::SRM, STR = LY::STR, SCC = LY::SCC, SXD = LY::SXD;
+    constexpr int SRM = LY::SRM, STR = LY::STR, SCC = LY::SCC, SXD = LY::SXD, HS = LY::HS;
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     E *sKL = reinterpret_cast<E *>(smem + LY::KL);  // also W (negated) after the Grams
@@ -217,12 +151,18 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
     E *sLN = reinterpret_cast<E *>(smem + LY::LN);
     E *sPM = reinterpret_cast<E *>(smem + LY::PM);
     E *sXD = reinterpret_cast<E *>(smem + LY::XD);
-    float *sND = reinterpret_cast<float *>(smem + LY::ND);
+    float *sNDT = reinterpret_cast<float *>(smem + LY::ND);  // diagonal blocks, transposed
     float *sG2 = reinterpret_cast<float *>(smem + LY::G2);
     float *sFD = reinterpret_cast<float *>(smem + LY::FD);
     float *sFO = reinterpret_cast<float *>(smem + LY::FO);
     float *sGAM = reinterpret_cast<float *>(smem + LY::GAM);
     float *sBET = reinterpret_cast<float *>(smem + LY::BET);
+    E *sHALO = reinterpret_cast<E *>(smem + LY::HALO);
+    const T *sRQ = reinterpret_cast<const T *>(smem + LY::RQ);
+    const T *sRK = reinterpret_cast<const T *>(smem + LY::RK);
+    const T *sRG = reinterpret_cast<const T *>(smem + LY::RG);
+    const T *sRV = reinterpret_cast<const T *>(smem + LY::RV);
+    float *sRB = reinterpret_cast<float *>(smem + LY::RB);
     E *sWN = sKL;
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -246,6 +186,29 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
     const bool glog = p.flags & KDA_F_GATE_IS_LOG;
     const int CCH = 3 * H * D;
 
+    // raw rows of chunk c -> LDS: q, k first (their slots die after the Grams),
+    // gate, v and beta later (their slots die after the triangular solve)
+    const unsigned char *gq = reinterpret_cast<const unsigned char *>(reinterpret_cast<const T *>(p.q) + (size_t)h * D);
+    const unsigned char *gk = reinterpret_cast<const unsigned char *>(reinterpret_cast<const T *>(p.k) + (size_t)h * D);
+    const unsigned char *gg = reinterpret_cast<const unsigned char *>(reinterpret_cast<const T *>(p.gate) + (size_t)h * D);
+    const unsigned char *gv = reinterpret_cast<const unsigned char *>(reinterpret_cast<const T *>(p.v) + (size_t)h * D + dvb);
+    const int64_t rstride = tokstride * (int64_t)sizeof(T);
+    auto stage_qk = [&](int64_t c) {
+        dma_rows<128 * sizeof(T), C * 128 * sizeof(T)>(smem + LY::RQ, gq, rstride, s0 + c * C, s0 + L - 1, w, lane);
+        dma_rows<128 * sizeof(T), C * 128 * sizeof(T)>(smem + LY::RK, gk, rstride, s0 + c * C, s0 + L - 1, w, lane);
+    };
+    auto stage_rest = [&](int64_t c) {
+        dma_rows<128 * sizeof(T), C * 128 * sizeof(T)>(smem + LY::RG, gg, rstride, s0 + c * C, s0 + L - 1, w, lane);
+        dma_rows<DVW * sizeof(T), C * DVW * sizeof(T)>(smem + LY::RV, gv, rstride, s0 + c * C, s0 + L - 1, w, lane);
+    };
+    // beta of chunk c: one element per lane of wave 0, loaded early and parked in
+    // LDS at the chunk boundary
+    auto load_beta = [&](int64_t c) -> float {
+        int64_t t = s0 + c * C + lane;
+        t = t > s0 + L - 1 ? s0 + L - 1 : t;
+        return to_f32(reinterpret_cast<const T *>(p.beta)[t * H + h]);
+    };
+
     // fp32 state slice in accumulator layout: tile mt covers dk rows 16 mt..,
     // tile j the dv columns dvb + 16 (w NTW + j)..
     f32x4 S[8][NTW];
@@ -262,76 +225,79 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
             }
         }
 
+    float beta_next = 0.f;
+    if (L > 0) {
+        stage_qk(0);
+        stage_rest(0);
+        if (w == 0 && lane < C) beta_next = load_beta(0);
+    }
     // the strictly upper blocks of P are never written: zero them once
     for (int idx = tid; idx < C * SCC; idx += 256) sPM[idx] = from_f32<E>(0.f);
+    // halo of the first chunk: the three raw rows before the sequence (conv state or zeros)
+    {
+        const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)n * 3 * CCH : nullptr;
+        E *hslot = sHALO + 1 * 3 * HS;  // read as the "previous" slot by chunk 0
+        for (int idx = tid; idx < 3 * HS; idx += 256) {
+            const int r = idx / HS, c = idx - r * HS;
+            const int ch = c < 128 ? h * D + c : (c < 256 ? H * D + h * D + (c - 128)
+                                                          : 2 * H * D + h * D + dvb + (c - 256));
+            hslot[idx] = csn ? csn[(size_t)r * CCH + ch] : from_f32<E>(0.f);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (w == 0 && lane < C) sRB[lane] = beta_next;
     __syncthreads();
 
     const int64_t nchunks = (L + C - 1) / C;
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t cbase = c * C;
         // ------------------------------------------------ phase 1: prologue
-        float qh[16][2], kh[16][2], bl[16][2], vh[16][2], Gw[2] = {0.f, 0.f};
+        float kl[16][2], ql[16][2], kr[16][2], vh[16][2], Gw[2] = {0.f, 0.f};
         const int c0 = 2 * lane;
         const bool has_v = c0 < DVW;
         if (w < NB) {
             const int R = w;
             const int64_t rowbase = cbase + 16 * R;
-            // rare cases: rows before the sequence (conv state or zeros) or past its end
-            const bool edge = rowbase < 3 || rowbase + 16 > L;
-            const T *qg = reinterpret_cast<const T *>(p.q) + (size_t)h * D + c0;
-            const T *kg = reinterpret_cast<const T *>(p.k) + (size_t)h * D + c0;
-            const T *vg = reinterpret_cast<const T *>(p.v) + (size_t)h * D + dvb + c0;
-            const T *vsrc = has_v ? vg : qg;  // lanes without v columns re-read q (unused)
-            const int qch = h * D + c0, kch = H * D + h * D + c0, vch = 2 * H * D + h * D + dvb + c0;
-            // raw rows rowbase-3 .. rowbase+15, clamped into the sequence: no branches,
-            // so all loads of the block are in flight together
+            const bool tail = rowbase + 16 > L;  // rows past the end in this block
+            const E *hprev = sHALO + (int)((c + 1) & 1) * 3 * HS;
+            const int vc = has_v ? c0 : 0;
+            // raw rows 16R-3 .. 16R+15 of the chunk (the first three of block 0
+            // come from the previous chunk or the conv state)
             float xq[19][2], xk[19][2], xv[19][2], ga[16][2];
 #pragma unroll
             for (int r = 0; r < 19; ++r) {
-                int64_t sp = rowbase + r - 3;
-                sp = sp < 0 ? 0 : (sp >= L ? L - 1 : sp);
-                const int64_t off = (s0 + sp) * tokstride;
-                Pair<T>::load(qg + off, xq[r][0], xq[r][1]);
-                Pair<T>::load(kg + off, xk[r][0], xk[r][1]);
-                Pair<T>::load(vsrc + off, xv[r][0], xv[r][1]);
+                const int cr = 16 * R + r - 3;
+                const T *rq = cr >= 0 ? sRQ + cr * 128 : hprev + (3 + cr) * HS;
+                const T *rk = cr >= 0 ? sRK + cr * 128 : hprev + (3 + cr) * HS + 128;
+                const T *rv = cr >= 0 ? sRV + cr * DVW : hprev + (3 + cr) * HS + 256;
+                Pair<T>::load(rq + c0, xq[r][0], xq[r][1]);
+                Pair<T>::load(rk + c0, xk[r][0], xk[r][1]);
+                Pair<T>::load(rv + vc, xv[r][0], xv[r][1]);
             }
-            const T *ag = reinterpret_cast<const T *>(p.gate) + (size_t)h * D + c0;
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int64_t sp = rowbase + rr < L ? rowbase + rr : L - 1;
-                Pair<T>::load(ag + (s0 + sp) * tokstride, ga[rr][0], ga[rr][1]);
-            }
-            if (edge) {
-                const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)n * 3 * CCH
-                                       : nullptr;
+            for (int rr = 0; rr < 16; ++rr) Pair<T>::load(sRG + (16 * R + rr) * 128 + c0, ga[rr][0], ga[rr][1]);
+            if (R == NB - 1) {  // keep the last three raw rows as the next chunk's halo
+                E *hnext = sHALO + (int)(c & 1) * 3 * HS;
 #pragma unroll
                 for (int r = 0; r < 3; ++r) {
-                    const int64_t sp = rowbase + r - 3;
-                    if (sp < 0) {
-                        float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, v0 = 0.f, v1 = 0.f;
-                        if (csn) {
-                            const T *row = csn + (size_t)(3 + sp) * CCH;
-                            Pair<T>::load(row + qch, a0, a1);
-                            Pair<T>::load(row + kch, b0, b1);
-                            if (has_v) Pair<T>::load(row + vch, v0, v1);
-                        }
-                        xq[r][0] = a0; xq[r][1] = a1;
-                        xk[r][0] = b0; xk[r][1] = b1;
-                        xv[r][0] = v0; xv[r][1] = v1;
-                    }
+                    Pair<E>::store(hnext + r * HS + c0, xq[16 + r][0], xq[16 + r][1]);
+                    Pair<E>::store(hnext + r * HS + 128 + c0, xk[16 + r][0], xk[16 + r][1]);
+                    if (has_v) Pair<E>::store(hnext + r * HS + 256 + c0, xv[16 + r][0], xv[16 + r][1]);
                 }
             }
+            if (lane < 16) sBET[16 * R + lane] = rowbase + lane < L ? sRB[16 * R + lane] : 0.f;
+            const int qch = h * D + c0, kch = H * D + h * D + c0, vch = 2 * H * D + h * D + dvb + vc;
             float wq[2][4], wk[2][4], wv[2][4], bq[2], bk[2], bv[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 f32x4 a = *reinterpret_cast<const f32x4 *>(p.w + 4 * (qch + e));
                 f32x4 b = *reinterpret_cast<const f32x4 *>(p.w + 4 * (kch + e));
-                f32x4 cc = *reinterpret_cast<const f32x4 *>(p.w + 4 * ((has_v ? vch : qch) + e));
+                f32x4 cc = *reinterpret_cast<const f32x4 *>(p.w + 4 * (vch + e));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) { wq[e][j] = a[j]; wk[e][j] = b[j]; wv[e][j] = cc[j]; }
                 bq[e] = p.bias ? p.bias[qch + e] : 0.f;
                 bk[e] = p.bias ? p.bias[kch + e] : 0.f;
-                bv[e] = (p.bias && has_v) ? p.bias[vch + e] : 0.f;
+                bv[e] = p.bias ? p.bias[vch + e] : 0.f;
             }
             // width-4 causal conv (tap 3 = current row)
             float yq[16][2], yk[16][2];
@@ -370,7 +336,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
 #pragma unroll
                     for (int e = 0; e < 2; ++e) g2[rr][e] = lb2 * sigmoidf_dev(ga[rr][e]);
             }
-            if (edge) {  // rows past the end: no input, no decay
+            if (tail) {  // rows past the end: no input, no decay
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr)
                     if (rowbase + rr >= L) {
@@ -405,26 +371,30 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) { rq[rr] = 1.f; rk[rr] = 1.f; }
             }
-            float run[2] = {0.f, 0.f};
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    qh[rr][e] = yq[rr][e] * rq[rr];
-                    kh[rr][e] = yk[rr][e] * rk[rr];
-                    run[e] += g2[rr][e];
-                    bl[rr][e] = run[e];
-                }
+            // decays inside the block as running products of alpha = 2^g2:
+            // eL_r = prod_{t<=r} alpha_t (<= 1), eR_r = prod_{t>r} alpha_t (<= 1)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                Gw[e] = run[e];
-                sG2[R * 128 + c0 + e] = run[e];
-                sFD[R * 128 + c0 + e] = exp2_fast(-run[e]);
-            }
-            if (lane < 16) {
-                const int64_t sp = rowbase + lane;
-                sBET[16 * R + lane] =
-                    sp < L ? to_f32(reinterpret_cast<const T *>(p.beta)[(s0 + sp) * H + h]) : 0.f;
+                float al[16], run = 1.f, gsum = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    al[rr] = exp2_fast(g2[rr][e]);
+                    gsum += g2[rr][e];
+                    run *= al[rr];
+                    const float qn = yq[rr][e] * rq[rr], kn = yk[rr][e] * rk[rr];
+                    ql[rr][e] = qn * run;
+                    kl[rr][e] = kn * run;
+                    kr[rr][e] = kn;  // times eR below
+                }
+                float back = 1.f;
+#pragma unroll
+                for (int rr = 15; rr >= 0; --rr) {
+                    kr[rr][e] *= back;
+                    back *= al[rr];
+                }
+                Gw[e] = gsum;
+                sG2[R * 128 + c0 + e] = gsum;
+                sFD[R * 128 + c0 + e] = exp2_fast(-gsum);
             }
         }
         __syncthreads();
@@ -452,22 +422,16 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
             for (int rr = 0; rr < 16; ++rr) {
                 const int row = 16 * R + rr;
                 const float bt = sBET[row];
-                float kl[2], ql[2], kr[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const float eL = exp2_fast(bl[rr][e]);
-                    const float eR = exp2_fast(Gw[e] - bl[rr][e]);
-                    kl[e] = kh[rr][e] * eL;
-                    ql[e] = qh[rr][e] * eL;
-                    kr[e] = kh[rr][e] * eR;
-                    kgt[e][rr] = bt * kl[e] * eB[e];
-                    kdt[e][rr] = kr[e] * eD[e];
+                    kgt[e][rr] = bt * kl[rr][e] * eB[e];
+                    kdt[e][rr] = kr[rr][e] * eD[e];
                     vtt[e][rr] = bt * vh[rr][e];
                 }
-                Pair<E>::store(sKL + row * SRM + c0, kl[0], kl[1]);
-                Pair<E>::store(sQL + row * SRM + c0, ql[0], ql[1]);
-                Pair<E>::store(sKR + row * SRM + c0, kr[0], kr[1]);
-                Pair<E>::store(sQG + row * SRM + c0, ql[0] * eB[0], ql[1] * eB[1]);
+                Pair<E>::store(sKL + row * SRM + c0, kl[rr][0], kl[rr][1]);
+                Pair<E>::store(sQL + row * SRM + c0, ql[rr][0], ql[rr][1]);
+                Pair<E>::store(sKR + row * SRM + c0, kr[rr][0], kr[rr][1]);
+                Pair<E>::store(sQG + row * SRM + c0, ql[rr][0] * eB[0], ql[rr][1] * eB[1]);
             }
 #pragma unroll
             for (int e = 0; e < 2; ++e)
@@ -514,7 +478,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
                 if (kind == 0) {
                     if (R == Sb && sl >= rl) val = 0.f;
                     val *= sBET[16 * R + rl];
-                    if (R == Sb) sND[R * 256 + rl * 16 + sl] = val;
+                    if (R == Sb) sNDT[R * 256 + sl * 16 + rl] = val;
                     else sLN[(16 * R + rl) * SCC + 16 * Sb + sl] = from_f32<E>(-val);
                 } else {
                     if (R == Sb && sl > rl) val = 0.f;
@@ -528,15 +492,18 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (lane < 16) {
-                // column `lane` of (I + N)^-1 with N the strictly lower diagonal block
-                const float *Nd = sND + w * 256;
+                // column `lane` of (I + N)^-1, N the strictly lower diagonal block
+                // (stored transposed): right-looking, so each step's updates are
+                // independent of one another
+                const float *Nt = sNDT + w * 256;
                 float x[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float acc = (i == lane) ? 1.f : 0.f;
+                for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
 #pragma unroll
-                    for (int s = 0; s < i; ++s) acc -= Nd[i * 16 + s] * x[s];
-                    x[i] = acc;
+                for (int s = 0; s < 15; ++s) {
+                    const float xs = x[s];
+#pragma unroll
+                    for (int i = s + 1; i < 16; ++i) x[i] -= Nt[s * 16 + i] * xs;
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sXD[(w * 16 + i) * SXD + lane] = from_f32<E>(x[i]);
@@ -553,6 +520,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
             }
         }
         __syncthreads();
+        if (c + 1 < nchunks) stage_qk(c + 1);  // q, k slots are free from here on
 
         // ----------------------- phase 3: W and U0 by block forward substitution
         f32x4 U0[NB][NTW];
@@ -581,7 +549,6 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
                     for (int j = 0; j < NTW; ++j) {
                         const int col = 16 * (w * NTW + j) + m16;
                         f32x4 rhs = OP::load4(sVT + col * STR + 16 * R + 4 * g4);
-                        // U0 blocks of earlier R are re-packed (cheap; keeps registers flat)
 #pragma unroll
                         for (int Rp = 0; Rp < R; ++Rp) Ub[j][Rp] = OP::pack(U0[Rp][j]);
                         rhs = OP::template chain<NB>(rhs, lnrow, Ub[j], R);
@@ -593,6 +560,10 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
             }
         }
         __syncthreads();
+        if (c + 1 < nchunks) {  // gate, v, beta slots are free from here on
+            stage_rest(c + 1);
+            if (w == 0 && lane < C) beta_next = load_beta(c + 1);
+        }
 
         // ----------------------------------------- phase 4: state path (per wave)
         if (st_wave) {
@@ -609,6 +580,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
                 for (int j = 0; j < NTW; ++j)
                     Ub[j][R] = OP::pack(OP::template chain<8>(U0[R][j], wrow, Sb[j], 8));
             }
+            const bool full = cbase + C <= L;
 #pragma unroll
             for (int R = 0; R < NB; ++R) {
                 const E *qrow = sQG + (16 * R + m16) * SRM + 4 * g4;
@@ -619,11 +591,16 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
                     acc = OP::template chain<8>(acc, qrow, Sb[j], 8);
                     acc = OP::template chain<NB>(acc, prow, Ub[j], NB);
                     const int col = dvb + 16 * (w * NTW + j) + m16;
-                    T *op = reinterpret_cast<T *>(p.o) + (size_t)h * D + col;
+                    T *op = reinterpret_cast<T *>(p.o) + (size_t)(s0 + cbase + 16 * R + 4 * g4) * tokstride +
+                            (size_t)h * D + col;
+                    if (full) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t sp = cbase + 16 * R + 4 * g4 + i;
-                        if (sp < L) op[(s0 + sp) * tokstride] = from_f32<T>(p.scale * acc[i]);
+                        for (int i = 0; i < 4; ++i) op[i * tokstride] = from_f32<T>(p.scale * acc[i]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (cbase + 16 * R + 4 * g4 + i < L)
+                                op[i * tokstride] = from_f32<T>(p.scale * acc[i]);
                     }
                 }
             }
@@ -636,6 +613,8 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
                     S[mt][j] = OP::template chain<NB>(S[mt][j] * gam, krow, Ub[j], NB);
             }
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // next chunk's staged rows
+        if (c + 1 < nchunks && w == 0 && lane < C) sRB[lane] = beta_next;
         __syncthreads();
     }
 

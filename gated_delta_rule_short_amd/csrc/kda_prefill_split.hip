@@ -1,0 +1,517 @@
+// kda_prefill_split.hip -- two-pass KDA prefill with 16-token sub-chunks.
+//
+// Source: "GLM-5.3-Flash im Detail" (flozi.net), section "Sequenz-Mixing":
+// in prefill the tokens inside chunks are evaluated in parallel while a state
+// is handed from chunk to chunk.  Per head: width-4 causal conv of q, k, v,
+// channel-wise forget gate (log-decay >= -5), scalar-beta delta-rule write into
+// a 128 x 128 fp32 state, query read of the updated state.
+//
+// Pass A (intra_kernel) is parallel over (head, 64-token block): each wave takes
+// one 16-token sub-chunk of one sequence and computes, relative to the state on
+// entry to the sub-chunk,
+//     A = strict_lower(K~ K^T . decay),  P = lower(Q~ K^T . decay),
+//     X = (I + diag(beta) A)^-1,  W = X diag(beta) (K . 2^b),
+// with b the log2-decay cumsum from the sub-chunk start (>= -115.4, so every
+// factor is a finite fp32/bf16 number), and writes them as matrix-core
+// fragments to a workspace record.  Pass B (scan_kernel) runs one workgroup per
+// (sequence, head, dv tile) over its sub-chunks in order:
+//     U = X diag(beta) V - W S,  O = scale ((Q . 2^b) S + P U),
+//     S = diag(2^b_last) S + (K . 2^(b_last - b))^T U.
+// Pass A does the conv / L2 / gate work once per token and head, over the
+// whole GPU; pass B keeps the fp32 state in registers (accumulator layout) for
+// the whole sequence.  The workspace costs extra HBM traffic (one 17.5 KiB
+// record per sub-chunk and head, written once and read once), which pays off
+// when there are too few (sequence, head) pairs to fill the GPU otherwise.
+#include <mutex>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_mma.h"
+
+namespace kda {
+
+namespace {
+
+constexpr float kLog2eS = 1.4426950408889634f;
+
+// Workspace record of one (head, sub-chunk), byte offsets; bf16 unless noted.
+//   WN  [4][64][8]  -W, A-operand fragments (rows tokens, K = dk, permuted pairs)
+//   QG  [4][64][8]  Q . 2^b, same fragment layout
+//   KD  [8][64][4]  (K . 2^(b_last - b))^T, A-operand fragments (rows dk, K = tokens)
+//   BV  [8][64][4]  beta . V, accumulator layout (rows tokens, columns dv)
+//   PP  [64][4]     P, A-operand fragment (rows tokens, K = tokens)
+//   XX  [64][4]     X, same
+//   GAM [128] fp32  2^b_last per dk channel
+constexpr int R_WN = 0, R_QG = 4096, R_KD = 8192, R_BV = 12288, R_PP = 16384, R_XX = 16896,
+              R_GAM = 17408;
+constexpr size_t kRec = 17920;
+
+struct SplitParams {
+    const void *q, *k, *v, *gate, *beta;
+    const float *w, *bias;
+    const void *cs_in;
+    const float *state_in;
+    float *state_out;
+    void *o;
+    const int32_t *cu;
+    unsigned char *ws;
+    int64_t total, nslots;
+    int num_seqs, H;
+    float scale, lb;
+    uint32_t flags;
+    int pairs, tiles;
+};
+
+// Slot of sub-chunk j of sequence n (start s0): distinct for all (n, j) and
+// below total/16 + num_seqs, with consecutive j in consecutive slots.
+__device__ __forceinline__ int64_t sub_slot(int64_t s0, int64_t j, int n) { return (s0 + 16 * j) / 16 + n; }
+
+// Per-wave LDS of pass A (bytes).
+constexpr int A_SRM = 132, A_STR = 20;
+constexpr int A_KL = 0, A_QL = A_KL + 16 * A_SRM * 2, A_KI = A_QL + 16 * A_SRM * 2;
+constexpr int A_KGT = A_KI + 16 * A_SRM * 2, A_NT = A_KGT + 128 * A_STR * 2;
+constexpr int A_XS = A_NT + 16 * 16 * 4, A_PS = A_XS + 16 * A_STR * 2;
+constexpr int A_BET = A_PS + 16 * A_STR * 2, A_WAVE = A_BET + 16 * 4;
+static_assert(A_WAVE % 16 == 0, "wave region alignment");
+
+typedef Ops<__bf16> OPB;
+
+// One 16-token sub-chunk (rows p0 .. p0+15 of sequence n, start s0, length L)
+// by one wave.  All LDS traffic stays inside the wave's region.
+__device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, int n,
+                                                int h, int64_t s0, int64_t L, int64_t j, int lane) {
+    constexpr int D = kHeadDim;
+    typedef __bf16 T;
+    const int m16 = lane & 15, g4 = lane >> 4;
+    const int H = p.H;
+    const int64_t tokstride = (int64_t)H * D;
+    const int64_t p0 = 16 * j;
+    const bool edge = p0 < 3 || p0 + 16 > L;
+    const bool silu = p.flags & KDA_F_SILU;
+    const bool l2 = !(p.flags & KDA_F_NO_QK_L2NORM);
+    const bool glog = p.flags & KDA_F_GATE_IS_LOG;
+    const int c0 = 2 * lane;
+    const int CCH = 3 * H * D;
+    __bf16 *sKL = reinterpret_cast<__bf16 *>(lds + A_KL);
+    __bf16 *sQL = reinterpret_cast<__bf16 *>(lds + A_QL);
+    __bf16 *sKI = reinterpret_cast<__bf16 *>(lds + A_KI);
+    __bf16 *sKGT = reinterpret_cast<__bf16 *>(lds + A_KGT);
+    float *sNT = reinterpret_cast<float *>(lds + A_NT);
+    __bf16 *sXS = reinterpret_cast<__bf16 *>(lds + A_XS);
+    __bf16 *sPS = reinterpret_cast<__bf16 *>(lds + A_PS);
+    float *sBET = reinterpret_cast<float *>(lds + A_BET);
+    unsigned char *rec = p.ws + ((size_t)h * p.nslots + sub_slot(s0, j, n)) * kRec;
+
+    // ---- raw rows p0-3 .. p0+15 (clamped into the sequence; rare fix-ups below)
+    const T *qg = reinterpret_cast<const T *>(p.q) + (size_t)h * D + c0;
+    const T *kg = reinterpret_cast<const T *>(p.k) + (size_t)h * D + c0;
+    const T *vg = reinterpret_cast<const T *>(p.v) + (size_t)h * D + c0;
+    const T *ag = reinterpret_cast<const T *>(p.gate) + (size_t)h * D + c0;
+    float xq[19][2], xk[19][2], xv[19][2], ga[16][2];
+#pragma unroll
+    for (int r = 0; r < 19; ++r) {
+        int64_t sp = p0 + r - 3;
+        sp = sp < 0 ? 0 : (sp >= L ? L - 1 : sp);
+        const int64_t off = (s0 + sp) * tokstride;
+        Pair<T>::load(qg + off, xq[r][0], xq[r][1]);
+        Pair<T>::load(kg + off, xk[r][0], xk[r][1]);
+        Pair<T>::load(vg + off, xv[r][0], xv[r][1]);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const int64_t sp = p0 + rr < L ? p0 + rr : L - 1;
+        Pair<T>::load(ag + (s0 + sp) * tokstride, ga[rr][0], ga[rr][1]);
+    }
+    float beta_r = 0.f;
+    if (lane < 16 && p0 + lane < L)
+        beta_r = to_f32(reinterpret_cast<const T *>(p.beta)[(s0 + p0 + lane) * H + h]);
+    const int qch = h * D + c0, kch = H * D + h * D + c0, vch = 2 * H * D + h * D + c0;
+    if (edge && p0 == 0) {  // the three rows before the sequence: conv state or zeros
+        const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)n * 3 * CCH : nullptr;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, v0 = 0.f, v1 = 0.f;
+            if (csn) {
+                const T *row = csn + (size_t)r * CCH;
+                Pair<T>::load(row + qch, a0, a1);
+                Pair<T>::load(row + kch, b0, b1);
+                Pair<T>::load(row + vch, v0, v1);
+            }
+            xq[r][0] = a0; xq[r][1] = a1;
+            xk[r][0] = b0; xk[r][1] = b1;
+            xv[r][0] = v0; xv[r][1] = v1;
+        }
+    }
+    if (lane < 16) sBET[lane] = beta_r;
+
+    // ---- conv, activation, gate, L2
+    float wq[2][4], wk[2][4], wv[2][4], bq[2], bk[2], bv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        f32x4 a = *reinterpret_cast<const f32x4 *>(p.w + 4 * (qch + e));
+        f32x4 b = *reinterpret_cast<const f32x4 *>(p.w + 4 * (kch + e));
+        f32x4 cc = *reinterpret_cast<const f32x4 *>(p.w + 4 * (vch + e));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) { wq[e][t] = a[t]; wk[e][t] = b[t]; wv[e][t] = cc[t]; }
+        bq[e] = p.bias ? p.bias[qch + e] : 0.f;
+        bk[e] = p.bias ? p.bias[kch + e] : 0.f;
+        bv[e] = p.bias ? p.bias[vch + e] : 0.f;
+    }
+    float yq[16][2], yk[16][2], yv[16][2];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            yq[rr][e] = bq[e] + wq[e][0] * xq[rr][e] + wq[e][1] * xq[rr + 1][e] +
+                        wq[e][2] * xq[rr + 2][e] + wq[e][3] * xq[rr + 3][e];
+            yk[rr][e] = bk[e] + wk[e][0] * xk[rr][e] + wk[e][1] * xk[rr + 1][e] +
+                        wk[e][2] * xk[rr + 2][e] + wk[e][3] * xk[rr + 3][e];
+            yv[rr][e] = bv[e] + wv[e][0] * xv[rr][e] + wv[e][1] * xv[rr + 1][e] +
+                        wv[e][2] * xv[rr + 2][e] + wv[e][3] * xv[rr + 3][e];
+        }
+    if (silu) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                yq[rr][e] *= sigmoidf_dev(yq[rr][e]);
+                yk[rr][e] *= sigmoidf_dev(yk[rr][e]);
+                yv[rr][e] *= sigmoidf_dev(yv[rr][e]);
+            }
+    }
+    float g2[16][2];
+    if (glog) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) g2[rr][e] = fmaxf(ga[rr][e], p.lb) * kLog2eS;
+    } else {
+        const float lb2 = p.lb * kLog2eS;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) g2[rr][e] = lb2 * sigmoidf_dev(ga[rr][e]);
+    }
+    if (edge) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            if (p0 + rr >= L) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    yq[rr][e] = 0.f; yk[rr][e] = 0.f; yv[rr][e] = 0.f; g2[rr][e] = 0.f;
+                }
+            }
+    }
+    float rq[16], rk[16];
+    if (l2) {
+        float pq[16], pk[16], sq4[4], sk4[4];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            pq[rr] = yq[rr][0] * yq[rr][0] + yq[rr][1] * yq[rr][1];
+            pk[rr] = yk[rr][0] * yk[rr][0] + yk[rr][1] * yk[rr][1];
+        }
+        rows16_sum(pq, sq4, lane);
+        rows16_sum(pk, sk4, lane);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            sq4[t] = __builtin_amdgcn_rsqf(sq4[t] + 1e-6f);
+            sk4[t] = __builtin_amdgcn_rsqf(sk4[t] + 1e-6f);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            rq[rr] = row_value(sq4, rr);
+            rk[rr] = row_value(sk4, rr);
+        }
+    } else {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) { rq[rr] = 1.f; rk[rr] = 1.f; }
+    }
+
+    // ---- decays as running products; operands relative to the sub-chunk start
+    float kl[16][2], ql[16][2], kr[16][2], gsum[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        float al[16], run = 1.f, gs = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            al[rr] = exp2_fast(g2[rr][e]);
+            gs += g2[rr][e];
+            run *= al[rr];
+            const float kn = yk[rr][e] * rk[rr];
+            ql[rr][e] = yq[rr][e] * rq[rr] * run;
+            kl[rr][e] = kn * run;
+            kr[rr][e] = kn;
+        }
+        float back = 1.f;
+#pragma unroll
+        for (int rr = 15; rr >= 0; --rr) {
+            kr[rr][e] *= back;
+            back *= al[rr];
+        }
+        gsum[e] = gs;
+    }
+    const float fd0 = exp2_fast(-gsum[0]), fd1 = exp2_fast(-gsum[1]);
+    {
+        f32x2 gm = {exp2_fast(gsum[0]), exp2_fast(gsum[1])};
+        *reinterpret_cast<f32x2 *>(rec + R_GAM + 4 * c0) = gm;
+    }
+    float bt[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) bt[rr] = sBET[rr];  // wave-local broadcast
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        Pair<__bf16>::store(sKL + rr * A_SRM + c0, kl[rr][0], kl[rr][1]);
+        Pair<__bf16>::store(sQL + rr * A_SRM + c0, ql[rr][0], ql[rr][1]);
+        Pair<__bf16>::store(sKI + rr * A_SRM + c0, kr[rr][0] * fd0, kr[rr][1] * fd1);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int c = c0 + e, r = 4 * q4;
+            OPB::store4(sKGT + c * A_STR + r, bt[r] * kl[r][e], bt[r + 1] * kl[r + 1][e],
+                        bt[r + 2] * kl[r + 2][e], bt[r + 3] * kl[r + 3][e]);
+            // accumulator / A-fragment layouts for pass B: element (token r, channel c)
+            // of tile c / 16 sits in lane (r / 4) * 16 + c % 16, slot r % 4
+            const size_t fo = ((size_t)((c >> 4) * 64 + q4 * 16 + (c & 15)) * 4) * 2;
+            OPB::store4(reinterpret_cast<__bf16 *>(rec + R_KD + fo), kr[r][e], kr[r + 1][e],
+                        kr[r + 2][e], kr[r + 3][e]);
+            OPB::store4(reinterpret_cast<__bf16 *>(rec + R_BV + fo), bt[r] * yv[r][e],
+                        bt[r + 1] * yv[r + 1][e], bt[r + 2] * yv[r + 2][e], bt[r + 3] * yv[r + 3][e]);
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- decayed Grams over the sub-chunk (one 16 x 16 tile each)
+    {
+        const f32x4 a = OPB::gram(sKL + m16 * A_SRM, sKI + m16 * A_SRM, nullptr, g4);
+        const f32x4 pq = OPB::gram(sQL + m16 * A_SRM, sKI + m16 * A_SRM, nullptr, g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rl = 4 * g4 + i, sl = m16;
+            sNT[sl * 16 + rl] = (sl < rl) ? a[i] * sBET[rl] : 0.f;
+            sPS[rl * A_STR + sl] = (__bf16)((sl <= rl) ? pq[i] : 0.f);
+        }
+    }
+    // Q . 2^b fragments (pairs of 16-channel blocks, matching pass B's state tiles)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const __bf16 *row = sQL + m16 * A_SRM + 32 * t + 4 * g4;
+        bf16x8 f = join8(*reinterpret_cast<const bf16x4 *>(row), *reinterpret_cast<const bf16x4 *>(row + 16));
+        *reinterpret_cast<bf16x8 *>(rec + R_QG + ((size_t)t * 64 + lane) * 16) = f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- X = (I + N)^-1, N strictly lower (stored transposed): right-looking
+    if (lane < 16) {
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < 15; ++s) {
+            const float xs = x[s];
+#pragma unroll
+            for (int i = s + 1; i < 16; ++i) x[i] -= sNT[s * 16 + i] * xs;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sXS[i * A_STR + lane] = (__bf16)x[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    *reinterpret_cast<bf16x4 *>(rec + R_XX + (size_t)lane * 8) =
+        *reinterpret_cast<const bf16x4 *>(sXS + m16 * A_STR + 4 * g4);
+    *reinterpret_cast<bf16x4 *>(rec + R_PP + (size_t)lane * 8) =
+        *reinterpret_cast<const bf16x4 *>(sPS + m16 * A_STR + 4 * g4);
+
+    // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL area
+    const bf16x4 xa = *reinterpret_cast<const bf16x4 *>(sXS + m16 * A_STR + 4 * g4);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        const int col = 16 * nt + m16;
+        const f32x4 rhs = OPB::load4(sKGT + col * A_STR + 4 * g4);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 wr = mma_k16(xa, pack4(rhs), z);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sKL[(4 * g4 + i) * A_SRM + col] = (__bf16)(-wr[i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const __bf16 *row = sKL + m16 * A_SRM + 32 * t + 4 * g4;
+        bf16x8 f = join8(*reinterpret_cast<const bf16x4 *>(row), *reinterpret_cast<const bf16x4 *>(row + 16));
+        *reinterpret_cast<bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16) = f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the region is reused by this wave's next sub-chunk
+}
+
+__global__ void __launch_bounds__(256, 1) intra_kernel(SplitParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_a[];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = blockIdx.y;
+    const int64_t b0 = (int64_t)blockIdx.x * 64, b1 = b0 + 64;
+    unsigned char *lds = smem_a + w * A_WAVE;
+    // sub-chunks (aligned to sequence starts) that begin inside [b0, b1), dealt
+    // round-robin to the four waves
+    int n = p.cu ? find_seq(p.cu, p.num_seqs, b0) : (int)(b0 / (p.total / p.num_seqs));
+    int count = 0;
+    for (; n < p.num_seqs; ++n) {
+        int64_t s0, L;
+        seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
+        if (s0 >= b1) break;
+        if (L == 0) continue;
+        int64_t j = s0 >= b0 ? 0 : (b0 - s0 + 15) / 16;
+        for (; s0 + 16 * j < b1 && 16 * j < L; ++j, ++count)
+            if ((count & 3) == w) intra_sub_chunk(p, lds, n, h, s0, L, j, lane);
+    }
+}
+
+template <int DVW>
+__global__ void __launch_bounds__(DVW * 4) scan_kernel(SplitParams p) {
+    constexpr int D = kHeadDim;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int m16 = lane & 15, g4 = lane >> 4;
+    const int bid = blockIdx.x;
+    const int grp = bid / (8 * p.tiles), rem = bid - grp * 8 * p.tiles;
+    const int tile = rem >> 3, pr = grp * 8 + (rem & 7);
+    if (pr >= p.pairs) return;
+    const int H = p.H;
+    const int n = pr / H, h = pr - n * H;
+    int64_t s0, L;
+    seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
+    const int nt = tile * (DVW / 16) + w;  // dv n-tile of this wave
+    const int col = 16 * nt + m16;
+    const int64_t tokstride = (int64_t)H * D;
+
+    f32x4 S[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * mt + 4 * g4 + i;
+            S[mt][i] = p.state_in ? p.state_in[((size_t)pr * D + row) * D + col] : 0.f;
+        }
+
+    struct Frag {
+        bf16x8 wn[4], qg[4];
+        bf16x4 kd[8], bv, pp, xx;
+        f32x4 gam[8];
+    };
+    const int64_t J = (L + 15) / 16;
+    const unsigned char *rec0 = p.ws + ((size_t)h * p.nslots + (J > 0 ? sub_slot(s0, 0, n) : 0)) * kRec;
+    auto load = [&](int64_t j, Frag &f) {
+        const unsigned char *rec = rec0 + (size_t)j * kRec;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f.wn[t] = *reinterpret_cast<const bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16);
+            f.qg[t] = *reinterpret_cast<const bf16x8 *>(rec + R_QG + ((size_t)t * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            f.kd[mt] = *reinterpret_cast<const bf16x4 *>(rec + R_KD + ((size_t)mt * 64 + lane) * 8);
+            f.gam[mt] = *reinterpret_cast<const f32x4 *>(rec + R_GAM + (size_t)(16 * mt + 4 * g4) * 4);
+        }
+        f.bv = *reinterpret_cast<const bf16x4 *>(rec + R_BV + ((size_t)nt * 64 + lane) * 8);
+        f.pp = *reinterpret_cast<const bf16x4 *>(rec + R_PP + (size_t)lane * 8);
+        f.xx = *reinterpret_cast<const bf16x4 *>(rec + R_XX + (size_t)lane * 8);
+    };
+    __bf16 *op = reinterpret_cast<__bf16 *>(p.o) + (size_t)h * D + col;
+    auto step = [&](const Frag &f, int64_t j) {
+        bf16x4 Sb[8];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) Sb[mt] = pack4(S[mt]);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 U = mma_k16(f.xx, f.bv, z);  // X diag(beta) V
+#pragma unroll
+        for (int t = 0; t < 4; ++t) U = mma_k32(f.wn[t], join8(Sb[2 * t], Sb[2 * t + 1]), U);
+        f32x4 O = z;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) O = mma_k32(f.qg[t], join8(Sb[2 * t], Sb[2 * t + 1]), O);
+        const bf16x4 Ub = pack4(U);
+        O = mma_k16(f.pp, Ub, O);
+        const int64_t r0 = 16 * j + 4 * g4;
+        if (r0 + 3 < L) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (r0 + i < L) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) S[mt] = mma_k16(f.kd[mt], Ub, S[mt] * f.gam[mt]);
+    };
+    // two fragment sets in flight: the next sub-chunk loads while this one computes
+    Frag fa, fb;
+    if (J > 0) load(0, fa);
+    for (int64_t j = 0; j < J; j += 2) {
+        if (j + 1 < J) load(j + 1, fb);
+        step(fa, j);
+        if (j + 1 < J) {
+            if (j + 2 < J) load(j + 2, fa);
+            step(fb, j + 1);
+        }
+    }
+    if (p.state_out) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mt + 4 * g4 + i;
+                p.state_out[((size_t)pr * D + row) * D + col] = S[mt][i];
+            }
+    }
+}
+
+template <int DVW>
+hipError_t launch_scan(const SplitParams &sp, hipStream_t s) {
+    const unsigned blocks = (unsigned)((sp.pairs + 7) / 8) * 8u * (unsigned)sp.tiles;
+    hipLaunchKernelGGL(scan_kernel<DVW>, dim3(blocks), dim3(DVW * 4), 0, s, sp);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t split_workspace_bytes(int64_t total_tokens, int num_seqs, int H) {
+    return (size_t)H * (size_t)(total_tokens / 16 + num_seqs) * kRec;
+}
+
+hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStream_t s) {
+    SplitParams sp;
+    sp.q = a->q; sp.k = a->k; sp.v = a->v; sp.gate = a->gate; sp.beta = a->beta;
+    sp.w = a->conv_weight; sp.bias = a->conv_bias; sp.cs_in = a->conv_state_in;
+    sp.state_in = a->state_in; sp.state_out = a->state_out; sp.o = a->o;
+    sp.cu = a->cu_seqlens; sp.ws = static_cast<unsigned char *>(a->workspace);
+    sp.total = a->total_tokens; sp.nslots = a->total_tokens / 16 + a->num_seqs;
+    sp.num_seqs = a->num_seqs; sp.H = a->num_heads;
+    sp.scale = a->scale; sp.lb = a->gate_lower_bound; sp.flags = a->flags;
+    sp.pairs = a->num_seqs * a->num_heads;
+    if (dv_tile > 64) dv_tile = 64;  // four waves of 16 dv columns per workgroup
+    sp.tiles = kHeadDim / dv_tile;
+    if (a->total_tokens > 0) {
+        static std::once_flag once;
+        static hipError_t attr = hipSuccess;
+        std::call_once(once, [] {
+            attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 4 * A_WAVE);
+        });
+        if (attr != hipSuccess) return attr;
+        dim3 grid((unsigned)((a->total_tokens + 63) / 64), (unsigned)a->num_heads);
+        hipLaunchKernelGGL(intra_kernel, grid, dim3(256), 4 * A_WAVE, s, sp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    switch (dv_tile) {
+        case 16: return launch_scan<16>(sp, s);
+        case 32: return launch_scan<32>(sp, s);
+        default: return launch_scan<64>(sp, s);
+    }
+}
+
+}  // namespace kda

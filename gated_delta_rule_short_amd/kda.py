@@ -21,7 +21,7 @@ KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG = 1, 2, 4
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_short_conv",
-           "kda_prefill", "kda_decode")
+           "kda_prefill", "kda_prefill_workspace_size", "kda_decode")
 
 _c_i32, _c_i64, _c_u32, _c_f32, _p = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                                       ctypes.c_float, ctypes.c_void_p)
@@ -36,7 +36,7 @@ class KdaPrefillArgs(ctypes.Structure):
         ("q", _p), ("k", _p), ("v", _p), ("gate", _p), ("beta", _p),
         ("conv_weight", _p), ("conv_bias", _p), ("conv_state_in", _p), ("conv_state_out", _p),
         ("state_in", _p), ("state_out", _p), ("o", _p), ("cu_seqlens", _p),
-        ("cu_seqlens_host", _p),
+        ("cu_seqlens_host", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH):
                                        ctypes.c_int, _c_u32, _p]
         lib.kda_prefill.restype = ctypes.c_int
         lib.kda_prefill.argtypes = [ctypes.POINTER(KdaPrefillArgs), _p]
+        lib.kda_prefill_workspace_size.restype = ctypes.c_size_t
+        lib.kda_prefill_workspace_size.argtypes = [ctypes.POINTER(KdaPrefillArgs)]
         lib.kda_decode.restype = ctypes.c_int
         lib.kda_decode.argtypes = [ctypes.POINTER(KdaDecodeArgs), _p]
         if path == LIB_PATH:
@@ -159,12 +161,14 @@ def kda_short_conv(x, weight, *, cu_seqlens=None, cu_seqlens_host=None, bias=Non
 def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens_host=None,
                 num_seqs=None, conv_bias=None, conv_state_in=None, conv_state_out=None,
                 state_in=None, state_out=None, o=None, scale=0.0, gate_lower_bound=-5.0,
-                chunk_size=0, flags=0, stream=None):
+                chunk_size=0, flags=0, workspace=None, stream=None):
     """Chunked KDA prefill of packed sequences.
 
     q, k, gate: [T, H, 128]; v: [T, H, 128]; beta: [T, H] (bf16 or fp32, one dtype);
     conv_weight: [3*H*128, 4] fp32.  state_out / conv_state_out: a tensor, or True
-    to allocate one.  Returns (o, state_out, conv_state_out)."""
+    to allocate one.  workspace: a uint8 device tensor for the two-pass schedule
+    (see prefill_workspace_bytes), True to allocate one, or None for the one-pass
+    schedule.  Returns (o, state_out, conv_state_out)."""
     lib = load_library()
     dev = q.device
     T, H, dk = q.shape
@@ -194,9 +198,26 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
         conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias),
         conv_state_in=_ptr(conv_state_in), conv_state_out=_ptr(conv_state_out),
         state_in=_ptr(state_in), state_out=_ptr(state_out), o=_ptr(o),
-        cu_seqlens=_ptr(cu_seqlens), cu_seqlens_host=_ptr(cuh))
+        cu_seqlens=_ptr(cu_seqlens), cu_seqlens_host=_ptr(cuh), workspace=None, workspace_bytes=0)
+    if workspace is True:
+        need = lib.kda_prefill_workspace_size(ctypes.byref(a))
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel()
     _check(lib, lib.kda_prefill(ctypes.byref(a), _stream(stream, dev)))
     return o, state_out, conv_state_out
+
+
+def prefill_workspace_bytes(total_tokens, num_heads, num_seqs=1, dtype=torch.bfloat16,
+                            chunk_size=0):
+    """Workspace bytes the two-pass prefill needs (0 when it does not apply)."""
+    lib = load_library()
+    a = KdaPrefillArgs(num_seqs=int(num_seqs), num_heads=int(num_heads), head_dim_k=128,
+                       head_dim_v=128, chunk_size=int(chunk_size), total_tokens=int(total_tokens),
+                       dtype=KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
+    return int(lib.kda_prefill_workspace_size(ctypes.byref(a)))
 
 
 def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias=None, o=None,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
@@ -138,9 +138,29 @@ typedef struct {
     void *o;                   /* [T][H][dv] output; must not overlap the inputs */
     const int32_t *cu_seqlens; /* [N+1] device, or NULL for N equal sequences */
     const int32_t *cu_seqlens_host; /* optional host copy, validated when given */
+    void *workspace;           /* device scratch for the two-pass schedule, or NULL */
+    size_t workspace_bytes;    /* its size; see kda_prefill_workspace_size */
 } kda_prefill_args;
 
+/*
+ * Two schedules compute the same mixer (identical in exact arithmetic):
+ *   - one pass: each workgroup owns a (sequence, head, dv tile) and runs the
+ *     chunk's WY/UT transform itself (chunk_size 16, 32 or 64; default 64);
+ *   - two passes (bf16 I/O only), chosen when chunk_size is 0 or 16 and a
+ *     workspace of at least kda_prefill_workspace_size() bytes is given: a
+ *     fully parallel pass turns every 16-token sub-chunk of every head into
+ *     matrix-core operands in the workspace, and a second pass carries the
+ *     state over them.  It keeps the whole GPU busy when there are few
+ *     (sequence, head) pairs.
+ * The workspace is owned by the caller, overwritten by each call, and must not
+ * be shared by concurrent calls.
+ */
 kda_status kda_prefill(const kda_prefill_args *args, hipStream_t stream);
+
+/* Bytes of workspace the two-pass schedule needs for these arguments (it depends
+ * on num_seqs, num_heads and total_tokens only); 0 when that schedule does not
+ * apply (fp32 I/O or an explicit chunk_size of 32 or 64). */
+size_t kda_prefill_workspace_size(const kda_prefill_args *args);
 
 /*
  * kda_decode -- one new token for each of N sequences (the single-token

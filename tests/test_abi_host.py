@@ -35,7 +35,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -49,7 +49,7 @@ def test_struct_layouts_match_header():
     # offsets of the first pointer fields follow the C layout rules (int64 aligned at 8)
     assert K.KdaPrefillArgs.total_tokens.offset == 24
     assert K.KdaPrefillArgs.q.offset == 48
-    assert ctypes.sizeof(K.KdaPrefillArgs) == 48 + 14 * 8
+    assert ctypes.sizeof(K.KdaPrefillArgs) == 48 + 16 * 8
     assert K.KdaDecodeArgs.q.offset == 32
     assert ctypes.sizeof(K.KdaDecodeArgs) == 32 + 10 * 8
 
@@ -168,6 +168,23 @@ def test_short_conv_rejects_bad_arguments(lib):
     cu = (ctypes.c_int32 * 3)(0, 5, 7)
     assert f(FAKE, ctypes.c_void_p(0x900000), 8, 4, FAKE, None, None, None, FAKE,
              ctypes.cast(cu, ctypes.c_void_p), 2, 1, 0, None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_workspace_size_query(lib):
+    a = _prefill_args(total_tokens=4096, num_heads=64)
+    need = lib.kda_prefill_workspace_size(ctypes.byref(a))
+    assert need == 64 * (4096 // 16 + 1) * 17920
+    a.chunk_size = 64
+    assert lib.kda_prefill_workspace_size(ctypes.byref(a)) == 0
+    b = _prefill_args(dtype=K.KDA_F32)
+    assert lib.kda_prefill_workspace_size(ctypes.byref(b)) == 0
+
+
+def test_prefill_rejects_workspace_overlapping_output(lib):
+    a = _prefill_args(total_tokens=64, num_heads=2)
+    a.workspace = a.o
+    a.workspace_bytes = lib.kda_prefill_workspace_size(ctypes.byref(a))
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -328,3 +328,75 @@ def test_empty_batch_and_zero_tokens():
     o, st, cs = _gpu_prefill(inp)
     assert o.numel() == 0
     assert torch.equal(st, inp["state_in"]) and torch.equal(cs, inp["conv_state_in"])
+
+
+# ------------------------------------------------- two-pass schedule (workspace)
+
+@pytest.mark.parametrize("flags", [0, kda.KDA_F_SILU, kda.KDA_F_NO_QK_L2NORM, kda.KDA_F_GATE_IS_LOG])
+def test_two_pass_ragged_matches_oracle(flags):
+    lengths = [1, 2, 3, 15, 16, 17, 0, 63, 64, 65, 130, 200]
+    inp = KI.make_prefill(3, lengths, seed=131, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    if flags & kda.KDA_F_GATE_IS_LOG:
+        inp["gate"] = (-6.0 * torch.rand(inp["gate"].shape, device=DEV)).to(torch.bfloat16)
+    bias = 0.1 * torch.randn(inp["conv_w"].shape[0], device=DEV)
+    ref = _oracle_prefill(inp, conv_b=bias, flags=flags)
+    o, st, cs = _gpu_prefill(inp, conv_bias=bias, flags=flags, workspace=True)
+    assert_bf16_close(o, ref["o"], inp["cu_seqlens"], 3, st, ref["state"], "two-pass")
+    np.testing.assert_array_equal(to_np(cs), ref["conv_state"])
+
+
+@pytest.mark.parametrize("dv_tile", ["16", "32", "64"])
+def test_two_pass_dv_tiles_agree_bitwise(dv_tile, monkeypatch):
+    inp = KI.make_prefill(2, [130, 70], seed=141, device=DEV, state_std=0.1)
+    ref = _oracle_prefill(inp)
+    base = _gpu_prefill(inp, workspace=True)
+    monkeypatch.setenv("KDA_PREFILL_DV_TILE", dv_tile)
+    o, st, _ = _gpu_prefill(inp, workspace=True)
+    assert_bf16_close(o, ref["o"], inp["cu_seqlens"], 2, st, ref["state"], "dv tile " + dv_tile)
+    assert torch.equal(o, base[0]) and torch.equal(st, base[1])
+
+
+def test_two_pass_agrees_with_one_pass_chunk16():
+    inp = KI.make_prefill(2, [257, 40], seed=151, device=DEV, state_std=0.1)
+    a = _gpu_prefill(inp, workspace=True)
+    b = _gpu_prefill(inp, chunk_size=16)
+    assert slice_rel_errors(a[0], b[0], inp["cu_seqlens"].cpu(), 2).max() <= 1e-2
+    assert state_rel_errors(a[1], b[1]).max() <= 1e-2
+
+
+def test_two_pass_workload1_full_size_sampled_heads():
+    inp = KI.workload_inputs(1, device=DEV)
+    o, st, _ = _gpu_prefill(inp, workspace=True)
+    assert torch.isfinite(o).all()
+    _sampled_check(inp, o, st, [0, 33, 63])
+
+
+def test_two_pass_workload3_long_sampled_heads():
+    inp = KI.workload_inputs(3, device=DEV)
+    o, st, _ = _gpu_prefill(inp, workspace=True)
+    assert torch.isfinite(o).all() and torch.isfinite(st).all()
+    _sampled_check(inp, o, st, [7, 50])
+
+
+def test_two_pass_workload4_varlen_sampled():
+    inp = KI.workload_inputs(4, device=DEV)
+    o, st, _ = _gpu_prefill(inp, workspace=True)
+    assert torch.isfinite(o).all()
+    lengths = inp["lengths"]
+    _sampled_check(inp, o, st, [1, 60], seqs=[int(np.argmax(lengths)), int(np.argmin(lengths)), 9])
+
+
+def test_two_pass_split_equals_whole_and_deterministic():
+    inp = KI.make_prefill(2, [300], seed=161, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    o, st, cs = _gpu_prefill(inp, workspace=True)
+    o_again, st_again, _ = _gpu_prefill(inp, workspace=True)
+    assert torch.equal(o, o_again) and torch.equal(st, st_again)
+    cut = 112  # a multiple of 16: sub-chunk boundaries coincide
+    a = {k_: (v_[:cut] if k_ in ("q", "k", "v", "gate", "beta") else v_) for k_, v_ in inp.items()}
+    a["cu_seqlens"] = torch.tensor([0, cut], dtype=torch.int32, device=DEV)
+    o1, st1, cs1 = _gpu_prefill(a, workspace=True)
+    b = {k_: (v_[cut:] if k_ in ("q", "k", "v", "gate", "beta") else v_) for k_, v_ in inp.items()}
+    b["cu_seqlens"] = torch.tensor([0, 300 - cut], dtype=torch.int32, device=DEV)
+    b["state_in"], b["conv_state_in"] = st1, cs1
+    o2, st2, cs2 = _gpu_prefill(b, workspace=True)
+    assert torch.equal(torch.cat([o1, o2]), o) and torch.equal(st2, st) and torch.equal(cs2, cs)
