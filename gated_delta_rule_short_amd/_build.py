@@ -2,7 +2,12 @@
 
 Each .hip source is compiled to an object in parallel, then linked into
 gated_delta_rule_short_amd/libkda.so.  Packed-fp32 instruction selection is
-disabled for all device code (-packed-fp32-ops).
+disabled for all device code (-packed-fp32-ops).  Matrix-core instructions are
+kept in their VGPR form (-amdgpu-mfma-vgpr-form): on gfx950 a 16x16x32 bf16
+result held in AGPRs needs about eight wait states before v_accvgpr_read sees
+all of it, which is exactly the padding the compiler emits, and a read at that
+distance returned stale rows behind an interleaved MFMA; the VGPR form is read
+fresh after five.
 """
 from __future__ import annotations
 
@@ -35,9 +40,16 @@ def flags():
             "-Wno-unused-command-line-argument"]
 
 
+# Sources whose matrix-core results must stay in VGPRs (see the module docstring).
+# The one-pass prefill is left to the default heuristic: the compiler does not
+# build it with the VGPR form forced.
+VGPR_FORM = {"kda_prefill_split.hip"}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-mllvm", "-amdgpu-mfma-vgpr-form"] if src in VGPR_FORM else []
+    cmd = [hipcc()] + flags() + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag: drop that line
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

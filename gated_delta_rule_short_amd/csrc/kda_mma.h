@@ -21,6 +21,9 @@ template <> struct Ops<__bf16> {
         f32x4 r = {(float)v.x, (float)v.y, (float)v.z, (float)v.w};
         return r;
     }
+    static __device__ __forceinline__ bf16x4 load4raw(const __bf16 *p) {
+        return *reinterpret_cast<const bf16x4 *>(p);
+    }
     static __device__ __forceinline__ void store4(__bf16 *p, float a, float b, float c, float d) {
         bf16x4 v;
         v.x = (__bf16)a; v.y = (__bf16)b; v.z = (__bf16)c; v.w = (__bf16)d;

@@ -102,7 +102,6 @@ template <typename E, int NB, int DVW> struct Layout {
                   "staging fits");
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // DMA of BYTES bytes (a multiple of 1 KiB) of row-gathered global data into
 // contiguous LDS: 16-byte piece i comes from row (16 i) / ROW_BYTES of the

@@ -10,18 +10,21 @@
 // one 16-token sub-chunk of one sequence and computes, relative to the state on
 // entry to the sub-chunk,
 //     A = strict_lower(K~ K^T . decay),  P = lower(Q~ K^T . decay),
-//     X = (I + diag(beta) A)^-1,  W = X diag(beta) (K . 2^b),
+//     X = (I + diag(beta) A)^-1,  W = X diag(beta) (K . 2^b),  U0 = X diag(beta) V,
 // with b the log2-decay cumsum from the sub-chunk start (>= -115.4, so every
 // factor is a finite fp32/bf16 number), and writes them as matrix-core
 // fragments to a workspace record.  Pass B (scan_kernel) runs one workgroup per
 // (sequence, head, dv tile) over its sub-chunks in order:
-//     U = X diag(beta) V - W S,  O = scale ((Q . 2^b) S + P U),
+//     U = U0 - W S,  O = scale ((Q . 2^b) S + P U),
 //     S = diag(2^b_last) S + (K . 2^(b_last - b))^T U.
 // Pass A does the conv / L2 / gate work once per token and head, over the
 // whole GPU; pass B keeps the fp32 state in registers (accumulator layout) for
-// the whole sequence.  The workspace costs extra HBM traffic (one 17.5 KiB
-// record per sub-chunk and head, written once and read once), which pays off
-// when there are too few (sequence, head) pairs to fill the GPU otherwise.
+// the whole sequence and streams the records through an LDS ring filled by
+// two producer waves with LDS DMA, so several sub-chunks are in flight while
+// the consumer waves run the recurrence.  The workspace costs extra HBM
+// traffic (one 17 KiB record per sub-chunk and head, written once and read
+// once), which pays off when there are too few (sequence, head) pairs to fill
+// the GPU otherwise.
 #include <mutex>
 
 #include "kda_device.h"
@@ -38,13 +41,14 @@ constexpr float kLog2eS = 1.4426950408889634f;
 //   WN  [4][64][8]  -W, A-operand fragments (rows tokens, K = dk, permuted pairs)
 //   QG  [4][64][8]  Q . 2^b, same fragment layout
 //   KD  [8][64][4]  (K . 2^(b_last - b))^T, A-operand fragments (rows dk, K = tokens)
-//   BV  [8][64][4]  beta . V, accumulator layout (rows tokens, columns dv)
 //   PP  [64][4]     P, A-operand fragment (rows tokens, K = tokens)
-//   XX  [64][4]     X, same
 //   GAM [128] fp32  2^b_last per dk channel
-constexpr int R_WN = 0, R_QG = 4096, R_KD = 8192, R_BV = 12288, R_PP = 16384, R_XX = 16896,
-              R_GAM = 17408;
-constexpr size_t kRec = 17920;
+//   U0  [8][64][4]  X diag(beta) V, accumulator layout (rows tokens, columns dv)
+// Everything a workgroup of pass B shares comes first (R_U0 bytes), then the
+// per-dv-tile U0 fragments, so each stage is two contiguous DMA ranges.
+constexpr int R_WN = 0, R_QG = 4096, R_KD = 8192, R_PP = 12288, R_GAM = 12800, R_U0 = 13312;
+constexpr size_t kRec = 17408;
+static_assert(R_U0 % 1024 == 0, "shared part moves in whole DMA KiB");
 
 struct SplitParams {
     const void *q, *k, *v, *gate, *beta;
@@ -71,7 +75,8 @@ constexpr int A_SRM = 132, A_STR = 20;
 constexpr int A_KL = 0, A_QL = A_KL + 16 * A_SRM * 2, A_KI = A_QL + 16 * A_SRM * 2;
 constexpr int A_KGT = A_KI + 16 * A_SRM * 2, A_NT = A_KGT + 128 * A_STR * 2;
 constexpr int A_XS = A_NT + 16 * 16 * 4, A_PS = A_XS + 16 * A_STR * 2;
-constexpr int A_BET = A_PS + 16 * A_STR * 2, A_WAVE = A_BET + 16 * 4;
+constexpr int A_VT = A_PS + 16 * A_STR * 2, A_BET = A_VT + 128 * A_STR * 2;
+constexpr int A_WAVE = A_BET + 16 * 4;
 static_assert(A_WAVE % 16 == 0, "wave region alignment");
 
 typedef Ops<__bf16> OPB;
@@ -99,6 +104,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     float *sNT = reinterpret_cast<float *>(lds + A_NT);
     __bf16 *sXS = reinterpret_cast<__bf16 *>(lds + A_XS);
     __bf16 *sPS = reinterpret_cast<__bf16 *>(lds + A_PS);
+    __bf16 *sVT = reinterpret_cast<__bf16 *>(lds + A_VT);
     float *sBET = reinterpret_cast<float *>(lds + A_BET);
     unsigned char *rec = p.ws + ((size_t)h * p.nslots + sub_slot(s0, j, n)) * kRec;
 
@@ -276,8 +282,8 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
             const size_t fo = ((size_t)((c >> 4) * 64 + q4 * 16 + (c & 15)) * 4) * 2;
             OPB::store4(reinterpret_cast<__bf16 *>(rec + R_KD + fo), kr[r][e], kr[r + 1][e],
                         kr[r + 2][e], kr[r + 3][e]);
-            OPB::store4(reinterpret_cast<__bf16 *>(rec + R_BV + fo), bt[r] * yv[r][e],
-                        bt[r + 1] * yv[r + 1][e], bt[r + 2] * yv[r + 2][e], bt[r + 3] * yv[r + 3][e]);
+            OPB::store4(sVT + c * A_STR + r, bt[r] * yv[r][e], bt[r + 1] * yv[r + 1][e],
+                        bt[r + 2] * yv[r + 2][e], bt[r + 3] * yv[r + 3][e]);
         }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -322,21 +328,21 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    *reinterpret_cast<bf16x4 *>(rec + R_XX + (size_t)lane * 8) =
-        *reinterpret_cast<const bf16x4 *>(sXS + m16 * A_STR + 4 * g4);
     *reinterpret_cast<bf16x4 *>(rec + R_PP + (size_t)lane * 8) =
         *reinterpret_cast<const bf16x4 *>(sPS + m16 * A_STR + 4 * g4);
 
-    // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL area
+    // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL
+    // area; U0 = X diag(beta) V straight to the record in accumulator layout
     const bf16x4 xa = *reinterpret_cast<const bf16x4 *>(sXS + m16 * A_STR + 4 * g4);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
         const int col = 16 * nt + m16;
-        const f32x4 rhs = OPB::load4(sKGT + col * A_STR + 4 * g4);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 wr = mma_k16(xa, pack4(rhs), z);
+        const f32x4 wr = mma_k16(xa, OPB::load4raw(sKGT + col * A_STR + 4 * g4), z);
+        const f32x4 ur = mma_k16(xa, OPB::load4raw(sVT + col * A_STR + 4 * g4), z);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sKL[(4 * g4 + i) * A_SRM + col] = (__bf16)(-wr[i]);
+        *reinterpret_cast<bf16x4 *>(rec + R_U0 + ((size_t)nt * 64 + lane) * 8) = pack4(ur);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -372,69 +378,142 @@ __global__ void __launch_bounds__(256, 1) intra_kernel(SplitParams p) {
     }
 }
 
-template <int DVW>
-__global__ void __launch_bounds__(DVW * 4) scan_kernel(SplitParams p) {
-    constexpr int D = kHeadDim;
+// Pass B geometry: NTW consumer waves of 16 dv columns each plus two producer
+// waves; NS ring stages of one record's shared part plus the NTW U0 tiles.
+template <int NTW> struct ScanGeom {
+    static constexpr int kStage = R_U0 + NTW * 512;
+    static constexpr int kInst = (kStage + 1023) / 1024;   // DMA instructions per stage
+    static constexpr int kInstP0 = (kInst + 1) / 2;        // producer 0 takes the even ones
+    static constexpr int kInstP1 = kInst / 2;
+    static constexpr int NS = NTW == 1 ? 5 : 8;            // two workgroups per CU at NTW = 1
+    static constexpr int kThreads = 64 * (NTW + 2);
+    static constexpr int kLds = NS * kStage;
+    static_assert(kInstP0 * (NS - 2) < 64, "in-flight DMA exceeds the vmcnt range");
+};
+
+// Producer wave `pw` moves its share of record j into ring stage `st`.
+template <int NTW>
+__device__ __forceinline__ void scan_issue(unsigned char *stage, const unsigned char *rec, int nt0,
+                                           int pw, int lane) {
+    typedef ScanGeom<NTW> G;
+#pragma unroll
+    for (int i = pw; i < G::kInst; i += 2) {
+        const int off = i * 1024 + lane * 16;  // byte within the stage
+        if (off < G::kStage) {
+            const unsigned char *src =
+                off < R_U0 ? rec + off : rec + R_U0 + nt0 * 512 + (off - R_U0);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(stage + i * 1024), 16, 0, 0);
+        }
+    }
+}
+
+// Producer wait: everything but the DMA of the `later` stages issued after
+// stage j has landed (in-order completion of one wave's vector-memory ops).
+template <int PER, int NSM2>
+__device__ __forceinline__ void scan_wait(int later) {
+    if (later >= NSM2) wait_vmcnt<PER * NSM2>();
+    else if constexpr (NSM2 > 0) {
+        switch (later) {
+            case 0: wait_vmcnt<0>(); break;
+            case 1: wait_vmcnt<PER * 1>(); break;
+            case 2: wait_vmcnt<PER * 2>(); break;
+            case 3: wait_vmcnt<PER * 3>(); break;
+            case 4: wait_vmcnt<PER * 4>(); break;
+            default: wait_vmcnt<PER * 5>(); break;
+        }
+    }
+}
+
+template <int NTW>
+__global__ void __launch_bounds__(ScanGeom<NTW>::kThreads) scan_kernel(SplitParams p) {
+    typedef ScanGeom<NTW> G;
+    constexpr int D = kHeadDim, NS = G::NS;
+    static_assert(NS - 2 <= 6, "scan_wait covers six later stages");
+    extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int bid = blockIdx.x;
     const int grp = bid / (8 * p.tiles), rem = bid - grp * 8 * p.tiles;
     const int tile = rem >> 3, pr = grp * 8 + (rem & 7);
-    if (pr >= p.pairs) return;
+    if (pr >= p.pairs) return;  // whole workgroup: no barrier is left waiting
     const int H = p.H;
     const int n = pr / H, h = pr - n * H;
     int64_t s0, L;
     seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
-    const int nt = tile * (DVW / 16) + w;  // dv n-tile of this wave
+    const int64_t J = (L + 15) / 16;
+    const int nt0 = tile * NTW;
+    const unsigned char *rec0 =
+        p.ws + ((size_t)h * p.nslots + (J > 0 ? sub_slot(s0, 0, n) : 0)) * kRec;
+
+    if (w >= NTW) {
+        // ---------------- producers
+        const int pw = w - NTW;
+        for (int64_t j = 0; j < NS - 1 && j < J; ++j)
+            scan_issue<NTW>(ring + j * G::kStage, rec0 + (size_t)j * kRec, nt0, pw, lane);
+        for (int64_t j = 0; j < J; ++j) {
+            const int64_t rest = J - 1 - j;
+            const int later = rest < NS - 2 ? (int)rest : NS - 2;
+            if (pw == 0) scan_wait<G::kInstP0, NS - 2>(later);
+            else scan_wait<G::kInstP1, NS - 2>(later);
+            // stage j complete (explicit wait above); every consumer is done with
+            // stage j - 1.  A bare barrier: a fence here would drain all DMA in flight.
+            __builtin_amdgcn_s_barrier();
+            const int64_t jn = j + NS - 1;
+            if (jn < J)
+                scan_issue<NTW>(ring + (jn % NS) * G::kStage, rec0 + (size_t)jn * kRec, nt0, pw, lane);
+        }
+        return;
+    }
+
+    // ---------------- consumers: one 16-column dv tile each
+    const int nt = nt0 + w;
     const int col = 16 * nt + m16;
     const int64_t tokstride = (int64_t)H * D;
-
     f32x4 S[8];
+    if (p.state_in) {
+        const float *sin = p.state_in + (size_t)pr * D * D + col;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * mt + 4 * g4 + i;
-            S[mt][i] = p.state_in ? p.state_in[((size_t)pr * D + row) * D + col] : 0.f;
-        }
-
-    struct Frag {
+            for (int i = 0; i < 4; ++i) S[mt][i] = sin[(16 * mt + 4 * g4 + i) * D];
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __bf16 *op = reinterpret_cast<__bf16 *>(p.o) + (size_t)h * D + col;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t j = 0; j < J; ++j) {
+        barrier_lds();
+        const unsigned char *st = ring + (j % NS) * G::kStage;
         bf16x8 wn[4], qg[4];
-        bf16x4 kd[8], bv, pp, xx;
+        bf16x4 kd[8];
         f32x4 gam[8];
-    };
-    const int64_t J = (L + 15) / 16;
-    const unsigned char *rec0 = p.ws + ((size_t)h * p.nslots + (J > 0 ? sub_slot(s0, 0, n) : 0)) * kRec;
-    auto load = [&](int64_t j, Frag &f) {
-        const unsigned char *rec = rec0 + (size_t)j * kRec;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            f.wn[t] = *reinterpret_cast<const bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16);
-            f.qg[t] = *reinterpret_cast<const bf16x8 *>(rec + R_QG + ((size_t)t * 64 + lane) * 16);
+            wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + (t * 64 + lane) * 16);
+            qg[t] = *reinterpret_cast<const bf16x8 *>(st + R_QG + (t * 64 + lane) * 16);
         }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            f.kd[mt] = *reinterpret_cast<const bf16x4 *>(rec + R_KD + ((size_t)mt * 64 + lane) * 8);
-            f.gam[mt] = *reinterpret_cast<const f32x4 *>(rec + R_GAM + (size_t)(16 * mt + 4 * g4) * 4);
+            kd[mt] = *reinterpret_cast<const bf16x4 *>(st + R_KD + (mt * 64 + lane) * 8);
+            gam[mt] = *reinterpret_cast<const f32x4 *>(st + R_GAM + (16 * mt + 4 * g4) * 4);
         }
-        f.bv = *reinterpret_cast<const bf16x4 *>(rec + R_BV + ((size_t)nt * 64 + lane) * 8);
-        f.pp = *reinterpret_cast<const bf16x4 *>(rec + R_PP + (size_t)lane * 8);
-        f.xx = *reinterpret_cast<const bf16x4 *>(rec + R_XX + (size_t)lane * 8);
-    };
-    __bf16 *op = reinterpret_cast<__bf16 *>(p.o) + (size_t)h * D + col;
-    auto step = [&](const Frag &f, int64_t j) {
+        const bf16x4 pp = *reinterpret_cast<const bf16x4 *>(st + R_PP + lane * 8);
+        const bf16x4 u0 = *reinterpret_cast<const bf16x4 *>(st + R_U0 + (w * 64 + lane) * 8);
+
         bf16x4 Sb[8];
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) Sb[mt] = pack4(S[mt]);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 U = mma_k16(f.xx, f.bv, z);  // X diag(beta) V
+        f32x4 U = {(float)u0.x, (float)u0.y, (float)u0.z, (float)u0.w};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) U = mma_k32(f.wn[t], join8(Sb[2 * t], Sb[2 * t + 1]), U);
+        for (int t = 0; t < 4; ++t) U = mma_k32(wn[t], join8(Sb[2 * t], Sb[2 * t + 1]), U);
         f32x4 O = z;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) O = mma_k32(f.qg[t], join8(Sb[2 * t], Sb[2 * t + 1]), O);
+        for (int t = 0; t < 4; ++t) O = mma_k32(qg[t], join8(Sb[2 * t], Sb[2 * t + 1]), O);
         const bf16x4 Ub = pack4(U);
-        O = mma_k16(f.pp, Ub, O);
+        O = mma_k16(pp, Ub, O);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) S[mt] = mma_k16(kd[mt], Ub, S[mt] * gam[mt]);
         const int64_t r0 = 16 * j + 4 * g4;
         if (r0 + 3 < L) {
 #pragma unroll
@@ -443,19 +522,6 @@ __global__ void __launch_bounds__(DVW * 4) scan_kernel(SplitParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (r0 + i < L) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) S[mt] = mma_k16(f.kd[mt], Ub, S[mt] * f.gam[mt]);
-    };
-    // two fragment sets in flight: the next sub-chunk loads while this one computes
-    Frag fa, fb;
-    if (J > 0) load(0, fa);
-    for (int64_t j = 0; j < J; j += 2) {
-        if (j + 1 < J) load(j + 1, fb);
-        step(fa, j);
-        if (j + 1 < J) {
-            if (j + 2 < J) load(j + 2, fa);
-            step(fb, j + 1);
         }
     }
     if (p.state_out) {
@@ -469,10 +535,18 @@ __global__ void __launch_bounds__(DVW * 4) scan_kernel(SplitParams p) {
     }
 }
 
-template <int DVW>
+template <int NTW>
 hipError_t launch_scan(const SplitParams &sp, hipStream_t s) {
+    typedef ScanGeom<NTW> G;
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_kernel<NTW>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
+    });
+    if (attr != hipSuccess) return attr;
     const unsigned blocks = (unsigned)((sp.pairs + 7) / 8) * 8u * (unsigned)sp.tiles;
-    hipLaunchKernelGGL(scan_kernel<DVW>, dim3(blocks), dim3(DVW * 4), 0, s, sp);
+    hipLaunchKernelGGL(scan_kernel<NTW>, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
     return hipGetLastError();
 }
 
@@ -508,9 +582,9 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
         if (e != hipSuccess) return e;
     }
     switch (dv_tile) {
-        case 16: return launch_scan<16>(sp, s);
-        case 32: return launch_scan<32>(sp, s);
-        default: return launch_scan<64>(sp, s);
+        case 16: return launch_scan<1>(sp, s);
+        case 32: return launch_scan<2>(sp, s);
+        default: return launch_scan<4>(sp, s);
     }
 }
 

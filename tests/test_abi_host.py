@@ -173,7 +173,7 @@ def test_short_conv_rejects_bad_arguments(lib):
 def test_workspace_size_query(lib):
     a = _prefill_args(total_tokens=4096, num_heads=64)
     need = lib.kda_prefill_workspace_size(ctypes.byref(a))
-    assert need == 64 * (4096 // 16 + 1) * 17920
+    assert need == 64 * (4096 // 16 + 1) * 17408
     a.chunk_size = 64
     assert lib.kda_prefill_workspace_size(ctypes.byref(a)) == 0
     b = _prefill_args(dtype=K.KDA_F32)
