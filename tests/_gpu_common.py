@@ -69,3 +69,10 @@ def head_conv_state(cs, H, heads, d=128):
             base = part * H * d + h * d
             cols.append(cs[:, :, base:base + d])
     return torch.cat(cols, 2)
+
+
+def seeded(shape, seed, kind="randn", device="cuda:0"):
+    """A seeded draw on the host, moved to the device (test inputs are reproducible)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn(shape, generator=g) if kind == "randn" else torch.rand(shape, generator=g)
+    return x.to(device)

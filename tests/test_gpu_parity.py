@@ -10,7 +10,7 @@ import kda_inputs as KI
 import oracle
 import gated_delta_rule_short_amd as kda
 from tests._gpu_common import (BF16_REL, assert_bf16_close, assert_f32_close, head_conv_state,
-                               head_conv_w, slice_rel_errors, state_rel_errors, to_np)
+                               head_conv_w, seeded, slice_rel_errors, state_rel_errors, to_np)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -89,8 +89,8 @@ def test_short_conv_dense_odd_channels_and_in_place_state():
 def test_decode_matches_oracle(dtype, flags):
     d = KI.make_decode(6, 3, dtype=dtype, seed=21, device=DEV)
     if flags & kda.KDA_F_GATE_IS_LOG:
-        d["gate"] = (-6.0 * torch.rand(d["gate"].shape, device=DEV)).to(dtype)
-    bias = (0.1 * torch.randn(d["conv_w"].shape[0], device=DEV))
+        d["gate"] = (-6.0 * seeded(d["gate"].shape, 22, "rand")).to(dtype)
+    bias = 0.1 * seeded(d["conv_w"].shape[0], 23)
     ref = oracle.decode(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"], d["conv_state"],
                         d["state"], conv_b=bias, flags=flags)
     o = kda.kda_decode(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"], d["conv_state"],
@@ -155,8 +155,10 @@ def test_prefill_flags_and_bias(dtype, flags):
     inp = KI.make_prefill(2, [40, 77], dtype=dtype, seed=41, device=DEV, state_std=0.1,
                           conv_cache_std=1.0)
     if flags & kda.KDA_F_GATE_IS_LOG:
-        inp["gate"] = (-6.0 * torch.rand(inp["gate"].shape, device=DEV)).to(dtype)
-    bias = 0.1 * torch.randn(inp["conv_w"].shape[0], device=DEV)
+        inp["gate"] = (-6.0 * seeded(inp["gate"].shape, 42, "rand")).to(dtype)
+    if flags & kda.KDA_F_NO_QK_L2NORM:  # keep the delta rule contractive (beta |k|^2 < 1)
+        inp["k"] = (0.5 * inp["k"].float()).to(dtype)
+    bias = 0.1 * seeded(inp["conv_w"].shape[0], 43)
     ref = _oracle_prefill(inp, conv_b=bias, flags=flags, scale=0.3, gate_lower_bound=-4.0)
     o, st, cs = _gpu_prefill(inp, conv_bias=bias, flags=flags, scale=0.3, gate_lower_bound=-4.0)
     if dtype == torch.float32:
@@ -337,8 +339,12 @@ def test_two_pass_ragged_matches_oracle(flags):
     lengths = [1, 2, 3, 15, 16, 17, 0, 63, 64, 65, 130, 200]
     inp = KI.make_prefill(3, lengths, seed=131, device=DEV, state_std=0.1, conv_cache_std=1.0)
     if flags & kda.KDA_F_GATE_IS_LOG:
-        inp["gate"] = (-6.0 * torch.rand(inp["gate"].shape, device=DEV)).to(torch.bfloat16)
-    bias = 0.1 * torch.randn(inp["conv_w"].shape[0], device=DEV)
+        inp["gate"] = (-6.0 * seeded(inp["gate"].shape, 132, "rand")).to(torch.bfloat16)
+    if flags & kda.KDA_F_NO_QK_L2NORM:
+        # without the L2 norm the caller scales k; keep beta |k|^2 < 1 so the delta
+        # rule stays contractive and bf16 rounding does not grow along the sequence
+        inp["k"] = (0.5 * inp["k"].float()).to(torch.bfloat16)
+    bias = 0.1 * seeded(inp["conv_w"].shape[0], 133)
     ref = _oracle_prefill(inp, conv_b=bias, flags=flags)
     o, st, cs = _gpu_prefill(inp, conv_bias=bias, flags=flags, workspace=True)
     assert_bf16_close(o, ref["o"], inp["cu_seqlens"], 3, st, ref["state"], "two-pass")
