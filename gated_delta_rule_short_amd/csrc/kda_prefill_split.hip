@@ -70,16 +70,63 @@ struct SplitParams {
 // below total/16 + num_seqs, with consecutive j in consecutive slots.
 __device__ __forceinline__ int64_t sub_slot(int64_t s0, int64_t j, int n) { return (s0 + 16 * j) / 16 + n; }
 
-// Per-wave LDS of pass A (bytes).
-constexpr int A_SRM = 132, A_STR = 20;
+// Per-wave LDS of pass A (bytes).  Row-major tiles hold A_SRM bf16 per token
+// row, transposed tiles A_STR (A_VTS) bf16 per channel row.  beta V
+// (transposed, VT) is formed after the QG export, in the then dead QL area.
+constexpr int A_SRM = 132, A_STR = 20, A_VTS = 16;
 constexpr int A_KL = 0, A_QL = A_KL + 16 * A_SRM * 2, A_KI = A_QL + 16 * A_SRM * 2;
 constexpr int A_KGT = A_KI + 16 * A_SRM * 2, A_NT = A_KGT + 128 * A_STR * 2;
 constexpr int A_XS = A_NT + 16 * 16 * 4, A_PS = A_XS + 16 * A_STR * 2;
-constexpr int A_VT = A_PS + 16 * A_STR * 2, A_BET = A_VT + 128 * A_STR * 2;
-constexpr int A_WAVE = A_BET + 16 * 4;
+constexpr int A_WAVE = A_PS + 16 * A_STR * 2;
+constexpr int A_VT = A_QL;
 static_assert(A_WAVE % 16 == 0, "wave region alignment");
+static_assert(128 * A_VTS * 2 <= 16 * A_SRM * 2, "VT fits in the QL area");
+static_assert(8 * A_WAVE <= 163840, "two workgroups of four waves per CU");
 
 typedef Ops<__bf16> OPB;
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf_ch(uint32_t u, int e) { return e ? bf_hi(u) : bf_lo(u); }
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Width-4 causal conv of 16 rows of this lane's two channels from 19 packed raw
+// rows (the 3 history rows first), bias folded into the first tap.
+__device__ __forceinline__ void conv16(const uint32_t (&x)[19], const float (&wt)[2][4],
+                                       const float (&bs)[2], float (&y)[16][2]) {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float a = fmaf(wt[e][0], bf_ch(x[rr], e), bs[e]);
+            a = fmaf(wt[e][1], bf_ch(x[rr + 1], e), a);
+            a = fmaf(wt[e][2], bf_ch(x[rr + 2], e), a);
+            y[rr][e] = fmaf(wt[e][3], bf_ch(x[rr + 3], e), a);
+        }
+}
+
+// Per-row 1 / sqrt(sum of squares + eps) over the 128 channels (two per lane; a
+// wave-uniform value per row), or 1 without the L2 step.
+__device__ __forceinline__ void l2_scale(const float (&y)[16][2], bool l2, int lane, float (&r)[16]) {
+    if (!l2) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) r[rr] = 1.f;
+        return;
+    }
+    float p[16], s4[4];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) p[rr] = fmaf(y[rr][0], y[rr][0], y[rr][1] * y[rr][1]);
+    rows16_sum(p, s4, lane);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s4[t] = __builtin_amdgcn_rsqf(s4[t] + 1e-6f);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) r[rr] = row_value(s4, rr);
+}
 
 // One 16-token sub-chunk (rows p0 .. p0+15 of sequence n, start s0, length L)
 // by one wave.  All LDS traffic stays inside the wave's region.
@@ -101,32 +148,31 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     __bf16 *sQL = reinterpret_cast<__bf16 *>(lds + A_QL);
     __bf16 *sKI = reinterpret_cast<__bf16 *>(lds + A_KI);
     __bf16 *sKGT = reinterpret_cast<__bf16 *>(lds + A_KGT);
+    __bf16 *sVT = reinterpret_cast<__bf16 *>(lds + A_VT);
     float *sNT = reinterpret_cast<float *>(lds + A_NT);
     __bf16 *sXS = reinterpret_cast<__bf16 *>(lds + A_XS);
     __bf16 *sPS = reinterpret_cast<__bf16 *>(lds + A_PS);
-    __bf16 *sVT = reinterpret_cast<__bf16 *>(lds + A_VT);
-    float *sBET = reinterpret_cast<float *>(lds + A_BET);
     unsigned char *rec = p.ws + ((size_t)h * p.nslots + sub_slot(s0, j, n)) * kRec;
 
-    // ---- raw rows p0-3 .. p0+15 (clamped into the sequence; rare fix-ups below)
+    // ---- raw rows p0-3 .. p0+15 as packed bf16 pairs (clamped into the sequence)
     const T *qg = reinterpret_cast<const T *>(p.q) + (size_t)h * D + c0;
     const T *kg = reinterpret_cast<const T *>(p.k) + (size_t)h * D + c0;
     const T *vg = reinterpret_cast<const T *>(p.v) + (size_t)h * D + c0;
     const T *ag = reinterpret_cast<const T *>(p.gate) + (size_t)h * D + c0;
-    float xq[19][2], xk[19][2], xv[19][2], ga[16][2];
+    uint32_t xq[19], xk[19], xv[19], xa[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const int64_t sp = p0 + rr < L ? p0 + rr : L - 1;
+        xa[rr] = *reinterpret_cast<const uint32_t *>(ag + (s0 + sp) * tokstride);
+    }
 #pragma unroll
     for (int r = 0; r < 19; ++r) {
         int64_t sp = p0 + r - 3;
         sp = sp < 0 ? 0 : (sp >= L ? L - 1 : sp);
         const int64_t off = (s0 + sp) * tokstride;
-        Pair<T>::load(qg + off, xq[r][0], xq[r][1]);
-        Pair<T>::load(kg + off, xk[r][0], xk[r][1]);
-        Pair<T>::load(vg + off, xv[r][0], xv[r][1]);
-    }
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        const int64_t sp = p0 + rr < L ? p0 + rr : L - 1;
-        Pair<T>::load(ag + (s0 + sp) * tokstride, ga[rr][0], ga[rr][1]);
+        xk[r] = *reinterpret_cast<const uint32_t *>(kg + off);
+        xq[r] = *reinterpret_cast<const uint32_t *>(qg + off);
+        xv[r] = *reinterpret_cast<const uint32_t *>(vg + off);
     }
     float beta_r = 0.f;
     if (lane < 16 && p0 + lane < L)
@@ -136,158 +182,122 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)n * 3 * CCH : nullptr;
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
-            float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, v0 = 0.f, v1 = 0.f;
+            uint32_t a = 0u, b = 0u, c = 0u;
             if (csn) {
                 const T *row = csn + (size_t)r * CCH;
-                Pair<T>::load(row + qch, a0, a1);
-                Pair<T>::load(row + kch, b0, b1);
-                Pair<T>::load(row + vch, v0, v1);
+                a = *reinterpret_cast<const uint32_t *>(row + qch);
+                b = *reinterpret_cast<const uint32_t *>(row + kch);
+                c = *reinterpret_cast<const uint32_t *>(row + vch);
             }
-            xq[r][0] = a0; xq[r][1] = a1;
-            xk[r][0] = b0; xk[r][1] = b1;
-            xv[r][0] = v0; xv[r][1] = v1;
+            xq[r] = a; xk[r] = b; xv[r] = c;
         }
     }
-    if (lane < 16) sBET[lane] = beta_r;
-
-    // ---- conv, activation, gate, L2
-    float wq[2][4], wk[2][4], wv[2][4], bq[2], bk[2], bv[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        f32x4 a = *reinterpret_cast<const f32x4 *>(p.w + 4 * (qch + e));
-        f32x4 b = *reinterpret_cast<const f32x4 *>(p.w + 4 * (kch + e));
-        f32x4 cc = *reinterpret_cast<const f32x4 *>(p.w + 4 * (vch + e));
-#pragma unroll
-        for (int t = 0; t < 4; ++t) { wq[e][t] = a[t]; wk[e][t] = b[t]; wv[e][t] = cc[t]; }
-        bq[e] = p.bias ? p.bias[qch + e] : 0.f;
-        bk[e] = p.bias ? p.bias[kch + e] : 0.f;
-        bv[e] = p.bias ? p.bias[vch + e] : 0.f;
-    }
-    float yq[16][2], yk[16][2], yv[16][2];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
+    auto load_w = [&](int ch, float (&wt)[2][4], float (&bs)[2]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            yq[rr][e] = bq[e] + wq[e][0] * xq[rr][e] + wq[e][1] * xq[rr + 1][e] +
-                        wq[e][2] * xq[rr + 2][e] + wq[e][3] * xq[rr + 3][e];
-            yk[rr][e] = bk[e] + wk[e][0] * xk[rr][e] + wk[e][1] * xk[rr + 1][e] +
-                        wk[e][2] * xk[rr + 2][e] + wk[e][3] * xk[rr + 3][e];
-            yv[rr][e] = bv[e] + wv[e][0] * xv[rr][e] + wv[e][1] * xv[rr + 1][e] +
-                        wv[e][2] * xv[rr + 2][e] + wv[e][3] * xv[rr + 3][e];
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(p.w + 4 * (ch + e));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) wt[e][t] = a[t];
+            bs[e] = p.bias ? p.bias[ch + e] : 0.f;
         }
-    if (silu) {
+    };
+    // activation and the rows past the sequence end (zero contribution)
+    auto finish = [&](float (&y)[16][2]) {
+        if (silu) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
+            for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                yq[rr][e] *= sigmoidf_dev(yq[rr][e]);
-                yk[rr][e] *= sigmoidf_dev(yk[rr][e]);
-                yv[rr][e] *= sigmoidf_dev(yv[rr][e]);
-            }
-    }
-    float g2[16][2];
-    if (glog) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) g2[rr][e] = fmaxf(ga[rr][e], p.lb) * kLog2eS;
-    } else {
-        const float lb2 = p.lb * kLog2eS;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) g2[rr][e] = lb2 * sigmoidf_dev(ga[rr][e]);
-    }
-    if (edge) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-            if (p0 + rr >= L) {
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    yq[rr][e] = 0.f; yk[rr][e] = 0.f; yv[rr][e] = 0.f; g2[rr][e] = 0.f;
-                }
-            }
-    }
-    float rq[16], rk[16];
-    if (l2) {
-        float pq[16], pk[16], sq4[4], sk4[4];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            pq[rr] = yq[rr][0] * yq[rr][0] + yq[rr][1] * yq[rr][1];
-            pk[rr] = yk[rr][0] * yk[rr][0] + yk[rr][1] * yk[rr][1];
+                for (int e = 0; e < 2; ++e) y[rr][e] *= sigmoidf_dev(y[rr][e]);
         }
-        rows16_sum(pq, sq4, lane);
-        rows16_sum(pk, sk4, lane);
+        if (edge) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            sq4[t] = __builtin_amdgcn_rsqf(sq4[t] + 1e-6f);
-            sk4[t] = __builtin_amdgcn_rsqf(sk4[t] + 1e-6f);
+            for (int rr = 0; rr < 16; ++rr)
+                if (p0 + rr >= L) { y[rr][0] = 0.f; y[rr][1] = 0.f; }
         }
+    };
+    float bt[16];  // beta per row, wave-uniform
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            rq[rr] = row_value(sq4, rr);
-            rk[rr] = row_value(sk4, rr);
-        }
-    } else {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) { rq[rr] = 1.f; rk[rr] = 1.f; }
-    }
+    for (int rr = 0; rr < 16; ++rr)
+        bt[rr] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(beta_r), rr));
 
-    // ---- decays as running products; operands relative to the sub-chunk start
-    float kl[16][2], ql[16][2], kr[16][2], gsum[2];
+    // ---- gate: log2 decays as running products from the sub-chunk start
+    //   run_r = 2^{b_r},  back_r = 2^{b_last - b_r},  fd = 2^{-b_last}
+    float run[16][2], back[16][2], fd[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        float al[16], run = 1.f, gs = 0.f;
+        float al[16], r = 1.f, gs = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            al[rr] = exp2_fast(g2[rr][e]);
-            gs += g2[rr][e];
-            run *= al[rr];
-            const float kn = yk[rr][e] * rk[rr];
-            ql[rr][e] = yq[rr][e] * rq[rr] * run;
-            kl[rr][e] = kn * run;
-            kr[rr][e] = kn;
+            const float a = bf_ch(xa[rr], e);
+            float g2 = glog ? fmaxf(a, p.lb) * kLog2eS : (p.lb * kLog2eS) * sigmoidf_dev(a);
+            if (edge && p0 + rr >= L) g2 = 0.f;
+            al[rr] = exp2_fast(g2);
+            gs += g2;
+            r *= al[rr];
+            run[rr][e] = r;
         }
-        float back = 1.f;
+        float bk = 1.f;
 #pragma unroll
         for (int rr = 15; rr >= 0; --rr) {
-            kr[rr][e] *= back;
-            back *= al[rr];
+            back[rr][e] = bk;
+            bk *= al[rr];
         }
-        gsum[e] = gs;
+        fd[e] = exp2_fast(-gs);
+        run[15][e] = exp2_fast(gs);  // equal up to rounding; the record takes the direct form
     }
-    const float fd0 = exp2_fast(-gsum[0]), fd1 = exp2_fast(-gsum[1]);
     {
-        f32x2 gm = {exp2_fast(gsum[0]), exp2_fast(gsum[1])};
+        f32x2 gm = {run[15][0], run[15][1]};
         *reinterpret_cast<f32x2 *>(rec + R_GAM + 4 * c0) = gm;
     }
-    float bt[16];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) bt[rr] = sBET[rr];  // wave-local broadcast
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        Pair<__bf16>::store(sKL + rr * A_SRM + c0, kl[rr][0], kl[rr][1]);
-        Pair<__bf16>::store(sQL + rr * A_SRM + c0, ql[rr][0], ql[rr][1]);
-        Pair<__bf16>::store(sKI + rr * A_SRM + c0, kr[rr][0] * fd0, kr[rr][1] * fd1);
-    }
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
+
+    // ---- k: KL = K.2^b, KI = K.2^-b (row-major), beta KL transposed, KD = K.2^(b_last-b)
+    {
+        float wt[2][4], bs[2], y[16][2], rk[16];
+        load_w(kch, wt, bs);
+        conv16(xk, wt, bs, y);
+        finish(y);
+        l2_scale(y, l2, lane, rk);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const int c = c0 + e, r = 4 * q4;
-            OPB::store4(sKGT + c * A_STR + r, bt[r] * kl[r][e], bt[r + 1] * kl[r + 1][e],
-                        bt[r + 2] * kl[r + 2][e], bt[r + 3] * kl[r + 3][e]);
-            // accumulator / A-fragment layouts for pass B: element (token r, channel c)
-            // of tile c / 16 sits in lane (r / 4) * 16 + c % 16, slot r % 4
-            const size_t fo = ((size_t)((c >> 4) * 64 + q4 * 16 + (c & 15)) * 4) * 2;
-            OPB::store4(reinterpret_cast<__bf16 *>(rec + R_KD + fo), kr[r][e], kr[r + 1][e],
-                        kr[r + 2][e], kr[r + 3][e]);
-            OPB::store4(sVT + c * A_STR + r, bt[r] * yv[r][e], bt[r + 1] * yv[r + 1][e],
-                        bt[r + 2] * yv[r + 2][e], bt[r + 3] * yv[r + 3][e]);
+            float kl[4][2], kr[4][2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * q4 + i;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float kn = y[r][e] * rk[r];
+                    kl[i][e] = kn * run[r][e];
+                    kr[i][e] = kn * back[r][e];
+                }
+                Pair<__bf16>::store(sKL + r * A_SRM + c0, kl[i][0], kl[i][1]);
+                Pair<__bf16>::store(sKI + r * A_SRM + c0, kr[i][0] * fd[0], kr[i][1] * fd[1]);
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int c = c0 + e, r = 4 * q4;
+                OPB::store4(sKGT + c * A_STR + r, bt[r] * kl[0][e], bt[r + 1] * kl[1][e],
+                            bt[r + 2] * kl[2][e], bt[r + 3] * kl[3][e]);
+                // accumulator / A-fragment layouts for pass B: element (token r, channel c)
+                // of tile c / 16 sits in lane (r / 4) * 16 + c % 16, slot r % 4
+                const size_t fo = ((size_t)((c >> 4) * 64 + q4 * 16 + (c & 15)) * 4) * 2;
+                OPB::store4(reinterpret_cast<__bf16 *>(rec + R_KD + fo), kr[0][e], kr[1][e],
+                            kr[2][e], kr[3][e]);
+            }
         }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // ---- q: QL = Q.2^b (row-major)
+    {
+        float wt[2][4], bs[2], y[16][2], rq[16];
+        load_w(qch, wt, bs);
+        conv16(xq, wt, bs, y);
+        finish(y);
+        l2_scale(y, l2, lane, rq);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            Pair<__bf16>::store(sQL + rr * A_SRM + c0, y[rr][0] * rq[rr] * run[rr][0],
+                                y[rr][1] * rq[rr] * run[rr][1]);
+    }
+    wave_sync_lds();
 
     // ---- decayed Grams over the sub-chunk (one 16 x 16 tile each)
     {
@@ -296,7 +306,8 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rl = 4 * g4 + i, sl = m16;
-            sNT[sl * 16 + rl] = (sl < rl) ? a[i] * sBET[rl] : 0.f;
+            const float brl = __shfl(beta_r, rl);  // beta of row rl (lanes 0..15 hold them)
+            sNT[sl * 16 + rl] = (sl < rl) ? a[i] * brl : 0.f;
             sPS[rl * A_STR + sl] = (__bf16)((sl <= rl) ? pq[i] : 0.f);
         }
     }
@@ -307,10 +318,23 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         bf16x8 f = join8(*reinterpret_cast<const bf16x4 *>(row), *reinterpret_cast<const bf16x4 *>(row + 16));
         *reinterpret_cast<bf16x8 *>(rec + R_QG + ((size_t)t * 64 + lane) * 16) = f;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();
 
+    // ---- v: beta V transposed into the dead QL area
+    {
+        float wt[2][4], bs[2], y[16][2];
+        load_w(vch, wt, bs);
+        conv16(xv, wt, bs, y);
+        finish(y);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int r = 4 * q4;
+                OPB::store4(sVT + (c0 + e) * A_VTS + r, bt[r] * y[r][e], bt[r + 1] * y[r + 1][e],
+                            bt[r + 2] * y[r + 2][e], bt[r + 3] * y[r + 3][e]);
+            }
+    }
     // ---- X = (I + N)^-1, N strictly lower (stored transposed): right-looking
     if (lane < 16) {
         float x[16];
@@ -325,57 +349,53 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 #pragma unroll
         for (int i = 0; i < 16; ++i) sXS[i * A_STR + lane] = (__bf16)x[i];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();
     *reinterpret_cast<bf16x4 *>(rec + R_PP + (size_t)lane * 8) =
         *reinterpret_cast<const bf16x4 *>(sPS + m16 * A_STR + 4 * g4);
 
     // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL
     // area; U0 = X diag(beta) V straight to the record in accumulator layout
-    const bf16x4 xa = *reinterpret_cast<const bf16x4 *>(sXS + m16 * A_STR + 4 * g4);
+    const bf16x4 xfr = *reinterpret_cast<const bf16x4 *>(sXS + m16 * A_STR + 4 * g4);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
         const int col = 16 * nt + m16;
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 wr = mma_k16(xa, OPB::load4raw(sKGT + col * A_STR + 4 * g4), z);
-        const f32x4 ur = mma_k16(xa, OPB::load4raw(sVT + col * A_STR + 4 * g4), z);
+        const f32x4 wr = mma_k16(xfr, OPB::load4raw(sKGT + col * A_STR + 4 * g4), z);
+        const f32x4 ur = mma_k16(xfr, OPB::load4raw(sVT + col * A_VTS + 4 * g4), z);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sKL[(4 * g4 + i) * A_SRM + col] = (__bf16)(-wr[i]);
         *reinterpret_cast<bf16x4 *>(rec + R_U0 + ((size_t)nt * 64 + lane) * 8) = pack4(ur);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const __bf16 *row = sKL + m16 * A_SRM + 32 * t + 4 * g4;
         bf16x8 f = join8(*reinterpret_cast<const bf16x4 *>(row), *reinterpret_cast<const bf16x4 *>(row + 16));
         *reinterpret_cast<bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16) = f;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();  // the region is reused by this wave's next sub-chunk
 }
 
-__global__ void __launch_bounds__(256, 1) intra_kernel(SplitParams p) {
+// One wave per workspace slot.  The slots of sequence n start at
+// base(n) = start_n / 16 + n (strictly increasing in n); slot base(n) + j holds
+// sub-chunk j of sequence n, and slots past the sequence's last sub-chunk are unused.
+__global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_a[];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int h = blockIdx.y;
-    const int64_t b0 = (int64_t)blockIdx.x * 64, b1 = b0 + 64;
-    unsigned char *lds = smem_a + w * A_WAVE;
-    // sub-chunks (aligned to sequence starts) that begin inside [b0, b1), dealt
-    // round-robin to the four waves
-    int n = p.cu ? find_seq(p.cu, p.num_seqs, b0) : (int)(b0 / (p.total / p.num_seqs));
-    int count = 0;
-    for (; n < p.num_seqs; ++n) {
-        int64_t s0, L;
-        seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
-        if (s0 >= b1) break;
-        if (L == 0) continue;
-        int64_t j = s0 >= b0 ? 0 : (b0 - s0 + 15) / 16;
-        for (; s0 + 16 * j < b1 && 16 * j < L; ++j, ++count)
-            if ((count & 3) == w) intra_sub_chunk(p, lds, n, h, s0, L, j, lane);
+    const int64_t slot = (int64_t)blockIdx.x * 4 + w;
+    if (slot >= p.nslots) return;
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        int64_t sm, lm;
+        seq_bounds(p.cu, p.total, p.num_seqs, mid, sm, lm);
+        if (sm / 16 + mid <= slot) lo = mid; else hi = mid - 1;
     }
+    int64_t s0, L;
+    seq_bounds(p.cu, p.total, p.num_seqs, lo, s0, L);
+    const int64_t j = slot - (s0 / 16 + lo);
+    if (16 * j >= L) return;
+    intra_sub_chunk(p, smem_a + w * A_WAVE, lo, h, s0, L, j, lane);
 }
 
 // Pass B geometry: NTW consumer waves of 16 dv columns each plus two producer
@@ -576,7 +596,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 4 * A_WAVE);
         });
         if (attr != hipSuccess) return attr;
-        dim3 grid((unsigned)((a->total_tokens + 63) / 64), (unsigned)a->num_heads);
+        dim3 grid((unsigned)((sp.nslots + 3) / 4), (unsigned)a->num_heads);
         hipLaunchKernelGGL(intra_kernel, grid, dim3(256), 4 * A_WAVE, s, sp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
