@@ -97,6 +97,127 @@ short_conv_kernel(const T *__restrict__ x, T *__restrict__ y, int64_t total, int
     }
 }
 
+// Vector path: each thread owns 16 bytes of channels (8 bf16 or 4 fp32) and a
+// run of kVecTokens tokens.  A run whose window (3 history rows + the run) lies
+// inside one sequence loads all its rows up front with 16-byte non-temporal
+// loads; runs that touch a sequence start or end take the per-token path.
+constexpr int kVecTokens = 16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Vec16;
+template <> struct Vec16<__bf16> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ void unpack(u32x4 r, float (&v)[8]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(r[i] << 16);
+            v[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ u32x4 pack(const float (&v)[8]) {
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16x2 p2 = {(__bf16)v[2 * i], (__bf16)v[2 * i + 1]};
+            r[i] = __builtin_bit_cast(uint32_t, p2);
+        }
+        return r;
+    }
+};
+template <> struct Vec16<float> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ void unpack(u32x4 r, float (&v)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r[i]);
+    }
+    static __device__ __forceinline__ u32x4 pack(const float (&v)[4]) {
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(v[i]);
+        return r;
+    }
+};
+
+template <typename T, bool SILU>
+__global__ void __launch_bounds__(kConvThreads)
+short_conv_vec_kernel(const T *__restrict__ x, T *__restrict__ y, int64_t total, int C,
+                      const float *__restrict__ w, const float *__restrict__ bias,
+                      const T *__restrict__ cs_in, const int32_t *__restrict__ cu, int num_seqs) {
+    typedef Vec16<T> V;
+    constexpr int NV = V::N;
+    // flat grid, channel blocks fastest: workgroups in flight together cover whole rows
+    const int nblk = (C / NV + kConvThreads - 1) / kConvThreads;
+    const int64_t run = blockIdx.x / nblk;
+    const int c = NV * ((int)(blockIdx.x - run * nblk) * kConvThreads + threadIdx.x);
+    if (c >= C) return;
+    const int64_t t0 = run * kVecTokens;
+    const int64_t t1 = min(total, t0 + (int64_t)kVecTokens);
+    float wt[NV][4], bs[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(w + 4 * (c + i));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wt[i][j] = a[j];
+        bs[i] = bias ? bias[c + i] : 0.f;
+    }
+    auto emit = [&](int64_t t, const float (&h0)[NV], const float (&h1)[NV], const float (&h2)[NV],
+                    const float (&cur)[NV]) {
+        float o[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float a = fmaf(wt[i][0], h0[i], bs[i]);
+            a = fmaf(wt[i][1], h1[i], a);
+            a = fmaf(wt[i][2], h2[i], a);
+            a = fmaf(wt[i][3], cur[i], a);
+            if (SILU) a *= sigmoidf_dev(a);
+            o[i] = a;
+        }
+        __builtin_nontemporal_store(V::pack(o), reinterpret_cast<u32x4 *>(y + t * C + c));
+    };
+    int n = cu ? find_seq(cu, num_seqs, t0) : (int)(t0 / (total / num_seqs));
+    int64_t s0, len;
+    seq_bounds(cu, total, num_seqs, n, s0, len);
+    if (t0 - 3 >= s0 && t1 <= s0 + len && t1 - t0 == kVecTokens) {
+        u32x4 raw[kVecTokens + 3];
+#pragma unroll
+        for (int r = 0; r < kVecTokens + 3; ++r)
+            raw[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + (t0 - 3 + r) * C + c));
+#pragma unroll
+        for (int r = 0; r < kVecTokens; ++r) {
+            float h0[NV], h1[NV], h2[NV], cur[NV];
+            V::unpack(raw[r], h0);
+            V::unpack(raw[r + 1], h1);
+            V::unpack(raw[r + 2], h2);
+            V::unpack(raw[r + 3], cur);
+            emit(t0 + r, h0, h1, h2, cur);
+        }
+        return;
+    }
+    // per-token path: history from this sequence, its conv state, or zeros
+    auto row = [&](int64_t p, float (&v)[NV]) {
+        if (p >= s0) {
+            V::unpack(*reinterpret_cast<const u32x4 *>(x + p * C + c), v);
+        } else if (cs_in) {
+            V::unpack(*reinterpret_cast<const u32x4 *>(cs_in + ((int64_t)n * 3 + (3 + (p - s0))) * C + c), v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) v[i] = 0.f;
+        }
+    };
+    for (int64_t t = t0; t < t1; ++t) {
+        while (t >= s0 + len) {  // next sequence (empty ones are skipped)
+            ++n;
+            seq_bounds(cu, total, num_seqs, n, s0, len);
+        }
+        float h0[NV], h1[NV], h2[NV], cur[NV];
+        row(t - 3, h0);
+        row(t - 2, h1);
+        row(t - 1, h2);
+        row(t, cur);
+        emit(t, h0, h1, h2, cur);
+    }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(kConvThreads)
 conv_tail_kernel(const T *__restrict__ s0p, const T *__restrict__ s1p, const T *__restrict__ s2p,
@@ -131,6 +252,22 @@ static hipError_t short_conv_t(const void *x, void *y, int64_t T_, int C, const 
                                const float *b, const void *cs_in, const int32_t *cu, int N,
                                bool silu, hipStream_t s) {
     if (T_ == 0) return hipSuccess;
+    constexpr int NV = Vec16<T>::N;
+    const int64_t nblk_v = (C / NV + kConvThreads - 1) / kConvThreads;
+    const int64_t items_v = ((T_ + kVecTokens - 1) / kVecTokens) * nblk_v * kConvThreads;
+    const bool vec = (C % NV) == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)y % 16) == 0 &&
+                     (cs_in == nullptr || ((uintptr_t)cs_in % 16) == 0) && ((uintptr_t)w % 16) == 0 &&
+                     items_v < (int64_t(1) << 32);  // one flat grid dimension
+    if (vec) {
+        dim3 grid((unsigned)(items_v / kConvThreads));
+        if (silu)
+            hipLaunchKernelGGL((short_conv_vec_kernel<T, true>), grid, dim3(kConvThreads), 0, s,
+                               (const T *)x, (T *)y, T_, C, w, b, (const T *)cs_in, cu, N);
+        else
+            hipLaunchKernelGGL((short_conv_vec_kernel<T, false>), grid, dim3(kConvThreads), 0, s,
+                               (const T *)x, (T *)y, T_, C, w, b, (const T *)cs_in, cu, N);
+        return hipGetLastError();
+    }
     // tokens on x (up to 2^31 blocks), channel pairs on y
     dim3 grid((unsigned)((T_ + kConvTokens - 1) / kConvTokens),
               (unsigned)(((C + 1) / 2 + kConvThreads - 1) / kConvThreads));

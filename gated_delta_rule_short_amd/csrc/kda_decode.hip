@@ -47,12 +47,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
     __shared__ float s_red[2][3];
     __shared__ f32x4 s_part[4][32][2];
 
-    // 1. issue the state loads (independent of the prologue)
+    // 1. issue the state loads (independent of the prologue).  The state is
+    // streamed exactly once each way: non-temporal loads and stores keep it from
+    // displacing the small, reused operands in L2.
     float *S = p.state + (size_t)pr * D * D;
     f32x4 st[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m)
-        st[m] = *reinterpret_cast<const f32x4 *>(S + (size_t)(rg + 8 * m) * D + 4 * cg);
+        st[m] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4 *>(S + (size_t)(rg + 8 * m) * D + 4 * cg));
 
     // 2. prologue: conv (and cache shift), L2 of q and k, gate
     const int CC = 3 * H * D;
@@ -148,7 +151,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
         st[m] += krow[m] * u;
-        *reinterpret_cast<f32x4 *>(S + (size_t)(rg + 8 * m) * D + 4 * cg) = st[m];
+        __builtin_nontemporal_store(st[m], reinterpret_cast<f32x4 *>(S + (size_t)(rg + 8 * m) * D + 4 * cg));
     }
 }
 

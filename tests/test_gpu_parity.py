@@ -67,6 +67,45 @@ def test_short_conv_matches_oracle(dtype, silu, with_state):
     np.testing.assert_array_equal(to_np(cso), ref_cs)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("silu", [False, True])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_short_conv_vector_path_matches_oracle(dtype, silu, with_state):
+    """Channels a multiple of 16 bytes: the 16-byte path, with runs that sit inside a
+    sequence, runs that straddle sequence starts and ends, and a partial channel block."""
+    g = torch.Generator(device="cpu").manual_seed(5)
+    lengths = [37, 0, 1, 2, 3, 100, 64, 5, 40, 19]
+    C = 520
+    cu = KI.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    x = torch.randn(T, C, generator=g).to(dtype)
+    w = torch.randn(C, 4, generator=g) * 0.5
+    b = torch.randn(C, generator=g) * 0.1
+    cs = torch.randn(len(lengths), 3, C, generator=g).to(dtype) if with_state else None
+    y, cso = kda.kda_short_conv(x.to(DEV), w.to(DEV), cu_seqlens=cu.to(DEV), cu_seqlens_host=cu,
+                                bias=b.to(DEV), conv_state_in=None if cs is None else cs.to(DEV),
+                                conv_state_out=True, silu=silu)
+    torch.cuda.synchronize()
+    ref, ref_cs = oracle.short_conv(x, w, cu, bias=b, conv_state_in=cs, silu=silu)
+    if dtype == torch.float32:
+        np.testing.assert_allclose(to_np(y), ref, rtol=1e-5, atol=1e-5)
+    else:
+        np.testing.assert_allclose(to_np(y), ref, rtol=2 ** -7, atol=1e-6)
+    np.testing.assert_array_equal(to_np(cso), ref_cs)
+
+
+def test_short_conv_vector_path_long_dense():
+    """A long dense batch (3 sequences x 1000 tokens, 2048 channels): mostly full runs."""
+    g = torch.Generator(device="cpu").manual_seed(6)
+    N, L, C = 3, 1000, 2048
+    x = torch.randn(N * L, C, generator=g).to(torch.bfloat16)
+    w = torch.randn(C, 4, generator=g) * 0.5
+    ref, _ = oracle.short_conv(x, w, KI.cu_from_lengths([L] * N))
+    y = kda.kda_short_conv(x.to(DEV), w.to(DEV), num_seqs=N)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_np(y), ref, rtol=2 ** -7, atol=1e-6)
+
+
 def test_short_conv_dense_odd_channels_and_in_place_state():
     g = torch.Generator(device="cpu").manual_seed(4)
     N, L, C = 3, 21, 33
