@@ -178,6 +178,17 @@ __device__ __forceinline__ bf16x8 join8(bf16x4 lo, bf16x4 hi) {
     return r;
 }
 
+// bf16, K = 16 issued as a K = 32 product whose upper K half is zero.  On gfx950
+// an accumulator must not pass between the 16x16x32 and 16x16x16 forms without
+// at least five wait states (measured; the compiler inserts none for that pair),
+// so every accumulation chain that also holds K = 32 steps uses this form for its
+// K = 16 steps.  The plain 16x16x16 form stays where the accumulator starts from
+// zero or a vector result and ends in vector reads.
+__device__ __forceinline__ f32x4 mma_k16w(bf16x4 a, bf16x4 b, f32x4 c) {
+    const bf16x4 z = {};
+    return mma_k32(join8(a, z), join8(b, z), c);
+}
+
 // Index of the sequence holding token t: the largest n with cu[n] <= t.
 __device__ __forceinline__ int find_seq(const int32_t *cu, int num_seqs, int64_t t) {
     int lo = 0, hi = num_seqs;

@@ -41,8 +41,8 @@ template <> struct Ops<__bf16> {
                 bf16x4 a0 = *reinterpret_cast<const bf16x4 *>(arow + 16 * kb);
                 bf16x4 a1 = *reinterpret_cast<const bf16x4 *>(arow + 16 * kb + 16);
                 acc = mma_k32(join8(a0, a1), join8(B[kb], B[kb + 1]), acc);
-            } else if (kb < kb1) {
-                acc = mma_k16(*reinterpret_cast<const bf16x4 *>(arow + 16 * kb), B[kb], acc);
+            } else if (kb < kb1) {  // odd trailing block: same MFMA form as the pairs
+                acc = mma_k16w(*reinterpret_cast<const bf16x4 *>(arow + 16 * kb), B[kb], acc);
             }
         }
         return acc;

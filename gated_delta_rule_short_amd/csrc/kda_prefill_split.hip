@@ -398,26 +398,39 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     intra_sub_chunk(p, smem_a + w * A_WAVE, lo, h, s0, L, j, lane);
 }
 
-// Pass B geometry: NTW consumer waves of 16 dv columns each plus two producer
-// waves; NS ring stages of one record's shared part plus the NTW U0 tiles.
+// Pass B geometry.  Per 16-column dv tile two recurrence waves (R, one per
+// half of the 128 dk rows of the state) and one output wave (O), plus two
+// producer waves that fill an NS-stage LDS ring with the records by LDS DMA.
+// A stage holds a record's shared part and the NTW U0 tiles.  Per tile the
+// exchange area passes the bf16 S fragments and U from R to O (double
+// buffered) and the two partial products W S between the R halves.
 template <int NTW> struct ScanGeom {
     static constexpr int kStage = R_U0 + NTW * 512;
     static constexpr int kInst = (kStage + 1023) / 1024;   // DMA instructions per stage
-    static constexpr int kInstP0 = (kInst + 1) / 2;        // producer 0 takes the even ones
-    static constexpr int kInstP1 = kInst / 2;
+    static constexpr int NP = 2;                           // producer waves
+    static constexpr int kInstP0 = (kInst + NP - 1) / NP;  // producer pw takes i = pw mod NP
     static constexpr int NS = NTW == 1 ? 5 : 8;            // two workgroups per CU at NTW = 1
-    static constexpr int kThreads = 64 * (NTW + 2);
-    static constexpr int kLds = NS * kStage;
-    static_assert(kInstP0 * (NS - 2) < 64, "in-flight DMA exceeds the vmcnt range");
+    static constexpr int kWaves = 3 * NTW + NP;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kExSlot = 4096 + 512;             // S fragments + U fragment
+    static constexpr int kExTile = 2 * kExSlot + 2 * 1024; // two slots + the W S partials
+    static constexpr int kExch = NS * kStage;              // exchange area offset
+    static constexpr int kLds = kExch + NTW * kExTile;
+    static constexpr int kMaxLater = NS - 3;
+    static_assert(NS >= 4, "the ring holds the stages of steps j - 1, j, j + 1 and the refill");
+    static_assert(kInstP0 * kMaxLater < 64, "in-flight DMA exceeds the vmcnt range");
+    static_assert(NP >= 1 && NP <= 4 && kLds <= 163840, "producers and LDS");
+    static_assert(NTW == 1 || NTW == 2, "at most two dv tiles per workgroup");
+    static_assert(NTW == 2 || 2 * kLds <= 163840, "two workgroups per CU at NTW = 1");
 };
 
-// Producer wave `pw` moves its share of record j into ring stage `st`.
+// Producer wave `pw` moves its share of a record into ring stage `stage`.
 template <int NTW>
 __device__ __forceinline__ void scan_issue(unsigned char *stage, const unsigned char *rec, int nt0,
                                            int pw, int lane) {
     typedef ScanGeom<NTW> G;
 #pragma unroll
-    for (int i = pw; i < G::kInst; i += 2) {
+    for (int i = pw; i < G::kInst; i += G::NP) {
         const int off = i * 1024 + lane * 16;  // byte within the stage
         if (off < G::kStage) {
             const unsigned char *src =
@@ -427,28 +440,33 @@ __device__ __forceinline__ void scan_issue(unsigned char *stage, const unsigned 
     }
 }
 
-// Producer wait: everything but the DMA of the `later` stages issued after
-// stage j has landed (in-order completion of one wave's vector-memory ops).
-template <int PER, int NSM2>
+// Producer wait: everything but the DMA of the `later` most recently issued
+// stages has landed (in-order completion of one wave's vector-memory ops).
+template <int PER, int MAXL>
 __device__ __forceinline__ void scan_wait(int later) {
-    if (later >= NSM2) wait_vmcnt<PER * NSM2>();
-    else if constexpr (NSM2 > 0) {
-        switch (later) {
-            case 0: wait_vmcnt<0>(); break;
-            case 1: wait_vmcnt<PER * 1>(); break;
-            case 2: wait_vmcnt<PER * 2>(); break;
-            case 3: wait_vmcnt<PER * 3>(); break;
-            case 4: wait_vmcnt<PER * 4>(); break;
-            default: wait_vmcnt<PER * 5>(); break;
-        }
+    static_assert(MAXL <= 8, "cases below");
+    switch (later < MAXL ? later : MAXL) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<PER * 1>(); break;
+        case 2: wait_vmcnt<PER * 2>(); break;
+        case 3: wait_vmcnt<PER * 3>(); break;
+        case 4: wait_vmcnt<PER * 4>(); break;
+        case 5: wait_vmcnt<PER * 5>(); break;
+        case 6: wait_vmcnt<PER * 6>(); break;
+        case 7: wait_vmcnt<PER * 7>(); break;
+        default: wait_vmcnt<PER * 8>(); break;
     }
 }
 
+// Barriers, taken by every wave: B_-1, then per j = 0 .. J the pair B_j, X_j.
+// At B_-1 stage 0 is in LDS; at B_j stage j + 1 is (when j + 1 < J).  During
+// step j the R waves read stages j and j + 1 and meet at X_j to add their
+// halves of W S; O reads stage j - 1; after B_j the producers refill the slot
+// of stage j - 2 with stage j + NS - 2.
 template <int NTW>
-__global__ void __launch_bounds__(ScanGeom<NTW>::kThreads) scan_kernel(SplitParams p) {
+__global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) scan_kernel(SplitParams p) {
     typedef ScanGeom<NTW> G;
     constexpr int D = kHeadDim, NS = G::NS;
-    static_assert(NS - 2 <= 6, "scan_wait covers six later stages");
     extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int m16 = lane & 15, g4 = lane >> 4;
@@ -464,94 +482,162 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads) scan_kernel(SplitPara
     const int nt0 = tile * NTW;
     const unsigned char *rec0 =
         p.ws + ((size_t)h * p.nslots + (J > 0 ? sub_slot(s0, 0, n) : 0)) * kRec;
+    auto stage = [&](int64_t j) { return ring + (j % NS) * G::kStage; };
 
-    if (w >= NTW) {
-        // ---------------- producers
-        const int pw = w - NTW;
-        for (int64_t j = 0; j < NS - 1 && j < J; ++j)
-            scan_issue<NTW>(ring + j * G::kStage, rec0 + (size_t)j * kRec, nt0, pw, lane);
-        for (int64_t j = 0; j < J; ++j) {
-            const int64_t rest = J - 1 - j;
-            const int later = rest < NS - 2 ? (int)rest : NS - 2;
-            if (pw == 0) scan_wait<G::kInstP0, NS - 2>(later);
-            else scan_wait<G::kInstP1, NS - 2>(later);
-            // stage j complete (explicit wait above); every consumer is done with
-            // stage j - 1.  A bare barrier: a fence here would drain all DMA in flight.
-            __builtin_amdgcn_s_barrier();
-            const int64_t jn = j + NS - 1;
-            if (jn < J)
-                scan_issue<NTW>(ring + (jn % NS) * G::kStage, rec0 + (size_t)jn * kRec, nt0, pw, lane);
+    if (w >= 3 * NTW) {
+        // ---------------- producers (a switch below covers up to four)
+        if (J == 0) return;
+        const int pw = w - 3 * NTW;
+        for (int64_t j = 0; j < NS - 2 && j < J; ++j)
+            scan_issue<NTW>(stage(j), rec0 + (size_t)j * kRec, nt0, pw, lane);
+        for (int64_t b = -1; b <= J; ++b) {
+            const int64_t need = b + 1;  // stage that must be in LDS at B_b
+            if (need < J) {
+                int64_t top = b + NS - 3;  // last stage issued before B_b
+                if (top > J - 1) top = J - 1;
+                const int later = (int)(top - need);
+                switch (pw) {  // DMA instructions per stage of this producer
+                    case 0: scan_wait<(G::kInst + G::NP - 1) / G::NP, G::kMaxLater>(later); break;
+                    case 1: scan_wait<(G::kInst + G::NP - 2) / G::NP, G::kMaxLater>(later); break;
+                    case 2: scan_wait<(G::kInst + G::NP - 3) / G::NP, G::kMaxLater>(later); break;
+                    default: scan_wait<(G::kInst + G::NP - 4) / G::NP, G::kMaxLater>(later); break;
+                }
+            }
+            // bare barriers: a fence here would drain all DMA in flight
+            __builtin_amdgcn_s_barrier();  // B_b
+            const int64_t jn = b + NS - 2;
+            if (b >= 0 && jn < J)
+                scan_issue<NTW>(stage(jn), rec0 + (size_t)jn * kRec, nt0, pw, lane);
+            if (b >= 0) __builtin_amdgcn_s_barrier();  // X_b
+        }
+        wait_vmcnt<0>();
+        return;
+    }
+
+    const bool is_r = w < 2 * NTW;
+    const int tw = is_r ? (w >> 1) : w - 2 * NTW;  // tile within the workgroup
+    const int hf = w & 1;                           // R: which half of the dk rows
+    const int nt = nt0 + tw;
+    const int col = 16 * nt + m16;
+    unsigned char *exch = ring + G::kExch + tw * G::kExTile;
+    unsigned char *xu = exch + 2 * G::kExSlot;      // [2][64 lanes][4 floats]
+
+    if (is_r) {
+        // ---------------- recurrence on dk rows 64 hf .. 64 hf + 63:
+        //   U = U0 - W S (halves added through LDS), S = diag(gam) S + Kd^T U
+        f32x4 S[4];
+        if (p.state_in) {
+            const float *sin = p.state_in + (size_t)pr * D * D + col;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[m][i] = sin[(16 * (4 * hf + m) + 4 * g4 + i) * D];
+        } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (J > 0) {
+            barrier_lds();  // B_-1
+            bf16x8 wn[2];
+            bf16x4 u0;
+            {
+                const unsigned char *st = stage(0);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + ((2 * hf + t) * 64 + lane) * 16);
+                u0 = *reinterpret_cast<const bf16x4 *>(st + R_U0 + (tw * 64 + lane) * 8);
+            }
+            for (int64_t j = 0; j < J; ++j) {
+                barrier_lds();  // B_j
+                const unsigned char *st = stage(j);
+                bf16x4 kd[4];
+                f32x4 gam[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int mt = 4 * hf + m;
+                    kd[m] = *reinterpret_cast<const bf16x4 *>(st + R_KD + (mt * 64 + lane) * 8);
+                    gam[m] = *reinterpret_cast<const f32x4 *>(st + R_GAM + (16 * mt + 4 * g4) * 4);
+                }
+                bf16x8 wn_n[2];
+                bf16x4 u0_n = u0;
+                if (j + 1 < J) {
+                    const unsigned char *sn = stage(j + 1);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        wn_n[t] = *reinterpret_cast<const bf16x8 *>(sn + R_WN + ((2 * hf + t) * 64 + lane) * 16);
+                    u0_n = *reinterpret_cast<const bf16x4 *>(sn + R_U0 + (tw * 64 + lane) * 8);
+                }
+                bf16x8 Sp[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) Sp[t] = join8(pack4(S[2 * t]), pack4(S[2 * t + 1]));
+                f32x4 U = {0.f, 0.f, 0.f, 0.f};
+                if (hf == 0) U = f32x4{(float)u0.x, (float)u0.y, (float)u0.z, (float)u0.w};
+#pragma unroll
+                for (int t = 0; t < 2; ++t) U = mma_k32(wn[t], Sp[t], U);
+                unsigned char *ex = exch + (j & 1) * G::kExSlot;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    *reinterpret_cast<bf16x8 *>(ex + (2 * hf + t) * 1024 + lane * 16) = Sp[t];
+                *reinterpret_cast<f32x4 *>(xu + hf * 1024 + lane * 16) = U;
+                barrier_lds();  // X_j
+                U += *reinterpret_cast<const f32x4 *>(xu + (1 - hf) * 1024 + lane * 16);
+                const bf16x4 Ub = pack4(U);
+                if (hf == 0) *reinterpret_cast<bf16x4 *>(ex + 4096 + lane * 8) = Ub;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) S[m] = mma_k16(kd[m], Ub, S[m] * gam[m]);
+                if (j + 1 < J) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) wn[t] = wn_n[t];
+                    u0 = u0_n;
+                }
+            }
+            barrier_lds();  // B_J
+            barrier_lds();  // X_J
+        }
+        if (p.state_out) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * (4 * hf + m) + 4 * g4 + i;
+                    p.state_out[((size_t)pr * D + row) * D + col] = S[m][i];
+                }
         }
         return;
     }
 
-    // ---------------- consumers: one 16-column dv tile each
-    const int nt = nt0 + w;
-    const int col = 16 * nt + m16;
+    // ---------------- output: O = scale ((Q . 2^b) S + P U) of step j - 1
+    if (J == 0) return;
     const int64_t tokstride = (int64_t)H * D;
-    f32x4 S[8];
-    if (p.state_in) {
-        const float *sin = p.state_in + (size_t)pr * D * D + col;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[mt][i] = sin[(16 * mt + 4 * g4 + i) * D];
-    } else {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     __bf16 *op = reinterpret_cast<__bf16 *>(p.o) + (size_t)h * D + col;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t j = 0; j < J; ++j) {
-        barrier_lds();
-        const unsigned char *st = ring + (j % NS) * G::kStage;
-        bf16x8 wn[4], qg[4];
-        bf16x4 kd[8];
-        f32x4 gam[8];
+    barrier_lds();  // B_-1
+    for (int64_t j = 0; j <= J; ++j) {
+        barrier_lds();  // B_j
+        if (j > 0) {
+            const int64_t jo = j - 1;
+            const unsigned char *st = stage(jo);
+            const unsigned char *ex = exch + (jo & 1) * G::kExSlot;
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + (t * 64 + lane) * 16);
-            qg[t] = *reinterpret_cast<const bf16x8 *>(st + R_QG + (t * 64 + lane) * 16);
-        }
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            kd[mt] = *reinterpret_cast<const bf16x4 *>(st + R_KD + (mt * 64 + lane) * 8);
-            gam[mt] = *reinterpret_cast<const f32x4 *>(st + R_GAM + (16 * mt + 4 * g4) * 4);
-        }
-        const bf16x4 pp = *reinterpret_cast<const bf16x4 *>(st + R_PP + lane * 8);
-        const bf16x4 u0 = *reinterpret_cast<const bf16x4 *>(st + R_U0 + (w * 64 + lane) * 8);
-
-        bf16x4 Sb[8];
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) Sb[mt] = pack4(S[mt]);
-        f32x4 U = {(float)u0.x, (float)u0.y, (float)u0.z, (float)u0.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) U = mma_k32(wn[t], join8(Sb[2 * t], Sb[2 * t + 1]), U);
-        f32x4 O = z;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) O = mma_k32(qg[t], join8(Sb[2 * t], Sb[2 * t + 1]), O);
-        const bf16x4 Ub = pack4(U);
-        O = mma_k16(pp, Ub, O);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) S[mt] = mma_k16(kd[mt], Ub, S[mt] * gam[mt]);
-        const int64_t r0 = 16 * j + 4 * g4;
-        if (r0 + 3 < L) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (r0 + i < L) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
-        }
-    }
-    if (p.state_out) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * mt + 4 * g4 + i;
-                p.state_out[((size_t)pr * D + row) * D + col] = S[mt][i];
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8 qg = *reinterpret_cast<const bf16x8 *>(st + R_QG + (t * 64 + lane) * 16);
+                const bf16x8 sp = *reinterpret_cast<const bf16x8 *>(ex + t * 1024 + lane * 16);
+                O = mma_k32(qg, sp, O);
             }
+            const bf16x4 pp = *reinterpret_cast<const bf16x4 *>(st + R_PP + lane * 8);
+            const bf16x4 ub = *reinterpret_cast<const bf16x4 *>(ex + 4096 + lane * 8);
+            O = mma_k16w(pp, ub, O);  // the accumulator comes from K = 32 steps
+            const int64_t r0 = 16 * jo + 4 * g4;
+            if (r0 + 3 < L) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (r0 + i < L) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
+            }
+        }
+        barrier_lds();  // X_j
     }
 }
 
@@ -586,7 +672,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
     sp.num_seqs = a->num_seqs; sp.H = a->num_heads;
     sp.scale = a->scale; sp.lb = a->gate_lower_bound; sp.flags = a->flags;
     sp.pairs = a->num_seqs * a->num_heads;
-    if (dv_tile > 64) dv_tile = 64;  // four waves of 16 dv columns per workgroup
+    if (dv_tile > 32) dv_tile = 32;  // at most two dv tiles of 16 columns per workgroup
     sp.tiles = kHeadDim / dv_tile;
     if (a->total_tokens > 0) {
         static std::once_flag once;
@@ -601,11 +687,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    switch (dv_tile) {
-        case 16: return launch_scan<1>(sp, s);
-        case 32: return launch_scan<2>(sp, s);
-        default: return launch_scan<4>(sp, s);
-    }
+    return dv_tile == 16 ? launch_scan<1>(sp, s) : launch_scan<2>(sp, s);
 }
 
 }  // namespace kda
