@@ -408,7 +408,9 @@ template <int NTW> struct ScanGeom {
     static constexpr int kStage = R_U0 + NTW * 512;
     static constexpr int kInst = (kStage + 1023) / 1024;   // DMA instructions per stage
     static constexpr int NP = 2;                           // producer waves
-    static constexpr int kInstP0 = (kInst + NP - 1) / NP;  // producer pw takes i = pw mod NP
+    // DMA instructions of producer pw per stage (it takes i = pw mod NP)
+    static constexpr int inst_of(int pw) { return (kInst + NP - 1 - pw) / NP; }
+    static constexpr int kInstP0 = inst_of(0);
     static constexpr int NS = NTW == 1 ? 5 : 8;            // two workgroups per CU at NTW = 1
     static constexpr int kWaves = 3 * NTW + NP;
     static constexpr int kThreads = 64 * kWaves;
@@ -421,7 +423,7 @@ template <int NTW> struct ScanGeom {
     static_assert(kInstP0 * kMaxLater < 64, "in-flight DMA exceeds the vmcnt range");
     static_assert(NP >= 1 && NP <= 4 && kLds <= 163840, "producers and LDS");
     static_assert(NTW == 1 || NTW == 2, "at most two dv tiles per workgroup");
-    static_assert(NTW == 2 || 2 * kLds <= 163840, "two workgroups per CU at NTW = 1");
+    static_assert(NTW != 1 || 2 * kLds <= 163840, "two workgroups per CU at NTW = 1");
 };
 
 // Producer wave `pw` moves its share of a record into ring stage `stage`.
@@ -444,17 +446,19 @@ __device__ __forceinline__ void scan_issue(unsigned char *stage, const unsigned 
 // stages has landed (in-order completion of one wave's vector-memory ops).
 template <int PER, int MAXL>
 __device__ __forceinline__ void scan_wait(int later) {
-    static_assert(MAXL <= 8, "cases below");
+    static_assert(MAXL <= 8 && PER * MAXL < 64, "cases below; the vmcnt range");
+    // cases above MAXL are unreachable; their counts are clamped only to compile
+    constexpr auto c = [](int k) { return PER * k < 64 ? PER * k : 63; };
     switch (later < MAXL ? later : MAXL) {
         case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<PER * 1>(); break;
-        case 2: wait_vmcnt<PER * 2>(); break;
-        case 3: wait_vmcnt<PER * 3>(); break;
-        case 4: wait_vmcnt<PER * 4>(); break;
-        case 5: wait_vmcnt<PER * 5>(); break;
-        case 6: wait_vmcnt<PER * 6>(); break;
-        case 7: wait_vmcnt<PER * 7>(); break;
-        default: wait_vmcnt<PER * 8>(); break;
+        case 1: wait_vmcnt<c(1)>(); break;
+        case 2: wait_vmcnt<c(2)>(); break;
+        case 3: wait_vmcnt<c(3)>(); break;
+        case 4: wait_vmcnt<c(4)>(); break;
+        case 5: wait_vmcnt<c(5)>(); break;
+        case 6: wait_vmcnt<c(6)>(); break;
+        case 7: wait_vmcnt<c(7)>(); break;
+        default: wait_vmcnt<c(8)>(); break;
     }
 }
 
@@ -497,10 +501,10 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                 if (top > J - 1) top = J - 1;
                 const int later = (int)(top - need);
                 switch (pw) {  // DMA instructions per stage of this producer
-                    case 0: scan_wait<(G::kInst + G::NP - 1) / G::NP, G::kMaxLater>(later); break;
-                    case 1: scan_wait<(G::kInst + G::NP - 2) / G::NP, G::kMaxLater>(later); break;
-                    case 2: scan_wait<(G::kInst + G::NP - 3) / G::NP, G::kMaxLater>(later); break;
-                    default: scan_wait<(G::kInst + G::NP - 4) / G::NP, G::kMaxLater>(later); break;
+                    case 0: scan_wait<G::inst_of(0), G::kMaxLater>(later); break;
+                    case 1: scan_wait<G::inst_of(1), G::kMaxLater>(later); break;
+                    case 2: scan_wait<G::inst_of(2), G::kMaxLater>(later); break;
+                    default: scan_wait<G::inst_of(3), G::kMaxLater>(later); break;
                 }
             }
             // bare barriers: a fence here would drain all DMA in flight
