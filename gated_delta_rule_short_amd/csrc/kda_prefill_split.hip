@@ -31,6 +31,12 @@
 #include "kda_internal.h"
 #include "kda_mma.h"
 
+// Producer waves of the pass-B workgroup (LDS DMA issue is per wave, so more
+// waves deliver records faster; four measured best on gfx950).
+#ifndef KDA_SCAN_PRODUCERS
+#define KDA_SCAN_PRODUCERS 4
+#endif
+
 namespace kda {
 
 namespace {
@@ -398,33 +404,54 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     intra_sub_chunk(p, smem_a + w * A_WAVE, lo, h, s0, L, j, lane);
 }
 
-// Pass B geometry.  Per 16-column dv tile two recurrence waves (R, one per
-// half of the 128 dk rows of the state) and one output wave (O), plus two
-// producer waves that fill an NS-stage LDS ring with the records by LDS DMA.
-// A stage holds a record's shared part and the NTW U0 tiles.  Per tile the
-// exchange area passes the bf16 S fragments and U from R to O (double
-// buffered) and the two partial products W S between the R halves.
+// Pass B geometry.  Per 16-column dv tile one recurrence wave (R: all 128 dk
+// rows of the state in registers) and one output wave (O), plus NP producer
+// waves that fill an NS-stage LDS ring with the records by LDS DMA.  A stage
+// holds a record's shared part and the NTW U0 tiles.  Per tile a double
+// buffered exchange slot passes the bf16 S fragments and U from R to O.  The
+// ring takes whatever LDS the exchange leaves (half of it at NTW = 1, where two
+// workgroups share a CU), up to 10 stages.
 template <int NTW> struct ScanGeom {
     static constexpr int kStage = R_U0 + NTW * 512;
     static constexpr int kInst = (kStage + 1023) / 1024;   // DMA instructions per stage
-    static constexpr int NP = 2;                           // producer waves
+    static constexpr int NP = KDA_SCAN_PRODUCERS;          // producer waves
     // DMA instructions of producer pw per stage (it takes i = pw mod NP)
     static constexpr int inst_of(int pw) { return (kInst + NP - 1 - pw) / NP; }
     static constexpr int kInstP0 = inst_of(0);
-    static constexpr int NS = NTW == 1 ? 5 : 8;            // two workgroups per CU at NTW = 1
-    static constexpr int kWaves = 3 * NTW + NP;
+    static constexpr int kWaves = 2 * NTW + NP;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kExSlot = 4096 + 512;             // S fragments + U fragment
-    static constexpr int kExTile = 2 * kExSlot + 2 * 1024; // two slots + the W S partials
+    static constexpr int kExTile = 2 * kExSlot;
+    static constexpr int kBudget = NTW == 1 ? 81920 : 163840;
+    static constexpr int NSfit = (kBudget - NTW * kExTile) / kStage;
+    static constexpr int NS = NSfit < 10 ? NSfit : 10;
     static constexpr int kExch = NS * kStage;              // exchange area offset
     static constexpr int kLds = kExch + NTW * kExTile;
     static constexpr int kMaxLater = NS - 3;
     static_assert(NS >= 4, "the ring holds the stages of steps j - 1, j, j + 1 and the refill");
     static_assert(kInstP0 * kMaxLater < 64, "in-flight DMA exceeds the vmcnt range");
-    static_assert(NP >= 1 && NP <= 4 && kLds <= 163840, "producers and LDS");
+    static_assert(NP >= 1 && NP <= 8 && kWaves <= 16 && kLds <= kBudget, "producers and LDS");
     static_assert(NTW == 1 || NTW == 2, "at most two dv tiles per workgroup");
-    static_assert(NTW != 1 || 2 * kLds <= 163840, "two workgroups per CU at NTW = 1");
 };
+
+// Lane K of each 16-lane row, broadcast to the whole row (DPP row_newbcast;
+// every source lane exists, so bound_ctrl changes nothing but lets the
+// compiler fold the move into the consuming multiply).
+template <int K>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + K, 0xf, 0xf, true));
+}
+
+// s (dk tile M of the state, rows 16 M + 4 g4 + i) *= gam of those rows.  gv[q]
+// holds, in lane (c, g4), gam of row 64 q + 16 (c >> 2) + 4 g4 + (c & 3), so the
+// factor of row 16 M + 4 g4 + i sits in lane 4 (M & 3) + i of the same row.
+template <int M>
+__device__ __forceinline__ void decay_tile(f32x4 &s, const float (&gv)[2]) {
+    s[0] *= row_bcast<4 * (M & 3) + 0>(gv[M >> 2]);
+    s[1] *= row_bcast<4 * (M & 3) + 1>(gv[M >> 2]);
+    s[2] *= row_bcast<4 * (M & 3) + 2>(gv[M >> 2]);
+    s[3] *= row_bcast<4 * (M & 3) + 3>(gv[M >> 2]);
+}
 
 // Producer wave `pw` moves its share of a record into ring stage `stage`.
 template <int NTW>
@@ -462,17 +489,32 @@ __device__ __forceinline__ void scan_wait(int later) {
     }
 }
 
-// Barriers, taken by every wave: B_-1, then per j = 0 .. J the pair B_j, X_j.
-// At B_-1 stage 0 is in LDS; at B_j stage j + 1 is (when j + 1 < J).  During
-// step j the R waves read stages j and j + 1 and meet at X_j to add their
-// halves of W S; O reads stage j - 1; after B_j the producers refill the slot
-// of stage j - 2 with stage j + NS - 2.
+// Producer wave `pw` waits until the stage issued `later` stages before its
+// most recent one has landed (scan_wait with that producer's per-stage count).
+template <int NTW, int K = 0>
+__device__ __forceinline__ void producer_wait(int pw, int later) {
+    typedef ScanGeom<NTW> G;
+    if constexpr (K < G::NP) {
+        if (pw == K) {
+            scan_wait<G::inst_of(K), G::kMaxLater>(later);
+            return;
+        }
+        producer_wait<NTW, K + 1>(pw, later);
+    }
+}
+
+// Barriers, taken by every wave: B_-1, then B_j for j = 0 .. J.  At B_-1
+// stage 0 is in LDS; at B_j stage j + 1 is (when j + 1 < J).  During step j
+// the R waves compute from registers read from stage j and read stage j + 1;
+// O reads stage j - 1 and the S and U fragments of step j - 1; after B_j the
+// producers refill the slot of stage j - 2 with stage j + NS - 2.
 template <int NTW>
 __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) scan_kernel(SplitParams p) {
     typedef ScanGeom<NTW> G;
     constexpr int D = kHeadDim, NS = G::NS;
     extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is uniform: keep it scalar so that role branches stay scalar
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int bid = blockIdx.x;
     const int grp = bid / (8 * p.tiles), rem = bid - grp * 8 * p.tiles;
@@ -486,12 +528,12 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
     const int nt0 = tile * NTW;
     const unsigned char *rec0 =
         p.ws + ((size_t)h * p.nslots + (J > 0 ? sub_slot(s0, 0, n) : 0)) * kRec;
-    auto stage = [&](int64_t j) { return ring + (j % NS) * G::kStage; };
+    auto stage = [&](int64_t j) { return ring + ((uint32_t)j % NS) * G::kStage; };
 
-    if (w >= 3 * NTW) {
-        // ---------------- producers (a switch below covers up to four)
+    if (w >= 2 * NTW) {
+        // ---------------- producers
         if (J == 0) return;
-        const int pw = w - 3 * NTW;
+        const int pw = w - 2 * NTW;
         for (int64_t j = 0; j < NS - 2 && j < J; ++j)
             scan_issue<NTW>(stage(j), rec0 + (size_t)j * kRec, nt0, pw, lane);
         for (int64_t b = -1; b <= J; ++b) {
@@ -499,111 +541,107 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
             if (need < J) {
                 int64_t top = b + NS - 3;  // last stage issued before B_b
                 if (top > J - 1) top = J - 1;
-                const int later = (int)(top - need);
-                switch (pw) {  // DMA instructions per stage of this producer
-                    case 0: scan_wait<G::inst_of(0), G::kMaxLater>(later); break;
-                    case 1: scan_wait<G::inst_of(1), G::kMaxLater>(later); break;
-                    case 2: scan_wait<G::inst_of(2), G::kMaxLater>(later); break;
-                    default: scan_wait<G::inst_of(3), G::kMaxLater>(later); break;
-                }
+                producer_wait<NTW>(pw, (int)(top - need));
             }
-            // bare barriers: a fence here would drain all DMA in flight
+            // a bare barrier: a fence here would drain all DMA in flight
             __builtin_amdgcn_s_barrier();  // B_b
             const int64_t jn = b + NS - 2;
             if (b >= 0 && jn < J)
                 scan_issue<NTW>(stage(jn), rec0 + (size_t)jn * kRec, nt0, pw, lane);
-            if (b >= 0) __builtin_amdgcn_s_barrier();  // X_b
         }
         wait_vmcnt<0>();
         return;
     }
 
-    const bool is_r = w < 2 * NTW;
-    const int tw = is_r ? (w >> 1) : w - 2 * NTW;  // tile within the workgroup
-    const int hf = w & 1;                           // R: which half of the dk rows
+    const bool is_r = w < NTW;
+    const int tw = is_r ? w : w - NTW;  // tile within the workgroup
     const int nt = nt0 + tw;
     const int col = 16 * nt + m16;
     unsigned char *exch = ring + G::kExch + tw * G::kExTile;
-    unsigned char *xu = exch + 2 * G::kExSlot;      // [2][64 lanes][4 floats]
 
     if (is_r) {
-        // ---------------- recurrence on dk rows 64 hf .. 64 hf + 63:
-        //   U = U0 - W S (halves added through LDS), S = diag(gam) S + Kd^T U
-        f32x4 S[4];
+        // ---------------- recurrence on the 128 x 16 state block of tile nt:
+        //   U = U0 - W S, S = diag(gam) S + Kd^T U
+        // S[m] holds rows 16 m + 4 g4 + i of column col (accumulator layout).
+        f32x4 S[8];
         if (p.state_in) {
             const float *sin = p.state_in + (size_t)pr * D * D + col;
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 8; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[m][i] = sin[(16 * (4 * hf + m) + 4 * g4 + i) * D];
+                for (int i = 0; i < 4; ++i) S[m][i] = sin[(16 * m + 4 * g4 + i) * D];
         } else {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         if (J > 0) {
-            barrier_lds();  // B_-1
-            bf16x8 wn[2];
-            bf16x4 u0;
-            {
-                const unsigned char *st = stage(0);
+            // A step's operands, read from the ring one step ahead: W (negated),
+            // Kd, gam (one row per lane, see decay_tile) and this tile's U0.
+            auto load = [&](const unsigned char *st, bf16x8 (&wn)[4], bf16x4 (&kd)[8], float (&gv)[2],
+                            bf16x4 &u0) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + ((2 * hf + t) * 64 + lane) * 16);
+                for (int t = 0; t < 4; ++t)
+                    wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + (t * 64 + lane) * 16);
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    kd[m] = *reinterpret_cast<const bf16x4 *>(st + R_KD + (m * 64 + lane) * 8);
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    gv[q] = *reinterpret_cast<const float *>(
+                        st + R_GAM + (64 * q + 16 * (m16 >> 2) + 4 * g4 + (m16 & 3)) * 4);
                 u0 = *reinterpret_cast<const bf16x4 *>(st + R_U0 + (tw * 64 + lane) * 8);
-            }
-            for (int64_t j = 0; j < J; ++j) {
+            };
+            // One step: operands of step j in the first set; the second set
+            // receives step j + 1's (the loop alternates the two sets).
+            auto step = [&](int64_t j, const bf16x8 (&wn)[4], const bf16x4 (&kd)[8], const float (&gv)[2],
+                            bf16x4 u0, bf16x8 (&wn_n)[4], bf16x4 (&kd_n)[8], float (&gv_n)[2], bf16x4 &u0_n) {
                 barrier_lds();  // B_j
-                const unsigned char *st = stage(j);
-                bf16x4 kd[4];
-                f32x4 gam[4];
+                if (j + 1 < J) load(stage(j + 1), wn_n, kd_n, gv_n, u0_n);
+                bf16x8 Sp[4];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int mt = 4 * hf + m;
-                    kd[m] = *reinterpret_cast<const bf16x4 *>(st + R_KD + (mt * 64 + lane) * 8);
-                    gam[m] = *reinterpret_cast<const f32x4 *>(st + R_GAM + (16 * mt + 4 * g4) * 4);
-                }
-                bf16x8 wn_n[2];
-                bf16x4 u0_n = u0;
-                if (j + 1 < J) {
-                    const unsigned char *sn = stage(j + 1);
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-                        wn_n[t] = *reinterpret_cast<const bf16x8 *>(sn + R_WN + ((2 * hf + t) * 64 + lane) * 16);
-                    u0_n = *reinterpret_cast<const bf16x4 *>(sn + R_U0 + (tw * 64 + lane) * 8);
-                }
-                bf16x8 Sp[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) Sp[t] = join8(pack4(S[2 * t]), pack4(S[2 * t + 1]));
-                f32x4 U = {0.f, 0.f, 0.f, 0.f};
-                if (hf == 0) U = f32x4{(float)u0.x, (float)u0.y, (float)u0.z, (float)u0.w};
-#pragma unroll
-                for (int t = 0; t < 2; ++t) U = mma_k32(wn[t], Sp[t], U);
+                for (int t = 0; t < 4; ++t) Sp[t] = join8(pack4(S[2 * t]), pack4(S[2 * t + 1]));
+                // two independent accumulation chains over the dk quarters
+                f32x4 Ua = {(float)u0.x, (float)u0.y, (float)u0.z, (float)u0.w};
+                f32x4 Uc = {0.f, 0.f, 0.f, 0.f};
+                Ua = mma_k32(wn[0], Sp[0], Ua);
+                Uc = mma_k32(wn[1], Sp[1], Uc);
+                Ua = mma_k32(wn[2], Sp[2], Ua);
+                Uc = mma_k32(wn[3], Sp[3], Uc);
                 unsigned char *ex = exch + (j & 1) * G::kExSlot;
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    *reinterpret_cast<bf16x8 *>(ex + (2 * hf + t) * 1024 + lane * 16) = Sp[t];
-                *reinterpret_cast<f32x4 *>(xu + hf * 1024 + lane * 16) = U;
-                barrier_lds();  // X_j
-                U += *reinterpret_cast<const f32x4 *>(xu + (1 - hf) * 1024 + lane * 16);
-                const bf16x4 Ub = pack4(U);
-                if (hf == 0) *reinterpret_cast<bf16x4 *>(ex + 4096 + lane * 8) = Ub;
+                for (int t = 0; t < 4; ++t) *reinterpret_cast<bf16x8 *>(ex + t * 1024 + lane * 16) = Sp[t];
+                decay_tile<0>(S[0], gv);
+                decay_tile<1>(S[1], gv);
+                decay_tile<2>(S[2], gv);
+                decay_tile<3>(S[3], gv);
+                decay_tile<4>(S[4], gv);
+                decay_tile<5>(S[5], gv);
+                decay_tile<6>(S[6], gv);
+                decay_tile<7>(S[7], gv);
+                const bf16x4 Ub = pack4(Ua + Uc);
+                *reinterpret_cast<bf16x4 *>(ex + 4096 + lane * 8) = Ub;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) S[m] = mma_k16(kd[m], Ub, S[m] * gam[m]);
-                if (j + 1 < J) {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) wn[t] = wn_n[t];
-                    u0 = u0_n;
-                }
+                for (int m = 0; m < 8; ++m) S[m] = mma_k16(kd[m], Ub, S[m]);
+            };
+            bf16x8 wnA[4], wnB[4];
+            bf16x4 kdA[8], kdB[8], u0A, u0B = {};
+            float gvA[2], gvB[2];
+            barrier_lds();  // B_-1
+            load(stage(0), wnA, kdA, gvA, u0A);
+            int64_t j = 0;
+            for (; j + 1 < J; j += 2) {
+                step(j, wnA, kdA, gvA, u0A, wnB, kdB, gvB, u0B);
+                step(j + 1, wnB, kdB, gvB, u0B, wnA, kdA, gvA, u0A);
             }
+            if (j < J) step(j, wnA, kdA, gvA, u0A, wnB, kdB, gvB, u0B);
             barrier_lds();  // B_J
-            barrier_lds();  // X_J
         }
         if (p.state_out) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 8; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * (4 * hf + m) + 4 * g4 + i;
+                    const int row = 16 * m + 4 * g4 + i;
                     p.state_out[((size_t)pr * D + row) * D + col] = S[m][i];
                 }
         }
@@ -641,7 +679,6 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                     if (r0 + i < L) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
             }
         }
-        barrier_lds();  // X_j
     }
 }
 
