@@ -134,22 +134,119 @@ __device__ __forceinline__ void l2_scale(const float (&y)[16][2], bool l2, int l
     for (int rr = 0; rr < 16; ++rr) r[rr] = row_value(s4, rr);
 }
 
-// One 16-token sub-chunk (rows p0 .. p0+15 of sequence n, start s0, length L)
-// by one wave.  All LDS traffic stays inside the wave's region.
-__device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, int n,
-                                                int h, int64_t s0, int64_t L, int64_t j, int lane) {
+// One pass-A task: sub-chunk j (rows 16 j .. 16 j + 15) of sequence n, which
+// starts at token s0 and holds L tokens.
+struct SubTask {
+    int64_t slot, s0, L, j;
+    int n;
+};
+
+// Raw inputs of one sub-chunk for this lane's two channels, as packed bf16
+// pairs: rows p0-3 .. p0+15 of q, k, v (clamped into the sequence; the three
+// rows before a sequence come from the conv state or are zero) and rows p0 ..
+// p0+15 of the gate; beta of row p0 + lane in lanes 0..15.  The gate, k and
+// beta ("early") are needed first and are loaded one sub-chunk ahead; q and v
+// ("late") are loaded when the sub-chunk starts.
+struct EarlyRows {
+    uint32_t xk[19], xa[16];
+    float beta;
+};
+struct LateRows {
+    uint32_t xq[19], xv[19];
+};
+
+// Conv taps and bias of this lane's two q, k and v channels of head h.
+struct ConvW {
+    float w[3][2][4], b[3][2];
+};
+
+__device__ __forceinline__ void load_conv_w(const SplitParams &p, int h, int lane, ConvW &cw) {
+    constexpr int D = kHeadDim;
+    const int c0 = 2 * lane;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        const int ch = t * p.H * D + h * D + c0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(p.w + 4 * (ch + e));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cw.w[t][e][i] = a[i];
+            cw.b[t][e] = p.bias ? p.bias[ch + e] : 0.f;
+        }
+    }
+}
+
+// Row r (-3 .. 15) of the sub-chunk, clamped into the sequence: its element offset.
+__device__ __forceinline__ int64_t raw_row_off(const SubTask &tk, int r, int64_t tokstride) {
+    int64_t sp = 16 * tk.j + r;
+    sp = sp < 0 ? 0 : (sp >= tk.L ? tk.L - 1 : sp);
+    return (tk.s0 + sp) * tokstride;
+}
+
+// The three rows before a sequence for tensor t (0 q, 1 k, 2 v): conv state or zeros.
+__device__ __forceinline__ void load_history(const SplitParams &p, const SubTask &tk, int h, int lane, int t,
+                                             uint32_t (&x)[19]) {
+    constexpr int D = kHeadDim;
+    const int CCH = 3 * p.H * D;
+    const int ch = t * p.H * D + h * D + 2 * lane;
+    const __bf16 *csn = p.cs_in ? reinterpret_cast<const __bf16 *>(p.cs_in) + (size_t)tk.n * 3 * CCH : nullptr;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        x[i] = csn ? *reinterpret_cast<const uint32_t *>(csn + (size_t)i * CCH + ch) : 0u;
+}
+
+__device__ __forceinline__ void load_early(const SplitParams &p, const SubTask &tk, int h, int lane, EarlyRows &r) {
     constexpr int D = kHeadDim;
     typedef __bf16 T;
+    const int64_t tokstride = (int64_t)p.H * D;
+    const int c0 = 2 * lane;
+    const T *kg = reinterpret_cast<const T *>(p.k) + (size_t)h * D + c0;
+    const T *ag = reinterpret_cast<const T *>(p.gate) + (size_t)h * D + c0;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) r.xa[rr] = *reinterpret_cast<const uint32_t *>(ag + raw_row_off(tk, rr, tokstride));
+#pragma unroll
+    for (int i = 0; i < 19; ++i) r.xk[i] = *reinterpret_cast<const uint32_t *>(kg + raw_row_off(tk, i - 3, tokstride));
+    r.beta = 0.f;
+    if (lane < 16 && 16 * tk.j + lane < tk.L)
+        r.beta = to_f32(reinterpret_cast<const T *>(p.beta)[(tk.s0 + 16 * tk.j + lane) * p.H + h]);
+    if (tk.j == 0) load_history(p, tk, h, lane, 1, r.xk);
+}
+
+__device__ __forceinline__ void load_late(const SplitParams &p, const SubTask &tk, int h, int lane, LateRows &r) {
+    constexpr int D = kHeadDim;
+    typedef __bf16 T;
+    const int64_t tokstride = (int64_t)p.H * D;
+    const int c0 = 2 * lane;
+    const T *qg = reinterpret_cast<const T *>(p.q) + (size_t)h * D + c0;
+    const T *vg = reinterpret_cast<const T *>(p.v) + (size_t)h * D + c0;
+#pragma unroll
+    for (int i = 0; i < 19; ++i) {
+        const int64_t off = raw_row_off(tk, i - 3, tokstride);
+        r.xq[i] = *reinterpret_cast<const uint32_t *>(qg + off);
+        r.xv[i] = *reinterpret_cast<const uint32_t *>(vg + off);
+    }
+    if (tk.j == 0) {
+        load_history(p, tk, h, lane, 0, r.xq);
+        load_history(p, tk, h, lane, 2, r.xv);
+    }
+}
+
+// One 16-token sub-chunk by one wave, from its early rows (loaded before) and
+// late rows (loaded here).  After the k block it starts the loads of the next
+// sub-chunk's early rows (when nx is set), so that they land during the rest.
+// All LDS traffic stays inside the wave's region.
+__device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, const SubTask &tk,
+                                                int h, int lane, const EarlyRows &er, const ConvW &cw,
+                                                const SubTask *nx, EarlyRows &ner) {
+    constexpr int D = kHeadDim;
     const int m16 = lane & 15, g4 = lane >> 4;
-    const int H = p.H;
-    const int64_t tokstride = (int64_t)H * D;
+    const int64_t s0 = tk.s0, L = tk.L, j = tk.j;
     const int64_t p0 = 16 * j;
     const bool edge = p0 < 3 || p0 + 16 > L;
     const bool silu = p.flags & KDA_F_SILU;
     const bool l2 = !(p.flags & KDA_F_NO_QK_L2NORM);
     const bool glog = p.flags & KDA_F_GATE_IS_LOG;
     const int c0 = 2 * lane;
-    const int CCH = 3 * H * D;
     __bf16 *sKL = reinterpret_cast<__bf16 *>(lds + A_KL);
     __bf16 *sQL = reinterpret_cast<__bf16 *>(lds + A_QL);
     __bf16 *sKI = reinterpret_cast<__bf16 *>(lds + A_KI);
@@ -158,53 +255,20 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     float *sNT = reinterpret_cast<float *>(lds + A_NT);
     __bf16 *sXS = reinterpret_cast<__bf16 *>(lds + A_XS);
     __bf16 *sPS = reinterpret_cast<__bf16 *>(lds + A_PS);
-    unsigned char *rec = p.ws + ((size_t)h * p.nslots + sub_slot(s0, j, n)) * kRec;
-
-    // ---- raw rows p0-3 .. p0+15 as packed bf16 pairs (clamped into the sequence)
-    const T *qg = reinterpret_cast<const T *>(p.q) + (size_t)h * D + c0;
-    const T *kg = reinterpret_cast<const T *>(p.k) + (size_t)h * D + c0;
-    const T *vg = reinterpret_cast<const T *>(p.v) + (size_t)h * D + c0;
-    const T *ag = reinterpret_cast<const T *>(p.gate) + (size_t)h * D + c0;
-    uint32_t xq[19], xk[19], xv[19], xa[16];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        const int64_t sp = p0 + rr < L ? p0 + rr : L - 1;
-        xa[rr] = *reinterpret_cast<const uint32_t *>(ag + (s0 + sp) * tokstride);
-    }
-#pragma unroll
-    for (int r = 0; r < 19; ++r) {
-        int64_t sp = p0 + r - 3;
-        sp = sp < 0 ? 0 : (sp >= L ? L - 1 : sp);
-        const int64_t off = (s0 + sp) * tokstride;
-        xk[r] = *reinterpret_cast<const uint32_t *>(kg + off);
-        xq[r] = *reinterpret_cast<const uint32_t *>(qg + off);
-        xv[r] = *reinterpret_cast<const uint32_t *>(vg + off);
-    }
-    float beta_r = 0.f;
-    if (lane < 16 && p0 + lane < L)
-        beta_r = to_f32(reinterpret_cast<const T *>(p.beta)[(s0 + p0 + lane) * H + h]);
-    const int qch = h * D + c0, kch = H * D + h * D + c0, vch = 2 * H * D + h * D + c0;
-    if (edge && p0 == 0) {  // the three rows before the sequence: conv state or zeros
-        const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)n * 3 * CCH : nullptr;
-#pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            uint32_t a = 0u, b = 0u, c = 0u;
-            if (csn) {
-                const T *row = csn + (size_t)r * CCH;
-                a = *reinterpret_cast<const uint32_t *>(row + qch);
-                b = *reinterpret_cast<const uint32_t *>(row + kch);
-                c = *reinterpret_cast<const uint32_t *>(row + vch);
-            }
-            xq[r] = a; xk[r] = b; xv[r] = c;
-        }
-    }
-    auto load_w = [&](int ch, float (&wt)[2][4], float (&bs)[2]) {
+    unsigned char *rec = p.ws + ((size_t)h * p.nslots + tk.slot) * kRec;
+    LateRows lr;
+    load_late(p, tk, h, lane, lr);
+    const uint32_t(&xq)[19] = lr.xq;
+    const uint32_t(&xk)[19] = er.xk;
+    const uint32_t(&xv)[19] = lr.xv;
+    const uint32_t(&xa)[16] = er.xa;
+    const float beta_r = er.beta;
+    auto load_w = [&](int t, float (&wt)[2][4], float (&bs)[2]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(p.w + 4 * (ch + e));
 #pragma unroll
-            for (int t = 0; t < 4; ++t) wt[e][t] = a[t];
-            bs[e] = p.bias ? p.bias[ch + e] : 0.f;
+            for (int i = 0; i < 4; ++i) wt[e][i] = cw.w[t][e][i];
+            bs[e] = cw.b[t][e];
         }
     };
     // activation and the rows past the sequence end (zero contribution)
@@ -259,7 +323,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     // ---- k: KL = K.2^b, KI = K.2^-b (row-major), beta KL transposed, KD = K.2^(b_last-b)
     {
         float wt[2][4], bs[2], y[16][2], rk[16];
-        load_w(kch, wt, bs);
+        load_w(1, wt, bs);
         conv16(xk, wt, bs, y);
         finish(y);
         l2_scale(y, l2, lane, rk);
@@ -291,10 +355,11 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
             }
         }
     }
+    if (nx) load_early(p, *nx, h, lane, ner);
     // ---- q: QL = Q.2^b (row-major)
     {
         float wt[2][4], bs[2], y[16][2], rq[16];
-        load_w(qch, wt, bs);
+        load_w(0, wt, bs);
         conv16(xq, wt, bs, y);
         finish(y);
         l2_scale(y, l2, lane, rq);
@@ -329,7 +394,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     // ---- v: beta V transposed into the dead QL area
     {
         float wt[2][4], bs[2], y[16][2];
-        load_w(vch, wt, bs);
+        load_w(2, wt, bs);
         conv16(xv, wt, bs, y);
         finish(y);
 #pragma unroll
@@ -381,27 +446,48 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     }
 }
 
-// One wave per workspace slot.  The slots of sequence n start at
-// base(n) = start_n / 16 + n (strictly increasing in n); slot base(n) + j holds
-// sub-chunk j of sequence n, and slots past the sequence's last sub-chunk are unused.
+// Pass A.  The slots of sequence n start at base(n) = start_n / 16 + n
+// (strictly increasing in n); slot base(n) + j holds sub-chunk j of sequence n,
+// and slots past the sequence's last sub-chunk are unused.  Wave w of block
+// (x, h) takes slots x * 4 + w and x * 4 + w + 4 * gridDim.x of head h (the
+// first valid ones from there), and loads the second one's early rows while it
+// computes the first.  Two slots in straight-line code: a loop over more slots
+// keeps loop-invariant values live and spills.
+__device__ __forceinline__ bool next_task(const SplitParams &p, int64_t slot, int64_t stride, SubTask &tk) {
+    for (; slot < p.nslots; slot += stride) {
+        int lo = 0, hi = p.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            int64_t sm, lm;
+            seq_bounds(p.cu, p.total, p.num_seqs, mid, sm, lm);
+            if (sm / 16 + mid <= slot) lo = mid; else hi = mid - 1;
+        }
+        int64_t s0, L;
+        seq_bounds(p.cu, p.total, p.num_seqs, lo, s0, L);
+        const int64_t j = slot - (s0 / 16 + lo);
+        if (16 * j < L) {
+            tk.slot = slot; tk.s0 = s0; tk.L = L; tk.j = j; tk.n = lo;
+            return true;
+        }
+    }
+    return false;
+}
+
 __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_a[];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int h = blockIdx.y;
-    const int64_t slot = (int64_t)blockIdx.x * 4 + w;
-    if (slot >= p.nslots) return;
-    int lo = 0, hi = p.num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        int64_t sm, lm;
-        seq_bounds(p.cu, p.total, p.num_seqs, mid, sm, lm);
-        if (sm / 16 + mid <= slot) lo = mid; else hi = mid - 1;
-    }
-    int64_t s0, L;
-    seq_bounds(p.cu, p.total, p.num_seqs, lo, s0, L);
-    const int64_t j = slot - (s0 / 16 + lo);
-    if (16 * j >= L) return;
-    intra_sub_chunk(p, smem_a + w * A_WAVE, lo, h, s0, L, j, lane);
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    unsigned char *lds = smem_a + w * A_WAVE;
+    SubTask ta, tb;
+    if (!next_task(p, (int64_t)blockIdx.x * 4 + w, stride, ta)) return;
+    ConvW cw;
+    load_conv_w(p, h, lane, cw);
+    EarlyRows ra, rb;
+    load_early(p, ta, h, lane, ra);
+    const bool hb = next_task(p, ta.slot + stride, stride, tb);
+    intra_sub_chunk(p, lds, ta, h, lane, ra, cw, hb ? &tb : nullptr, rb);
+    if (hb) intra_sub_chunk(p, lds, tb, h, lane, rb, cw, nullptr, ra);
 }
 
 // Pass B geometry.  Per 16-column dv tile one recurrence wave (R: all 128 dk
@@ -723,7 +809,8 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 4 * A_WAVE);
         });
         if (attr != hipSuccess) return attr;
-        dim3 grid((unsigned)((sp.nslots + 3) / 4), (unsigned)a->num_heads);
+        const int64_t gx = (sp.nslots + 7) / 8;  // two slots per wave
+        dim3 grid((unsigned)gx, (unsigned)a->num_heads);
         hipLaunchKernelGGL(intra_kernel, grid, dim3(256), 4 * A_WAVE, s, sp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
