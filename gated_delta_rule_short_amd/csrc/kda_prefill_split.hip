@@ -176,11 +176,36 @@ __device__ __forceinline__ void load_conv_w(const SplitParams &p, int h, int lan
     }
 }
 
-// Row r (-3 .. 15) of the sub-chunk, clamped into the sequence: its element offset.
-__device__ __forceinline__ int64_t raw_row_off(const SubTask &tk, int r, int64_t tokstride) {
-    int64_t sp = 16 * tk.j + r;
+// Token rows of one sub-chunk as a buffer resource: rows p0-3 .. p0+15 of the
+// sequence, clamped into it, starting at the first one used (all offsets are
+// then small and non-negative).  Each lane reads its two channels (4 bytes at
+// 4 * lane) of a row at a wave-uniform row offset, so no per-lane address
+// arithmetic is needed.
+struct RowWindow {
+    int64_t lo, hi, p0;  // first and last row used (sequence-relative), and p0
+};
+__device__ __forceinline__ RowWindow row_window(const SubTask &tk, int first) {
+    RowWindow w;
+    w.p0 = 16 * tk.j;
+    int64_t lo = w.p0 + first, hi = w.p0 + 15;
+    lo = lo < 0 ? 0 : (lo >= tk.L ? tk.L - 1 : lo);
+    hi = hi >= tk.L ? tk.L - 1 : hi;
+    w.lo = lo;
+    w.hi = hi;
+    return w;
+}
+// Buffer resource over rows lo .. hi of this head's channels of tensor x (data
+// format 32-bit, raw addressing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *x, const SubTask &tk, int h,
+                                                          const RowWindow &w, int64_t rowbytes) {
+    const char *b = reinterpret_cast<const char *>(x) + (size_t)h * kHeadDim * 2 + (size_t)(tk.s0 + w.lo) * rowbytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(b), 0, (int)((w.hi - w.lo + 1) * rowbytes), 0x00020000);
+}
+// Byte offset of sub-chunk row r (-3 .. 15), clamped into the sequence, in the window.
+__device__ __forceinline__ int row_soff(const SubTask &tk, const RowWindow &w, int r, int64_t rowbytes) {
+    int64_t sp = w.p0 + r;
     sp = sp < 0 ? 0 : (sp >= tk.L ? tk.L - 1 : sp);
-    return (tk.s0 + sp) * tokstride;
+    return (int)((sp - w.lo) * rowbytes);
 }
 
 // The three rows before a sequence for tensor t (0 q, 1 k, 2 v): conv state or zeros.
@@ -198,14 +223,16 @@ __device__ __forceinline__ void load_history(const SplitParams &p, const SubTask
 __device__ __forceinline__ void load_early(const SplitParams &p, const SubTask &tk, int h, int lane, EarlyRows &r) {
     constexpr int D = kHeadDim;
     typedef __bf16 T;
-    const int64_t tokstride = (int64_t)p.H * D;
-    const int c0 = 2 * lane;
-    const T *kg = reinterpret_cast<const T *>(p.k) + (size_t)h * D + c0;
-    const T *ag = reinterpret_cast<const T *>(p.gate) + (size_t)h * D + c0;
+    const int64_t rowbytes = (int64_t)p.H * D * 2;
+    const RowWindow wa = row_window(tk, 0), wk = row_window(tk, -3);
+    const __amdgpu_buffer_rsrc_t ra = row_rsrc(p.gate, tk, h, wa, rowbytes);
+    const __amdgpu_buffer_rsrc_t rk = row_rsrc(p.k, tk, h, wk, rowbytes);
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) r.xa[rr] = *reinterpret_cast<const uint32_t *>(ag + raw_row_off(tk, rr, tokstride));
+    for (int rr = 0; rr < 16; ++rr)
+        r.xa[rr] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * lane, row_soff(tk, wa, rr, rowbytes), 0);
 #pragma unroll
-    for (int i = 0; i < 19; ++i) r.xk[i] = *reinterpret_cast<const uint32_t *>(kg + raw_row_off(tk, i - 3, tokstride));
+    for (int i = 0; i < 19; ++i)
+        r.xk[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, row_soff(tk, wk, i - 3, rowbytes), 0);
     r.beta = 0.f;
     if (lane < 16 && 16 * tk.j + lane < tk.L)
         r.beta = to_f32(reinterpret_cast<const T *>(p.beta)[(tk.s0 + 16 * tk.j + lane) * p.H + h]);
@@ -214,16 +241,15 @@ __device__ __forceinline__ void load_early(const SplitParams &p, const SubTask &
 
 __device__ __forceinline__ void load_late(const SplitParams &p, const SubTask &tk, int h, int lane, LateRows &r) {
     constexpr int D = kHeadDim;
-    typedef __bf16 T;
-    const int64_t tokstride = (int64_t)p.H * D;
-    const int c0 = 2 * lane;
-    const T *qg = reinterpret_cast<const T *>(p.q) + (size_t)h * D + c0;
-    const T *vg = reinterpret_cast<const T *>(p.v) + (size_t)h * D + c0;
+    const int64_t rowbytes = (int64_t)p.H * D * 2;
+    const RowWindow wr = row_window(tk, -3);
+    const __amdgpu_buffer_rsrc_t rq = row_rsrc(p.q, tk, h, wr, rowbytes);
+    const __amdgpu_buffer_rsrc_t rv = row_rsrc(p.v, tk, h, wr, rowbytes);
 #pragma unroll
     for (int i = 0; i < 19; ++i) {
-        const int64_t off = raw_row_off(tk, i - 3, tokstride);
-        r.xq[i] = *reinterpret_cast<const uint32_t *>(qg + off);
-        r.xv[i] = *reinterpret_cast<const uint32_t *>(vg + off);
+        const int so = row_soff(tk, wr, i - 3, rowbytes);
+        r.xq[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, so, 0);
+        r.xv[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, 4 * lane, so, 0);
     }
     if (tk.j == 0) {
         load_history(p, tk, h, lane, 0, r.xq);
@@ -475,7 +501,9 @@ __device__ __forceinline__ bool next_task(const SplitParams &p, int64_t slot, in
 
 __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_a[];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the slot (and all derived from it) is wave-uniform: keep it scalar, so the
+    // row buffer resources and offsets live in SGPRs
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int h = blockIdx.y;
     const int64_t stride = (int64_t)gridDim.x * 4;
     unsigned char *lds = smem_a + w * A_WAVE;
