@@ -567,22 +567,6 @@ __device__ __forceinline__ void decay_tile(f32x4 &s, const float (&gv)[2]) {
     s[3] *= row_bcast<4 * (M & 3) + 3>(gv[M >> 2]);
 }
 
-// Producer wave `pw` moves its share of a record into ring stage `stage`.
-template <int NTW>
-__device__ __forceinline__ void scan_issue(unsigned char *stage, const unsigned char *rec, int nt0,
-                                           int pw, int lane) {
-    typedef ScanGeom<NTW> G;
-#pragma unroll
-    for (int i = pw; i < G::kInst; i += G::NP) {
-        const int off = i * 1024 + lane * 16;  // byte within the stage
-        if (off < G::kStage) {
-            const unsigned char *src =
-                off < R_U0 ? rec + off : rec + R_U0 + nt0 * 512 + (off - R_U0);
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)(stage + i * 1024), 16, 0, 0);
-        }
-    }
-}
-
 // Producer wait: everything but the DMA of the `later` most recently issued
 // stages has landed (in-order completion of one wave's vector-memory ops).
 template <int PER, int MAXL>
@@ -603,17 +587,60 @@ __device__ __forceinline__ void scan_wait(int later) {
     }
 }
 
-// Producer wave `pw` waits until the stage issued `later` stages before its
-// most recent one has landed (scan_wait with that producer's per-stage count).
-template <int NTW, int K = 0>
-__device__ __forceinline__ void producer_wait(int pw, int later) {
+// One producer wave with its index PW fixed at compile time, so that its share
+// of a stage (instructions PW, PW + NP, ...) has constant offsets and its
+// per-stage count PER is a constant.  Stages and record pointers advance
+// incrementally; in the steady state the wait is a constant vmcnt, and the
+// dispatch over the in-flight count runs only before B_-1 and in the tail.
+template <int NTW, int PW>
+__device__ __forceinline__ void producer_run(unsigned char *ring, const unsigned char *rec0, int nt0, int lane,
+                                             int J) {
     typedef ScanGeom<NTW> G;
-    if constexpr (K < G::NP) {
+    constexpr int NS = G::NS, NP = G::NP, PER = G::inst_of(PW);
+    auto issue = [&](int slot, const unsigned char *rec) {
+        unsigned char *st = ring + slot * G::kStage;
+#pragma unroll
+        for (int i = PW; i < G::kInst; i += NP) {
+            const int off = i * 1024 + lane * 16;  // byte within the stage
+            if (off < G::kStage) {
+                const unsigned char *src = off < R_U0 ? rec + off : rec + R_U0 + nt0 * 512 + (off - R_U0);
+                __builtin_amdgcn_global_load_lds(src, (lds_void *)(st + i * 1024), 16, 0, 0);
+            }
+        }
+    };
+    const int first = J < NS - 2 ? J : NS - 2;  // stages issued before B_-1
+    const unsigned char *rec = rec0;
+    for (int j = 0; j < first; ++j, rec += kRec) issue(j, rec);
+    // B_-1 needs stage 0; stages 1 .. first - 1 may stay in flight
+    scan_wait<PER, G::kMaxLater>(first - 1);
+    __builtin_amdgcn_s_barrier();  // B_-1
+    // steady state, b = 0 .. J - NS + 1: B_b needs stage b + 1 with NS - 4 later
+    // stages in flight; after it, stage b + NS - 2 goes to slot (b + NS - 2) mod NS
+    int slot = NS - 2;
+    int b = 0;
+    for (; b <= J - NS + 1; ++b, rec += kRec) {
+        wait_vmcnt<PER * (NS - 4)>();
+        __builtin_amdgcn_s_barrier();  // B_b
+        issue(slot, rec);
+        slot = slot + 1 == NS ? 0 : slot + 1;
+    }
+    // tail: nothing left to issue
+    for (; b <= J; ++b) {
+        if (b + 1 < J) scan_wait<PER, G::kMaxLater>(J - 1 - (b + 1));
+        __builtin_amdgcn_s_barrier();  // B_b
+    }
+    wait_vmcnt<0>();
+}
+
+template <int NTW, int K = 0>
+__device__ __forceinline__ void producer_dispatch(int pw, unsigned char *ring, const unsigned char *rec0, int nt0,
+                                                  int lane, int J) {
+    if constexpr (K < ScanGeom<NTW>::NP) {
         if (pw == K) {
-            scan_wait<G::inst_of(K), G::kMaxLater>(later);
+            producer_run<NTW, K>(ring, rec0, nt0, lane, J);
             return;
         }
-        producer_wait<NTW, K + 1>(pw, later);
+        producer_dispatch<NTW, K + 1>(pw, ring, rec0, nt0, lane, J);
     }
 }
 
@@ -646,24 +673,9 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
 
     if (w >= 2 * NTW) {
         // ---------------- producers
+        // bare barriers throughout: a fence would drain all DMA in flight
         if (J == 0) return;
-        const int pw = w - 2 * NTW;
-        for (int64_t j = 0; j < NS - 2 && j < J; ++j)
-            scan_issue<NTW>(stage(j), rec0 + (size_t)j * kRec, nt0, pw, lane);
-        for (int64_t b = -1; b <= J; ++b) {
-            const int64_t need = b + 1;  // stage that must be in LDS at B_b
-            if (need < J) {
-                int64_t top = b + NS - 3;  // last stage issued before B_b
-                if (top > J - 1) top = J - 1;
-                producer_wait<NTW>(pw, (int)(top - need));
-            }
-            // a bare barrier: a fence here would drain all DMA in flight
-            __builtin_amdgcn_s_barrier();  // B_b
-            const int64_t jn = b + NS - 2;
-            if (b >= 0 && jn < J)
-                scan_issue<NTW>(stage(jn), rec0 + (size_t)jn * kRec, nt0, pw, lane);
-        }
-        wait_vmcnt<0>();
+        producer_dispatch<NTW>(w - 2 * NTW, ring, rec0, nt0, lane, (int)J);
         return;
     }
 
