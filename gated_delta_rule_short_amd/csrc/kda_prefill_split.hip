@@ -70,6 +70,7 @@ struct SplitParams {
     float scale, lb;
     uint32_t flags;
     int pairs, tiles;
+    int a_heads_fast;  // pass-A grid: heads in x (slot groups in y), else the reverse
 };
 
 // Slot of sub-chunk j of sequence n (start s0): distinct for all (n, j) and
@@ -474,9 +475,9 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 
 // Pass A.  The slots of sequence n start at base(n) = start_n / 16 + n
 // (strictly increasing in n); slot base(n) + j holds sub-chunk j of sequence n,
-// and slots past the sequence's last sub-chunk are unused.  Wave w of block
-// (x, h) takes slots x * 4 + w and x * 4 + w + 4 * gridDim.x of head h (the
-// first valid ones from there), and loads the second one's early rows while it
+// and slots past the sequence's last sub-chunk are unused.  Wave w of the block
+// for head h and slot group x takes slots x * 4 + w and x * 4 + w + 4 * (number
+// of slot groups) of head h (the first valid ones from there), and loads the second one's early rows while it
 // computes the first.  Two slots in straight-line code: a loop over more slots
 // keeps loop-invariant values live and spills.
 __device__ __forceinline__ bool next_task(const SplitParams &p, int64_t slot, int64_t stride, SubTask &tk) {
@@ -504,11 +505,14 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     // the slot (and all derived from it) is wave-uniform: keep it scalar, so the
     // row buffer resources and offsets live in SGPRs
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int h = blockIdx.y;
-    const int64_t stride = (int64_t)gridDim.x * 4;
+    // heads fastest when the grid allows, so that the workgroups resident at a
+    // time read the same token rows of all heads together
+    const int h = p.a_heads_fast ? blockIdx.x : blockIdx.y;
+    const int64_t gb = p.a_heads_fast ? blockIdx.y : blockIdx.x;
+    const int64_t stride = (int64_t)(p.a_heads_fast ? gridDim.y : gridDim.x) * 4;
     unsigned char *lds = smem_a + w * A_WAVE;
     SubTask ta, tb;
-    if (!next_task(p, (int64_t)blockIdx.x * 4 + w, stride, ta)) return;
+    if (!next_task(p, gb * 4 + w, stride, ta)) return;
     ConvW cw;
     load_conv_w(p, h, lane, cw);
     EarlyRows ra, rb;
@@ -839,6 +843,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
     sp.num_seqs = a->num_seqs; sp.H = a->num_heads;
     sp.scale = a->scale; sp.lb = a->gate_lower_bound; sp.flags = a->flags;
     sp.pairs = a->num_seqs * a->num_heads;
+    sp.a_heads_fast = 0;
     if (dv_tile > 32) dv_tile = 32;  // at most two dv tiles of 16 columns per workgroup
     sp.tiles = kHeadDim / dv_tile;
     if (a->total_tokens > 0) {
@@ -850,7 +855,9 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
         });
         if (attr != hipSuccess) return attr;
         const int64_t gx = (sp.nslots + 7) / 8;  // two slots per wave
-        dim3 grid((unsigned)gx, (unsigned)a->num_heads);
+        sp.a_heads_fast = gx <= 65535;
+        const dim3 grid = sp.a_heads_fast ? dim3((unsigned)a->num_heads, (unsigned)gx)
+                                          : dim3((unsigned)gx, (unsigned)a->num_heads);
         hipLaunchKernelGGL(intra_kernel, grid, dim3(256), 4 * A_WAVE, s, sp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
