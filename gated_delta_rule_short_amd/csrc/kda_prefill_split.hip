@@ -150,7 +150,7 @@ struct SubTask {
 // ("late") are loaded when the sub-chunk starts.
 struct EarlyRows {
     uint32_t xk[19], xa[16];
-    float beta;
+    uint32_t beta_bits;  // raw bf16 of beta (row clamped into the sequence); masked at use
 };
 struct LateRows {
     uint32_t xq[19], xv[19];
@@ -234,9 +234,11 @@ __device__ __forceinline__ void load_early(const SplitParams &p, const SubTask &
 #pragma unroll
     for (int i = 0; i < 19; ++i)
         r.xk[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, row_soff(tk, wk, i - 3, rowbytes), 0);
-    r.beta = 0.f;
-    if (lane < 16 && 16 * tk.j + lane < tk.L)
-        r.beta = to_f32(reinterpret_cast<const T *>(p.beta)[(tk.s0 + 16 * tk.j + lane) * p.H + h]);
+    // unconditional load from a row inside the sequence; the conversion and the
+    // mask wait for the use, so this load does not force a wait on the others
+    int64_t br = 16 * tk.j + (lane & 15);
+    br = br < tk.L ? br : tk.L - 1;
+    r.beta_bits = *reinterpret_cast<const unsigned short *>(reinterpret_cast<const T *>(p.beta) + (tk.s0 + br) * p.H + h);
     if (tk.j == 0) load_history(p, tk, h, lane, 1, r.xk);
 }
 
@@ -289,7 +291,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     const uint32_t(&xk)[19] = er.xk;
     const uint32_t(&xv)[19] = lr.xv;
     const uint32_t(&xa)[16] = er.xa;
-    const float beta_r = er.beta;
+    const float beta_r = (lane < 16 && p0 + lane < L) ? __uint_as_float(er.beta_bits << 16) : 0.f;
     auto load_w = [&](int t, float (&wt)[2][4], float (&bs)[2]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
