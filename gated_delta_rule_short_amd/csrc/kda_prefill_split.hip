@@ -856,7 +856,13 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 4 * A_WAVE);
         });
         if (attr != hipSuccess) return attr;
-        const int64_t gx = (sp.nslots + 7) / 8;  // two slots per wave
+        // two slots per wave: wave (x, w) owns slots x * 4 + w + k * 4 * gx and takes
+        // the valid ones, so 8 * gx must cover every valid slot index.  Those are
+        // below ceil(total / 16) + num_seqs - 1 (the slot past a sequence's last
+        // sub-chunk is never valid), which for one 16-aligned sequence is the
+        // sub-chunk count itself and leaves no partly filled last round.
+        const int64_t span = (a->total_tokens + 15) / 16 + a->num_seqs - 1;
+        const int64_t gx = (span + 7) / 8;
         sp.a_heads_fast = gx <= 65535;
         const dim3 grid = sp.a_heads_fast ? dim3((unsigned)a->num_heads, (unsigned)gx)
                                           : dim3((unsigned)gx, (unsigned)a->num_heads);
