@@ -107,21 +107,30 @@ __device__ __forceinline__ float sigmoidf_dev(float x) {
 // then xor 16) halve the row set per lane while doubling the lanes summed; the
 // remaining 16 lanes of each row block are combined with DPP.  On return, every
 // lane of 16-lane block b holds in out[j] the full sum of row 4 b + j.
-// (The gfx950 lane-swap builtins would save the selects, but this compiler
-// folds their two results into one value when both feed an expression.)
+//
+// The butterflies use the gfx950 lane-swap instructions, which exchange half
+// of one register with half of another inside the VALU (no LDS round trip):
+// permlane32_swap(a, b) leaves (a.lo, b.lo) in the first result and (a.hi,
+// b.hi) in the second, so their sum is a + a^32 in the low 32 lanes and
+// b + b^32 in the high ones; permlane16_swap does the same for the even and odd
+// 16-lane rows.  The two operands are always distinct rows' partials.
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                    false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                    false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
 __device__ __forceinline__ void rows16_sum(float p[16], float out[4], int lane) {
-    const bool hi32 = lane & 32, hi16 = lane & 16;
+    (void)lane;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float send = hi32 ? p[j] : p[j + 8];
-        const float keep = hi32 ? p[j + 8] : p[j];
-        p[j] = keep + __shfl_xor(send, 32, kWave);
-    }
+    for (int j = 0; j < 8; ++j) p[j] = swap32_sum(p[j], p[j + 8]);  // rows j (low half), j + 8 (high half)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float send = hi16 ? p[j] : p[j + 4];
-        const float keep = hi16 ? p[j + 4] : p[j];
-        float x = keep + __shfl_xor(send, 16, kWave);
+        float x = swap16_sum(p[j], p[j + 4]);  // rows j, j + 4 of the half in even and odd 16-lane rows
         x += KDA_DPP(x, 0xb1);   // quad_perm [1,0,3,2]
         x += KDA_DPP(x, 0x4e);   // quad_perm [2,3,0,1]
         x += KDA_DPP(x, 0x141);  // row_half_mirror

@@ -71,6 +71,7 @@ struct SplitParams {
     uint32_t flags;
     int pairs, tiles;
     int a_heads_fast;  // pass-A grid: heads in x (slot groups in y), else the reverse
+    int64_t a_stride;  // pass A: slot distance between a wave's two tasks (4 x slot groups)
 };
 
 // Slot of sub-chunk j of sequence n (start s0): distinct for all (n, j) and
@@ -82,8 +83,7 @@ __device__ __forceinline__ int64_t sub_slot(int64_t s0, int64_t j, int n) { retu
 // (transposed, VT) is formed after the QG export, in the then dead QL area.
 constexpr int A_SRM = 132, A_STR = 20, A_VTS = 16;
 constexpr int A_KL = 0, A_QL = A_KL + 16 * A_SRM * 2, A_KI = A_QL + 16 * A_SRM * 2;
-constexpr int A_KGT = A_KI + 16 * A_SRM * 2, A_NT = A_KGT + 128 * A_STR * 2;
-constexpr int A_XS = A_NT + 16 * 16 * 4, A_PS = A_XS + 16 * A_STR * 2;
+constexpr int A_KGT = A_KI + 16 * A_SRM * 2, A_PS = A_KGT + 128 * A_STR * 2;
 constexpr int A_WAVE = A_PS + 16 * A_STR * 2;
 constexpr int A_VT = A_QL;
 static_assert(A_WAVE % 16 == 0, "wave region alignment");
@@ -260,13 +260,14 @@ __device__ __forceinline__ void load_late(const SplitParams &p, const SubTask &t
     }
 }
 
-// One 16-token sub-chunk by one wave, from its early rows (loaded before) and
-// late rows (loaded here).  After the k block it starts the loads of the next
-// sub-chunk's early rows (when nx is set), so that they land during the rest.
-// All LDS traffic stays inside the wave's region.
+// One 16-token sub-chunk by one wave, from its early and late rows (loads
+// issued before).  When nx is set it starts the loads of the next sub-chunk's
+// rows as soon as their registers are free: the early rows after the k block
+// (into ner), the late rows after the v conv (into lr), so that they land while
+// this sub-chunk finishes.  All LDS traffic stays inside the wave's region.
 __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, const SubTask &tk,
-                                                int h, int lane, const EarlyRows &er, const ConvW &cw,
-                                                const SubTask *nx, EarlyRows &ner) {
+                                                int h, int lane, const EarlyRows &er, LateRows &lr,
+                                                const ConvW &cw, const SubTask *nx, EarlyRows &ner) {
     constexpr int D = kHeadDim;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int64_t s0 = tk.s0, L = tk.L, j = tk.j;
@@ -281,12 +282,8 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     __bf16 *sKI = reinterpret_cast<__bf16 *>(lds + A_KI);
     __bf16 *sKGT = reinterpret_cast<__bf16 *>(lds + A_KGT);
     __bf16 *sVT = reinterpret_cast<__bf16 *>(lds + A_VT);
-    float *sNT = reinterpret_cast<float *>(lds + A_NT);
-    __bf16 *sXS = reinterpret_cast<__bf16 *>(lds + A_XS);
     __bf16 *sPS = reinterpret_cast<__bf16 *>(lds + A_PS);
     unsigned char *rec = p.ws + ((size_t)h * p.nslots + tk.slot) * kRec;
-    LateRows lr;
-    load_late(p, tk, h, lane, lr);
     const uint32_t(&xq)[19] = lr.xq;
     const uint32_t(&xk)[19] = er.xk;
     const uint32_t(&xv)[19] = lr.xv;
@@ -322,14 +319,30 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     // ---- gate: log2 decays as running products from the sub-chunk start
     //   run_r = 2^{b_r},  back_r = 2^{b_last - b_r},  fd = 2^{-b_last}
     float run[16][2], back[16][2], fd[2];
+    float g2v[2][16];
+    if (glog) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) g2v[e][rr] = fmaxf(bf_ch(xa[rr], e), p.lb) * kLog2eS;
+    } else {
+        const float c = p.lb * kLog2eS;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) g2v[e][rr] = c * sigmoidf_dev(bf_ch(xa[rr], e));
+    }
+    if (edge) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            if (p0 + rr >= L) g2v[0][rr] = g2v[1][rr] = 0.f;
+    }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         float al[16], r = 1.f, gs = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            const float a = bf_ch(xa[rr], e);
-            float g2 = glog ? fmaxf(a, p.lb) * kLog2eS : (p.lb * kLog2eS) * sigmoidf_dev(a);
-            if (edge && p0 + rr >= L) g2 = 0.f;
+            const float g2 = g2v[e][rr];
             al[rr] = exp2_fast(g2);
             gs += g2;
             r *= al[rr];
@@ -399,15 +412,24 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     }
     wave_sync_lds();
 
-    // ---- decayed Grams over the sub-chunk (one 16 x 16 tile each)
+    // ---- decayed Grams over the sub-chunk (one 16 x 16 tile each).  N = diag(beta)
+    // strict_lower(A) stays in registers in accumulator layout (row 4 g4 + i,
+    // column m16 in slot i) for the inverse; P goes to LDS for its transpose.
+    float nacc[4];
     {
         const f32x4 a = OPB::gram(sKL + m16 * A_SRM, sKI + m16 * A_SRM, nullptr, g4);
         const f32x4 pq = OPB::gram(sQL + m16 * A_SRM, sKI + m16 * A_SRM, nullptr, g4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rl = 4 * g4 + i, sl = m16;
-            const float brl = __shfl(beta_r, rl);  // beta of row rl (lanes 0..15 hold them)
-            sNT[sl * 16 + rl] = (sl < rl) ? a[i] * brl : 0.f;
+            // beta of row rl (lanes 0..15 of beta_r hold rows 0..15), read as scalars and selected
+            const int bb = __float_as_int(beta_r);
+            const float b0 = __int_as_float(__builtin_amdgcn_readlane(bb, i));
+            const float b1 = __int_as_float(__builtin_amdgcn_readlane(bb, 4 + i));
+            const float b2 = __int_as_float(__builtin_amdgcn_readlane(bb, 8 + i));
+            const float b3 = __int_as_float(__builtin_amdgcn_readlane(bb, 12 + i));
+            const float brl = g4 < 2 ? (g4 == 0 ? b0 : b1) : (g4 == 2 ? b2 : b3);
+            nacc[i] = (sl < rl) ? a[i] * brl : 0.f;
             sPS[rl * A_STR + sl] = (__bf16)((sl <= rl) ? pq[i] : 0.f);
         }
     }
@@ -419,12 +441,15 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         *reinterpret_cast<bf16x8 *>(rec + R_QG + ((size_t)t * 64 + lane) * 16) = f;
     }
     wave_sync_lds();
+    *reinterpret_cast<bf16x4 *>(rec + R_PP + (size_t)lane * 8) =
+        *reinterpret_cast<const bf16x4 *>(sPS + m16 * A_STR + 4 * g4);
 
     // ---- v: beta V transposed into the dead QL area
     {
         float wt[2][4], bs[2], y[16][2];
         load_w(2, wt, bs);
         conv16(xv, wt, bs, y);
+        if (nx) load_late(p, *nx, h, lane, lr);
         finish(y);
 #pragma unroll
         for (int e = 0; e < 2; ++e)
@@ -435,27 +460,38 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
                             bt[r + 2] * y[r + 2][e], bt[r + 3] * y[r + 3][e]);
             }
     }
-    // ---- X = (I + N)^-1, N strictly lower (stored transposed): right-looking
-    if (lane < 16) {
+    // ---- X = (I + N)^-1, one row per lane: lane r (mod 16) solves
+    // x (I + N) = e_r from the last column down, x_c = [c == r] - sum_{s > c} x_s N[s][c],
+    // with N[s][c] read as a wave-uniform scalar from the register tile.  The
+    // term with x_{c+1} comes last, so the dependent chain is one FMA per column.
+    bf16x4 xfr;  // row m16 of X, columns 4 g4 .. 4 g4 + 3 (A-operand fragment)
+    {
         float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
+        for (int c = 0; c < 16; ++c) x[c] = (c == m16) ? 1.f : 0.f;
 #pragma unroll
-        for (int s = 0; s < 15; ++s) {
-            const float xs = x[s];
+        for (int c = 14; c >= 0; --c) {
+            float acc = x[c];
 #pragma unroll
-            for (int i = s + 1; i < 16; ++i) x[i] -= sNT[s * 16 + i] * xs;
+            for (int s = 15; s > c; --s) {
+                const float nsc = __int_as_float(
+                    __builtin_amdgcn_readlane(__float_as_int(nacc[s & 3]), 16 * (s >> 2) + c));
+                acc = fmaf(-nsc, x[s], acc);
+            }
+            x[c] = acc;
         }
+        // arithmetic selection by lane group (a select chain over x would be
+        // turned into an indexed array access)
+        const float m0 = g4 == 0 ? 1.f : 0.f, m1 = g4 == 1 ? 1.f : 0.f;
+        const float m2 = g4 == 2 ? 1.f : 0.f, m3 = g4 == 3 ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sXS[i * A_STR + lane] = (__bf16)x[i];
+        for (int i = 0; i < 4; ++i)
+            xfr[i] = (__bf16)fmaf(x[i], m0, fmaf(x[4 + i], m1, fmaf(x[8 + i], m2, x[12 + i] * m3)));
     }
     wave_sync_lds();
-    *reinterpret_cast<bf16x4 *>(rec + R_PP + (size_t)lane * 8) =
-        *reinterpret_cast<const bf16x4 *>(sPS + m16 * A_STR + 4 * g4);
 
     // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL
     // area; U0 = X diag(beta) V straight to the record in accumulator layout
-    const bf16x4 xfr = *reinterpret_cast<const bf16x4 *>(sXS + m16 * A_STR + 4 * g4);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
         const int col = 16 * nt + m16;
@@ -479,9 +515,9 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 // (strictly increasing in n); slot base(n) + j holds sub-chunk j of sequence n,
 // and slots past the sequence's last sub-chunk are unused.  Wave w of the block
 // for head h and slot group x takes slots x * 4 + w and x * 4 + w + 4 * (number
-// of slot groups) of head h (the first valid ones from there), and loads the second one's early rows while it
-// computes the first.  Two slots in straight-line code: a loop over more slots
-// keeps loop-invariant values live and spills.
+// of slot groups) of head h (the first valid ones from there), and loads the
+// second one's rows while it computes the first.  Two slots in straight-line
+// code: a loop over more slots keeps loop-invariant values live and spills.
 __device__ __forceinline__ bool next_task(const SplitParams &p, int64_t slot, int64_t stride, SubTask &tk) {
     for (; slot < p.nslots; slot += stride) {
         int lo = 0, hi = p.num_seqs - 1;
@@ -511,17 +547,19 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     // time read the same token rows of all heads together
     const int h = p.a_heads_fast ? blockIdx.x : blockIdx.y;
     const int64_t gb = p.a_heads_fast ? blockIdx.y : blockIdx.x;
-    const int64_t stride = (int64_t)(p.a_heads_fast ? gridDim.y : gridDim.x) * 4;
+    const int64_t stride = p.a_stride;
     unsigned char *lds = smem_a + w * A_WAVE;
     SubTask ta, tb;
     if (!next_task(p, gb * 4 + w, stride, ta)) return;
     ConvW cw;
     load_conv_w(p, h, lane, cw);
     EarlyRows ra, rb;
+    LateRows lr;
     load_early(p, ta, h, lane, ra);
+    load_late(p, ta, h, lane, lr);
     const bool hb = next_task(p, ta.slot + stride, stride, tb);
-    intra_sub_chunk(p, lds, ta, h, lane, ra, cw, hb ? &tb : nullptr, rb);
-    if (hb) intra_sub_chunk(p, lds, tb, h, lane, rb, cw, nullptr, ra);
+    intra_sub_chunk(p, lds, ta, h, lane, ra, lr, cw, hb ? &tb : nullptr, rb);
+    if (hb) intra_sub_chunk(p, lds, tb, h, lane, rb, lr, cw, nullptr, ra);
 }
 
 // Pass B geometry.  Per 16-column dv tile one recurrence wave (R: all 128 dk
@@ -707,6 +745,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
             for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         if (J > 0) {
+            int rslot = 1 % NS;  // ring slot of stage j + 1 during step j
             // A step's operands, read from the ring one step ahead: W (negated),
             // Kd, gam (one row per lane, see decay_tile) and this tile's U0.
             auto load = [&](const unsigned char *st, bf16x8 (&wn)[4], bf16x4 (&kd)[8], float (&gv)[2],
@@ -728,7 +767,8 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
             auto step = [&](int64_t j, const bf16x8 (&wn)[4], const bf16x4 (&kd)[8], const float (&gv)[2],
                             bf16x4 u0, bf16x8 (&wn_n)[4], bf16x4 (&kd_n)[8], float (&gv_n)[2], bf16x4 &u0_n) {
                 barrier_lds();  // B_j
-                if (j + 1 < J) load(stage(j + 1), wn_n, kd_n, gv_n, u0_n);
+                if (j + 1 < J) load(ring + rslot * G::kStage, wn_n, kd_n, gv_n, u0_n);
+                rslot = rslot + 1 == NS ? 0 : rslot + 1;
                 bf16x8 Sp[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) Sp[t] = join8(pack4(S[2 * t]), pack4(S[2 * t + 1]));
@@ -783,32 +823,41 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
     // ---------------- output: O = scale ((Q . 2^b) S + P U) of step j - 1
     if (J == 0) return;
     const int64_t tokstride = (int64_t)H * D;
-    __bf16 *op = reinterpret_cast<__bf16 *>(p.o) + (size_t)h * D + col;
+    // stores: a wave-uniform row base plus one 32-bit per-lane offset (column col
+    // of row 4 g4 of the group), so the per-row address arithmetic is scalar
+    __bf16 *ob = reinterpret_cast<__bf16 *>(p.o) + ((size_t)s0 * tokstride + (size_t)h * D);
+    const uint32_t loff = (uint32_t)col + 4u * (uint32_t)g4 * (uint32_t)tokstride;
+    int oslot = 0;  // ring slot of stage j - 1
     barrier_lds();  // B_-1
     for (int64_t j = 0; j <= J; ++j) {
         barrier_lds();  // B_j
         if (j > 0) {
             const int64_t jo = j - 1;
-            const unsigned char *st = stage(jo);
+            const unsigned char *st = ring + oslot * G::kStage;
+            oslot = oslot + 1 == NS ? 0 : oslot + 1;
             const unsigned char *ex = exch + (jo & 1) * G::kExSlot;
-            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+            // every operand first (one LDS round trip), then the product chain
+            bf16x8 qg[4], sp[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const bf16x8 qg = *reinterpret_cast<const bf16x8 *>(st + R_QG + (t * 64 + lane) * 16);
-                const bf16x8 sp = *reinterpret_cast<const bf16x8 *>(ex + t * 1024 + lane * 16);
-                O = mma_k32(qg, sp, O);
+                qg[t] = *reinterpret_cast<const bf16x8 *>(st + R_QG + (t * 64 + lane) * 16);
+                sp[t] = *reinterpret_cast<const bf16x8 *>(ex + t * 1024 + lane * 16);
             }
             const bf16x4 pp = *reinterpret_cast<const bf16x4 *>(st + R_PP + lane * 8);
             const bf16x4 ub = *reinterpret_cast<const bf16x4 *>(ex + 4096 + lane * 8);
-            O = mma_k16w(pp, ub, O);  // the accumulator comes from K = 32 steps
-            const int64_t r0 = 16 * jo + 4 * g4;
-            if (r0 + 3 < L) {
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
+            for (int t = 0; t < 4; ++t) O = mma_k32(qg[t], sp[t], O);
+            O = mma_k16w(pp, ub, O);  // the accumulator comes from K = 32 steps
+            __bf16 *orow = ob + (size_t)(16 * jo) * tokstride;
+            if (16 * jo + 16 <= L) {  // the whole sub-chunk lies in the sequence
+#pragma unroll
+                for (int i = 0; i < 4; ++i) (orow + (size_t)i * tokstride)[loff] = (__bf16)(p.scale * O[i]);
             } else {
+                const int64_t r0 = 16 * jo + 4 * g4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (r0 + i < L) op[(s0 + r0 + i) * tokstride] = (__bf16)(p.scale * O[i]);
+                    if (r0 + i < L) (orow + (size_t)i * tokstride)[loff] = (__bf16)(p.scale * O[i]);
             }
         }
     }
@@ -846,6 +895,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
     sp.scale = a->scale; sp.lb = a->gate_lower_bound; sp.flags = a->flags;
     sp.pairs = a->num_seqs * a->num_heads;
     sp.a_heads_fast = 0;
+    sp.a_stride = 0;
     if (dv_tile > 32) dv_tile = 32;  // at most two dv tiles of 16 columns per workgroup
     sp.tiles = kHeadDim / dv_tile;
     if (a->total_tokens > 0) {
@@ -864,6 +914,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
         const int64_t span = (a->total_tokens + 15) / 16 + a->num_seqs - 1;
         const int64_t gx = (span + 7) / 8;
         sp.a_heads_fast = gx <= 65535;
+        sp.a_stride = 4 * gx;
         const dim3 grid = sp.a_heads_fast ? dim3((unsigned)a->num_heads, (unsigned)gx)
                                           : dim3((unsigned)gx, (unsigned)a->num_heads);
         hipLaunchKernelGGL(intra_kernel, grid, dim3(256), 4 * A_WAVE, s, sp);
