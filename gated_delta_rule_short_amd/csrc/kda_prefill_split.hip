@@ -767,7 +767,10 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
             auto step = [&](int64_t j, const bf16x8 (&wn)[4], const bf16x4 (&kd)[8], const float (&gv)[2],
                             bf16x4 u0, bf16x8 (&wn_n)[4], bf16x4 (&kd_n)[8], float (&gv_n)[2], bf16x4 &u0_n) {
                 barrier_lds();  // B_j
-                if (j + 1 < J) load(ring + rslot * G::kStage, wn_n, kd_n, gv_n, u0_n);
+                __builtin_amdgcn_sched_barrier(0);
+                // (past the last step this reads a stale stage: harmless, and it keeps
+                // the step one basic block so that the issue order below holds)
+                load(ring + rslot * G::kStage, wn_n, kd_n, gv_n, u0_n);
                 rslot = rslot + 1 == NS ? 0 : rslot + 1;
                 bf16x8 Sp[4];
 #pragma unroll
@@ -794,6 +797,24 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                 *reinterpret_cast<bf16x4 *>(ex + 4096 + lane * 8) = Ub;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) S[m] = mma_k16(kd[m], Ub, S[m]);
+                // issue order: next operands; S_j to bf16 interleaved with the U
+                // products; the decay under their latency; the S_j exchange; U; the
+                // U exchange; the state products (the barrier's LDS wait then finds
+                // the writes done)
+                __builtin_amdgcn_sched_group_barrier(0x100, 11, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             };
             bf16x8 wnA[4], wnB[4];
             bf16x4 kdA[8], kdB[8], u0A, u0B = {};
