@@ -113,7 +113,8 @@ __device__ __forceinline__ float sigmoidf_dev(float x) {
 // permlane32_swap(a, b) leaves (a.lo, b.lo) in the first result and (a.hi,
 // b.hi) in the second, so their sum is a + a^32 in the low 32 lanes and
 // b + b^32 in the high ones; permlane16_swap does the same for the even and odd
-// 16-lane rows.  The two operands are always distinct rows' partials.
+// 16-lane rows.  The two operands are always distinct rows' partials (with one
+// value in both, this compiler has been seen to fold the two results into one).
 __device__ __forceinline__ float swap32_sum(float a, float b) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
                                                     false, false);

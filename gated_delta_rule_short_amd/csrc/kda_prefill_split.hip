@@ -20,7 +20,7 @@
 // Pass A does the conv / L2 / gate work once per token and head, over the
 // whole GPU; pass B keeps the fp32 state in registers (accumulator layout) for
 // the whole sequence and streams the records through an LDS ring filled by
-// two producer waves with LDS DMA, so several sub-chunks are in flight while
+// producer waves with LDS DMA, so several sub-chunks are in flight while
 // the consumer waves run the recurrence.  The workspace costs extra HBM
 // traffic (one 17 KiB record per sub-chunk and head, written once and read
 // once), which pays off when there are too few (sequence, head) pairs to fill
