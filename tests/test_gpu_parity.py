@@ -401,6 +401,25 @@ def test_two_pass_dv_tiles_agree_bitwise(dv_tile, monkeypatch):
     assert torch.equal(o, base[0]) and torch.equal(st, base[1])
 
 
+@pytest.mark.parametrize("schedule", [{"workspace": True}, {"chunk_size": 64}])
+def test_near_degenerate_keys(schedule):
+    """beta = 1, nearly parallel keys and a weak decay: the strictly lower Gram of a
+    chunk is close to all ones, so the triangular inverse and the delta rule's
+    cancellation (each write overwrites almost the same direction) are at their
+    hardest; still within the bf16 bar of the oracle, on both schedules."""
+    H, lengths = 2, [16, 47, 100]
+    inp = KI.make_prefill(H, lengths, seed=171, device=DEV, state_std=0.1)
+    T = sum(lengths)
+    base = seeded((1, H, 128), 172)
+    inp["k"] = (base + 0.05 * seeded((T, H, 128), 173)).to(torch.bfloat16)
+    inp["beta"] = torch.ones((T, H), dtype=torch.bfloat16, device=DEV)
+    inp["gate"] = torch.full((T, H, 128), -4.0, dtype=torch.bfloat16, device=DEV)
+    ref = _oracle_prefill(inp)
+    o, st, _ = _gpu_prefill(inp, **schedule)
+    assert torch.isfinite(o).all() and torch.isfinite(st).all()
+    assert_bf16_close(o, ref["o"], inp["cu_seqlens"], H, st, ref["state"], "near-degenerate keys")
+
+
 def test_two_pass_agrees_with_one_pass_chunk16():
     inp = KI.make_prefill(2, [257, 40], seed=151, device=DEV, state_std=0.1)
     a = _gpu_prefill(inp, workspace=True)
