@@ -145,10 +145,15 @@ short_conv_vec_kernel(const T *__restrict__ x, T *__restrict__ y, int64_t total,
                       const T *__restrict__ cs_in, const int32_t *__restrict__ cu, int num_seqs) {
     typedef Vec16<T> V;
     constexpr int NV = V::N;
-    // flat grid, channel blocks fastest: workgroups in flight together cover whole rows
-    const int nblk = (C / NV + kConvThreads - 1) / kConvThreads;
+    // flat grid, channel blocks fastest: workgroups in flight together cover whole
+    // rows.  The launcher picks the block width so that the block count per run is
+    // a multiple of 8 where it can: workgroup b runs on XCD b mod 8, so every run of
+    // a channel block then lands on the same XCD (and L2) as the run before it,
+    // whose last rows are this run's history rows.
+    const int bt = blockDim.x;
+    const int nblk = (C / NV + bt - 1) / bt;
     const int64_t run = blockIdx.x / nblk;
-    const int c = NV * ((int)(blockIdx.x - run * nblk) * kConvThreads + threadIdx.x);
+    const int c = NV * ((int)(blockIdx.x - run * nblk) * bt + threadIdx.x);
     if (c >= C) return;
     const int64_t t0 = run * kVecTokens;
     const int64_t t1 = min(total, t0 + (int64_t)kVecTokens);
@@ -253,18 +258,24 @@ static hipError_t short_conv_t(const void *x, void *y, int64_t T_, int C, const 
                                bool silu, hipStream_t s) {
     if (T_ == 0) return hipSuccess;
     constexpr int NV = Vec16<T>::N;
-    const int64_t nblk_v = (C / NV + kConvThreads - 1) / kConvThreads;
-    const int64_t items_v = ((T_ + kVecTokens - 1) / kVecTokens) * nblk_v * kConvThreads;
+    int vt = kConvThreads;  // block width of the vector path (see short_conv_vec_kernel)
+    for (const int cand : {256, 192, 128, 64})
+        if (((C / NV + cand - 1) / cand) % 8 == 0) {
+            vt = cand;
+            break;
+        }
+    const int64_t nblk_v = (C / NV + vt - 1) / vt;
+    const int64_t items_v = ((T_ + kVecTokens - 1) / kVecTokens) * nblk_v * vt;
     const bool vec = (C % NV) == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)y % 16) == 0 &&
                      (cs_in == nullptr || ((uintptr_t)cs_in % 16) == 0) && ((uintptr_t)w % 16) == 0 &&
                      items_v < (int64_t(1) << 32);  // one flat grid dimension
     if (vec) {
-        dim3 grid((unsigned)(items_v / kConvThreads));
+        dim3 grid((unsigned)(items_v / vt));
         if (silu)
-            hipLaunchKernelGGL((short_conv_vec_kernel<T, true>), grid, dim3(kConvThreads), 0, s,
+            hipLaunchKernelGGL((short_conv_vec_kernel<T, true>), grid, dim3(vt), 0, s,
                                (const T *)x, (T *)y, T_, C, w, b, (const T *)cs_in, cu, N);
         else
-            hipLaunchKernelGGL((short_conv_vec_kernel<T, false>), grid, dim3(kConvThreads), 0, s,
+            hipLaunchKernelGGL((short_conv_vec_kernel<T, false>), grid, dim3(vt), 0, s,
                                (const T *)x, (T *)y, T_, C, w, b, (const T *)cs_in, cu, N);
         return hipGetLastError();
     }
