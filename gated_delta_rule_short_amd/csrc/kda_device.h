@@ -167,13 +167,17 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Two paired conversions (v_cvt_pk_bf16_f32), joined as 32-bit words: with a
+// four-wide conversion this compiler converts element by element and permutes
+// when the result feeds an MFMA operand as well as a store.
 __device__ __forceinline__ bf16x4 pack4(f32x4 v) {
-    bf16x4 r;
-    r.x = (__bf16)v.x;
-    r.y = (__bf16)v.y;
-    r.z = (__bf16)v.z;
-    r.w = (__bf16)v.w;
-    return r;
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t lo = __builtin_convertvector((f32x2_t){v.x, v.y}, bf16x2_t);
+    const bf16x2_t hi = __builtin_convertvector((f32x2_t){v.z, v.w}, bf16x2_t);
+    const u32x2_t u = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    return __builtin_bit_cast(bf16x4, u);
 }
 __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
     bf16x8 r;
