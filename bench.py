@@ -9,6 +9,12 @@ with all inputs already resident in HBM:
                updated in place, bf16 tokens                  (kda_decode)
   short_conv : the same 4096-token q|k|v rows as a [4096, 24576] bf16 tensor,
                conv width 4                                   (kda_short_conv)
+and, reported beside the step, one speculative decode step (verification of
+k = 5 drafted tokens plus one):
+  spec_decode: 256 sequences x 6 tokens, 64 heads, fp32 state; each call first
+               commits the previous call's accepted prefix (1 + Binomial(5, 0.8)
+               tokens per sequence), then verifies 6 new tokens
+                                         (kda_decode_multi with pending records)
 Every call is bracketed by HIP events on the stream it is launched on, after a
 512 MiB scratch write that evicts L2 and the MALL (not timed); `value` is
 prefill tokens per second per layer from the median prefill call time, decode
@@ -58,7 +64,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "short_conv", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "short_conv", "spec_decode",
+                                       "copy"],
                     default="all", help="run one entry point only (for profiler passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -94,6 +101,13 @@ def main():
     X = torch.cat([P["q"].reshape(T, -1), P["k"].reshape(T, -1), P["v"].reshape(T, -1)], 1).contiguous()
     Y = torch.empty_like(X)
     cu1 = P["cu_seqlens"]
+    Sp = KI.workload_inputs(5, device=dev)
+    N_sp, T_sp = Sp["q"].shape[0], Sp["q"].shape[1]
+    acc_sp = KI.make_accepted(N_sp, T_sp, seed=5, device=dev)
+    rec_sp = [torch.empty((N_sp, H, T_sp, kda.UPDATE_FLOATS), dtype=torch.float32, device=dev)
+              for _ in range(2)]
+    o_sp = torch.empty_like(Sp["v"])
+    sp_turn = [0]
     copy_src = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
     copy_dst = torch.empty_like(copy_src)
     scratch = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
@@ -106,15 +120,29 @@ def main():
         kda.kda_decode(Dd["q"], Dd["k"], Dd["v"], Dd["gate"], Dd["beta"], Dd["conv_w"],
                        Dd["conv_state"], Dd["state"], o=o_dec)
 
+    def run_spec():
+        # records alternate between two buffers: this call commits the other one
+        i = sp_turn[0]
+        sp_turn[0] ^= 1
+        kda.kda_decode_multi(Sp["q"], Sp["k"], Sp["v"], Sp["gate"], Sp["beta"], Sp["conv_w"],
+                             Sp["conv_state"], Sp["state"], updates=rec_sp[i], o=o_sp,
+                             pending_updates=rec_sp[i ^ 1], pending_accepted=acc_sp)
+
+    # the first verification has nothing to commit: it primes the pending records
+    kda.kda_decode_multi(Sp["q"], Sp["k"], Sp["v"], Sp["gate"], Sp["beta"], Sp["conv_w"],
+                         Sp["conv_state"], Sp["state"], updates=rec_sp[1], o=o_sp)
+
     def run_conv():
         kda.kda_short_conv(X, P["conv_w"], cu_seqlens=cu1, y=Y)
 
     def run_copy():
         copy_dst.copy_(copy_src)
 
-    ops = {"prefill": run_prefill, "decode": run_decode, "short_conv": run_conv, "copy": run_copy}
+    ops = {"prefill": run_prefill, "decode": run_decode, "short_conv": run_conv,
+           "spec_decode": run_spec, "copy": run_copy}
+    step_names = ["short_conv", "prefill", "decode"]
     if args.only == "all":
-        names = ["short_conv", "prefill", "decode"]
+        names = step_names + ["spec_decode"]
     else:
         names = [args.only]
 
@@ -157,6 +185,20 @@ def main():
     dec_other = N_dec * H * (KI.bytes_per_token_head() + 2 * 3 * 128 * 2)  # tokens + conv cache
     dec_s = ms["decode"] * 1e-3
     conv_bytes = 2 * X.numel() * X.element_size()
+    # speculative step, per (sequence, head): state read and written back, the
+    # pending records' alpha, k, u rows and the raw rows of the last <= 3 accepted
+    # tokens, conv cache read and written, the 6 new tokens (q, k, v, gate, beta),
+    # their outputs and their records
+    acc_l = acc_sp.cpu().tolist()
+    sp_bytes = 0
+    for a_ in acc_l:
+        a_ = max(0, min(T_sp, a_))
+        per = 65536 + (65536 if a_ else 0) + a_ * 3 * 512 + min(a_, 3) * 3 * 512
+        per += 3 * 384 * 2 * (2 if a_ else 1)
+        per += T_sp * (4 * 128 * 2 + 2) + T_sp * 128 * 2 + T_sp * 6 * 512
+        sp_bytes += per * H
+    sp_s = ms["spec_decode"] * 1e-3
+    sp_state_bytes = 2 * N_sp * H * 128 * 128 * 4
     traffic = _traffic_from_profile("kda_prefill_split.hip", "prefill_bf16_T4096_H64_pmc.md")
     dec_traffic = _traffic_from_profile("kda_decode.hip", "decode_bf16_N256_H64_pmc.md")
 
@@ -167,7 +209,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(sum(ms.values()), 4),
+        "ms_per_step": round(sum(ms[nm] for nm in step_names), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -202,6 +244,25 @@ def main():
             "algorithmic_bytes_per_launch": dec_state_bytes + dec_other,
         },
         "short_conv_GBps": round(conv_bytes / (ms["short_conv"] * 1e-3) / 1e9, 1),
+        "spec_decode": {
+            "workload": "256 sequences x 6 tokens (k=5 drafts + 1), H=64, bf16 tokens, fp32 "
+                        "state; fused commit of the previous step's accepted prefix",
+            "us_per_call": round(ms["spec_decode"] * 1e3, 2),
+            "verified_tokens_per_s": round(N_sp * T_sp / sp_s, 1),
+            "accepted_tokens_per_s": round(sum(max(0, min(T_sp, a_)) for a_ in acc_l) / sp_s, 1),
+            "mean_accepted": round(sum(acc_l) / len(acc_l), 3),
+            "state_GBps": round(sp_state_bytes / sp_s / 1e9, 1),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(sp_bytes / sp_s / 1e9, 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(sp_bytes / sp_s / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": _traffic_from_profile("kda_decode.hip",
+                                                 "spec_decode_bf16_N256_T6_H64_pmc.md"),
+                "algorithmic_bytes_per_launch": sp_bytes,
+            },
+        },
     }
 
     if not args.no_cpu_baseline:

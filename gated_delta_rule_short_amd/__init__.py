@@ -4,10 +4,12 @@ The computation runs in libkda.so (hand-written HIP kernels behind the C ABI of
 include/kda.h); this package is its thin Python binding.
 """
 from .kda import (KDA_F32, KDA_BF16, KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG,
-                  KdaError, abi_version, kda_decode, kda_prefill, kda_short_conv, load_library,
+                  KdaError, MAX_SPEC_TOKENS, UPDATE_FLOATS, abi_version, kda_decode, kda_decode_commit,
+                  kda_decode_multi, kda_prefill, kda_short_conv, load_library,
                   prefill_workspace_bytes)
 
-__all__ = ["kda_short_conv", "kda_prefill", "kda_decode", "abi_version", "load_library",
+__all__ = ["kda_short_conv", "kda_prefill", "kda_decode", "kda_decode_multi",
+           "kda_decode_commit", "abi_version", "load_library",
            "prefill_workspace_bytes",
-           "KdaError", "KDA_F32", "KDA_BF16", "KDA_F_SILU", "KDA_F_NO_QK_L2NORM",
+           "KdaError", "MAX_SPEC_TOKENS", "UPDATE_FLOATS", "KDA_F32", "KDA_BF16", "KDA_F_SILU", "KDA_F_NO_QK_L2NORM",
            "KDA_F_GATE_IS_LOG"]

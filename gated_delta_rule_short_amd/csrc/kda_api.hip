@@ -241,4 +241,79 @@ kda_status kda_decode(const kda_decode_args *a, hipStream_t stream) {
     return KDA_OK;
 }
 
+kda_status kda_decode_multi(const kda_decode_multi_args *a, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
+    kda_status st = check_common(a->num_seqs, a->num_heads, a->head_dim_k, a->head_dim_v, a->dtype,
+                                 a->flags, a->scale, a->gate_lower_bound);
+    if (st != KDA_OK) return st;
+    if (a->num_tokens < 1 || a->num_tokens > KDA_MAX_SPEC_TOKENS)
+        return fail(KDA_ERR_INVALID_ARG, "num_tokens = %d, must be in 1..%d", a->num_tokens,
+                    KDA_MAX_SPEC_TOKENS);
+    if (!a->q || !a->k || !a->v || !a->gate || !a->beta || !a->o || !a->conv_weight ||
+        !a->conv_state || !a->state || !a->updates)
+        return fail(KDA_ERR_INVALID_ARG, "q, k, v, gate, beta, o, conv_weight, conv_state, state "
+                                         "and updates must be non-NULL");
+    if (a->pending_updates) {
+        if (!a->pending_accepted)
+            return fail(KDA_ERR_INVALID_ARG, "pending_updates needs pending_accepted");
+        if (a->pending_tokens < 1 || a->pending_tokens > KDA_MAX_SPEC_TOKENS)
+            return fail(KDA_ERR_INVALID_ARG, "pending_tokens = %d, must be in 1..%d",
+                        a->pending_tokens, KDA_MAX_SPEC_TOKENS);
+    }
+    const size_t es = esize(a->dtype);
+    const size_t NH = (size_t)a->num_seqs * a->num_heads;
+    const size_t tok = NH * a->num_tokens * 128 * es;
+    const size_t sb = NH * 128 * 128 * 4;
+    const size_t cb = (size_t)a->num_seqs * 3 * 3 * a->num_heads * 128 * es;
+    const size_t rb = NH * a->num_tokens * KDA_UPDATE_FLOATS * 4;
+    const size_t pb = a->pending_updates ? NH * a->pending_tokens * KDA_UPDATE_FLOATS * 4 : 0;
+    const void *ins[4] = {a->q, a->k, a->v, a->gate};
+    for (const void *in : ins) {
+        if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
+        if (overlap(a->updates, rb, in, tok))
+            return fail(KDA_ERR_INVALID_ARG, "updates overlaps an input");
+        if (overlap(a->state, sb, in, tok) || overlap(a->conv_state, cb, in, tok))
+            return fail(KDA_ERR_INVALID_ARG, "state or conv_state overlaps an input");
+    }
+    if (overlap(a->state, sb, a->o, tok) || overlap(a->conv_state, cb, a->o, tok))
+        return fail(KDA_ERR_INVALID_ARG, "state or conv_state overlaps o");
+    if (overlap(a->updates, rb, a->o, tok) || overlap(a->updates, rb, a->state, sb) ||
+        overlap(a->updates, rb, a->conv_state, cb))
+        return fail(KDA_ERR_INVALID_ARG, "updates overlaps o, state or conv_state");
+    if (overlap(a->updates, rb, a->pending_updates, pb))
+        return fail(KDA_ERR_INVALID_ARG, "updates overlaps pending_updates");
+    if (overlap(a->pending_updates, pb, a->state, sb) ||
+        overlap(a->pending_updates, pb, a->conv_state, cb))
+        return fail(KDA_ERR_INVALID_ARG, "pending_updates overlaps state or conv_state");
+    kda_decode_multi_args args = *a;
+    if (args.scale == 0.f) args.scale = 1.0f / std::sqrt(128.0f);
+    hipError_t e = kda::launch_decode_multi(&args, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode_multi launch");
+    return KDA_OK;
+}
+
+kda_status kda_decode_commit(const kda_decode_commit_args *a, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
+    kda_status st = check_common(a->num_seqs, a->num_heads, a->head_dim_k, a->head_dim_v, a->dtype,
+                                 0u, 0.f, -1.f);
+    if (st != KDA_OK) return st;
+    if (a->num_tokens < 1 || a->num_tokens > KDA_MAX_SPEC_TOKENS)
+        return fail(KDA_ERR_INVALID_ARG, "num_tokens = %d, must be in 1..%d", a->num_tokens,
+                    KDA_MAX_SPEC_TOKENS);
+    if (!a->accepted || !a->updates || !a->conv_state || !a->state)
+        return fail(KDA_ERR_INVALID_ARG, "accepted, updates, conv_state and state must be non-NULL");
+    const size_t NH = (size_t)a->num_seqs * a->num_heads;
+    const size_t sb = NH * 128 * 128 * 4;
+    const size_t cb = (size_t)a->num_seqs * 3 * 3 * a->num_heads * 128 * esize(a->dtype);
+    const size_t rb = NH * a->num_tokens * KDA_UPDATE_FLOATS * 4;
+    if (overlap(a->updates, rb, a->state, sb) || overlap(a->updates, rb, a->conv_state, cb) ||
+        overlap(a->state, sb, a->conv_state, cb))
+        return fail(KDA_ERR_INVALID_ARG, "updates, state and conv_state must not overlap");
+    hipError_t e = kda::launch_decode_commit(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode_commit launch");
+    return KDA_OK;
+}
+
 }  // extern "C"

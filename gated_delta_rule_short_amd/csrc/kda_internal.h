@@ -29,6 +29,8 @@ struct PrefillLaunch {
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t s);
 
 hipError_t launch_decode(const kda_decode_args *a, hipStream_t s);
+hipError_t launch_decode_multi(const kda_decode_multi_args *a, hipStream_t s);
+hipError_t launch_decode_commit(const kda_decode_commit_args *a, hipStream_t s);
 
 // Two-pass prefill (bf16 I/O, 16-token sub-chunks) and its workspace size.
 size_t split_workspace_bytes(int64_t total_tokens, int num_seqs, int H);

@@ -21,7 +21,10 @@ KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG = 1, 2, 4
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_short_conv",
-           "kda_prefill", "kda_prefill_workspace_size", "kda_decode")
+           "kda_prefill", "kda_prefill_workspace_size", "kda_decode", "kda_decode_multi",
+           "kda_decode_commit")
+MAX_SPEC_TOKENS = 8
+UPDATE_FLOATS = 6 * 128  # floats per (sequence, head, token) update record
 
 _c_i32, _c_i64, _c_u32, _c_f32, _p = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                                       ctypes.c_float, ctypes.c_void_p)
@@ -47,6 +50,26 @@ class KdaDecodeArgs(ctypes.Structure):
         ("scale", _c_f32), ("gate_lower_bound", _c_f32),
         ("q", _p), ("k", _p), ("v", _p), ("gate", _p), ("beta", _p),
         ("conv_weight", _p), ("conv_bias", _p), ("conv_state", _p), ("state", _p), ("o", _p),
+    ]
+
+
+class KdaDecodeMultiArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", _c_i32), ("num_heads", _c_i32), ("head_dim_k", _c_i32),
+        ("head_dim_v", _c_i32), ("num_tokens", _c_i32), ("dtype", ctypes.c_int),
+        ("flags", _c_u32), ("scale", _c_f32), ("gate_lower_bound", _c_f32),
+        ("q", _p), ("k", _p), ("v", _p), ("gate", _p), ("beta", _p),
+        ("conv_weight", _p), ("conv_bias", _p), ("conv_state", _p), ("state", _p), ("o", _p),
+        ("updates", _p), ("pending_updates", _p), ("pending_accepted", _p),
+        ("pending_tokens", _c_i32),
+    ]
+
+
+class KdaDecodeCommitArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", _c_i32), ("num_heads", _c_i32), ("head_dim_k", _c_i32),
+        ("head_dim_v", _c_i32), ("num_tokens", _c_i32), ("dtype", ctypes.c_int),
+        ("accepted", _p), ("updates", _p), ("conv_state", _p), ("state", _p),
     ]
 
 
@@ -83,6 +106,10 @@ def load_library(path: str = LIB_PATH):
         lib.kda_prefill_workspace_size.argtypes = [ctypes.POINTER(KdaPrefillArgs)]
         lib.kda_decode.restype = ctypes.c_int
         lib.kda_decode.argtypes = [ctypes.POINTER(KdaDecodeArgs), _p]
+        lib.kda_decode_multi.restype = ctypes.c_int
+        lib.kda_decode_multi.argtypes = [ctypes.POINTER(KdaDecodeMultiArgs), _p]
+        lib.kda_decode_commit.restype = ctypes.c_int
+        lib.kda_decode_commit.argtypes = [ctypes.POINTER(KdaDecodeCommitArgs), _p]
         if path == LIB_PATH:
             _lib = lib
         return lib
@@ -243,3 +270,70 @@ def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias
         state=_ptr(state), o=_ptr(o))
     _check(lib, lib.kda_decode(ctypes.byref(a), _stream(stream, dev)))
     return o
+
+
+def kda_decode_multi(q, k, v, gate, beta, conv_weight, conv_state, state, *, updates=None,
+                     conv_bias=None, o=None, pending_updates=None, pending_accepted=None,
+                     scale=0.0, gate_lower_bound=-5.0, flags=0, stream=None):
+    """Speculative decode of T tokens per sequence.  q, k, gate, v: [N, T, H, 128];
+    beta [N, T, H].  conv_state [N, 3, CC] and state [N, H, 128, 128] fp32 are only
+    read, unless pending_updates ([N, H, T', 768] fp32 records of a previous call) and
+    pending_accepted ([N] int32) are given: that commit is applied to them first.
+    Returns (o [N, T, H, 128], updates [N, H, T, 768] fp32)."""
+    lib = load_library()
+    dev = q.device
+    N, T, H, dk = q.shape
+    dv = v.shape[3]
+    if o is None:
+        o = torch.empty((N, T, H, dv), dtype=q.dtype, device=dev)
+    if updates is None:
+        updates = torch.empty((N, H, T, UPDATE_FLOATS), dtype=torch.float32, device=dev)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (o, "o"),
+                  (conv_state, "conv_state")):
+        _need(t, nm, q.dtype, dev)
+    for t, nm in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"), (state, "state"),
+                  (updates, "updates"), (pending_updates, "pending_updates")):
+        _need(t, nm, torch.float32, dev)
+    _need(pending_accepted, "pending_accepted", torch.int32, dev)
+    if updates.numel() != N * H * T * UPDATE_FLOATS:
+        raise ValueError("updates must hold N*H*T*%d floats" % UPDATE_FLOATS)
+    pt = 0
+    if pending_updates is not None:
+        pt = pending_updates.numel() // (N * H * UPDATE_FLOATS)
+        if pending_updates.numel() != N * H * pt * UPDATE_FLOATS:
+            raise ValueError("pending_updates must hold N*H*T'*%d floats" % UPDATE_FLOATS)
+        if pending_accepted is None or pending_accepted.numel() != N:
+            raise ValueError("pending_accepted must be an int32 tensor of N counts")
+    a = KdaDecodeMultiArgs(
+        num_seqs=N, num_heads=H, head_dim_k=dk, head_dim_v=dv, num_tokens=T,
+        dtype=_dtype_code(q), flags=int(flags), scale=float(scale),
+        gate_lower_bound=float(gate_lower_bound),
+        q=_ptr(q), k=_ptr(k), v=_ptr(v), gate=_ptr(gate), beta=_ptr(beta),
+        conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias), conv_state=_ptr(conv_state),
+        state=_ptr(state), o=_ptr(o), updates=_ptr(updates),
+        pending_updates=_ptr(pending_updates), pending_accepted=_ptr(pending_accepted),
+        pending_tokens=pt)
+    _check(lib, lib.kda_decode_multi(ctypes.byref(a), _stream(stream, dev)))
+    return o, updates
+
+
+def kda_decode_commit(updates, accepted, conv_state, state, *, stream=None):
+    """Advance state [N, H, 128, 128] fp32 and conv_state [N, 3, CC] in place over the
+    first accepted[n] tokens ([N] int32 on the device) recorded in updates
+    ([N, H, T, 768] fp32, written by kda_decode_multi)."""
+    lib = load_library()
+    dev = state.device
+    N, H, dk, dv = state.shape
+    T = updates.numel() // (N * H * UPDATE_FLOATS)
+    if updates.numel() != N * H * T * UPDATE_FLOATS:
+        raise ValueError("updates must hold N*H*T*%d floats" % UPDATE_FLOATS)
+    _need(updates, "updates", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    _need(conv_state, "conv_state", None, dev)
+    _need(accepted, "accepted", torch.int32, dev)
+    if accepted.numel() != N:
+        raise ValueError("accepted must hold N counts")
+    a = KdaDecodeCommitArgs(num_seqs=N, num_heads=H, head_dim_k=dk, head_dim_v=dv,
+                            num_tokens=T, dtype=_dtype_code(conv_state), accepted=_ptr(accepted),
+                            updates=_ptr(updates), conv_state=_ptr(conv_state), state=_ptr(state))
+    _check(lib, lib.kda_decode_commit(ctypes.byref(a), _stream(stream, dev)))

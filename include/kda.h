@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -188,6 +188,90 @@ typedef struct {
 } kda_decode_args;
 
 kda_status kda_decode(const kda_decode_args *args, hipStream_t stream);
+
+/*
+ * Speculative multi-token decode.  The serving rig of the pages runs a
+ * one-layer draft head (MTP, k = 5 drafted tokens per step) whose proposals the
+ * target model verifies, about four of five being accepted ("GLM-5.3-Flash
+ * Internals", sections "Serve rig" and "Architecture" (MTP), and the research
+ * directions on MTP acceptance; "GLM-5.3-Flash im Detail", the draft-path row of
+ * the architecture table).  Verification feeds T = k + 1 tokens per sequence
+ * through the mixer at once; only a prefix of them is kept, so the state may
+ * advance over the accepted tokens only.
+ *
+ * kda_decode_multi evaluates T tokens per sequence in order, exactly as T calls
+ * of kda_decode would (output t sees tokens 0..t-1 of the same call), but
+ * leaves the state and the conv cache where they were and writes one update
+ * record per (sequence, head, token) instead.  kda_decode_commit then advances
+ * the state and conv cache over the first `accepted[n]` tokens of each sequence
+ * from those records.  The same commit can be fused into the next
+ * kda_decode_multi call (the `pending_*` fields), so that a steady-state
+ * speculative step reads and writes each state once.  Given the same inputs,
+ * the outputs and the committed state and conv cache are bit-identical to
+ * those of that many kda_decode calls.
+ *
+ * Update record of (sequence n, head h, token t): KDA_UPDATE_ROWS rows of 128
+ * fp32 at updates + ((n * H + h) * T + t) * KDA_UPDATE_FLOATS:
+ *   row 0  exp(g_t), the per-row decay of the state
+ *   row 1  the conv-ed, normalised key k_t
+ *   row 2  u_t = beta_t (v_t - S'^T k_t), the delta-rule value
+ *   rows 3, 4, 5  the raw (pre-conv) q_t, k_t, v_t of head h, exact in fp32
+ * so that the commit needs neither the token buffers nor the gates again.
+ */
+#define KDA_MAX_SPEC_TOKENS 8
+#define KDA_UPDATE_ROWS 6
+#define KDA_UPDATE_FLOATS (KDA_UPDATE_ROWS * 128)
+
+typedef struct {
+    int32_t num_seqs;        /* N >= 1 */
+    int32_t num_heads;       /* H >= 1 */
+    int32_t head_dim_k;      /* must be 128 */
+    int32_t head_dim_v;      /* must be 128 */
+    int32_t num_tokens;      /* T, 1..KDA_MAX_SPEC_TOKENS tokens per sequence */
+    kda_dtype dtype;
+    uint32_t flags;          /* KDA_F_* */
+    float scale;             /* 0 = 1/sqrt(dk) */
+    float gate_lower_bound;  /* < 0 */
+    const void *q, *k;       /* [N][T][H][dk] raw */
+    const void *v;           /* [N][T][H][dv] raw */
+    const void *gate;        /* [N][T][H][dk] */
+    const void *beta;        /* [N][T][H] */
+    const float *conv_weight;/* [CC][4] */
+    const float *conv_bias;  /* [CC] or NULL */
+    void *conv_state;        /* [N][3][CC]; written only by a pending commit */
+    float *state;            /* [N][H][dk][dv] fp32; written only by a pending commit */
+    void *o;                 /* [N][T][H][dv] */
+    float *updates;          /* [N][H][T][KDA_UPDATE_FLOATS] fp32 records (written) */
+    /* Optional fused commit of the previous call, applied to state and conv_state
+     * before the T new tokens are evaluated (NULL pending_updates: none). */
+    const float *pending_updates;    /* that call's records; must not overlap updates */
+    const int32_t *pending_accepted; /* [N] device: tokens of that call to keep */
+    int32_t pending_tokens;          /* that call's T */
+} kda_decode_multi_args;
+
+kda_status kda_decode_multi(const kda_decode_multi_args *args, hipStream_t stream);
+
+/*
+ * kda_decode_commit -- advance state and conv cache over the first accepted[n]
+ * tokens of sequence n, from the records one kda_decode_multi call wrote.
+ * accepted[] lives in device memory (it is usually computed on the GPU); a
+ * value outside [0, T] is clamped to that range, and 0 leaves the sequence
+ * untouched.
+ */
+typedef struct {
+    int32_t num_seqs;        /* N >= 1, as in the kda_decode_multi call */
+    int32_t num_heads;       /* H >= 1 */
+    int32_t head_dim_k;      /* must be 128 */
+    int32_t head_dim_v;      /* must be 128 */
+    int32_t num_tokens;      /* T of the kda_decode_multi call */
+    kda_dtype dtype;         /* dtype of conv_state */
+    const int32_t *accepted; /* [N] device */
+    const float *updates;    /* [N][H][T][KDA_UPDATE_FLOATS] records */
+    void *conv_state;        /* [N][3][CC] in/out */
+    float *state;            /* [N][H][dk][dv] fp32 in/out */
+} kda_decode_commit_args;
+
+kda_status kda_decode_commit(const kda_decode_commit_args *args, hipStream_t stream);
 
 #ifdef __cplusplus
 }

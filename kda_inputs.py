@@ -12,6 +12,9 @@ Workloads (H heads of dimension d = dk = dv = 128, the published head shape):
   2  decode   : 256 sequences x 1 token, H=64, bf16 tokens, state ~ 0.1 N(0,1)
   3  long     : 1 sequence, H=64, T=65536, gate pre-activation ~ N(2,1)
   4  varlen   : 16 sequences, lengths ~ U{512..16384}, state ~ 0.1 N(0,1)
+  5  spec     : 256 sequences x 6 speculative tokens (k = 5 drafts + 1), H=64,
+                bf16 tokens, state ~ 0.1 N(0,1), conv cache; accepted counts
+                1 + Binomial(5, 0.8) (about four of five drafts kept)
 
 Draw recipe (torch.Generator on the target device, seeded with the workload's
 seed, all draws fp32 standard normals unless stated), in this order:
@@ -37,7 +40,7 @@ H_MODEL = 64
 @dataclass
 class Workload:
     name: str
-    kind: str                      # "prefill" or "decode"
+    kind: str                      # "prefill", "decode" or "spec_decode"
     H: int = H_MODEL
     T: int = 0                     # tokens per sequence (dense prefill)
     num_seqs: int = 1
@@ -59,6 +62,8 @@ WORKLOADS = {
     3: Workload("long_prefill_bf16_B1_T65536_H64", "prefill", T=65536, gate_mean=2.0, seed=3),
     4: Workload("varlen_prefill_bf16_N16_U512_16384_H64", "prefill", num_seqs=16,
                 lengths=(512, 16384), state_std=0.1, seed=4),
+    5: Workload("spec_decode_bf16_N256_T6_H64", "spec_decode", num_seqs=256, T=6,
+                state_std=0.1, conv_cache=True, seed=5, extra={"accept_p": 0.8}),
 }
 
 
@@ -146,12 +151,45 @@ def make_decode(N, H, dtype=torch.bfloat16, seed=2, device="cpu", state_std=0.1,
     }
 
 
+def make_spec_decode(N, T, H, dtype=torch.bfloat16, seed=5, device="cpu", state_std=0.1,
+                     conv_w_std=0.5, gate_mean=0.0, dk=D, dv=D):
+    """T speculative tokens for each of N sequences ([N, T, H, .] layouts), with a
+    state and a conv cache; draws in the order of make_decode."""
+    g = _gen(device, seed)
+    q = _randn(g, (N, T, H, dk), device)
+    k = _unit_rows(_randn(g, (N, T, H, dk), device))
+    v = _randn(g, (N, T, H, dv), device)
+    CC = 2 * H * dk + H * dv
+    conv_w = _randn(g, (CC, 4), device, std=conv_w_std)
+    a = _randn(g, (N, T, H, dk), device, mean=gate_mean)
+    beta = torch.sigmoid(_randn(g, (N, T, H), device))
+    state = _randn(g, (N, H, dk, dv), device, std=state_std)
+    conv_state = _randn(g, (N, 3, CC), device).to(dtype)
+    return {
+        "q": q.to(dtype), "k": k.to(dtype), "v": v.to(dtype), "gate": a.to(dtype),
+        "beta": beta.to(dtype), "conv_w": conv_w, "state": state, "conv_state": conv_state,
+        "H": H, "T": T, "dk": dk, "dv": dv,
+    }
+
+
+def make_accepted(N, T, seed, p=0.8, device="cpu"):
+    """Accepted tokens per sequence of a speculative step: the first token always,
+    then each of the T - 1 drafts with probability p (int32 [N], values 1..T)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    kept = (torch.rand((N, T - 1), generator=g) < p).sum(1) if T > 1 else torch.zeros(N)
+    return (1 + kept).to(torch.int32).to(device)
+
+
 def workload_inputs(idx, device="cpu", H=None, T=None, num_seqs=None, seed=None):
     """Inputs of workload `idx`, optionally shrunk (fewer heads/tokens/sequences)
     with the same distributions, for parity cases the oracle finishes quickly."""
     w = WORKLOADS[idx]
     H = w.H if H is None else H
     seed = w.seed if seed is None else seed
+    if w.kind == "spec_decode":
+        N = w.num_seqs if num_seqs is None else num_seqs
+        return make_spec_decode(N, w.T if T is None else T, H, dtype=w.dtype, seed=seed,
+                                device=device, state_std=w.state_std, gate_mean=w.gate_mean)
     if w.kind == "decode":
         N = w.num_seqs if num_seqs is None else num_seqs
         return make_decode(N, H, dtype=w.dtype, seed=seed, device=device, state_std=w.state_std,
@@ -184,6 +222,7 @@ def prefill_flops_per_token_head(C=64, dk=D, dv=D):
     return 2 * (3 * lower * C * dk + 2 * lower * C * dv + 3 * dk * dv)
 
 
-__all__ = ["WORKLOADS", "Workload", "make_prefill", "make_decode", "workload_inputs",
+__all__ = ["WORKLOADS", "Workload", "make_prefill", "make_decode", "make_spec_decode",
+           "make_accepted", "workload_inputs",
            "make_lengths", "cu_from_lengths", "bytes_per_token_head",
            "prefill_flops_per_token_head", "D", "H_MODEL"]

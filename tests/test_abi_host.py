@@ -35,7 +35,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -52,6 +52,11 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(K.KdaPrefillArgs) == 48 + 16 * 8
     assert K.KdaDecodeArgs.q.offset == 32
     assert ctypes.sizeof(K.KdaDecodeArgs) == 32 + 10 * 8
+    assert K.KdaDecodeMultiArgs.q.offset == 40
+    assert K.KdaDecodeMultiArgs.pending_tokens.offset == 40 + 13 * 8
+    assert ctypes.sizeof(K.KdaDecodeMultiArgs) == 40 + 14 * 8
+    assert K.KdaDecodeCommitArgs.accepted.offset == 24
+    assert ctypes.sizeof(K.KdaDecodeCommitArgs) == 24 + 4 * 8
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
@@ -151,6 +156,75 @@ def test_decode_rejects_state_overlapping_output(lib):
     a = _decode_args()
     a.state = a.o
     assert lib.kda_decode(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def _multi_args(**kw):
+    a = K.KdaDecodeMultiArgs(num_seqs=2, num_heads=2, head_dim_k=128, head_dim_v=128,
+                             num_tokens=6, dtype=K.KDA_BF16, flags=0, scale=0.0,
+                             gate_lower_bound=-5.0)
+    base = 0x100000
+    for i, f in enumerate(("q", "k", "v", "gate", "beta", "conv_weight", "conv_state", "state",
+                           "o", "updates")):
+        setattr(a, f, ctypes.c_void_p(base + i * 0x1000000))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_tokens", 0, K.KDA_ERR_INVALID_ARG),
+    ("num_tokens", K.MAX_SPEC_TOKENS + 1, K.KDA_ERR_INVALID_ARG),
+    ("head_dim_v", 64, K.KDA_ERR_UNSUPPORTED),
+    ("updates", None, K.KDA_ERR_INVALID_ARG),
+    ("state", None, K.KDA_ERR_INVALID_ARG),
+    ("flags", 0x40, K.KDA_ERR_UNSUPPORTED),
+    ("pending_updates", ctypes.c_void_p(0x70000000), K.KDA_ERR_INVALID_ARG),  # no counts
+])
+def test_decode_multi_rejects_bad_arguments(lib, field, value, status):
+    a = _multi_args(**{field: value})
+    assert lib.kda_decode_multi(ctypes.byref(a), None) == status
+    assert lib.kda_last_error() != b""
+
+
+def test_decode_multi_rejects_overlaps(lib):
+    a = _multi_args()
+    a.updates = a.state  # records over the state
+    assert lib.kda_decode_multi(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    a = _multi_args(pending_accepted=ctypes.c_void_p(0x71000000), pending_tokens=6)
+    a.pending_updates = ctypes.c_void_p(a.updates + 64)  # overlaps this call's records
+    assert lib.kda_decode_multi(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    a = _multi_args(pending_updates=ctypes.c_void_p(0x70000000),
+                    pending_accepted=ctypes.c_void_p(0x71000000), pending_tokens=9)
+    assert lib.kda_decode_multi(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def _commit_args(**kw):
+    a = K.KdaDecodeCommitArgs(num_seqs=2, num_heads=2, head_dim_k=128, head_dim_v=128,
+                              num_tokens=6, dtype=K.KDA_BF16)
+    for i, f in enumerate(("accepted", "updates", "conv_state", "state")):
+        setattr(a, f, ctypes.c_void_p(0x100000 + i * 0x1000000))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_seqs", 0, K.KDA_ERR_INVALID_ARG),
+    ("num_tokens", 9, K.KDA_ERR_INVALID_ARG),
+    ("head_dim_k", 256, K.KDA_ERR_UNSUPPORTED),
+    ("accepted", None, K.KDA_ERR_INVALID_ARG),
+    ("updates", None, K.KDA_ERR_INVALID_ARG),
+    ("dtype", 5, K.KDA_ERR_INVALID_ARG),
+])
+def test_decode_commit_rejects_bad_arguments(lib, field, value, status):
+    a = _commit_args(**{field: value})
+    assert lib.kda_decode_commit(ctypes.byref(a), None) == status
+
+
+def test_decode_commit_rejects_records_over_state(lib):
+    a = _commit_args()
+    a.updates = ctypes.c_void_p(a.state + 4096)
+    assert lib.kda_decode_commit(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
 
 
 def test_short_conv_rejects_bad_arguments(lib):

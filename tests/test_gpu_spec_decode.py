@@ -1,0 +1,225 @@
+"""GPU parity of speculative multi-token decode (kda_decode_multi + kda_decode_commit).
+
+The oracle is the token-by-token fp64 prefill: T speculative tokens of a sequence
+are a prefill of T tokens from the sequence's state and conv cache, and a commit
+of `a` accepted tokens is that prefill over the first `a` of them.  Bars as for
+every entry point: fp32 max-abs <= 1e-4; bf16 relative L2 <= 2e-2 per (sequence,
+head).  A second, stricter property ties the path to single-token decode: the
+outputs, the committed state and the conv cache equal those of `a` kda_decode
+calls bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as KI
+import oracle
+import gated_delta_rule_short_amd as kda
+from tests._gpu_common import (BF16_REL, assert_f32_close, seeded, slice_rel_errors,
+                               state_rel_errors, to_np)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kda.load_library()
+
+
+def _flat(x):
+    """[N, T, ...] -> [N*T, ...] (the packed prefill layout)."""
+    return x.reshape((-1,) + tuple(x.shape[2:]))
+
+
+def _oracle_prefix(d, counts, state, conv_state, t0=0, **kw):
+    """Oracle prefill of tokens t0 .. t0+counts[n]-1 of every sequence n."""
+    N = d["q"].shape[0]
+    sel = [slice(t0, t0 + int(c)) for c in counts]
+    cat = lambda x: torch.cat([x[n, sel[n]].cpu() for n in range(N)], 0)
+    cu = np.concatenate([[0], np.cumsum([int(c) for c in counts])]).astype(np.int32)
+    return oracle.prefill(cat(d["q"]), cat(d["k"]), cat(d["v"]), cat(d["gate"]), cat(d["beta"]),
+                          d["conv_w"], cu, state_in=state, conv_state_in=conv_state, **kw)
+
+
+def _check(x, ref, dtype, what):
+    """x, ref: [..., 128] rows; fp32 max-abs, bf16 relative L2 per row group."""
+    if dtype == torch.float32:
+        assert_f32_close(x, ref, what)
+    else:
+        a, b = to_np(x).reshape(-1, 128), to_np(ref).reshape(-1, 128)
+        e = np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-30)
+        assert e.max() <= BF16_REL, "%s rel err %.3g" % (what, e.max())
+
+
+def _check_state(st, ref, dtype, what):
+    if dtype == torch.float32:
+        assert_f32_close(st, ref, what)
+    else:
+        assert state_rel_errors(st, ref).max() <= BF16_REL, what
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("flags", [0, kda.KDA_F_SILU | kda.KDA_F_GATE_IS_LOG, kda.KDA_F_NO_QK_L2NORM])
+@pytest.mark.parametrize("T", [1, 6, 8])
+def test_multi_and_commit_match_oracle(dtype, flags, T):
+    N, H = 7, 3
+    d = KI.make_spec_decode(N, T, H, dtype=dtype, seed=31 + T, device=DEV)
+    if flags & kda.KDA_F_GATE_IS_LOG:
+        d["gate"] = (-6.0 * seeded(d["gate"].shape, 32, "rand")).to(dtype)
+    bias = 0.1 * seeded(d["conv_w"].shape[0], 33)
+    st0, cs0 = d["state"].clone(), d["conv_state"].clone()
+    o, upd = kda.kda_decode_multi(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"],
+                                  d["conv_state"], d["state"], conv_bias=bias, flags=flags)
+    torch.cuda.synchronize()
+    # verification leaves the state and the conv cache untouched
+    assert torch.equal(d["state"], st0) and torch.equal(d["conv_state"], cs0)
+    ref = _oracle_prefix(d, [T] * N, st0.cpu(), cs0.cpu(), conv_b=bias.cpu(), flags=flags)
+    _check(o, ref["o"].reshape(N, T, H, 128), dtype, "multi o")
+    # rows 3..5 of the records hold the raw tokens exactly
+    u = upd.view(N, H, T, 6, 128)
+    for row, x in ((3, d["q"]), (4, d["k"]), (5, d["v"])):
+        assert torch.equal(u[:, :, :, row], x.float().permute(0, 2, 1, 3))
+    # commit accepted prefixes, including none, all and out-of-range counts
+    acc = torch.tensor([0, 1, T, min(3, T), T + 4, -2, max(T - 1, 0)], dtype=torch.int32)
+    kda.kda_decode_commit(upd, acc.to(DEV), d["conv_state"], d["state"])
+    torch.cuda.synchronize()
+    keep = acc.clamp(0, T)
+    refc = _oracle_prefix(d, keep.tolist(), st0.cpu(), cs0.cpu(), conv_b=bias.cpu(), flags=flags)
+    _check_state(d["state"], refc["state"], dtype, "committed state")
+    np.testing.assert_array_equal(to_np(d["conv_state"]), refc["conv_state"])
+    for n in (0, 5):  # nothing accepted: bit-identical
+        assert torch.equal(d["state"][n], st0[n]) and torch.equal(d["conv_state"][n], cs0[n])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_multi_and_commit_equal_decode_steps_bitwise(dtype):
+    N, H, T = 5, 4, 6
+    d = KI.make_spec_decode(N, T, H, dtype=dtype, seed=41, device=DEV)
+    bias = 0.1 * seeded(d["conv_w"].shape[0], 42)
+    flags = kda.KDA_F_SILU
+    # T single-token decode steps, keeping every intermediate state
+    st, cs = d["state"].clone(), d["conv_state"].clone()
+    outs, states, convs = [], [st.clone()], [cs.clone()]
+    for t in range(T):
+        outs.append(kda.kda_decode(d["q"][:, t].contiguous(), d["k"][:, t].contiguous(),
+                                   d["v"][:, t].contiguous(), d["gate"][:, t].contiguous(),
+                                   d["beta"][:, t].contiguous(), d["conv_w"], cs, st,
+                                   conv_bias=bias, flags=flags))
+        states.append(st.clone())
+        convs.append(cs.clone())
+    o, upd = kda.kda_decode_multi(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"],
+                                  d["conv_state"], d["state"], conv_bias=bias, flags=flags)
+    acc = torch.tensor([1, 2, 4, 6, 3], dtype=torch.int32)
+    kda.kda_decode_commit(upd, acc.to(DEV), d["conv_state"], d["state"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, torch.stack(outs, 1))
+    for n, a in enumerate(acc.tolist()):
+        assert torch.equal(d["state"][n], states[a][n]), n
+        assert torch.equal(d["conv_state"][n], convs[a][n]), n
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_fused_pending_commit(dtype):
+    """Two speculative steps; the second applies the first's commit itself."""
+    N, H, T1, T2 = 6, 3, 6, 4
+    d1 = KI.make_spec_decode(N, T1, H, dtype=dtype, seed=51, device=DEV)
+    d2 = KI.make_spec_decode(N, T2, H, dtype=dtype, seed=52, device=DEV)
+    d2["conv_w"] = d1["conv_w"]
+    st0, cs0 = d1["state"].clone(), d1["conv_state"].clone()
+    acc1 = torch.tensor([1, 6, 3, 0, 5, 2], dtype=torch.int32, device=DEV)
+    _, upd1 = kda.kda_decode_multi(d1["q"], d1["k"], d1["v"], d1["gate"], d1["beta"],
+                                   d1["conv_w"], d1["conv_state"], d1["state"])
+    # separate commit, then step two
+    st_a, cs_a = st0.clone(), cs0.clone()
+    kda.kda_decode_commit(upd1, acc1, cs_a, st_a)
+    o_a, upd_a = kda.kda_decode_multi(d2["q"], d2["k"], d2["v"], d2["gate"], d2["beta"],
+                                      d2["conv_w"], cs_a, st_a)
+    # fused: step two commits step one first
+    o_b, upd_b = kda.kda_decode_multi(d2["q"], d2["k"], d2["v"], d2["gate"], d2["beta"],
+                                      d2["conv_w"], d1["conv_state"], d1["state"],
+                                      pending_updates=upd1, pending_accepted=acc1)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(upd_a, upd_b)
+    assert torch.equal(d1["state"], st_a) and torch.equal(d1["conv_state"], cs_a)
+    # against the oracle: accepted prefix of step one, then all of step two
+    a1 = acc1.cpu().tolist()
+    cat = lambda x1, x2: torch.cat([torch.cat([x1[n, :a1[n]].cpu(), x2[n].cpu()], 0)
+                                    for n in range(N)], 0)
+    cu = np.concatenate([[0], np.cumsum([a + T2 for a in a1])]).astype(np.int32)
+    ref = oracle.prefill(cat(d1["q"], d2["q"]), cat(d1["k"], d2["k"]), cat(d1["v"], d2["v"]),
+                         cat(d1["gate"], d2["gate"]), cat(d1["beta"], d2["beta"]), d1["conv_w"],
+                         cu, state_in=st0.cpu(), conv_state_in=cs0.cpu())
+    ro = np.stack([ref["o"][cu[n + 1] - T2:cu[n + 1]] for n in range(N)])
+    _check(o_b, ro, dtype, "step two o")
+
+
+def test_commit_all_equals_prefill_chunks():
+    """Accepting every token equals a bf16 prefill over them (one state layout for
+    both); the bar is the bf16 one per (sequence, head), as both sides round
+    differently (bf16 matrix-core operands in prefill, fp32 in decode)."""
+    N, H, T = 4, 2, 8
+    d = KI.make_spec_decode(N, T, H, seed=61, device=DEV)
+    st0, cs0 = d["state"].clone(), d["conv_state"].clone()
+    o, upd = kda.kda_decode_multi(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"],
+                                  d["conv_state"], d["state"])
+    kda.kda_decode_commit(upd, torch.full((N,), T, dtype=torch.int32, device=DEV),
+                          d["conv_state"], d["state"])
+    cu = torch.arange(0, (N + 1) * T, T, dtype=torch.int32, device=DEV)
+    po, pst, pcs = kda.kda_prefill(_flat(d["q"]), _flat(d["k"]), _flat(d["v"]), _flat(d["gate"]),
+                                   _flat(d["beta"]), d["conv_w"], cu_seqlens=cu, state_in=st0,
+                                   conv_state_in=cs0, state_out=True, conv_state_out=True)
+    torch.cuda.synchronize()
+    e = slice_rel_errors(_flat(o), po, cu.cpu().tolist(), H)
+    assert e.max() <= BF16_REL, e.max()
+    assert state_rel_errors(d["state"], pst).max() <= BF16_REL
+    assert torch.equal(d["conv_state"], pcs)
+
+
+def test_spec_workload_full_size_sampled():
+    """256 sequences x 6 tokens x 64 heads, fused with the previous step's commit, as
+    timed; the oracle checks sampled sequences."""
+    d0 = KI.workload_inputs(5, device=DEV)
+    d = KI.workload_inputs(5, device=DEV, seed=105)
+    d["conv_w"] = d0["conv_w"]
+    N, T = d0["q"].shape[:2]
+    acc0 = KI.make_accepted(N, T, seed=5, device=DEV)
+    st0, cs0 = d0["state"].clone(), d0["conv_state"].clone()
+    _, upd0 = kda.kda_decode_multi(d0["q"], d0["k"], d0["v"], d0["gate"], d0["beta"],
+                                   d0["conv_w"], d0["conv_state"], d0["state"])
+    o, upd = kda.kda_decode_multi(d["q"], d["k"], d["v"], d["gate"], d["beta"], d0["conv_w"],
+                                  d0["conv_state"], d0["state"], pending_updates=upd0,
+                                  pending_accepted=acc0)
+    acc = KI.make_accepted(N, T, seed=6, device=DEV)
+    kda.kda_decode_commit(upd, acc, d0["conv_state"], d0["state"])
+    torch.cuda.synchronize()
+    a0, a1 = acc0.cpu().tolist(), acc.cpu().tolist()
+    for n in (0, 77, 255):
+        sl = slice(n, n + 1)
+        L = a0[n] + T
+        cat = lambda x0, x1: torch.cat([x0[n, :a0[n]].cpu(), x1[n].cpu()], 0)
+        ref = oracle.prefill(cat(d0["q"], d["q"]), cat(d0["k"], d["k"]), cat(d0["v"], d["v"]),
+                             cat(d0["gate"], d["gate"]), cat(d0["beta"], d["beta"]), d0["conv_w"],
+                             np.array([0, L], np.int32), state_in=st0[sl].cpu(),
+                             conv_state_in=cs0[sl].cpu())
+        _check(o[n], ref["o"][a0[n]:], torch.bfloat16, "o seq %d" % n)
+        # state after both commits: a0 of step one, then a1 of step two
+        L2 = a0[n] + a1[n]
+        ref2 = oracle.prefill(cat(d0["q"], d["q"])[:L2], cat(d0["k"], d["k"])[:L2],
+                              cat(d0["v"], d["v"])[:L2], cat(d0["gate"], d["gate"])[:L2],
+                              cat(d0["beta"], d["beta"])[:L2], d0["conv_w"],
+                              np.array([0, L2], np.int32), state_in=st0[sl].cpu(),
+                              conv_state_in=cs0[sl].cpu())
+        assert state_rel_errors(d0["state"][sl], ref2["state"]).max() <= BF16_REL, n
+        np.testing.assert_array_equal(to_np(d0["conv_state"][sl]), ref2["conv_state"])
+
+
+def test_multi_rejects_overlapping_records():
+    d = KI.make_spec_decode(2, 4, 2, seed=71, device=DEV)
+    _, upd = kda.kda_decode_multi(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"],
+                                  d["conv_state"], d["state"])
+    acc = torch.ones(2, dtype=torch.int32, device=DEV)
+    with pytest.raises(kda.KdaError):
+        kda.kda_decode_multi(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"],
+                             d["conv_state"], d["state"], updates=upd, pending_updates=upd,
+                             pending_accepted=acc)
