@@ -107,7 +107,7 @@ __device__ __forceinline__ f32x4 token_step(f32x4 (&st)[16], const float *sa, co
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[e] = swap32_sum(ak[e], aq[e]);
     part[wave][cg][(tid >> 5) & 1] = red;
-    __syncthreads();
+    barrier_lds();
     const f32x4 s_k = part[0][cg][0] + part[1][cg][0] + part[2][cg][0] + part[3][cg][0];
     const f32x4 s_q = part[0][cg][1] + part[1][cg][1] + part[2][cg][1] + part[3][cg][1];
     const f32x4 u = beta * (vv - s_k);
@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
             s_red[wave][2] = part_qk;
         }
     }
-    __syncthreads();
+    barrier_lds();
     float iq, ik, kq;
     norm_scales(s_red, l2, iq, ik, kq);
     const float beta = to_f32(reinterpret_cast<const T *>(p.beta)[pr]);
@@ -410,7 +410,7 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
             }
         }
     }
-    __syncthreads();
+    barrier_lds();
 
     // apply the pending commit and store the committed state
     if (na > 0) {
@@ -431,7 +431,7 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
             rec[(size_t)t * kRec + D + c] = kn;
         }
     }
-    __syncthreads();
+    barrier_lds();
 
     // the T tokens in order, on the state held in registers
     T *ob = reinterpret_cast<T *>(p.o) + base + 4 * cg;
@@ -488,7 +488,7 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
         cs[CC + ch] = from_f32<T>(h1);
         cs[2 * CC + ch] = from_f32<T>(h2);
     }
-    __syncthreads();
+    barrier_lds();
     for (int t = 0; t < na; ++t)
         replay_token(st, s_pend[t][0], s_pend[t][1],
                      *reinterpret_cast<const f32x4 *>(&s_pend[t][2][4 * cg]), tid);
