@@ -15,6 +15,8 @@ k = 5 drafted tokens plus one):
                commits the previous call's accepted prefix (1 + Binomial(5, 0.8)
                tokens per sequence), then verifies 6 new tokens
                                          (kda_decode_multi with pending records)
+  spec_commit: the same commit on its own, as at the end of a speculative
+               run                                          (kda_decode_commit)
 Every call is bracketed by HIP events on the stream it is launched on, after a
 512 MiB scratch write that evicts L2 and the MALL (not timed); `value` is
 prefill tokens per second per layer from the median prefill call time, decode
@@ -65,7 +67,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "short_conv", "spec_decode",
-                                       "copy"],
+                                       "spec_commit", "copy"],
                     default="all", help="run one entry point only (for profiler passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -128,6 +130,9 @@ def main():
                              Sp["conv_state"], Sp["state"], updates=rec_sp[i], o=o_sp,
                              pending_updates=rec_sp[i ^ 1], pending_accepted=acc_sp)
 
+    def run_commit():
+        kda.kda_decode_commit(rec_sp[0], acc_sp, Sp["conv_state"], Sp["state"])
+
     # the first verification has nothing to commit: it primes the pending records
     kda.kda_decode_multi(Sp["q"], Sp["k"], Sp["v"], Sp["gate"], Sp["beta"], Sp["conv_w"],
                          Sp["conv_state"], Sp["state"], updates=rec_sp[1], o=o_sp)
@@ -139,10 +144,10 @@ def main():
         copy_dst.copy_(copy_src)
 
     ops = {"prefill": run_prefill, "decode": run_decode, "short_conv": run_conv,
-           "spec_decode": run_spec, "copy": run_copy}
+           "spec_decode": run_spec, "spec_commit": run_commit, "copy": run_copy}
     step_names = ["short_conv", "prefill", "decode"]
     if args.only == "all":
-        names = step_names + ["spec_decode"]
+        names = step_names + ["spec_decode", "spec_commit"]
     else:
         names = [args.only]
 
@@ -248,6 +253,7 @@ def main():
             "workload": "256 sequences x 6 tokens (k=5 drafts + 1), H=64, bf16 tokens, fp32 "
                         "state; fused commit of the previous step's accepted prefix",
             "us_per_call": round(ms["spec_decode"] * 1e3, 2),
+            "commit_us_per_call": round(ms["spec_commit"] * 1e3, 2),
             "verified_tokens_per_s": round(N_sp * T_sp / sp_s, 1),
             "accepted_tokens_per_s": round(sum(max(0, min(T_sp, a_)) for a_ in acc_l) / sp_s, 1),
             "mean_accepted": round(sum(acc_l) / len(acc_l), 3),
