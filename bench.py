@@ -9,8 +9,9 @@ with all inputs already resident in HBM:
                updated in place, bf16 tokens                  (kda_decode)
   short_conv : the same 4096-token q|k|v rows as a [4096, 24576] bf16 tensor,
                conv width 4                                   (kda_short_conv)
-and, reported beside the step, one speculative decode step (verification of
-k = 5 drafted tokens plus one):
+and, reported beside the step, the same decode with the state stored as bf16
+(KDA_F_STATE_BF16), and one speculative decode step (verification of k = 5
+drafted tokens plus one):
   spec_decode: 256 sequences x 6 tokens, 64 heads, fp32 state; each call first
                commits the previous call's accepted prefix (1 + Binomial(5, 0.8)
                tokens per sequence), then verifies 6 new tokens
@@ -66,8 +67,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "short_conv", "spec_decode",
-                                       "spec_commit", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "decode_bf16_state", "short_conv",
+                                       "spec_decode", "spec_commit", "copy"],
                     default="all", help="run one entry point only (for profiler passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -100,6 +101,9 @@ def main():
     Dd = KI.workload_inputs(2, device=dev)
     N_dec = Dd["q"].shape[0]
     o_dec = torch.empty_like(Dd["v"])
+    st16 = Dd["state"].to(torch.bfloat16)  # the same workload with 16-bit state storage
+    cs16 = Dd["conv_state"].clone()
+    o_dec16 = torch.empty_like(Dd["v"])
     X = torch.cat([P["q"].reshape(T, -1), P["k"].reshape(T, -1), P["v"].reshape(T, -1)], 1).contiguous()
     Y = torch.empty_like(X)
     cu1 = P["cu_seqlens"]
@@ -137,6 +141,10 @@ def main():
     kda.kda_decode_multi(Sp["q"], Sp["k"], Sp["v"], Sp["gate"], Sp["beta"], Sp["conv_w"],
                          Sp["conv_state"], Sp["state"], updates=rec_sp[1], o=o_sp)
 
+    def run_decode16():
+        kda.kda_decode(Dd["q"], Dd["k"], Dd["v"], Dd["gate"], Dd["beta"], Dd["conv_w"], cs16, st16,
+                       o=o_dec16)
+
     def run_conv():
         kda.kda_short_conv(X, P["conv_w"], cu_seqlens=cu1, y=Y)
 
@@ -144,10 +152,11 @@ def main():
         copy_dst.copy_(copy_src)
 
     ops = {"prefill": run_prefill, "decode": run_decode, "short_conv": run_conv,
-           "spec_decode": run_spec, "spec_commit": run_commit, "copy": run_copy}
+           "decode_bf16_state": run_decode16, "spec_decode": run_spec, "spec_commit": run_commit,
+           "copy": run_copy}
     step_names = ["short_conv", "prefill", "decode"]
     if args.only == "all":
-        names = step_names + ["spec_decode", "spec_commit"]
+        names = step_names + ["decode_bf16_state", "spec_decode", "spec_commit"]
     else:
         names = [args.only]
 
@@ -249,6 +258,20 @@ def main():
             "algorithmic_bytes_per_launch": dec_state_bytes + dec_other,
         },
         "short_conv_GBps": round(conv_bytes / (ms["short_conv"] * 1e-3) / 1e9, 1),
+        "decode_bf16_state": {
+            "workload": "workload 2 with the state stored as bf16 (256 x 64 x 128 x 128, 512 MiB)",
+            "us_per_call": round(ms["decode_bf16_state"] * 1e3, 2),
+            "state_GBps": round(dec_state_bytes / 2 / (ms["decode_bf16_state"] * 1e-3) / 1e9, 1),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round((dec_state_bytes / 2 + dec_other) / (ms["decode_bf16_state"] * 1e-3) / 1e9, 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round((dec_state_bytes / 2 + dec_other) / (ms["decode_bf16_state"] * 1e-3) / 1e9
+                              / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes_per_launch": dec_state_bytes // 2 + dec_other,
+            },
+        },
         "spec_decode": {
             "workload": "256 sequences x 6 tokens (k=5 drafts + 1), H=64, bf16 tokens, fp32 "
                         "state; fused commit of the previous step's accepted prefix",

@@ -29,6 +29,7 @@ kda_status hip_fail(hipError_t e, const char *what) {
 }
 
 size_t esize(kda_dtype d) { return d == KDA_BF16 ? 2 : 4; }
+size_t state_esize(uint32_t flags) { return (flags & KDA_F_STATE_BF16) ? 2 : 4; }
 
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
@@ -51,13 +52,13 @@ kda_status check_cu_host(const int32_t *cu, int32_t n, int64_t total) {
 }
 
 kda_status check_common(int32_t num_seqs, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
-                        uint32_t flags, float scale, float lb) {
+                        uint32_t flags, float scale, float lb, uint32_t allowed = KDA_F_ALL) {
     if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs = %d, must be >= 1", num_seqs);
     if (H < 1) return fail(KDA_ERR_INVALID_ARG, "num_heads = %d, must be >= 1", H);
     if (dk != 128 || dv != 128)
         return fail(KDA_ERR_UNSUPPORTED, "head dims %d x %d: only 128 x 128 is supported", dk, dv);
     if (dt != KDA_F32 && dt != KDA_BF16) return fail(KDA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
-    if (flags & ~(uint32_t)KDA_F_ALL) return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+    if (flags & ~allowed) return fail(KDA_ERR_UNSUPPORTED, "unsupported flags 0x%x", flags);
     if (!std::isfinite(scale) || scale < 0.f)
         return fail(KDA_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 = default)");
     if (!std::isfinite(lb) || !(lb < 0.f))
@@ -168,7 +169,7 @@ kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
         if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
     if (overlap(a->o, tok, a->beta, (size_t)T * H * es))
         return fail(KDA_ERR_INVALID_ARG, "o overlaps beta");
-    const size_t sb = (size_t)a->num_seqs * H * 128 * 128 * 4;
+    const size_t sb = (size_t)a->num_seqs * H * 128 * 128 * state_esize(a->flags);
     if (a->state_out && (const void *)a->state_out != (const void *)a->state_in &&
         overlap(a->state_out, sb, a->state_in, sb))
         return fail(KDA_ERR_INVALID_ARG, "state_out partially overlaps state_in");
@@ -227,7 +228,7 @@ kda_status kda_decode(const kda_decode_args *a, hipStream_t stream) {
                                          "state must be non-NULL");
     const size_t es = esize(a->dtype);
     const size_t tok = (size_t)a->num_seqs * a->num_heads * 128 * es;
-    const size_t sb = (size_t)a->num_seqs * a->num_heads * 128 * 128 * 4;
+    const size_t sb = (size_t)a->num_seqs * a->num_heads * 128 * 128 * state_esize(a->flags);
     const void *ins[4] = {a->q, a->k, a->v, a->gate};
     for (const void *in : ins) {
         if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
@@ -264,7 +265,7 @@ kda_status kda_decode_multi(const kda_decode_multi_args *a, hipStream_t stream) 
     const size_t es = esize(a->dtype);
     const size_t NH = (size_t)a->num_seqs * a->num_heads;
     const size_t tok = NH * a->num_tokens * 128 * es;
-    const size_t sb = NH * 128 * 128 * 4;
+    const size_t sb = NH * 128 * 128 * state_esize(a->flags);
     const size_t cb = (size_t)a->num_seqs * 3 * 3 * a->num_heads * 128 * es;
     const size_t rb = NH * a->num_tokens * KDA_UPDATE_FLOATS * 4;
     const size_t pb = a->pending_updates ? NH * a->pending_tokens * KDA_UPDATE_FLOATS * 4 : 0;
@@ -297,7 +298,7 @@ kda_status kda_decode_commit(const kda_decode_commit_args *a, hipStream_t stream
     g_err[0] = 0;
     if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
     kda_status st = check_common(a->num_seqs, a->num_heads, a->head_dim_k, a->head_dim_v, a->dtype,
-                                 0u, 0.f, -1.f);
+                                 a->flags, 0.f, -1.f, KDA_F_STATE_BF16);
     if (st != KDA_OK) return st;
     if (a->num_tokens < 1 || a->num_tokens > KDA_MAX_SPEC_TOKENS)
         return fail(KDA_ERR_INVALID_ARG, "num_tokens = %d, must be in 1..%d", a->num_tokens,
@@ -305,7 +306,7 @@ kda_status kda_decode_commit(const kda_decode_commit_args *a, hipStream_t stream
     if (!a->accepted || !a->updates || !a->conv_state || !a->state)
         return fail(KDA_ERR_INVALID_ARG, "accepted, updates, conv_state and state must be non-NULL");
     const size_t NH = (size_t)a->num_seqs * a->num_heads;
-    const size_t sb = NH * 128 * 128 * 4;
+    const size_t sb = NH * 128 * 128 * state_esize(a->flags);
     const size_t cb = (size_t)a->num_seqs * 3 * 3 * a->num_heads * 128 * esize(a->dtype);
     const size_t rb = NH * a->num_tokens * KDA_UPDATE_FLOATS * 4;
     if (overlap(a->updates, rb, a->state, sb) || overlap(a->updates, rb, a->conv_state, cb) ||

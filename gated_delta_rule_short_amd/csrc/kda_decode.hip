@@ -130,19 +130,39 @@ __device__ __forceinline__ void replay_token(f32x4 (&st)[16], const float *alpha
     }
 }
 
-__device__ __forceinline__ void load_state(f32x4 (&st)[16], const float *S, int tid) {
+// The state of one (sequence, head) moves between HBM and this thread's 16 x 4
+// slice with non-temporal accesses: it is streamed exactly once each way, and
+// must not displace the small, reused operands in L2.  SB is the storage type:
+// fp32, or bf16 (widened exactly on load, rounded to nearest even on store).
+template <typename SB>
+__device__ __forceinline__ void load_state(f32x4 (&st)[16], const SB *S, int tid) {
     const int cg = tid & 31, rg = tid >> 5;
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-        st[m] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4 *>(S + (size_t)(rg + 8 * m) * D + 4 * cg));
+    for (int m = 0; m < 16; ++m) {
+        const SB *src = S + (size_t)(rg + 8 * m) * D + 4 * cg;
+        if constexpr (sizeof(SB) == 4) {
+            st[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src));
+        } else {
+            const uint64_t w = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(src));
+            const uint32_t lo = (uint32_t)w, hi = (uint32_t)(w >> 32);
+            st[m] = f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                          __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+        }
+    }
 }
 
-__device__ __forceinline__ void store_state(const f32x4 (&st)[16], float *S, int tid) {
+template <typename SB>
+__device__ __forceinline__ void store_state(const f32x4 (&st)[16], SB *S, int tid) {
     const int cg = tid & 31, rg = tid >> 5;
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-        __builtin_nontemporal_store(st[m], reinterpret_cast<f32x4 *>(S + (size_t)(rg + 8 * m) * D + 4 * cg));
+    for (int m = 0; m < 16; ++m) {
+        SB *dst = S + (size_t)(rg + 8 * m) * D + 4 * cg;
+        if constexpr (sizeof(SB) == 4)
+            __builtin_nontemporal_store(st[m], reinterpret_cast<f32x4 *>(dst));
+        else
+            __builtin_nontemporal_store(__builtin_bit_cast(uint64_t, pack4(st[m])),
+                                        reinterpret_cast<uint64_t *>(dst));
+    }
 }
 
 __device__ __forceinline__ int clamp_count(int a, int hi) { return a < 0 ? 0 : (a > hi ? hi : a); }
@@ -180,14 +200,14 @@ struct DecodeParams {
     const void *q, *k, *v, *gate, *beta;
     const float *w, *bias;
     void *cs;
-    float *state;
+    void *state;  // fp32 or bf16 (SB)
     void *o;
     int H;
     float scale, lb;
     uint32_t flags;
 };
 
-template <typename T>
+template <typename T, typename SB>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
 #pragma clang fp contract(off)
     const int pr = blockIdx.x;
@@ -203,7 +223,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
     // 1. issue the state loads (independent of the prologue).  The state is
     // streamed exactly once each way: non-temporal loads and stores keep it from
     // displacing the small, reused operands in L2.
-    float *S = p.state + (size_t)pr * D * D;
+    SB *S = reinterpret_cast<SB *>(p.state) + (size_t)pr * D * D;
     f32x4 st[16];
     load_state(st, S, tid);
 
@@ -270,7 +290,7 @@ struct MultiParams {
     const void *q, *k, *v, *gate, *beta;
     const float *w, *bias;
     void *cs;
-    float *state;
+    void *state;          // fp32 or bf16 (SB)
     void *o;
     float *rec;           // [N][H][T][kRec] written
     const float *prec;    // pending records [N][H][pT][kRec] or null
@@ -280,7 +300,7 @@ struct MultiParams {
     uint32_t flags;
 };
 
-template <typename T>
+template <typename T, typename SB>
 __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
 #pragma clang fp contract(off)
     const int pr = blockIdx.x;
@@ -329,7 +349,7 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
     const float b0 = p.bias ? p.bias[ch0] : 0.f, b1 = p.bias ? p.bias[ch1] : 0.f;
     if (!qk && c < NT) s_beta[c] = to_f32(reinterpret_cast<const T *>(p.beta)[((size_t)n * NT + c) * H + h]);
 
-    float *S = p.state + (size_t)pr * D * D;
+    SB *S = reinterpret_cast<SB *>(p.state) + (size_t)pr * D * D;
     f32x4 st[16];
     load_state(st, S, tid);
 
@@ -455,11 +475,11 @@ struct CommitParams {
     const int32_t *acc;
     const float *rec;
     void *cs;
-    float *state;
+    void *state;  // fp32 or bf16 (SB)
     int H, T;
 };
 
-template <typename T>
+template <typename T, typename SB>
 __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
 #pragma clang fp contract(off)
     const int pr = blockIdx.x;
@@ -470,7 +490,7 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
     if (na == 0) return;  // uniform over the workgroup
 
     __shared__ __attribute__((aligned(16))) float s_pend[kMaxSpec][3][D];
-    float *S = p.state + (size_t)pr * D * D;
+    SB *S = reinterpret_cast<SB *>(p.state) + (size_t)pr * D * D;
     f32x4 st[16];
     load_state(st, S, tid);
     const float *rec = p.rec + (size_t)pr * p.T * kRec;
@@ -495,6 +515,16 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
     store_state(st, S, tid);
 }
 
+// Launch of the instance for (token dtype, state storage): one workgroup of 256
+// threads per (sequence, head).
+template <typename P>
+static void launch_typed(kda_dtype dt, uint32_t flags, unsigned blocks, const P &p, hipStream_t s,
+                         void (*bb)(P), void (*bf)(P), void (*fb)(P), void (*ff)(P)) {
+    const bool sb16 = flags & KDA_F_STATE_BF16;
+    void (*k)(P) = dt == KDA_BF16 ? (sb16 ? bb : bf) : (sb16 ? fb : ff);
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, s, p);
+}
+
 hipError_t launch_decode(const kda_decode_args *a, hipStream_t s) {
     DecodeParams p;
     p.q = a->q; p.k = a->k; p.v = a->v; p.gate = a->gate; p.beta = a->beta;
@@ -503,10 +533,8 @@ hipError_t launch_decode(const kda_decode_args *a, hipStream_t s) {
     p.H = a->num_heads;
     p.scale = a->scale; p.lb = a->gate_lower_bound; p.flags = a->flags;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    if (a->dtype == KDA_BF16)
-        hipLaunchKernelGGL(decode_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL(decode_kernel<float>, dim3(blocks), dim3(256), 0, s, p);
+    launch_typed<DecodeParams>(a->dtype, a->flags, blocks, p, s,
+                     decode_kernel<__bf16, __bf16>, decode_kernel<__bf16, float>, decode_kernel<float, __bf16>, decode_kernel<float, float>);
     return hipGetLastError();
 }
 
@@ -519,10 +547,8 @@ hipError_t launch_decode_multi(const kda_decode_multi_args *a, hipStream_t s) {
     p.H = a->num_heads; p.T = a->num_tokens; p.pT = a->pending_updates ? a->pending_tokens : 0;
     p.scale = a->scale; p.lb = a->gate_lower_bound; p.flags = a->flags;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    if (a->dtype == KDA_BF16)
-        hipLaunchKernelGGL(multi_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL(multi_kernel<float>, dim3(blocks), dim3(256), 0, s, p);
+    launch_typed<MultiParams>(a->dtype, a->flags, blocks, p, s,
+                     multi_kernel<__bf16, __bf16>, multi_kernel<__bf16, float>, multi_kernel<float, __bf16>, multi_kernel<float, float>);
     return hipGetLastError();
 }
 
@@ -531,10 +557,8 @@ hipError_t launch_decode_commit(const kda_decode_commit_args *a, hipStream_t s) 
     p.acc = a->accepted; p.rec = a->updates; p.cs = a->conv_state; p.state = a->state;
     p.H = a->num_heads; p.T = a->num_tokens;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    if (a->dtype == KDA_BF16)
-        hipLaunchKernelGGL(commit_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL(commit_kernel<float>, dim3(blocks), dim3(256), 0, s, p);
+    launch_typed<CommitParams>(a->dtype, a->flags, blocks, p, s,
+                     commit_kernel<__bf16, __bf16>, commit_kernel<__bf16, float>, commit_kernel<float, __bf16>, commit_kernel<float, float>);
     return hipGetLastError();
 }
 

@@ -59,8 +59,9 @@ struct PrefillParams {
     const void *q, *k, *v, *gate, *beta;
     const float *w, *bias;
     const void *cs_in;
-    const float *state_in;
-    float *state_out;
+    const void *state_in;   // fp32, or bf16 when state_bf16
+    void *state_out;
+    int state_bf16;
     void *o;
     const int32_t *cu;
     int64_t total;
@@ -219,8 +220,10 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * mt + 4 * g4 + i;
-                S[mt][j][i] = (st_wave && p.state_in)
-                                  ? p.state_in[((size_t)pr * D + row) * D + col] : 0.f;
+                const size_t at = ((size_t)pr * D + row) * D + col;
+                S[mt][j][i] = !(st_wave && p.state_in) ? 0.f
+                              : p.state_bf16 ? (float)reinterpret_cast<const __bf16 *>(p.state_in)[at]
+                                             : reinterpret_cast<const float *>(p.state_in)[at];
             }
         }
 
@@ -625,8 +628,11 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
                 const int col = dvb + 16 * (w * NTW + j) + m16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * mt + 4 * g4 + i;
-                    p.state_out[((size_t)pr * D + row) * D + col] = S[mt][j][i];
+                    const size_t at = ((size_t)pr * D + 16 * mt + 4 * g4 + i) * D + col;
+                    if (p.state_bf16)
+                        reinterpret_cast<__bf16 *>(p.state_out)[at] = (__bf16)S[mt][j][i];
+                    else
+                        reinterpret_cast<float *>(p.state_out)[at] = S[mt][j][i];
                 }
             }
     }
@@ -665,6 +671,7 @@ hipError_t launch_prefill(const PrefillLaunch &L, hipStream_t s) {
     pp.w = a->conv_weight; pp.bias = a->conv_bias;
     pp.cs_in = a->conv_state_in;
     pp.state_in = a->state_in; pp.state_out = a->state_out;
+    pp.state_bf16 = (a->flags & KDA_F_STATE_BF16) ? 1 : 0;
     pp.o = a->o;
     pp.cu = a->cu_seqlens;
     pp.total = a->total_tokens;

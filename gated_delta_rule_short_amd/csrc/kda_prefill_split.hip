@@ -60,8 +60,9 @@ struct SplitParams {
     const void *q, *k, *v, *gate, *beta;
     const float *w, *bias;
     const void *cs_in;
-    const float *state_in;
-    float *state_out;
+    const void *state_in;   // fp32, or bf16 when state_bf16
+    void *state_out;
+    int state_bf16;
     void *o;
     const int32_t *cu;
     unsigned char *ws;
@@ -734,8 +735,14 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
         //   U = U0 - W S, S = diag(gam) S + Kd^T U
         // S[m] holds rows 16 m + 4 g4 + i of column col (accumulator layout).
         f32x4 S[8];
-        if (p.state_in) {
-            const float *sin = p.state_in + (size_t)pr * D * D + col;
+        if (p.state_in && p.state_bf16) {
+            const __bf16 *sin = reinterpret_cast<const __bf16 *>(p.state_in) + (size_t)pr * D * D + col;
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[m][i] = (float)sin[(16 * m + 4 * g4 + i) * D];
+        } else if (p.state_in) {
+            const float *sin = reinterpret_cast<const float *>(p.state_in) + (size_t)pr * D * D + col;
 #pragma unroll
             for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -834,8 +841,11 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
             for (int m = 0; m < 8; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * m + 4 * g4 + i;
-                    p.state_out[((size_t)pr * D + row) * D + col] = S[m][i];
+                    const size_t at = ((size_t)pr * D + 16 * m + 4 * g4 + i) * D + col;
+                    if (p.state_bf16)
+                        reinterpret_cast<__bf16 *>(p.state_out)[at] = (__bf16)S[m][i];
+                    else
+                        reinterpret_cast<float *>(p.state_out)[at] = S[m][i];
                 }
         }
         return;
@@ -910,6 +920,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
     sp.q = a->q; sp.k = a->k; sp.v = a->v; sp.gate = a->gate; sp.beta = a->beta;
     sp.w = a->conv_weight; sp.bias = a->conv_bias; sp.cs_in = a->conv_state_in;
     sp.state_in = a->state_in; sp.state_out = a->state_out; sp.o = a->o;
+    sp.state_bf16 = (a->flags & KDA_F_STATE_BF16) ? 1 : 0;
     sp.cu = a->cu_seqlens; sp.ws = static_cast<unsigned char *>(a->workspace);
     sp.total = a->total_tokens; sp.nslots = a->total_tokens / 16 + a->num_seqs;
     sp.num_seqs = a->num_seqs; sp.H = a->num_heads;

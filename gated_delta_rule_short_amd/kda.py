@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
-KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG = 1, 2, 4
+KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG, KDA_F_STATE_BF16 = 1, 2, 4, 8
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_short_conv",
@@ -69,7 +69,7 @@ class KdaDecodeCommitArgs(ctypes.Structure):
     _fields_ = [
         ("num_seqs", _c_i32), ("num_heads", _c_i32), ("head_dim_k", _c_i32),
         ("head_dim_v", _c_i32), ("num_tokens", _c_i32), ("dtype", ctypes.c_int),
-        ("accepted", _p), ("updates", _p), ("conv_state", _p), ("state", _p),
+        ("flags", _c_u32), ("accepted", _p), ("updates", _p), ("conv_state", _p), ("state", _p),
     ]
 
 
@@ -132,6 +132,15 @@ def _dtype_code(t):
     raise TypeError("unsupported dtype %s (bf16 or fp32)" % t.dtype)
 
 
+def _state_flag(state):
+    """KDA_F_STATE_BF16 for a bf16 state tensor, 0 for fp32 (decode entry points)."""
+    if state.dtype == torch.bfloat16:
+        return KDA_F_STATE_BF16
+    if state.dtype == torch.float32:
+        return 0
+    raise TypeError("state must be float32 or bfloat16, got %s" % state.dtype)
+
+
 def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -191,6 +200,9 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
                 chunk_size=0, flags=0, workspace=None, stream=None):
     """Chunked KDA prefill of packed sequences.
 
+    The state (state_in / state_out) is fp32, or bf16 storage when those tensors are
+    bf16 (state_out=True allocates the dtype of state_in, else fp32).
+
     q, k, gate: [T, H, 128]; v: [T, H, 128]; beta: [T, H] (bf16 or fp32, one dtype);
     conv_weight: [3*H*128, 4] fp32.  state_out / conv_state_out: a tensor, or True
     to allocate one.  workspace: a uint8 device tensor for the two-pass schedule
@@ -204,22 +216,30 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
     if o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
     if state_out is True:
-        state_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        sdt = state_in.dtype if state_in is not None else torch.float32
+        state_out = torch.empty((N, H, dk, dv), dtype=sdt, device=dev)
     if conv_state_out is True:
         conv_state_out = torch.empty((N, 3, 2 * H * dk + H * dv), dtype=q.dtype, device=dev)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (o, "o"),
                   (conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
         _need(t, nm, q.dtype, dev)
-    for t, nm in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"),
-                  (state_in, "state_in"), (state_out, "state_out")):
+    for t, nm in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias")):
         _need(t, nm, torch.float32, dev)
+    sflag = 0
+    for t, nm in ((state_in, "state_in"), (state_out, "state_out")):
+        _need(t, nm, None, dev)
+    if state_in is not None and state_out is not None and state_in.dtype != state_out.dtype:
+        raise TypeError("state_in and state_out must have one dtype")
+    for t in (state_in, state_out):
+        if t is not None:
+            sflag = _state_flag(t)
     _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     cuh = None
     if cu_seqlens_host is not None:
         cuh = cu_seqlens_host.to(torch.int32).contiguous().cpu()
     a = KdaPrefillArgs(
         num_seqs=N, num_heads=H, head_dim_k=dk, head_dim_v=dv, chunk_size=int(chunk_size),
-        total_tokens=T, dtype=_dtype_code(q), flags=int(flags), scale=float(scale),
+        total_tokens=T, dtype=_dtype_code(q), flags=int(flags) | sflag, scale=float(scale),
         gate_lower_bound=float(gate_lower_bound),
         q=_ptr(q), k=_ptr(k), v=_ptr(v), gate=_ptr(gate), beta=_ptr(beta),
         conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias),
@@ -250,7 +270,8 @@ def prefill_workspace_bytes(total_tokens, num_heads, num_seqs=1, dtype=torch.bfl
 def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias=None, o=None,
                scale=0.0, gate_lower_bound=-5.0, flags=0, stream=None):
     """One decode step: q, k, gate, v: [N, H, 128]; beta [N, H]; conv_state [N, 3, CC]
-    and state [N, H, 128, 128] fp32 are updated in place.  Returns o [N, H, 128]."""
+    and state [N, H, 128, 128] (fp32, or bf16 storage) are updated in place.
+    Returns o [N, H, 128]."""
     lib = load_library()
     dev = q.device
     N, H, dk = q.shape
@@ -260,11 +281,12 @@ def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (o, "o"),
                   (conv_state, "conv_state")):
         _need(t, nm, q.dtype, dev)
-    for t, nm in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"), (state, "state")):
+    for t, nm in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias")):
         _need(t, nm, torch.float32, dev)
+    _need(state, "state", None, dev)
     a = KdaDecodeArgs(
         num_seqs=N, num_heads=H, head_dim_k=dk, head_dim_v=dv, dtype=_dtype_code(q),
-        flags=int(flags), scale=float(scale), gate_lower_bound=float(gate_lower_bound),
+        flags=int(flags) | _state_flag(state), scale=float(scale), gate_lower_bound=float(gate_lower_bound),
         q=_ptr(q), k=_ptr(k), v=_ptr(v), gate=_ptr(gate), beta=_ptr(beta),
         conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias), conv_state=_ptr(conv_state),
         state=_ptr(state), o=_ptr(o))
@@ -291,9 +313,10 @@ def kda_decode_multi(q, k, v, gate, beta, conv_weight, conv_state, state, *, upd
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (o, "o"),
                   (conv_state, "conv_state")):
         _need(t, nm, q.dtype, dev)
-    for t, nm in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"), (state, "state"),
+    for t, nm in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"),
                   (updates, "updates"), (pending_updates, "pending_updates")):
         _need(t, nm, torch.float32, dev)
+    _need(state, "state", None, dev)
     _need(pending_accepted, "pending_accepted", torch.int32, dev)
     if updates.numel() != N * H * T * UPDATE_FLOATS:
         raise ValueError("updates must hold N*H*T*%d floats" % UPDATE_FLOATS)
@@ -306,7 +329,7 @@ def kda_decode_multi(q, k, v, gate, beta, conv_weight, conv_state, state, *, upd
             raise ValueError("pending_accepted must be an int32 tensor of N counts")
     a = KdaDecodeMultiArgs(
         num_seqs=N, num_heads=H, head_dim_k=dk, head_dim_v=dv, num_tokens=T,
-        dtype=_dtype_code(q), flags=int(flags), scale=float(scale),
+        dtype=_dtype_code(q), flags=int(flags) | _state_flag(state), scale=float(scale),
         gate_lower_bound=float(gate_lower_bound),
         q=_ptr(q), k=_ptr(k), v=_ptr(v), gate=_ptr(gate), beta=_ptr(beta),
         conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias), conv_state=_ptr(conv_state),
@@ -318,7 +341,7 @@ def kda_decode_multi(q, k, v, gate, beta, conv_weight, conv_state, state, *, upd
 
 
 def kda_decode_commit(updates, accepted, conv_state, state, *, stream=None):
-    """Advance state [N, H, 128, 128] fp32 and conv_state [N, 3, CC] in place over the
+    """Advance state [N, H, 128, 128] (fp32 or bf16) and conv_state [N, 3, CC] in place over the
     first accepted[n] tokens ([N] int32 on the device) recorded in updates
     ([N, H, T, 768] fp32, written by kda_decode_multi)."""
     lib = load_library()
@@ -328,12 +351,13 @@ def kda_decode_commit(updates, accepted, conv_state, state, *, stream=None):
     if updates.numel() != N * H * T * UPDATE_FLOATS:
         raise ValueError("updates must hold N*H*T*%d floats" % UPDATE_FLOATS)
     _need(updates, "updates", torch.float32, dev)
-    _need(state, "state", torch.float32, dev)
+    _need(state, "state", None, dev)
     _need(conv_state, "conv_state", None, dev)
     _need(accepted, "accepted", torch.int32, dev)
     if accepted.numel() != N:
         raise ValueError("accepted must hold N counts")
     a = KdaDecodeCommitArgs(num_seqs=N, num_heads=H, head_dim_k=dk, head_dim_v=dv,
-                            num_tokens=T, dtype=_dtype_code(conv_state), accepted=_ptr(accepted),
+                            num_tokens=T, dtype=_dtype_code(conv_state),
+                            flags=_state_flag(state), accepted=_ptr(accepted),
                             updates=_ptr(updates), conv_state=_ptr(conv_state), state=_ptr(state))
     _check(lib, lib.kda_decode_commit(ctypes.byref(a), _stream(stream, dev)))

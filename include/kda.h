@@ -68,9 +68,23 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 enum {
     KDA_F_SILU = 1u,          /* y <- y * sigmoid(y) after the conv (q, k and v) */
     KDA_F_NO_QK_L2NORM = 2u,  /* skip q/k L2 normalisation x / sqrt(|x|^2 + 1e-6) */
-    KDA_F_GATE_IS_LOG = 4u    /* gate holds the log-decay: g = max(gate, lb) */
+    KDA_F_GATE_IS_LOG = 4u,   /* gate holds the log-decay: g = max(gate, lb) */
+    KDA_F_STATE_BF16 = 8u     /* the recurrent state is stored as bf16 (see below) */
 };
-#define KDA_F_ALL (KDA_F_SILU | KDA_F_NO_QK_L2NORM | KDA_F_GATE_IS_LOG)
+#define KDA_F_ALL (KDA_F_SILU | KDA_F_NO_QK_L2NORM | KDA_F_GATE_IS_LOG | KDA_F_STATE_BF16)
+
+/* 16-bit state storage (KDA_F_STATE_BF16).  One page prints the 1M-context
+ * state as 0.07 GB, which is the 64x128x128 per layer and 34 layers at 2 bytes
+ * per value, while the state-size arithmetic of the same source stores FP32
+ * ("GLM-5.3-Flash im Detail", section "Sequenz-Mixing" and the KV-cache
+ * derivation).  With the flag, kda_prefill (state_in, state_out), kda_decode,
+ * kda_decode_multi and kda_decode_commit read and write the state as bf16
+ * [N][H][dk][dv]: each call widens it exactly to fp32, runs the same fp32
+ * arithmetic, and rounds the result to nearest even once when it stores it.
+ * It halves the state traffic, the whole cost of a decode step.  Rounding once
+ * per call adds error that levels off rather than growing with the number of
+ * steps, at a size set by how slowly the state decays; fp32 stays the
+ * default. */
 
 /* Version of this ABI (KDA_ABI_VERSION). */
 int kda_abi_version(void);
@@ -133,8 +147,8 @@ typedef struct {
     const float *conv_bias;  /* [CC] or NULL */
     const void *conv_state_in; /* [N][3][CC] or NULL (zeros) */
     void *conv_state_out;      /* [N][3][CC] or NULL; may alias conv_state_in */
-    const float *state_in;     /* [N][H][dk][dv] fp32 or NULL (zeros) */
-    float *state_out;          /* [N][H][dk][dv] fp32 or NULL; may alias state_in */
+    const void *state_in;      /* [N][H][dk][dv] fp32 (bf16 with KDA_F_STATE_BF16) or NULL */
+    void *state_out;           /* [N][H][dk][dv], same type, or NULL; may alias state_in */
     void *o;                   /* [T][H][dv] output; must not overlap the inputs */
     const int32_t *cu_seqlens; /* [N+1] device, or NULL for N equal sequences */
     const int32_t *cu_seqlens_host; /* optional host copy, validated when given */
@@ -173,7 +187,7 @@ typedef struct {
     int32_t head_dim_k;      /* must be 128 */
     int32_t head_dim_v;      /* must be 128 */
     kda_dtype dtype;
-    uint32_t flags;          /* KDA_F_* */
+    uint32_t flags;          /* KDA_F_* (KDA_F_STATE_BF16 allowed) */
     float scale;             /* 0 = 1/sqrt(dk) */
     float gate_lower_bound;  /* < 0 */
     const void *q, *k;       /* [N][H][dk] raw */
@@ -183,7 +197,7 @@ typedef struct {
     const float *conv_weight;/* [CC][4] */
     const float *conv_bias;  /* [CC] or NULL */
     void *conv_state;        /* [N][3][CC] in/out (shifted by one token) */
-    float *state;            /* [N][H][dk][dv] fp32 in/out */
+    void *state;             /* [N][H][dk][dv] in/out: fp32, or bf16 with KDA_F_STATE_BF16 */
     void *o;                 /* [N][H][dv] */
 } kda_decode_args;
 
@@ -229,7 +243,7 @@ typedef struct {
     int32_t head_dim_v;      /* must be 128 */
     int32_t num_tokens;      /* T, 1..KDA_MAX_SPEC_TOKENS tokens per sequence */
     kda_dtype dtype;
-    uint32_t flags;          /* KDA_F_* */
+    uint32_t flags;          /* KDA_F_* (KDA_F_STATE_BF16 allowed) */
     float scale;             /* 0 = 1/sqrt(dk) */
     float gate_lower_bound;  /* < 0 */
     const void *q, *k;       /* [N][T][H][dk] raw */
@@ -239,7 +253,8 @@ typedef struct {
     const float *conv_weight;/* [CC][4] */
     const float *conv_bias;  /* [CC] or NULL */
     void *conv_state;        /* [N][3][CC]; written only by a pending commit */
-    float *state;            /* [N][H][dk][dv] fp32; written only by a pending commit */
+    void *state;             /* [N][H][dk][dv] fp32 (bf16 with KDA_F_STATE_BF16);
+                                written only by a pending commit */
     void *o;                 /* [N][T][H][dv] */
     float *updates;          /* [N][H][T][KDA_UPDATE_FLOATS] fp32 records (written) */
     /* Optional fused commit of the previous call, applied to state and conv_state
@@ -265,10 +280,11 @@ typedef struct {
     int32_t head_dim_v;      /* must be 128 */
     int32_t num_tokens;      /* T of the kda_decode_multi call */
     kda_dtype dtype;         /* dtype of conv_state */
+    uint32_t flags;          /* 0 or KDA_F_STATE_BF16 */
     const int32_t *accepted; /* [N] device */
     const float *updates;    /* [N][H][T][KDA_UPDATE_FLOATS] records */
     void *conv_state;        /* [N][3][CC] in/out */
-    float *state;            /* [N][H][dk][dv] fp32 in/out */
+    void *state;             /* [N][H][dk][dv] in/out, fp32 or bf16 */
 } kda_decode_commit_args;
 
 kda_status kda_decode_commit(const kda_decode_commit_args *args, hipStream_t stream);

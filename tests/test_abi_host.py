@@ -55,8 +55,8 @@ def test_struct_layouts_match_header():
     assert K.KdaDecodeMultiArgs.q.offset == 40
     assert K.KdaDecodeMultiArgs.pending_tokens.offset == 40 + 13 * 8
     assert ctypes.sizeof(K.KdaDecodeMultiArgs) == 40 + 14 * 8
-    assert K.KdaDecodeCommitArgs.accepted.offset == 24
-    assert ctypes.sizeof(K.KdaDecodeCommitArgs) == 24 + 4 * 8
+    assert K.KdaDecodeCommitArgs.accepted.offset == 32
+    assert ctypes.sizeof(K.KdaDecodeCommitArgs) == 32 + 4 * 8
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
@@ -82,7 +82,7 @@ def _prefill_args(**kw):
     ("head_dim_k", 64, K.KDA_ERR_UNSUPPORTED),
     ("head_dim_v", 256, K.KDA_ERR_UNSUPPORTED),
     ("chunk_size", 48, K.KDA_ERR_UNSUPPORTED),
-    ("flags", 8, K.KDA_ERR_UNSUPPORTED),
+    ("flags", 16, K.KDA_ERR_UNSUPPORTED),
     ("dtype", 7, K.KDA_ERR_INVALID_ARG),
     ("gate_lower_bound", 0.0, K.KDA_ERR_INVALID_ARG),
     ("gate_lower_bound", float("nan"), K.KDA_ERR_INVALID_ARG),
@@ -152,6 +152,17 @@ def test_decode_rejects_bad_arguments(lib, field, value, status):
     assert lib.kda_decode(ctypes.byref(a), None) == status
 
 
+def test_decode_state_overlap_size_follows_storage(lib):
+    # every case here is rejected before a launch (the pointers are fake)
+    bf16_bytes = 2 * 2 * 128 * 128 * 2
+    a = _decode_args(flags=K.KDA_F_STATE_BF16)
+    a.o = ctypes.c_void_p(a.state + bf16_bytes - 2)  # last element of a bf16 state
+    assert lib.kda_decode(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    a = _decode_args()
+    a.o = ctypes.c_void_p(a.state + bf16_bytes)  # inside an fp32 state of the same shape
+    assert lib.kda_decode(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
 def test_decode_rejects_state_overlapping_output(lib):
     a = _decode_args()
     a.state = a.o
@@ -215,6 +226,7 @@ def _commit_args(**kw):
     ("accepted", None, K.KDA_ERR_INVALID_ARG),
     ("updates", None, K.KDA_ERR_INVALID_ARG),
     ("dtype", 5, K.KDA_ERR_INVALID_ARG),
+    ("flags", K.KDA_F_SILU, K.KDA_ERR_UNSUPPORTED),
 ])
 def test_decode_commit_rejects_bad_arguments(lib, field, value, status):
     a = _commit_args(**{field: value})
