@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_conv.hip", "kda_decode.hip", "kda_prefill.hip",
+SOURCES = ["kda_api.hip", "kda_conv.hip", "kda_decode.hip", "kda_pool.hip", "kda_prefill.hip",
            "kda_prefill_split.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 

@@ -68,6 +68,18 @@ kda_status check_common(int32_t num_seqs, int32_t H, int32_t dk, int32_t dv, kda
     return KDA_OK;
 }
 
+// Rows of the state and conv-state arrays: the pool size with a slot map, else
+// one per sequence.
+kda_status pool_rows(const int32_t *slots, int32_t num_slots, int32_t num_seqs, size_t &rows) {
+    if (!slots) {
+        rows = (size_t)num_seqs;
+        return KDA_OK;
+    }
+    if (num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "state_slots needs num_slots >= 1");
+    rows = (size_t)num_slots;
+    return KDA_OK;
+}
+
 int env_int(const char *name, int dflt) {
     const char *v = std::getenv(name);
     return v && *v ? std::atoi(v) : dflt;
@@ -128,7 +140,8 @@ kda_status kda_short_conv(const void *x, void *y, int64_t total_tokens, int32_t 
         const void *src[3] = {x, x, x};
         const int ch[3] = {channels, 0, 0};
         hipError_t e = kda::launch_conv_tail(dtype, src, ch, total_tokens, conv_state_in,
-                                             conv_state_out, cu_seqlens, num_seqs, stream);
+                                             conv_state_out, cu_seqlens, num_seqs, nullptr, 0,
+                                             stream);
         if (e != hipSuccess) return hip_fail(e, "conv tail launch");
     }
     return KDA_OK;
@@ -169,12 +182,15 @@ kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
         if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
     if (overlap(a->o, tok, a->beta, (size_t)T * H * es))
         return fail(KDA_ERR_INVALID_ARG, "o overlaps beta");
-    const size_t sb = (size_t)a->num_seqs * H * 128 * 128 * state_esize(a->flags);
+    size_t rows = 0;
+    st = pool_rows(a->state_slots, a->num_slots, a->num_seqs, rows);
+    if (st != KDA_OK) return st;
+    const size_t sb = rows * H * 128 * 128 * state_esize(a->flags);
     if (a->state_out && (const void *)a->state_out != (const void *)a->state_in &&
         overlap(a->state_out, sb, a->state_in, sb))
         return fail(KDA_ERR_INVALID_ARG, "state_out partially overlaps state_in");
     if (overlap(a->state_out, sb, a->o, tok)) return fail(KDA_ERR_INVALID_ARG, "state_out overlaps o");
-    const size_t csb = (size_t)a->num_seqs * 3 * 3 * H * 128 * es;
+    const size_t csb = rows * 3 * 3 * H * 128 * es;
     if (a->conv_state_out && a->conv_state_out != a->conv_state_in &&
         overlap(a->conv_state_out, csb, a->conv_state_in, csb))
         return fail(KDA_ERR_INVALID_ARG, "conv_state_out partially overlaps conv_state_in");
@@ -210,7 +226,8 @@ kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
         const int c = (int)(H * 128);
         const int ch[3] = {c, c, c};
         e = kda::launch_conv_tail(a->dtype, src, ch, T, a->conv_state_in, a->conv_state_out,
-                                  a->cu_seqlens, a->num_seqs, stream);
+                                  a->cu_seqlens, a->num_seqs, a->state_slots, a->num_slots,
+                                  stream);
         if (e != hipSuccess) return hip_fail(e, "conv tail launch");
     }
     return KDA_OK;
@@ -228,13 +245,19 @@ kda_status kda_decode(const kda_decode_args *a, hipStream_t stream) {
                                          "state must be non-NULL");
     const size_t es = esize(a->dtype);
     const size_t tok = (size_t)a->num_seqs * a->num_heads * 128 * es;
-    const size_t sb = (size_t)a->num_seqs * a->num_heads * 128 * 128 * state_esize(a->flags);
+    size_t rows = 0;
+    st = pool_rows(a->state_slots, a->num_slots, a->num_seqs, rows);
+    if (st != KDA_OK) return st;
+    const size_t sb = rows * a->num_heads * 128 * 128 * state_esize(a->flags);
+    const size_t cb = rows * 3 * 3 * a->num_heads * 128 * es;
     const void *ins[4] = {a->q, a->k, a->v, a->gate};
     for (const void *in : ins) {
         if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
         if (overlap(a->state, sb, in, tok)) return fail(KDA_ERR_INVALID_ARG, "state overlaps an input");
     }
     if (overlap(a->state, sb, a->o, tok)) return fail(KDA_ERR_INVALID_ARG, "state overlaps o");
+    if (overlap(a->state, sb, a->conv_state, cb) || overlap(a->conv_state, cb, a->o, tok))
+        return fail(KDA_ERR_INVALID_ARG, "conv_state overlaps state or o");
     kda_decode_args args = *a;
     if (args.scale == 0.f) args.scale = 1.0f / std::sqrt(128.0f);
     hipError_t e = kda::launch_decode(&args, stream);
@@ -265,8 +288,11 @@ kda_status kda_decode_multi(const kda_decode_multi_args *a, hipStream_t stream) 
     const size_t es = esize(a->dtype);
     const size_t NH = (size_t)a->num_seqs * a->num_heads;
     const size_t tok = NH * a->num_tokens * 128 * es;
-    const size_t sb = NH * 128 * 128 * state_esize(a->flags);
-    const size_t cb = (size_t)a->num_seqs * 3 * 3 * a->num_heads * 128 * es;
+    size_t rows = 0;
+    st = pool_rows(a->state_slots, a->num_slots, a->num_seqs, rows);
+    if (st != KDA_OK) return st;
+    const size_t sb = rows * a->num_heads * 128 * 128 * state_esize(a->flags);
+    const size_t cb = rows * 3 * 3 * a->num_heads * 128 * es;
     const size_t rb = NH * a->num_tokens * KDA_UPDATE_FLOATS * 4;
     const size_t pb = a->pending_updates ? NH * a->pending_tokens * KDA_UPDATE_FLOATS * 4 : 0;
     const void *ins[4] = {a->q, a->k, a->v, a->gate};
@@ -306,14 +332,48 @@ kda_status kda_decode_commit(const kda_decode_commit_args *a, hipStream_t stream
     if (!a->accepted || !a->updates || !a->conv_state || !a->state)
         return fail(KDA_ERR_INVALID_ARG, "accepted, updates, conv_state and state must be non-NULL");
     const size_t NH = (size_t)a->num_seqs * a->num_heads;
-    const size_t sb = NH * 128 * 128 * state_esize(a->flags);
-    const size_t cb = (size_t)a->num_seqs * 3 * 3 * a->num_heads * 128 * esize(a->dtype);
+    size_t rows = 0;
+    st = pool_rows(a->state_slots, a->num_slots, a->num_seqs, rows);
+    if (st != KDA_OK) return st;
+    const size_t sb = rows * a->num_heads * 128 * 128 * state_esize(a->flags);
+    const size_t cb = rows * 3 * 3 * a->num_heads * 128 * esize(a->dtype);
     const size_t rb = NH * a->num_tokens * KDA_UPDATE_FLOATS * 4;
     if (overlap(a->updates, rb, a->state, sb) || overlap(a->updates, rb, a->conv_state, cb) ||
         overlap(a->state, sb, a->conv_state, cb))
         return fail(KDA_ERR_INVALID_ARG, "updates, state and conv_state must not overlap");
     hipError_t e = kda::launch_decode_commit(a, stream);
     if (e != hipSuccess) return hip_fail(e, "decode_commit launch");
+    return KDA_OK;
+}
+
+kda_status kda_state_copy(const kda_state_copy_args *a, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
+    if (a->count < 0) return fail(KDA_ERR_INVALID_ARG, "count = %d, must be >= 0", a->count);
+    kda_status st = check_common(1, a->num_heads, a->head_dim_k, a->head_dim_v, a->dtype, a->flags,
+                                 0.f, -1.f, KDA_F_STATE_BF16);
+    if (st != KDA_OK) return st;
+    if (a->num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "num_slots must be >= 1");
+    if ((int64_t)a->num_slots * a->num_heads > (int64_t)1 << 26 ||
+        (int64_t)a->count * a->num_heads > (int64_t)1 << 26)
+        return fail(KDA_ERR_INVALID_ARG, "num_slots * num_heads or count * num_heads too large");
+    if (!a->src_slots || !a->dst_slots || !a->state_src || !a->state_dst)
+        return fail(KDA_ERR_INVALID_ARG, "src_slots, dst_slots, state_src and state_dst must be "
+                                         "non-NULL");
+    if (!a->conv_src != !a->conv_dst)
+        return fail(KDA_ERR_INVALID_ARG, "conv_src and conv_dst must both be given or both NULL");
+    const size_t sb = (size_t)a->num_slots * a->num_heads * 128 * 128 * state_esize(a->flags);
+    const size_t cb = (size_t)a->num_slots * 3 * 3 * a->num_heads * 128 * esize(a->dtype);
+    if (a->state_src != a->state_dst && overlap(a->state_src, sb, a->state_dst, sb))
+        return fail(KDA_ERR_INVALID_ARG, "state_dst partially overlaps state_src");
+    if (a->conv_src != a->conv_dst && overlap(a->conv_src, cb, a->conv_dst, cb))
+        return fail(KDA_ERR_INVALID_ARG, "conv_dst partially overlaps conv_src");
+    if (overlap(a->state_dst, sb, a->conv_src, cb) || overlap(a->state_dst, sb, a->conv_dst, cb) ||
+        overlap(a->conv_dst, cb, a->state_src, sb))
+        return fail(KDA_ERR_INVALID_ARG, "state and conv-state pools overlap");
+    if (a->count == 0) return KDA_OK;
+    hipError_t e = kda::launch_state_copy(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "state_copy launch");
     return KDA_OK;
 }
 

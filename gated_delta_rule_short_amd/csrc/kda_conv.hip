@@ -227,11 +227,13 @@ template <typename T>
 __global__ void __launch_bounds__(kConvThreads)
 conv_tail_kernel(const T *__restrict__ s0p, const T *__restrict__ s1p, const T *__restrict__ s2p,
                  int c0, int c1, int c2, int64_t total, const T *cs_in, T *cs_out,
-                 const int32_t *__restrict__ cu, int num_seqs) {
+                 const int32_t *__restrict__ cu, int num_seqs, const int32_t *slots,
+                 int num_slots) {
     const int CC = c0 + c1 + c2;
     const int c = blockIdx.y * kConvThreads + threadIdx.x;
     const int n = blockIdx.x;
-    if (c >= CC) return;
+    const int slot = pool_slot(slots, num_slots, n);  // conv-state row of sequence n
+    if (c >= CC || slot < 0) return;
     int64_t st, len;
     seq_bounds(cu, total, num_seqs, n, st, len);
     const T *src;
@@ -244,12 +246,12 @@ conv_tail_kernel(const T *__restrict__ s0p, const T *__restrict__ s1p, const T *
     for (int s = 0; s < 3; ++s) {
         const int64_t p = len - 3 + s;
         if (p >= 0) vals[s] = src[(st + p) * ch + cc];
-        else if (cs_in) vals[s] = cs_in[((int64_t)n * 3 + (3 + p)) * CC + c];
+        else if (cs_in) vals[s] = cs_in[((int64_t)slot * 3 + (3 + p)) * CC + c];
         else vals[s] = from_f32<T>(0.f);
     }
-    // every thread reads its own (n, c) slots before writing them: in place is safe
+    // every thread reads its own (slot, c) entries before writing them: in place is safe
 #pragma unroll
-    for (int s = 0; s < 3; ++s) cs_out[((int64_t)n * 3 + s) * CC + c] = vals[s];
+    for (int s = 0; s < 3; ++s) cs_out[((int64_t)slot * 3 + s) * CC + c] = vals[s];
 }
 
 template <typename T>
@@ -300,17 +302,19 @@ hipError_t launch_short_conv(kda_dtype dt, const void *x, void *y, int64_t T_, i
 
 hipError_t launch_conv_tail(kda_dtype dt, const void *const src[3], const int ch[3], int64_t T_,
                             const void *cs_in, void *cs_out, const int32_t *cu, int N,
-                            hipStream_t s) {
+                            const int32_t *slots, int num_slots, hipStream_t s) {
     const int CC = ch[0] + ch[1] + ch[2];
     dim3 grid((unsigned)N, (unsigned)((CC + kConvThreads - 1) / kConvThreads));
     if (dt == KDA_BF16)
         hipLaunchKernelGGL((conv_tail_kernel<__bf16>), grid, dim3(kConvThreads), 0, s,
                            (const __bf16 *)src[0], (const __bf16 *)src[1], (const __bf16 *)src[2],
-                           ch[0], ch[1], ch[2], T_, (const __bf16 *)cs_in, (__bf16 *)cs_out, cu, N);
+                           ch[0], ch[1], ch[2], T_, (const __bf16 *)cs_in, (__bf16 *)cs_out, cu, N,
+                           slots, num_slots);
     else
         hipLaunchKernelGGL((conv_tail_kernel<float>), grid, dim3(kConvThreads), 0, s,
                            (const float *)src[0], (const float *)src[1], (const float *)src[2],
-                           ch[0], ch[1], ch[2], T_, (const float *)cs_in, (float *)cs_out, cu, N);
+                           ch[0], ch[1], ch[2], T_, (const float *)cs_in, (float *)cs_out, cu, N,
+                           slots, num_slots);
     return hipGetLastError();
 }
 

@@ -202,6 +202,8 @@ struct DecodeParams {
     void *cs;
     void *state;  // fp32 or bf16 (SB)
     void *o;
+    const int32_t *slots;  // pool row of each sequence (state, conv cache), or null
+    int num_slots;
     int H;
     float scale, lb;
     uint32_t flags;
@@ -213,6 +215,8 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
     const int pr = blockIdx.x;
     const int H = p.H;
     const int n = pr / H, h = pr - n * H;
+    const int slot = pool_slot(p.slots, p.num_slots, n);
+    if (slot < 0) return;  // whole workgroup, before any barrier
     const int tid = threadIdx.x;
     const int cg = tid & 31, rg = tid >> 5, wave = tid >> 6;
 
@@ -223,13 +227,13 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
     // 1. issue the state loads (independent of the prologue).  The state is
     // streamed exactly once each way: non-temporal loads and stores keep it from
     // displacing the small, reused operands in L2.
-    SB *S = reinterpret_cast<SB *>(p.state) + (size_t)pr * D * D;
+    SB *S = reinterpret_cast<SB *>(p.state) + ((size_t)slot * H + h) * D * D;
     f32x4 st[16];
     load_state(st, S, tid);
 
     // 2. prologue: conv (and cache shift), L2 of q and k, gate
     const int CC = 3 * H * D;
-    T *cs = reinterpret_cast<T *>(p.cs) + (size_t)n * 3 * CC;
+    T *cs = reinterpret_cast<T *>(p.cs) + (size_t)slot * 3 * CC;
     const bool silu = p.flags & KDA_F_SILU;
     const bool l2 = !(p.flags & KDA_F_NO_QK_L2NORM);
     const bool glog = p.flags & KDA_F_GATE_IS_LOG;
@@ -295,6 +299,8 @@ struct MultiParams {
     float *rec;           // [N][H][T][kRec] written
     const float *prec;    // pending records [N][H][pT][kRec] or null
     const int32_t *pacc;  // [N] pending accepted counts
+    const int32_t *slots;  // pool row of each sequence (state, conv cache), or null
+    int num_slots;
     int H, T, pT;
     float scale, lb;
     uint32_t flags;
@@ -306,6 +312,8 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
     const int pr = blockIdx.x;
     const int H = p.H, NT = p.T;
     const int n = pr / H, h = pr - n * H;
+    const int slot = pool_slot(p.slots, p.num_slots, n);
+    if (slot < 0) return;  // whole workgroup, before any barrier
     const int tid = threadIdx.x;
     const int cg = tid & 31, rg = tid >> 5, wave = tid >> 6;
 
@@ -336,7 +344,7 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
             x1[t] = src1[base + t * tstride + c];
         }
     }
-    T *cs = reinterpret_cast<T *>(p.cs) + (size_t)n * 3 * CC;
+    T *cs = reinterpret_cast<T *>(p.cs) + (size_t)slot * 3 * CC;
     const T cr0[3] = {cs[ch0], cs[CC + ch0], cs[2 * CC + ch0]};
     T cr1[3] = {};
     if (qk) {
@@ -349,7 +357,7 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
     const float b0 = p.bias ? p.bias[ch0] : 0.f, b1 = p.bias ? p.bias[ch1] : 0.f;
     if (!qk && c < NT) s_beta[c] = to_f32(reinterpret_cast<const T *>(p.beta)[((size_t)n * NT + c) * H + h]);
 
-    SB *S = reinterpret_cast<SB *>(p.state) + (size_t)pr * D * D;
+    SB *S = reinterpret_cast<SB *>(p.state) + ((size_t)slot * H + h) * D * D;
     f32x4 st[16];
     load_state(st, S, tid);
 
@@ -476,6 +484,8 @@ struct CommitParams {
     const float *rec;
     void *cs;
     void *state;  // fp32 or bf16 (SB)
+    const int32_t *slots;  // pool row of each sequence (state, conv cache), or null
+    int num_slots;
     int H, T;
 };
 
@@ -486,18 +496,19 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
     const int H = p.H;
     const int n = pr / H, h = pr - n * H;
     const int tid = threadIdx.x, cg = tid & 31;
+    const int slot = pool_slot(p.slots, p.num_slots, n);
     const int na = clamp_count(p.acc[n], p.T);
-    if (na == 0) return;  // uniform over the workgroup
+    if (na == 0 || slot < 0) return;  // uniform over the workgroup
 
     __shared__ __attribute__((aligned(16))) float s_pend[kMaxSpec][3][D];
-    SB *S = reinterpret_cast<SB *>(p.state) + (size_t)pr * D * D;
+    SB *S = reinterpret_cast<SB *>(p.state) + ((size_t)slot * H + h) * D * D;
     f32x4 st[16];
     load_state(st, S, tid);
     const float *rec = p.rec + (size_t)pr * p.T * kRec;
     stage_records(s_pend, rec, na, tid);
 
     const int CC = 3 * H * D;
-    T *cs = reinterpret_cast<T *>(p.cs) + (size_t)n * 3 * CC;
+    T *cs = reinterpret_cast<T *>(p.cs) + (size_t)slot * 3 * CC;
     for (int i = tid; i < 3 * D; i += 256) {
         const int part = i / D, c = i - part * D;  // 0 q, 1 k, 2 v
         const int ch = part * H * D + h * D + c;
@@ -530,6 +541,7 @@ hipError_t launch_decode(const kda_decode_args *a, hipStream_t s) {
     p.q = a->q; p.k = a->k; p.v = a->v; p.gate = a->gate; p.beta = a->beta;
     p.w = a->conv_weight; p.bias = a->conv_bias;
     p.cs = a->conv_state; p.state = a->state; p.o = a->o;
+    p.slots = a->state_slots; p.num_slots = a->num_slots;
     p.H = a->num_heads;
     p.scale = a->scale; p.lb = a->gate_lower_bound; p.flags = a->flags;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
@@ -544,6 +556,7 @@ hipError_t launch_decode_multi(const kda_decode_multi_args *a, hipStream_t s) {
     p.w = a->conv_weight; p.bias = a->conv_bias;
     p.cs = a->conv_state; p.state = a->state; p.o = a->o; p.rec = a->updates;
     p.prec = a->pending_updates; p.pacc = a->pending_accepted;
+    p.slots = a->state_slots; p.num_slots = a->num_slots;
     p.H = a->num_heads; p.T = a->num_tokens; p.pT = a->pending_updates ? a->pending_tokens : 0;
     p.scale = a->scale; p.lb = a->gate_lower_bound; p.flags = a->flags;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
@@ -555,6 +568,7 @@ hipError_t launch_decode_multi(const kda_decode_multi_args *a, hipStream_t s) {
 hipError_t launch_decode_commit(const kda_decode_commit_args *a, hipStream_t s) {
     CommitParams p;
     p.acc = a->accepted; p.rec = a->updates; p.cs = a->conv_state; p.state = a->state;
+    p.slots = a->state_slots; p.num_slots = a->num_slots;
     p.H = a->num_heads; p.T = a->num_tokens;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
     launch_typed<CommitParams>(a->dtype, a->flags, blocks, p, s,

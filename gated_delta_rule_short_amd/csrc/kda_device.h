@@ -203,6 +203,14 @@ __device__ __forceinline__ f32x4 mma_k16w(bf16x4 a, bf16x4 b, f32x4 c) {
     return mma_k32(join8(a, z), join8(b, z), c);
 }
 
+// Pool row of sequence n: slots[n] when a slot map is given, else n.  A slot
+// outside [0, num_slots) gives -1, and the caller then skips the sequence.
+__device__ __forceinline__ int pool_slot(const int32_t *slots, int num_slots, int n) {
+    if (!slots) return n;
+    const int s = slots[n];
+    return (s >= 0 && s < num_slots) ? s : -1;
+}
+
 // Index of the sequence holding token t: the largest n with cu[n] <= t.
 __device__ __forceinline__ int find_seq(const int32_t *cu, int num_seqs, int64_t t) {
     int lo = 0, hi = num_seqs;

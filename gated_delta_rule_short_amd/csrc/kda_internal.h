@@ -16,10 +16,15 @@ hipError_t launch_short_conv(kda_dtype dt, const void *x, void *y, int64_t T, in
 
 // Last three raw tokens of (conv_state_in ++ sequence) for up to three sources that
 // together form the conv channels: source i has `ch[i]` channels and rows of `ch[i]`
-// elements ([T][ch[i]]).  Writes cs_out [N][3][sum ch]; cs_out may alias cs_in.
+// elements ([T][ch[i]]).  Writes cs_out [rows][3][sum ch]; cs_out may alias cs_in.
+// Sequence n uses row slots[n] (skipped when outside [0, num_slots)), or row n
+// when slots is null.
 hipError_t launch_conv_tail(kda_dtype dt, const void *const src[3], const int ch[3],
                             int64_t T, const void *cs_in, void *cs_out, const int32_t *cu,
-                            int num_seqs, hipStream_t s);
+                            int num_seqs, const int32_t *slots, int num_slots, hipStream_t s);
+
+// Pool rows: state (and conv state when given) of slot src[i] -> slot dst[i].
+hipError_t launch_state_copy(const kda_state_copy_args *a, hipStream_t s);
 
 struct PrefillLaunch {
     const kda_prefill_args *a;

@@ -62,6 +62,8 @@ struct PrefillParams {
     const void *state_in;   // fp32, or bf16 when state_bf16
     void *state_out;
     int state_bf16;
+    const int32_t *slots;   // pool row of each sequence (state, conv state), or null
+    int num_slots;
     void *o;
     const int32_t *cu;
     int64_t total;
@@ -176,6 +178,9 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
     if (pr >= p.pairs) return;
     const int H = p.H;
     const int n = pr / H, h = pr - n * H;
+    const int slot = pool_slot(p.slots, p.num_slots, n);
+    if (slot < 0) return;  // whole workgroup, before any barrier
+    const size_t spr = (size_t)slot * H + h;  // pool row of this (sequence, head)
     int64_t s0, L;
     seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
     const int dvb = tile * DVW;
@@ -220,7 +225,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * mt + 4 * g4 + i;
-                const size_t at = ((size_t)pr * D + row) * D + col;
+                const size_t at = (spr * D + row) * D + col;
                 S[mt][j][i] = !(st_wave && p.state_in) ? 0.f
                               : p.state_bf16 ? (float)reinterpret_cast<const __bf16 *>(p.state_in)[at]
                                              : reinterpret_cast<const float *>(p.state_in)[at];
@@ -237,7 +242,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
     for (int idx = tid; idx < C * SCC; idx += 256) sPM[idx] = from_f32<E>(0.f);
     // halo of the first chunk: the three raw rows before the sequence (conv state or zeros)
     {
-        const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)n * 3 * CCH : nullptr;
+        const T *csn = p.cs_in ? reinterpret_cast<const T *>(p.cs_in) + (size_t)slot * 3 * CCH : nullptr;
         E *hslot = sHALO + 1 * 3 * HS;  // read as the "previous" slot by chunk 0
         for (int idx = tid; idx < 3 * HS; idx += 256) {
             const int r = idx / HS, c = idx - r * HS;
@@ -628,7 +633,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillParams p) {
                 const int col = dvb + 16 * (w * NTW + j) + m16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const size_t at = ((size_t)pr * D + 16 * mt + 4 * g4 + i) * D + col;
+                    const size_t at = (spr * D + 16 * mt + 4 * g4 + i) * D + col;
                     if (p.state_bf16)
                         reinterpret_cast<__bf16 *>(p.state_out)[at] = (__bf16)S[mt][j][i];
                     else
@@ -672,6 +677,7 @@ hipError_t launch_prefill(const PrefillLaunch &L, hipStream_t s) {
     pp.cs_in = a->conv_state_in;
     pp.state_in = a->state_in; pp.state_out = a->state_out;
     pp.state_bf16 = (a->flags & KDA_F_STATE_BF16) ? 1 : 0;
+    pp.slots = a->state_slots; pp.num_slots = a->num_slots;
     pp.o = a->o;
     pp.cu = a->cu_seqlens;
     pp.total = a->total_tokens;

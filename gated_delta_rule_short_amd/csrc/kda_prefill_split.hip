@@ -63,6 +63,8 @@ struct SplitParams {
     const void *state_in;   // fp32, or bf16 when state_bf16
     void *state_out;
     int state_bf16;
+    const int32_t *slots;   // pool row of each sequence (state, conv state), or null
+    int num_slots;
     void *o;
     const int32_t *cu;
     unsigned char *ws;
@@ -216,7 +218,9 @@ __device__ __forceinline__ void load_history(const SplitParams &p, const SubTask
     constexpr int D = kHeadDim;
     const int CCH = 3 * p.H * D;
     const int ch = t * p.H * D + h * D + 2 * lane;
-    const __bf16 *csn = p.cs_in ? reinterpret_cast<const __bf16 *>(p.cs_in) + (size_t)tk.n * 3 * CCH : nullptr;
+    const int slot = pool_slot(p.slots, p.num_slots, tk.n);
+    const __bf16 *csn =
+        p.cs_in && slot >= 0 ? reinterpret_cast<const __bf16 *>(p.cs_in) + (size_t)slot * 3 * CCH : nullptr;
 #pragma unroll
     for (int i = 0; i < 3; ++i)
         x[i] = csn ? *reinterpret_cast<const uint32_t *>(csn + (size_t)i * CCH + ch) : 0u;
@@ -708,6 +712,9 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
     if (pr >= p.pairs) return;  // whole workgroup: no barrier is left waiting
     const int H = p.H;
     const int n = pr / H, h = pr - n * H;
+    const int slot = pool_slot(p.slots, p.num_slots, n);
+    if (slot < 0) return;  // whole workgroup: no barrier is left waiting
+    const size_t spr = (size_t)slot * H + h;  // pool row of this (sequence, head)
     int64_t s0, L;
     seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
     const int64_t J = (L + 15) / 16;
@@ -736,13 +743,13 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
         // S[m] holds rows 16 m + 4 g4 + i of column col (accumulator layout).
         f32x4 S[8];
         if (p.state_in && p.state_bf16) {
-            const __bf16 *sin = reinterpret_cast<const __bf16 *>(p.state_in) + (size_t)pr * D * D + col;
+            const __bf16 *sin = reinterpret_cast<const __bf16 *>(p.state_in) + spr * D * D + col;
 #pragma unroll
             for (int m = 0; m < 8; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[m][i] = (float)sin[(16 * m + 4 * g4 + i) * D];
         } else if (p.state_in) {
-            const float *sin = reinterpret_cast<const float *>(p.state_in) + (size_t)pr * D * D + col;
+            const float *sin = reinterpret_cast<const float *>(p.state_in) + spr * D * D + col;
 #pragma unroll
             for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -841,7 +848,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
             for (int m = 0; m < 8; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const size_t at = ((size_t)pr * D + 16 * m + 4 * g4 + i) * D + col;
+                    const size_t at = (spr * D + 16 * m + 4 * g4 + i) * D + col;
                     if (p.state_bf16)
                         reinterpret_cast<__bf16 *>(p.state_out)[at] = (__bf16)S[m][i];
                     else
@@ -921,6 +928,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
     sp.w = a->conv_weight; sp.bias = a->conv_bias; sp.cs_in = a->conv_state_in;
     sp.state_in = a->state_in; sp.state_out = a->state_out; sp.o = a->o;
     sp.state_bf16 = (a->flags & KDA_F_STATE_BF16) ? 1 : 0;
+    sp.slots = a->state_slots; sp.num_slots = a->num_slots;
     sp.cu = a->cu_seqlens; sp.ws = static_cast<unsigned char *>(a->workspace);
     sp.total = a->total_tokens; sp.nslots = a->total_tokens / 16 + a->num_seqs;
     sp.num_seqs = a->num_seqs; sp.H = a->num_heads;

@@ -22,7 +22,7 @@ KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG, KDA_F_STATE_BF16 = 1, 2, 4, 8
 # every symbol include/kda.h declares
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_short_conv",
            "kda_prefill", "kda_prefill_workspace_size", "kda_decode", "kda_decode_multi",
-           "kda_decode_commit")
+           "kda_decode_commit", "kda_state_copy")
 MAX_SPEC_TOKENS = 8
 UPDATE_FLOATS = 6 * 128  # floats per (sequence, head, token) update record
 
@@ -40,6 +40,7 @@ class KdaPrefillArgs(ctypes.Structure):
         ("conv_weight", _p), ("conv_bias", _p), ("conv_state_in", _p), ("conv_state_out", _p),
         ("state_in", _p), ("state_out", _p), ("o", _p), ("cu_seqlens", _p),
         ("cu_seqlens_host", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+        ("state_slots", _p), ("num_slots", _c_i32),
     ]
 
 
@@ -50,6 +51,7 @@ class KdaDecodeArgs(ctypes.Structure):
         ("scale", _c_f32), ("gate_lower_bound", _c_f32),
         ("q", _p), ("k", _p), ("v", _p), ("gate", _p), ("beta", _p),
         ("conv_weight", _p), ("conv_bias", _p), ("conv_state", _p), ("state", _p), ("o", _p),
+        ("state_slots", _p), ("num_slots", _c_i32),
     ]
 
 
@@ -61,7 +63,7 @@ class KdaDecodeMultiArgs(ctypes.Structure):
         ("q", _p), ("k", _p), ("v", _p), ("gate", _p), ("beta", _p),
         ("conv_weight", _p), ("conv_bias", _p), ("conv_state", _p), ("state", _p), ("o", _p),
         ("updates", _p), ("pending_updates", _p), ("pending_accepted", _p),
-        ("pending_tokens", _c_i32),
+        ("pending_tokens", _c_i32), ("state_slots", _p), ("num_slots", _c_i32),
     ]
 
 
@@ -70,6 +72,16 @@ class KdaDecodeCommitArgs(ctypes.Structure):
         ("num_seqs", _c_i32), ("num_heads", _c_i32), ("head_dim_k", _c_i32),
         ("head_dim_v", _c_i32), ("num_tokens", _c_i32), ("dtype", ctypes.c_int),
         ("flags", _c_u32), ("accepted", _p), ("updates", _p), ("conv_state", _p), ("state", _p),
+        ("state_slots", _p), ("num_slots", _c_i32),
+    ]
+
+
+class KdaStateCopyArgs(ctypes.Structure):
+    _fields_ = [
+        ("count", _c_i32), ("num_heads", _c_i32), ("head_dim_k", _c_i32), ("head_dim_v", _c_i32),
+        ("num_slots", _c_i32), ("dtype", ctypes.c_int), ("flags", _c_u32),
+        ("src_slots", _p), ("dst_slots", _p), ("state_src", _p), ("state_dst", _p),
+        ("conv_src", _p), ("conv_dst", _p),
     ]
 
 
@@ -110,6 +122,8 @@ def load_library(path: str = LIB_PATH):
         lib.kda_decode_multi.argtypes = [ctypes.POINTER(KdaDecodeMultiArgs), _p]
         lib.kda_decode_commit.restype = ctypes.c_int
         lib.kda_decode_commit.argtypes = [ctypes.POINTER(KdaDecodeCommitArgs), _p]
+        lib.kda_state_copy.restype = ctypes.c_int
+        lib.kda_state_copy.argtypes = [ctypes.POINTER(KdaStateCopyArgs), _p]
         if path == LIB_PATH:
             _lib = lib
         return lib
@@ -139,6 +153,17 @@ def _state_flag(state):
     if state.dtype == torch.float32:
         return 0
     raise TypeError("state must be float32 or bfloat16, got %s" % state.dtype)
+
+
+def _slots(state_slots, state, n, dev):
+    """(pointer, num_slots) of an optional int32 slot map into a pool whose first
+    dimension is its number of rows."""
+    if state_slots is None:
+        return None, 0
+    _need(state_slots, "state_slots", torch.int32, dev)
+    if state_slots.numel() != n:
+        raise ValueError("state_slots must hold one slot per sequence")
+    return _ptr(state_slots), int(state.shape[0])
 
 
 def _stream(stream, device):
@@ -197,11 +222,13 @@ def kda_short_conv(x, weight, *, cu_seqlens=None, cu_seqlens_host=None, bias=Non
 def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens_host=None,
                 num_seqs=None, conv_bias=None, conv_state_in=None, conv_state_out=None,
                 state_in=None, state_out=None, o=None, scale=0.0, gate_lower_bound=-5.0,
-                chunk_size=0, flags=0, workspace=None, stream=None):
+                chunk_size=0, flags=0, workspace=None, state_slots=None, stream=None):
     """Chunked KDA prefill of packed sequences.
 
     The state (state_in / state_out) is fp32, or bf16 storage when those tensors are
-    bf16 (state_out=True allocates the dtype of state_in, else fp32).
+    bf16 (state_out=True allocates the dtype of state_in, else fp32).  With
+    state_slots (int32 [N]) the state and conv-state tensors are pools and sequence n
+    uses row state_slots[n] (state_out / conv_state_out must then be given).
 
     q, k, gate: [T, H, 128]; v: [T, H, 128]; beta: [T, H] (bf16 or fp32, one dtype);
     conv_weight: [3*H*128, 4] fp32.  state_out / conv_state_out: a tensor, or True
@@ -246,6 +273,12 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
         conv_state_in=_ptr(conv_state_in), conv_state_out=_ptr(conv_state_out),
         state_in=_ptr(state_in), state_out=_ptr(state_out), o=_ptr(o),
         cu_seqlens=_ptr(cu_seqlens), cu_seqlens_host=_ptr(cuh), workspace=None, workspace_bytes=0)
+    if state_slots is not None:
+        pool = next((t for t in (state_in, state_out, conv_state_in, conv_state_out)
+                     if torch.is_tensor(t)), None)
+        if pool is None:
+            raise ValueError("state_slots needs a state or conv-state pool")
+        a.state_slots, a.num_slots = _slots(state_slots, pool, N, dev)
     if workspace is True:
         need = lib.kda_prefill_workspace_size(ctypes.byref(a))
         workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
@@ -268,7 +301,7 @@ def prefill_workspace_bytes(total_tokens, num_heads, num_seqs=1, dtype=torch.bfl
 
 
 def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias=None, o=None,
-               scale=0.0, gate_lower_bound=-5.0, flags=0, stream=None):
+               scale=0.0, gate_lower_bound=-5.0, flags=0, state_slots=None, stream=None):
     """One decode step: q, k, gate, v: [N, H, 128]; beta [N, H]; conv_state [N, 3, CC]
     and state [N, H, 128, 128] (fp32, or bf16 storage) are updated in place.
     Returns o [N, H, 128]."""
@@ -290,13 +323,14 @@ def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias
         q=_ptr(q), k=_ptr(k), v=_ptr(v), gate=_ptr(gate), beta=_ptr(beta),
         conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias), conv_state=_ptr(conv_state),
         state=_ptr(state), o=_ptr(o))
+    a.state_slots, a.num_slots = _slots(state_slots, state, N, dev)
     _check(lib, lib.kda_decode(ctypes.byref(a), _stream(stream, dev)))
     return o
 
 
 def kda_decode_multi(q, k, v, gate, beta, conv_weight, conv_state, state, *, updates=None,
                      conv_bias=None, o=None, pending_updates=None, pending_accepted=None,
-                     scale=0.0, gate_lower_bound=-5.0, flags=0, stream=None):
+                     scale=0.0, gate_lower_bound=-5.0, flags=0, state_slots=None, stream=None):
     """Speculative decode of T tokens per sequence.  q, k, gate, v: [N, T, H, 128];
     beta [N, T, H].  conv_state [N, 3, CC] and state [N, H, 128, 128] fp32 are only
     read, unless pending_updates ([N, H, T', 768] fp32 records of a previous call) and
@@ -336,17 +370,19 @@ def kda_decode_multi(q, k, v, gate, beta, conv_weight, conv_state, state, *, upd
         state=_ptr(state), o=_ptr(o), updates=_ptr(updates),
         pending_updates=_ptr(pending_updates), pending_accepted=_ptr(pending_accepted),
         pending_tokens=pt)
+    a.state_slots, a.num_slots = _slots(state_slots, state, N, dev)
     _check(lib, lib.kda_decode_multi(ctypes.byref(a), _stream(stream, dev)))
     return o, updates
 
 
-def kda_decode_commit(updates, accepted, conv_state, state, *, stream=None):
+def kda_decode_commit(updates, accepted, conv_state, state, *, state_slots=None, stream=None):
     """Advance state [N, H, 128, 128] (fp32 or bf16) and conv_state [N, 3, CC] in place over the
     first accepted[n] tokens ([N] int32 on the device) recorded in updates
     ([N, H, T, 768] fp32, written by kda_decode_multi)."""
     lib = load_library()
     dev = state.device
-    N, H, dk, dv = state.shape
+    N = accepted.numel()
+    H, dk, dv = state.shape[1:]
     T = updates.numel() // (N * H * UPDATE_FLOATS)
     if updates.numel() != N * H * T * UPDATE_FLOATS:
         raise ValueError("updates must hold N*H*T*%d floats" % UPDATE_FLOATS)
@@ -360,4 +396,33 @@ def kda_decode_commit(updates, accepted, conv_state, state, *, stream=None):
                             num_tokens=T, dtype=_dtype_code(conv_state),
                             flags=_state_flag(state), accepted=_ptr(accepted),
                             updates=_ptr(updates), conv_state=_ptr(conv_state), state=_ptr(state))
+    a.state_slots, a.num_slots = _slots(state_slots, state, N, dev)
     _check(lib, lib.kda_decode_commit(ctypes.byref(a), _stream(stream, dev)))
+
+
+def kda_state_copy(state_pool, src_slots, dst_slots, *, conv_pool=None, dst_state_pool=None,
+                   dst_conv_pool=None, stream=None):
+    """Copy pool rows: state (and conv state) of slot src_slots[i] to dst_slots[i]
+    (int32 device tensors).  The destination pools default to the source pools."""
+    lib = load_library()
+    dev = state_pool.device
+    P, H, dk, dv = state_pool.shape
+    dst_state_pool = state_pool if dst_state_pool is None else dst_state_pool
+    if conv_pool is not None and dst_conv_pool is None:
+        dst_conv_pool = conv_pool
+    for t, nm in ((state_pool, "state_pool"), (dst_state_pool, "dst_state_pool"),
+                  (conv_pool, "conv_pool"), (dst_conv_pool, "dst_conv_pool")):
+        _need(t, nm, None, dev)
+    for t, nm in ((src_slots, "src_slots"), (dst_slots, "dst_slots")):
+        _need(t, nm, torch.int32, dev)
+    if src_slots.numel() != dst_slots.numel():
+        raise ValueError("src_slots and dst_slots must have one length")
+    if dst_state_pool.shape != state_pool.shape or dst_state_pool.dtype != state_pool.dtype:
+        raise ValueError("the state pools must match in shape and dtype")
+    a = KdaStateCopyArgs(count=src_slots.numel(), num_heads=H, head_dim_k=dk, head_dim_v=dv,
+                         num_slots=P, dtype=_dtype_code(conv_pool) if conv_pool is not None else KDA_BF16,
+                         flags=_state_flag(state_pool), src_slots=_ptr(src_slots),
+                         dst_slots=_ptr(dst_slots), state_src=_ptr(state_pool),
+                         state_dst=_ptr(dst_state_pool), conv_src=_ptr(conv_pool),
+                         conv_dst=_ptr(dst_conv_pool))
+    _check(lib, lib.kda_state_copy(ctypes.byref(a), _stream(stream, dev)))

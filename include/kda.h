@@ -40,6 +40,20 @@
  *     for the calling thread's last failure.  No exception crosses the ABI.
  *   - Thread safety: no global mutable state besides that per-thread message;
  *     concurrent calls on different buffers are safe.
+ *
+ * State pool (prefill, decode, decode_multi, decode_commit).  By default
+ * sequence n of a call owns row n of the state and conv-state arrays.  With
+ * `state_slots` (int32 [N], device memory) it owns row state_slots[n] of a pool
+ * of `num_slots` rows instead: the state and conv-state arguments then point
+ * to [num_slots][...] arrays, and a serving loop keeps every live sequence's
+ * state resident and passes each call's batch as slot numbers.  Prefix reuse
+ * fits the same pool: kda_state_copy snapshots or forks slots.  The disaggregated
+ * deployment of the pages keeps identical KDA layouts for prefill and decode
+ * ("GLM-5.3-Flash im Detail", section "FP8-Checkpoint und Betriebsgrenzen"),
+ * and this pool is one such layout.  Slots of one call must be distinct.  A
+ * slot outside [0, num_slots) cannot be checked on the host; on the device
+ * that sequence is skipped: none of its outputs, state or conv state is read
+ * or written.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -51,7 +65,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
     KDA_OK = 0,
@@ -154,6 +168,8 @@ typedef struct {
     const int32_t *cu_seqlens_host; /* optional host copy, validated when given */
     void *workspace;           /* device scratch for the two-pass schedule, or NULL */
     size_t workspace_bytes;    /* its size; see kda_prefill_workspace_size */
+    const int32_t *state_slots;/* [N] device pool slots, or NULL (see "State pool") */
+    int32_t num_slots;         /* pool rows when state_slots is given */
 } kda_prefill_args;
 
 /*
@@ -199,6 +215,8 @@ typedef struct {
     void *conv_state;        /* [N][3][CC] in/out (shifted by one token) */
     void *state;             /* [N][H][dk][dv] in/out: fp32, or bf16 with KDA_F_STATE_BF16 */
     void *o;                 /* [N][H][dv] */
+    const int32_t *state_slots; /* [N] device pool slots, or NULL (see "State pool") */
+    int32_t num_slots;          /* pool rows when state_slots is given */
 } kda_decode_args;
 
 kda_status kda_decode(const kda_decode_args *args, hipStream_t stream);
@@ -261,7 +279,10 @@ typedef struct {
      * before the T new tokens are evaluated (NULL pending_updates: none). */
     const float *pending_updates;    /* that call's records; must not overlap updates */
     const int32_t *pending_accepted; /* [N] device: tokens of that call to keep */
-    int32_t pending_tokens;          /* that call's T */
+    int32_t pending_tokens;          /* that call's T; the previous call must have had
+                                        the same N, H and state_slots */
+    const int32_t *state_slots; /* [N] device pool slots, or NULL (see "State pool") */
+    int32_t num_slots;          /* pool rows when state_slots is given */
 } kda_decode_multi_args;
 
 kda_status kda_decode_multi(const kda_decode_multi_args *args, hipStream_t stream);
@@ -285,9 +306,38 @@ typedef struct {
     const float *updates;    /* [N][H][T][KDA_UPDATE_FLOATS] records */
     void *conv_state;        /* [N][3][CC] in/out */
     void *state;             /* [N][H][dk][dv] in/out, fp32 or bf16 */
+    const int32_t *state_slots; /* [N] device pool slots, or NULL (see "State pool") */
+    int32_t num_slots;          /* pool rows when state_slots is given */
 } kda_decode_commit_args;
 
 kda_status kda_decode_commit(const kda_decode_commit_args *args, hipStream_t stream);
+
+/*
+ * kda_state_copy -- copy `count` pool rows: state and conv state of slot
+ * src_slots[i] to slot dst_slots[i] (a prefix snapshot, or a fork of a cached
+ * prefix into a new sequence: the serving branch of "GLM-5.3-Flash Internals"
+ * runs with prefix caching, see its context-ladder battery).  Source and destination pools may be the same
+ * array.  A destination slot must not also be a source of the same call, and
+ * destination slots must be distinct.  Pairs with a slot outside
+ * [0, num_slots) are skipped on the device.
+ */
+typedef struct {
+    int32_t count;           /* copies, >= 0 */
+    int32_t num_heads;       /* H >= 1 */
+    int32_t head_dim_k;      /* must be 128 */
+    int32_t head_dim_v;      /* must be 128 */
+    int32_t num_slots;       /* rows of each pool, >= 1 */
+    kda_dtype dtype;         /* dtype of the conv states */
+    uint32_t flags;          /* 0 or KDA_F_STATE_BF16 */
+    const int32_t *src_slots;/* [count] device */
+    const int32_t *dst_slots;/* [count] device */
+    const void *state_src;   /* [num_slots][H][dk][dv] */
+    void *state_dst;         /* [num_slots][H][dk][dv]; may be state_src */
+    const void *conv_src;    /* [num_slots][3][CC], or NULL (state only) */
+    void *conv_dst;          /* [num_slots][3][CC]; NULL exactly when conv_src is */
+} kda_state_copy_args;
+
+kda_status kda_state_copy(const kda_state_copy_args *args, hipStream_t stream);
 
 #ifdef __cplusplus
 }

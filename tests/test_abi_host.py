@@ -35,7 +35,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -49,14 +49,19 @@ def test_struct_layouts_match_header():
     # offsets of the first pointer fields follow the C layout rules (int64 aligned at 8)
     assert K.KdaPrefillArgs.total_tokens.offset == 24
     assert K.KdaPrefillArgs.q.offset == 48
-    assert ctypes.sizeof(K.KdaPrefillArgs) == 48 + 16 * 8
+    assert K.KdaPrefillArgs.state_slots.offset == 48 + 16 * 8
+    assert ctypes.sizeof(K.KdaPrefillArgs) == 48 + 18 * 8
     assert K.KdaDecodeArgs.q.offset == 32
-    assert ctypes.sizeof(K.KdaDecodeArgs) == 32 + 10 * 8
+    assert K.KdaDecodeArgs.state_slots.offset == 32 + 10 * 8
+    assert ctypes.sizeof(K.KdaDecodeArgs) == 32 + 12 * 8
     assert K.KdaDecodeMultiArgs.q.offset == 40
     assert K.KdaDecodeMultiArgs.pending_tokens.offset == 40 + 13 * 8
-    assert ctypes.sizeof(K.KdaDecodeMultiArgs) == 40 + 14 * 8
+    assert K.KdaDecodeMultiArgs.state_slots.offset == 40 + 14 * 8
+    assert ctypes.sizeof(K.KdaDecodeMultiArgs) == 40 + 16 * 8
     assert K.KdaDecodeCommitArgs.accepted.offset == 32
-    assert ctypes.sizeof(K.KdaDecodeCommitArgs) == 32 + 4 * 8
+    assert ctypes.sizeof(K.KdaDecodeCommitArgs) == 32 + 6 * 8
+    assert K.KdaStateCopyArgs.src_slots.offset == 32
+    assert ctypes.sizeof(K.KdaStateCopyArgs) == 32 + 6 * 8
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
@@ -237,6 +242,62 @@ def test_decode_commit_rejects_records_over_state(lib):
     a = _commit_args()
     a.updates = ctypes.c_void_p(a.state + 4096)
     assert lib.kda_decode_commit(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_pool_needs_num_slots(lib):
+    # a slot map without a pool size is rejected on the host (no launch)
+    a = _prefill_args(state_slots=FAKE, num_slots=0)
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    a = _decode_args(state_slots=FAKE, num_slots=0)
+    assert lib.kda_decode(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    a = _multi_args(state_slots=FAKE, num_slots=-3)
+    assert lib.kda_decode_multi(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    a = _commit_args(state_slots=FAKE, num_slots=0)
+    assert lib.kda_decode_commit(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_pool_size_drives_overlap_checks(lib):
+    # with 9 pool rows the fp32 state of 2 heads spans 9 * 2 * 64 KiB: o inside it is rejected
+    a = _decode_args(state_slots=FAKE, num_slots=9)
+    a.o = ctypes.c_void_p(a.state + 8 * 2 * 65536)
+    assert lib.kda_decode(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def _copy_args(**kw):
+    a = K.KdaStateCopyArgs(count=2, num_heads=2, head_dim_k=128, head_dim_v=128, num_slots=4,
+                           dtype=K.KDA_BF16, flags=0)
+    for i, f in enumerate(("src_slots", "dst_slots", "state_src", "state_dst", "conv_src",
+                           "conv_dst")):
+        setattr(a, f, ctypes.c_void_p(0x100000 + i * 0x1000000))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("count", -1, K.KDA_ERR_INVALID_ARG),
+    ("num_slots", 0, K.KDA_ERR_INVALID_ARG),
+    ("num_heads", 0, K.KDA_ERR_INVALID_ARG),
+    ("head_dim_k", 64, K.KDA_ERR_UNSUPPORTED),
+    ("flags", K.KDA_F_SILU, K.KDA_ERR_UNSUPPORTED),
+    ("src_slots", None, K.KDA_ERR_INVALID_ARG),
+    ("state_dst", None, K.KDA_ERR_INVALID_ARG),
+    ("conv_dst", None, K.KDA_ERR_INVALID_ARG),  # conv_src given without conv_dst
+])
+def test_state_copy_rejects_bad_arguments(lib, field, value, status):
+    a = _copy_args(**{field: value})
+    assert lib.kda_state_copy(ctypes.byref(a), None) == status
+
+
+def test_state_copy_rejects_partial_pool_overlap(lib):
+    a = _copy_args()
+    a.state_dst = ctypes.c_void_p(a.state_src + 4096)
+    assert lib.kda_state_copy(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+
+
+def test_state_copy_of_nothing_is_ok(lib):
+    a = _copy_args(count=0)  # validated, then nothing is launched
+    assert lib.kda_state_copy(ctypes.byref(a), None) == K.KDA_OK
 
 
 def test_short_conv_rejects_bad_arguments(lib):
