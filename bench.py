@@ -18,6 +18,8 @@ drafted tokens plus one):
                                          (kda_decode_multi with pending records)
   spec_commit: the same commit on its own, as at the end of a speculative
                run                                          (kda_decode_commit)
+  gate_proj  : the gate and beta in-projections of the prefill's tokens
+               (hidden 4096, rank 128, log-decay epilogue)  (kda_gate_beta_proj)
 Every call is bracketed by HIP events on the stream it is launched on, after a
 512 MiB scratch write that evicts L2 and the MALL (not timed); `value` is
 prefill tokens per second per layer from the median prefill call time, decode
@@ -68,7 +70,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "decode_bf16_state", "short_conv",
-                                       "spec_decode", "spec_commit", "copy"],
+                                       "spec_decode", "spec_commit", "gate_proj", "copy"],
                     default="all", help="run one entry point only (for profiler passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -114,6 +116,10 @@ def main():
               for _ in range(2)]
     o_sp = torch.empty_like(Sp["v"])
     sp_turn = [0]
+    Gp = KI.make_gate_proj(T, H=H, device=dev)  # the prefill's 4096 tokens, hidden 4096
+    g_out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    b_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    g_ws = torch.empty(kda.gate_beta_workspace_bytes(T, H), dtype=torch.uint8, device=dev)
     copy_src = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
     copy_dst = torch.empty_like(copy_src)
     scratch = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
@@ -145,6 +151,10 @@ def main():
         kda.kda_decode(Dd["q"], Dd["k"], Dd["v"], Dd["gate"], Dd["beta"], Dd["conv_w"], cs16, st16,
                        o=o_dec16)
 
+    def run_gate_proj():
+        kda.kda_gate_beta_proj(Gp["x"], Gp["w_a"], Gp["w_b"], Gp["w_beta"], gate=g_out, beta=b_out,
+                               workspace=g_ws, log=True)
+
     def run_conv():
         kda.kda_short_conv(X, P["conv_w"], cu_seqlens=cu1, y=Y)
 
@@ -153,10 +163,10 @@ def main():
 
     ops = {"prefill": run_prefill, "decode": run_decode, "short_conv": run_conv,
            "decode_bf16_state": run_decode16, "spec_decode": run_spec, "spec_commit": run_commit,
-           "copy": run_copy}
+           "gate_proj": run_gate_proj, "copy": run_copy}
     step_names = ["short_conv", "prefill", "decode"]
     if args.only == "all":
-        names = step_names + ["decode_bf16_state", "spec_decode", "spec_commit"]
+        names = step_names + ["decode_bf16_state", "spec_decode", "spec_commit", "gate_proj"]
     else:
         names = [args.only]
 
@@ -213,6 +223,10 @@ def main():
         sp_bytes += per * H
     sp_s = ms["spec_decode"] * 1e-3
     sp_state_bytes = 2 * N_sp * H * 128 * 128 * 4
+    # gate projections: x [T][4096] and the three weights in, gate [T][H*128] and beta out
+    hid_gp = Gp["x"].shape[1]
+    gp_flops = 2 * T * hid_gp * (128 + H) + 2 * T * 128 * H * 128
+    gp_bytes = 2 * (T * hid_gp + (128 + H) * hid_gp + H * 128 * 128 + T * H * 128 + T * H)
     traffic = _traffic_from_profile("kda_prefill_split.hip", "prefill_bf16_T4096_H64_pmc.md")
     dec_traffic = _traffic_from_profile("kda_decode.hip", "decode_bf16_N256_H64_pmc.md")
 
@@ -258,6 +272,15 @@ def main():
             "algorithmic_bytes_per_launch": dec_state_bytes + dec_other,
         },
         "short_conv_GBps": round(conv_bytes / (ms["short_conv"] * 1e-3) / 1e9, 1),
+        "gate_proj": {
+            "workload": "gate and beta in-projections of the prefill's 4096 tokens: hidden 4096, "
+                        "rank 128, 64 heads x 128 gate channels, bf16, log-decay epilogue",
+            "us_per_call": round(ms["gate_proj"] * 1e3, 2),
+            "TFLOPs": round(gp_flops / (ms["gate_proj"] * 1e-3) / 1e12, 1),
+            "GBps": round(gp_bytes / (ms["gate_proj"] * 1e-3) / 1e9, 1),
+            "flops_per_call": gp_flops,
+            "algorithmic_bytes_per_call": gp_bytes,
+        },
         "decode_bf16_state": {
             "workload": "workload 2 with the state stored as bf16 (256 x 64 x 128 x 128, 512 MiB)",
             "us_per_call": round(ms["decode_bf16_state"] * 1e3, 2),

@@ -6,11 +6,13 @@ include/kda.h); this package is its thin Python binding.
 from .kda import (KDA_F32, KDA_BF16, KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG,
                   KDA_F_STATE_BF16,
                   KdaError, MAX_SPEC_TOKENS, UPDATE_FLOATS, abi_version, kda_decode, kda_decode_commit,
-                  kda_decode_multi, kda_prefill, kda_short_conv, kda_state_copy, load_library,
+                  kda_decode_multi, kda_gate_beta_proj, kda_prefill, kda_short_conv,
+                  kda_state_copy, gate_beta_workspace_bytes, load_library,
                   prefill_workspace_bytes)
 
 __all__ = ["kda_short_conv", "kda_prefill", "kda_decode", "kda_decode_multi",
-           "kda_decode_commit", "kda_state_copy", "abi_version", "load_library",
+           "kda_decode_commit", "kda_state_copy", "kda_gate_beta_proj",
+           "gate_beta_workspace_bytes", "abi_version", "load_library",
            "prefill_workspace_bytes",
            "KdaError", "MAX_SPEC_TOKENS", "UPDATE_FLOATS", "KDA_F32", "KDA_BF16", "KDA_F_SILU", "KDA_F_NO_QK_L2NORM",
            "KDA_F_GATE_IS_LOG", "KDA_F_STATE_BF16"]

@@ -22,8 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_conv.hip", "kda_decode.hip", "kda_pool.hip", "kda_prefill.hip",
-           "kda_prefill_split.hip"]
+SOURCES = ["kda_api.hip", "kda_conv.hip", "kda_decode.hip", "kda_gate_proj.hip", "kda_pool.hip",
+           "kda_prefill.hip", "kda_prefill_split.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 

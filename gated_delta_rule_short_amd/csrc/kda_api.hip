@@ -377,4 +377,57 @@ kda_status kda_state_copy(const kda_state_copy_args *a, hipStream_t stream) {
     return KDA_OK;
 }
 
+size_t kda_gate_beta_workspace_size(const kda_gate_beta_args *a) {
+    if (!a || a->total_tokens < 0 || a->num_heads < 1) return 0;
+    return kda::gate_proj_workspace_bytes(a->total_tokens, a->num_heads);
+}
+
+kda_status kda_gate_beta_proj(const kda_gate_beta_args *a, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
+    const int64_t T = a->total_tokens;
+    if (T < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens < 0");
+    if (T > ((int64_t)1 << 31) - 64) return fail(KDA_ERR_INVALID_ARG, "total_tokens too large");
+    if (a->hidden < 128 || a->hidden % 128)
+        return fail(KDA_ERR_UNSUPPORTED, "hidden = %d: a positive multiple of 128 is needed", a->hidden);
+    if (a->rank != 128) return fail(KDA_ERR_UNSUPPORTED, "rank = %d: only 128 is supported", a->rank);
+    if (a->head_dim_k != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "head_dim_k = %d: only 128 is supported", a->head_dim_k);
+    if (a->num_heads < 32 || a->num_heads > 128 || a->num_heads % 32)
+        return fail(KDA_ERR_UNSUPPORTED, "num_heads = %d: 32, 64, 96 or 128", a->num_heads);
+    if (a->flags & ~(uint32_t)KDA_F_GATE_IS_LOG)
+        return fail(KDA_ERR_UNSUPPORTED, "unsupported flags 0x%x", a->flags);
+    if (!std::isfinite(a->gate_lower_bound) || !(a->gate_lower_bound < 0.f))
+        return fail(KDA_ERR_INVALID_ARG, "gate_lower_bound must be finite and < 0");
+    if (T == 0) return KDA_OK;
+    const void *ptrs[8] = {a->x, a->w_a, a->w_b, a->w_beta, a->gate, a->beta, a->workspace, nullptr};
+    for (int i = 0; i < 7; ++i) {
+        if (!ptrs[i])
+            return fail(KDA_ERR_INVALID_ARG, "x, w_a, w_b, w_beta, gate, beta and workspace must be "
+                                             "non-NULL");
+        if ((uintptr_t)ptrs[i] % 16)
+            return fail(KDA_ERR_INVALID_ARG, "every tensor must be 16-byte aligned");
+    }
+    const size_t need = kda::gate_proj_workspace_bytes(T, a->num_heads);
+    if (a->workspace_bytes < need)
+        return fail(KDA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", a->workspace_bytes, need);
+    const size_t H = (size_t)a->num_heads, hid = (size_t)a->hidden;
+    const size_t xb = (size_t)T * hid * 2, gb = (size_t)T * H * 128 * 2, bb = (size_t)T * H * 2;
+    const void *ins[4] = {a->x, a->w_a, a->w_b, a->w_beta};
+    const size_t inb[4] = {xb, 128 * hid * 2, H * 128 * 128 * 2, H * hid * 2};
+    const void *outs[3] = {a->gate, a->beta, a->workspace};
+    const size_t outb[3] = {gb, bb, need};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 4; ++i)
+            if (overlap(outs[o], outb[o], ins[i], inb[i]))
+                return fail(KDA_ERR_INVALID_ARG, "an output or the workspace overlaps an input");
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (overlap(outs[o], outb[o], outs[o2], outb[o2]))
+                return fail(KDA_ERR_INVALID_ARG, "gate, beta and workspace must not overlap");
+    }
+    hipError_t e = kda::launch_gate_proj(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "gate_beta_proj launch");
+    return KDA_OK;
+}
+
 }  // extern "C"

@@ -23,6 +23,10 @@ hipError_t launch_conv_tail(kda_dtype dt, const void *const src[3], const int ch
                             int64_t T, const void *cs_in, void *cs_out, const int32_t *cu,
                             int num_seqs, const int32_t *slots, int num_slots, hipStream_t s);
 
+// Gate and beta in-projections (two matrix-core passes through the workspace).
+size_t gate_proj_workspace_bytes(int64_t T, int H);
+hipError_t launch_gate_proj(const kda_gate_beta_args *a, hipStream_t s);
+
 // Pool rows: state (and conv state when given) of slot src[i] -> slot dst[i].
 hipError_t launch_state_copy(const kda_state_copy_args *a, hipStream_t s);
 

@@ -22,7 +22,8 @@ KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG, KDA_F_STATE_BF16 = 1, 2, 4, 8
 # every symbol include/kda.h declares
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_short_conv",
            "kda_prefill", "kda_prefill_workspace_size", "kda_decode", "kda_decode_multi",
-           "kda_decode_commit", "kda_state_copy")
+           "kda_decode_commit", "kda_state_copy", "kda_gate_beta_proj",
+           "kda_gate_beta_workspace_size")
 MAX_SPEC_TOKENS = 8
 UPDATE_FLOATS = 6 * 128  # floats per (sequence, head, token) update record
 
@@ -85,6 +86,15 @@ class KdaStateCopyArgs(ctypes.Structure):
     ]
 
 
+class KdaGateBetaArgs(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", _c_i64), ("hidden", _c_i32), ("rank", _c_i32), ("num_heads", _c_i32),
+        ("head_dim_k", _c_i32), ("flags", _c_u32), ("gate_lower_bound", _c_f32),
+        ("x", _p), ("w_a", _p), ("w_b", _p), ("w_beta", _p), ("gate", _p), ("beta", _p),
+        ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class KdaError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__("%s: %s" % (status, msg))
@@ -122,6 +132,10 @@ def load_library(path: str = LIB_PATH):
         lib.kda_decode_multi.argtypes = [ctypes.POINTER(KdaDecodeMultiArgs), _p]
         lib.kda_decode_commit.restype = ctypes.c_int
         lib.kda_decode_commit.argtypes = [ctypes.POINTER(KdaDecodeCommitArgs), _p]
+        lib.kda_gate_beta_proj.restype = ctypes.c_int
+        lib.kda_gate_beta_proj.argtypes = [ctypes.POINTER(KdaGateBetaArgs), _p]
+        lib.kda_gate_beta_workspace_size.restype = ctypes.c_size_t
+        lib.kda_gate_beta_workspace_size.argtypes = [ctypes.POINTER(KdaGateBetaArgs)]
         lib.kda_state_copy.restype = ctypes.c_int
         lib.kda_state_copy.argtypes = [ctypes.POINTER(KdaStateCopyArgs), _p]
         if path == LIB_PATH:
@@ -426,3 +440,41 @@ def kda_state_copy(state_pool, src_slots, dst_slots, *, conv_pool=None, dst_stat
                          state_dst=_ptr(dst_state_pool), conv_src=_ptr(conv_pool),
                          conv_dst=_ptr(dst_conv_pool))
     _check(lib, lib.kda_state_copy(ctypes.byref(a), _stream(stream, dev)))
+
+
+def kda_gate_beta_proj(x, w_a, w_b, w_beta, *, gate=None, beta=None, workspace=None, log=False,
+                       gate_lower_bound=-5.0, stream=None):
+    """Gate and beta in-projections: x [T, hidden], w_a [128, hidden], w_b [H*128, 128],
+    w_beta [H, hidden], all bf16.  Returns (gate [T, H, 128], beta [T, H]); with log=True
+    the gate is lb * sigmoid(a) (pass KDA_F_GATE_IS_LOG to the mixer), else a.
+    workspace: a uint8 tensor of at least kda_gate_beta_workspace_size bytes, or None
+    to allocate one."""
+    lib = load_library()
+    dev = x.device
+    T, hidden = x.shape
+    H = w_beta.shape[0]
+    if gate is None:
+        gate = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    if beta is None:
+        beta = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    for t, nm in ((x, "x"), (w_a, "w_a"), (w_b, "w_b"), (w_beta, "w_beta"), (gate, "gate"),
+                  (beta, "beta")):
+        _need(t, nm, torch.bfloat16, dev)
+    a = KdaGateBetaArgs(total_tokens=T, hidden=hidden, rank=w_a.shape[0], num_heads=H,
+                        head_dim_k=128, flags=KDA_F_GATE_IS_LOG if log else 0,
+                        gate_lower_bound=float(gate_lower_bound), x=_ptr(x), w_a=_ptr(w_a),
+                        w_b=_ptr(w_b), w_beta=_ptr(w_beta), gate=_ptr(gate), beta=_ptr(beta))
+    if workspace is None:
+        need = lib.kda_gate_beta_workspace_size(ctypes.byref(a))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    _check(lib, lib.kda_gate_beta_proj(ctypes.byref(a), _stream(stream, dev)))
+    return gate, beta
+
+
+def gate_beta_workspace_bytes(total_tokens, num_heads):
+    """Workspace bytes kda_gate_beta_proj needs."""
+    lib = load_library()
+    a = KdaGateBetaArgs(total_tokens=int(total_tokens), num_heads=int(num_heads))
+    return int(lib.kda_gate_beta_workspace_size(ctypes.byref(a)))

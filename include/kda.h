@@ -339,6 +339,45 @@ typedef struct {
 
 kda_status kda_state_copy(const kda_state_copy_args *args, hipStream_t stream);
 
+/*
+ * kda_gate_beta_proj -- the gate and beta in-projections that feed the mixer,
+ * with their activations fused into the matrix-core epilogues.  The decoder
+ * is 4096 wide and its activation batteries name a KDA gate projection and the
+ * second factor ("g_b_proj") of a two-factor one ("GLM-5.3-Flash Internals",
+ * sections "Anatomy" and the activation batteries); the gate is channel-wise with
+ * log-decay >= lb and beta is one scalar per head and token ("GLM-5.3-Flash im
+ * Detail", section "Sequenz-Mixing").  Per token x:
+ *     a    = W_b (W_a x)              rank r = 128, H * dk channels head-major
+ *     gate = a, or lb * sigmoid(a) with KDA_F_GATE_IS_LOG (then pass that flag
+ *            to kda_prefill / kda_decode, which read it as the log-decay)
+ *     beta = sigmoid(W_beta x)
+ * The first product runs in bf16 with fp32 accumulation and is rounded to bf16
+ * before the second.  All tensors are bf16 and 16-byte aligned; the workspace
+ * is overwritten by each call and must not be shared by concurrent calls.
+ */
+typedef struct {
+    int64_t total_tokens;    /* T >= 0 */
+    int32_t hidden;          /* width of x: a positive multiple of 128 */
+    int32_t rank;            /* r: must be 128 */
+    int32_t num_heads;       /* H: 32, 64, 96 or 128 */
+    int32_t head_dim_k;      /* must be 128 */
+    uint32_t flags;          /* 0 or KDA_F_GATE_IS_LOG */
+    float gate_lower_bound;  /* lb < 0 */
+    const void *x;           /* [T][hidden] */
+    const void *w_a;         /* [r][hidden] */
+    const void *w_b;         /* [H * dk][r] */
+    const void *w_beta;      /* [H][hidden] */
+    void *gate;              /* [T][H][dk]: the mixer's gate input */
+    void *beta;              /* [T][H] */
+    void *workspace;         /* kda_gate_beta_workspace_size() bytes */
+    size_t workspace_bytes;
+} kda_gate_beta_args;
+
+kda_status kda_gate_beta_proj(const kda_gate_beta_args *args, hipStream_t stream);
+
+/* Workspace bytes kda_gate_beta_proj needs (2 * T * r: z between the two products). */
+size_t kda_gate_beta_workspace_size(const kda_gate_beta_args *args);
+
 #ifdef __cplusplus
 }
 #endif

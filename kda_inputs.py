@@ -180,6 +180,20 @@ def make_accepted(N, T, seed, p=0.8, device="cpu"):
     return (1 + kept).to(torch.int32).to(device)
 
 
+def make_gate_proj(T, hidden=4096, H=H_MODEL, rank=128, seed=6, device="cpu", dk=D):
+    """Hidden states and synthetic in-projection weights for the gate and beta
+    projections: x ~ N(0, 1) (a normalised residual stream), W_a ~ N(0, 1/hidden),
+    W_b ~ N(0, 1/rank), W_beta ~ N(0, 1/hidden), so the gate pre-activation and
+    beta's argument are about N(0, 1), as in the mixer workloads.  All bf16."""
+    g = _gen(device, seed)
+    x = _randn(g, (T, hidden), device)
+    w_a = _randn(g, (rank, hidden), device, std=hidden ** -0.5)
+    w_b = _randn(g, (H * dk, rank), device, std=rank ** -0.5)
+    w_beta = _randn(g, (H, hidden), device, std=hidden ** -0.5)
+    bf = torch.bfloat16
+    return {"x": x.to(bf), "w_a": w_a.to(bf), "w_b": w_b.to(bf), "w_beta": w_beta.to(bf), "H": H}
+
+
 def workload_inputs(idx, device="cpu", H=None, T=None, num_seqs=None, seed=None):
     """Inputs of workload `idx`, optionally shrunk (fewer heads/tokens/sequences)
     with the same distributions, for parity cases the oracle finishes quickly."""
@@ -223,6 +237,6 @@ def prefill_flops_per_token_head(C=64, dk=D, dv=D):
 
 
 __all__ = ["WORKLOADS", "Workload", "make_prefill", "make_decode", "make_spec_decode",
-           "make_accepted", "workload_inputs",
+           "make_accepted", "make_gate_proj", "workload_inputs",
            "make_lengths", "cu_from_lengths", "bytes_per_token_head",
            "prefill_flops_per_token_head", "D", "H_MODEL"]

@@ -18,6 +18,9 @@ Parity status of each function:
                 for T<=8; L2 and gate limits).
   decode     -- pinned through prefill (same recurrence, length-one sequences)
                 and the decode-steps == prefill composition.
+  gate_beta_proj -- pinned (zero weights give the sigmoid midpoints exactly;
+                a brute-force scalar loop on tiny shapes; selection weights give
+                the closed form; the sign symmetry of the sigmoid).
 """
 from __future__ import annotations
 
@@ -172,3 +175,25 @@ def decode(q, k, v, gate, beta, conv_w, conv_state, state, conv_b=None, scale=No
                           _ptr(w), _ptr(b), _ptr(cs), _ptr(st), _ptr(o), float(scale),
                           float(gate_lower_bound), int(flags), int(nthreads))
     return {"o": o, "state": st, "conv_state": cs}
+
+
+def gate_beta_proj(x, w_a, w_b, w_beta, num_heads, gate_lower_bound=-5.0, log=False):
+    """The gate and beta in-projections in fp64 (numpy products as primitives).
+
+    Follows "GLM-5.3-Flash Internals" (hidden width, the named two-factor gate
+    projection) and "GLM-5.3-Flash im Detail", section "Sequenz-Mixing"
+    (channel-wise gate with log-decay >= lb, one beta per head and token):
+        a    = (x W_a^T) W_b^T      x [T][hidden], W_a [r][hidden], W_b [H*dk][r]
+        gate = a, or lb * sigmoid(a) when `log`
+        beta = sigmoid(x W_beta^T)  W_beta [H][hidden]
+    Returns dict(gate [T][H][dk], beta [T][H], a [T][H*dk]).  The reading that the
+    two factors multiply in this order, with no bias and no other activation, is
+    recorded in the design notes."""
+    x, w_a, w_b, w_beta = map(_f64, (x, w_a, w_b, w_beta))
+    T = x.shape[0]
+    z = x @ w_a.T
+    a = z @ w_b.T
+    sig = lambda u: 1.0 / (1.0 + np.exp(-u))
+    gate = gate_lower_bound * sig(a) if log else a
+    beta = sig(x @ w_beta.T)
+    return {"gate": gate.reshape(T, num_heads, -1), "beta": beta, "a": a}

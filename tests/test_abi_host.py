@@ -300,6 +300,45 @@ def test_state_copy_of_nothing_is_ok(lib):
     assert lib.kda_state_copy(ctypes.byref(a), None) == K.KDA_OK
 
 
+def _gb_args(**kw):
+    a = K.KdaGateBetaArgs(total_tokens=64, hidden=256, rank=128, num_heads=64, head_dim_k=128,
+                          flags=0, gate_lower_bound=-5.0)
+    for i, f in enumerate(("x", "w_a", "w_b", "w_beta", "gate", "beta", "workspace")):
+        setattr(a, f, ctypes.c_void_p(0x100000 + i * 0x1000000))
+    a.workspace_bytes = 2 * 64 * 128
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("total_tokens", -1, K.KDA_ERR_INVALID_ARG),
+    ("hidden", 200, K.KDA_ERR_UNSUPPORTED),
+    ("rank", 64, K.KDA_ERR_UNSUPPORTED),
+    ("num_heads", 48, K.KDA_ERR_UNSUPPORTED),
+    ("head_dim_k", 64, K.KDA_ERR_UNSUPPORTED),
+    ("flags", K.KDA_F_SILU, K.KDA_ERR_UNSUPPORTED),
+    ("gate_lower_bound", 0.5, K.KDA_ERR_INVALID_ARG),
+    ("x", None, K.KDA_ERR_INVALID_ARG),
+    ("w_b", ctypes.c_void_p(0x2000008), K.KDA_ERR_INVALID_ARG),  # not 16-byte aligned
+    ("workspace_bytes", 1024, K.KDA_ERR_INVALID_ARG),
+])
+def test_gate_beta_rejects_bad_arguments(lib, field, value, status):
+    a = _gb_args(**{field: value})
+    assert lib.kda_gate_beta_proj(ctypes.byref(a), None) == status
+
+
+def test_gate_beta_rejects_overlaps_and_sizes_workspace(lib):
+    a = _gb_args()
+    a.gate = a.x  # output over an input
+    assert lib.kda_gate_beta_proj(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    a = _gb_args()
+    a.beta = ctypes.c_void_p(a.workspace + 16)
+    assert lib.kda_gate_beta_proj(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    assert lib.kda_gate_beta_workspace_size(ctypes.byref(_gb_args())) == 2 * 64 * 128
+    assert lib.kda_gate_beta_proj(ctypes.byref(_gb_args(total_tokens=0)), None) == K.KDA_OK
+
+
 def test_short_conv_rejects_bad_arguments(lib):
     f = lib.kda_short_conv
     # num_seqs 0

@@ -9,6 +9,7 @@ gate with log-decay >= -5; scalar-beta delta-rule write; query read of the
 updated state.
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -369,3 +370,55 @@ def test_state_size_matches_published_arithmetic():
     assert per_layer * g["kda_layers"] == g["state_scalars_per_request"]
     mib = per_layer * g["kda_layers"] * 4 / 2 ** 20
     assert abs(mib - g["fp32_state_mib_approx"]) < 0.5
+
+
+# -------------------------------------------------------- gate / beta projection
+
+def _proj_inputs(T, hid, H, r=8, dk=4, seed=0):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((T, hid)), g.standard_normal((r, hid)) / np.sqrt(hid),
+            g.standard_normal((H * dk, r)) / np.sqrt(r), g.standard_normal((H, hid)) / np.sqrt(hid))
+
+
+def test_gate_proj_zero_weights_give_sigmoid_midpoints():
+    x, wa, wb, wbeta = _proj_inputs(5, 16, 3)
+    out = oracle.gate_beta_proj(x, 0 * wa, wb, 0 * wbeta, 3, gate_lower_bound=-5.0, log=True)
+    assert np.all(out["gate"] == -2.5) and np.all(out["beta"] == 0.5)
+    out = oracle.gate_beta_proj(x, wa, 0 * wb, wbeta, 3)
+    assert np.all(out["gate"] == 0.0)
+
+
+def test_gate_proj_brute_force_scalar_loops():
+    """Every output against explicit scalar sums on a tiny shape."""
+    T, hid, H, r, dk = 3, 6, 2, 4, 3
+    x, wa, wb, wbeta = _proj_inputs(T, hid, H, r, dk, seed=1)
+    out = oracle.gate_beta_proj(x, wa, wb, wbeta, H, gate_lower_bound=-5.0, log=True)
+    for t in range(T):
+        z = [sum(wa[i][j] * x[t][j] for j in range(hid)) for i in range(r)]
+        for h in range(H):
+            for c in range(dk):
+                a = sum(wb[h * dk + c][i] * z[i] for i in range(r))
+                assert abs(out["gate"][t, h, c] - (-5.0 / (1.0 + math.exp(-a)))) < 1e-12
+            b = sum(wbeta[h][j] * x[t][j] for j in range(hid))
+            assert abs(out["beta"][t, h] - 1.0 / (1.0 + math.exp(-b))) < 1e-12
+
+
+def test_gate_proj_selection_weights_closed_form():
+    """W_a picks hidden channels 0..r-1, W_b copies z channel (h*dk + c) % r: then
+    a[t, h, c] = x[t, (h*dk + c) % r] exactly."""
+    T, hid, H, r, dk = 4, 10, 2, 4, 3
+    x = np.random.default_rng(2).standard_normal((T, hid))
+    wa = np.eye(r, hid)
+    wb = np.zeros((H * dk, r))
+    for n in range(H * dk):
+        wb[n, n % r] = 1.0
+    out = oracle.gate_beta_proj(x, wa, wb, np.zeros((H, hid)), H)
+    for n in range(H * dk):
+        assert np.array_equal(out["gate"].reshape(T, -1)[:, n], x[:, n % r])
+
+
+def test_gate_proj_beta_sign_symmetry():
+    x, wa, wb, wbeta = _proj_inputs(7, 12, 4, seed=3)
+    b1 = oracle.gate_beta_proj(x, wa, wb, wbeta, 4)["beta"]
+    b2 = oracle.gate_beta_proj(x, wa, wb, -wbeta, 4)["beta"]
+    np.testing.assert_allclose(b1 + b2, 1.0, atol=1e-15)
