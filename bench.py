@@ -20,6 +20,8 @@ drafted tokens plus one):
                run                                          (kda_decode_commit)
   gate_proj  : the gate and beta in-projections of the prefill's tokens
                (hidden 4096, rank 128, log-decay epilogue)  (kda_gate_beta_proj)
+  state_copy : 128 rows of the decode pool (state + conv state) copied to
+               128 others, as prefix snapshots             (kda_state_copy)
 Every call is bracketed by HIP events on the stream it is launched on, after a
 512 MiB scratch write that evicts L2 and the MALL (not timed); `value` is
 prefill tokens per second per layer from the median prefill call time, decode
@@ -70,7 +72,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "decode_bf16_state", "short_conv",
-                                       "spec_decode", "spec_commit", "gate_proj", "copy"],
+                                       "spec_decode", "spec_commit", "gate_proj", "state_copy",
+                                       "copy"],
                     default="all", help="run one entry point only (for profiler passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -120,6 +123,10 @@ def main():
     g_out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
     b_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     g_ws = torch.empty(kda.gate_beta_workspace_bytes(T, H), dtype=torch.uint8, device=dev)
+    # prefix snapshots: 128 pool rows of the decode workload's pool copied to 128 others
+    n_cp = N_dec // 2
+    cp_src = torch.arange(0, n_cp, dtype=torch.int32, device=dev)
+    cp_dst = cp_src + n_cp
     copy_src = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
     copy_dst = torch.empty_like(copy_src)
     scratch = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
@@ -155,6 +162,9 @@ def main():
         kda.kda_gate_beta_proj(Gp["x"], Gp["w_a"], Gp["w_b"], Gp["w_beta"], gate=g_out, beta=b_out,
                                workspace=g_ws, log=True)
 
+    def run_state_copy():
+        kda.kda_state_copy(Dd["state"], cp_src, cp_dst, conv_pool=Dd["conv_state"])
+
     def run_conv():
         kda.kda_short_conv(X, P["conv_w"], cu_seqlens=cu1, y=Y)
 
@@ -163,10 +173,11 @@ def main():
 
     ops = {"prefill": run_prefill, "decode": run_decode, "short_conv": run_conv,
            "decode_bf16_state": run_decode16, "spec_decode": run_spec, "spec_commit": run_commit,
-           "gate_proj": run_gate_proj, "copy": run_copy}
+           "gate_proj": run_gate_proj, "state_copy": run_state_copy, "copy": run_copy}
     step_names = ["short_conv", "prefill", "decode"]
     if args.only == "all":
-        names = step_names + ["decode_bf16_state", "spec_decode", "spec_commit", "gate_proj"]
+        names = step_names + ["decode_bf16_state", "spec_decode", "spec_commit", "gate_proj",
+                              "state_copy"]
     else:
         names = [args.only]
 
@@ -224,6 +235,7 @@ def main():
     sp_s = ms["spec_decode"] * 1e-3
     sp_state_bytes = 2 * N_sp * H * 128 * 128 * 4
     # gate projections: x [T][4096] and the three weights in, gate [T][H*128] and beta out
+    cp_bytes = 2 * n_cp * H * (128 * 128 * 4 + 9 * 128 * 2)  # state and conv rows, read + written
     hid_gp = Gp["x"].shape[1]
     gp_flops = 2 * T * hid_gp * (128 + H) + 2 * T * 128 * H * 128
     gp_bytes = 2 * (T * hid_gp + (128 + H) * hid_gp + H * 128 * 128 + T * H * 128 + T * H)
@@ -280,6 +292,16 @@ def main():
             "GBps": round(gp_bytes / (ms["gate_proj"] * 1e-3) / 1e9, 1),
             "flops_per_call": gp_flops,
             "algorithmic_bytes_per_call": gp_bytes,
+        },
+        "state_copy": {
+            "workload": "%d pool rows (fp32 state, 64 heads, and conv state) copied to %d other "
+                        "rows of the decode workload's pool" % (n_cp, n_cp),
+            "us_per_call": round(ms["state_copy"] * 1e3, 2),
+            "GBps": round(cp_bytes / (ms["state_copy"] * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(cp_bytes / (ms["state_copy"] * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(cp_bytes / (ms["state_copy"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": cp_bytes},
         },
         "decode_bf16_state": {
             "workload": "workload 2 with the state stored as bf16 (256 x 64 x 128 x 128, 512 MiB)",

@@ -388,13 +388,14 @@ kda_status kda_gate_beta_proj(const kda_gate_beta_args *a, hipStream_t stream) {
     const int64_t T = a->total_tokens;
     if (T < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens < 0");
     if (T > ((int64_t)1 << 31) - 64) return fail(KDA_ERR_INVALID_ARG, "total_tokens too large");
-    if (a->hidden < 128 || a->hidden % 128)
-        return fail(KDA_ERR_UNSUPPORTED, "hidden = %d: a positive multiple of 128 is needed", a->hidden);
+    if (a->hidden < 256 || a->hidden % 256)  // four K quarters of whole 64-wide super-steps
+        return fail(KDA_ERR_UNSUPPORTED, "hidden = %d: a positive multiple of 256 is needed", a->hidden);
     if (a->rank != 128) return fail(KDA_ERR_UNSUPPORTED, "rank = %d: only 128 is supported", a->rank);
     if (a->head_dim_k != 128)
         return fail(KDA_ERR_UNSUPPORTED, "head_dim_k = %d: only 128 is supported", a->head_dim_k);
     if (a->num_heads < 32 || a->num_heads > 128 || a->num_heads % 32)
         return fail(KDA_ERR_UNSUPPORTED, "num_heads = %d: 32, 64, 96 or 128", a->num_heads);
+    // (H * 128 gate channels: a multiple of the 1024 channels of an expansion workgroup)
     if (a->flags & ~(uint32_t)KDA_F_GATE_IS_LOG)
         return fail(KDA_ERR_UNSUPPORTED, "unsupported flags 0x%x", a->flags);
     if (!std::isfinite(a->gate_lower_bound) || !(a->gate_lower_bound < 0.f))

@@ -13,14 +13,17 @@
 //     beta = sigmoid(W_beta x)
 //
 // zproj_kernel: y = x [W_a; W_beta]^T, N = r + H columns, K = hidden.  A
-// workgroup owns 16 tokens and every column; its four waves take one quarter of
-// K each (both operands are K-contiguous rows, the order the 16x16x32 bf16 MFMA
-// reads, fetched from L2 three k-steps ahead) and add their partial tiles in LDS.
+// workgroup owns 32 tokens and every column; its eight waves take one column half
+// and one K quarter each (both operands are K-contiguous rows, the order the
+// 16x16x32 bf16 MFMA reads; a lane's two k-steps of a super-step read one whole
+// 128-byte line of a row, fetched a super-step ahead), and the K quarters add
+// their tiles through LDS in K order.
 // The sums leave as z (bf16, the workspace) and as the finished beta.
 //
-// gate_expand_kernel: per 64 tokens x 256 gate channels, z (from the workspace,
-// via LDS) times W_b (K = 128) with MFMA, the gate activation, the tile staged
-// in LDS and written as whole 512-byte rows.
+// gate_expand_kernel: per 64 tokens x 1024 gate channels (four tiles of 256),
+// z (from the workspace, via LDS) times W_b (K = 128) with MFMA, the gate
+// activation, each tile staged in LDS and written as whole 512-byte rows; the
+// next tile's weights load while a tile is written.
 #include <mutex>
 
 #include "kda_device.h"
@@ -31,7 +34,7 @@ namespace kda {
 namespace {
 
 constexpr int kRank = 128;   // r
-constexpr int kZT = 16;      // tokens per zproj workgroup
+constexpr int kZT = 32;      // tokens per zproj workgroup
 
 __device__ __forceinline__ bf16x8 ld8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
@@ -42,70 +45,102 @@ struct ZParams {
     int hid, H;
 };
 
-template <int NT>  // 16-column tiles: (r + H) / 16
-__global__ void __launch_bounds__(256) zproj_kernel(ZParams p) {
-    constexpr int N1 = 16 * NT;
-    constexpr int PF = 3;  // k-steps of fragments in flight ahead of the MFMAs
-    extern __shared__ __attribute__((aligned(16))) float red[];  // [4 waves][kZT][N1]
+template <int NT>  // 16-column tiles: (r + H) / 16, even
+__global__ void __launch_bounds__(512) zproj_kernel(ZParams p) {
+    constexpr int N1 = 16 * NT, NTW = NT / 2;  // columns, column tiles per wave
+    extern __shared__ __attribute__((aligned(16))) float red[];  // [3 K quarters][2 halves][kZT][N1 / 2]
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int m16 = lane & 15, k8 = (lane >> 4) * 8;
+    const int m16 = lane & 15, g = lane >> 4;
+    const int wn = wave & 1, wk = wave >> 1;  // column half, K quarter
     const int64_t t0 = (int64_t)blockIdx.x * kZT;
-    const int kq = p.hid / 4, kb = wave * kq;  // this wave's quarter of K
-    const int steps = kq / 32;
-    int64_t t = t0 + m16;
-    t = t < p.T ? t : p.T - 1;
-    const __bf16 *xr = p.x + t * p.hid + kb + k8;
-    const __bf16 *wr[NT];
+    const int kh = p.hid / 4, kb = wk * kh;
+    const int steps = kh / 64;  // super-steps of 64 K values: one 128-byte line per row
+    // In super-step u, k-step h (0, 1) lane group g covers K values
+    // kb + 64 u + 16 g + 8 h .. + 7 of both operands: the two k-steps of a row read
+    // one whole line, back to back.  (Any K order gives the same sums as long as
+    // both operands use it.)
+    const __bf16 *xr[2];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const int n = 16 * j + m16;
-        wr[j] = (n < kRank ? p.w_a + (size_t)n * p.hid : p.w_beta + (size_t)(n - kRank) * p.hid) + kb + k8;
+    for (int i = 0; i < 2; ++i) {
+        int64_t t = t0 + 16 * i + m16;
+        t = t < p.T ? t : p.T - 1;
+        xr[i] = p.x + t * p.hid + kb + 16 * g;
     }
-    f32x4 acc[NT];
+    const __bf16 *wr[NTW];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // a ring of PF k-steps of fragments: step s sits in slot s % PF
-    bf16x8 a[PF], b[PF][NT];
+    for (int j = 0; j < NTW; ++j) {
+        const int n = wn * 16 * NTW + 16 * j + m16;
+        wr[j] = (n < kRank ? p.w_a + (size_t)n * p.hid : p.w_beta + (size_t)(n - kRank) * p.hid) + kb + 16 * g;
+    }
+    f32x4 acc[2][NTW];
 #pragma unroll
-    for (int q = 0; q < PF; ++q)
-        if (q < steps) {
-            a[q] = ld8(xr + 32 * q);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) b[q][j] = ld8(wr[j] + 32 * q);
-        }
-    for (int s0 = 0; s0 < steps; s0 += PF) {
+        for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a[2][2], b[2][NTW];  // [k-step h][...]
+    auto load = [&](int u, bf16x8 (&la)[2][2], bf16x8 (&lb)[2][NTW]) {
 #pragma unroll
-        for (int q = 0; q < PF; ++q) {
-            const int st = s0 + q;
-            if (st < steps) {
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < NT; ++j) acc[j] = mma_k32(a[q], b[q][j], acc[j]);
-                if (st + PF < steps) {  // refill the slot just consumed
-                    a[q] = ld8(xr + 32 * (st + PF));
+            for (int h = 0; h < 2; ++h) la[h][i] = ld8(xr[i] + 64 * u + 8 * h);
 #pragma unroll
-                    for (int j = 0; j < NT; ++j) b[q][j] = ld8(wr[j] + 32 * (st + PF));
-                }
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) lb[h][j] = ld8(wr[j] + 64 * u + 8 * h);
+    };
+    load(0, a, b);
+    for (int u = 0; u < steps; ++u) {
+        bf16x8 an[2][2], bn[2][NTW];
+        if (u + 1 < steps) load(u + 1, an, bn);  // in flight during this super-step's MFMAs
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) acc[i][j] = mma_k32(a[h][i], b[h][j], acc[i][j]);
+        if (u + 1 < steps) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) a[h][i] = an[h][i];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) b[h][j] = bn[h][j];
             }
         }
     }
-    // partial tile of this wave into LDS (lane: rows 4 (lane / 16) + e, column m16)
-    float *mine = red + wave * kZT * N1;
+    // K quarters 1..3 hand their tiles to quarter 0 through LDS (lane: rows
+    // 4 g + e of each 16-row block, column m16)
+    constexpr int HW = N1 / 2, TILE = kZT * HW;
+    if (wk > 0) {
+        float *mine = red + ((wk - 1) * 2 + wn) * TILE;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < NT; ++j) mine[(4 * (lane >> 4) + e) * N1 + 16 * j + m16] = acc[j][e];
-    __syncthreads();
-    // the four quarters summed in K order; z rounded to bf16, beta through the sigmoid
-    for (int idx = tid; idx < kZT * N1; idx += 256) {
-        const int r = idx / N1, n = idx - r * N1;
-        const int64_t tt = t0 + r;
-        if (tt >= p.T) continue;
-        const float y = ((red[idx] + red[kZT * N1 + idx]) + red[2 * kZT * N1 + idx]) + red[3 * kZT * N1 + idx];
-        if (n < kRank)
-            p.z[tt * kRank + n] = (__bf16)y;
-        else
-            p.beta[tt * p.H + (n - kRank)] = (__bf16)sigmoidf_dev(y);
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) mine[(16 * i + 4 * g + e) * HW + 16 * j + m16] = acc[i][j][e];
     }
+    barrier_lds();
+    if (wk > 0) return;
+    const float *q1 = red + wn * TILE, *q2 = red + (2 + wn) * TILE, *q3 = red + (4 + wn) * TILE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * i + 4 * g + e;
+            const int64_t t = t0 + r;
+            if (t >= p.T) continue;
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int n = wn * HW + 16 * j + m16;
+                const int at = r * HW + 16 * j + m16;
+                const float y = ((acc[i][j][e] + q1[at]) + q2[at]) + q3[at];  // K order
+                if (n < kRank)
+                    p.z[t * kRank + n] = (__bf16)y;
+                else
+                    p.beta[t * p.H + (n - kRank)] = (__bf16)sigmoidf_dev(y);
+            }
+        }
 }
 
 struct EParams {
@@ -120,21 +155,26 @@ struct EParams {
 constexpr int kZS = kRank + 8;    // LDS row stride of z (bf16 elements)
 constexpr int kOS = 256 + 8;      // LDS row stride of the output tile
 
+constexpr int kCT = 4;  // 256-channel tiles per gate_expand workgroup
+
 __global__ void __launch_bounds__(256) gate_expand_kernel(EParams p) {
     __shared__ __attribute__((aligned(16))) __bf16 zs[64 * kZS];
     __shared__ __attribute__((aligned(16))) __bf16 os[64 * kOS];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int m16 = lane & 15, k8 = (lane >> 4) * 8;
     const int64_t t0 = (int64_t)blockIdx.x * 64;
-    const int c0 = blockIdx.y * 256;
-    // this wave's W_b fragments (64 channels c0 + 64 wave .., all of K = 128), in
-    // flight while z is staged
-    const __bf16 *wb = p.w_b + (size_t)(c0 + 64 * wave + m16) * kRank + k8;
+    const int cbase = blockIdx.y * (256 * kCT);
+    // this wave's W_b fragments for channel tile ct: channels cbase + 256 ct +
+    // 64 wave .., all of K = 128
     bf16x8 bw[kRank / 32][4];
+    auto load_w = [&](int ct) {
+        const __bf16 *wb = p.w_b + (size_t)(cbase + 256 * ct + 64 * wave + m16) * kRank + k8;
 #pragma unroll
-    for (int kk = 0; kk < kRank / 32; ++kk)
+        for (int kk = 0; kk < kRank / 32; ++kk)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bw[kk][j] = ld8(wb + (size_t)16 * j * kRank + 32 * kk);
+            for (int j = 0; j < 4; ++j) bw[kk][j] = ld8(wb + (size_t)16 * j * kRank + 32 * kk);
+    };
+    load_w(0);
     // z rows of the 64 tokens (the last one repeated past T): 16 pieces of 16 B per row
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -143,48 +183,52 @@ __global__ void __launch_bounds__(256) gate_expand_kernel(EParams p) {
         t = t < p.T ? t : p.T - 1;
         *reinterpret_cast<bf16x8 *>(zs + r * kZS + c) = ld8(p.z + t * kRank + c);
     }
-    __syncthreads();
-    // this wave: all 64 tokens x 64 channels c0 + 64 wave ..
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < kRank / 32; ++kk) {
-        bf16x8 a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = ld8(zs + (16 * i + m16) * kZS + 32 * kk + k8);
+    barrier_lds();  // LDS only: the weight loads stay in flight
+    for (int ct = 0; ct < kCT; ++ct) {
+        f32x4 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mma_k32(a[i], bw[kk][j], acc[i][j]);
-    }
-    // epilogue: the gate activation, then the tile transposed to rows in LDS
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int kk = 0; kk < kRank / 32; ++kk) {
+            bf16x8 a[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < 4; ++i) a[i] = ld8(zs + (16 * i + m16) * kZS + 32 * kk + k8);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v = p.glog ? p.lb * sigmoidf_dev(acc[i][j][e]) : acc[i][j][e];
-                os[(16 * i + 4 * (lane >> 4) + e) * kOS + 64 * wave + 16 * j + m16] = (__bf16)v;
-            }
-    __syncthreads();
-    // 64 rows of 512 bytes, 16 bytes per lane
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int piece = q * 256 + tid, r = piece >> 5, c = (piece & 31) * 8;
-        const int64_t t = t0 + r;
-        if (t < p.T)
-            *reinterpret_cast<bf16x8 *>(p.gate + t * p.hd + c0 + c) =
-                *reinterpret_cast<const bf16x8 *>(os + r * kOS + c);
+                for (int j = 0; j < 4; ++j) acc[i][j] = mma_k32(a[i], bw[kk][j], acc[i][j]);
+        }
+        if (ct + 1 < kCT) load_w(ct + 1);  // next tile's weights, in flight during the epilogue
+        // epilogue: the gate activation, then the tile transposed to rows in LDS
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = p.glog ? p.lb * sigmoidf_dev(acc[i][j][e]) : acc[i][j][e];
+                    os[(16 * i + 4 * (lane >> 4) + e) * kOS + 64 * wave + 16 * j + m16] = (__bf16)v;
+                }
+        barrier_lds();
+        // 64 rows of 512 bytes, 16 bytes per lane
+        const int c0 = cbase + 256 * ct;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int piece = q * 256 + tid, r = piece >> 5, c = (piece & 31) * 8;
+            const int64_t t = t0 + r;
+            if (t < p.T)
+                *reinterpret_cast<bf16x8 *>(p.gate + t * p.hd + c0 + c) =
+                    *reinterpret_cast<const bf16x8 *>(os + r * kOS + c);
+        }
+        barrier_lds();  // the next tile's epilogue rewrites os (stores stay in flight)
     }
 }
 
 template <int NT>
 static hipError_t launch_zproj(const ZParams &zp, hipStream_t s) {
-    constexpr int lds = 4 * kZT * 16 * NT * (int)sizeof(float);
+    constexpr int lds = 3 * kZT * 16 * NT * (int)sizeof(float);  // three K quarters' tiles
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
@@ -192,7 +236,7 @@ static hipError_t launch_zproj(const ZParams &zp, hipStream_t s) {
                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     });
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(zproj_kernel<NT>, dim3((unsigned)((zp.T + kZT - 1) / kZT)), dim3(256), lds, s, zp);
+    hipLaunchKernelGGL(zproj_kernel<NT>, dim3((unsigned)((zp.T + kZT - 1) / kZT)), dim3(512), lds, s, zp);
     return hipGetLastError();
 }
 
@@ -229,7 +273,7 @@ hipError_t launch_gate_proj(const kda_gate_beta_args *a, hipStream_t s) {
     ep.T = T; ep.hd = H * kHeadDim;
     ep.lb = a->gate_lower_bound;
     ep.glog = (a->flags & KDA_F_GATE_IS_LOG) ? 1 : 0;
-    const dim3 g2((unsigned)((T + 63) / 64), (unsigned)(ep.hd / 256));
+    const dim3 g2((unsigned)((T + 63) / 64), (unsigned)(ep.hd / (256 * kCT)));
     hipLaunchKernelGGL(gate_expand_kernel, g2, dim3(256), 0, s, ep);
     return hipGetLastError();
 }

@@ -357,7 +357,7 @@ kda_status kda_state_copy(const kda_state_copy_args *args, hipStream_t stream);
  */
 typedef struct {
     int64_t total_tokens;    /* T >= 0 */
-    int32_t hidden;          /* width of x: a positive multiple of 128 */
+    int32_t hidden;          /* width of x: a positive multiple of 256 */
     int32_t rank;            /* r: must be 128 */
     int32_t num_heads;       /* H: 32, 64, 96 or 128 */
     int32_t head_dim_k;      /* must be 128 */

@@ -314,6 +314,7 @@ def _gb_args(**kw):
 @pytest.mark.parametrize("field,value,status", [
     ("total_tokens", -1, K.KDA_ERR_INVALID_ARG),
     ("hidden", 200, K.KDA_ERR_UNSUPPORTED),
+    ("hidden", 384, K.KDA_ERR_UNSUPPORTED),  # a multiple of 128 but not of 256
     ("rank", 64, K.KDA_ERR_UNSUPPORTED),
     ("num_heads", 48, K.KDA_ERR_UNSUPPORTED),
     ("head_dim_k", 64, K.KDA_ERR_UNSUPPORTED),
