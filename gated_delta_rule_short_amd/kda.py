@@ -169,15 +169,24 @@ def _state_flag(state):
     raise TypeError("state must be float32 or bfloat16, got %s" % state.dtype)
 
 
-def _slots(state_slots, state, n, dev):
-    """(pointer, num_slots) of an optional int32 slot map into a pool whose first
-    dimension is its number of rows."""
+def _slots(state_slots, pools, n, dev):
+    """(pointer, num_slots) of an optional int32 slot map.  `pools` are the state and
+    conv-state tensors the map indexes: all of them must have the same number of
+    rows (their first dimension), which becomes num_slots.  Without a map, each
+    given pool must have one row per sequence."""
+    pools = [t for t in pools if torch.is_tensor(t)]
+    rows = {int(t.shape[0]) for t in pools}
     if state_slots is None:
+        if rows and rows != {n}:
+            raise ValueError("without state_slots, state and conv-state tensors need one row "
+                             "per sequence (%d)" % n)
         return None, 0
     _need(state_slots, "state_slots", torch.int32, dev)
     if state_slots.numel() != n:
         raise ValueError("state_slots must hold one slot per sequence")
-    return _ptr(state_slots), int(state.shape[0])
+    if len(rows) != 1:
+        raise ValueError("the state and conv-state pools must have the same number of rows")
+    return _ptr(state_slots), rows.pop()
 
 
 def _stream(stream, device):
@@ -256,6 +265,8 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
     N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else int(num_seqs or 1)
     if o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    if state_slots is not None and (state_out is True or conv_state_out is True):
+        raise ValueError("with state_slots, pass the pool tensors as state_out / conv_state_out")
     if state_out is True:
         sdt = state_in.dtype if state_in is not None else torch.float32
         state_out = torch.empty((N, H, dk, dv), dtype=sdt, device=dev)
@@ -287,12 +298,10 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
         conv_state_in=_ptr(conv_state_in), conv_state_out=_ptr(conv_state_out),
         state_in=_ptr(state_in), state_out=_ptr(state_out), o=_ptr(o),
         cu_seqlens=_ptr(cu_seqlens), cu_seqlens_host=_ptr(cuh), workspace=None, workspace_bytes=0)
-    if state_slots is not None:
-        pool = next((t for t in (state_in, state_out, conv_state_in, conv_state_out)
-                     if torch.is_tensor(t)), None)
-        if pool is None:
-            raise ValueError("state_slots needs a state or conv-state pool")
-        a.state_slots, a.num_slots = _slots(state_slots, pool, N, dev)
+    pools = (state_in, state_out, conv_state_in, conv_state_out)
+    if state_slots is not None and not any(torch.is_tensor(t) for t in pools):
+        raise ValueError("state_slots needs a state or conv-state pool")
+    a.state_slots, a.num_slots = _slots(state_slots, pools, N, dev)
     if workspace is True:
         need = lib.kda_prefill_workspace_size(ctypes.byref(a))
         workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
@@ -337,7 +346,7 @@ def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias
         q=_ptr(q), k=_ptr(k), v=_ptr(v), gate=_ptr(gate), beta=_ptr(beta),
         conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias), conv_state=_ptr(conv_state),
         state=_ptr(state), o=_ptr(o))
-    a.state_slots, a.num_slots = _slots(state_slots, state, N, dev)
+    a.state_slots, a.num_slots = _slots(state_slots, (state, conv_state), N, dev)
     _check(lib, lib.kda_decode(ctypes.byref(a), _stream(stream, dev)))
     return o
 
@@ -384,7 +393,7 @@ def kda_decode_multi(q, k, v, gate, beta, conv_weight, conv_state, state, *, upd
         state=_ptr(state), o=_ptr(o), updates=_ptr(updates),
         pending_updates=_ptr(pending_updates), pending_accepted=_ptr(pending_accepted),
         pending_tokens=pt)
-    a.state_slots, a.num_slots = _slots(state_slots, state, N, dev)
+    a.state_slots, a.num_slots = _slots(state_slots, (state, conv_state), N, dev)
     _check(lib, lib.kda_decode_multi(ctypes.byref(a), _stream(stream, dev)))
     return o, updates
 
@@ -410,7 +419,7 @@ def kda_decode_commit(updates, accepted, conv_state, state, *, state_slots=None,
                             num_tokens=T, dtype=_dtype_code(conv_state),
                             flags=_state_flag(state), accepted=_ptr(accepted),
                             updates=_ptr(updates), conv_state=_ptr(conv_state), state=_ptr(state))
-    a.state_slots, a.num_slots = _slots(state_slots, state, N, dev)
+    a.state_slots, a.num_slots = _slots(state_slots, (state, conv_state), N, dev)
     _check(lib, lib.kda_decode_commit(ctypes.byref(a), _stream(stream, dev)))
 
 

@@ -377,3 +377,28 @@ def test_prefill_rejects_workspace_overlapping_output(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         K.load_library(str(tmp_path / "missing.so"))
+
+
+def test_binding_checks_pool_rows_before_any_launch(lib):
+    """The binding rejects pools of different sizes, a missing pool, and an allocated
+    state_out with a slot map (the library would write past it); these fail before any
+    device call, on CPU tensors."""
+    import torch
+    dev = torch.device("cpu")
+    q = torch.zeros((4, 2, 128), dtype=torch.bfloat16)
+    beta = torch.zeros((4, 2), dtype=torch.bfloat16)
+    w = torch.zeros((3 * 2 * 128, 4))
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    slots = torch.zeros(1, dtype=torch.int32)
+    pool = torch.zeros((5, 2, 128, 128))
+    with pytest.raises(ValueError):
+        K.kda_prefill(q, q, q, q, beta, w, cu_seqlens=cu, state_in=pool, state_out=True,
+                      state_slots=slots)
+    with pytest.raises(ValueError):
+        K.kda_prefill(q, q, q, q, beta, w, cu_seqlens=cu, state_slots=slots)
+    cpool = torch.zeros((3, 3, 3 * 2 * 128), dtype=torch.bfloat16)
+    qd = torch.zeros((1, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        K.kda_decode(qd, qd, qd, qd, beta[:1], w, cpool, pool, state_slots=slots)
+    with pytest.raises(ValueError):  # no slot map: one row per sequence
+        K.kda_decode(qd, qd, qd, qd, beta[:1], w, cpool[:1], pool)
