@@ -393,8 +393,8 @@ kda_status kda_gate_beta_proj(const kda_gate_beta_args *a, hipStream_t stream) {
     if (a->rank != 128) return fail(KDA_ERR_UNSUPPORTED, "rank = %d: only 128 is supported", a->rank);
     if (a->head_dim_k != 128)
         return fail(KDA_ERR_UNSUPPORTED, "head_dim_k = %d: only 128 is supported", a->head_dim_k);
-    if (a->num_heads < 32 || a->num_heads > 128 || a->num_heads % 32)
-        return fail(KDA_ERR_UNSUPPORTED, "num_heads = %d: 32, 64, 96 or 128", a->num_heads);
+    if (a->num_heads != 64 && a->num_heads != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "num_heads = %d: 64 or 128", a->num_heads);
     // (H * 128 gate channels: a multiple of the 1024 channels of an expansion workgroup)
     if (a->flags & ~(uint32_t)KDA_F_GATE_IS_LOG)
         return fail(KDA_ERR_UNSUPPORTED, "unsupported flags 0x%x", a->flags);

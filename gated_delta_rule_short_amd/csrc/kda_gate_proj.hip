@@ -13,12 +13,13 @@
 //     beta = sigmoid(W_beta x)
 //
 // zproj_kernel: y = x [W_a; W_beta]^T, N = r + H columns, K = hidden.  A
-// workgroup owns 32 tokens and every column; its eight waves take one column half
-// and one K quarter each (both operands are K-contiguous rows, the order the
-// 16x16x32 bf16 MFMA reads; a lane's two k-steps of a super-step read one whole
-// 128-byte line of a row, fetched a super-step ahead), and the K quarters add
-// their tiles through LDS in K order.
-// The sums leave as z (bf16, the workspace) and as the finished beta.
+// workgroup owns 64 tokens, every column and one quarter of K.  Two producer
+// waves stream 64-wide K slabs of the token rows and the weight rows into a
+// three-slab LDS ring with LDS-DMA (whole 128-byte row segments); eight compute
+// waves, each 32 tokens x a quarter of the columns, read their MFMA fragments
+// from the ring.  Reading the weights once per 64 tokens, in whole lines, is
+// what bounds this product.  The quarters' fp32 partials go to the workspace and
+// zreduce_kernel sums them in K order into z (bf16) and the finished beta.
 //
 // gate_expand_kernel: per 64 tokens x 1024 gate channels (four tiles of 256),
 // z (from the workspace, via LDS) times W_b (K = 128) with MFMA, the gate
@@ -34,113 +35,147 @@ namespace kda {
 namespace {
 
 constexpr int kRank = 128;   // r
-constexpr int kZT = 32;      // tokens per zproj workgroup
+constexpr int kSplit = 4;    // K ranges of the first product (one per workgroup)
+constexpr int kMT = 64;      // tokens per zproj workgroup
+constexpr int kSlabK = 64;   // K values per LDS slab: one 128-byte row segment
+constexpr int kRing = 3;     // slabs in the ring (two in flight ahead of the MFMAs)
 
 __device__ __forceinline__ bf16x8 ld8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
 struct ZParams {
     const __bf16 *x, *w_a, *w_beta;
-    __bf16 *z, *beta;  // z [T][r] (workspace), beta [T][H]
+    float *part;  // [kSplit][T][N1] fp32 partial products (workspace)
     int64_t T;
     int hid, H;
 };
 
-template <int NT>  // 16-column tiles: (r + H) / 16, even
-__global__ void __launch_bounds__(512) zproj_kernel(ZParams p) {
-    constexpr int N1 = 16 * NT, NTW = NT / 2;  // columns, column tiles per wave
-    extern __shared__ __attribute__((aligned(16))) float red[];  // [3 K quarters][2 halves][kZT][N1 / 2]
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+// Slab rows: kMT token rows, then the N1 weight rows (W_a, then W_beta), 128 bytes
+// each.  16-byte chunk c of row r sits at chunk c ^ (r & 7) of its LDS row, so the
+// 16 rows one fragment read touches fall in different banks.
+template <int NT>
+struct ZGeom {
+    static constexpr int N1 = 16 * NT, ROWS = kMT + N1;
+    static constexpr int SLAB = ROWS * 128;           // bytes
+    static constexpr int INST = SLAB / 1024;          // 1 KiB DMA instructions per slab
+    static constexpr int LDS = kRing * SLAB;
+    static constexpr int PW = 2;                      // producer waves
+    static_assert(SLAB % 1024 == 0 && INST % PW == 0, "whole DMA instructions per producer");
+    static_assert(INST / PW * (kRing - 1) < 64, "vmcnt range");
+};
+
+template <int NT>
+__device__ __forceinline__ void zproj_issue(unsigned char *slot, const ZParams &p, int64_t t0, int k0,
+                                            int pw, int lane) {
+    typedef ZGeom<NT> G;
+#pragma unroll
+    for (int i = pw; i < G::INST; i += G::PW) {
+        const int row = 8 * i + (lane >> 3), gc = (lane & 7) ^ (row & 7);
+        const __bf16 *src;
+        if (row < kMT) {
+            int64_t t = t0 + row;
+            t = t < p.T ? t : p.T - 1;
+            src = p.x + t * p.hid;
+        } else {
+            const int n = row - kMT;
+            src = n < kRank ? p.w_a + (size_t)n * p.hid : p.w_beta + (size_t)(n - kRank) * p.hid;
+        }
+        __builtin_amdgcn_global_load_lds(src + k0 + 8 * gc, (lds_void *)(slot + i * 1024), 16, 0, 0);
+    }
+}
+
+template <int NT>
+__global__ void __launch_bounds__(640) zproj_kernel(ZParams p) {
+    typedef ZGeom<NT> G;
+    constexpr int N1 = G::N1, PER = G::INST / G::PW;
+    extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t t0 = (int64_t)blockIdx.x * kMT;
+    const int kq = p.hid / kSplit, kb = blockIdx.y * kq;
+    const int nsl = kq / kSlabK;
+
+    if (wave >= 8) {
+        // producers: slab s + 2 goes into the slot slab s - 1 used, once every
+        // compute wave has passed barrier B_s (and so finished slab s - 1); bare
+        // barriers, since a fence would drain the DMA in flight
+        const int pw = wave - 8;
+        zproj_issue<NT>(ring, p, t0, kb, pw, lane);
+        if (nsl > 1) zproj_issue<NT>(ring + G::SLAB, p, t0, kb + kSlabK, pw, lane);
+        for (int s = 0; s < nsl; ++s) {
+            if (s + 1 < nsl) wait_vmcnt<PER>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();  // B_s: slab s in LDS
+            if (s + 2 < nsl)
+                zproj_issue<NT>(ring + ((s + 2) % kRing) * G::SLAB, p, t0, kb + (s + 2) * kSlabK, pw, lane);
+        }
+        return;
+    }
+
+    // compute wave: 32 tokens (half mh) x 16 NT / 4 columns (quarter nq)
+    constexpr int NJ = NT / 4;
+    static_assert(NT % 4 == 0, "column quarters of whole 16-column tiles");
+    const int mh = wave & 1, nq = wave >> 1;
     const int m16 = lane & 15, g = lane >> 4;
-    const int wn = wave & 1, wk = wave >> 1;  // column half, K quarter
-    const int64_t t0 = (int64_t)blockIdx.x * kZT;
-    const int kh = p.hid / 4, kb = wk * kh;
-    const int steps = kh / 64;  // super-steps of 64 K values: one 128-byte line per row
-    // In super-step u, k-step h (0, 1) lane group g covers K values
-    // kb + 64 u + 16 g + 8 h .. + 7 of both operands: the two k-steps of a row read
-    // one whole line, back to back.  (Any K order gives the same sums as long as
-    // both operands use it.)
-    const __bf16 *xr[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        int64_t t = t0 + 16 * i + m16;
-        t = t < p.T ? t : p.T - 1;
-        xr[i] = p.x + t * p.hid + kb + 16 * g;
-    }
-    const __bf16 *wr[NTW];
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-        const int n = wn * 16 * NTW + 16 * j + m16;
-        wr[j] = (n < kRank ? p.w_a + (size_t)n * p.hid : p.w_beta + (size_t)(n - kRank) * p.hid) + kb + 16 * g;
-    }
-    f32x4 acc[2][NTW];
+    f32x4 acc[2][NJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 a[2][2], b[2][NTW];  // [k-step h][...]
-    auto load = [&](int u, bf16x8 (&la)[2][2], bf16x8 (&lb)[2][NTW]) {
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int arow[2], brow[NJ];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) arow[i] = 32 * mh + 16 * i + m16;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) la[h][i] = ld8(xr[i] + 64 * u + 8 * h);
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) lb[h][j] = ld8(wr[j] + 64 * u + 8 * h);
+    for (int j = 0; j < NJ; ++j) brow[j] = kMT + 16 * NJ * nq + 16 * j + m16;
+    auto frag = [&](const unsigned char *slot, int row, int chunk) {
+        return *reinterpret_cast<const bf16x8 *>(slot + row * 128 + ((chunk ^ (row & 7)) << 4));
     };
-    load(0, a, b);
-    for (int u = 0; u < steps; ++u) {
-        bf16x8 an[2][2], bn[2][NTW];
-        if (u + 1 < steps) load(u + 1, an, bn);  // in flight during this super-step's MFMAs
+    for (int s = 0; s < nsl; ++s) {
+        // B_s, with LDS fences: no fragment read moves across it (these waves have
+        // no DMA of their own in flight, so the fences wait for nothing else)
+        barrier_lds();
+        const unsigned char *slot = ring + (s % kRing) * G::SLAB;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {  // the slab's two k-steps of 32
+            bf16x8 a[2], b[NJ];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = frag(slot, arow[i], 4 * h + g);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) b[j] = frag(slot, brow[j], 4 * h + g);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) acc[i][j] = mma_k32(a[h][i], b[h][j], acc[i][j]);
-        if (u + 1 < steps) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) a[h][i] = an[h][i];
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) b[h][j] = bn[h][j];
-            }
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mma_k32(a[i], b[j], acc[i][j]);
         }
     }
-    // K quarters 1..3 hand their tiles to quarter 0 through LDS (lane: rows
-    // 4 g + e of each 16-row block, column m16)
-    constexpr int HW = N1 / 2, TILE = kZT * HW;
-    if (wk > 0) {
-        float *mine = red + ((wk - 1) * 2 + wn) * TILE;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) mine[(16 * i + 4 * g + e) * HW + 16 * j + m16] = acc[i][j][e];
-    }
-    barrier_lds();
-    if (wk > 0) return;
-    const float *q1 = red + wn * TILE, *q2 = red + (2 + wn) * TILE, *q3 = red + (4 + wn) * TILE;
+    // this K range's partial products (lane: rows 4 g + e of each 16-row block, column m16)
+    float *part = p.part + (size_t)blockIdx.y * p.T * N1;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = 16 * i + 4 * g + e;
-            const int64_t t = t0 + r;
-            if (t >= p.T) continue;
+            const int64_t t = t0 + 32 * mh + 16 * i + 4 * g + e;
+            if (t < p.T) {
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int n = wn * HW + 16 * j + m16;
-                const int at = r * HW + 16 * j + m16;
-                const float y = ((acc[i][j][e] + q1[at]) + q2[at]) + q3[at];  // K order
-                if (n < kRank)
-                    p.z[t * kRank + n] = (__bf16)y;
-                else
-                    p.beta[t * p.H + (n - kRank)] = (__bf16)sigmoidf_dev(y);
+                for (int j = 0; j < NJ; ++j) part[t * N1 + 16 * NJ * nq + 16 * j + m16] = acc[i][j][e];
             }
         }
+}
+
+// The kSplit partials summed in K order: z (bf16) and beta = sigmoid.
+__global__ void __launch_bounds__(256) zreduce_kernel(const float *part, __bf16 *z, __bf16 *beta,
+                                                      int64_t T, int H) {
+    const int N1 = kRank + H;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= T * N1) return;
+    const int64_t t = idx / N1;
+    const int n = (int)(idx - t * N1);
+    const size_t sz = (size_t)T * N1;
+    float y = part[idx];
+#pragma unroll
+    for (int q = 1; q < kSplit; ++q) y += part[q * sz + idx];
+    if (n < kRank)
+        z[t * kRank + n] = (__bf16)y;
+    else
+        beta[t * H + (n - kRank)] = (__bf16)sigmoidf_dev(y);
 }
 
 struct EParams {
@@ -228,46 +263,50 @@ __global__ void __launch_bounds__(256) gate_expand_kernel(EParams p) {
 
 template <int NT>
 static hipError_t launch_zproj(const ZParams &zp, hipStream_t s) {
-    constexpr int lds = 3 * kZT * 16 * NT * (int)sizeof(float);  // three K quarters' tiles
+    typedef ZGeom<NT> G;
+    static_assert(G::LDS <= 160 * 1024, "LDS budget");
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
         attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&zproj_kernel<NT>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     });
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(zproj_kernel<NT>, dim3((unsigned)((zp.T + kZT - 1) / kZT)), dim3(512), lds, s, zp);
+    const dim3 grid((unsigned)((zp.T + kMT - 1) / kMT), kSplit);
+    hipLaunchKernelGGL(zproj_kernel<NT>, grid, dim3(640), G::LDS, s, zp);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t gate_proj_workspace_bytes(int64_t T, int H) {
-    (void)H;
-    return (size_t)T * kRank * sizeof(__bf16);  // z
+    // fp32 partials of the first product, then z (bf16)
+    return (size_t)kSplit * (size_t)T * (size_t)(kRank + H) * sizeof(float) + (size_t)T * kRank * sizeof(__bf16);
 }
 
 hipError_t launch_gate_proj(const kda_gate_beta_args *a, hipStream_t s) {
     const int64_t T = a->total_tokens;
     if (T == 0) return hipSuccess;
-    const int H = a->num_heads;
+    const int H = a->num_heads, N1 = kRank + H;
     ZParams zp;
     zp.x = static_cast<const __bf16 *>(a->x);
     zp.w_a = static_cast<const __bf16 *>(a->w_a);
     zp.w_beta = static_cast<const __bf16 *>(a->w_beta);
-    zp.z = static_cast<__bf16 *>(a->workspace);
-    zp.beta = static_cast<__bf16 *>(a->beta);
+    zp.part = static_cast<float *>(a->workspace);
     zp.T = T; zp.hid = a->hidden; zp.H = H;
+    __bf16 *z = reinterpret_cast<__bf16 *>(zp.part + (size_t)kSplit * T * N1);
     hipError_t e;
-    switch ((kRank + H) / 16) {
-        case 10: e = launch_zproj<10>(zp, s); break;
+    switch (N1 / 16) {
         case 12: e = launch_zproj<12>(zp, s); break;
-        case 14: e = launch_zproj<14>(zp, s); break;
         default: e = launch_zproj<16>(zp, s); break;
     }
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(zreduce_kernel, dim3((unsigned)((T * N1 + 255) / 256)), dim3(256), 0, s, zp.part, z,
+                       static_cast<__bf16 *>(a->beta), T, H);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     EParams ep;
-    ep.z = zp.z;
+    ep.z = z;
     ep.w_b = static_cast<const __bf16 *>(a->w_b);
     ep.gate = static_cast<__bf16 *>(a->gate);
     ep.T = T; ep.hd = H * kHeadDim;

@@ -359,7 +359,7 @@ typedef struct {
     int64_t total_tokens;    /* T >= 0 */
     int32_t hidden;          /* width of x: a positive multiple of 256 */
     int32_t rank;            /* r: must be 128 */
-    int32_t num_heads;       /* H: 32, 64, 96 or 128 */
+    int32_t num_heads;       /* H: 64 or 128 */
     int32_t head_dim_k;      /* must be 128 */
     uint32_t flags;          /* 0 or KDA_F_GATE_IS_LOG */
     float gate_lower_bound;  /* lb < 0 */
@@ -375,7 +375,8 @@ typedef struct {
 
 kda_status kda_gate_beta_proj(const kda_gate_beta_args *args, hipStream_t stream);
 
-/* Workspace bytes kda_gate_beta_proj needs (2 * T * r: z between the two products). */
+/* Workspace bytes kda_gate_beta_proj needs: 16 T (r + H) for the split first
+ * product's fp32 partials, then 2 T r for z. */
 size_t kda_gate_beta_workspace_size(const kda_gate_beta_args *args);
 
 #ifdef __cplusplus

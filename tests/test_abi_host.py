@@ -305,7 +305,7 @@ def _gb_args(**kw):
                           flags=0, gate_lower_bound=-5.0)
     for i, f in enumerate(("x", "w_a", "w_b", "w_beta", "gate", "beta", "workspace")):
         setattr(a, f, ctypes.c_void_p(0x100000 + i * 0x1000000))
-    a.workspace_bytes = 2 * 64 * 128
+    a.workspace_bytes = 16 * 64 * (128 + 64) + 2 * 64 * 128
     for key, val in kw.items():
         setattr(a, key, val)
     return a
@@ -317,6 +317,7 @@ def _gb_args(**kw):
     ("hidden", 384, K.KDA_ERR_UNSUPPORTED),  # a multiple of 128 but not of 256
     ("rank", 64, K.KDA_ERR_UNSUPPORTED),
     ("num_heads", 48, K.KDA_ERR_UNSUPPORTED),
+    ("num_heads", 96, K.KDA_ERR_UNSUPPORTED),
     ("head_dim_k", 64, K.KDA_ERR_UNSUPPORTED),
     ("flags", K.KDA_F_SILU, K.KDA_ERR_UNSUPPORTED),
     ("gate_lower_bound", 0.5, K.KDA_ERR_INVALID_ARG),
@@ -336,7 +337,7 @@ def test_gate_beta_rejects_overlaps_and_sizes_workspace(lib):
     a = _gb_args()
     a.beta = ctypes.c_void_p(a.workspace + 16)
     assert lib.kda_gate_beta_proj(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
-    assert lib.kda_gate_beta_workspace_size(ctypes.byref(_gb_args())) == 2 * 64 * 128
+    assert lib.kda_gate_beta_workspace_size(ctypes.byref(_gb_args())) == 16 * 64 * (128 + 64) + 2 * 64 * 128
     assert lib.kda_gate_beta_proj(ctypes.byref(_gb_args(total_tokens=0)), None) == K.KDA_OK
 
 

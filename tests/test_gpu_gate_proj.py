@@ -31,8 +31,8 @@ def _per_head_rel(x, ref):
     return d / np.maximum(r, 1e-30)
 
 
-@pytest.mark.parametrize("T,hidden,H", [(1, 256, 32), (100, 512, 64), (333, 1024, 128),
-                                        (70, 768, 96)])
+@pytest.mark.parametrize("T,hidden,H", [(1, 256, 64), (100, 512, 64), (333, 1024, 128),
+                                        (70, 768, 128), (129, 4096, 64)])
 @pytest.mark.parametrize("log", [False, True])
 def test_gate_beta_proj_matches_oracle(T, hidden, H, log):
     d = KI.make_gate_proj(T, hidden=hidden, H=H, seed=110 + T, device=DEV)
