@@ -71,3 +71,54 @@ def test_planted_mistake_is_caught(mutant, tmp_path, monkeypatch):
 
 def test_unmutated_oracle_passes_the_same_pins():
     assert _run_pins() == []
+
+
+# --------------------------------------------- the projection oracle (Python)
+
+PROJ_MUTANTS = {
+    "gate_sigmoid_sign_flipped": ("gate_lower_bound * sig(a)", "gate_lower_bound * sig(-a)"),
+    "gate_bound_dropped": ("gate_lower_bound * sig(a)", "sig(a)"),
+    "beta_without_sigmoid": ("beta = sig(x @ w_beta.T)", "beta = x @ w_beta.T"),
+    "head_and_channel_swapped": ('gate.reshape(T, num_heads, -1)',
+                                 'gate.reshape(T, -1, num_heads).transpose(0, 2, 1)'),
+    "second_factor_dropped": ("a = z @ w_b.T", "a = z @ np.eye(z.shape[1], w_b.shape[0])"),
+}
+
+PROJ_PINS = ["test_gate_proj_zero_weights_give_sigmoid_midpoints",
+             "test_gate_proj_brute_force_scalar_loops",
+             "test_gate_proj_selection_weights_closed_form",
+             "test_gate_proj_beta_sign_symmetry"]
+
+
+@pytest.mark.parametrize("mutant", sorted(PROJ_MUTANTS))
+def test_planted_projection_mistake_is_caught(mutant, monkeypatch):
+    import inspect
+    import textwrap
+    import numpy as np
+    from tests import test_oracle_pins as P
+    old, new = PROJ_MUTANTS[mutant]
+    src = textwrap.dedent(inspect.getsource(oracle.gate_beta_proj))
+    assert src.count(old) == 1, "mutation anchor missing: " + old
+    ns = {"np": np, "_f64": oracle._f64}
+    exec(src.replace(old, new), ns)
+    monkeypatch.setattr(oracle, "gate_beta_proj", ns["gate_beta_proj"])
+    caught = []
+    for name in PROJ_PINS:
+        try:
+            getattr(P, name)()
+        except (AssertionError, ValueError):
+            caught.append(name)
+    assert caught, "no pin catches " + mutant
+
+
+def test_projection_harness_control(monkeypatch):
+    """The same path with the source unchanged: every pin passes."""
+    import inspect
+    import textwrap
+    import numpy as np
+    from tests import test_oracle_pins as P
+    ns = {"np": np, "_f64": oracle._f64}
+    exec(textwrap.dedent(inspect.getsource(oracle.gate_beta_proj)), ns)
+    monkeypatch.setattr(oracle, "gate_beta_proj", ns["gate_beta_proj"])
+    for name in PROJ_PINS:
+        getattr(P, name)()
