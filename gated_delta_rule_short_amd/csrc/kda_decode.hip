@@ -167,17 +167,6 @@ __device__ __forceinline__ void store_state(const f32x4 (&st)[16], SB *S, int ti
 
 __device__ __forceinline__ int clamp_count(int a, int hi) { return a < 0 ? 0 : (a > hi ? hi : a); }
 
-// Copies rows 0..2 (alpha, k, u) of `count` records into LDS dst[t][3][128].
-__device__ __forceinline__ void stage_records(float (*dst)[3][D], const float *rec, int count,
-                                              int tid) {
-    constexpr int per = 3 * D / 4;  // float4 per record
-    for (int i = tid; i < count * per; i += 256) {
-        const int t = i / per, c = i - t * per;
-        reinterpret_cast<f32x4 *>(&dst[t][0][0])[c] =
-            reinterpret_cast<const f32x4 *>(rec + (size_t)t * kRec)[c];
-    }
-}
-
 // Conv window of one channel after a commit of `count` tokens: the last three
 // raw tokens of (cache ++ the records' row `row`, tokens 0..count-1).  c0..c2:
 // the cache as stored (oldest first); rec: the sequence-head's first record.
@@ -505,19 +494,49 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
     f32x4 st[16];
     load_state(st, S, tid);
     const float *rec = p.rec + (size_t)pr * p.T * kRec;
-    stage_records(s_pend, rec, na, tid);
-
+    // every load below is issued before any is used: the records' alpha, k and u
+    // rows (at most three float4 per thread), then this thread's conv channels
+    // (i = tid and tid + 256 of the head's 3 x 128: their cached taps and the raw
+    // rows of the last three accepted tokens)
+    constexpr int per = 3 * D / 4;
+    f32x4 pv[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int i = tid + 256 * j, t = i / per;
+        if (i < na * per) pv[j] = reinterpret_cast<const f32x4 *>(rec + (size_t)t * kRec)[i - t * per];
+    }
     const int CC = 3 * H * D;
     T *cs = reinterpret_cast<T *>(p.cs) + (size_t)slot * 3 * CC;
-    for (int i = tid; i < 3 * D; i += 256) {
-        const int part = i / D, c = i - part * D;  // 0 q, 1 k, 2 v
-        const int ch = part * H * D + h * D + c;
-        float h0, h1, h2;
-        committed_window(to_f32(cs[ch]), to_f32(cs[CC + ch]), to_f32(cs[2 * CC + ch]), rec,
-                         3 + part, c, na, h0, h1, h2);
-        cs[ch] = from_f32<T>(h0);
-        cs[CC + ch] = from_f32<T>(h1);
-        cs[2 * CC + ch] = from_f32<T>(h2);
+    T cr[2][3];
+    float hw[2][3];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = tid + 256 * q;
+        if (i < 3 * D) {
+            const int part = i / D, c = i - part * D;  // 0 q, 1 k, 2 v
+            const int ch = part * H * D + h * D + c;
+            cr[q][0] = cs[ch];
+            cr[q][1] = cs[CC + ch];
+            cr[q][2] = cs[2 * CC + ch];
+            committed_window(to_f32(cr[q][0]), to_f32(cr[q][1]), to_f32(cr[q][2]), rec, 3 + part, c,
+                             na, hw[q][0], hw[q][1], hw[q][2]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int i = tid + 256 * j, t = i / per;
+        if (i < na * per) reinterpret_cast<f32x4 *>(&s_pend[t][0][0])[i - t * per] = pv[j];
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = tid + 256 * q;
+        if (i < 3 * D) {
+            const int part = i / D, c = i - part * D;
+            const int ch = part * H * D + h * D + c;
+            cs[ch] = from_f32<T>(hw[q][0]);
+            cs[CC + ch] = from_f32<T>(hw[q][1]);
+            cs[2 * CC + ch] = from_f32<T>(hw[q][2]);
+        }
     }
     barrier_lds();
     for (int t = 0; t < na; ++t)
