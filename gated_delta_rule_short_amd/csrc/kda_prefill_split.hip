@@ -185,15 +185,18 @@ __device__ __forceinline__ void load_conv_w(const SplitParams &p, int h, int lan
 // then small and non-negative).  Each lane reads its two channels (4 bytes at
 // 4 * lane) of a row at a wave-uniform row offset, so no per-lane address
 // arithmetic is needed.
+// Sequence-relative rows are 32-bit (the token count is below 2^31), so the
+// clamps are scalar compares rather than 64-bit vector ones.
 struct RowWindow {
-    int64_t lo, hi, p0;  // first and last row used (sequence-relative), and p0
+    int lo, hi, p0, L;  // first and last row used (sequence-relative), p0, length
 };
 __device__ __forceinline__ RowWindow row_window(const SubTask &tk, int first) {
     RowWindow w;
-    w.p0 = 16 * tk.j;
-    int64_t lo = w.p0 + first, hi = w.p0 + 15;
-    lo = lo < 0 ? 0 : (lo >= tk.L ? tk.L - 1 : lo);
-    hi = hi >= tk.L ? tk.L - 1 : hi;
+    w.p0 = 16 * (int)tk.j;
+    w.L = (int)tk.L;
+    int lo = w.p0 + first, hi = w.p0 + 15;
+    lo = lo < 0 ? 0 : (lo >= w.L ? w.L - 1 : lo);
+    hi = hi >= w.L ? w.L - 1 : hi;
     w.lo = lo;
     w.hi = hi;
     return w;
@@ -206,10 +209,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *x, const 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(b), 0, (int)((w.hi - w.lo + 1) * rowbytes), 0x00020000);
 }
 // Byte offset of sub-chunk row r (-3 .. 15), clamped into the sequence, in the window.
-__device__ __forceinline__ int row_soff(const SubTask &tk, const RowWindow &w, int r, int64_t rowbytes) {
-    int64_t sp = w.p0 + r;
-    sp = sp < 0 ? 0 : (sp >= tk.L ? tk.L - 1 : sp);
-    return (int)((sp - w.lo) * rowbytes);
+__device__ __forceinline__ int row_soff(const RowWindow &w, int r, int rowbytes) {
+    int sp = w.p0 + r;
+    sp = sp < 0 ? 0 : (sp >= w.L ? w.L - 1 : sp);
+    return (sp - w.lo) * rowbytes;
 }
 
 // The three rows before a sequence for tensor t (0 q, 1 k, 2 v): conv state or zeros.
@@ -235,14 +238,14 @@ __device__ __forceinline__ void load_early(const SplitParams &p, const SubTask &
     const __amdgpu_buffer_rsrc_t rk = row_rsrc(p.k, tk, h, wk, rowbytes);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)
-        r.xa[rr] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * lane, row_soff(tk, wa, rr, rowbytes), 0);
+        r.xa[rr] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * lane, row_soff(wa, rr, rowbytes), 0);
 #pragma unroll
     for (int i = 0; i < 19; ++i)
-        r.xk[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, row_soff(tk, wk, i - 3, rowbytes), 0);
+        r.xk[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, row_soff(wk, i - 3, rowbytes), 0);
     // unconditional load from a row inside the sequence; the conversion and the
     // mask wait for the use, so this load does not force a wait on the others
-    int64_t br = 16 * tk.j + (lane & 15);
-    br = br < tk.L ? br : tk.L - 1;
+    int br = 16 * (int)tk.j + (lane & 15);
+    br = br < (int)tk.L ? br : (int)tk.L - 1;
     r.beta_bits = *reinterpret_cast<const unsigned short *>(reinterpret_cast<const T *>(p.beta) + (tk.s0 + br) * p.H + h);
     if (tk.j == 0) load_history(p, tk, h, lane, 1, r.xk);
 }
@@ -255,7 +258,7 @@ __device__ __forceinline__ void load_late(const SplitParams &p, const SubTask &t
     const __amdgpu_buffer_rsrc_t rv = row_rsrc(p.v, tk, h, wr, rowbytes);
 #pragma unroll
     for (int i = 0; i < 19; ++i) {
-        const int so = row_soff(tk, wr, i - 3, rowbytes);
+        const int so = row_soff(wr, i - 3, rowbytes);
         r.xq[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, so, 0);
         r.xv[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, 4 * lane, so, 0);
     }
@@ -277,7 +280,8 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     const int m16 = lane & 15, g4 = lane >> 4;
     const int64_t s0 = tk.s0, L = tk.L, j = tk.j;
     const int64_t p0 = 16 * j;
-    const bool edge = p0 < 3 || p0 + 16 > L;
+    const int rem = (int)(L - p0);  // rows of the sequence from p0 on (32-bit: scalar compares)
+    const bool edge = p0 < 3 || rem < 16;
     const bool silu = p.flags & KDA_F_SILU;
     const bool l2 = !(p.flags & KDA_F_NO_QK_L2NORM);
     const bool glog = p.flags & KDA_F_GATE_IS_LOG;
@@ -293,7 +297,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     const uint32_t(&xk)[19] = er.xk;
     const uint32_t(&xv)[19] = lr.xv;
     const uint32_t(&xa)[16] = er.xa;
-    const float beta_r = (lane < 16 && p0 + lane < L) ? __uint_as_float(er.beta_bits << 16) : 0.f;
+    const float beta_r = (lane < 16 && lane < rem) ? __uint_as_float(er.beta_bits << 16) : 0.f;
     auto load_w = [&](int t, float (&wt)[2][4], float (&bs)[2]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -313,7 +317,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         if (edge) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr)
-                if (p0 + rr >= L) { y[rr][0] = 0.f; y[rr][1] = 0.f; }
+                if (rr >= rem) { y[rr][0] = 0.f; y[rr][1] = 0.f; }
         }
     };
     float bt[16];  // beta per row, wave-uniform
@@ -340,7 +344,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     if (edge) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
-            if (p0 + rr >= L) g2v[0][rr] = g2v[1][rr] = 0.f;
+            if (rr >= rem) g2v[0][rr] = g2v[1][rr] = 0.f;
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
