@@ -160,6 +160,8 @@ kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
                                  a->flags, a->scale, a->gate_lower_bound);
     if (st != KDA_OK) return st;
     if (a->total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens < 0");
+    // token positions inside a sequence are 32-bit in the kernels (cu_seqlens is int32)
+    if (a->total_tokens > ((int64_t)1 << 31) - 64) return fail(KDA_ERR_INVALID_ARG, "total_tokens too large");
     int chunk = a->chunk_size;
     if (chunk == 0) chunk = a->dtype == KDA_BF16 ? 64 : 32;
     if (chunk != 16 && chunk != 32 && chunk != 64)

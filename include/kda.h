@@ -148,7 +148,7 @@ typedef struct {
     int32_t head_dim_v;      /* must be 128 */
     int32_t chunk_size;      /* 0 = default (64 for bf16, 32 for fp32); 16, 32 or 64
                                 (fp32 I/O: 16 or 32) */
-    int64_t total_tokens;    /* T >= 0 */
+    int64_t total_tokens;    /* 0 <= T <= 2^31 - 64 (token offsets are int32) */
     kda_dtype dtype;
     uint32_t flags;          /* KDA_F_* */
     float scale;             /* 0 = 1/sqrt(dk) */

@@ -93,6 +93,7 @@ def _prefill_args(**kw):
     ("gate_lower_bound", float("nan"), K.KDA_ERR_INVALID_ARG),
     ("scale", -1.0, K.KDA_ERR_INVALID_ARG),
     ("total_tokens", -1, K.KDA_ERR_INVALID_ARG),
+    ("total_tokens", 1 << 31, K.KDA_ERR_INVALID_ARG),
     ("q", None, K.KDA_ERR_INVALID_ARG),
     ("conv_weight", None, K.KDA_ERR_INVALID_ARG),
 ])
