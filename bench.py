@@ -83,8 +83,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py: the KDA mixer is built and measured on one GPU; --gpus %d is not "
-              "supported (sharding over heads, sequences or dv columns is described in "
-              "DESIGN.md but not built)" % args.gpus, file=sys.stderr)
+              "supported (the path would shard over heads, sequences or dv columns; only the "
+              "one-GPU path is built)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
