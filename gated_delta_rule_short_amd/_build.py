@@ -24,6 +24,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.hip", "kda_conv.hip", "kda_decode.hip", "kda_gate_proj.hip", "kda_pool.hip",
            "kda_prefill.hip", "kda_prefill_split.hip"]
+# measurement-only streaming kernels (include/kda_calib.h), a library of their own
+CALIB_LIB = os.path.join(PKG, "libkda_calib.so")
+CALIB_SOURCES = ["kda_calib.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 
@@ -58,17 +61,23 @@ def _compile(src):
     return obj, err
 
 
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for obj, err in results:
+    srcs = SOURCES + CALIB_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        results = dict(zip(srcs, ex.map(_compile, srcs)))
+    for obj, err in results.values():
         if verbose and err.strip():
             print(err)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    _link([results[s][0] for s in SOURCES], LIB)
+    _link([results[s][0] for s in CALIB_SOURCES], CALIB_LIB)
     return LIB
 
 

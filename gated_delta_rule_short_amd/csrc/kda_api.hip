@@ -80,18 +80,57 @@ kda_status pool_rows(const int32_t *slots, int32_t num_slots, int32_t num_seqs, 
     return KDA_OK;
 }
 
-int env_int(const char *name, int dflt) {
-    const char *v = std::getenv(name);
-    return v && *v ? std::atoi(v) : dflt;
+// A call's buffers as (pointer, bytes, name); the first `n_written` are written
+// by the call.  Every written buffer must overlap no other buffer of the call.
+// NULL or empty buffers overlap nothing; an allowed in-place pair is passed with
+// the input side's size set to 0.
+struct Buf {
+    const void *p;
+    size_t bytes;
+    const char *name;
+};
+kda_status check_written(const Buf *b, int n, int n_written) {
+    for (int i = 0; i < n_written; ++i)
+        for (int j = 0; j < n; ++j) {
+            if (j == i || (j < n_written && j < i)) continue;
+            if (overlap(b[i].p, b[i].bytes, b[j].p, b[j].bytes))
+                return fail(KDA_ERR_INVALID_ARG, "%s overlaps %s", b[i].name, b[j].name);
+        }
+    return KDA_OK;
 }
 
 }  // namespace
+
+namespace kda {
+
+// Launch log: one line per kernel launch on stderr when the environment variable
+// KDA_TRACE is set to a nonzero value when the library first launches (grid,
+// block, dynamic LDS and the instantiation; no numerics).
+bool trace_on() {
+    static const bool on = [] {
+        const char *v = std::getenv("KDA_TRACE");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+void trace(const char *fmt, ...) {
+    if (!trace_on()) return;
+    char line[384];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(line, sizeof(line), fmt, ap);
+    va_end(ap);
+    std::fprintf(stderr, "[kda] %s\n", line);
+}
+
+}  // namespace kda
 
 extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
-const char *kda_status_string(int s) {
+const char *kda_status_string(kda_status s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";
         case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
@@ -125,11 +164,17 @@ kda_status kda_short_conv(const void *x, void *y, int64_t total_tokens, int32_t 
     kda_status st = check_cu_host(cu_seqlens_host, num_seqs, total_tokens);
     if (st != KDA_OK) return st;
     const size_t bytes = (size_t)total_tokens * channels * esize(dtype);
-    if (overlap(x, bytes, y, bytes)) return fail(KDA_ERR_INVALID_ARG, "y overlaps x");
     const size_t csb = (size_t)num_seqs * 3 * channels * esize(dtype);
     if (conv_state_out && conv_state_out != conv_state_in &&
         overlap(conv_state_out, csb, conv_state_in, csb))
         return fail(KDA_ERR_INVALID_ARG, "conv_state_out partially overlaps conv_state_in");
+    const Buf bufs[] = {{y, bytes, "y"}, {conv_state_out, conv_state_out ? csb : 0, "conv_state_out"},
+                        {x, bytes, "x"}, {weight, (size_t)channels * 16, "weight"},
+                        {bias, bias ? (size_t)channels * 4 : 0, "bias"},
+                        {conv_state_in, conv_state_out == conv_state_in ? 0 : csb, "conv_state_in"},
+                        {cu_seqlens, cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0, "cu_seqlens"}};
+    st = check_written(bufs, 7, 2);
+    if (st != KDA_OK) return st;
     if (total_tokens > 0) {
         hipError_t e = kda::launch_short_conv(dtype, x, y, total_tokens, channels, weight, bias,
                                               conv_state_in, cu_seqlens, num_seqs,
@@ -179,42 +224,53 @@ kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
     const int64_t T = a->total_tokens, H = a->num_heads;
     const size_t es = esize(a->dtype);
     const size_t tok = (size_t)T * H * 128 * es;
-    const void *ins[4] = {a->q, a->k, a->v, a->gate};
-    for (const void *in : ins)
-        if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
-    if (overlap(a->o, tok, a->beta, (size_t)T * H * es))
-        return fail(KDA_ERR_INVALID_ARG, "o overlaps beta");
     size_t rows = 0;
     st = pool_rows(a->state_slots, a->num_slots, a->num_seqs, rows);
     if (st != KDA_OK) return st;
     const size_t sb = rows * H * 128 * 128 * state_esize(a->flags);
+    const size_t csb = rows * 3 * 3 * H * 128 * es;
     if (a->state_out && (const void *)a->state_out != (const void *)a->state_in &&
         overlap(a->state_out, sb, a->state_in, sb))
         return fail(KDA_ERR_INVALID_ARG, "state_out partially overlaps state_in");
-    if (overlap(a->state_out, sb, a->o, tok)) return fail(KDA_ERR_INVALID_ARG, "state_out overlaps o");
-    const size_t csb = rows * 3 * 3 * H * 128 * es;
     if (a->conv_state_out && a->conv_state_out != a->conv_state_in &&
         overlap(a->conv_state_out, csb, a->conv_state_in, csb))
         return fail(KDA_ERR_INVALID_ARG, "conv_state_out partially overlaps conv_state_in");
+    const size_t need = kda_prefill_workspace_size(a);
+    const bool two_pass = need > 0 && a->workspace && a->workspace_bytes >= need;
+    const size_t wb = two_pass ? a->workspace_bytes : 0;
+    const int N = a->num_seqs;
+    const size_t CC = (size_t)3 * H * 128;
+    // Every written buffer (o, state_out, conv_state_out, workspace) against every
+    // other buffer.  state_out may equal state_in and conv_state_out may equal
+    // conv_state_in (in-place update); those two pairs were checked above.
+    const bool sio = a->state_out && (const void *)a->state_out == (const void *)a->state_in;
+    const bool cio = a->conv_state_out && a->conv_state_out == a->conv_state_in;
+    const Buf bufs[] = {{a->o, tok, "o"}, {a->state_out, sb, "state_out"},
+                        {a->conv_state_out, csb, "conv_state_out"},
+                        {two_pass ? a->workspace : nullptr, wb, "workspace"},
+                        {a->q, tok, "q"}, {a->k, tok, "k"}, {a->v, tok, "v"}, {a->gate, tok, "gate"},
+                        {a->beta, (size_t)T * H * es, "beta"}, {a->conv_weight, CC * 16, "conv_weight"},
+                        {a->conv_bias, a->conv_bias ? CC * 4 : 0, "conv_bias"},
+                        {a->state_in, sio ? 0 : sb, "state_in"},
+                        {a->conv_state_in, cio ? 0 : csb, "conv_state_in"},
+                        {a->cu_seqlens, a->cu_seqlens ? (size_t)(N + 1) * 4 : 0, "cu_seqlens"},
+                        {a->state_slots, a->state_slots ? (size_t)N * 4 : 0, "state_slots"}};
+    st = check_written(bufs, 15, 4);
+    if (st != KDA_OK) return st;
 
     kda_prefill_args args = *a;
     if (args.scale == 0.f) args.scale = 1.0f / std::sqrt(128.0f);
     const int64_t pairs = (int64_t)a->num_seqs * H;
-    const size_t need = kda_prefill_workspace_size(a);
-    const bool two_pass = need > 0 && a->workspace && a->workspace_bytes >= need;
-    if (two_pass) {
-        const size_t wb = a->workspace_bytes;
-        if (overlap(a->workspace, wb, a->o, tok) || overlap(a->workspace, wb, a->state_out, sb))
-            return fail(KDA_ERR_INVALID_ARG, "workspace overlaps an output");
-        for (const void *in : ins)
-            if (overlap(a->workspace, wb, in, tok))
-                return fail(KDA_ERR_INVALID_ARG, "workspace overlaps an input");
-    }
     // dv tile per workgroup: enough workgroups for 256 compute units.  The tile
     // changes only which workgroup computes a column, not the arithmetic.
     int dv_tile = pairs >= 256 ? 128 : (pairs >= 128 ? 64 : 32);
-    const int forced = env_int("KDA_PREFILL_DV_TILE", 0);
-    if (forced == 32 || forced == 64 || forced == 128 || (two_pass && forced == 16)) dv_tile = forced;
+    if (a->dv_tile != 0) {
+        if (!(a->dv_tile == 32 || a->dv_tile == 64 || a->dv_tile == 128 ||
+              (two_pass && a->dv_tile == 16)))
+            return fail(KDA_ERR_UNSUPPORTED, "dv_tile %d: use 0, 32, 64 or 128 (16 with the "
+                                             "two-pass schedule)", a->dv_tile);
+        dv_tile = a->dv_tile;
+    }
     hipError_t e;
     if (two_pass) {
         e = kda::launch_prefill_split(&args, dv_tile, stream);
@@ -252,14 +308,14 @@ kda_status kda_decode(const kda_decode_args *a, hipStream_t stream) {
     if (st != KDA_OK) return st;
     const size_t sb = rows * a->num_heads * 128 * 128 * state_esize(a->flags);
     const size_t cb = rows * 3 * 3 * a->num_heads * 128 * es;
-    const void *ins[4] = {a->q, a->k, a->v, a->gate};
-    for (const void *in : ins) {
-        if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
-        if (overlap(a->state, sb, in, tok)) return fail(KDA_ERR_INVALID_ARG, "state overlaps an input");
-    }
-    if (overlap(a->state, sb, a->o, tok)) return fail(KDA_ERR_INVALID_ARG, "state overlaps o");
-    if (overlap(a->state, sb, a->conv_state, cb) || overlap(a->conv_state, cb, a->o, tok))
-        return fail(KDA_ERR_INVALID_ARG, "conv_state overlaps state or o");
+    const size_t CC = (size_t)3 * a->num_heads * 128;
+    const Buf bufs[] = {{a->o, tok, "o"}, {a->state, sb, "state"}, {a->conv_state, cb, "conv_state"},
+                        {a->q, tok, "q"}, {a->k, tok, "k"}, {a->v, tok, "v"}, {a->gate, tok, "gate"},
+                        {a->beta, tok / 128, "beta"}, {a->conv_weight, CC * 16, "conv_weight"},
+                        {a->conv_bias, a->conv_bias ? CC * 4 : 0, "conv_bias"},
+                        {a->state_slots, a->state_slots ? (size_t)a->num_seqs * 4 : 0, "state_slots"}};
+    st = check_written(bufs, 11, 3);
+    if (st != KDA_OK) return st;
     kda_decode_args args = *a;
     if (args.scale == 0.f) args.scale = 1.0f / std::sqrt(128.0f);
     hipError_t e = kda::launch_decode(&args, stream);
@@ -297,24 +353,20 @@ kda_status kda_decode_multi(const kda_decode_multi_args *a, hipStream_t stream) 
     const size_t cb = rows * 3 * 3 * a->num_heads * 128 * es;
     const size_t rb = NH * a->num_tokens * KDA_UPDATE_FLOATS * 4;
     const size_t pb = a->pending_updates ? NH * a->pending_tokens * KDA_UPDATE_FLOATS * 4 : 0;
-    const void *ins[4] = {a->q, a->k, a->v, a->gate};
-    for (const void *in : ins) {
-        if (overlap(a->o, tok, in, tok)) return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
-        if (overlap(a->updates, rb, in, tok))
-            return fail(KDA_ERR_INVALID_ARG, "updates overlaps an input");
-        if (overlap(a->state, sb, in, tok) || overlap(a->conv_state, cb, in, tok))
-            return fail(KDA_ERR_INVALID_ARG, "state or conv_state overlaps an input");
-    }
-    if (overlap(a->state, sb, a->o, tok) || overlap(a->conv_state, cb, a->o, tok))
-        return fail(KDA_ERR_INVALID_ARG, "state or conv_state overlaps o");
-    if (overlap(a->updates, rb, a->o, tok) || overlap(a->updates, rb, a->state, sb) ||
-        overlap(a->updates, rb, a->conv_state, cb))
-        return fail(KDA_ERR_INVALID_ARG, "updates overlaps o, state or conv_state");
-    if (overlap(a->updates, rb, a->pending_updates, pb))
-        return fail(KDA_ERR_INVALID_ARG, "updates overlaps pending_updates");
-    if (overlap(a->pending_updates, pb, a->state, sb) ||
-        overlap(a->pending_updates, pb, a->conv_state, cb))
-        return fail(KDA_ERR_INVALID_ARG, "pending_updates overlaps state or conv_state");
+    const size_t CC = (size_t)3 * a->num_heads * 128;
+    // state and conv_state are written only by a pending commit, but are always
+    // treated as written
+    const Buf bufs[] = {{a->o, tok, "o"}, {a->updates, rb, "updates"}, {a->state, sb, "state"},
+                        {a->conv_state, cb, "conv_state"},
+                        {a->q, tok, "q"}, {a->k, tok, "k"}, {a->v, tok, "v"}, {a->gate, tok, "gate"},
+                        {a->beta, tok / 128, "beta"}, {a->conv_weight, CC * 16, "conv_weight"},
+                        {a->conv_bias, a->conv_bias ? CC * 4 : 0, "conv_bias"},
+                        {a->pending_updates, pb, "pending_updates"},
+                        {a->pending_accepted, a->pending_updates ? (size_t)a->num_seqs * 4 : 0,
+                         "pending_accepted"},
+                        {a->state_slots, a->state_slots ? (size_t)a->num_seqs * 4 : 0, "state_slots"}};
+    st = check_written(bufs, 14, 4);
+    if (st != KDA_OK) return st;
     kda_decode_multi_args args = *a;
     if (args.scale == 0.f) args.scale = 1.0f / std::sqrt(128.0f);
     hipError_t e = kda::launch_decode_multi(&args, stream);
@@ -340,9 +392,11 @@ kda_status kda_decode_commit(const kda_decode_commit_args *a, hipStream_t stream
     const size_t sb = rows * a->num_heads * 128 * 128 * state_esize(a->flags);
     const size_t cb = rows * 3 * 3 * a->num_heads * 128 * esize(a->dtype);
     const size_t rb = NH * a->num_tokens * KDA_UPDATE_FLOATS * 4;
-    if (overlap(a->updates, rb, a->state, sb) || overlap(a->updates, rb, a->conv_state, cb) ||
-        overlap(a->state, sb, a->conv_state, cb))
-        return fail(KDA_ERR_INVALID_ARG, "updates, state and conv_state must not overlap");
+    const Buf bufs[] = {{a->state, sb, "state"}, {a->conv_state, cb, "conv_state"},
+                        {a->updates, rb, "updates"}, {a->accepted, (size_t)a->num_seqs * 4, "accepted"},
+                        {a->state_slots, a->state_slots ? (size_t)a->num_seqs * 4 : 0, "state_slots"}};
+    st = check_written(bufs, 5, 2);
+    if (st != KDA_OK) return st;
     hipError_t e = kda::launch_decode_commit(a, stream);
     if (e != hipSuccess) return hip_fail(e, "decode_commit launch");
     return KDA_OK;
@@ -373,6 +427,12 @@ kda_status kda_state_copy(const kda_state_copy_args *a, hipStream_t stream) {
     if (overlap(a->state_dst, sb, a->conv_src, cb) || overlap(a->state_dst, sb, a->conv_dst, cb) ||
         overlap(a->conv_dst, cb, a->state_src, sb))
         return fail(KDA_ERR_INVALID_ARG, "state and conv-state pools overlap");
+    // the slot lists must survive the writes into the destination pools
+    const size_t lb = (size_t)a->count * 4;
+    const Buf bufs[] = {{a->state_dst, sb, "state_dst"}, {a->conv_dst, a->conv_dst ? cb : 0, "conv_dst"},
+                        {a->src_slots, lb, "src_slots"}, {a->dst_slots, lb, "dst_slots"}};
+    st = check_written(bufs, 4, 2);
+    if (st != KDA_OK) return st;
     if (a->count == 0) return KDA_OK;
     hipError_t e = kda::launch_state_copy(a, stream);
     if (e != hipSuccess) return hip_fail(e, "state_copy launch");

@@ -279,6 +279,8 @@ static hipError_t short_conv_t(const void *x, void *y, int64_t T_, int C, const 
         else
             hipLaunchKernelGGL((short_conv_vec_kernel<T, false>), grid, dim3(vt), 0, s,
                                (const T *)x, (T *)y, T_, C, w, b, (const T *)cs_in, cu, N);
+        trace("short_conv_vec_kernel<%s, silu=%d> grid=(%u) block=%d lds=0", sizeof(T) == 2 ? "bf16" : "f32",
+              (int)silu, grid.x, vt);
         return hipGetLastError();
     }
     // tokens on x (up to 2^31 blocks), channel pairs on y
@@ -290,6 +292,8 @@ static hipError_t short_conv_t(const void *x, void *y, int64_t T_, int C, const 
     else
         hipLaunchKernelGGL((short_conv_kernel<T, false>), grid, dim3(kConvThreads), 0, s,
                            (const T *)x, (T *)y, T_, C, w, b, (const T *)cs_in, cu, N);
+    trace("short_conv_kernel<%s, silu=%d> grid=(%u,%u) block=%d lds=0", sizeof(T) == 2 ? "bf16" : "f32",
+          (int)silu, grid.x, grid.y, kConvThreads);
     return hipGetLastError();
 }
 
@@ -315,6 +319,8 @@ hipError_t launch_conv_tail(kda_dtype dt, const void *const src[3], const int ch
                            (const float *)src[0], (const float *)src[1], (const float *)src[2],
                            ch[0], ch[1], ch[2], T_, (const float *)cs_in, (float *)cs_out, cu, N,
                            slots, num_slots);
+    trace("conv_tail_kernel<%s> grid=(%u,%u) block=%d lds=0", dt == KDA_BF16 ? "bf16" : "f32", grid.x,
+          grid.y, kConvThreads);
     return hipGetLastError();
 }
 

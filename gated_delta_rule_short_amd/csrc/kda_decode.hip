@@ -548,11 +548,13 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
 // Launch of the instance for (token dtype, state storage): one workgroup of 256
 // threads per (sequence, head).
 template <typename P>
-static void launch_typed(kda_dtype dt, uint32_t flags, unsigned blocks, const P &p, hipStream_t s,
-                         void (*bb)(P), void (*bf)(P), void (*fb)(P), void (*ff)(P)) {
+static void launch_typed(const char *name, kda_dtype dt, uint32_t flags, unsigned blocks, const P &p,
+                         hipStream_t s, void (*bb)(P), void (*bf)(P), void (*fb)(P), void (*ff)(P)) {
     const bool sb16 = flags & KDA_F_STATE_BF16;
     void (*k)(P) = dt == KDA_BF16 ? (sb16 ? bb : bf) : (sb16 ? fb : ff);
     hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, s, p);
+    trace("%s<tokens %s, state %s> grid=(%u) block=256 lds=0", name, dt == KDA_BF16 ? "bf16" : "f32",
+          sb16 ? "bf16" : "f32", blocks);
 }
 
 hipError_t launch_decode(const kda_decode_args *a, hipStream_t s) {
@@ -564,7 +566,7 @@ hipError_t launch_decode(const kda_decode_args *a, hipStream_t s) {
     p.H = a->num_heads;
     p.scale = a->scale; p.lb = a->gate_lower_bound; p.flags = a->flags;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    launch_typed<DecodeParams>(a->dtype, a->flags, blocks, p, s,
+    launch_typed<DecodeParams>("decode_kernel", a->dtype, a->flags, blocks, p, s,
                      decode_kernel<__bf16, __bf16>, decode_kernel<__bf16, float>, decode_kernel<float, __bf16>, decode_kernel<float, float>);
     return hipGetLastError();
 }
@@ -579,7 +581,7 @@ hipError_t launch_decode_multi(const kda_decode_multi_args *a, hipStream_t s) {
     p.H = a->num_heads; p.T = a->num_tokens; p.pT = a->pending_updates ? a->pending_tokens : 0;
     p.scale = a->scale; p.lb = a->gate_lower_bound; p.flags = a->flags;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    launch_typed<MultiParams>(a->dtype, a->flags, blocks, p, s,
+    launch_typed<MultiParams>("multi_kernel", a->dtype, a->flags, blocks, p, s,
                      multi_kernel<__bf16, __bf16>, multi_kernel<__bf16, float>, multi_kernel<float, __bf16>, multi_kernel<float, float>);
     return hipGetLastError();
 }
@@ -590,7 +592,7 @@ hipError_t launch_decode_commit(const kda_decode_commit_args *a, hipStream_t s) 
     p.slots = a->state_slots; p.num_slots = a->num_slots;
     p.H = a->num_heads; p.T = a->num_tokens;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    launch_typed<CommitParams>(a->dtype, a->flags, blocks, p, s,
+    launch_typed<CommitParams>("commit_kernel", a->dtype, a->flags, blocks, p, s,
                      commit_kernel<__bf16, __bf16>, commit_kernel<__bf16, float>, commit_kernel<float, __bf16>, commit_kernel<float, float>);
     return hipGetLastError();
 }

@@ -274,6 +274,7 @@ static hipError_t launch_zproj(const ZParams &zp, hipStream_t s) {
     if (attr != hipSuccess) return attr;
     const dim3 grid((unsigned)((zp.T + kMT - 1) / kMT), kSplit);
     hipLaunchKernelGGL(zproj_kernel<NT>, grid, dim3(640), G::LDS, s, zp);
+    trace("zproj_kernel<%d> grid=(%u,%u) block=640 lds=%d", NT, grid.x, grid.y, (int)G::LDS);
     return hipGetLastError();
 }
 
@@ -303,6 +304,7 @@ hipError_t launch_gate_proj(const kda_gate_beta_args *a, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(zreduce_kernel, dim3((unsigned)((T * N1 + 255) / 256)), dim3(256), 0, s, zp.part, z,
                        static_cast<__bf16 *>(a->beta), T, H);
+    trace("zreduce_kernel grid=(%u) block=256 lds=0", (unsigned)((T * N1 + 255) / 256));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     EParams ep;
@@ -314,6 +316,7 @@ hipError_t launch_gate_proj(const kda_gate_beta_args *a, hipStream_t s) {
     ep.glog = (a->flags & KDA_F_GATE_IS_LOG) ? 1 : 0;
     const dim3 g2((unsigned)((T + 63) / 64), (unsigned)(ep.hd / (256 * kCT)));
     hipLaunchKernelGGL(gate_expand_kernel, g2, dim3(256), 0, s, ep);
+    trace("gate_expand_kernel grid=(%u,%u) block=256", g2.x, g2.y);
     return hipGetLastError();
 }
 

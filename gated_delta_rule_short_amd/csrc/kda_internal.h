@@ -9,6 +9,11 @@
 
 namespace kda {
 
+// Launch log (KDA_TRACE=1 in the environment): one stderr line per launch with
+// the kernel, its grid, block and dynamic LDS.
+bool trace_on();
+void trace(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+
 // Conv over packed sequences; x, y: [T][channels].
 hipError_t launch_short_conv(kda_dtype dt, const void *x, void *y, int64_t T, int channels,
                              const float *w, const float *b, const void *cs_in,

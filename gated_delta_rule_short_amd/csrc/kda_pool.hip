@@ -66,6 +66,7 @@ hipError_t launch_state_copy(const kda_state_copy_args *a, hipStream_t s) {
     p.conv_elem = a->dtype == KDA_BF16 ? 2 : 4;
     const unsigned blocks = (unsigned)a->count * (unsigned)a->num_heads;
     hipLaunchKernelGGL(state_copy_kernel, dim3(blocks), dim3(256), 0, s, p);
+    trace("state_copy_kernel grid=(%u) block=256 lds=0", blocks);
     return hipGetLastError();
 }
 

@@ -657,6 +657,8 @@ static hipError_t launch_t(const PrefillParams &pp, hipStream_t s) {
     const int groups = (pp.pairs + 7) / 8;
     const unsigned blocks = (unsigned)groups * 8u * (unsigned)pp.tiles;
     hipLaunchKernelGGL((prefill_kernel<T, NB, DVW>), dim3(blocks), dim3(256), LY::TOTAL, s, pp);
+    trace("prefill_kernel<%s, chunk=%d, dv_tile=%d> grid=(%u) block=256 lds=%d",
+          sizeof(T) == 2 ? "bf16" : "f32", 16 * NB, DVW, blocks, (int)LY::TOTAL);
     return hipGetLastError();
 }
 

@@ -917,6 +917,7 @@ hipError_t launch_scan(const SplitParams &sp, hipStream_t s) {
     if (attr != hipSuccess) return attr;
     const unsigned blocks = (unsigned)((sp.pairs + 7) / 8) * 8u * (unsigned)sp.tiles;
     hipLaunchKernelGGL(scan_kernel<NTW>, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
+    trace("scan_kernel<%d> grid=(%u) block=%d lds=%d ring=%d", NTW, blocks, G::kThreads, G::kLds, G::NS);
     return hipGetLastError();
 }
 
@@ -962,6 +963,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
         const dim3 grid = sp.a_heads_fast ? dim3((unsigned)a->num_heads, (unsigned)gx)
                                           : dim3((unsigned)gx, (unsigned)a->num_heads);
         hipLaunchKernelGGL(intra_kernel, grid, dim3(256), 4 * A_WAVE, s, sp);
+        trace("intra_kernel grid=(%u,%u) block=256 lds=%d", grid.x, grid.y, 4 * A_WAVE);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

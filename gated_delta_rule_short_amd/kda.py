@@ -41,7 +41,7 @@ class KdaPrefillArgs(ctypes.Structure):
         ("conv_weight", _p), ("conv_bias", _p), ("conv_state_in", _p), ("conv_state_out", _p),
         ("state_in", _p), ("state_out", _p), ("o", _p), ("cu_seqlens", _p),
         ("cu_seqlens_host", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
-        ("state_slots", _p), ("num_slots", _c_i32),
+        ("state_slots", _p), ("num_slots", _c_i32), ("dv_tile", _c_i32),
     ]
 
 
@@ -117,7 +117,7 @@ def load_library(path: str = LIB_PATH):
         lib = ctypes.CDLL(path)
         lib.kda_abi_version.restype = ctypes.c_int
         lib.kda_status_string.restype = ctypes.c_char_p
-        lib.kda_status_string.argtypes = [ctypes.c_int]
+        lib.kda_status_string.argtypes = [ctypes.c_int]  # kda_status (an int-sized enum)
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_short_conv.restype = ctypes.c_int
         lib.kda_short_conv.argtypes = [_p, _p, _c_i64, _c_i32, _p, _p, _p, _p, _p, _p, _c_i32,
@@ -206,6 +206,30 @@ def _need(t, name, dtype=None, device=None):
         raise ValueError("%s must be on %s" % (name, device))
 
 
+def _shape(t, name, shape):
+    """Raise ValueError unless tensor `t` (if given) has exactly `shape`."""
+    if t is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(int(x) for x in shape),
+                                                            tuple(t.shape)))
+
+
+def _conv_weight_shape(t, name, channels):
+    """Conv weights hold 4 taps per channel: [channels, 4], or [3, channels / 3, 4]."""
+    if t is None:
+        return
+    if t.numel() != channels * 4 or t.shape[-1] != 4:
+        raise ValueError("%s must hold %d channels x 4 taps, got shape %s" % (name, channels,
+                                                                             tuple(t.shape)))
+
+
+def _pool_shape(t, name, rows_shape_tail):
+    """A state or conv-state pool: any number of rows of the given trailing shape."""
+    if t is not None and (t.dim() != 1 + len(rows_shape_tail) or
+                          tuple(t.shape[1:]) != tuple(rows_shape_tail)):
+        raise ValueError("%s must have shape [rows, %s], got %s" % (
+            name, ", ".join(str(x) for x in rows_shape_tail), tuple(t.shape)))
+
+
 def abi_version():
     return load_library().kda_abi_version()
 
@@ -218,12 +242,20 @@ def kda_short_conv(x, weight, *, cu_seqlens=None, cu_seqlens_host=None, bias=Non
     Returns y (allocated when not given).  conv_state_out=True allocates [N, 3, C]."""
     lib = load_library()
     dev = x.device
+    if x.dim() != 2:
+        raise ValueError("x must be [T, C], got %s" % (tuple(x.shape),))
     T, C = x.shape
     N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else int(num_seqs or 1)
     if y is None:
         y = torch.empty_like(x)
     if conv_state_out is True:
         conv_state_out = torch.empty((N, 3, C), dtype=x.dtype, device=dev)
+    _shape(y, "y", (T, C))
+    _shape(weight, "weight", (C, 4))
+    _shape(bias, "bias", (C,))
+    _shape(conv_state_in, "conv_state_in", (N, 3, C))
+    _shape(conv_state_out, "conv_state_out", (N, 3, C))
+    _shape(cu_seqlens, "cu_seqlens", (N + 1,))
     for t, nm in ((x, "x"), (y, "y"), (conv_state_in, "conv_state_in"),
                   (conv_state_out, "conv_state_out")):
         _need(t, nm, x.dtype, dev)
@@ -245,7 +277,7 @@ def kda_short_conv(x, weight, *, cu_seqlens=None, cu_seqlens_host=None, bias=Non
 def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens_host=None,
                 num_seqs=None, conv_bias=None, conv_state_in=None, conv_state_out=None,
                 state_in=None, state_out=None, o=None, scale=0.0, gate_lower_bound=-5.0,
-                chunk_size=0, flags=0, workspace=None, state_slots=None, stream=None):
+                chunk_size=0, flags=0, workspace=True, state_slots=None, dv_tile=0, stream=None):
     """Chunked KDA prefill of packed sequences.
 
     The state (state_in / state_out) is fp32, or bf16 storage when those tensors are
@@ -255,14 +287,19 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
 
     q, k, gate: [T, H, 128]; v: [T, H, 128]; beta: [T, H] (bf16 or fp32, one dtype);
     conv_weight: [3*H*128, 4] fp32.  state_out / conv_state_out: a tensor, or True
-    to allocate one.  workspace: a uint8 device tensor for the two-pass schedule
-    (see prefill_workspace_bytes), True to allocate one, or None for the one-pass
-    schedule.  Returns (o, state_out, conv_state_out)."""
+    to allocate one.  workspace selects the schedule: True (the default) allocates
+    the two-pass workspace wherever that schedule applies (bf16 with chunk_size 0
+    or 16); a uint8 device tensor is used as that workspace; None or False runs
+    the one-pass schedule.  dv_tile: state columns per workgroup (0 = automatic).
+    Returns (o, state_out, conv_state_out)."""
     lib = load_library()
     dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, 128], got %s" % (tuple(q.shape),))
     T, H, dk = q.shape
-    dv = v.shape[2]
+    dv = v.shape[-1] if v.dim() == 3 else -1
     N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else int(num_seqs or 1)
+    CC = 2 * H * dk + H * dv
     if o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
     if state_slots is not None and (state_out is True or conv_state_out is True):
@@ -271,7 +308,25 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
         sdt = state_in.dtype if state_in is not None else torch.float32
         state_out = torch.empty((N, H, dk, dv), dtype=sdt, device=dev)
     if conv_state_out is True:
-        conv_state_out = torch.empty((N, 3, 2 * H * dk + H * dv), dtype=q.dtype, device=dev)
+        conv_state_out = torch.empty((N, 3, CC), dtype=q.dtype, device=dev)
+    for t, nm in ((k, "k"), (gate, "gate")):
+        _shape(t, nm, (T, H, dk))
+    _shape(v, "v", (T, H, dv))
+    _shape(o, "o", (T, H, dv))
+    _shape(beta, "beta", (T, H))
+    _conv_weight_shape(conv_weight, "conv_weight", CC)
+    _shape(conv_bias, "conv_bias", (CC,))
+    _shape(cu_seqlens, "cu_seqlens", (N + 1,))
+    if state_slots is None:
+        _shape(state_in, "state_in", (N, H, dk, dv))
+        _shape(state_out, "state_out", (N, H, dk, dv))
+        _shape(conv_state_in, "conv_state_in", (N, 3, CC))
+        _shape(conv_state_out, "conv_state_out", (N, 3, CC))
+    else:
+        for t, nm in ((state_in, "state_in"), (state_out, "state_out")):
+            _pool_shape(t, nm, (H, dk, dv))
+        for t, nm in ((conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
+            _pool_shape(t, nm, (3, CC))
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (o, "o"),
                   (conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
         _need(t, nm, q.dtype, dev)
@@ -288,7 +343,8 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
     _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     cuh = None
     if cu_seqlens_host is not None:
-        cuh = cu_seqlens_host.to(torch.int32).contiguous().cpu()
+        cuh = torch.as_tensor(cu_seqlens_host).to(torch.int32).contiguous().cpu()
+        _shape(cuh, "cu_seqlens_host", (N + 1,))
     a = KdaPrefillArgs(
         num_seqs=N, num_heads=H, head_dim_k=dk, head_dim_v=dv, chunk_size=int(chunk_size),
         total_tokens=T, dtype=_dtype_code(q), flags=int(flags) | sflag, scale=float(scale),
@@ -297,7 +353,8 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
         conv_weight=_ptr(conv_weight), conv_bias=_ptr(conv_bias),
         conv_state_in=_ptr(conv_state_in), conv_state_out=_ptr(conv_state_out),
         state_in=_ptr(state_in), state_out=_ptr(state_out), o=_ptr(o),
-        cu_seqlens=_ptr(cu_seqlens), cu_seqlens_host=_ptr(cuh), workspace=None, workspace_bytes=0)
+        cu_seqlens=_ptr(cu_seqlens), cu_seqlens_host=_ptr(cuh), workspace=None, workspace_bytes=0,
+        dv_tile=int(dv_tile))
     pools = (state_in, state_out, conv_state_in, conv_state_out)
     if state_slots is not None and not any(torch.is_tensor(t) for t in pools):
         raise ValueError("state_slots needs a state or conv-state pool")
@@ -305,6 +362,8 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
     if workspace is True:
         need = lib.kda_prefill_workspace_size(ctypes.byref(a))
         workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    elif workspace is False:
+        workspace = None
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, dev)
         a.workspace = _ptr(workspace)
@@ -330,10 +389,26 @@ def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias
     Returns o [N, H, 128]."""
     lib = load_library()
     dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, 128], got %s" % (tuple(q.shape),))
     N, H, dk = q.shape
-    dv = v.shape[2]
+    dv = v.shape[-1] if v.dim() == 3 else -1
+    CC = 2 * H * dk + H * dv
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    for t, nm in ((k, "k"), (gate, "gate")):
+        _shape(t, nm, (N, H, dk))
+    _shape(v, "v", (N, H, dv))
+    _shape(o, "o", (N, H, dv))
+    _shape(beta, "beta", (N, H))
+    _conv_weight_shape(conv_weight, "conv_weight", CC)
+    _shape(conv_bias, "conv_bias", (CC,))
+    if state_slots is None:
+        _shape(state, "state", (N, H, dk, dv))
+        _shape(conv_state, "conv_state", (N, 3, CC))
+    else:
+        _pool_shape(state, "state", (H, dk, dv))
+        _pool_shape(conv_state, "conv_state", (3, CC))
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (o, "o"),
                   (conv_state, "conv_state")):
         _need(t, nm, q.dtype, dev)
@@ -361,12 +436,28 @@ def kda_decode_multi(q, k, v, gate, beta, conv_weight, conv_state, state, *, upd
     Returns (o [N, T, H, 128], updates [N, H, T, 768] fp32)."""
     lib = load_library()
     dev = q.device
+    if q.dim() != 4:
+        raise ValueError("q must be [N, T, H, 128], got %s" % (tuple(q.shape),))
     N, T, H, dk = q.shape
-    dv = v.shape[3]
+    dv = v.shape[-1] if v.dim() == 4 else -1
+    CC = 2 * H * dk + H * dv
     if o is None:
         o = torch.empty((N, T, H, dv), dtype=q.dtype, device=dev)
     if updates is None:
         updates = torch.empty((N, H, T, UPDATE_FLOATS), dtype=torch.float32, device=dev)
+    for t, nm in ((k, "k"), (gate, "gate")):
+        _shape(t, nm, (N, T, H, dk))
+    _shape(v, "v", (N, T, H, dv))
+    _shape(o, "o", (N, T, H, dv))
+    _shape(beta, "beta", (N, T, H))
+    _conv_weight_shape(conv_weight, "conv_weight", CC)
+    _shape(conv_bias, "conv_bias", (CC,))
+    if state_slots is None:
+        _shape(state, "state", (N, H, dk, dv))
+        _shape(conv_state, "conv_state", (N, 3, CC))
+    else:
+        _pool_shape(state, "state", (H, dk, dv))
+        _pool_shape(conv_state, "conv_state", (3, CC))
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (o, "o"),
                   (conv_state, "conv_state")):
         _need(t, nm, q.dtype, dev)
@@ -405,7 +496,15 @@ def kda_decode_commit(updates, accepted, conv_state, state, *, state_slots=None,
     lib = load_library()
     dev = state.device
     N = accepted.numel()
+    if state.dim() != 4:
+        raise ValueError("state must be [rows, H, 128, 128], got %s" % (tuple(state.shape),))
     H, dk, dv = state.shape[1:]
+    CC = 2 * H * dk + H * dv
+    if state_slots is None:
+        _shape(state, "state", (N, H, dk, dv))
+        _shape(conv_state, "conv_state", (N, 3, CC))
+    else:
+        _pool_shape(conv_state, "conv_state", (3, CC))
     T = updates.numel() // (N * H * UPDATE_FLOATS)
     if updates.numel() != N * H * T * UPDATE_FLOATS:
         raise ValueError("updates must hold N*H*T*%d floats" % UPDATE_FLOATS)
@@ -429,7 +528,12 @@ def kda_state_copy(state_pool, src_slots, dst_slots, *, conv_pool=None, dst_stat
     (int32 device tensors).  The destination pools default to the source pools."""
     lib = load_library()
     dev = state_pool.device
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [rows, H, 128, 128], got %s" % (tuple(state_pool.shape),))
     P, H, dk, dv = state_pool.shape
+    CC = 2 * H * dk + H * dv
+    for t, nm in ((conv_pool, "conv_pool"), (dst_conv_pool, "dst_conv_pool")):
+        _shape(t, nm, (P, 3, CC))
     dst_state_pool = state_pool if dst_state_pool is None else dst_state_pool
     if conv_pool is not None and dst_conv_pool is None:
         dst_conv_pool = conv_pool
@@ -460,12 +564,20 @@ def kda_gate_beta_proj(x, w_a, w_b, w_beta, *, gate=None, beta=None, workspace=N
     to allocate one."""
     lib = load_library()
     dev = x.device
+    if x.dim() != 2 or w_beta.dim() != 2:
+        raise ValueError("x must be [T, hidden] and w_beta [H, hidden]")
     T, hidden = x.shape
     H = w_beta.shape[0]
+    R = w_a.shape[0] if w_a.dim() == 2 else -1
+    _shape(w_a, "w_a", (R, hidden))
+    _shape(w_b, "w_b", (H * 128, R))
+    _shape(w_beta, "w_beta", (H, hidden))
     if gate is None:
         gate = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
     if beta is None:
         beta = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _shape(gate, "gate", (T, H, 128))
+    _shape(beta, "beta", (T, H))
     for t, nm in ((x, "x"), (w_a, "w_a"), (w_b, "w_b"), (w_beta, "w_beta"), (gate, "gate"),
                   (beta, "beta")):
         _need(t, nm, torch.bfloat16, dev)
@@ -487,3 +599,65 @@ def gate_beta_workspace_bytes(total_tokens, num_heads):
     lib = load_library()
     a = KdaGateBetaArgs(total_tokens=int(total_tokens), num_heads=int(num_heads))
     return int(lib.kda_gate_beta_workspace_size(ctypes.byref(a)))
+
+
+# ------------------------------------------------------------------ calibration
+CALIB_PATH = os.path.join(_HERE, "libkda_calib.so")
+CALIB_EXPORTS = ("kda_calib_state_rmw", "kda_calib_copy", "kda_calib_fill")
+_calib = None
+
+
+def load_calib_library(path: str = CALIB_PATH):
+    """Load libkda_calib.so: the measurement-only streaming kernels of known bytes
+    (include/kda_calib.h)."""
+    global _calib
+    with _lock:
+        if _calib is not None and path == CALIB_PATH:
+            return _calib
+        if not os.path.exists(path):
+            raise RuntimeError("libkda_calib.so not found at %s: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`" % path)
+        lib = ctypes.CDLL(path)
+        lib.kda_calib_state_rmw.argtypes = [_p, _c_i64, _c_f32, _p]
+        lib.kda_calib_copy.argtypes = [_p, _p, ctypes.c_size_t, _p]
+        lib.kda_calib_fill.argtypes = [_p, ctypes.c_size_t, _c_f32, _p]
+        for f in CALIB_EXPORTS:
+            getattr(lib, f).restype = ctypes.c_int
+        if path == CALIB_PATH:
+            _calib = lib
+        return lib
+
+
+def _calib_check(st, what):
+    if st != 0:
+        raise RuntimeError("%s failed with status %d" % (what, st))
+
+
+def calib_state_rmw(state, scale=1.0, stream=None):
+    """Read-modify-write of fp32 [rows, 128, 128]-shaped states in place (decode's
+    state stream without its arithmetic)."""
+    _need(state, "state", torch.float32, state.device)
+    if state.numel() % (128 * 128):
+        raise ValueError("state must hold whole 128 x 128 fp32 states")
+    _calib_check(load_calib_library().kda_calib_state_rmw(
+        _ptr(state), state.numel() // (128 * 128), float(scale), _stream(stream, state.device)),
+        "kda_calib_state_rmw")
+
+
+def calib_copy(dst, src, stream=None):
+    """dst = src (byte sizes equal, multiples of 16)."""
+    if dst.numel() * dst.element_size() != src.numel() * src.element_size():
+        raise ValueError("dst and src must have one byte size")
+    _need(dst, "dst", None, dst.device)
+    _need(src, "src", None, dst.device)
+    _calib_check(load_calib_library().kda_calib_copy(
+        _ptr(dst), _ptr(src), dst.numel() * dst.element_size(), _stream(stream, dst.device)),
+        "kda_calib_copy")
+
+
+def calib_fill(dst, value=0.0, stream=None):
+    """Every fp32 value of dst set to `value`."""
+    _need(dst, "dst", None, dst.device)
+    _calib_check(load_calib_library().kda_calib_fill(
+        _ptr(dst), dst.numel() * dst.element_size(), float(value), _stream(stream, dst.device)),
+        "kda_calib_fill")

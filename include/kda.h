@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
     KDA_OK = 0,
@@ -98,13 +98,17 @@ enum {
  * It halves the state traffic, the whole cost of a decode step.  Rounding once
  * per call adds error that levels off rather than growing with the number of
  * steps, at a size set by how slowly the state decays; fp32 stays the
- * default. */
+ * default.  Supported regime: measured against the fp64 recurrence over 256 to
+ * 8192 decode steps, outputs and states stay within a relative error of 2e-2
+ * while the per-row decays exp(g) stay below about 0.998 (memories of up to
+ * about 600 tokens); with decays near 0.9998 the error levels off at about
+ * 2.4e-2.  Keep fp32 storage where the gates hold the state that long. */
 
 /* Version of this ABI (KDA_ABI_VERSION). */
 int kda_abi_version(void);
 
-/* Static string naming a kda_status value. */
-const char *kda_status_string(int status);
+/* Static string naming a kda_status value ("KDA_UNKNOWN_STATUS" for any other value). */
+const char *kda_status_string(kda_status status);
 
 /* Message describing the calling thread's most recent failing call ("" if none). */
 const char *kda_last_error(void);
@@ -146,8 +150,12 @@ typedef struct {
     int32_t num_heads;       /* H >= 1 */
     int32_t head_dim_k;      /* must be 128 */
     int32_t head_dim_v;      /* must be 128 */
-    int32_t chunk_size;      /* 0 = default (64 for bf16, 32 for fp32); 16, 32 or 64
-                                (fp32 I/O: 16 or 32) */
+    int32_t chunk_size;      /* 0 = default; 16, 32 or 64.  The default is the
+                                two-pass schedule (16-token sub-chunks) when a
+                                workspace is given, else one pass with 64-token
+                                chunks for bf16 and 32-token chunks for fp32 I/O
+                                (an fp32 64-token chunk does not fit in LDS:
+                                KDA_ERR_UNSUPPORTED) */
     int64_t total_tokens;    /* 0 <= T <= 2^31 - 64 (token offsets are int32) */
     kda_dtype dtype;
     uint32_t flags;          /* KDA_F_* */
@@ -170,6 +178,11 @@ typedef struct {
     size_t workspace_bytes;    /* its size; see kda_prefill_workspace_size */
     const int32_t *state_slots;/* [N] device pool slots, or NULL (see "State pool") */
     int32_t num_slots;         /* pool rows when state_slots is given */
+    int32_t dv_tile;           /* state columns per workgroup: 0 = chosen from the
+                                  number of (sequence, head) pairs; else 32, 64 or
+                                  128 (and 16 for the two-pass schedule).  Changes
+                                  which workgroup computes a column, never the
+                                  arithmetic: results are bit-identical. */
 } kda_prefill_args;
 
 /*

@@ -12,6 +12,7 @@ from gated_delta_rule_short_amd import kda as K
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
+CALIB_HEADER = os.path.join(ROOT, "include", "kda_calib.h")
 
 
 @pytest.fixture(scope="module")
@@ -22,20 +23,30 @@ def lib():
     return K.load_library()
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text))
 
 
 def test_header_and_binding_agree():
     assert _declared_functions() == set(K.EXPORTS)
+    assert _declared_functions(CALIB_HEADER) == set(K.CALIB_EXPORTS)
+
+
+def test_calibration_library_exports_and_rejects_bad_arguments():
+    calib = K.load_calib_library()
+    for name in _declared_functions(CALIB_HEADER):
+        assert hasattr(calib, name), name
+    assert calib.kda_calib_copy(FAKE, FAKE, 17, None) == 1      # not a multiple of 16
+    assert calib.kda_calib_fill(None, 16, 0.0, None) == 1
+    assert calib.kda_calib_state_rmw(FAKE, 0, 1.0, None) == 1
 
 
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -43,6 +54,7 @@ def test_status_strings(lib):
     assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARG"
     assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
     assert lib.kda_status_string(3) == b"KDA_ERR_HIP"
+    assert lib.kda_status_string(99) == b"KDA_UNKNOWN_STATUS"
 
 
 def test_struct_layouts_match_header():
@@ -50,6 +62,8 @@ def test_struct_layouts_match_header():
     assert K.KdaPrefillArgs.total_tokens.offset == 24
     assert K.KdaPrefillArgs.q.offset == 48
     assert K.KdaPrefillArgs.state_slots.offset == 48 + 16 * 8
+    assert K.KdaPrefillArgs.num_slots.offset == 48 + 17 * 8
+    assert K.KdaPrefillArgs.dv_tile.offset == 48 + 17 * 8 + 4
     assert ctypes.sizeof(K.KdaPrefillArgs) == 48 + 18 * 8
     assert K.KdaDecodeArgs.q.offset == 32
     assert K.KdaDecodeArgs.state_slots.offset == 32 + 10 * 8
@@ -404,3 +418,157 @@ def test_binding_checks_pool_rows_before_any_launch(lib):
         K.kda_decode(qd, qd, qd, qd, beta[:1], w, cpool, pool, state_slots=slots)
     with pytest.raises(ValueError):  # no slot map: one row per sequence
         K.kda_decode(qd, qd, qd, qd, beta[:1], w, cpool[:1], pool)
+
+
+@pytest.mark.parametrize("dv_tile,status", [(48, K.KDA_ERR_UNSUPPORTED), (-1, K.KDA_ERR_UNSUPPORTED),
+                                            (16, K.KDA_ERR_UNSUPPORTED)])
+def test_prefill_rejects_bad_dv_tile(lib, dv_tile, status):
+    # 16 columns per workgroup exist only in the two-pass schedule (no workspace here)
+    a = _prefill_args(dv_tile=dv_tile)
+    assert lib.kda_prefill(ctypes.byref(a), None) == status
+    assert b"dv_tile" in lib.kda_last_error()
+
+
+# Every buffer a prefill call writes (o, state_out, conv_state_out, workspace) is
+# checked against every other buffer of the call: these aliases would let one
+# wave overwrite what another still reads.
+@pytest.mark.parametrize("written,other", [
+    ("workspace", "beta"), ("workspace", "state_in"), ("workspace", "conv_state_in"),
+    ("workspace", "conv_weight"), ("workspace", "cu_seqlens"), ("workspace", "state_slots"),
+    ("conv_state_out", "o"), ("conv_state_out", "q"), ("conv_state_out", "state_out"),
+    ("conv_state_out", "beta"), ("state_out", "conv_state_in"), ("state_out", "beta"),
+    ("o", "conv_weight"), ("o", "cu_seqlens"),
+])
+def test_prefill_rejects_written_buffer_aliases(lib, written, other):
+    a = _prefill_args(total_tokens=64, num_heads=2)
+    region = 0x40000000
+    for i, f in enumerate(("state_in", "state_out", "conv_state_in", "conv_state_out",
+                           "cu_seqlens", "state_slots", "workspace")):
+        setattr(a, f, ctypes.c_void_p(region + i * 0x4000000))
+    a.num_slots = 4
+    a.workspace_bytes = lib.kda_prefill_workspace_size(ctypes.byref(a))
+    setattr(a, written, getattr(a, other))
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    msg = lib.kda_last_error().decode()
+    assert written in msg and other in msg, msg
+
+
+def test_prefill_allows_exact_in_place_state_and_conv_state(lib):
+    """state_out == state_in and conv_state_out == conv_state_in are the documented
+    in-place updates: the overlap checks pass them, and the call stops at the next
+    check (an unsupported dv_tile), before any launch."""
+    a = _prefill_args(total_tokens=64, num_heads=2, dv_tile=48)
+    a.state_in = a.state_out = ctypes.c_void_p(0x40000000)
+    a.conv_state_in = a.conv_state_out = ctypes.c_void_p(0x48000000)
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_UNSUPPORTED
+    assert b"dv_tile" in lib.kda_last_error(), lib.kda_last_error()
+
+
+@pytest.mark.parametrize("written,other", [("o", "beta"), ("state", "conv_weight"),
+                                           ("conv_state", "beta"), ("o", "state_slots")])
+def test_decode_rejects_written_buffer_aliases(lib, written, other):
+    a = _decode_args()
+    a.state_slots = ctypes.c_void_p(0x50000000)
+    a.num_slots = 4
+    setattr(a, written, getattr(a, other))
+    assert lib.kda_decode(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    msg = lib.kda_last_error().decode()
+    assert written in msg and other in msg, msg
+
+
+def test_short_conv_rejects_conv_state_out_aliasing_y(lib):
+    y = ctypes.c_void_p(0x200000)
+    st = lib.kda_short_conv(ctypes.c_void_p(0x100000), y, 16, 64, ctypes.c_void_p(0x300000), None,
+                            None, y, None, None, 1, K.KDA_BF16, 0, None)
+    assert st == K.KDA_ERR_INVALID_ARG
+    assert b"conv_state_out" in lib.kda_last_error()
+
+
+def _cpu_prefill_inputs(T=4, H=2):
+    import torch
+    q = torch.zeros((T, H, 128), dtype=torch.bfloat16)
+    beta = torch.zeros((T, H), dtype=torch.bfloat16)
+    w = torch.zeros((3 * H * 128, 4))
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    return q, beta, w, cu
+
+
+@pytest.mark.parametrize("bad", ["beta", "state_in", "state_out", "conv_w", "conv_bias",
+                                 "conv_state_in", "o", "v", "cu"])
+def test_binding_checks_full_shapes_prefill(lib, bad):
+    """A tensor of the wrong shape never reaches the kernels (they would read or
+    write past its end): the binding raises ValueError first, on CPU tensors."""
+    import torch
+    T, H = 4, 2
+    q, beta, w, cu = _cpu_prefill_inputs(T, H)
+    kw = dict(cu_seqlens=cu, workspace=None)
+    args = [q, q.clone(), q.clone(), q.clone(), beta, w]
+    if bad == "beta":
+        args[4] = torch.zeros((T,), dtype=torch.bfloat16)
+    elif bad == "state_in":
+        kw["state_in"] = torch.zeros((1, H - 1, 128, 128))
+    elif bad == "state_out":
+        kw["state_out"] = torch.zeros((1, H, 128, 64))
+    elif bad == "conv_w":
+        args[5] = torch.zeros((3 * H * 128 - 4, 4))
+    elif bad == "conv_bias":
+        kw["conv_bias"] = torch.zeros(3 * H * 128 - 1)
+    elif bad == "conv_state_in":
+        kw["conv_state_in"] = torch.zeros((1, 3, 3 * H * 128 - 2), dtype=torch.bfloat16)
+    elif bad == "o":
+        kw["o"] = torch.zeros((T - 1, H, 128), dtype=torch.bfloat16)
+    elif bad == "v":
+        args[2] = torch.zeros((T, H, 64), dtype=torch.bfloat16)
+    elif bad == "cu":
+        kw["cu_seqlens"] = torch.tensor([0, 2, T], dtype=torch.int32)
+        kw["num_seqs"] = 1
+        kw["state_in"] = torch.zeros((1, H, 128, 128))
+    with pytest.raises(ValueError):
+        K.kda_prefill(*args, **kw)
+
+
+@pytest.mark.parametrize("bad", ["beta", "state", "conv_state", "gate", "o"])
+def test_binding_checks_full_shapes_decode(lib, bad):
+    import torch
+    N, H = 3, 2
+    q = torch.zeros((N, H, 128), dtype=torch.bfloat16)
+    beta = torch.zeros((N, H), dtype=torch.bfloat16)
+    w = torch.zeros((3 * H * 128, 4))
+    state = torch.zeros((N, H, 128, 128))
+    cs = torch.zeros((N, 3, 3 * H * 128), dtype=torch.bfloat16)
+    args = [q, q.clone(), q.clone(), q.clone(), beta, w, cs, state]
+    kw = {}
+    if bad == "beta":
+        args[4] = torch.zeros((N * H,), dtype=torch.bfloat16)
+    elif bad == "state":
+        args[7] = torch.zeros((N, H - 1, 128, 128))
+    elif bad == "conv_state":
+        args[6] = torch.zeros((N, 3, 3 * H * 128 - 128), dtype=torch.bfloat16)
+    elif bad == "gate":
+        args[3] = torch.zeros((N, H, 64), dtype=torch.bfloat16)
+    elif bad == "o":
+        kw["o"] = torch.zeros((N, H + 1, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        K.kda_decode(*args, **kw)
+
+
+def test_binding_checks_full_shapes_decode_multi_and_projection(lib):
+    import torch
+    N, T, H = 2, 3, 2
+    q = torch.zeros((N, T, H, 128), dtype=torch.bfloat16)
+    beta = torch.zeros((N, T, H), dtype=torch.bfloat16)
+    w = torch.zeros((3 * H * 128, 4))
+    state = torch.zeros((N, H, 128, 128))
+    cs = torch.zeros((N, 3, 3 * H * 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        K.kda_decode_multi(q, q, q, q, beta[:, :2], w, cs, state)
+    with pytest.raises(ValueError):
+        K.kda_decode_multi(q, q, q, q, beta, w, cs, state[:, :1])
+    with pytest.raises(ValueError):
+        K.kda_decode_commit(torch.zeros((N, H, T, K.UPDATE_FLOATS)), torch.zeros(N, dtype=torch.int32),
+                            cs[:, :, :-1], state)
+    x = torch.zeros((8, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        K.kda_gate_beta_proj(x, torch.zeros((128, 256), dtype=torch.bfloat16),
+                             torch.zeros((H * 128, 64), dtype=torch.bfloat16),
+                             torch.zeros((H, 256), dtype=torch.bfloat16))

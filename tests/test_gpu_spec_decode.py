@@ -273,14 +273,23 @@ def test_bf16_state_multi_and_commit(dtype):
 # 0.8, 0.99, 0.998 and 0.9998; the last (a memory of thousands of tokens) is the
 # case where one rounding per step no longer stays inside the 2e-2 bar, and its
 # bound records the measured level (2.4e-2) rather than the bar.
-BF16_STATE_STUDY = [(0.0, 256, BF16_REL), (-3.0, 256, BF16_REL), (-6.0, 384, BF16_REL),
-                    (-8.0, 2048, BF16_REL), (-10.0, 2048, 3e-2)]
+# (gate pre-activation mean, decode steps).  Row decays exp(-5 sigmoid(a)) of about
+# 0.08, 0.8, 0.99, 0.998 and 0.9998.  bf16 storage meets the bf16 bar (2e-2) while
+# the decays stay below about 0.998; at 0.9998 (memories of thousands of tokens) it
+# measured 2.4e-2: a documented limit of the flag (include/kda.h), kept as a
+# strict expected failure of the bar and bounded by the level test below.
+BF16_STATE_LIMIT = 3e-2
+BF16_STATE_STUDY = [(0.0, 256), (-3.0, 256), (-6.0, 384), (-8.0, 2048),
+                    pytest.param(-10.0, 2048, marks=pytest.mark.xfail(
+                        strict=True, raises=AssertionError,
+                        reason="known limit of bf16 state storage: row decays near 0.9998 "
+                               "measure 2.4e-2 against the 2e-2 bar"))]
 
 
-@pytest.mark.parametrize("gate_mean,L,bound", BF16_STATE_STUDY)
-def test_bf16_state_long_decode_accuracy(gate_mean, L, bound):
+def _bf16_state_errors(gate_mean, L):
     """L decode steps with the state stored as fp32 and as bf16 between steps, against
-    the fp64 oracle over the same tokens (relative L2 per (sequence, head), max)."""
+    the fp64 oracle over the same tokens (relative L2 per (sequence, head), max).
+    Returns (fp32-storage o error, bf16-storage o error, bf16 final-state error)."""
     N, H = 2, 4
     inp = KI.make_prefill(H, [L] * N, seed=90, device=DEV, gate_mean=gate_mean, state_std=0.1,
                           conv_cache_std=1.0)
@@ -304,8 +313,22 @@ def test_bf16_state_long_decode_accuracy(gate_mean, L, bound):
     e32 = slice_rel_errors(res[torch.float32][0], ref["o"], cu, H).max()
     e16 = slice_rel_errors(res[torch.bfloat16][0], ref["o"], cu, H).max()
     s16 = state_rel_errors(res[torch.bfloat16][1], ref["state"]).max()
+    return e32, e16, s16
+
+
+@pytest.mark.parametrize("gate_mean,L", BF16_STATE_STUDY)
+def test_bf16_state_long_decode_accuracy(gate_mean, L):
+    e32, e16, s16 = _bf16_state_errors(gate_mean, L)
     assert e32 <= BF16_REL, e32
-    assert e16 <= bound and s16 <= bound, (e16, s16)
+    assert e16 <= BF16_REL and s16 <= BF16_REL, (e16, s16)
+
+
+def test_bf16_state_near_one_decay_level():
+    """Where bf16 storage misses the bar (decays near 0.9998) its error stays at the
+    measured level rather than growing: each rounding decays with the state."""
+    e32, e16, s16 = _bf16_state_errors(-10.0, 2048)
+    assert e32 <= BF16_REL, e32
+    assert e16 <= BF16_STATE_LIMIT and s16 <= BF16_STATE_LIMIT, (e16, s16)
 
 
 @pytest.mark.parametrize("dtype,kw", [(torch.bfloat16, {"workspace": True}),
