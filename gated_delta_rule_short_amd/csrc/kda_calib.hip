@@ -8,8 +8,10 @@
 //     of 256 threads per 64 KiB fp32 state, each thread reading 16 float4 of
 //     whole 512-byte rows with non-temporal loads and writing them back in
 //     place after one multiply, the same mapping as the decode kernel.
-//   kda_calib_copy: dst = src, float4 per lane, non-temporal, grid-stride.
-//   kda_calib_fill: dst = value, float4 per lane, grid-stride.
+//   kda_calib_copy: dst = src, non-temporal, grid-stride, four float4 per lane
+//     in flight (the fastest copy shape of a launch sweep on this chip).
+//   kda_calib_fill: dst = value, non-temporal float4 stores, four per lane per
+//     iteration, grid-stride.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,22 +35,40 @@ __global__ void __launch_bounds__(256) state_rmw_kernel(float *state, float scal
     }
 }
 
+constexpr int kU = 4;  // float4 per lane per iteration
+
 __global__ void __launch_bounds__(256) copy_kernel(const f32x4c *src, f32x4c *dst, size_t n) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    const size_t stride = (size_t)gridDim.x * 256 * kU;
+    for (size_t base = (size_t)blockIdx.x * 256 * kU + threadIdx.x; base < n; base += stride) {
+        f32x4c v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const size_t i = base + (size_t)u * 256;
+            v[u] = i < n ? __builtin_nontemporal_load(src + i) : f32x4c{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const size_t i = base + (size_t)u * 256;
+            if (i < n) __builtin_nontemporal_store(v[u], dst + i);
+        }
+    }
 }
 
 __global__ void __launch_bounds__(256) fill_kernel(f32x4c *dst, size_t n, float value) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const size_t stride = (size_t)gridDim.x * 256 * kU;
     const f32x4c v = {value, value, value, value};
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = v;
+    for (size_t base = (size_t)blockIdx.x * 256 * kU + threadIdx.x; base < n; base += stride)
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const size_t i = base + (size_t)u * 256;
+            if (i < n) __builtin_nontemporal_store(v, dst + i);
+        }
 }
 
 unsigned grid_for(size_t n) {
-    // eight workgroups of 256 lanes per compute unit, at most one float4 per lane
-    const size_t want = (n + 255) / 256;
-    return (unsigned)(want < 2048 ? (want ? want : 1) : 2048);
+    // 16384 workgroups of 256 lanes (64 per compute unit) at most, four float4 per lane
+    const size_t want = (n + 256 * kU - 1) / (256 * kU);
+    return (unsigned)(want < 16384 ? (want ? want : 1) : 16384);
 }
 
 }  // namespace

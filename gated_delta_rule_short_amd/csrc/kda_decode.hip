@@ -9,18 +9,22 @@
 // "Serve rig": MTP with k = 5 drafted tokens) evaluates k + 1 tokens at once and
 // keeps an accepted prefix.
 //
-// One workgroup of 256 threads per (sequence, head).  A step is bound by HBM:
+// One workgroup of NT threads per (sequence, head).  A step is bound by HBM:
 // the 64 KiB state is read once and written once.  Thread t owns columns
-// 4*(t%32)..+3 of rows (t/32) + 8*m, m = 0..15: every load instruction of the
-// workgroup covers eight whole 512-byte rows (fully coalesced float4 accesses),
-// and the 64 state values stay in registers between the read and the write.
+// 4*(t%32)..+3 of rows (t/32) + (NT/32)*m: every load instruction of a wave
+// covers two whole 512-byte rows (fully coalesced float4 accesses), and the
+// state values stay in registers between the read and the write.  Single-token
+// decode uses NT = 512 (eight float4 per lane): the bare read-and-write-back of
+// 1 GiB of states streams at 5.7 TB/s on this chip that way, against 5.2 TB/s
+// with sixteen float4 per lane over 256 threads.  The multi-token verify and the
+// commit keep NT = 256, the faster layout for their longer per-state work.
 // The state loads are issued before the conv / L2 / gate prologue, so the
 // prologue runs under the memory latency.  Per column j with decayed rows
 // S'_i = alpha_i S_i:
 //     a_j = sum_i S'_ij k_i,  c_j = sum_i S'_ij q_i
 //     u_j = beta (v_j - a_j), o_j = scale (c_j + u_j (k . q)), S_ij = S'_ij + k_i u_j
 // The row sums reduce across the two row groups of a wave (lane xor 32) and
-// across the four waves through LDS.
+// across the waves through LDS.
 //
 // The multi-token kernel runs that step for each of T tokens on the state held
 // in registers and never writes it back; it writes per-token update records
@@ -38,6 +42,16 @@ namespace {
 
 constexpr int D = kHeadDim;
 constexpr int kMaxSpec = KDA_MAX_SPEC_TOKENS;
+
+// Thread layout of the state for NT threads per (sequence, head).
+template <int NT> struct Lay {
+    static constexpr int kWaves = NT / 64;
+    static constexpr int kRowStep = NT / 32;  // rows between a thread's state rows
+    static constexpr int kRows = D / kRowStep;  // state rows (float4 each) per thread
+    static_assert(kRows * kRowStep == D && 2 * D <= NT, "thread layout of the state");
+};
+constexpr int kDecodeThreads = 512;  // single-token decode
+constexpr int kMultiThreads = 256;   // multi-token verify and commit
 constexpr int kRec = KDA_UPDATE_FLOATS;  // floats per (sequence, head, token) record
 static_assert(KDA_UPDATE_FLOATS == 6 * kHeadDim, "record = six rows of dk");
 
@@ -75,25 +89,29 @@ __device__ __forceinline__ void norm_scales(const float (*red)[3], bool l2, floa
     kq = sqk * iq * ik;
 }
 
-// One token on this thread's 16 x 4 slice of the state (rows (tid/32) + 8m,
+// One token on this thread's slice of the state (rows (tid/32) + (NT/32) m,
 // columns 4 (tid%32)..+3).  sa, sk, sq: the token's decay, conv-ed key and query
 // for all 128 rows, in LDS; with PRESCALED they already carry their L2 scales
 // (ik, iq unused), else the step applies them (the same products either way).
-// vv: this thread's four v.  part: LDS for the cross-wave sums (must not be read
-// by a previous step that some thread may still be in).  Returns u; ov receives
-// the output columns.
-template <bool PRESCALED>
-__device__ __forceinline__ f32x4 token_step(f32x4 (&st)[16], const float *sa, const float *sk,
+// vv: this thread's four v.  part: LDS for the cross-wave partial sums.  With
+// four waves every thread adds the partials itself (part must not be read by a
+// previous step that some thread may still be in); with eight, wave 0 adds them
+// once into `tot` behind a second barrier, and the two barriers make one buffer
+// of each enough for consecutive calls.  Returns u; ov receives the output
+// columns.
+template <bool PRESCALED, int NT>
+__device__ __forceinline__ f32x4 token_step(f32x4 (&st)[Lay<NT>::kRows], const float *sa, const float *sk,
                                             const float *sq, f32x4 vv, float ik, float iq, float kq,
-                                            float beta, float scale, f32x4 (*part)[32][2], int tid,
-                                            f32x4 &ov) {
+                                            float beta, float scale, f32x4 (*part)[32][2],
+                                            f32x4 (*tot)[2], int tid, f32x4 &ov) {
 #pragma clang fp contract(off)
+    typedef Lay<NT> LY;
     const int cg = tid & 31, rg = tid >> 5, wave = tid >> 6;
     f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-    float krow[16];
+    float krow[LY::kRows];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int r = rg + 8 * m;
+    for (int m = 0; m < LY::kRows; ++m) {
+        const int r = rg + LY::kRowStep * m;
         const float kr = PRESCALED ? sk[r] : sk[r] * ik;
         const float qr = PRESCALED ? sq[r] : sq[r] * iq;
         krow[m] = kr;
@@ -108,24 +126,46 @@ __device__ __forceinline__ f32x4 token_step(f32x4 (&st)[16], const float *sa, co
     for (int e = 0; e < 4; ++e) red[e] = swap32_sum(ak[e], aq[e]);
     part[wave][cg][(tid >> 5) & 1] = red;
     barrier_lds();
-    const f32x4 s_k = part[0][cg][0] + part[1][cg][0] + part[2][cg][0] + part[3][cg][0];
-    const f32x4 s_q = part[0][cg][1] + part[1][cg][1] + part[2][cg][1] + part[3][cg][1];
+    f32x4 s_k, s_q;
+    if constexpr (LY::kWaves <= 4) {
+        s_k = part[0][cg][0];
+        s_q = part[0][cg][1];
+#pragma unroll
+        for (int w = 1; w < LY::kWaves; ++w) {
+            s_k = s_k + part[w][cg][0];
+            s_q = s_q + part[w][cg][1];
+        }
+    } else {
+        // wave 0 adds the waves' partials in wave order (lanes 0..31 the k sums,
+        // 32..63 the q sums of column group cg) once for the whole workgroup
+        if (wave == 0) {
+            const int half = tid >> 5;
+            f32x4 acc = part[0][cg][half];
+#pragma unroll
+            for (int w = 1; w < LY::kWaves; ++w) acc = acc + part[w][cg][half];
+            tot[cg][half] = acc;
+        }
+        barrier_lds();
+        s_k = tot[cg][0];
+        s_q = tot[cg][1];
+    }
     const f32x4 u = beta * (vv - s_k);
     ov = scale * (s_q + u * kq);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) st[m] = fma4(u, krow[m], st[m]);
+    for (int m = 0; m < LY::kRows; ++m) st[m] = fma4(u, krow[m], st[m]);
     return u;
 }
 
 // Replays one update record on this thread's slice: S <- diag(alpha) S + k u^T,
 // in the operation order token_step uses.
-__device__ __forceinline__ void replay_token(f32x4 (&st)[16], const float *alpha, const float *kn,
+template <int NT>
+__device__ __forceinline__ void replay_token(f32x4 (&st)[Lay<NT>::kRows], const float *alpha, const float *kn,
                                              f32x4 u, int tid) {
 #pragma clang fp contract(off)
     const int rg = tid >> 5;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int r = rg + 8 * m;
+    for (int m = 0; m < Lay<NT>::kRows; ++m) {
+        const int r = rg + Lay<NT>::kRowStep * m;
         st[m] = fma4(u, kn[r], st[m] * alpha[r]);
     }
 }
@@ -134,12 +174,12 @@ __device__ __forceinline__ void replay_token(f32x4 (&st)[16], const float *alpha
 // slice with non-temporal accesses: it is streamed exactly once each way, and
 // must not displace the small, reused operands in L2.  SB is the storage type:
 // fp32, or bf16 (widened exactly on load, rounded to nearest even on store).
-template <typename SB>
-__device__ __forceinline__ void load_state(f32x4 (&st)[16], const SB *S, int tid) {
+template <int NT, typename SB>
+__device__ __forceinline__ void load_state(f32x4 (&st)[Lay<NT>::kRows], const SB *S, int tid) {
     const int cg = tid & 31, rg = tid >> 5;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const SB *src = S + (size_t)(rg + 8 * m) * D + 4 * cg;
+    for (int m = 0; m < Lay<NT>::kRows; ++m) {
+        const SB *src = S + (size_t)(rg + Lay<NT>::kRowStep * m) * D + 4 * cg;
         if constexpr (sizeof(SB) == 4) {
             st[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src));
         } else {
@@ -151,12 +191,12 @@ __device__ __forceinline__ void load_state(f32x4 (&st)[16], const SB *S, int tid
     }
 }
 
-template <typename SB>
-__device__ __forceinline__ void store_state(const f32x4 (&st)[16], SB *S, int tid) {
+template <int NT, typename SB>
+__device__ __forceinline__ void store_state(const f32x4 (&st)[Lay<NT>::kRows], SB *S, int tid) {
     const int cg = tid & 31, rg = tid >> 5;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        SB *dst = S + (size_t)(rg + 8 * m) * D + 4 * cg;
+    for (int m = 0; m < Lay<NT>::kRows; ++m) {
+        SB *dst = S + (size_t)(rg + Lay<NT>::kRowStep * m) * D + 4 * cg;
         if constexpr (sizeof(SB) == 4)
             __builtin_nontemporal_store(st[m], reinterpret_cast<f32x4 *>(dst));
         else
@@ -199,8 +239,10 @@ struct DecodeParams {
 };
 
 template <typename T, typename SB>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) {
 #pragma clang fp contract(off)
+    constexpr int NTH = kDecodeThreads;
+    typedef Lay<NTH> LY;
     const int pr = blockIdx.x;
     const int H = p.H;
     const int n = pr / H, h = pr - n * H;
@@ -211,14 +253,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
 
     __shared__ __attribute__((aligned(16))) float s_q[D], s_k[D], s_v[D], s_alpha[D];
     __shared__ float s_red[2][3];
-    __shared__ f32x4 s_part[4][32][2];
+    __shared__ f32x4 s_part[LY::kWaves][32][2];
+    __shared__ f32x4 s_tot[32][2];
 
     // 1. issue the state loads (independent of the prologue).  The state is
     // streamed exactly once each way: non-temporal loads and stores keep it from
     // displacing the small, reused operands in L2.
     SB *S = reinterpret_cast<SB *>(p.state) + ((size_t)slot * H + h) * D * D;
-    f32x4 st[16];
-    load_state(st, S, tid);
+    f32x4 st[LY::kRows];
+    load_state<NTH>(st, S, tid);
 
     // 2. prologue: conv (and cache shift), L2 of q and k, gate
     const int CC = 3 * H * D;
@@ -237,6 +280,8 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
         cs[2 * CC + ch] = from_f32<T>(raw);
         return y;
     };
+    // threads 0..127: q and k channel c; 128..255: v channel c and the gate of row
+    // c; the others only hold state
     float part_qq = 0.f, part_kk = 0.f, part_qk = 0.f;
     if (tid < D) {
         const int c = tid;
@@ -247,7 +292,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
         part_qq = qc * qc;
         part_kk = kc * kc;
         part_qk = qc * kc;
-    } else {
+    } else if (tid < 2 * D) {
         const int c = tid - D;
         s_v[c] = conv(reinterpret_cast<const T *>(p.v), 2 * H * D + h * D + c);
         s_alpha[c] = gate_alpha(to_f32(reinterpret_cast<const T *>(p.gate)[tok + c]), p.lb, glog);
@@ -270,13 +315,13 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeParams p) {
     // 3. decay, S'^T k and S'^T q, delta-rule value, output, write-back
     const f32x4 vv = *reinterpret_cast<const f32x4 *>(&s_v[4 * cg]);
     f32x4 ov;
-    token_step<false>(st, s_alpha, s_k, s_q, vv, ik, iq, kq, beta, p.scale, s_part, tid, ov);
+    token_step<false, NTH>(st, s_alpha, s_k, s_q, vv, ik, iq, kq, beta, p.scale, s_part, s_tot, tid, ov);
     if (rg == 0) {
         T *o = reinterpret_cast<T *>(p.o) + tok + 4 * cg;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(ov[e]);
     }
-    store_state(st, S, tid);
+    store_state<NTH>(st, S, tid);
 }
 
 struct MultiParams {
@@ -296,8 +341,10 @@ struct MultiParams {
 };
 
 template <typename T, typename SB>
-__global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
+__global__ void __launch_bounds__(kMultiThreads) multi_kernel(MultiParams p) {
 #pragma clang fp contract(off)
+    constexpr int NTH = kMultiThreads, kThreads = NTH;
+    typedef Lay<NTH> LY;
     const int pr = blockIdx.x;
     const int H = p.H, NT = p.T;
     const int n = pr / H, h = pr - n * H;
@@ -311,13 +358,15 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
     __shared__ __attribute__((aligned(16))) float s_pend[kMaxSpec][3][D];
     __shared__ float s_red[kMaxSpec][2][3];
     __shared__ float s_beta[kMaxSpec];
-    __shared__ f32x4 s_part[2][4][32][2];
+    __shared__ f32x4 s_part[2][LY::kWaves][32][2];  // alternate tokens: one barrier per token
 
     // Every global load of the prologue is issued before any of them is used, so
     // the workgroup waits for memory once.  Threads 0..127 own q and k channel c,
-    // threads 128..255 v channel c and the gate of row c.
+    // threads 128..255 v channel c and the gate of row c; the others only hold
+    // state (`act` is false for them: they take no part in the prologue).
+    const bool act = tid < 2 * D;
     const bool qk = tid < D;
-    const int c = qk ? tid : tid - D;
+    const int c = qk ? tid : (act ? tid - D : 0);
     const int CC = 3 * H * D;
     const int ch0 = (qk ? 0 : 2 * H * D) + h * D + c;  // q or v channel
     const int ch1 = H * D + h * D + c;                  // k channel (q/k threads)
@@ -325,16 +374,21 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
     const size_t base = ((size_t)n * NT * H + h) * D;   // token 0 of this (sequence, head)
     const T *src0 = reinterpret_cast<const T *>(qk ? p.q : p.v);
     const T *src1 = reinterpret_cast<const T *>(qk ? p.k : p.gate);
-    T x0[kMaxSpec], x1[kMaxSpec];
+    T x0[kMaxSpec] = {}, x1[kMaxSpec] = {};
 #pragma unroll
     for (int t = 0; t < kMaxSpec; ++t) {
-        if (t < NT) {
+        if (act && t < NT) {
             x0[t] = src0[base + t * tstride + c];
             x1[t] = src1[base + t * tstride + c];
         }
     }
     T *cs = reinterpret_cast<T *>(p.cs) + (size_t)slot * 3 * CC;
-    const T cr0[3] = {cs[ch0], cs[CC + ch0], cs[2 * CC + ch0]};
+    T cr0[3] = {};
+    if (act) {
+        cr0[0] = cs[ch0];
+        cr0[1] = cs[CC + ch0];
+        cr0[2] = cs[2 * CC + ch0];
+    }
     T cr1[3] = {};
     if (qk) {
         cr1[0] = cs[ch1];
@@ -344,11 +398,12 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
     const f32x4 w0 = *reinterpret_cast<const f32x4 *>(p.w + 4 * ch0);
     const f32x4 w1 = *reinterpret_cast<const f32x4 *>(p.w + 4 * ch1);  // unused by v threads
     const float b0 = p.bias ? p.bias[ch0] : 0.f, b1 = p.bias ? p.bias[ch1] : 0.f;
-    if (!qk && c < NT) s_beta[c] = to_f32(reinterpret_cast<const T *>(p.beta)[((size_t)n * NT + c) * H + h]);
+    if (act && !qk && c < NT)
+        s_beta[c] = to_f32(reinterpret_cast<const T *>(p.beta)[((size_t)n * NT + c) * H + h]);
 
     SB *S = reinterpret_cast<SB *>(p.state) + ((size_t)slot * H + h) * D * D;
-    f32x4 st[16];
-    load_state(st, S, tid);
+    f32x4 st[LY::kRows];
+    load_state<NTH>(st, S, tid);
 
     // pending commit: the accepted prefix of the previous call's records
     int na = 0;
@@ -357,25 +412,27 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
         na = clamp_count(p.pacc[n], p.pT);
         prec = p.prec + (size_t)pr * p.pT * kRec;
         constexpr int per = 3 * D / 4;  // float4 of rows 0..2 per record
-        f32x4 pv[3];
+        constexpr int kPend = (kMaxSpec * per + kThreads - 1) / kThreads;
+        f32x4 pv[kPend];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int i = tid + 256 * j, t = i / per;
+        for (int j = 0; j < kPend; ++j) {
+            const int i = tid + kThreads * j, t = i / per;
             if (i < na * per) pv[j] = reinterpret_cast<const f32x4 *>(prec + (size_t)t * kRec)[i - t * per];
         }
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int i = tid + 256 * j, t = i / per;
+        for (int j = 0; j < kPend; ++j) {
+            const int i = tid + kThreads * j, t = i / per;
             if (i < na * per) reinterpret_cast<f32x4 *>(&s_pend[t][0][0])[i - t * per] = pv[j];
         }
     }
     // conv windows after the pending commit (stored back when it moved them)
-    float h0, h1, h2, g0 = 0.f, g1 = 0.f, g2 = 0.f;
-    committed_window(to_f32(cr0[0]), to_f32(cr0[1]), to_f32(cr0[2]), prec, qk ? 3 : 5, c, na, h0,
-                     h1, h2);
+    float h0 = 0.f, h1 = 0.f, h2 = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f;
+    if (act)
+        committed_window(to_f32(cr0[0]), to_f32(cr0[1]), to_f32(cr0[2]), prec, qk ? 3 : 5, c, na, h0,
+                         h1, h2);
     if (qk)
         committed_window(to_f32(cr1[0]), to_f32(cr1[1]), to_f32(cr1[2]), prec, 4, c, na, g0, g1, g2);
-    if (na > 0) {
+    if (act && na > 0) {
         cs[ch0] = from_f32<T>(h0);
         cs[CC + ch0] = from_f32<T>(h1);
         cs[2 * CC + ch0] = from_f32<T>(h2);
@@ -395,7 +452,7 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
     float *rec = p.rec + (size_t)pr * NT * kRec;
 #pragma unroll
     for (int t = 0; t < kMaxSpec; ++t) {
-        if (t < NT) {
+        if (act && t < NT) {
             float *rt = rec + (size_t)t * kRec;
             const float r0 = to_f32(x0[t]);
             const float y0 = conv4(wc0, b0, h0, h1, h2, r0, silu);
@@ -432,9 +489,9 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
     // apply the pending commit and store the committed state
     if (na > 0) {
         for (int t = 0; t < na; ++t)
-            replay_token(st, s_pend[t][0], s_pend[t][1],
-                         *reinterpret_cast<const f32x4 *>(&s_pend[t][2][4 * cg]), tid);
-        store_state(st, S, tid);
+            replay_token<NTH>(st, s_pend[t][0], s_pend[t][1],
+                              *reinterpret_cast<const f32x4 *>(&s_pend[t][2][4 * cg]), tid);
+        store_state<NTH>(st, S, tid);
     }
     // L2-normalised q and k of the new tokens, in place; k also into row 1 of
     // the records
@@ -457,8 +514,8 @@ __global__ void __launch_bounds__(256) multi_kernel(MultiParams p) {
         norm_scales(s_red[t], l2, iq, ik, kq);
         const f32x4 vv = *reinterpret_cast<const f32x4 *>(&s_v[t][4 * cg]);
         f32x4 ov;
-        const f32x4 u = token_step<true>(st, s_alpha[t], s_k[t], s_q[t], vv, ik, iq, kq, s_beta[t],
-                                         p.scale, s_part[t & 1], tid, ov);
+        const f32x4 u = token_step<true, NTH>(st, s_alpha[t], s_k[t], s_q[t], vv, ik, iq, kq, s_beta[t],
+                                              p.scale, s_part[t & 1], nullptr, tid, ov);
         if (rg == 0) {
             T *o = ob + t * tstride;
 #pragma unroll
@@ -479,8 +536,10 @@ struct CommitParams {
 };
 
 template <typename T, typename SB>
-__global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
+__global__ void __launch_bounds__(kMultiThreads) commit_kernel(CommitParams p) {
 #pragma clang fp contract(off)
+    constexpr int NTH = kMultiThreads, kThreads = NTH;
+    typedef Lay<NTH> LY;
     const int pr = blockIdx.x;
     const int H = p.H;
     const int n = pr / H, h = pr - n * H;
@@ -491,27 +550,29 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
 
     __shared__ __attribute__((aligned(16))) float s_pend[kMaxSpec][3][D];
     SB *S = reinterpret_cast<SB *>(p.state) + ((size_t)slot * H + h) * D * D;
-    f32x4 st[16];
-    load_state(st, S, tid);
+    f32x4 st[LY::kRows];
+    load_state<NTH>(st, S, tid);
     const float *rec = p.rec + (size_t)pr * p.T * kRec;
     // every load below is issued before any is used: the records' alpha, k and u
-    // rows (at most three float4 per thread), then this thread's conv channels
-    // (i = tid and tid + 256 of the head's 3 x 128: their cached taps and the raw
-    // rows of the last three accepted tokens)
+    // rows (at most kPend float4 per thread), then this thread's conv channel
+    // (i = tid of the head's 3 x 128: its cached taps and the raw rows of the last
+    // three accepted tokens)
     constexpr int per = 3 * D / 4;
-    f32x4 pv[3];
+    constexpr int kPend = (kMaxSpec * per + kThreads - 1) / kThreads;
+    constexpr int kConvPer = (3 * D + kThreads - 1) / kThreads;  // conv channels per thread
+    f32x4 pv[kPend];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int i = tid + 256 * j, t = i / per;
+    for (int j = 0; j < kPend; ++j) {
+        const int i = tid + kThreads * j, t = i / per;
         if (i < na * per) pv[j] = reinterpret_cast<const f32x4 *>(rec + (size_t)t * kRec)[i - t * per];
     }
     const int CC = 3 * H * D;
     T *cs = reinterpret_cast<T *>(p.cs) + (size_t)slot * 3 * CC;
-    T cr[2][3];
-    float hw[2][3];
+    T cr[kConvPer][3];
+    float hw[kConvPer][3];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int i = tid + 256 * q;
+    for (int q = 0; q < kConvPer; ++q) {
+        const int i = tid + kThreads * q;
         if (i < 3 * D) {
             const int part = i / D, c = i - part * D;  // 0 q, 1 k, 2 v
             const int ch = part * H * D + h * D + c;
@@ -523,13 +584,13 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
         }
     }
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int i = tid + 256 * j, t = i / per;
+    for (int j = 0; j < kPend; ++j) {
+        const int i = tid + kThreads * j, t = i / per;
         if (i < na * per) reinterpret_cast<f32x4 *>(&s_pend[t][0][0])[i - t * per] = pv[j];
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int i = tid + 256 * q;
+    for (int q = 0; q < kConvPer; ++q) {
+        const int i = tid + kThreads * q;
         if (i < 3 * D) {
             const int part = i / D, c = i - part * D;
             const int ch = part * H * D + h * D + c;
@@ -540,21 +601,22 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitParams p) {
     }
     barrier_lds();
     for (int t = 0; t < na; ++t)
-        replay_token(st, s_pend[t][0], s_pend[t][1],
-                     *reinterpret_cast<const f32x4 *>(&s_pend[t][2][4 * cg]), tid);
-    store_state(st, S, tid);
+        replay_token<NTH>(st, s_pend[t][0], s_pend[t][1],
+                          *reinterpret_cast<const f32x4 *>(&s_pend[t][2][4 * cg]), tid);
+    store_state<NTH>(st, S, tid);
 }
 
-// Launch of the instance for (token dtype, state storage): one workgroup of 256
-// threads per (sequence, head).
+// Launch of the instance for (token dtype, state storage): one workgroup of
+// `threads` threads per (sequence, head).
 template <typename P>
-static void launch_typed(const char *name, kda_dtype dt, uint32_t flags, unsigned blocks, const P &p,
-                         hipStream_t s, void (*bb)(P), void (*bf)(P), void (*fb)(P), void (*ff)(P)) {
+static void launch_typed(const char *name, int threads, kda_dtype dt, uint32_t flags, unsigned blocks,
+                         const P &p, hipStream_t s, void (*bb)(P), void (*bf)(P), void (*fb)(P),
+                         void (*ff)(P)) {
     const bool sb16 = flags & KDA_F_STATE_BF16;
     void (*k)(P) = dt == KDA_BF16 ? (sb16 ? bb : bf) : (sb16 ? fb : ff);
-    hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, s, p);
-    trace("%s<tokens %s, state %s> grid=(%u) block=256 lds=0", name, dt == KDA_BF16 ? "bf16" : "f32",
-          sb16 ? "bf16" : "f32", blocks);
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(threads), 0, s, p);
+    trace("%s<tokens %s, state %s> grid=(%u) block=%d lds=0", name, dt == KDA_BF16 ? "bf16" : "f32",
+          sb16 ? "bf16" : "f32", blocks, threads);
 }
 
 hipError_t launch_decode(const kda_decode_args *a, hipStream_t s) {
@@ -566,7 +628,7 @@ hipError_t launch_decode(const kda_decode_args *a, hipStream_t s) {
     p.H = a->num_heads;
     p.scale = a->scale; p.lb = a->gate_lower_bound; p.flags = a->flags;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    launch_typed<DecodeParams>("decode_kernel", a->dtype, a->flags, blocks, p, s,
+    launch_typed<DecodeParams>("decode_kernel", kDecodeThreads, a->dtype, a->flags, blocks, p, s,
                      decode_kernel<__bf16, __bf16>, decode_kernel<__bf16, float>, decode_kernel<float, __bf16>, decode_kernel<float, float>);
     return hipGetLastError();
 }
@@ -581,7 +643,7 @@ hipError_t launch_decode_multi(const kda_decode_multi_args *a, hipStream_t s) {
     p.H = a->num_heads; p.T = a->num_tokens; p.pT = a->pending_updates ? a->pending_tokens : 0;
     p.scale = a->scale; p.lb = a->gate_lower_bound; p.flags = a->flags;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    launch_typed<MultiParams>("multi_kernel", a->dtype, a->flags, blocks, p, s,
+    launch_typed<MultiParams>("multi_kernel", kMultiThreads, a->dtype, a->flags, blocks, p, s,
                      multi_kernel<__bf16, __bf16>, multi_kernel<__bf16, float>, multi_kernel<float, __bf16>, multi_kernel<float, float>);
     return hipGetLastError();
 }
@@ -592,7 +654,7 @@ hipError_t launch_decode_commit(const kda_decode_commit_args *a, hipStream_t s) 
     p.slots = a->state_slots; p.num_slots = a->num_slots;
     p.H = a->num_heads; p.T = a->num_tokens;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    launch_typed<CommitParams>("commit_kernel", a->dtype, a->flags, blocks, p, s,
+    launch_typed<CommitParams>("commit_kernel", kMultiThreads, a->dtype, a->flags, blocks, p, s,
                      commit_kernel<__bf16, __bf16>, commit_kernel<__bf16, float>, commit_kernel<float, __bf16>, commit_kernel<float, float>);
     return hipGetLastError();
 }

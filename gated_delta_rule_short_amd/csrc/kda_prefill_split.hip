@@ -645,10 +645,9 @@ __device__ __forceinline__ void scan_wait(int later) {
 // per-stage count PER is a constant.  Stages and record pointers advance
 // incrementally; in the steady state the wait is a constant vmcnt, and the
 // dispatch over the in-flight count runs only before B_-1 and in the tail.
-template <int NTW, int PW>
+template <class G, int PW>
 __device__ __forceinline__ void producer_run(unsigned char *ring, const unsigned char *rec0, int nt0, int lane,
                                              int J) {
-    typedef ScanGeom<NTW> G;
     constexpr int NS = G::NS, NP = G::NP, PER = G::inst_of(PW);
     auto issue = [&](int slot, const unsigned char *rec) {
         unsigned char *st = ring + slot * G::kStage;
@@ -685,15 +684,15 @@ __device__ __forceinline__ void producer_run(unsigned char *ring, const unsigned
     wait_vmcnt<0>();
 }
 
-template <int NTW, int K = 0>
+template <class G, int K = 0>
 __device__ __forceinline__ void producer_dispatch(int pw, unsigned char *ring, const unsigned char *rec0, int nt0,
                                                   int lane, int J) {
-    if constexpr (K < ScanGeom<NTW>::NP) {
+    if constexpr (K < G::NP) {
         if (pw == K) {
-            producer_run<NTW, K>(ring, rec0, nt0, lane, J);
+            producer_run<G, K>(ring, rec0, nt0, lane, J);
             return;
         }
-        producer_dispatch<NTW, K + 1>(pw, ring, rec0, nt0, lane, J);
+        producer_dispatch<G, K + 1>(pw, ring, rec0, nt0, lane, J);
     }
 }
 
@@ -731,7 +730,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
         // ---------------- producers
         // bare barriers throughout: a fence would drain all DMA in flight
         if (J == 0) return;
-        producer_dispatch<NTW>(w - 2 * NTW, ring, rec0, nt0, lane, (int)J);
+        producer_dispatch<G>(w - 2 * NTW, ring, rec0, nt0, lane, (int)J);
         return;
     }
 
@@ -905,6 +904,227 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
     }
 }
 
+// Pass B for many (sequence, head) pairs: one workgroup per pair covering all 128
+// dv columns, so each record crosses HBM and LDS once.  kRW recurrence waves hold
+// two 16-column tiles of the state each (64 fp32 per lane) and also form the
+// output of their columns; NP producer waves fill an NS-stage ring of whole
+// records.  With enough pairs to fill every compute unit, per-step latency is
+// hidden by the other workgroups' memory traffic and the kernel streams the
+// records at the bandwidth the workgroups can draw, so the output products that
+// a separate wave would take off the recurrence's chain stay in the same wave
+// and no exchange area is needed.
+struct WideGeom {
+    static constexpr int kStage = (int)kRec;
+    static constexpr int kInst = (kStage + 1023) / 1024;  // DMA instructions per stage
+    static constexpr int NP = KDA_SCAN_PRODUCERS;
+    static constexpr int inst_of(int pw) { return (kInst + NP - 1 - pw) / NP; }
+    static constexpr int kInstP0 = (kInst + NP - 1) / NP;  // inst_of(0)
+    static constexpr int kRW = 4;                          // recurrence waves, two tiles each
+    static constexpr int kWaves = kRW + NP;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int NSfit = 163840 / kStage;
+    static constexpr int NS = NSfit < 10 ? NSfit : 10;
+    static constexpr int kLds = NS * kStage;
+    static constexpr int kMaxLater = NS - 3;
+    static_assert(kStage % 1024 == 0, "stages move in whole DMA KiB");
+    static_assert(2 * kRW * 16 == kHeadDim, "the recurrence waves cover every dv column");
+    static_assert(NS >= 4, "the ring holds the stages of steps j - 1, j, j + 1 and the refill");
+    static_assert(kInstP0 * kMaxLater < 64, "in-flight DMA exceeds the vmcnt range");
+    static_assert(NP >= 1 && NP <= 8 && kWaves <= 16, "producers");
+};
+
+// Barriers as in scan_kernel (B_-1, then B_j for j = 0 .. J; at B_j stage j + 1
+// is in LDS, and after it the producers refill the slot of stage j - 2).  During
+// step j the recurrence waves compute step j from registers read from stage j
+// and read stage j + 1.
+__global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitParams p) {
+    typedef WideGeom G;
+    constexpr int D = kHeadDim, NS = G::NS;
+    extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int m16 = lane & 15, g4 = lane >> 4;
+    const int pr = blockIdx.x;
+    if (pr >= p.pairs) return;  // whole workgroup: no barrier is left waiting
+    const int H = p.H;
+    const int n = pr / H, h = pr - n * H;
+    const int slot = pool_slot(p.slots, p.num_slots, n);
+    if (slot < 0) return;  // whole workgroup: no barrier is left waiting
+    const size_t spr = (size_t)slot * H + h;
+    int64_t s0, L;
+    seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
+    const int64_t J = (L + 15) / 16;
+    const unsigned char *rec0 =
+        p.ws + ((size_t)h * p.nslots + (J > 0 ? sub_slot(s0, 0, n) : 0)) * kRec;
+
+    if (w >= G::kRW) {
+        // ---------------- producers (bare barriers: a fence would drain the DMA)
+        if (J == 0) return;
+        producer_dispatch<G>(w - G::kRW, ring, rec0, 0, lane, (int)J);
+        return;
+    }
+
+    // ---------------- recurrence and output on tiles 2w, 2w + 1 (columns 32w ..)
+    //   U = U0 - W S,  O = scale (Q~ S + P U),  S = diag(gam) S + Kd^T U
+    // S[t][m] holds rows 16 m + 4 g4 + i of column col[t] (accumulator layout).
+    int col[2];
+    col[0] = 32 * w + m16;
+    col[1] = 32 * w + 16 + m16;
+    f32x4 S[2][8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (p.state_in && p.state_bf16) {
+            const __bf16 *sin = reinterpret_cast<const __bf16 *>(p.state_in) + spr * D * D + col[t];
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[t][m][i] = (float)sin[(16 * m + 4 * g4 + i) * D];
+        } else if (p.state_in) {
+            const float *sin = reinterpret_cast<const float *>(p.state_in) + spr * D * D + col[t];
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[t][m][i] = sin[(16 * m + 4 * g4 + i) * D];
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) S[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    if (J > 0) {
+        const int64_t tokstride = (int64_t)H * D;
+        __bf16 *ob = reinterpret_cast<__bf16 *>(p.o) + ((size_t)s0 * tokstride + (size_t)h * D);
+        const uint32_t loff = (uint32_t)col[0] + 4u * (uint32_t)g4 * (uint32_t)tokstride;
+        int rslot = 1 % NS;  // ring slot of stage j + 1 during step j
+        struct Ops {
+            bf16x8 wn[4], qg[4];
+            bf16x4 kd[8], u0[2], pp;
+            float gv[2];
+        };
+        auto load = [&](const unsigned char *st, Ops &o) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                o.wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + (t * 64 + lane) * 16);
+                o.qg[t] = *reinterpret_cast<const bf16x8 *>(st + R_QG + (t * 64 + lane) * 16);
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                o.kd[m] = *reinterpret_cast<const bf16x4 *>(st + R_KD + (m * 64 + lane) * 8);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                o.gv[q] = *reinterpret_cast<const float *>(
+                    st + R_GAM + (64 * q + 16 * (m16 >> 2) + 4 * g4 + (m16 & 3)) * 4);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                o.u0[t] = *reinterpret_cast<const bf16x4 *>(st + R_U0 + ((2 * w + t) * 64 + lane) * 8);
+            o.pp = *reinterpret_cast<const bf16x4 *>(st + R_PP + lane * 8);
+        };
+        auto step = [&](int64_t j, const Ops &c, Ops &nx) {
+            barrier_lds();  // B_j
+            __builtin_amdgcn_sched_barrier(0);
+            // (past the last step this reads a stale stage: harmless)
+            load(ring + rslot * G::kStage, nx);
+            rslot = rslot + 1 == NS ? 0 : rslot + 1;
+            bf16x8 Sp[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Sp[t][q] = join8(pack4(S[t][2 * q]), pack4(S[t][2 * q + 1]));
+            f32x4 Ua[2], Uc[2], O[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                Ua[t] = f32x4{(float)c.u0[t].x, (float)c.u0[t].y, (float)c.u0[t].z, (float)c.u0[t].w};
+                Uc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            // four independent U chains (two per tile), then the output products
+#pragma unroll
+            for (int q = 0; q < 4; q += 2)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    Ua[t] = mma_k32(c.wn[q], Sp[t][q], Ua[t]);
+                    Uc[t] = mma_k32(c.wn[q + 1], Sp[t][q + 1], Uc[t]);
+                }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) O[t] = mma_k32(c.qg[q], Sp[t][q], O[t]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                decay_tile<0>(S[t][0], c.gv);
+                decay_tile<1>(S[t][1], c.gv);
+                decay_tile<2>(S[t][2], c.gv);
+                decay_tile<3>(S[t][3], c.gv);
+                decay_tile<4>(S[t][4], c.gv);
+                decay_tile<5>(S[t][5], c.gv);
+                decay_tile<6>(S[t][6], c.gv);
+                decay_tile<7>(S[t][7], c.gv);
+            }
+            bf16x4 Ub[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) Ub[t] = pack4(Ua[t] + Uc[t]);
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) S[t][m] = mma_k16(c.kd[m], Ub[t], S[t][m]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) O[t] = mma_k16w(c.pp, Ub[t], O[t]);  // after K = 32 steps
+            __bf16 *orow = ob + (size_t)(16 * j) * tokstride;
+            if (16 * j + 16 <= L) {  // the whole sub-chunk lies in the sequence
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)(p.scale * O[t][i]);
+            } else {
+                const int64_t r0 = 16 * j + 4 * g4;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (r0 + i < L) (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)(p.scale * O[t][i]);
+            }
+        };
+        Ops A, B;
+        barrier_lds();  // B_-1
+        load(ring, A);  // stage 0 sits in slot 0
+        int64_t j = 0;
+        for (; j + 1 < J; j += 2) {
+            step(j, A, B);
+            step(j + 1, B, A);
+        }
+        if (j < J) step(j, A, B);
+        barrier_lds();  // B_J
+    }
+    if (p.state_out) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t at = (spr * D + 16 * m + 4 * g4 + i) * D + col[t];
+                    if (p.state_bf16)
+                        reinterpret_cast<__bf16 *>(p.state_out)[at] = (__bf16)S[t][m][i];
+                    else
+                        reinterpret_cast<float *>(p.state_out)[at] = S[t][m][i];
+                }
+    }
+}
+
+hipError_t launch_scan_wide(const SplitParams &sp, hipStream_t s) {
+    typedef WideGeom G;
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_wide_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
+    });
+    if (attr != hipSuccess) return attr;
+    const unsigned blocks = (unsigned)sp.pairs;
+    hipLaunchKernelGGL(scan_wide_kernel, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
+    trace("scan_wide_kernel grid=(%u) block=%d lds=%d ring=%d", blocks, G::kThreads, G::kLds, G::NS);
+    return hipGetLastError();
+}
+
 template <int NTW>
 hipError_t launch_scan(const SplitParams &sp, hipStream_t s) {
     typedef ScanGeom<NTW> G;
@@ -941,7 +1161,10 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
     sp.pairs = a->num_seqs * a->num_heads;
     sp.a_heads_fast = 0;
     sp.a_stride = 0;
-    if (dv_tile > 32) dv_tile = 32;  // at most two dv tiles of 16 columns per workgroup
+    // 128 columns per workgroup: the wide pass B; otherwise at most two dv tiles of
+    // 16 columns per workgroup
+    const bool wide = dv_tile == kHeadDim;
+    if (!wide && dv_tile > 32) dv_tile = 32;
     sp.tiles = kHeadDim / dv_tile;
     if (a->total_tokens > 0) {
         static std::once_flag once;
@@ -967,6 +1190,7 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (wide) return launch_scan_wide(sp, s);
     return dv_tile == 16 ? launch_scan<1>(sp, s) : launch_scan<2>(sp, s);
 }
 

@@ -252,8 +252,11 @@ kda_status kda_decode(const kda_decode_args *args, hipStream_t stream);
  * from those records.  The same commit can be fused into the next
  * kda_decode_multi call (the `pending_*` fields), so that a steady-state
  * speculative step reads and writes each state once.  Given the same inputs,
- * the outputs and the committed state and conv cache are bit-identical to
- * those of that many kda_decode calls.
+ * the outputs and the committed state equal those of that many kda_decode calls
+ * up to the order of fp32 additions (kda_decode spreads a state over more
+ * threads and groups the 128-row column sums differently), and the conv cache
+ * equals theirs exactly; a commit fused into the next kda_decode_multi call
+ * equals a separate kda_decode_commit bit for bit.
  *
  * Update record of (sequence n, head h, token t): KDA_UPDATE_ROWS rows of 128
  * fp32 at updates + ((n * H + h) * T + t) * KDA_UPDATE_FLOATS:
