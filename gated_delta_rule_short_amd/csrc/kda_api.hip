@@ -99,6 +99,34 @@ kda_status check_written(const Buf *b, int n, int n_written) {
     return KDA_OK;
 }
 
+// The two-pass schedule applies to bf16 I/O with chunk_size 0 or 16.
+bool two_pass_applies(const kda_prefill_args *a) {
+    return a && a->dtype == KDA_BF16 && (a->chunk_size == 0 || a->chunk_size == 16) && a->num_seqs >= 1 &&
+           a->num_heads >= 1 && a->total_tokens >= 0;
+}
+
+// Most 16-token sub-chunks of any sequence: from the host copy of cu_seqlens
+// when given (already validated), else an upper bound.
+int64_t max_subchunks(const kda_prefill_args *a) {
+    if (a->cu_seqlens_host) {
+        int64_t m = 0;
+        for (int32_t n = 0; n < a->num_seqs; ++n) {
+            const int64_t L = (int64_t)a->cu_seqlens_host[n + 1] - a->cu_seqlens_host[n];
+            m = L > m ? L : m;
+        }
+        return (m + 15) / 16;
+    }
+    if (!a->cu_seqlens) return (a->total_tokens / a->num_seqs + 15) / 16;
+    return (a->total_tokens + 15) / 16;
+}
+
+// Sub-chunks per sequence per window that `bytes` of workspace hold (0: none).
+int64_t window_subchunks(const kda_prefill_args *a, size_t bytes) {
+    const size_t carry = kda::split_carry_bytes(a->num_seqs, a->num_heads);
+    const size_t per = kda::split_window_bytes(a->num_seqs, a->num_heads, 1) - carry;
+    return bytes > carry ? (int64_t)((bytes - carry) / per) : 0;
+}
+
 }  // namespace
 
 namespace kda {
@@ -193,9 +221,27 @@ kda_status kda_short_conv(const void *x, void *y, int64_t total_tokens, int32_t 
 }
 
 size_t kda_prefill_workspace_size(const kda_prefill_args *a) {
-    if (!a || a->dtype != KDA_BF16 || (a->chunk_size != 0 && a->chunk_size != 16)) return 0;
-    if (a->num_seqs < 1 || a->num_heads < 1 || a->total_tokens < 0) return 0;
+    if (!two_pass_applies(a)) return 0;
+    const size_t full = kda::split_workspace_bytes(a->total_tokens, a->num_seqs, a->num_heads);
+    if (full <= KDA_PREFILL_WORKSPACE_CAP) return full;
+    int64_t jw = window_subchunks(a, KDA_PREFILL_WORKSPACE_CAP);
+    if (jw < 1) jw = 1;
+    const int64_t mj = max_subchunks(a);
+    if (jw > mj) jw = mj > 0 ? mj : 1;
+    const size_t win = kda::split_window_bytes(a->num_seqs, a->num_heads, jw);
+    return win < full ? win : full;
+}
+
+size_t kda_prefill_workspace_full_size(const kda_prefill_args *a) {
+    if (!two_pass_applies(a)) return 0;
     return kda::split_workspace_bytes(a->total_tokens, a->num_seqs, a->num_heads);
+}
+
+size_t kda_prefill_workspace_min_size(const kda_prefill_args *a) {
+    if (!two_pass_applies(a)) return 0;
+    const size_t full = kda::split_workspace_bytes(a->total_tokens, a->num_seqs, a->num_heads);
+    const size_t one = kda::split_window_bytes(a->num_seqs, a->num_heads, 1);
+    return one < full ? one : full;
 }
 
 kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
@@ -235,8 +281,25 @@ kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
     if (a->conv_state_out && a->conv_state_out != a->conv_state_in &&
         overlap(a->conv_state_out, csb, a->conv_state_in, csb))
         return fail(KDA_ERR_INVALID_ARG, "conv_state_out partially overlaps conv_state_in");
-    const size_t need = kda_prefill_workspace_size(a);
-    const bool two_pass = need > 0 && a->workspace && a->workspace_bytes >= need;
+    // schedule: two passes when a workspace is given and the two-pass schedule
+    // applies; windows when the workspace holds less than the whole call
+    const bool two_pass = two_pass_applies(a) && a->workspace;
+    kda::SplitPlan plan{0, 1};
+    if (two_pass) {
+        const size_t need_min = kda_prefill_workspace_min_size(a);
+        if (a->workspace_bytes < need_min)
+            return fail(KDA_ERR_INVALID_ARG, "workspace of %zu bytes: the two-pass schedule needs at least "
+                                             "%zu (kda_prefill_workspace_min_size)", a->workspace_bytes, need_min);
+        const size_t full = kda::split_workspace_bytes(T, a->num_seqs, a->num_heads);
+        if (a->workspace_bytes < full) {
+            const int64_t mj = max_subchunks(a);
+            int64_t jw = window_subchunks(a, a->workspace_bytes);
+            if (jw > mj) jw = mj;
+            if (jw < 1) jw = 1;
+            plan.jw = jw;
+            plan.windows = mj > 0 ? (mj + jw - 1) / jw : 1;
+        }
+    }
     const size_t wb = two_pass ? a->workspace_bytes : 0;
     const int N = a->num_seqs;
     const size_t CC = (size_t)3 * H * 128;
@@ -273,7 +336,7 @@ kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
     }
     hipError_t e;
     if (two_pass) {
-        e = kda::launch_prefill_split(&args, dv_tile, stream);
+        e = kda::launch_prefill_split(&args, dv_tile, plan, stream);
     } else {
         kda::PrefillLaunch pl{&args, chunk, dv_tile};
         e = kda::launch_prefill(pl, stream);

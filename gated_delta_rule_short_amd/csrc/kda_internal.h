@@ -46,8 +46,16 @@ hipError_t launch_decode(const kda_decode_args *a, hipStream_t s);
 hipError_t launch_decode_multi(const kda_decode_multi_args *a, hipStream_t s);
 hipError_t launch_decode_commit(const kda_decode_commit_args *a, hipStream_t s);
 
-// Two-pass prefill (bf16 I/O, 16-token sub-chunks) and its workspace size.
+// Two-pass prefill (bf16 I/O, 16-token sub-chunks).  Workspace for the whole call
+// in one window (packed slots), and for windows of jw sub-chunks per sequence
+// (the window's records, then the fp32 carry of every (sequence, head) state).
 size_t split_workspace_bytes(int64_t total_tokens, int num_seqs, int H);
-hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStream_t s);
+size_t split_window_bytes(int num_seqs, int H, int64_t jw);
+size_t split_carry_bytes(int num_seqs, int H);
+struct SplitPlan {
+    int64_t jw;       // sub-chunks per sequence per window; 0: one window, packed slots
+    int64_t windows;  // windows to run when jw > 0
+};
+hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, const SplitPlan &plan, hipStream_t s);
 
 }  // namespace kda

@@ -75,6 +75,12 @@ struct SplitParams {
     int pairs, tiles;
     int a_heads_fast;  // pass-A grid: heads in x (slot groups in y), else the reverse
     int64_t a_stride;  // pass A: slot distance between a wave's two tasks (4 x slot groups)
+    // Windows (jw > 0): the call runs in windows of jw sub-chunks of every sequence;
+    // window `win` covers sub-chunks win * jw .. win * jw + jw - 1 of each sequence,
+    // in slots n * jw + (j - win * jw), and the fp32 state of each (sequence, head)
+    // waits in `carry` ([N][H][128][128]) from one window to the next.
+    int64_t jw, win;
+    float *carry;
 };
 
 // Slot of sub-chunk j of sequence n (start s0): distinct for all (n, j) and
@@ -528,6 +534,19 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 // second one's rows while it computes the first.  Two slots in straight-line
 // code: a loop over more slots keeps loop-invariant values live and spills.
 __device__ __forceinline__ bool next_task(const SplitParams &p, int64_t slot, int64_t stride, SubTask &tk) {
+    if (p.jw > 0) {  // windows: slot n * jw + i holds sub-chunk win * jw + i of sequence n
+        for (; slot < p.nslots; slot += stride) {
+            const int n = (int)(slot / p.jw);
+            const int64_t j = p.win * p.jw + (slot - (int64_t)n * p.jw);
+            int64_t s0, L;
+            seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
+            if (16 * j < L) {
+                tk.slot = slot; tk.s0 = s0; tk.L = L; tk.j = j; tk.n = n;
+                return true;
+            }
+        }
+        return false;
+    }
     for (; slot < p.nslots; slot += stride) {
         int lo = 0, hi = p.num_seqs - 1;
         while (lo < hi) {
@@ -696,6 +715,94 @@ __device__ __forceinline__ void producer_dispatch(int pw, unsigned char *ring, c
     }
 }
 
+// What one pass-B workgroup does in this call for sequence n, head h (pool row
+// slot): its steps (sub-chunks j0 .. j0 + steps - 1), where its state comes from
+// and goes to, and its first record.  Without windows that is the whole
+// sequence, from state_in (or zeros) to state_out.  With windows, window 0 starts
+// from state_in, later ones from the carry, and a window that does not hold the
+// sequence's last sub-chunk leaves the state in the carry.  Returns false when the
+// sequence has nothing in this window (an empty sequence passes its state through
+// in window 0); the caller's whole workgroup then exits before any barrier.
+struct PairWork {
+    int64_t s0, L, j0, steps;
+    const void *sin;
+    void *sout;
+    size_t sin_row, sout_row;
+    bool sin16, sout16;
+    const unsigned char *rec0;
+};
+__device__ __forceinline__ bool pair_work(const SplitParams &p, int n, int h, int slot, PairWork &w) {
+    seq_bounds(p.cu, p.total, p.num_seqs, n, w.s0, w.L);
+    const int64_t J = (w.L + 15) / 16;
+    const size_t spr = (size_t)slot * p.H + h;
+    w.sin = p.state_in;
+    w.sout = p.state_out;
+    w.sin_row = w.sout_row = spr;
+    w.sin16 = w.sout16 = p.state_bf16 != 0;
+    w.j0 = 0;
+    w.steps = J;
+    int64_t first = J > 0 ? sub_slot(w.s0, 0, n) : 0;
+    if (p.jw > 0) {
+        w.j0 = p.win * p.jw;
+        if (w.j0 >= J && !(p.win == 0 && J == 0)) return false;
+        const int64_t j1 = J < w.j0 + p.jw ? J : w.j0 + p.jw;
+        w.steps = j1 > w.j0 ? j1 - w.j0 : 0;
+        const size_t crow = (size_t)n * p.H + h;
+        if (p.win > 0) {
+            w.sin = p.carry;
+            w.sin_row = crow;
+            w.sin16 = false;
+        }
+        if (j1 < J) {
+            w.sout = p.carry;
+            w.sout_row = crow;
+            w.sout16 = false;
+        }
+        first = (int64_t)n * p.jw;
+    }
+    w.rec0 = p.ws + ((size_t)h * p.nslots + first) * kRec;
+    return true;
+}
+
+// Rows 16 m + 4 g4 + i of state column col, accumulator layout, from or to state
+// row `row` (fp32, or bf16 widened exactly / rounded to nearest even); a null
+// source gives zeros, a null destination is not written.
+__device__ __forceinline__ void load_state_tile(f32x4 (&S)[8], const void *src, size_t row, bool bf16, int col,
+                                                int g4) {
+    constexpr int D = kHeadDim;
+    if (src && bf16) {
+        const __bf16 *sin = reinterpret_cast<const __bf16 *>(src) + row * D * D + col;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[m][i] = (float)sin[(16 * m + 4 * g4 + i) * D];
+    } else if (src) {
+        const float *sin = reinterpret_cast<const float *>(src) + row * D * D + col;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[m][i] = sin[(16 * m + 4 * g4 + i) * D];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+__device__ __forceinline__ void store_state_tile(const f32x4 (&S)[8], void *dst, size_t row, bool bf16, int col,
+                                                 int g4) {
+    constexpr int D = kHeadDim;
+    if (!dst) return;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const size_t at = (row * D + 16 * m + 4 * g4 + i) * D + col;
+            if (bf16)
+                reinterpret_cast<__bf16 *>(dst)[at] = (__bf16)S[m][i];
+            else
+                reinterpret_cast<float *>(dst)[at] = S[m][i];
+        }
+}
+
 // Barriers, taken by every wave: B_-1, then B_j for j = 0 .. J.  At B_-1
 // stage 0 is in LDS; at B_j stage j + 1 is (when j + 1 < J).  During step j
 // the R waves compute from registers read from stage j and read stage j + 1;
@@ -717,13 +824,11 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
     const int n = pr / H, h = pr - n * H;
     const int slot = pool_slot(p.slots, p.num_slots, n);
     if (slot < 0) return;  // whole workgroup: no barrier is left waiting
-    const size_t spr = (size_t)slot * H + h;  // pool row of this (sequence, head)
-    int64_t s0, L;
-    seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
-    const int64_t J = (L + 15) / 16;
+    PairWork pw;
+    if (!pair_work(p, n, h, slot, pw)) return;  // whole workgroup: no barrier is left waiting
+    const int64_t s0 = pw.s0, L = pw.L, j0 = pw.j0, J = pw.steps;
     const int nt0 = tile * NTW;
-    const unsigned char *rec0 =
-        p.ws + ((size_t)h * p.nslots + (J > 0 ? sub_slot(s0, 0, n) : 0)) * kRec;
+    const unsigned char *rec0 = pw.rec0;
     auto stage = [&](int64_t j) { return ring + ((uint32_t)j % NS) * G::kStage; };
 
     if (w >= 2 * NTW) {
@@ -745,22 +850,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
         //   U = U0 - W S, S = diag(gam) S + Kd^T U
         // S[m] holds rows 16 m + 4 g4 + i of column col (accumulator layout).
         f32x4 S[8];
-        if (p.state_in && p.state_bf16) {
-            const __bf16 *sin = reinterpret_cast<const __bf16 *>(p.state_in) + spr * D * D + col;
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[m][i] = (float)sin[(16 * m + 4 * g4 + i) * D];
-        } else if (p.state_in) {
-            const float *sin = reinterpret_cast<const float *>(p.state_in) + spr * D * D + col;
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[m][i] = sin[(16 * m + 4 * g4 + i) * D];
-        } else {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        load_state_tile(S, pw.sin, pw.sin_row, pw.sin16, col, g4);
         if (J > 0) {
             int rslot = 1 % NS;  // ring slot of stage j + 1 during step j
             // A step's operands, read from the ring one step ahead: W (negated),
@@ -846,18 +936,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
             if (j < J) step(j, wnA, kdA, gvA, u0A, wnB, kdB, gvB, u0B);
             barrier_lds();  // B_J
         }
-        if (p.state_out) {
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const size_t at = (spr * D + 16 * m + 4 * g4 + i) * D + col;
-                    if (p.state_bf16)
-                        reinterpret_cast<__bf16 *>(p.state_out)[at] = (__bf16)S[m][i];
-                    else
-                        reinterpret_cast<float *>(p.state_out)[at] = S[m][i];
-                }
-        }
+        store_state_tile(S, pw.sout, pw.sout_row, pw.sout16, col, g4);
         return;
     }
 
@@ -890,12 +969,13 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
 #pragma unroll
             for (int t = 0; t < 4; ++t) O = mma_k32(qg[t], sp[t], O);
             O = mma_k16w(pp, ub, O);  // the accumulator comes from K = 32 steps
-            __bf16 *orow = ob + (size_t)(16 * jo) * tokstride;
-            if (16 * jo + 16 <= L) {  // the whole sub-chunk lies in the sequence
+            const int64_t ja = j0 + jo;  // sub-chunk of the sequence
+            __bf16 *orow = ob + (size_t)(16 * ja) * tokstride;
+            if (16 * ja + 16 <= L) {  // the whole sub-chunk lies in the sequence
 #pragma unroll
                 for (int i = 0; i < 4; ++i) (orow + (size_t)i * tokstride)[loff] = (__bf16)(p.scale * O[i]);
             } else {
-                const int64_t r0 = 16 * jo + 4 * g4;
+                const int64_t r0 = 16 * ja + 4 * g4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (r0 + i < L) (orow + (size_t)i * tokstride)[loff] = (__bf16)(p.scale * O[i]);
@@ -949,12 +1029,10 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
     const int n = pr / H, h = pr - n * H;
     const int slot = pool_slot(p.slots, p.num_slots, n);
     if (slot < 0) return;  // whole workgroup: no barrier is left waiting
-    const size_t spr = (size_t)slot * H + h;
-    int64_t s0, L;
-    seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
-    const int64_t J = (L + 15) / 16;
-    const unsigned char *rec0 =
-        p.ws + ((size_t)h * p.nslots + (J > 0 ? sub_slot(s0, 0, n) : 0)) * kRec;
+    PairWork pw;
+    if (!pair_work(p, n, h, slot, pw)) return;  // whole workgroup: no barrier is left waiting
+    const int64_t s0 = pw.s0, L = pw.L, j0 = pw.j0, J = pw.steps;
+    const unsigned char *rec0 = pw.rec0;
 
     if (w >= G::kRW) {
         // ---------------- producers (bare barriers: a fence would drain the DMA)
@@ -971,24 +1049,7 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
     col[1] = 32 * w + 16 + m16;
     f32x4 S[2][8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        if (p.state_in && p.state_bf16) {
-            const __bf16 *sin = reinterpret_cast<const __bf16 *>(p.state_in) + spr * D * D + col[t];
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[t][m][i] = (float)sin[(16 * m + 4 * g4 + i) * D];
-        } else if (p.state_in) {
-            const float *sin = reinterpret_cast<const float *>(p.state_in) + spr * D * D + col[t];
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[t][m][i] = sin[(16 * m + 4 * g4 + i) * D];
-        } else {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) S[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
+    for (int t = 0; t < 2; ++t) load_state_tile(S[t], pw.sin, pw.sin_row, pw.sin16, col[t], g4);
     if (J > 0) {
         const int64_t tokstride = (int64_t)H * D;
         __bf16 *ob = reinterpret_cast<__bf16 *>(p.o) + ((size_t)s0 * tokstride + (size_t)h * D);
@@ -1067,15 +1128,16 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
                 for (int t = 0; t < 2; ++t) S[t][m] = mma_k16(c.kd[m], Ub[t], S[t][m]);
 #pragma unroll
             for (int t = 0; t < 2; ++t) O[t] = mma_k16w(c.pp, Ub[t], O[t]);  // after K = 32 steps
-            __bf16 *orow = ob + (size_t)(16 * j) * tokstride;
-            if (16 * j + 16 <= L) {  // the whole sub-chunk lies in the sequence
+            const int64_t ja = j0 + j;  // sub-chunk of the sequence
+            __bf16 *orow = ob + (size_t)(16 * ja) * tokstride;
+            if (16 * ja + 16 <= L) {  // the whole sub-chunk lies in the sequence
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)(p.scale * O[t][i]);
             } else {
-                const int64_t r0 = 16 * j + 4 * g4;
+                const int64_t r0 = 16 * ja + 4 * g4;
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1094,20 +1156,8 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
         if (j < J) step(j, A, B);
         barrier_lds();  // B_J
     }
-    if (p.state_out) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const size_t at = (spr * D + 16 * m + 4 * g4 + i) * D + col[t];
-                    if (p.state_bf16)
-                        reinterpret_cast<__bf16 *>(p.state_out)[at] = (__bf16)S[t][m][i];
-                    else
-                        reinterpret_cast<float *>(p.state_out)[at] = S[t][m][i];
-                }
-    }
+    for (int t = 0; t < 2; ++t) store_state_tile(S[t], pw.sout, pw.sout_row, pw.sout16, col[t], g4);
 }
 
 hipError_t launch_scan_wide(const SplitParams &sp, hipStream_t s) {
@@ -1147,7 +1197,15 @@ size_t split_workspace_bytes(int64_t total_tokens, int num_seqs, int H) {
     return (size_t)H * (size_t)(total_tokens / 16 + num_seqs) * kRec;
 }
 
-hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStream_t s) {
+size_t split_window_bytes(int num_seqs, int H, int64_t jw) {
+    return (size_t)H * (size_t)num_seqs * (size_t)jw * kRec + split_carry_bytes(num_seqs, H);
+}
+
+size_t split_carry_bytes(int num_seqs, int H) {
+    return (size_t)num_seqs * (size_t)H * kHeadDim * kHeadDim * sizeof(float);
+}
+
+hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, const SplitPlan &plan, hipStream_t s) {
     SplitParams sp;
     sp.q = a->q; sp.k = a->k; sp.v = a->v; sp.gate = a->gate; sp.beta = a->beta;
     sp.w = a->conv_weight; sp.bias = a->conv_bias; sp.cs_in = a->conv_state_in;
@@ -1155,43 +1213,60 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, hipStrea
     sp.state_bf16 = (a->flags & KDA_F_STATE_BF16) ? 1 : 0;
     sp.slots = a->state_slots; sp.num_slots = a->num_slots;
     sp.cu = a->cu_seqlens; sp.ws = static_cast<unsigned char *>(a->workspace);
-    sp.total = a->total_tokens; sp.nslots = a->total_tokens / 16 + a->num_seqs;
+    sp.total = a->total_tokens;
     sp.num_seqs = a->num_seqs; sp.H = a->num_heads;
     sp.scale = a->scale; sp.lb = a->gate_lower_bound; sp.flags = a->flags;
     sp.pairs = a->num_seqs * a->num_heads;
     sp.a_heads_fast = 0;
     sp.a_stride = 0;
+    sp.jw = plan.jw;
+    sp.win = 0;
+    sp.carry = nullptr;
+    if (plan.jw > 0) {
+        // records of one window first, then the carry
+        sp.nslots = (int64_t)a->num_seqs * plan.jw;
+        sp.carry = reinterpret_cast<float *>(sp.ws + (size_t)a->num_heads * (size_t)sp.nslots * kRec);
+    } else {
+        sp.nslots = a->total_tokens / 16 + a->num_seqs;
+    }
     // 128 columns per workgroup: the wide pass B; otherwise at most two dv tiles of
     // 16 columns per workgroup
     const bool wide = dv_tile == kHeadDim;
     if (!wide && dv_tile > 32) dv_tile = 32;
     sp.tiles = kHeadDim / dv_tile;
-    if (a->total_tokens > 0) {
-        static std::once_flag once;
-        static hipError_t attr = hipSuccess;
-        std::call_once(once, [] {
-            attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 4 * A_WAVE);
-        });
-        if (attr != hipSuccess) return attr;
-        // two slots per wave: wave (x, w) owns slots x * 4 + w + k * 4 * gx and takes
-        // the valid ones, so 8 * gx must cover every valid slot index.  Those are
-        // below ceil(total / 16) + num_seqs - 1 (the slot past a sequence's last
-        // sub-chunk is never valid), which for one 16-aligned sequence is the
-        // sub-chunk count itself and leaves no partly filled last round.
-        const int64_t span = (a->total_tokens + 15) / 16 + a->num_seqs - 1;
-        const int64_t gx = (span + 7) / 8;
-        sp.a_heads_fast = gx <= 65535;
-        sp.a_stride = 4 * gx;
-        const dim3 grid = sp.a_heads_fast ? dim3((unsigned)a->num_heads, (unsigned)gx)
-                                          : dim3((unsigned)gx, (unsigned)a->num_heads);
-        hipLaunchKernelGGL(intra_kernel, grid, dim3(256), 4 * A_WAVE, s, sp);
-        trace("intra_kernel grid=(%u,%u) block=256 lds=%d", grid.x, grid.y, 4 * A_WAVE);
-        hipError_t e = hipGetLastError();
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 4 * A_WAVE);
+    });
+    if (attr != hipSuccess) return attr;
+    // two slots per wave: wave (x, w) owns slots x * 4 + w + k * 4 * gx and takes
+    // the valid ones, so 8 * gx must cover every valid slot index.  Without windows
+    // those are below ceil(total / 16) + num_seqs - 1 (the slot past a sequence's
+    // last sub-chunk is never valid), which for one 16-aligned sequence is the
+    // sub-chunk count itself and leaves no partly filled last round; with windows
+    // they are the num_seqs * jw slots of a window.
+    const int64_t span = plan.jw > 0 ? sp.nslots : (a->total_tokens + 15) / 16 + a->num_seqs - 1;
+    const int64_t gx = (span + 7) / 8;
+    sp.a_heads_fast = gx <= 65535;
+    sp.a_stride = 4 * gx;
+    const dim3 grid = sp.a_heads_fast ? dim3((unsigned)a->num_heads, (unsigned)gx)
+                                      : dim3((unsigned)gx, (unsigned)a->num_heads);
+    const int64_t windows = plan.jw > 0 ? plan.windows : 1;
+    for (int64_t w = 0; w < windows; ++w) {
+        sp.win = w;
+        if (a->total_tokens > 0) {
+            hipLaunchKernelGGL(intra_kernel, grid, dim3(256), 4 * A_WAVE, s, sp);
+            trace("intra_kernel grid=(%u,%u) block=256 lds=%d window=%lld/%lld", grid.x, grid.y, 4 * A_WAVE,
+                  (long long)w, (long long)windows);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        hipError_t e = wide ? launch_scan_wide(sp, s) : (dv_tile == 16 ? launch_scan<1>(sp, s) : launch_scan<2>(sp, s));
         if (e != hipSuccess) return e;
     }
-    if (wide) return launch_scan_wide(sp, s);
-    return dv_tile == 16 ? launch_scan<1>(sp, s) : launch_scan<2>(sp, s);
+    return hipSuccess;
 }
 
 }  // namespace kda

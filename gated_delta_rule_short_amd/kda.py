@@ -18,10 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
 KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG, KDA_F_STATE_BF16 = 1, 2, 4, 8
+PREFILL_WORKSPACE_CAP = 4 << 30  # KDA_PREFILL_WORKSPACE_CAP
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_short_conv",
-           "kda_prefill", "kda_prefill_workspace_size", "kda_decode", "kda_decode_multi",
+           "kda_prefill", "kda_prefill_workspace_size", "kda_prefill_workspace_full_size",
+           "kda_prefill_workspace_min_size", "kda_decode", "kda_decode_multi",
            "kda_decode_commit", "kda_state_copy", "kda_gate_beta_proj",
            "kda_gate_beta_workspace_size")
 MAX_SPEC_TOKENS = 8
@@ -124,8 +126,10 @@ def load_library(path: str = LIB_PATH):
                                        ctypes.c_int, _c_u32, _p]
         lib.kda_prefill.restype = ctypes.c_int
         lib.kda_prefill.argtypes = [ctypes.POINTER(KdaPrefillArgs), _p]
-        lib.kda_prefill_workspace_size.restype = ctypes.c_size_t
-        lib.kda_prefill_workspace_size.argtypes = [ctypes.POINTER(KdaPrefillArgs)]
+        for f in ("kda_prefill_workspace_size", "kda_prefill_workspace_full_size",
+                  "kda_prefill_workspace_min_size"):
+            getattr(lib, f).restype = ctypes.c_size_t
+            getattr(lib, f).argtypes = [ctypes.POINTER(KdaPrefillArgs)]
         lib.kda_decode.restype = ctypes.c_int
         lib.kda_decode.argtypes = [ctypes.POINTER(KdaDecodeArgs), _p]
         lib.kda_decode_multi.restype = ctypes.c_int
@@ -373,13 +377,22 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
 
 
 def prefill_workspace_bytes(total_tokens, num_heads, num_seqs=1, dtype=torch.bfloat16,
-                            chunk_size=0):
-    """Workspace bytes the two-pass prefill needs (0 when it does not apply)."""
+                            chunk_size=0, cu_seqlens_host=None, which="recommended"):
+    """Workspace bytes of the two-pass prefill (0 when it does not apply): the
+    recommended size ("recommended": the whole call up to PREFILL_WORKSPACE_CAP,
+    windows beyond), the whole call at once ("full") or the smallest accepted
+    ("min")."""
     lib = load_library()
     a = KdaPrefillArgs(num_seqs=int(num_seqs), num_heads=int(num_heads), head_dim_k=128,
                        head_dim_v=128, chunk_size=int(chunk_size), total_tokens=int(total_tokens),
                        dtype=KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
-    return int(lib.kda_prefill_workspace_size(ctypes.byref(a)))
+    cuh = None
+    if cu_seqlens_host is not None:
+        cuh = torch.as_tensor(cu_seqlens_host).to(torch.int32).contiguous().cpu()
+        a.cu_seqlens_host = _ptr(cuh)
+    fn = {"recommended": lib.kda_prefill_workspace_size, "full": lib.kda_prefill_workspace_full_size,
+          "min": lib.kda_prefill_workspace_min_size}[which]
+    return int(fn(ctypes.byref(a)))
 
 
 def kda_decode(q, k, v, gate, beta, conv_weight, conv_state, state, *, conv_bias=None, o=None,

@@ -189,21 +189,42 @@ typedef struct {
  * Two schedules compute the same mixer (identical in exact arithmetic):
  *   - one pass: each workgroup owns a (sequence, head, dv tile) and runs the
  *     chunk's WY/UT transform itself (chunk_size 16, 32 or 64; default 64);
- *   - two passes (bf16 I/O only), chosen when chunk_size is 0 or 16 and a
- *     workspace of at least kda_prefill_workspace_size() bytes is given: a
- *     fully parallel pass turns every 16-token sub-chunk of every head into
- *     matrix-core operands in the workspace, and a second pass carries the
- *     state over them.  It keeps the whole GPU busy when there are few
- *     (sequence, head) pairs.
- * The workspace is owned by the caller, overwritten by each call, and must not
- * be shared by concurrent calls.
+ *   - two passes (bf16 I/O with chunk_size 0 or 16), chosen when a workspace is
+ *     given: a fully parallel pass turns every 16-token sub-chunk of every head
+ *     into matrix-core operands in the workspace (17,408 bytes per sub-chunk and
+ *     head), and a second pass carries the state over them.  It keeps the whole
+ *     GPU busy when there are few (sequence, head) pairs.
+ * Workspace and windows.  A workspace of kda_prefill_workspace_full_size()
+ * bytes runs the whole call at once.  A smaller one, of at least
+ * kda_prefill_workspace_min_size() bytes, runs it in windows: every sequence
+ * advances by the same number of sub-chunks per window (as many as the
+ * workspace holds next to an fp32 carry of every (sequence, head) state), so
+ * the memory needed is bounded whatever the sequence lengths; results are bit
+ * for bit those of the whole call.  kda_prefill_workspace_size() recommends the
+ * whole-call size up to KDA_PREFILL_WORKSPACE_CAP bytes and windows beyond it.
+ * Giving cu_seqlens_host lets the library count the windows exactly (without
+ * it, it plans for one sequence holding every token, and windows past the
+ * longest sequence do nothing).  A workspace below the minimum returns
+ * KDA_ERR_INVALID_ARG.  The workspace is owned by the caller, overwritten by
+ * each call, and must not be shared by concurrent calls.
  */
 kda_status kda_prefill(const kda_prefill_args *args, hipStream_t stream);
 
-/* Bytes of workspace the two-pass schedule needs for these arguments (it depends
- * on num_seqs, num_heads and total_tokens only); 0 when that schedule does not
- * apply (fp32 I/O or an explicit chunk_size of 32 or 64). */
+/* Recommended workspace bytes for the two-pass schedule (whole call when that
+ * fits in KDA_PREFILL_WORKSPACE_CAP, else windows within it); 0 when that
+ * schedule does not apply (fp32 I/O or an explicit chunk_size of 32 or 64).
+ * Depends on num_seqs, num_heads, total_tokens, dtype, chunk_size and, for the
+ * window count, cu_seqlens_host. */
+#define KDA_PREFILL_WORKSPACE_CAP ((size_t)4 << 30)
 size_t kda_prefill_workspace_size(const kda_prefill_args *args);
+
+/* Workspace bytes for the whole call in one window (no cap). */
+size_t kda_prefill_workspace_full_size(const kda_prefill_args *args);
+
+/* Smallest workspace the two-pass schedule accepts: one sub-chunk per sequence
+ * per window plus the carry (or the whole call, if that is smaller); 0 when the
+ * schedule does not apply. */
+size_t kda_prefill_workspace_min_size(const kda_prefill_args *args);
 
 /*
  * kda_decode -- one new token for each of N sequences (the single-token

@@ -377,10 +377,43 @@ def test_workspace_size_query(lib):
     a = _prefill_args(total_tokens=4096, num_heads=64)
     need = lib.kda_prefill_workspace_size(ctypes.byref(a))
     assert need == 64 * (4096 // 16 + 1) * 17408
+    assert lib.kda_prefill_workspace_full_size(ctypes.byref(a)) == need
     a.chunk_size = 64
     assert lib.kda_prefill_workspace_size(ctypes.byref(a)) == 0
+    assert lib.kda_prefill_workspace_min_size(ctypes.byref(a)) == 0
     b = _prefill_args(dtype=K.KDA_F32)
     assert lib.kda_prefill_workspace_size(ctypes.byref(b)) == 0
+
+
+REC, CARRY = 17408, 128 * 128 * 4  # bytes per (sub-chunk, head) record and per carried state
+
+
+@pytest.mark.parametrize("T,N,H", [(260408, 1, 64), (137314, 16, 64), (1 << 20, 1, 64),
+                                   (65536, 1, 64), (300, 40, 8)])
+def test_workspace_is_bounded(lib, T, N, H):
+    """The recommended workspace never exceeds the cap (the call then runs in
+    windows); the whole-call size is the packed record count; the minimum is one
+    sub-chunk per sequence plus the carry, or the whole call if smaller."""
+    a = _prefill_args(total_tokens=T, num_seqs=N, num_heads=H, cu_seqlens=FAKE)
+    full = lib.kda_prefill_workspace_full_size(ctypes.byref(a))
+    rec = lib.kda_prefill_workspace_size(ctypes.byref(a))
+    mini = lib.kda_prefill_workspace_min_size(ctypes.byref(a))
+    assert full == H * (T // 16 + N) * REC
+    assert mini == min(full, H * N * REC + N * H * CARRY)
+    assert mini <= rec <= full
+    assert rec <= max(K.PREFILL_WORKSPACE_CAP, mini)
+    if full > K.PREFILL_WORKSPACE_CAP:
+        jw = (rec - N * H * CARRY) // (H * N * REC)
+        assert rec == H * N * jw * REC + N * H * CARRY
+        assert K.PREFILL_WORKSPACE_CAP - rec < H * N * REC  # as many sub-chunks as fit
+
+
+def test_prefill_rejects_workspace_below_minimum(lib):
+    a = _prefill_args(total_tokens=4096, num_heads=2, workspace=ctypes.c_void_p(0x40000000))
+    mini = lib.kda_prefill_workspace_min_size(ctypes.byref(a))
+    a.workspace_bytes = mini - 1
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
+    assert b"workspace" in lib.kda_last_error()
 
 
 def test_prefill_rejects_workspace_overlapping_output(lib):
