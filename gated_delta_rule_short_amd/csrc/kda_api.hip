@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -244,9 +245,13 @@ size_t kda_prefill_workspace_min_size(const kda_prefill_args *a) {
     return one < full ? one : full;
 }
 
-kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
-    g_err[0] = 0;
-    if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
+}  // extern "C"
+
+namespace {
+
+// kda_prefill's checks and launches, with the workspace the caller's or the
+// scratch array's (kda_prefill_noalloc).
+kda_status prefill_impl(const kda_prefill_args *a, hipStream_t stream) {
     kda_status st = check_common(a->num_seqs, a->num_heads, a->head_dim_k, a->head_dim_v, a->dtype,
                                  a->flags, a->scale, a->gate_lower_bound);
     if (st != KDA_OK) return st;
@@ -352,6 +357,67 @@ kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
         if (e != hipSuccess) return hip_fail(e, "conv tail launch");
     }
     return KDA_OK;
+}
+
+
+// Scratch of kda_prefill_noalloc: one array per GPU the library runs on, held
+// until the process ends.  Host code uses only the address that
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[KDA_PREFILL_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+kda_status scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(KDA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill(const kda_prefill_args *a, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
+    return prefill_impl(a, stream);
+}
+
+kda_status kda_prefill_noalloc(const kda_prefill_args *a, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!a) return fail(KDA_ERR_INVALID_ARG, "args is NULL");
+    if (a->workspace || a->workspace_bytes)
+        return fail(KDA_ERR_INVALID_ARG, "kda_prefill_noalloc takes no workspace (workspace must be NULL, "
+                                         "workspace_bytes 0)");
+    kda_prefill_args args = *a;
+    if (two_pass_applies(a)) {
+        const size_t need = kda_prefill_workspace_min_size(a);
+        if (need > KDA_PREFILL_SCRATCH_BYTES)
+            return fail(KDA_ERR_INVALID_ARG, "this call needs at least %zu bytes of two-pass workspace; the "
+                                             "scratch of kda_prefill_noalloc holds %zu (use kda_prefill with a "
+                                             "workspace)", need, (size_t)KDA_PREFILL_SCRATCH_BYTES);
+        kda_status st = check_common(a->num_seqs, a->num_heads, a->head_dim_k, a->head_dim_v, a->dtype,
+                                     a->flags, a->scale, a->gate_lower_bound);
+        if (st != KDA_OK) return st;
+        st = scratch_address(&args.workspace);
+        if (st != KDA_OK) return st;
+        args.workspace_bytes = KDA_PREFILL_SCRATCH_BYTES;
+    }
+    return prefill_impl(&args, stream);
 }
 
 kda_status kda_decode(const kda_decode_args *a, hipStream_t stream) {

@@ -19,11 +19,12 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
 KDA_F_SILU, KDA_F_NO_QK_L2NORM, KDA_F_GATE_IS_LOG, KDA_F_STATE_BF16 = 1, 2, 4, 8
 PREFILL_WORKSPACE_CAP = 4 << 30  # KDA_PREFILL_WORKSPACE_CAP
+PREFILL_SCRATCH_BYTES = 256 << 20  # KDA_PREFILL_SCRATCH_BYTES (kda_prefill_noalloc)
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_short_conv",
            "kda_prefill", "kda_prefill_workspace_size", "kda_prefill_workspace_full_size",
-           "kda_prefill_workspace_min_size", "kda_decode", "kda_decode_multi",
+           "kda_prefill_workspace_min_size", "kda_prefill_noalloc", "kda_decode", "kda_decode_multi",
            "kda_decode_commit", "kda_state_copy", "kda_gate_beta_proj",
            "kda_gate_beta_workspace_size")
 MAX_SPEC_TOKENS = 8
@@ -124,8 +125,9 @@ def load_library(path: str = LIB_PATH):
         lib.kda_short_conv.restype = ctypes.c_int
         lib.kda_short_conv.argtypes = [_p, _p, _c_i64, _c_i32, _p, _p, _p, _p, _p, _p, _c_i32,
                                        ctypes.c_int, _c_u32, _p]
-        lib.kda_prefill.restype = ctypes.c_int
-        lib.kda_prefill.argtypes = [ctypes.POINTER(KdaPrefillArgs), _p]
+        for f in ("kda_prefill", "kda_prefill_noalloc"):
+            getattr(lib, f).restype = ctypes.c_int
+            getattr(lib, f).argtypes = [ctypes.POINTER(KdaPrefillArgs), _p]
         for f in ("kda_prefill_workspace_size", "kda_prefill_workspace_full_size",
                   "kda_prefill_workspace_min_size"):
             getattr(lib, f).restype = ctypes.c_size_t
@@ -281,8 +283,9 @@ def kda_short_conv(x, weight, *, cu_seqlens=None, cu_seqlens_host=None, bias=Non
 def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens_host=None,
                 num_seqs=None, conv_bias=None, conv_state_in=None, conv_state_out=None,
                 state_in=None, state_out=None, o=None, scale=0.0, gate_lower_bound=-5.0,
-                chunk_size=0, flags=0, workspace=True, state_slots=None, dv_tile=0, stream=None):
-    """Chunked KDA prefill of packed sequences.
+                chunk_size=0, flags=0, workspace=True, state_slots=None, dv_tile=0, stream=None,
+                _entry="kda_prefill"):
+    """Chunked KDA prefill of packed sequences (kda_prefill).
 
     The state (state_in / state_out) is fp32, or bf16 storage when those tensors are
     bf16 (state_out=True allocates the dtype of state_in, else fp32).  With
@@ -372,8 +375,19 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
         _need(workspace, "workspace", torch.uint8, dev)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = workspace.numel()
-    _check(lib, lib.kda_prefill(ctypes.byref(a), _stream(stream, dev)))
+    _check(lib, getattr(lib, _entry)(ctypes.byref(a), _stream(stream, dev)))
     return o, state_out, conv_state_out
+
+
+def kda_prefill_noalloc(q, k, v, gate, beta, conv_weight, **kw):
+    """kda_prefill through the entry point that allocates nothing (kda_prefill_noalloc):
+    the two-pass schedule runs in the library's per-GPU scratch.  Same arguments as
+    kda_prefill except `workspace`; pass o, state_out and conv_state_out as tensors
+    where the caller must not allocate either."""
+    if "workspace" in kw:
+        raise ValueError("kda_prefill_noalloc takes no workspace")
+    return kda_prefill(q, k, v, gate, beta, conv_weight, workspace=None, _entry="kda_prefill_noalloc",
+                       **kw)
 
 
 def prefill_workspace_bytes(total_tokens, num_heads, num_seqs=1, dtype=torch.bfloat16,

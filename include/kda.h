@@ -38,8 +38,9 @@
  *     KDA_ERR_UNSUPPORTED (head dim != 128, unknown flag, unsupported chunk).
  *     A failed launch returns KDA_ERR_HIP.  kda_last_error() gives a message
  *     for the calling thread's last failure.  No exception crosses the ABI.
- *   - Thread safety: no global mutable state besides that per-thread message;
- *     concurrent calls on different buffers are safe.
+ *   - Thread safety: no global mutable state besides that per-thread message
+ *     (and kda_prefill_noalloc's per-GPU scratch, see there); concurrent calls
+ *     on different buffers are safe.
  *
  * State pool (prefill, decode, decode_multi, decode_commit).  By default
  * sequence n of a call owns row n of the state and conv-state arrays.  With
@@ -225,6 +226,25 @@ size_t kda_prefill_workspace_full_size(const kda_prefill_args *args);
  * per window plus the carry (or the whole call, if that is smaller); 0 when the
  * schedule does not apply. */
 size_t kda_prefill_workspace_min_size(const kda_prefill_args *args);
+
+/*
+ * kda_prefill_noalloc -- kda_prefill for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and results as kda_prefill, except that
+ * `workspace` must be NULL and `workspace_bytes` 0 (else KDA_ERR_INVALID_ARG):
+ * the two-pass schedule (bf16 I/O, chunk_size 0 or 16) runs in a scratch array
+ * of KDA_PREFILL_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, in windows when the call needs more than that; other
+ * inputs run the one-pass schedule, which needs no scratch.  The call allocates
+ * nothing.  A call whose smallest two-pass workspace
+ * (kda_prefill_workspace_min_size) exceeds the scratch returns
+ * KDA_ERR_INVALID_ARG: use kda_prefill with a workspace for it.  Every call on
+ * one GPU shares that GPU's scratch and leaves its contents behind (nothing in
+ * it needs clearing between calls): calls that overlap in time on one GPU
+ * (different streams or threads) race, and the caller must order them.
+ */
+#define KDA_PREFILL_SCRATCH_BYTES ((size_t)256 << 20)
+kda_status kda_prefill_noalloc(const kda_prefill_args *args, hipStream_t stream);
 
 /*
  * kda_decode -- one new token for each of N sequences (the single-token
