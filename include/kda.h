@@ -72,7 +72,9 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1,
     KDA_ERR_UNSUPPORTED = 2,
-    KDA_ERR_HIP = 3
+    KDA_ERR_HIP = 3,
+    KDA_STATUS_INT_RANGE = 0x7fffffff  /* never returned: makes every int a valid kda_status
+                                          value, so kda_status_string may be given any int */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
