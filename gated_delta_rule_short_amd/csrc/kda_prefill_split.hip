@@ -10,21 +10,25 @@
 // one 16-token sub-chunk of one sequence and computes, relative to the state on
 // entry to the sub-chunk,
 //     A = strict_lower(K~ K^T . decay),  P = lower(Q~ K^T . decay),
-//     X = (I + diag(beta) A)^-1,  W = X diag(beta) (K . 2^b),  U0 = X diag(beta) V,
+//     X = (I + diag(beta) A)^-1,  W = X diag(beta) (K . 2^b),
 // with b the log2-decay cumsum from the sub-chunk start (>= -115.4, so every
 // factor is a finite fp32/bf16 number), and writes them as matrix-core
-// fragments to a workspace record.  Pass B (scan_kernel) runs one workgroup per
-// (sequence, head, dv tile) over its sub-chunks in order:
+// fragments to a workspace record, with X diag(beta) itself.  Pass B
+// (scan_kernel) runs one workgroup per (sequence, head, dv tile) over its
+// sub-chunks in order, forms U0 = X diag(beta) V from the conv of the raw v rows
+// of its columns, and carries the state:
 //     U = U0 - W S,  O = scale ((Q . 2^b) S + P U),
 //     S = diag(2^b_last) S + (K . 2^(b_last - b))^T U.
-// Pass A does the conv / L2 / gate work once per token and head, over the
-// whole GPU; pass B keeps the fp32 state in registers (accumulator layout) for
+// Pass A does the conv / L2 / gate work of q and k once per token and head,
+// over the whole GPU; pass B keeps the fp32 state in registers (accumulator layout) for
 // the whole sequence and streams the records through an LDS ring filled by
 // producer waves with LDS DMA, so several sub-chunks are in flight while
 // the consumer waves run the recurrence.  The workspace costs extra HBM
-// traffic (one 17 KiB record per sub-chunk and head, written once and read
+// traffic (one 13.5 KiB record per sub-chunk and head, written once and read
 // once), which pays off when there are too few (sequence, head) pairs to fill
-// the GPU otherwise.
+// the GPU otherwise.  v never enters the record: pass B reads its raw rows (the
+// same bytes the record's V part would take) and pass A neither reads v nor
+// writes U0.
 #include <mutex>
 
 #include "kda_device.h"
@@ -49,12 +53,15 @@ constexpr float kLog2eS = 1.4426950408889634f;
 //   KD  [8][64][4]  (K . 2^(b_last - b))^T, A-operand fragments (rows dk, K = tokens)
 //   PP  [64][4]     P, A-operand fragment (rows tokens, K = tokens)
 //   GAM [128] fp32  2^b_last per dk channel
-//   U0  [8][64][4]  X diag(beta) V, accumulator layout (rows tokens, columns dv)
-// Everything a workgroup of pass B shares comes first (R_U0 bytes), then the
-// per-dv-tile U0 fragments, so each stage is two contiguous DMA ranges.
-constexpr int R_WN = 0, R_QG = 4096, R_KD = 8192, R_PP = 12288, R_GAM = 12800, R_U0 = 13312;
-constexpr size_t kRec = 17408;
-static_assert(R_U0 % 1024 == 0, "shared part moves in whole DMA KiB");
+//   XB  [64][4]     X diag(beta), A-operand fragment (rows tokens, K = tokens)
+// Every part is shared by all dv columns.  In LDS a record takes kRecArea bytes
+// (whole DMA KiB; the tail past kRec receives duplicate bytes).
+constexpr int R_WN = 0, R_QG = 4096, R_KD = 8192, R_PP = 12288, R_GAM = 12800, R_XB = 13312;
+constexpr size_t kRec = 13824;
+constexpr int kRecArea = 14336;
+constexpr int kRecInst = kRecArea / 1024;  // DMA instructions of a record
+static_assert(kRecArea % 1024 == 0 && kRecArea >= (int)kRec && kRecArea - (int)kRec <= 512,
+              "the last record DMA reads its tail twice");
 
 struct SplitParams {
     const void *q, *k, *v, *gate, *beta;
@@ -88,15 +95,12 @@ struct SplitParams {
 __device__ __forceinline__ int64_t sub_slot(int64_t s0, int64_t j, int n) { return (s0 + 16 * j) / 16 + n; }
 
 // Per-wave LDS of pass A (bytes).  Row-major tiles hold A_SRM bf16 per token
-// row, transposed tiles A_STR (A_VTS) bf16 per channel row.  beta V
-// (transposed, VT) is formed after the QG export, in the then dead QL area.
-constexpr int A_SRM = 132, A_STR = 20, A_VTS = 16;
+// row, transposed tiles A_STR bf16 per channel row.
+constexpr int A_SRM = 132, A_STR = 20;
 constexpr int A_KL = 0, A_QL = A_KL + 16 * A_SRM * 2, A_KI = A_QL + 16 * A_SRM * 2;
 constexpr int A_KGT = A_KI + 16 * A_SRM * 2, A_PS = A_KGT + 128 * A_STR * 2;
 constexpr int A_WAVE = A_PS + 16 * A_STR * 2;
-constexpr int A_VT = A_QL;
 static_assert(A_WAVE % 16 == 0, "wave region alignment");
-static_assert(128 * A_VTS * 2 <= 16 * A_SRM * 2, "VT fits in the QL area");
 static_assert(8 * A_WAVE <= 163840, "two workgroups of four waves per CU");
 
 typedef Ops<__bf16> OPB;
@@ -152,29 +156,29 @@ struct SubTask {
 };
 
 // Raw inputs of one sub-chunk for this lane's two channels, as packed bf16
-// pairs: rows p0-3 .. p0+15 of q, k, v (clamped into the sequence; the three
+// pairs: rows p0-3 .. p0+15 of q and k (clamped into the sequence; the three
 // rows before a sequence come from the conv state or are zero) and rows p0 ..
 // p0+15 of the gate; beta of row p0 + lane in lanes 0..15.  The gate, k and
-// beta ("early") are needed first and are loaded one sub-chunk ahead; q and v
-// ("late") are loaded when the sub-chunk starts.
+// beta ("early") are needed first and are loaded one sub-chunk ahead; q
+// ("late") is loaded when the sub-chunk starts.
 struct EarlyRows {
     uint32_t xk[19], xa[16];
     uint32_t beta_bits;  // raw bf16 of beta (row clamped into the sequence); masked at use
 };
 struct LateRows {
-    uint32_t xq[19], xv[19];
+    uint32_t xq[19];
 };
 
-// Conv taps and bias of this lane's two q, k and v channels of head h.
+// Conv taps and bias of this lane's two q and k channels of head h.
 struct ConvW {
-    float w[3][2][4], b[3][2];
+    float w[2][2][4], b[2][2];
 };
 
 __device__ __forceinline__ void load_conv_w(const SplitParams &p, int h, int lane, ConvW &cw) {
     constexpr int D = kHeadDim;
     const int c0 = 2 * lane;
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
+    for (int t = 0; t < 2; ++t) {
         const int ch = t * p.H * D + h * D + c0;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -261,23 +265,15 @@ __device__ __forceinline__ void load_late(const SplitParams &p, const SubTask &t
     const int64_t rowbytes = (int64_t)p.H * D * 2;
     const RowWindow wr = row_window(tk, -3);
     const __amdgpu_buffer_rsrc_t rq = row_rsrc(p.q, tk, h, wr, rowbytes);
-    const __amdgpu_buffer_rsrc_t rv = row_rsrc(p.v, tk, h, wr, rowbytes);
 #pragma unroll
-    for (int i = 0; i < 19; ++i) {
-        const int so = row_soff(wr, i - 3, rowbytes);
-        r.xq[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, so, 0);
-        r.xv[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, 4 * lane, so, 0);
-    }
-    if (tk.j == 0) {
-        load_history(p, tk, h, lane, 0, r.xq);
-        load_history(p, tk, h, lane, 2, r.xv);
-    }
+    for (int i = 0; i < 19; ++i) r.xq[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, row_soff(wr, i - 3, rowbytes), 0);
+    if (tk.j == 0) load_history(p, tk, h, lane, 0, r.xq);
 }
 
 // One 16-token sub-chunk by one wave, from its early and late rows (loads
 // issued before).  When nx is set it starts the loads of the next sub-chunk's
 // rows as soon as their registers are free: the early rows after the k block
-// (into ner), the late rows after the v conv (into lr), so that they land while
+// (into ner), the late rows after the q block (into lr), so that they land while
 // this sub-chunk finishes.  All LDS traffic stays inside the wave's region.
 __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, const SubTask &tk,
                                                 int h, int lane, const EarlyRows &er, LateRows &lr,
@@ -296,12 +292,10 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     __bf16 *sQL = reinterpret_cast<__bf16 *>(lds + A_QL);
     __bf16 *sKI = reinterpret_cast<__bf16 *>(lds + A_KI);
     __bf16 *sKGT = reinterpret_cast<__bf16 *>(lds + A_KGT);
-    __bf16 *sVT = reinterpret_cast<__bf16 *>(lds + A_VT);
     __bf16 *sPS = reinterpret_cast<__bf16 *>(lds + A_PS);
     unsigned char *rec = p.ws + ((size_t)h * p.nslots + tk.slot) * kRec;
     const uint32_t(&xq)[19] = lr.xq;
     const uint32_t(&xk)[19] = er.xk;
-    const uint32_t(&xv)[19] = lr.xv;
     const uint32_t(&xa)[16] = er.xa;
     const float beta_r = (lane < 16 && lane < rem) ? __uint_as_float(er.beta_bits << 16) : 0.f;
     auto load_w = [&](int t, float (&wt)[2][4], float (&bs)[2]) {
@@ -418,6 +412,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         float wt[2][4], bs[2], y[16][2], rq[16];
         load_w(0, wt, bs);
         conv16(xq, wt, bs, y);
+        if (nx) load_late(p, *nx, h, lane, lr);
         finish(y);
         l2_scale(y, l2, lane, rq);
 #pragma unroll
@@ -459,22 +454,6 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     *reinterpret_cast<bf16x4 *>(rec + R_PP + (size_t)lane * 8) =
         *reinterpret_cast<const bf16x4 *>(sPS + m16 * A_STR + 4 * g4);
 
-    // ---- v: beta V transposed into the dead QL area
-    {
-        float wt[2][4], bs[2], y[16][2];
-        load_w(2, wt, bs);
-        conv16(xv, wt, bs, y);
-        if (nx) load_late(p, *nx, h, lane, lr);
-        finish(y);
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int r = 4 * q4;
-                OPB::store4(sVT + (c0 + e) * A_VTS + r, bt[r] * y[r][e], bt[r + 1] * y[r + 1][e],
-                            bt[r + 2] * y[r + 2][e], bt[r + 3] * y[r + 3][e]);
-            }
-    }
     // ---- X = (I + N)^-1, one row per lane: lane r (mod 16) solves
     // x (I + N) = e_r from the last column down, x_c = [c == r] - sum_{s > c} x_s N[s][c],
     // with N[s][c] read as a wave-uniform scalar from the register tile.  The
@@ -499,23 +478,37 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         // turned into an indexed array access)
         const float m0 = g4 == 0 ? 1.f : 0.f, m1 = g4 == 1 ? 1.f : 0.f;
         const float m2 = g4 == 2 ? 1.f : 0.f, m3 = g4 == 3 ? 1.f : 0.f;
+        float xs[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            xfr[i] = (__bf16)fmaf(x[i], m0, fmaf(x[4 + i], m1, fmaf(x[8 + i], m2, x[12 + i] * m3)));
+        for (int i = 0; i < 4; ++i) {
+            xs[i] = fmaf(x[i], m0, fmaf(x[4 + i], m1, fmaf(x[8 + i], m2, x[12 + i] * m3)));
+            xfr[i] = (__bf16)xs[i];
+        }
+        // X diag(beta) for pass B's U0 = X diag(beta) V: column 4 g4 + i carries
+        // beta of row 4 g4 + i (read from lanes i, 4 + i, 8 + i, 12 + i of beta_r)
+        const int bb = __float_as_int(beta_r);
+        bf16x4 xb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float b0 = __int_as_float(__builtin_amdgcn_readlane(bb, i));
+            const float b1 = __int_as_float(__builtin_amdgcn_readlane(bb, 4 + i));
+            const float b2 = __int_as_float(__builtin_amdgcn_readlane(bb, 8 + i));
+            const float b3 = __int_as_float(__builtin_amdgcn_readlane(bb, 12 + i));
+            const float bc = g4 < 2 ? (g4 == 0 ? b0 : b1) : (g4 == 2 ? b2 : b3);
+            xb[i] = (__bf16)(xs[i] * bc);
+        }
+        *reinterpret_cast<bf16x4 *>(rec + R_XB + (size_t)lane * 8) = xb;
     }
     wave_sync_lds();
 
-    // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL
-    // area; U0 = X diag(beta) V straight to the record in accumulator layout
+    // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL area
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
         const int col = 16 * nt + m16;
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const f32x4 wr = mma_k16(xfr, OPB::load4raw(sKGT + col * A_STR + 4 * g4), z);
-        const f32x4 ur = mma_k16(xfr, OPB::load4raw(sVT + col * A_VTS + 4 * g4), z);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sKL[(4 * g4 + i) * A_SRM + col] = (__bf16)(-wr[i]);
-        *reinterpret_cast<bf16x4 *>(rec + R_U0 + ((size_t)nt * 64 + lane) * 8) = pack4(ur);
     }
     wave_sync_lds();
 #pragma unroll
@@ -592,15 +585,21 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
 
 // Pass B geometry.  Per 16-column dv tile one recurrence wave (R: all 128 dk
 // rows of the state in registers) and one output wave (O), plus NP producer
-// waves that fill an NS-stage LDS ring with the records by LDS DMA.  A stage
-// holds a record's shared part and the NTW U0 tiles.  Per tile a double
-// buffered exchange slot passes the bf16 S fragments and U from R to O.  The
-// ring takes whatever LDS the exchange leaves (half of it at NTW = 1, where two
-// workgroups share a CU), up to 10 stages.
+// waves that fill an NS-stage LDS ring by LDS DMA.  A stage holds a record and
+// the 19 raw v rows (3 before the sub-chunk, 16 in it) of the workgroup's
+// 16 NTW columns.  Per tile a double buffered exchange slot passes the bf16 S
+// fragments and U from R to O, and O passes back U0 of the step after next,
+// which it forms from the raw v rows (O issues no DMA, so its LDS reads never
+// wait for the ring's copies).  The ring takes whatever
+// LDS the exchange leaves (half of it at NTW = 1, where two workgroups share a
+// CU), up to 10 stages.
 template <int NTW> struct ScanGeom {
-    static constexpr int kStage = R_U0 + NTW * 512;
-    static constexpr int kInst = (kStage + 1023) / 1024;   // DMA instructions per stage
-    static constexpr int NP = KDA_SCAN_PRODUCERS;          // producer waves
+    static constexpr int kVRow = 32 * NTW;                      // bytes of a raw v row
+    static constexpr int kVInst = (19 * kVRow + 1023) / 1024;   // DMA instructions of the v rows
+    static constexpr int kVOff = kRecArea;                      // v rows within a stage
+    static constexpr int kStage = kRecArea + kVInst * 1024;
+    static constexpr int kInst = kRecInst + kVInst;             // DMA instructions per stage
+    static constexpr int NP = KDA_SCAN_PRODUCERS;               // producer waves
     // DMA instructions of producer pw per stage (it takes i = pw mod NP)
     static constexpr int inst_of(int pw) { return (kInst + NP - 1 - pw) / NP; }
     static constexpr int kInstP0 = inst_of(0);
@@ -619,6 +618,70 @@ template <int NTW> struct ScanGeom {
     static_assert(NP >= 1 && NP <= 8 && kWaves <= 16 && kLds <= kBudget, "producers and LDS");
     static_assert(NTW == 1 || NTW == 2, "at most two dv tiles per workgroup");
 };
+
+// Raw v rows of a workgroup's columns for one sequence and head: `base` is the
+// first column of the workgroup in row 0 of the sequence; rows are `rowbytes`
+// apart; L is the sequence length.
+struct VRows {
+    const unsigned char *base;
+    int64_t rowbytes;
+    int L;
+};
+
+// Conv taps, bias and the three rows before the sequence (conv state, or zeros)
+// of this lane's v column, for U0.
+struct VConv {
+    float w[4], b, hist[3];
+};
+
+__device__ __forceinline__ void load_vconv(const SplitParams &p, int slot, int h, int colh, bool first_window,
+                                           VConv &vc) {
+    constexpr int D = kHeadDim;
+    const int ch = 2 * p.H * D + h * D + colh;  // v channel of the conv
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p.w + 4 * ch);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vc.w[i] = a[i];
+    vc.b = p.bias ? p.bias[ch] : 0.f;
+    const int CCH = 3 * p.H * D;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        vc.hist[i] = (first_window && p.cs_in)
+                         ? (float)reinterpret_cast<const __bf16 *>(p.cs_in)[((size_t)slot * 3 + i) * CCH + ch]
+                         : 0.f;
+}
+
+// U0 = X diag(beta) V of one 16-column tile from a stage: the width-4 conv of the
+// raw v rows 4 g4 - 3 .. 4 g4 + 3 of the sub-chunk in this lane's column (byte
+// colb of a row; at a sequence's first sub-chunk the three rows before it come
+// from the conv state), SiLU with the flag, rounded to bf16, times the record's
+// X diag(beta) fragment.  Rows past the sequence end hold clamped copies of its
+// last row: finite, and X diag(beta) has zero columns for them.
+template <int kVOff, int kVRow>
+__device__ __forceinline__ f32x4 u0_tile(const unsigned char *st, int colb, int lane, bool first, const VConv &vc,
+                                         bool silu) {
+    const int g4 = lane >> 4;
+    const unsigned char *vb = st + kVOff + colb + 4 * g4 * kVRow;
+    float x[7];
+#pragma unroll
+    for (int r = 0; r < 7; ++r) x[r] = (float)*reinterpret_cast<const __bf16 *>(vb + r * kVRow);
+    if (first && g4 == 0) {
+        x[0] = vc.hist[0];
+        x[1] = vc.hist[1];
+        x[2] = vc.hist[2];
+    }
+    f32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float a = fmaf(vc.w[0], x[i], vc.b);
+        a = fmaf(vc.w[1], x[i + 1], a);
+        a = fmaf(vc.w[2], x[i + 2], a);
+        a = fmaf(vc.w[3], x[i + 3], a);
+        y[i] = silu ? a * sigmoidf_dev(a) : a;
+    }
+    const bf16x4 xb = *reinterpret_cast<const bf16x4 *>(st + R_XB + lane * 8);
+    // a K = 32 shape, as the U chain it starts
+    return mma_k16w(xb, pack4(y), f32x4{0.f, 0.f, 0.f, 0.f});
+}
 
 // Lane K of each 16-lane row, broadcast to the whole row (DPP row_newbcast;
 // every source lane exists, so bound_ctrl changes nothing but lets the
@@ -665,23 +728,38 @@ __device__ __forceinline__ void scan_wait(int later) {
 // incrementally; in the steady state the wait is a constant vmcnt, and the
 // dispatch over the in-flight count runs only before B_-1 and in the tail.
 template <class G, int PW>
-__device__ __forceinline__ void producer_run(unsigned char *ring, const unsigned char *rec0, int nt0, int lane,
-                                             int J) {
+__device__ __forceinline__ void producer_run(unsigned char *ring, const unsigned char *rec0, const VRows &vr,
+                                             int64_t j0, int lane, int J) {
     constexpr int NS = G::NS, NP = G::NP, PER = G::inst_of(PW);
-    auto issue = [&](int slot, const unsigned char *rec) {
+    // stage of sub-chunk jabs: the record (its last DMA reads the record's tail
+    // twice, so every lane stays inside it) and the raw v rows 16 jabs - 3 ..
+    // 16 jabs + 15 clamped into the sequence (lanes past row 18 repeat it).  Every
+    // instruction is issued by every lane: PER per stage, exactly.
+    auto issue = [&](int slot, const unsigned char *rec, int64_t jabs) {
         unsigned char *st = ring + slot * G::kStage;
 #pragma unroll
         for (int i = PW; i < G::kInst; i += NP) {
-            const int off = i * 1024 + lane * 16;  // byte within the stage
-            if (off < G::kStage) {
-                const unsigned char *src = off < R_U0 ? rec + off : rec + R_U0 + nt0 * 512 + (off - R_U0);
-                __builtin_amdgcn_global_load_lds(src, (lds_void *)(st + i * 1024), 16, 0, 0);
+            if (i < kRecInst) {
+                const int off = i * 1024 + lane * 16;
+                const int so = off < (int)kRec ? off : off - 512;
+                __builtin_amdgcn_global_load_lds(rec + so, (lds_void *)(st + i * 1024), 16, 0, 0);
+            } else {
+                const int vi = i - kRecInst;
+                const int byte = vi * 1024 + lane * 16;
+                int r = byte / G::kVRow;
+                const int cb = byte - r * G::kVRow;
+                r = r > 18 ? 18 : r;
+                int t = 16 * (int)jabs - 3 + r;
+                t = t < 0 ? 0 : (t >= vr.L ? vr.L - 1 : t);
+                __builtin_amdgcn_global_load_lds(vr.base + (size_t)t * vr.rowbytes + cb,
+                                                 (lds_void *)(st + G::kVOff + vi * 1024), 16, 0, 0);
             }
         }
     };
     const int first = J < NS - 2 ? J : NS - 2;  // stages issued before B_-1
     const unsigned char *rec = rec0;
-    for (int j = 0; j < first; ++j, rec += kRec) issue(j, rec);
+    int64_t jabs = j0;
+    for (int j = 0; j < first; ++j, rec += kRec, ++jabs) issue(j, rec, jabs);
     // B_-1 needs stage 0; stages 1 .. first - 1 may stay in flight
     scan_wait<PER, G::kMaxLater>(first - 1);
     __builtin_amdgcn_s_barrier();  // B_-1
@@ -689,10 +767,10 @@ __device__ __forceinline__ void producer_run(unsigned char *ring, const unsigned
     // stages in flight; after it, stage b + NS - 2 goes to slot (b + NS - 2) mod NS
     int slot = NS - 2;
     int b = 0;
-    for (; b <= J - NS + 1; ++b, rec += kRec) {
+    for (; b <= J - NS + 1; ++b, rec += kRec, ++jabs) {
         wait_vmcnt<PER * (NS - 4)>();
         __builtin_amdgcn_s_barrier();  // B_b
-        issue(slot, rec);
+        issue(slot, rec, jabs);
         slot = slot + 1 == NS ? 0 : slot + 1;
     }
     // tail: nothing left to issue
@@ -704,14 +782,14 @@ __device__ __forceinline__ void producer_run(unsigned char *ring, const unsigned
 }
 
 template <class G, int K = 0>
-__device__ __forceinline__ void producer_dispatch(int pw, unsigned char *ring, const unsigned char *rec0, int nt0,
-                                                  int lane, int J) {
+__device__ __forceinline__ void producer_dispatch(int pw, unsigned char *ring, const unsigned char *rec0,
+                                                  const VRows &vr, int64_t j0, int lane, int J) {
     if constexpr (K < G::NP) {
         if (pw == K) {
-            producer_run<G, K>(ring, rec0, nt0, lane, J);
+            producer_run<G, K>(ring, rec0, vr, j0, lane, J);
             return;
         }
-        producer_dispatch<G, K + 1>(pw, ring, rec0, nt0, lane, J);
+        producer_dispatch<G, K + 1>(pw, ring, rec0, vr, j0, lane, J);
     }
 }
 
@@ -835,7 +913,9 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
         // ---------------- producers
         // bare barriers throughout: a fence would drain all DMA in flight
         if (J == 0) return;
-        producer_dispatch<G>(w - 2 * NTW, ring, rec0, nt0, lane, (int)J);
+        const VRows vr{reinterpret_cast<const unsigned char *>(p.v) + ((size_t)s0 * H + h) * D * 2 + nt0 * 32,
+                       (int64_t)H * D * 2, (int)L};
+        producer_dispatch<G>(w - 2 * NTW, ring, rec0, vr, j0, lane, (int)J);
         return;
     }
 
@@ -853,10 +933,14 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
         load_state_tile(S, pw.sin, pw.sin_row, pw.sin16, col, g4);
         if (J > 0) {
             int rslot = 1 % NS;  // ring slot of stage j + 1 during step j
+            const bool silu = p.flags & KDA_F_SILU;
+            VConv vc;
+            load_vconv(p, slot, h, col, j0 == 0, vc);
             // A step's operands, read from the ring one step ahead: W (negated),
-            // Kd, gam (one row per lane, see decay_tile) and this tile's U0.
-            auto load = [&](const unsigned char *st, bf16x8 (&wn)[4], bf16x4 (&kd)[8], float (&gv)[2],
-                            bf16x4 &u0) {
+            // Kd, gam (one row per lane, see decay_tile) and U0 (formed from the
+            // raw v rows of the stage).
+            auto load = [&](const unsigned char *st, int64_t jabs, bf16x8 (&wn)[4], bf16x4 (&kd)[8], f32x4 &u0,
+                            float (&gv)[2]) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                     wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + (t * 64 + lane) * 16);
@@ -867,23 +951,23 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                 for (int q = 0; q < 2; ++q)
                     gv[q] = *reinterpret_cast<const float *>(
                         st + R_GAM + (64 * q + 16 * (m16 >> 2) + 4 * g4 + (m16 & 3)) * 4);
-                u0 = *reinterpret_cast<const bf16x4 *>(st + R_U0 + (tw * 64 + lane) * 8);
+                u0 = u0_tile<G::kVOff, G::kVRow>(st, (tw * 16 + m16) * 2, lane, jabs == 0, vc, silu);
             };
             // One step: operands of step j in the first set; the second set
             // receives step j + 1's (the loop alternates the two sets).
-            auto step = [&](int64_t j, const bf16x8 (&wn)[4], const bf16x4 (&kd)[8], const float (&gv)[2],
-                            bf16x4 u0, bf16x8 (&wn_n)[4], bf16x4 (&kd_n)[8], float (&gv_n)[2], bf16x4 &u0_n) {
+            auto step = [&](int64_t j, const bf16x8 (&wn)[4], const bf16x4 (&kd)[8], const f32x4 &u0,
+                            const float (&gv)[2], bf16x8 (&wn_n)[4], bf16x4 (&kd_n)[8], f32x4 &u0_n,
+                            float (&gv_n)[2]) {
                 barrier_lds();  // B_j
                 __builtin_amdgcn_sched_barrier(0);
-                // (past the last step this reads a stale stage: harmless, and it keeps
-                // the step one basic block so that the issue order below holds)
-                load(ring + rslot * G::kStage, wn_n, kd_n, gv_n, u0_n);
+                // (past the last step this reads a stale stage: harmless)
+                load(ring + rslot * G::kStage, j0 + j + 1, wn_n, kd_n, u0_n, gv_n);
                 rslot = rslot + 1 == NS ? 0 : rslot + 1;
                 bf16x8 Sp[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) Sp[t] = join8(pack4(S[2 * t]), pack4(S[2 * t + 1]));
                 // two independent accumulation chains over the dk quarters
-                f32x4 Ua = {(float)u0.x, (float)u0.y, (float)u0.z, (float)u0.w};
+                f32x4 Ua = u0;
                 f32x4 Uc = {0.f, 0.f, 0.f, 0.f};
                 Ua = mma_k32(wn[0], Sp[0], Ua);
                 Uc = mma_k32(wn[1], Sp[1], Uc);
@@ -904,36 +988,19 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                 *reinterpret_cast<bf16x4 *>(ex + 4096 + lane * 8) = Ub;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) S[m] = mma_k16(kd[m], Ub, S[m]);
-                // issue order: next operands; S_j to bf16 interleaved with the U
-                // products; the decay under their latency; the S_j exchange; U; the
-                // U exchange; the state products (the barrier's LDS wait then finds
-                // the writes done)
-                __builtin_amdgcn_sched_group_barrier(0x100, 11, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
-                __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             };
             bf16x8 wnA[4], wnB[4];
-            bf16x4 kdA[8], kdB[8], u0A, u0B = {};
+            bf16x4 kdA[8], kdB[8];
+            f32x4 u0A, u0B;
             float gvA[2], gvB[2];
             barrier_lds();  // B_-1
-            load(stage(0), wnA, kdA, gvA, u0A);
+            load(stage(0), j0, wnA, kdA, u0A, gvA);
             int64_t j = 0;
             for (; j + 1 < J; j += 2) {
-                step(j, wnA, kdA, gvA, u0A, wnB, kdB, gvB, u0B);
-                step(j + 1, wnB, kdB, gvB, u0B, wnA, kdA, gvA, u0A);
+                step(j, wnA, kdA, u0A, gvA, wnB, kdB, u0B, gvB);
+                step(j + 1, wnB, kdB, u0B, gvB, wnA, kdA, u0A, gvA);
             }
-            if (j < J) step(j, wnA, kdA, gvA, u0A, wnB, kdB, gvB, u0B);
+            if (j < J) step(j, wnA, kdA, u0A, gvA, wnB, kdB, u0B, gvB);
             barrier_lds();  // B_J
         }
         store_state_tile(S, pw.sout, pw.sout_row, pw.sout16, col, g4);
@@ -988,14 +1055,17 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
 // dv columns, so each record crosses HBM and LDS once.  kRW recurrence waves hold
 // two 16-column tiles of the state each (64 fp32 per lane) and also form the
 // output of their columns; NP producer waves fill an NS-stage ring of whole
-// records.  With enough pairs to fill every compute unit, per-step latency is
+// records with the raw v rows of the head.  With enough pairs to fill every compute unit, per-step latency is
 // hidden by the other workgroups' memory traffic and the kernel streams the
 // records at the bandwidth the workgroups can draw, so the output products that
 // a separate wave would take off the recurrence's chain stay in the same wave
 // and no exchange area is needed.
 struct WideGeom {
-    static constexpr int kStage = (int)kRec;
-    static constexpr int kInst = (kStage + 1023) / 1024;  // DMA instructions per stage
+    static constexpr int kVRow = 2 * kHeadDim;                   // bytes of a raw v row
+    static constexpr int kVInst = (19 * kVRow + 1023) / 1024;    // DMA instructions of the v rows
+    static constexpr int kVOff = kRecArea;
+    static constexpr int kStage = kRecArea + kVInst * 1024;
+    static constexpr int kInst = kRecInst + kVInst;              // DMA instructions per stage
     static constexpr int NP = KDA_SCAN_PRODUCERS;
     static constexpr int inst_of(int pw) { return (kInst + NP - 1 - pw) / NP; }
     static constexpr int kInstP0 = (kInst + NP - 1) / NP;  // inst_of(0)
@@ -1037,7 +1107,9 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
     if (w >= G::kRW) {
         // ---------------- producers (bare barriers: a fence would drain the DMA)
         if (J == 0) return;
-        producer_dispatch<G>(w - G::kRW, ring, rec0, 0, lane, (int)J);
+        const VRows vr{reinterpret_cast<const unsigned char *>(p.v) + ((size_t)s0 * H + h) * D * 2,
+                       (int64_t)H * D * 2, (int)L};
+        producer_dispatch<G>(w - G::kRW, ring, rec0, vr, j0, lane, (int)J);
         return;
     }
 
@@ -1055,12 +1127,17 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
         __bf16 *ob = reinterpret_cast<__bf16 *>(p.o) + ((size_t)s0 * tokstride + (size_t)h * D);
         const uint32_t loff = (uint32_t)col[0] + 4u * (uint32_t)g4 * (uint32_t)tokstride;
         int rslot = 1 % NS;  // ring slot of stage j + 1 during step j
+        const bool silu = p.flags & KDA_F_SILU;
+        VConv vc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) load_vconv(p, slot, h, col[t], j0 == 0, vc[t]);
         struct Ops {
             bf16x8 wn[4], qg[4];
-            bf16x4 kd[8], u0[2], pp;
+            bf16x4 kd[8], pp;
+            f32x4 u0[2];
             float gv[2];
         };
-        auto load = [&](const unsigned char *st, Ops &o) {
+        auto load = [&](const unsigned char *st, int64_t jabs, Ops &o) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 o.wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + (t * 64 + lane) * 16);
@@ -1075,14 +1152,14 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
                     st + R_GAM + (64 * q + 16 * (m16 >> 2) + 4 * g4 + (m16 & 3)) * 4);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
-                o.u0[t] = *reinterpret_cast<const bf16x4 *>(st + R_U0 + ((2 * w + t) * 64 + lane) * 8);
+                o.u0[t] = u0_tile<G::kVOff, G::kVRow>(st, col[t] * 2, lane, jabs == 0, vc[t], silu);
             o.pp = *reinterpret_cast<const bf16x4 *>(st + R_PP + lane * 8);
         };
         auto step = [&](int64_t j, const Ops &c, Ops &nx) {
             barrier_lds();  // B_j
             __builtin_amdgcn_sched_barrier(0);
             // (past the last step this reads a stale stage: harmless)
-            load(ring + rslot * G::kStage, nx);
+            load(ring + rslot * G::kStage, j0 + j + 1, nx);
             rslot = rslot + 1 == NS ? 0 : rslot + 1;
             bf16x8 Sp[2][4];
 #pragma unroll
@@ -1092,7 +1169,7 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
             f32x4 Ua[2], Uc[2], O[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                Ua[t] = f32x4{(float)c.u0[t].x, (float)c.u0[t].y, (float)c.u0[t].z, (float)c.u0[t].w};
+                Ua[t] = c.u0[t];
                 Uc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -1147,7 +1224,7 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
         };
         Ops A, B;
         barrier_lds();  // B_-1
-        load(ring, A);  // stage 0 sits in slot 0
+        load(ring, j0, A);  // stage 0 sits in slot 0
         int64_t j = 0;
         for (; j + 1 < J; j += 2) {
             step(j, A, B);

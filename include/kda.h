@@ -194,7 +194,7 @@ typedef struct {
  *     chunk's WY/UT transform itself (chunk_size 16, 32 or 64; default 64);
  *   - two passes (bf16 I/O with chunk_size 0 or 16), chosen when a workspace is
  *     given: a fully parallel pass turns every 16-token sub-chunk of every head
- *     into matrix-core operands in the workspace (17,408 bytes per sub-chunk and
+ *     into matrix-core operands in the workspace (13,824 bytes per sub-chunk and
  *     head), and a second pass carries the state over them.  It keeps the whole
  *     GPU busy when there are few (sequence, head) pairs.
  * Workspace and windows.  A workspace of kda_prefill_workspace_full_size()

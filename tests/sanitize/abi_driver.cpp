@@ -18,7 +18,7 @@ namespace kda {
 static int g_launch = 0;
 static SplitPlan g_plan{-1, -1};
 static int g_dv = -1;
-static const size_t kRecBytes = 17408, kCarry = 128 * 128 * 4;
+static const size_t kRecBytes = 13824, kCarry = 128 * 128 * 4;
 hipError_t launch_short_conv(kda_dtype, const void *, void *, int64_t, int, const float *, const float *,
                              const void *, const int32_t *, int, bool, hipStream_t) { ++g_launch; return hipSuccess; }
 hipError_t launch_conv_tail(kda_dtype, const void *const[3], const int[3], int64_t, const void *, void *,
@@ -87,7 +87,7 @@ int main() {
         kda::g_launch = 0;
         CHECK(kda_prefill(&a, nullptr) == KDA_OK && kda::g_plan.jw == -2, "no workspace: one pass");
         const size_t full = kda_prefill_workspace_full_size(&a);
-        CHECK(full == (size_t)H * (T / 16 + N) * 17408, "full size");
+        CHECK(full == (size_t)H * (T / 16 + N) * kda::kRecBytes, "full size");
         a.workspace = addr(15); a.workspace_bytes = full;
         CHECK(kda_prefill(&a, nullptr) == KDA_OK && kda::g_plan.jw == 0, "whole call in one window");
         CHECK(kda::g_dv == 128, "1024 pairs: 128 columns per workgroup (dv %d)", kda::g_dv);
@@ -96,7 +96,7 @@ int main() {
         a.workspace_bytes = rec;
         CHECK(kda_prefill(&a, nullptr) == KDA_OK, "recommended size runs");
         const int64_t maxj = (cu[N] - cu[N - 1] + 15) / 16;
-        const int64_t jw = (int64_t)((rec - (size_t)N * H * 65536) / ((size_t)N * H * 17408));
+        const int64_t jw = (int64_t)((rec - (size_t)N * H * 65536) / ((size_t)N * H * kda::kRecBytes));
         CHECK(kda::g_plan.jw == jw && kda::g_plan.windows == (maxj + jw - 1) / jw,
               "windows %lld x %lld (want %lld x %lld)", (long long)kda::g_plan.jw,
               (long long)kda::g_plan.windows, (long long)jw, (long long)((maxj + jw - 1) / jw));

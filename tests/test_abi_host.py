@@ -376,7 +376,7 @@ def test_short_conv_rejects_bad_arguments(lib):
 def test_workspace_size_query(lib):
     a = _prefill_args(total_tokens=4096, num_heads=64)
     need = lib.kda_prefill_workspace_size(ctypes.byref(a))
-    assert need == 64 * (4096 // 16 + 1) * 17408
+    assert need == 64 * (4096 // 16 + 1) * _rec_bytes(lib)
     assert lib.kda_prefill_workspace_full_size(ctypes.byref(a)) == need
     a.chunk_size = 64
     assert lib.kda_prefill_workspace_size(ctypes.byref(a)) == 0
@@ -385,7 +385,14 @@ def test_workspace_size_query(lib):
     assert lib.kda_prefill_workspace_size(ctypes.byref(b)) == 0
 
 
-REC, CARRY = 17408, 128 * 128 * 4  # bytes per (sub-chunk, head) record and per carried state
+CARRY = 128 * 128 * 4  # bytes per carried (sequence, head) state
+
+
+def _rec_bytes(lib):
+    """Bytes of one (sub-chunk, head) workspace record: the whole-call size of one
+    16-token sequence and one head holds two record slots."""
+    a = _prefill_args(total_tokens=16, num_seqs=1, num_heads=1)
+    return lib.kda_prefill_workspace_full_size(ctypes.byref(a)) // 2
 
 
 @pytest.mark.parametrize("T,N,H", [(260408, 1, 64), (137314, 16, 64), (1 << 20, 1, 64),
@@ -394,6 +401,8 @@ def test_workspace_is_bounded(lib, T, N, H):
     """The recommended workspace never exceeds the cap (the call then runs in
     windows); the whole-call size is the packed record count; the minimum is one
     sub-chunk per sequence plus the carry, or the whole call if smaller."""
+    REC = _rec_bytes(lib)
+    assert REC % 512 == 0 and REC <= 16384  # 13.5 KiB: no V part
     a = _prefill_args(total_tokens=T, num_seqs=N, num_heads=H, cu_seqlens=FAKE)
     full = lib.kda_prefill_workspace_full_size(ctypes.byref(a))
     rec = lib.kda_prefill_workspace_size(ctypes.byref(a))

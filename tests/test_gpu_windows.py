@@ -20,7 +20,7 @@ from tests._gpu_common import assert_bf16_close, head_conv_w, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-REC, CARRY = 17408, 128 * 128 * 4
+CARRY = 128 * 128 * 4
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -30,7 +30,9 @@ def _lib():
 
 
 def _window_ws(N, H, jw):
-    return torch.empty(N * H * (jw * REC + CARRY), dtype=torch.uint8, device=DEV)
+    """A workspace of exactly jw sub-chunks per sequence and head plus the carry."""
+    rec = kda.prefill_workspace_bytes(16, 1, 1, which="full") // 2  # bytes of one record
+    return torch.empty(N * H * (jw * rec + CARRY), dtype=torch.uint8, device=DEV)
 
 
 def _run(inp, ws, host_cu=True, **kw):
@@ -98,7 +100,7 @@ def _progress(msg):
 
 @pytest.mark.timeout(600)
 def test_prompt_of_260408_tokens_within_the_cap():
-    """One sequence of 260,408 tokens, 64 heads (the whole call would need 18.1 GB of
+    """One sequence of 260,408 tokens, 64 heads (the whole call would need 14.4 GB of
     workspace): the recommended workspace stays within the cap, the call runs in
     windows, and sampled heads match the oracle per 16-token block."""
     T, H = 260408, 64

@@ -2,7 +2,7 @@
 that cannot: graph capture, tight serving loops) against kda_prefill, through the
 C ABI: two calls in a row on one GPU's scratch, the second with a smaller input.
 
-The first call (1 x 4096 tokens, 64 heads) needs more two-pass workspace than the
+The first call (1 x 6144 tokens, 64 heads) needs more two-pass workspace than the
 scratch holds, so it runs in windows; the second (three short sequences, 4 heads)
 fits at once and leaves most of the first call's scratch contents in place.  Both
 must equal kda_prefill with a whole-call workspace bit for bit (the same kernels;
@@ -47,8 +47,8 @@ def _both(inp, **kw):
 
 
 def test_noalloc_equals_prefill_twice_second_smaller():
-    big = KI.workload_inputs(1, device=DEV)  # 1 x 4096 tokens, 64 heads: windows in the scratch
-    assert kda.prefill_workspace_bytes(4096, 64, 1, which="full") > kda.PREFILL_SCRATCH_BYTES
+    big = KI.workload_inputs(1, device=DEV, T=6144)  # 1 x 6144 tokens, 64 heads: windows in the scratch
+    assert kda.prefill_workspace_bytes(6144, 64, 1, which="full") > kda.PREFILL_SCRATCH_BYTES
     (o_a, st_a, cs_a), (o_b, st_b, cs_b) = _both(big)
     assert torch.equal(o_a, o_b) and torch.equal(st_a, st_b) and torch.equal(cs_a, cs_b)
     small = KI.make_prefill(4, [300, 17, 65], seed=191, device=DEV, state_std=0.1,
