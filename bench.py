@@ -5,7 +5,8 @@ inputs already resident in HBM:
   prefill    : 16 packed sequences of 512..16,384 tokens (137,314 in all), 64
                heads of 128, bf16, fp32 initial and final states, two-pass
                schedule with the binding's default workspace
-               (kda_prefill: intra_kernel + scan_kernel + conv_tail_kernel)
+               (kda_prefill: intra_kernel, then scan_kernel or scan_wide_kernel,
+               once per workspace window)
   decode     : 256 sequences x 1 token, 64 heads, fp32 state 256x64x128x128
                updated in place, bf16 tokens                  (kda_decode)
   short_conv : the prefill's q|k|v rows as one [137,314, 24,576] bf16 tensor,
@@ -42,10 +43,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
 METRIC = "KDA prefill tokens/s/layer (H=64,d=128) + decode state GB/s, 1 MI355X"
 PREFILL = {4: "prefill_varlen", 1: "prefill_T4096", 3: "prefill_T65536"}
 PROFILE_OF = {  # committed rocprofv3 counter summaries holding HBM bytes per launch
-    "prefill_varlen": ("kda_prefill_split.hip", "prefill_varlen_N16_H64_pmc.md"),
-    "prefill_T4096": ("kda_prefill_split.hip", "prefill_T4096_H64_pmc.md"),
-    "prefill_T65536": ("kda_prefill_split.hip", "prefill_T65536_H64_pmc.md"),
-    "decode": ("kda_decode.hip", "decode_N256_H64_pmc.md"),
+    "prefill_varlen": ("kda_prefill_split.hip", "prefill_varlen_N16_H64.md"),
+    "prefill_T4096": ("kda_prefill_split.hip", "prefill_T4096_H64.md"),
+    "prefill_T65536": ("kda_prefill_split.hip", "prefill_T65536_H64.md"),
+    "decode": ("kda_decode.hip", "decode_N256_H64.md"),
 }
 OPS = ["prefill_varlen", "prefill_T4096", "prefill_T65536", "decode", "short_conv",
        "decode_bf16_state", "spec_decode", "spec_commit", "gate_proj", "state_copy",
@@ -262,15 +263,16 @@ def main():
             "tokens_per_s_per_layer": round(P["T"] / sec, 1),
             "us_per_call": round(ms[key] * 1e3, 2),
             "roofline": roofline(byts, sec, _profile_field(key, "hbm_bytes_per_launch"),
-                                 kernel="kda_prefill = intra_kernel + scan_kernel + conv_tail_kernel "
-                                        "(one call)",
+                                 kernel="kda_prefill (one call: intra_kernel, then scan_kernel or "
+                                        "scan_wide_kernel, per workspace window)",
                                  mfma_algorithmic_frac=round(units * fpth / sec / 1e12 /
                                                              BF16_PEAK_TFLOPS, 4),
-                                 mfma_busy_frac=_profile_field(key, "mfma_busy_frac")),
+                                 mfma_busy_frac=_profile_field(key, "mfma_busy_frac"),
+                                 valu_busy_frac=_profile_field(key, "valu_busy_frac")),
         }
     Pv = pre["prefill_varlen"]
     dec_state_bytes = 2 * N_dec * H * 128 * 128 * 4
-    dec_other = N_dec * H * (bpth + 2 * 3 * 128 * 2)  # tokens + conv cache read and written
+    dec_other = N_dec * H * (bpth + 2 * 3 * 3 * 128 * 2)  # tokens + q|k|v conv cache read and written
     dec_s = ms["decode"] * 1e-3
     conv_bytes = 2 * X.numel() * X.element_size()
     acc_l = acc_sp.cpu().tolist()

@@ -5,7 +5,7 @@
 // pattern, and kernels whose bytes are known exactly, against which the
 // hardware byte counters are calibrated.
 //   kda_calib_state_rmw: the state stream of one decode step -- one workgroup
-//     of 256 threads per 64 KiB fp32 state, each thread reading 16 float4 of
+//     of 512 threads per 64 KiB fp32 state, each thread reading 8 float4 of
 //     whole 512-byte rows with non-temporal loads and writing them back in
 //     place after one multiply, the same mapping as the decode kernel.
 //   kda_calib_copy: dst = src, non-temporal, grid-stride, four float4 per lane
@@ -21,17 +21,17 @@ namespace {
 
 typedef float f32x4c __attribute__((ext_vector_type(4)));
 
-__global__ void __launch_bounds__(256) state_rmw_kernel(float *state, float scale) {
+__global__ void __launch_bounds__(512) state_rmw_kernel(float *state, float scale) {
     const int tid = threadIdx.x, cg = tid & 31, rg = tid >> 5;
     float *S = state + (size_t)blockIdx.x * 128 * 128;
-    f32x4c st[16];
+    f32x4c st[8];
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-        st[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4c *>(S + (size_t)(rg + 8 * m) * 128 + 4 * cg));
+    for (int m = 0; m < 8; ++m)
+        st[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4c *>(S + (size_t)(rg + 16 * m) * 128 + 4 * cg));
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < 8; ++m) {
         st[m] *= scale;
-        __builtin_nontemporal_store(st[m], reinterpret_cast<f32x4c *>(S + (size_t)(rg + 8 * m) * 128 + 4 * cg));
+        __builtin_nontemporal_store(st[m], reinterpret_cast<f32x4c *>(S + (size_t)(rg + 16 * m) * 128 + 4 * cg));
     }
 }
 
@@ -78,7 +78,7 @@ extern "C" {
 int kda_calib_state_rmw(void *state, int64_t num_states, float scale, hipStream_t stream) {
     if (!state || num_states < 1 || num_states > ((int64_t)1 << 31) - 1 || (uintptr_t)state % 16)
         return 1;
-    hipLaunchKernelGGL(state_rmw_kernel, dim3((unsigned)num_states), dim3(256), 0, stream,
+    hipLaunchKernelGGL(state_rmw_kernel, dim3((unsigned)num_states), dim3(512), 0, stream,
                        static_cast<float *>(state), scale);
     return hipGetLastError() == hipSuccess ? 0 : 3;
 }

@@ -22,9 +22,9 @@ extern "C" {
 #endif
 
 /* In-place read-modify-write of `num_states` fp32 128 x 128 states (64 KiB each,
- * 16-byte aligned): every value is multiplied by `scale`.  One workgroup of 256
+ * 16-byte aligned): every value is multiplied by `scale`.  One workgroup of 512
  * threads per state with the decode kernel's mapping (thread t reads columns
- * 4 (t % 32) .. +3 of rows t / 32 + 8 m, m = 0..15, non-temporal): reads and
+ * 4 (t % 32) .. +3 of rows t / 32 + 16 m, m = 0..7, non-temporal): reads and
  * writes exactly 65,536 B per state. */
 int kda_calib_state_rmw(void *state, int64_t num_states, float scale, hipStream_t stream);
 
