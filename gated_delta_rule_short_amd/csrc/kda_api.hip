@@ -100,10 +100,19 @@ kda_status check_written(const Buf *b, int n, int n_written) {
     return KDA_OK;
 }
 
-// The two-pass schedule applies to bf16 I/O with chunk_size 0 or 16.
+// The two-pass and fused schedules apply to bf16 I/O with chunk_size 0 or 16.
 bool two_pass_applies(const kda_prefill_args *a) {
     return a && a->dtype == KDA_BF16 && (a->chunk_size == 0 || a->chunk_size == 16) && a->num_seqs >= 1 &&
            a->num_heads >= 1 && a->total_tokens >= 0;
+}
+
+// The schedule a call runs: explicit, or chosen (the fused one for many pairs,
+// else two passes when a workspace is given, else one pass).
+int resolve_schedule(const kda_prefill_args *a, bool with_workspace) {
+    if (a->schedule != KDA_SCHEDULE_AUTO) return a->schedule;
+    if (two_pass_applies(a) && (int64_t)a->num_seqs * a->num_heads >= KDA_FUSED_MIN_PAIRS)
+        return KDA_SCHEDULE_FUSED;
+    return two_pass_applies(a) && with_workspace ? KDA_SCHEDULE_TWO_PASS : KDA_SCHEDULE_ONE_PASS;
 }
 
 // Most 16-token sub-chunks of any sequence: from the host copy of cu_seqlens
@@ -222,7 +231,7 @@ kda_status kda_short_conv(const void *x, void *y, int64_t total_tokens, int32_t 
 }
 
 size_t kda_prefill_workspace_size(const kda_prefill_args *a) {
-    if (!two_pass_applies(a)) return 0;
+    if (!two_pass_applies(a) || resolve_schedule(a, true) != KDA_SCHEDULE_TWO_PASS) return 0;
     const size_t full = kda::split_workspace_bytes(a->total_tokens, a->num_seqs, a->num_heads);
     if (full <= KDA_PREFILL_WORKSPACE_CAP) return full;
     int64_t jw = window_subchunks(a, KDA_PREFILL_WORKSPACE_CAP);
@@ -286,9 +295,18 @@ kda_status prefill_impl(const kda_prefill_args *a, hipStream_t stream) {
     if (a->conv_state_out && a->conv_state_out != a->conv_state_in &&
         overlap(a->conv_state_out, csb, a->conv_state_in, csb))
         return fail(KDA_ERR_INVALID_ARG, "conv_state_out partially overlaps conv_state_in");
-    // schedule: two passes when a workspace is given and the two-pass schedule
-    // applies; windows when the workspace holds less than the whole call
-    const bool two_pass = two_pass_applies(a) && a->workspace;
+    // schedule; windows when a two-pass workspace holds less than the whole call
+    if (a->schedule < KDA_SCHEDULE_AUTO || a->schedule > KDA_SCHEDULE_FUSED)
+        return fail(KDA_ERR_INVALID_ARG, "schedule %d: use a KDA_SCHEDULE_* value", a->schedule);
+    const int sched = resolve_schedule(a, a->workspace != nullptr);
+    if ((sched == KDA_SCHEDULE_TWO_PASS || sched == KDA_SCHEDULE_FUSED) && !two_pass_applies(a))
+        return fail(KDA_ERR_UNSUPPORTED, "the %s schedule needs bf16 I/O and chunk_size 0 or 16",
+                    sched == KDA_SCHEDULE_FUSED ? "fused" : "two-pass");
+    if (sched == KDA_SCHEDULE_TWO_PASS && !a->workspace)
+        return fail(KDA_ERR_INVALID_ARG, "the two-pass schedule needs a workspace "
+                                         "(kda_prefill_workspace_size)");
+    const bool two_pass = sched == KDA_SCHEDULE_TWO_PASS;
+    const bool fused = sched == KDA_SCHEDULE_FUSED;
     kda::SplitPlan plan{0, 1};
     if (two_pass) {
         const size_t need_min = kda_prefill_workspace_min_size(a);
@@ -332,6 +350,8 @@ kda_status prefill_impl(const kda_prefill_args *a, hipStream_t stream) {
     // dv tile per workgroup: enough workgroups for 256 compute units.  The tile
     // changes only which workgroup computes a column, not the arithmetic.
     int dv_tile = pairs >= 256 ? 128 : (pairs >= 128 ? 64 : 32);
+    if (fused && a->dv_tile != 0 && a->dv_tile != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "dv_tile %d: the fused schedule takes 0 or 128", a->dv_tile);
     if (a->dv_tile != 0) {
         if (!(a->dv_tile == 32 || a->dv_tile == 64 || a->dv_tile == 128 ||
               (two_pass && a->dv_tile == 16)))
@@ -340,7 +360,9 @@ kda_status prefill_impl(const kda_prefill_args *a, hipStream_t stream) {
         dv_tile = a->dv_tile;
     }
     hipError_t e;
-    if (two_pass) {
+    if (fused) {
+        e = kda::launch_prefill_fused(&args, stream);
+    } else if (two_pass) {
         e = kda::launch_prefill_split(&args, dv_tile, plan, stream);
     } else {
         kda::PrefillLaunch pl{&args, chunk, dv_tile};
@@ -404,7 +426,7 @@ kda_status kda_prefill_noalloc(const kda_prefill_args *a, hipStream_t stream) {
         return fail(KDA_ERR_INVALID_ARG, "kda_prefill_noalloc takes no workspace (workspace must be NULL, "
                                          "workspace_bytes 0)");
     kda_prefill_args args = *a;
-    if (two_pass_applies(a)) {
+    if (two_pass_applies(a) && resolve_schedule(a, true) == KDA_SCHEDULE_TWO_PASS) {
         const size_t need = kda_prefill_workspace_min_size(a);
         if (need > KDA_PREFILL_SCRATCH_BYTES)
             return fail(KDA_ERR_INVALID_ARG, "this call needs at least %zu bytes of two-pass workspace; the "

@@ -57,5 +57,7 @@ struct SplitPlan {
     int64_t windows;  // windows to run when jw > 0
 };
 hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, const SplitPlan &plan, hipStream_t s);
+// Fused schedule: one workgroup per (sequence, head), no workspace.
+hipError_t launch_prefill_fused(const kda_prefill_args *a, hipStream_t s);
 
 }  // namespace kda

@@ -47,7 +47,7 @@ namespace {
 
 constexpr float kLog2eS = 1.4426950408889634f;
 
-// Workspace record of one (head, sub-chunk), byte offsets; bf16 unless noted.
+// Record of one (head, sub-chunk), byte offsets; bf16 unless noted.
 //   WN  [4][64][8]  -W, A-operand fragments (rows tokens, K = dk, permuted pairs)
 //   QG  [4][64][8]  Q . 2^b, same fragment layout
 //   KD  [8][64][4]  (K . 2^(b_last - b))^T, A-operand fragments (rows dk, K = tokens)
@@ -55,8 +55,11 @@ constexpr float kLog2eS = 1.4426950408889634f;
 //   GAM [128] fp32  2^b_last per dk channel
 //   XB  [64][4]     X diag(beta), A-operand fragment (rows tokens, K = tokens)
 // Every part is shared by all dv columns.  In LDS a record takes kRecArea bytes
-// (whole DMA KiB; the tail past kRec receives duplicate bytes).
+// (whole DMA KiB; the tail past kRec receives duplicate bytes).  The fused
+// schedule keeps its records in LDS only and holds U0 = X diag(beta) V
+// ([8][64][4], accumulator layout) at R_U0 in place of XB.
 constexpr int R_WN = 0, R_QG = 4096, R_KD = 8192, R_PP = 12288, R_GAM = 12800, R_XB = 13312;
+constexpr int R_U0 = 13312, kRecFused = R_U0 + 4096;
 constexpr size_t kRec = 13824;
 constexpr int kRecArea = 14336;
 constexpr int kRecInst = kRecArea / 1024;  // DMA instructions of a record
@@ -100,6 +103,10 @@ constexpr int A_SRM = 132, A_STR = 20;
 constexpr int A_KL = 0, A_QL = A_KL + 16 * A_SRM * 2, A_KI = A_QL + 16 * A_SRM * 2;
 constexpr int A_KGT = A_KI + 16 * A_SRM * 2, A_PS = A_KGT + 128 * A_STR * 2;
 constexpr int A_WAVE = A_PS + 16 * A_STR * 2;
+// beta V transposed (fused schedule): A_VTS bf16 per channel row, in the QL area
+// once QL is dead
+constexpr int A_VTS = 16, A_VT = A_QL;
+static_assert(128 * A_VTS * 2 <= 16 * A_SRM * 2, "VT fits in the QL area");
 static_assert(A_WAVE % 16 == 0, "wave region alignment");
 static_assert(8 * A_WAVE <= 163840, "two workgroups of four waves per CU");
 
@@ -270,14 +277,37 @@ __device__ __forceinline__ void load_late(const SplitParams &p, const SubTask &t
     if (tk.j == 0) load_history(p, tk, h, lane, 0, r.xq);
 }
 
+// Rows p0-3 .. p0+15 of v (fused schedule: loaded inside the sub-chunk, when its
+// q block starts, so they are not held across sub-chunks).
+__device__ __forceinline__ void load_v_rows(const SplitParams &p, const SubTask &tk, int h, int lane,
+                                            uint32_t (&xv)[19]) {
+    constexpr int D = kHeadDim;
+    const int64_t rowbytes = (int64_t)p.H * D * 2;
+    const RowWindow wr = row_window(tk, -3);
+    const __amdgpu_buffer_rsrc_t rv = row_rsrc(p.v, tk, h, wr, rowbytes);
+#pragma unroll
+    for (int i = 0; i < 19; ++i)
+        xv[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, 4 * lane, row_soff(wr, i - 3, rowbytes), 0);
+    if (tk.j == 0) load_history(p, tk, h, lane, 2, xv);
+}
+
+// Conv taps and bias of one head in LDS (fused schedule): taps [3][128][4] for
+// q, k, v, then biases [3][128]; fp32.
+constexpr int kConvLdsBytes = 3 * 128 * 5 * 4;
+
 // One 16-token sub-chunk by one wave, from its early and late rows (loads
-// issued before).  When nx is set it starts the loads of the next sub-chunk's
-// rows as soon as their registers are free: the early rows after the k block
-// (into ner), the late rows after the q block (into lr), so that they land while
-// this sub-chunk finishes.  All LDS traffic stays inside the wave's region.
-__device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, const SubTask &tk,
-                                                int h, int lane, const EarlyRows &er, LateRows &lr,
-                                                const ConvW &cw, const SubTask *nx, EarlyRows &ner) {
+// issued before), into the record at rec.  When nx is set it starts the loads
+// of the next sub-chunk's rows as soon as their registers are free: the early
+// rows after the k block (into ner), the late rows after the last conv that
+// reads them (into lr), so that they land while this sub-chunk finishes.  All
+// scratch LDS traffic stays inside the wave's region.  FU (the fused schedule)
+// also convolves v and writes U0 = X diag(beta) V in place of X diag(beta); its
+// conv taps come from LDS (cwl) instead of registers (cw).
+template <bool FU>
+__device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, unsigned char *rec,
+                                                const SubTask &tk, int h, int lane, const EarlyRows &er,
+                                                LateRows &lr, const ConvW &cw, const float *cwl,
+                                                const SubTask *nx, EarlyRows &ner) {
     constexpr int D = kHeadDim;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int64_t s0 = tk.s0, L = tk.L, j = tk.j;
@@ -293,17 +323,28 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     __bf16 *sKI = reinterpret_cast<__bf16 *>(lds + A_KI);
     __bf16 *sKGT = reinterpret_cast<__bf16 *>(lds + A_KGT);
     __bf16 *sPS = reinterpret_cast<__bf16 *>(lds + A_PS);
-    unsigned char *rec = p.ws + ((size_t)h * p.nslots + tk.slot) * kRec;
     const uint32_t(&xq)[19] = lr.xq;
     const uint32_t(&xk)[19] = er.xk;
     const uint32_t(&xa)[16] = er.xa;
     const float beta_r = (lane < 16 && lane < rem) ? __uint_as_float(er.beta_bits << 16) : 0.f;
     auto load_w = [&](int t, float (&wt)[2][4], float (&bs)[2]) {
+        if constexpr (FU) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+            for (int e = 0; e < 2; ++e) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(cwl + (t * 128 + c0 + e) * 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wt[e][i] = cw.w[t][e][i];
-            bs[e] = cw.b[t][e];
+                for (int i = 0; i < 4; ++i) wt[e][i] = a[i];
+            }
+            const f32x2 b = *reinterpret_cast<const f32x2 *>(cwl + 3 * 128 * 4 + t * 128 + c0);
+            bs[0] = b[0];
+            bs[1] = b[1];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wt[e][i] = cw.w[t][e][i];
+                bs[e] = cw.b[t][e];
+            }
         }
     };
     // activation and the rows past the sequence end (zero contribution)
@@ -407,6 +448,8 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         }
     }
     if (nx) load_early(p, *nx, h, lane, ner);
+    uint32_t xv[FU ? 19 : 1];
+    if constexpr (FU) load_v_rows(p, tk, h, lane, xv);
     // ---- q: QL = Q.2^b (row-major)
     {
         float wt[2][4], bs[2], y[16][2], rq[16];
@@ -453,6 +496,22 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     wave_sync_lds();
     *reinterpret_cast<bf16x4 *>(rec + R_PP + (size_t)lane * 8) =
         *reinterpret_cast<const bf16x4 *>(sPS + m16 * A_STR + 4 * g4);
+    if constexpr (FU) {
+        // ---- v: beta V transposed into the dead QL area
+        __bf16 *sVT = reinterpret_cast<__bf16 *>(lds + A_VT);
+        float wt[2][4], bs[2], y[16][2];
+        load_w(2, wt, bs);
+        conv16(xv, wt, bs, y);
+        finish(y);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int r = 4 * q4;
+                OPB::store4(sVT + (c0 + e) * A_VTS + r, bt[r] * y[r][e], bt[r + 1] * y[r + 1][e],
+                            bt[r + 2] * y[r + 2][e], bt[r + 3] * y[r + 3][e]);
+            }
+    }
 
     // ---- X = (I + N)^-1, one row per lane: lane r (mod 16) solves
     // x (I + N) = e_r from the last column down, x_c = [c == r] - sum_{s > c} x_s N[s][c],
@@ -484,24 +543,28 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
             xs[i] = fmaf(x[i], m0, fmaf(x[4 + i], m1, fmaf(x[8 + i], m2, x[12 + i] * m3)));
             xfr[i] = (__bf16)xs[i];
         }
-        // X diag(beta) for pass B's U0 = X diag(beta) V: column 4 g4 + i carries
-        // beta of row 4 g4 + i (read from lanes i, 4 + i, 8 + i, 12 + i of beta_r)
-        const int bb = __float_as_int(beta_r);
-        bf16x4 xb;
+        if constexpr (!FU) {
+            // X diag(beta) for pass B's U0 = X diag(beta) V: column 4 g4 + i carries
+            // beta of row 4 g4 + i (read from lanes i, 4 + i, 8 + i, 12 + i of beta_r)
+            const int bb = __float_as_int(beta_r);
+            bf16x4 xb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float b0 = __int_as_float(__builtin_amdgcn_readlane(bb, i));
-            const float b1 = __int_as_float(__builtin_amdgcn_readlane(bb, 4 + i));
-            const float b2 = __int_as_float(__builtin_amdgcn_readlane(bb, 8 + i));
-            const float b3 = __int_as_float(__builtin_amdgcn_readlane(bb, 12 + i));
-            const float bc = g4 < 2 ? (g4 == 0 ? b0 : b1) : (g4 == 2 ? b2 : b3);
-            xb[i] = (__bf16)(xs[i] * bc);
+            for (int i = 0; i < 4; ++i) {
+                const float b0 = __int_as_float(__builtin_amdgcn_readlane(bb, i));
+                const float b1 = __int_as_float(__builtin_amdgcn_readlane(bb, 4 + i));
+                const float b2 = __int_as_float(__builtin_amdgcn_readlane(bb, 8 + i));
+                const float b3 = __int_as_float(__builtin_amdgcn_readlane(bb, 12 + i));
+                const float bc = g4 < 2 ? (g4 == 0 ? b0 : b1) : (g4 == 2 ? b2 : b3);
+                xb[i] = (__bf16)(xs[i] * bc);
+            }
+            *reinterpret_cast<bf16x4 *>(rec + R_XB + (size_t)lane * 8) = xb;
         }
-        *reinterpret_cast<bf16x4 *>(rec + R_XB + (size_t)lane * 8) = xb;
     }
     wave_sync_lds();
 
-    // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL area
+    // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL
+    // area; with FU also U0 = X (diag(beta) V) straight to the record in
+    // accumulator layout
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
         const int col = 16 * nt + m16;
@@ -509,6 +572,11 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         const f32x4 wr = mma_k16(xfr, OPB::load4raw(sKGT + col * A_STR + 4 * g4), z);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sKL[(4 * g4 + i) * A_SRM + col] = (__bf16)(-wr[i]);
+        if constexpr (FU) {
+            const __bf16 *sVT = reinterpret_cast<const __bf16 *>(lds + A_VT);
+            const f32x4 ur = mma_k16(xfr, OPB::load4raw(sVT + col * A_VTS + 4 * g4), z);
+            *reinterpret_cast<bf16x4 *>(rec + R_U0 + ((size_t)nt * 64 + lane) * 8) = pack4(ur);
+        }
     }
     wave_sync_lds();
 #pragma unroll
@@ -579,8 +647,11 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     load_early(p, ta, h, lane, ra);
     load_late(p, ta, h, lane, lr);
     const bool hb = next_task(p, ta.slot + stride, stride, tb);
-    intra_sub_chunk(p, lds, ta, h, lane, ra, lr, cw, hb ? &tb : nullptr, rb);
-    if (hb) intra_sub_chunk(p, lds, tb, h, lane, rb, lr, cw, nullptr, ra);
+    intra_sub_chunk<false>(p, lds, p.ws + ((size_t)h * p.nslots + ta.slot) * kRec, ta, h, lane, ra, lr, cw,
+                           nullptr, hb ? &tb : nullptr, rb);
+    if (hb)
+        intra_sub_chunk<false>(p, lds, p.ws + ((size_t)h * p.nslots + tb.slot) * kRec, tb, h, lane, rb, lr, cw,
+                               nullptr, nullptr, ra);
 }
 
 // Pass B geometry.  Per 16-column dv tile one recurrence wave (R: all 128 dk
@@ -1237,6 +1308,266 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
     for (int t = 0; t < 2; ++t) store_state_tile(S[t], pw.sout, pw.sout_row, pw.sout16, col[t], g4);
 }
 
+// ---------------------------------------------------------------------------
+// Fused schedule for many (sequence, head) pairs: one workgroup per pair over
+// all 128 dv columns.  Four pass-A waves form the records of the pair's
+// sub-chunks (sub-chunks a, a + 4, ... for wave a; U0 included, from v) in an
+// NS-slot ring in LDS, and four recurrence waves run pass B's steps on them
+// (two 16-column tiles each, output included), so no record leaves the CU.
+// Slot j mod NS holds sub-chunk j.  The waves hand slots over through LDS
+// words instead of barriers (a pass-A task spans several steps):
+//   ready[s]  = j + 1 once sub-chunk j's record is complete in slot s;
+//   done[w]   = the number of records recurrence wave w has read into registers.
+// Pass-A wave a waits for min_w done[w] >= j - NS + 1 before writing sub-chunk j;
+// recurrence wave w waits for ready[j mod NS] >= j + 1 before reading it.  A
+// wait that polls kSpinLimit times without success sets the abort word, after
+// which no wave of the workgroup waits again: a broken hand-over yields wrong
+// results and never a workgroup that does not end.
+struct FusedGeom {
+    static constexpr int NS = 4;                  // record slots
+    static constexpr int kAW = 4, kRW = 4;        // pass-A waves, recurrence waves
+    static constexpr int kThreads = 64 * (kAW + kRW);
+    static constexpr int kAOff = NS * kRecFused;  // pass-A scratch, A_WAVE bytes per wave
+    static constexpr int kConvOff = kAOff + kAW * A_WAVE;
+    static constexpr int kFlagOff = kConvOff + kConvLdsBytes;
+    static constexpr int kReady = kFlagOff, kDone = kFlagOff + 32, kAbort = kFlagOff + 60;
+    static constexpr int kLds = kFlagOff + 64;
+    static_assert(NS >= kAW && NS <= 8, "every pass-A wave has a slot to fill; ready[] fits 32 bytes");
+    static_assert(kRecFused % 16 == 0 && kLds <= 163840, "LDS");
+    static_assert(2 * kRW * 16 == kHeadDim, "the recurrence waves cover every dv column");
+};
+constexpr int kSpinLimit = 1 << 22;
+
+__device__ __forceinline__ int lds_word(const unsigned char *lds, int off) {
+    return __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(reinterpret_cast<const int *>(lds + off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+__device__ __forceinline__ void lds_word_set(unsigned char *lds, int off, int v) {
+    // every earlier LDS access of this wave completes first (lgkmcnt only: the
+    // fence is restricted to LDS, so loads from memory stay in flight)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __hip_atomic_store(reinterpret_cast<int *>(lds + off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void give_up(unsigned char *lds) {
+    __hip_atomic_store(reinterpret_cast<int *>(lds + FusedGeom::kAbort), 1, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void wait_ready(unsigned char *lds, int64_t j) {
+    const int off = FusedGeom::kReady + 4 * (int)(j % FusedGeom::NS);
+    for (int it = 0;; ++it) {
+        if (lds_word(lds, off) >= (int)j + 1 || lds_word(lds, FusedGeom::kAbort)) break;
+        if (it == kSpinLimit) {
+            give_up(lds);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ void wait_slot_free(unsigned char *lds, int64_t j) {
+    const int want = (int)j - FusedGeom::NS + 1;
+    if (want <= 0) return;
+    for (int it = 0;; ++it) {
+        int m = lds_word(lds, FusedGeom::kDone);
+#pragma unroll
+        for (int w = 1; w < FusedGeom::kRW; ++w) {
+            const int d = lds_word(lds, FusedGeom::kDone + 4 * w);
+            m = d < m ? d : m;
+        }
+        if (m >= want || lds_word(lds, FusedGeom::kAbort)) break;
+        if (it == kSpinLimit) {
+            give_up(lds);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitParams p) {
+    typedef FusedGeom G;
+    constexpr int D = kHeadDim, NS = G::NS;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_f[];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int m16 = lane & 15, g4 = lane >> 4;
+    const int pr = blockIdx.x;
+    if (pr >= p.pairs) return;  // whole workgroup
+    const int H = p.H;
+    const int n = pr / H, h = pr - n * H;
+    const int slot = pool_slot(p.slots, p.num_slots, n);
+    if (slot < 0) return;  // whole workgroup
+    int64_t s0, L;
+    seq_bounds(p.cu, p.total, p.num_seqs, n, s0, L);
+    const int64_t J = (L + 15) / 16;
+    if (threadIdx.x < 16) reinterpret_cast<int *>(smem_f + G::kFlagOff)[threadIdx.x] = 0;
+    {
+        // the head's q, k, v conv taps and biases into LDS for the pass-A waves
+        float *cwl = reinterpret_cast<float *>(smem_f + G::kConvOff);
+        for (int i = threadIdx.x; i < 3 * 128; i += G::kThreads) {
+            const int t = i >> 7, c = i & 127, ch = t * H * D + h * D + c;
+            *reinterpret_cast<f32x4 *>(cwl + 4 * i) = *reinterpret_cast<const f32x4 *>(p.w + 4 * ch);
+            cwl[3 * 128 * 4 + i] = p.bias ? p.bias[ch] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    if (w >= G::kRW) {
+        // ---------------- pass A: sub-chunks a, a + 4, ... into slot j mod NS
+        const int a = w - G::kRW;
+        if (a >= J) return;
+        unsigned char *scratch = smem_f + G::kAOff + a * A_WAVE;
+        const float *cwl = reinterpret_cast<const float *>(smem_f + G::kConvOff);
+        ConvW unused;  // the fused body reads its taps from LDS
+        SubTask t0, t1;
+        t0.slot = t1.slot = 0; t0.s0 = t1.s0 = s0; t0.L = t1.L = L; t0.n = t1.n = n;
+        EarlyRows r0, r1;
+        LateRows lr;
+        t0.j = a;
+        load_early(p, t0, h, lane, r0);
+        load_late(p, t0, h, lane, lr);
+        for (int64_t j = a; j < J; j += G::kAW) {
+            t1.j = j + G::kAW;
+            const bool h1 = t1.j < J;
+            wait_slot_free(smem_f, j);
+            intra_sub_chunk<true>(p, scratch, smem_f + (int)(j % NS) * kRecFused, t0, h, lane, r0, lr, unused,
+                                  cwl, h1 ? &t1 : nullptr, r1);
+            lds_word_set(smem_f, G::kReady + 4 * (int)(j % NS), (int)j + 1);
+            t0.j = t1.j;
+            r0 = r1;
+        }
+        return;
+    }
+
+    // ---------------- recurrence and output on tiles 2w, 2w + 1 (columns 32w ..)
+    //   U = U0 - W S,  O = scale (Q~ S + P U),  S = diag(gam) S + Kd^T U
+    int col[2];
+    col[0] = 32 * w + m16;
+    col[1] = 32 * w + 16 + m16;
+    const size_t srow = (size_t)slot * H + h;
+    const bool st16 = p.state_bf16 != 0;
+    f32x4 S[2][8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) load_state_tile(S[t], p.state_in, srow, st16, col[t], g4);
+    if (J > 0) {
+        const int64_t tokstride = (int64_t)H * D;
+        __bf16 *ob = reinterpret_cast<__bf16 *>(p.o) + ((size_t)s0 * tokstride + (size_t)h * D);
+        const uint32_t loff = (uint32_t)col[0] + 4u * (uint32_t)g4 * (uint32_t)tokstride;
+        struct Ops {
+            bf16x8 wn[4], qg[4];
+            bf16x4 kd[8], pp, u0[2];
+            float gv[2];
+        };
+        auto load = [&](int64_t jr, Ops &o) {
+            wait_ready(smem_f, jr);
+            const unsigned char *st = smem_f + (int)(jr % NS) * kRecFused;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                o.wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + (t * 64 + lane) * 16);
+                o.qg[t] = *reinterpret_cast<const bf16x8 *>(st + R_QG + (t * 64 + lane) * 16);
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                o.kd[m] = *reinterpret_cast<const bf16x4 *>(st + R_KD + (m * 64 + lane) * 8);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                o.gv[q] = *reinterpret_cast<const float *>(
+                    st + R_GAM + (64 * q + 16 * (m16 >> 2) + 4 * g4 + (m16 & 3)) * 4);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                o.u0[t] = *reinterpret_cast<const bf16x4 *>(st + R_U0 + ((2 * w + t) * 64 + lane) * 8);
+            o.pp = *reinterpret_cast<const bf16x4 *>(st + R_PP + lane * 8);
+        };
+        auto step = [&](int64_t j, const Ops &c, Ops &nx) {
+            if (j + 1 < J) load(j + 1, nx);
+            bf16x8 Sp[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Sp[t][q] = join8(pack4(S[t][2 * q]), pack4(S[t][2 * q + 1]));
+            f32x4 Ua[2], Uc[2], O[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                Ua[t] = f32x4{(float)c.u0[t].x, (float)c.u0[t].y, (float)c.u0[t].z, (float)c.u0[t].w};
+                Uc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q += 2)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    Ua[t] = mma_k32(c.wn[q], Sp[t][q], Ua[t]);
+                    Uc[t] = mma_k32(c.wn[q + 1], Sp[t][q + 1], Uc[t]);
+                }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) O[t] = mma_k32(c.qg[q], Sp[t][q], O[t]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                decay_tile<0>(S[t][0], c.gv);
+                decay_tile<1>(S[t][1], c.gv);
+                decay_tile<2>(S[t][2], c.gv);
+                decay_tile<3>(S[t][3], c.gv);
+                decay_tile<4>(S[t][4], c.gv);
+                decay_tile<5>(S[t][5], c.gv);
+                decay_tile<6>(S[t][6], c.gv);
+                decay_tile<7>(S[t][7], c.gv);
+            }
+            bf16x4 Ub[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) Ub[t] = pack4(Ua[t] + Uc[t]);
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) S[t][m] = mma_k16(c.kd[m], Ub[t], S[t][m]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) O[t] = mma_k16w(c.pp, Ub[t], O[t]);  // after K = 32 steps
+            __bf16 *orow = ob + (size_t)(16 * j) * tokstride;
+            if (16 * j + 16 <= L) {  // the whole sub-chunk lies in the sequence
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)(p.scale * O[t][i]);
+            } else {
+                const int64_t r0 = 16 * j + 4 * g4;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (r0 + i < L) (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)(p.scale * O[t][i]);
+            }
+            // records 0 .. j + 1 are in registers (or past the end): their slots are free
+            lds_word_set(smem_f, G::kDone + 4 * w, (int)j + 2);
+        };
+        Ops A, B;
+        load(0, A);
+        int64_t j = 0;
+        for (; j + 1 < J; j += 2) {
+            step(j, A, B);
+            step(j + 1, B, A);
+        }
+        if (j < J) step(j, A, B);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) store_state_tile(S[t], p.state_out, srow, st16, col[t], g4);
+}
+
+hipError_t launch_fused(const SplitParams &sp, hipStream_t s) {
+    typedef FusedGeom G;
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
+    });
+    if (attr != hipSuccess) return attr;
+    const unsigned blocks = (unsigned)sp.pairs;
+    hipLaunchKernelGGL(fused_kernel, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
+    trace("fused_kernel grid=(%u) block=%d lds=%d slots=%d", blocks, G::kThreads, G::kLds, G::NS);
+    return hipGetLastError();
+}
+
 hipError_t launch_scan_wide(const SplitParams &sp, hipStream_t s) {
     typedef WideGeom G;
     static std::once_flag once;
@@ -1282,7 +1613,9 @@ size_t split_carry_bytes(int num_seqs, int H) {
     return (size_t)num_seqs * (size_t)H * kHeadDim * kHeadDim * sizeof(float);
 }
 
-hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, const SplitPlan &plan, hipStream_t s) {
+namespace {
+// The kernel parameters every schedule of this file shares.
+SplitParams common_params(const kda_prefill_args *a) {
     SplitParams sp;
     sp.q = a->q; sp.k = a->k; sp.v = a->v; sp.gate = a->gate; sp.beta = a->beta;
     sp.w = a->conv_weight; sp.bias = a->conv_bias; sp.cs_in = a->conv_state_in;
@@ -1296,9 +1629,22 @@ hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, const Sp
     sp.pairs = a->num_seqs * a->num_heads;
     sp.a_heads_fast = 0;
     sp.a_stride = 0;
-    sp.jw = plan.jw;
+    sp.jw = 0;
     sp.win = 0;
     sp.carry = nullptr;
+    sp.nslots = 0;
+    sp.tiles = 1;
+    return sp;
+}
+}  // namespace
+
+hipError_t launch_prefill_fused(const kda_prefill_args *a, hipStream_t s) {
+    return launch_fused(common_params(a), s);
+}
+
+hipError_t launch_prefill_split(const kda_prefill_args *a, int dv_tile, const SplitPlan &plan, hipStream_t s) {
+    SplitParams sp = common_params(a);
+    sp.jw = plan.jw;
     if (plan.jw > 0) {
         // records of one window first, then the carry
         sp.nslots = (int64_t)a->num_seqs * plan.jw;

@@ -44,8 +44,20 @@ class KdaPrefillArgs(ctypes.Structure):
         ("conv_weight", _p), ("conv_bias", _p), ("conv_state_in", _p), ("conv_state_out", _p),
         ("state_in", _p), ("state_out", _p), ("o", _p), ("cu_seqlens", _p),
         ("cu_seqlens_host", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
-        ("state_slots", _p), ("num_slots", _c_i32), ("dv_tile", _c_i32),
+        ("state_slots", _p), ("num_slots", _c_i32), ("dv_tile", _c_i32), ("schedule", _c_i32),
     ]
+
+
+# kda_schedule (include/kda.h)
+SCHEDULES = {"auto": 0, "one_pass": 1, "two_pass": 2, "fused": 3}
+
+
+def _schedule_code(schedule):
+    if isinstance(schedule, str):
+        if schedule not in SCHEDULES:
+            raise ValueError("schedule must be one of %s" % sorted(SCHEDULES))
+        return SCHEDULES[schedule]
+    return int(schedule)
 
 
 class KdaDecodeArgs(ctypes.Structure):
@@ -283,8 +295,8 @@ def kda_short_conv(x, weight, *, cu_seqlens=None, cu_seqlens_host=None, bias=Non
 def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens_host=None,
                 num_seqs=None, conv_bias=None, conv_state_in=None, conv_state_out=None,
                 state_in=None, state_out=None, o=None, scale=0.0, gate_lower_bound=-5.0,
-                chunk_size=0, flags=0, workspace=True, state_slots=None, dv_tile=0, stream=None,
-                _entry="kda_prefill"):
+                chunk_size=0, flags=0, workspace=True, state_slots=None, dv_tile=0, schedule="auto",
+                stream=None, _entry="kda_prefill"):
     """Chunked KDA prefill of packed sequences (kda_prefill).
 
     The state (state_in / state_out) is fp32, or bf16 storage when those tensors are
@@ -294,11 +306,13 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
 
     q, k, gate: [T, H, 128]; v: [T, H, 128]; beta: [T, H] (bf16 or fp32, one dtype);
     conv_weight: [3*H*128, 4] fp32.  state_out / conv_state_out: a tensor, or True
-    to allocate one.  workspace selects the schedule: True (the default) allocates
-    the two-pass workspace wherever that schedule applies (bf16 with chunk_size 0
-    or 16); a uint8 device tensor is used as that workspace; None or False runs
-    the one-pass schedule.  dv_tile: state columns per workgroup (0 = automatic).
-    Returns (o, state_out, conv_state_out)."""
+    to allocate one.  schedule: "auto" (the library's choice), "one_pass",
+    "two_pass" or "fused" (include/kda.h).  workspace: True (the default)
+    allocates the two-pass workspace when the call will run that schedule; a
+    uint8 device tensor is used as that workspace; None or False gives none (the
+    automatic choice then runs the fused or the one-pass schedule).  dv_tile:
+    state columns per workgroup (0 = automatic).  Returns (o, state_out,
+    conv_state_out)."""
     lib = load_library()
     dev = q.device
     if q.dim() != 3:
@@ -361,7 +375,7 @@ def kda_prefill(q, k, v, gate, beta, conv_weight, *, cu_seqlens=None, cu_seqlens
         conv_state_in=_ptr(conv_state_in), conv_state_out=_ptr(conv_state_out),
         state_in=_ptr(state_in), state_out=_ptr(state_out), o=_ptr(o),
         cu_seqlens=_ptr(cu_seqlens), cu_seqlens_host=_ptr(cuh), workspace=None, workspace_bytes=0,
-        dv_tile=int(dv_tile))
+        dv_tile=int(dv_tile), schedule=_schedule_code(schedule))
     pools = (state_in, state_out, conv_state_in, conv_state_out)
     if state_slots is not None and not any(torch.is_tensor(t) for t in pools):
         raise ValueError("state_slots needs a state or conv-state pool")
@@ -391,15 +405,17 @@ def kda_prefill_noalloc(q, k, v, gate, beta, conv_weight, **kw):
 
 
 def prefill_workspace_bytes(total_tokens, num_heads, num_seqs=1, dtype=torch.bfloat16,
-                            chunk_size=0, cu_seqlens_host=None, which="recommended"):
-    """Workspace bytes of the two-pass prefill (0 when it does not apply): the
-    recommended size ("recommended": the whole call up to PREFILL_WORKSPACE_CAP,
-    windows beyond), the whole call at once ("full") or the smallest accepted
-    ("min")."""
+                            chunk_size=0, cu_seqlens_host=None, which="recommended", schedule="auto"):
+    """Workspace bytes of the two-pass prefill: the recommended size
+    ("recommended": the whole call up to PREFILL_WORKSPACE_CAP, windows beyond; 0
+    when the call will not run two passes), the whole call at once ("full") or
+    the smallest accepted ("min"; both 0 when the dtype or chunk excludes the
+    schedule)."""
     lib = load_library()
     a = KdaPrefillArgs(num_seqs=int(num_seqs), num_heads=int(num_heads), head_dim_k=128,
                        head_dim_v=128, chunk_size=int(chunk_size), total_tokens=int(total_tokens),
-                       dtype=KDA_BF16 if dtype == torch.bfloat16 else KDA_F32)
+                       dtype=KDA_BF16 if dtype == torch.bfloat16 else KDA_F32,
+                       schedule=_schedule_code(schedule))
     cuh = None
     if cu_seqlens_host is not None:
         cuh = torch.as_tensor(cu_seqlens_host).to(torch.int32).contiguous().cpu()

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum {
     KDA_OK = 0,
@@ -153,12 +153,11 @@ typedef struct {
     int32_t num_heads;       /* H >= 1 */
     int32_t head_dim_k;      /* must be 128 */
     int32_t head_dim_v;      /* must be 128 */
-    int32_t chunk_size;      /* 0 = default; 16, 32 or 64.  The default is the
-                                two-pass schedule (16-token sub-chunks) when a
-                                workspace is given, else one pass with 64-token
-                                chunks for bf16 and 32-token chunks for fp32 I/O
-                                (an fp32 64-token chunk does not fit in LDS:
-                                KDA_ERR_UNSUPPORTED) */
+    int32_t chunk_size;      /* 0 = default; 16, 32 or 64.  The fused and two-pass
+                                schedules use 16-token sub-chunks (0 or 16); the
+                                one-pass default is 64-token chunks for bf16 and
+                                32-token chunks for fp32 I/O (an fp32 64-token
+                                chunk does not fit in LDS: KDA_ERR_UNSUPPORTED) */
     int64_t total_tokens;    /* 0 <= T <= 2^31 - 64 (token offsets are int32) */
     kda_dtype dtype;
     uint32_t flags;          /* KDA_F_* */
@@ -183,20 +182,43 @@ typedef struct {
     int32_t num_slots;         /* pool rows when state_slots is given */
     int32_t dv_tile;           /* state columns per workgroup: 0 = chosen from the
                                   number of (sequence, head) pairs; else 32, 64 or
-                                  128 (and 16 for the two-pass schedule).  Changes
-                                  which workgroup computes a column, never the
+                                  128 (and 16 for the two-pass schedule; the fused
+                                  schedule takes 0 or 128).  Changes which
+                                  workgroup computes a column, never the
                                   arithmetic: results are bit-identical. */
+    int32_t schedule;          /* KDA_SCHEDULE_*; 0 = chosen (see below) */
 } kda_prefill_args;
 
+typedef enum {
+    KDA_SCHEDULE_AUTO = 0,
+    KDA_SCHEDULE_ONE_PASS = 1,
+    KDA_SCHEDULE_TWO_PASS = 2,
+    KDA_SCHEDULE_FUSED = 3,
+} kda_schedule;
+
+/* The automatic choice takes the fused schedule from this many (sequence, head)
+ * pairs on (bf16 I/O, chunk_size 0 or 16). */
+#define KDA_FUSED_MIN_PAIRS 1024
+
 /*
- * Two schedules compute the same mixer (identical in exact arithmetic):
- *   - one pass: each workgroup owns a (sequence, head, dv tile) and runs the
- *     chunk's WY/UT transform itself (chunk_size 16, 32 or 64; default 64);
- *   - two passes (bf16 I/O with chunk_size 0 or 16), chosen when a workspace is
- *     given: a fully parallel pass turns every 16-token sub-chunk of every head
- *     into matrix-core operands in the workspace (13,824 bytes per sub-chunk and
+ * Three schedules compute the same mixer (identical in exact arithmetic):
+ *   - one pass (KDA_SCHEDULE_ONE_PASS): each workgroup owns a (sequence, head,
+ *     dv tile) and runs the chunk's WY/UT transform itself (chunk_size 16, 32 or
+ *     64; default 64); any dtype, no workspace;
+ *   - two passes (KDA_SCHEDULE_TWO_PASS; bf16 I/O, chunk_size 0 or 16): a fully
+ *     parallel pass turns every 16-token sub-chunk of every head into
+ *     matrix-core operands in the workspace (13,824 bytes per sub-chunk and
  *     head), and a second pass carries the state over them.  It keeps the whole
- *     GPU busy when there are few (sequence, head) pairs.
+ *     GPU busy when there are few (sequence, head) pairs;
+ *   - fused (KDA_SCHEDULE_FUSED; bf16 I/O, chunk_size 0 or 16): one workgroup
+ *     per (sequence, head) forms the same 16-token operands in its own LDS while
+ *     it carries the state over them, so they never reach memory; no workspace.
+ *     It needs enough pairs to fill the GPU (one workgroup per compute unit).
+ * KDA_SCHEDULE_AUTO takes the fused schedule when it applies and there are at
+ * least KDA_FUSED_MIN_PAIRS pairs, else two passes when a workspace is given,
+ * else one pass.  An explicit schedule that the dtype or chunk_size excludes
+ * returns KDA_ERR_UNSUPPORTED; KDA_SCHEDULE_TWO_PASS without a workspace returns
+ * KDA_ERR_INVALID_ARG.  The fused and one-pass schedules ignore the workspace.
  * Workspace and windows.  A workspace of kda_prefill_workspace_full_size()
  * bytes runs the whole call at once.  A smaller one, of at least
  * kda_prefill_workspace_min_size() bytes, runs it in windows: every sequence
@@ -214,19 +236,21 @@ typedef struct {
 kda_status kda_prefill(const kda_prefill_args *args, hipStream_t stream);
 
 /* Recommended workspace bytes for the two-pass schedule (whole call when that
- * fits in KDA_PREFILL_WORKSPACE_CAP, else windows within it); 0 when that
- * schedule does not apply (fp32 I/O or an explicit chunk_size of 32 or 64).
- * Depends on num_seqs, num_heads, total_tokens, dtype, chunk_size and, for the
- * window count, cu_seqlens_host. */
+ * fits in KDA_PREFILL_WORKSPACE_CAP, else windows within it); 0 when the call
+ * will not run that schedule (fp32 I/O, an explicit chunk_size of 32 or 64, an
+ * explicit one-pass or fused schedule, or the automatic choice of the fused
+ * one).  Depends on num_seqs, num_heads, total_tokens, dtype, chunk_size,
+ * schedule and, for the window count, cu_seqlens_host. */
 #define KDA_PREFILL_WORKSPACE_CAP ((size_t)4 << 30)
 size_t kda_prefill_workspace_size(const kda_prefill_args *args);
 
-/* Workspace bytes for the whole call in one window (no cap). */
+/* Two-pass workspace bytes for the whole call in one window (no cap); 0 when
+ * the dtype or chunk_size excludes the two-pass schedule. */
 size_t kda_prefill_workspace_full_size(const kda_prefill_args *args);
 
 /* Smallest workspace the two-pass schedule accepts: one sub-chunk per sequence
  * per window plus the carry (or the whole call, if that is smaller); 0 when the
- * schedule does not apply. */
+ * dtype or chunk_size excludes the schedule. */
 size_t kda_prefill_workspace_min_size(const kda_prefill_args *args);
 
 /*
@@ -236,8 +260,9 @@ size_t kda_prefill_workspace_min_size(const kda_prefill_args *args);
  * `workspace` must be NULL and `workspace_bytes` 0 (else KDA_ERR_INVALID_ARG):
  * the two-pass schedule (bf16 I/O, chunk_size 0 or 16) runs in a scratch array
  * of KDA_PREFILL_SCRATCH_BYTES that the library holds on every GPU it runs on
- * until the process ends, in windows when the call needs more than that; other
- * inputs run the one-pass schedule, which needs no scratch.  The call allocates
+ * until the process ends, in windows when the call needs more than that; the
+ * fused and one-pass schedules need no scratch.  The schedule is chosen as for
+ * kda_prefill, with the scratch array as the workspace.  The call allocates
  * nothing.  A call whose smallest two-pass workspace
  * (kda_prefill_workspace_min_size) exceeds the scratch returns
  * KDA_ERR_INVALID_ARG: use kda_prefill with a workspace for it.  Every call on

@@ -36,6 +36,9 @@ size_t split_window_bytes(int N, int H, int64_t jw) { return (size_t)H * N * jw 
 hipError_t launch_prefill_split(const kda_prefill_args *, int dv, const SplitPlan &plan, hipStream_t) {
     ++g_launch; g_dv = dv; g_plan = plan; return hipSuccess;
 }
+hipError_t launch_prefill_fused(const kda_prefill_args *, hipStream_t) {
+    ++g_launch; g_plan.jw = -3; return hipSuccess;
+}
 }  // namespace kda
 
 static int failures = 0;
@@ -85,7 +88,12 @@ int main() {
         a.cu_seqlens_host = cu.data();
         a.state_in = addr(13); a.state_out = addr(14);
         kda::g_launch = 0;
-        CHECK(kda_prefill(&a, nullptr) == KDA_OK && kda::g_plan.jw == -2, "no workspace: one pass");
+        CHECK(kda_prefill(&a, nullptr) == KDA_OK && kda::g_plan.jw == -3, "1024 pairs: fused");
+        CHECK(kda_prefill_workspace_size(&a) == 0, "the fused schedule needs no workspace");
+        a.schedule = KDA_SCHEDULE_ONE_PASS;
+        CHECK(kda_prefill(&a, nullptr) == KDA_OK && kda::g_plan.jw == -2, "explicit one pass");
+        a.schedule = KDA_SCHEDULE_TWO_PASS;
+        CHECK(kda_prefill(&a, nullptr) == KDA_ERR_INVALID_ARG, "two passes without a workspace");
         const size_t full = kda_prefill_workspace_full_size(&a);
         CHECK(full == (size_t)H * (T / 16 + N) * kda::kRecBytes, "full size");
         a.workspace = addr(15); a.workspace_bytes = full;

@@ -46,7 +46,7 @@ def test_calibration_library_exports_and_rejects_bad_arguments():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == 5
+    assert lib.kda_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -64,7 +64,8 @@ def test_struct_layouts_match_header():
     assert K.KdaPrefillArgs.state_slots.offset == 48 + 16 * 8
     assert K.KdaPrefillArgs.num_slots.offset == 48 + 17 * 8
     assert K.KdaPrefillArgs.dv_tile.offset == 48 + 17 * 8 + 4
-    assert ctypes.sizeof(K.KdaPrefillArgs) == 48 + 18 * 8
+    assert K.KdaPrefillArgs.schedule.offset == 48 + 18 * 8
+    assert ctypes.sizeof(K.KdaPrefillArgs) == 48 + 19 * 8
     assert K.KdaDecodeArgs.q.offset == 32
     assert K.KdaDecodeArgs.state_slots.offset == 32 + 10 * 8
     assert ctypes.sizeof(K.KdaDecodeArgs) == 32 + 12 * 8
@@ -403,7 +404,7 @@ def test_workspace_is_bounded(lib, T, N, H):
     sub-chunk per sequence plus the carry, or the whole call if smaller."""
     REC = _rec_bytes(lib)
     assert REC % 512 == 0 and REC <= 16384  # 13.5 KiB: no V part
-    a = _prefill_args(total_tokens=T, num_seqs=N, num_heads=H, cu_seqlens=FAKE)
+    a = _prefill_args(total_tokens=T, num_seqs=N, num_heads=H, cu_seqlens=FAKE, schedule=2)
     full = lib.kda_prefill_workspace_full_size(ctypes.byref(a))
     rec = lib.kda_prefill_workspace_size(ctypes.byref(a))
     mini = lib.kda_prefill_workspace_min_size(ctypes.byref(a))
@@ -469,6 +470,47 @@ def test_prefill_rejects_bad_dv_tile(lib, dv_tile, status):
     a = _prefill_args(dv_tile=dv_tile)
     assert lib.kda_prefill(ctypes.byref(a), None) == status
     assert b"dv_tile" in lib.kda_last_error()
+
+
+@pytest.mark.parametrize("schedule,dtype,chunk,ws,status,msg", [
+    (7, K.KDA_BF16, 0, False, K.KDA_ERR_INVALID_ARG, b"schedule"),
+    (-1, K.KDA_BF16, 0, False, K.KDA_ERR_INVALID_ARG, b"schedule"),
+    (2, K.KDA_BF16, 0, False, K.KDA_ERR_INVALID_ARG, b"workspace"),   # two passes need one
+    (2, K.KDA_F32, 0, True, K.KDA_ERR_UNSUPPORTED, b"two-pass"),
+    (3, K.KDA_F32, 0, False, K.KDA_ERR_UNSUPPORTED, b"fused"),
+    (3, K.KDA_BF16, 64, False, K.KDA_ERR_UNSUPPORTED, b"fused"),
+])
+def test_prefill_rejects_schedules_that_do_not_apply(lib, schedule, dtype, chunk, ws, status, msg):
+    a = _prefill_args(schedule=schedule, dtype=dtype, chunk_size=chunk)
+    if ws:
+        a.workspace = ctypes.c_void_p(0x70000000)
+        a.workspace_bytes = 1 << 30
+    assert lib.kda_prefill(ctypes.byref(a), None) == status
+    assert msg in lib.kda_last_error(), lib.kda_last_error()
+
+
+def test_fused_schedule_takes_whole_heads_only(lib):
+    a = _prefill_args(schedule=3, dv_tile=32)
+    assert lib.kda_prefill(ctypes.byref(a), None) == K.KDA_ERR_UNSUPPORTED
+    assert b"fused" in lib.kda_last_error() and b"dv_tile" in lib.kda_last_error()
+
+
+def test_workspace_size_follows_the_schedule(lib):
+    """The recommended workspace is the two-pass one only when the call will run
+    two passes: not for an explicit one-pass or fused schedule, and not when the
+    automatic choice is the fused schedule (from KDA_FUSED_MIN_PAIRS pairs on)."""
+    few = _prefill_args(num_seqs=2, num_heads=64, total_tokens=4096)
+    full = lib.kda_prefill_workspace_full_size(ctypes.byref(few))
+    assert full > 0 and lib.kda_prefill_workspace_size(ctypes.byref(few)) == full
+    for sched, want in ((1, 0), (2, full), (3, 0)):
+        few.schedule = sched
+        assert lib.kda_prefill_workspace_size(ctypes.byref(few)) == want
+    many = _prefill_args(num_seqs=16, num_heads=64, total_tokens=16 * 256)
+    assert 16 * 64 >= 1024  # KDA_FUSED_MIN_PAIRS
+    assert lib.kda_prefill_workspace_size(ctypes.byref(many)) == 0
+    many.schedule = 2
+    assert lib.kda_prefill_workspace_size(ctypes.byref(many)) == lib.kda_prefill_workspace_full_size(
+        ctypes.byref(many)) > 0
 
 
 # Every buffer a prefill call writes (o, state_out, conv_state_out, workspace) is

@@ -1,8 +1,9 @@
 """Full-size GPU parity: every (sequence, head) pair of the three prefill workloads
 (1 x 4096 tokens; 1 x 65,536 tokens with decays near the bound; 16 packed
 sequences of 512..16,384 tokens with initial states) and every sequence of the
-256-sequence decode step, on the launch configuration the benchmark times and
-on the one-pass schedule, against the fp64 oracle.
+256-sequence decode step, on every prefill schedule (the benchmark times the
+automatic choice: two passes for the single sequences, fused for the 16), against
+the fp64 oracle.
 
 o is checked per (sequence, head) slice and per 16-token block of each slice
 (relative L2 <= 2e-2, see tests/_gpu_common.py); the final state per (sequence,
@@ -39,9 +40,10 @@ def _lib():
 
 
 def _schedules():
-    # the benchmarked two-pass schedule (the binding's default for bf16) and the
-    # one-pass schedule with 64-token chunks
-    return {"two_pass": {}, "one_pass_chunk64": {"chunk_size": 64, "workspace": None}}
+    # the three schedules: two passes (the default for few pairs), fused (the
+    # default from 1024 pairs on) and one pass with 64-token chunks
+    return {"two_pass": {"schedule": "two_pass"}, "fused": {"schedule": "fused"},
+            "one_pass_chunk64": {"chunk_size": 64, "workspace": None, "schedule": "one_pass"}}
 
 
 def _run_gpu(inp, **kw):
@@ -88,7 +90,7 @@ def test_prefill_full_size_every_head(workload):
     _progress("workload %d: %d tokens, %d sequences" % (workload, inp["q"].shape[0],
                                                          len(inp["lengths"])))
     results = {name: _run_gpu(inp, **kw) for name, kw in _schedules().items()}
-    _progress("workload %d: both schedules ran" % workload)
+    _progress("workload %d: every schedule ran" % workload)
     worst = _check_all_heads(inp, results)
     print("workload %d: worst final-state rel err %s" % (workload, worst))
 

@@ -1,0 +1,152 @@
+"""The fused prefill schedule (one workgroup per (sequence, head): the 16-token
+operands are formed in LDS while the state is carried over them) against the
+fp64 oracle, on ragged lengths and every flag, and the properties the other
+schedules keep: bf16 state storage equals fp32 storage rounded once, pool slots
+equal gathered rows, in-place state, a split sequence equals the whole one bit for
+bit, determinism, and the automatic choice for many pairs."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as KI
+import oracle
+import gated_delta_rule_short_amd as kda
+from tests._gpu_common import assert_bf16_close, seeded, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kda.load_library()
+
+
+def _oracle(inp, **kw):
+    return oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["conv_w"],
+                          inp["cu_seqlens"], state_in=inp.get("state_in"),
+                          conv_state_in=inp.get("conv_state_in"), **kw)
+
+
+def _fused(inp, **kw):
+    kw.setdefault("schedule", "fused")
+    kw.setdefault("state_out", True)
+    kw.setdefault("conv_state_out", True)
+    o, st, cs = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                                inp["conv_w"], cu_seqlens=inp["cu_seqlens"],
+                                state_in=inp.get("state_in"),
+                                conv_state_in=inp.get("conv_state_in"), **kw)
+    torch.cuda.synchronize()
+    return o, st, cs
+
+
+LENGTHS = [1, 2, 3, 15, 16, 17, 0, 63, 64, 65, 130, 200, 1000]
+
+
+@pytest.mark.parametrize("flags", [0, kda.KDA_F_SILU, kda.KDA_F_NO_QK_L2NORM, kda.KDA_F_GATE_IS_LOG])
+def test_fused_ragged_matches_oracle(flags):
+    inp = KI.make_prefill(3, LENGTHS, seed=231, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    if flags & kda.KDA_F_GATE_IS_LOG:
+        inp["gate"] = (-6.0 * seeded(inp["gate"].shape, 232, "rand")).to(torch.bfloat16)
+    if flags & kda.KDA_F_NO_QK_L2NORM:
+        # without the L2 norm the caller scales k (beta |k|^2 < 1 keeps the delta rule
+        # contractive, so bf16 rounding does not grow along the sequence)
+        inp["k"] = (0.5 * inp["k"].float()).to(torch.bfloat16)
+    bias = 0.1 * seeded(inp["conv_w"].shape[0], 233)
+    ref = _oracle(inp, conv_b=bias, flags=flags)
+    o, st, cs = _fused(inp, conv_bias=bias, flags=flags)
+    assert_bf16_close(o, ref["o"], inp["cu_seqlens"], 3, st, ref["state"], "fused")
+    np.testing.assert_array_equal(to_np(cs), ref["conv_state"])
+
+
+def test_fused_without_initial_state_and_near_degenerate_keys():
+    """No initial state or conv cache (zeros); then beta = 1 with nearly parallel
+    keys and a weak decay, where the triangular inverse is hardest."""
+    H, lengths = 2, [16, 47, 100, 333]
+    inp = KI.make_prefill(H, lengths, seed=241, device=DEV)
+    inp.pop("state_in", None)
+    inp.pop("conv_state_in", None)
+    ref = _oracle(inp)
+    o, st, _ = _fused(inp)
+    assert_bf16_close(o, ref["o"], inp["cu_seqlens"], H, st, ref["state"], "zero initial state")
+    T = sum(lengths)
+    base = seeded((1, H, 128), 242)
+    inp["k"] = (base + 0.05 * seeded((T, H, 128), 243)).to(torch.bfloat16)
+    inp["beta"] = torch.ones((T, H), dtype=torch.bfloat16, device=DEV)
+    inp["gate"] = torch.full((T, H, 128), -4.0, dtype=torch.bfloat16, device=DEV)
+    ref = _oracle(inp)
+    o, st, _ = _fused(inp)
+    assert torch.isfinite(o).all() and torch.isfinite(st).all()
+    assert_bf16_close(o, ref["o"], inp["cu_seqlens"], H, st, ref["state"], "near-degenerate keys")
+
+
+def test_fused_split_equals_whole_in_place_and_deterministic():
+    inp = KI.make_prefill(2, [300], seed=251, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    o, st, cs = _fused(inp)
+    o2, st2, cs2 = _fused(inp)
+    assert torch.equal(o, o2) and torch.equal(st, st2) and torch.equal(cs, cs2)
+    cut = 112  # a multiple of 16: sub-chunk boundaries coincide
+    a = {k_: (v_[:cut] if k_ in ("q", "k", "v", "gate", "beta") else v_) for k_, v_ in inp.items()}
+    a["cu_seqlens"] = torch.tensor([0, cut], dtype=torch.int32, device=DEV)
+    oa, sta, csa = _fused(a)
+    b = {k_: (v_[cut:] if k_ in ("q", "k", "v", "gate", "beta") else v_) for k_, v_ in inp.items()}
+    b["cu_seqlens"] = torch.tensor([0, 300 - cut], dtype=torch.int32, device=DEV)
+    b["state_in"], b["conv_state_in"] = sta, csa
+    ob, stb, csb = _fused(b)
+    assert torch.equal(torch.cat([oa, ob]), o) and torch.equal(stb, st) and torch.equal(csb, cs)
+    # in place: state_out = state_in, conv_state_out = conv_state_in
+    s_io = inp["state_in"].clone()
+    c_io = inp["conv_state_in"].clone()
+    inp2 = dict(inp, state_in=s_io, conv_state_in=c_io)
+    o3, _, _ = _fused(inp2, state_out=s_io, conv_state_out=c_io)
+    assert torch.equal(o3, o) and torch.equal(s_io, st) and torch.equal(c_io, cs)
+
+
+def test_fused_bf16_state_and_pool_slots():
+    """bf16 state storage equals fp32 storage of the same state rounded once at the
+    end; pool slots map each sequence to its rows and leave the others alone."""
+    H, lengths = 2, [70, 0, 33, 160]
+    inp = KI.make_prefill(H, lengths, seed=261, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    s16 = inp["state_in"].to(torch.bfloat16)
+    o_a, st_a, _ = _fused(dict(inp, state_in=s16))
+    o_b, st_b, _ = _fused(dict(inp, state_in=s16.float()))
+    assert torch.equal(o_a, o_b) and torch.equal(st_a, st_b.to(torch.bfloat16))
+    slots = torch.tensor([5, 0, 3, 1], dtype=torch.int32, device=DEV)
+    pool = seeded((6, H, 128, 128), 262)
+    pool[slots.long()] = inp["state_in"]
+    cpool = seeded((6, 3, 3 * H * 128), 263).to(torch.bfloat16)
+    cpool[slots.long()] = inp["conv_state_in"]
+    untouched = [r for r in range(6) if r not in slots.tolist()]
+    keep_s, keep_c = pool[untouched].clone(), cpool[untouched].clone()
+    o_p, _, _ = _fused(dict(inp, state_in=pool, conv_state_in=cpool), state_out=pool,
+                       conv_state_out=cpool, state_slots=slots)
+    o_w, st_w, cs_w = _fused(inp)
+    assert torch.equal(o_p, o_w)
+    assert torch.equal(pool[slots.long()], st_w) and torch.equal(cpool[slots.long()], cs_w)
+    assert torch.equal(pool[untouched], keep_s) and torch.equal(cpool[untouched], keep_c)
+
+
+def test_many_pairs_choose_the_fused_schedule():
+    """From 1024 (sequence, head) pairs the automatic choice is the fused schedule:
+    the recommended workspace is 0 and the default call equals an explicit fused
+    call bit for bit; an explicit two-pass call of the same input stays within
+    the bar of it."""
+    lengths = [40, 17, 64, 5] * 4
+    H = 64
+    inp = KI.make_prefill(H, lengths, seed=271, device=DEV, state_std=0.1)
+    T = sum(lengths)
+    assert kda.prefill_workspace_bytes(T, H, len(lengths)) == 0
+    auto = _fused(inp, schedule="auto")
+    fused = _fused(inp)
+    assert torch.equal(auto[0], fused[0]) and torch.equal(auto[1], fused[1])
+    two = _fused(inp, schedule="two_pass", workspace=True)
+    heads = [0, 63]
+    cu = inp["cu_seqlens"].cpu()
+    from tests._gpu_common import head_conv_w
+    ref = oracle.prefill(inp["q"][:, heads], inp["k"][:, heads], inp["v"][:, heads],
+                         inp["gate"][:, heads], inp["beta"][:, heads],
+                         head_conv_w(inp["conv_w"], H, heads), cu,
+                         state_in=inp["state_in"][:, heads])
+    for name, (o, st, _) in (("fused", fused), ("two-pass", two)):
+        assert_bf16_close(o[:, heads], ref["o"], cu, len(heads), st[:, heads], ref["state"], name)

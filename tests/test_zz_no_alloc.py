@@ -80,8 +80,11 @@ def test_noalloc_rejects_a_workspace_and_calls_beyond_the_scratch():
     a.workspace, a.workspace_bytes = ctypes.c_void_p(0x200000), 1 << 20
     assert lib.kda_prefill_noalloc(ctypes.byref(a), None) == K.KDA_ERR_INVALID_ARG
     assert b"no workspace" in lib.kda_last_error()
+    # an explicit two-pass call whose smallest workspace exceeds the scratch (the
+    # automatic choice for these 262,144 pairs is the fused schedule, which needs none)
     b = K.KdaPrefillArgs(num_seqs=4096, num_heads=64, head_dim_k=128, head_dim_v=128,
-                         total_tokens=4096 * 64, dtype=kda.KDA_BF16, gate_lower_bound=-5.0)
+                         total_tokens=4096 * 64, dtype=kda.KDA_BF16, gate_lower_bound=-5.0,
+                         schedule=kda.SCHEDULES["two_pass"])
     assert lib.kda_prefill_workspace_min_size(ctypes.byref(b)) > kda.PREFILL_SCRATCH_BYTES
     assert lib.kda_prefill_noalloc(ctypes.byref(b), None) == K.KDA_ERR_INVALID_ARG
     assert b"scratch" in lib.kda_last_error()
