@@ -302,12 +302,14 @@ constexpr int kConvLdsBytes = 3 * 128 * 5 * 4;
 // reads them (into lr), so that they land while this sub-chunk finishes.  All
 // scratch LDS traffic stays inside the wave's region.  FU (the fused schedule)
 // also convolves v and writes U0 = X diag(beta) V in place of X diag(beta); its
-// conv taps come from LDS (cwl) instead of registers (cw).
-template <bool FU>
+// conv taps come from LDS (cwl) instead of registers (cw).  before_rec() runs
+// right before the first write to rec (the fused schedule waits there for its
+// ring slot, after the gate, which needs no slot).
+template <bool FU, class BeforeRec>
 __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, unsigned char *rec,
                                                 const SubTask &tk, int h, int lane, const EarlyRows &er,
                                                 LateRows &lr, const ConvW &cw, const float *cwl,
-                                                const SubTask *nx, EarlyRows &ner) {
+                                                const SubTask *nx, EarlyRows &ner, BeforeRec &&before_rec) {
     constexpr int D = kHeadDim;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int64_t s0 = tk.s0, L = tk.L, j = tk.j;
@@ -407,6 +409,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         fd[e] = exp2_fast(-gs);
         run[15][e] = exp2_fast(gs);  // equal up to rounding; the record takes the direct form
     }
+    before_rec();
     {
         f32x2 gm = {run[15][0], run[15][1]};
         *reinterpret_cast<f32x2 *>(rec + R_GAM + 4 * c0) = gm;
@@ -648,10 +651,10 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     load_late(p, ta, h, lane, lr);
     const bool hb = next_task(p, ta.slot + stride, stride, tb);
     intra_sub_chunk<false>(p, lds, p.ws + ((size_t)h * p.nslots + ta.slot) * kRec, ta, h, lane, ra, lr, cw,
-                           nullptr, hb ? &tb : nullptr, rb);
+                           nullptr, hb ? &tb : nullptr, rb, [] {});
     if (hb)
         intra_sub_chunk<false>(p, lds, p.ws + ((size_t)h * p.nslots + tb.slot) * kRec, tb, h, lane, rb, lr, cw,
-                               nullptr, nullptr, ra);
+                               nullptr, nullptr, ra, [] {});
 }
 
 // Pass B geometry.  Per 16-column dv tile one recurrence wave (R: all 128 dk
@@ -1428,9 +1431,8 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
         for (int64_t j = a; j < J; j += G::kAW) {
             t1.j = j + G::kAW;
             const bool h1 = t1.j < J;
-            wait_slot_free(smem_f, j);
             intra_sub_chunk<true>(p, scratch, smem_f + (int)(j % NS) * kRecFused, t0, h, lane, r0, lr, unused,
-                                  cwl, h1 ? &t1 : nullptr, r1);
+                                  cwl, h1 ? &t1 : nullptr, r1, [&] { wait_slot_free(smem_f, j); });
             lds_word_set(smem_f, G::kReady + 4 * (int)(j % NS), (int)j + 1);
             t0.j = t1.j;
             r0 = r1;
