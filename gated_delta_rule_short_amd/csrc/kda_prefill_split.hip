@@ -157,9 +157,10 @@ __device__ __forceinline__ void l2_scale(const float (&y)[16][2], bool l2, int l
 
 // One pass-A task: sub-chunk j (rows 16 j .. 16 j + 15) of sequence n, which
 // starts at token s0 and holds L tokens.
+// Token positions are 32-bit (the token count is below 2^31), which keeps the
+// per-row address arithmetic in single scalar instructions.
 struct SubTask {
-    int64_t slot, s0, L, j;
-    int n;
+    int slot, s0, L, j, n;
 };
 
 // Raw inputs of one sub-chunk for this lane's two channels, as packed bf16
@@ -209,8 +210,8 @@ struct RowWindow {
 };
 __device__ __forceinline__ RowWindow row_window(const SubTask &tk, int first) {
     RowWindow w;
-    w.p0 = 16 * (int)tk.j;
-    w.L = (int)tk.L;
+    w.p0 = 16 * tk.j;
+    w.L = tk.L;
     int lo = w.p0 + first, hi = w.p0 + 15;
     lo = lo < 0 ? 0 : (lo >= w.L ? w.L - 1 : lo);
     hi = hi >= w.L ? w.L - 1 : hi;
@@ -225,11 +226,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *x, const 
     const char *b = reinterpret_cast<const char *>(x) + (size_t)h * kHeadDim * 2 + (size_t)(tk.s0 + w.lo) * rowbytes;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(b), 0, (int)((w.hi - w.lo + 1) * rowbytes), 0x00020000);
 }
-// Byte offset of sub-chunk row r (-3 .. 15), clamped into the sequence, in the window.
+// Byte offset of sub-chunk row r (-3 .. 15), clamped into the sequence, in the
+// window: the rows lo .. hi are consecutive, so the clamp is one of the row index
+// relative to lo into [0, hi - lo].
 __device__ __forceinline__ int row_soff(const RowWindow &w, int r, int rowbytes) {
-    int sp = w.p0 + r;
-    sp = sp < 0 ? 0 : (sp >= w.L ? w.L - 1 : sp);
-    return (sp - w.lo) * rowbytes;
+    int i = w.p0 - w.lo + r;
+    i = i < 0 ? 0 : i;
+    i = i > w.hi - w.lo ? w.hi - w.lo : i;
+    return i * rowbytes;
 }
 
 // The three rows before a sequence for tensor t (0 q, 1 k, 2 v): conv state or zeros.
@@ -261,9 +265,10 @@ __device__ __forceinline__ void load_early(const SplitParams &p, const SubTask &
         r.xk[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, row_soff(wk, i - 3, rowbytes), 0);
     // unconditional load from a row inside the sequence; the conversion and the
     // mask wait for the use, so this load does not force a wait on the others
-    int br = 16 * (int)tk.j + (lane & 15);
-    br = br < (int)tk.L ? br : (int)tk.L - 1;
-    r.beta_bits = *reinterpret_cast<const unsigned short *>(reinterpret_cast<const T *>(p.beta) + (tk.s0 + br) * p.H + h);
+    int br = 16 * tk.j + (lane & 15);
+    br = br < tk.L ? br : tk.L - 1;
+    r.beta_bits = *reinterpret_cast<const unsigned short *>(reinterpret_cast<const T *>(p.beta) +
+                                                            ((size_t)tk.s0 + br) * p.H + h);
     if (tk.j == 0) load_history(p, tk, h, lane, 1, r.xk);
 }
 
@@ -312,9 +317,8 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
                                                 const SubTask *nx, EarlyRows &ner, BeforeRec &&before_rec) {
     constexpr int D = kHeadDim;
     const int m16 = lane & 15, g4 = lane >> 4;
-    const int64_t s0 = tk.s0, L = tk.L, j = tk.j;
-    const int64_t p0 = 16 * j;
-    const int rem = (int)(L - p0);  // rows of the sequence from p0 on (32-bit: scalar compares)
+    const int p0 = 16 * tk.j;
+    const int rem = tk.L - p0;  // rows of the sequence from p0 on
     const bool edge = p0 < 3 || rem < 16;
     const bool silu = p.flags & KDA_F_SILU;
     const bool l2 = !(p.flags & KDA_F_NO_QK_L2NORM);
@@ -565,28 +569,25 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     }
     wave_sync_lds();
 
-    // ---- W = X diag(beta) (K . 2^b), staged row-major (negated) in the dead KL
-    // area; with FU also U0 = X (diag(beta) V) straight to the record in
-    // accumulator layout
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        const int col = 16 * nt + m16;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 wr = mma_k16(xfr, OPB::load4raw(sKGT + col * A_STR + 4 * g4), z);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sKL[(4 * g4 + i) * A_SRM + col] = (__bf16)(-wr[i]);
-        if constexpr (FU) {
-            const __bf16 *sVT = reinterpret_cast<const __bf16 *>(lds + A_VT);
-            const f32x4 ur = mma_k16(xfr, OPB::load4raw(sVT + col * A_VTS + 4 * g4), z);
-            *reinterpret_cast<bf16x4 *>(rec + R_U0 + ((size_t)nt * 64 + lane) * 8) = pack4(ur);
-        }
-    }
-    wave_sync_lds();
+    // ---- W = X diag(beta) (K . 2^b), formed transposed: W^T = (diag(beta) K . 2^b)^T X^T
+    // puts row r of W, channels 16 nt + 4 g4 .. + 3, in lane r + 16 g4 of tile nt,
+    // which is the A-operand fragment pass B reads (tiles 2t and 2t + 1 give the two
+    // halves of fragment t), so W goes to the record without an LDS round trip.
+    // With FU also U0 = X (diag(beta) V) to the record in accumulator layout.
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const __bf16 *row = sKL + m16 * A_SRM + 32 * t + 4 * g4;
-        bf16x8 f = join8(*reinterpret_cast<const bf16x4 *>(row), *reinterpret_cast<const bf16x4 *>(row + 16));
-        *reinterpret_cast<bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16) = f;
+        const f32x4 w0 = mma_k16(OPB::load4raw(sKGT + (32 * t + m16) * A_STR + 4 * g4), xfr, z);
+        const f32x4 w1 = mma_k16(OPB::load4raw(sKGT + (32 * t + 16 + m16) * A_STR + 4 * g4), xfr, z);
+        *reinterpret_cast<bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16) = join8(pack4(-w0), pack4(-w1));
+    }
+    if constexpr (FU) {
+        const __bf16 *sVT = reinterpret_cast<const __bf16 *>(lds + A_VT);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const f32x4 ur = mma_k16(xfr, OPB::load4raw(sVT + (16 * nt + m16) * A_VTS + 4 * g4), z);
+            *reinterpret_cast<bf16x4 *>(rec + R_U0 + ((size_t)nt * 64 + lane) * 8) = pack4(ur);
+        }
     }
 }
 
