@@ -99,6 +99,14 @@ def roofline(bytes_, seconds, traffic=None, **extra):
     r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
          "algorithmic_bytes_per_launch": int(bytes_)}
+    if traffic is not None:
+        # counted bytes over the measured time: a rate above the peak means the
+        # summary does not describe this run, so it is not reported as traffic
+        rate = traffic / seconds / 1e9
+        r["traffic_GBps"] = round(rate, 1)
+        if rate > HBM_PEAK_GBS:
+            r["traffic"] = None
+            r["traffic_note"] = "counted bytes / time exceed the HBM peak: summary not used"
     r.update(extra)
     return r
 
