@@ -678,10 +678,15 @@ template <int NTW> struct ScanGeom {
     // DMA instructions of producer pw per stage (it takes i = pw mod NP)
     static constexpr int inst_of(int pw) { return (kInst + NP - 1 - pw) / NP; }
     static constexpr int kInstP0 = inst_of(0);
-    static constexpr int kWaves = 2 * NTW + NP;
+    // With two tiles a third wave per tile forms U0 (UW); one tile keeps it on the
+    // recurrence wave, since seven waves would not leave two workgroups per CU
+    // their registers.
+    static constexpr bool UW = NTW == 2;
+    static constexpr int kWaves = (UW ? 3 : 2) * NTW + NP;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kExSlot = 4096 + 512;             // S fragments + U fragment
-    static constexpr int kExTile = 2 * kExSlot;
+    static constexpr int kU0Off = 2 * kExSlot;             // U0 of steps j, j + 1 (fp32), UW
+    static constexpr int kExTile = 2 * kExSlot + (UW ? 2 * 1024 : 0);
     static constexpr int kBudget = NTW == 1 ? 81920 : 163840;
     static constexpr int NSfit = (kBudget - NTW * kExTile) / kStage;
     static constexpr int NS = NSfit < 10 ? NSfit : 10;
@@ -984,21 +989,43 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
     const unsigned char *rec0 = pw.rec0;
     auto stage = [&](int64_t j) { return ring + ((uint32_t)j % NS) * G::kStage; };
 
-    if (w >= 2 * NTW) {
+    constexpr int kRole = G::UW ? 3 : 2;  // waves per tile
+    if (w >= kRole * NTW) {
         // ---------------- producers
         // bare barriers throughout: a fence would drain all DMA in flight
         if (J == 0) return;
         const VRows vr{reinterpret_cast<const unsigned char *>(p.v) + ((size_t)s0 * H + h) * D * 2 + nt0 * 32,
                        (int64_t)H * D * 2, (int)L};
-        producer_dispatch<G>(w - 2 * NTW, ring, rec0, vr, j0, lane, (int)J);
+        producer_dispatch<G>(w - kRole * NTW, ring, rec0, vr, j0, lane, (int)J);
         return;
     }
 
     const bool is_r = w < NTW;
-    const int tw = is_r ? w : w - NTW;  // tile within the workgroup
+    const int tw = w % NTW;  // tile within the workgroup
     const int nt = nt0 + tw;
     const int col = 16 * nt + m16;
     unsigned char *exch = ring + G::kExch + tw * G::kExTile;
+
+    if (G::UW && w >= 2 * NTW) {
+        // ---------------- U0 of step j + 1 during step j (stage j + 1 is in LDS at
+        // B_j), into the exchange slot of its step's parity
+        if (J == 0) return;
+        const bool silu = p.flags & KDA_F_SILU;
+        VConv vc;
+        load_vconv(p, slot, h, col, j0 == 0, vc);
+        auto put_u0 = [&](int64_t js) {
+            const f32x4 u0 = u0_tile<G::kVOff, G::kVRow>(stage(js), (tw * 16 + m16) * 2, lane, j0 + js == 0, vc,
+                                                         silu);
+            *reinterpret_cast<f32x4 *>(exch + G::kU0Off + (js & 1) * 1024 + lane * 16) = u0;
+        };
+        barrier_lds();  // B_-1
+        put_u0(0);
+        for (int64_t j = 0; j <= J; ++j) {
+            barrier_lds();  // B_j
+            if (j + 1 < J) put_u0(j + 1);
+        }
+        return;
+    }
 
     if (is_r) {
         // ---------------- recurrence on the 128 x 16 state block of tile nt:
@@ -1010,10 +1037,10 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
             int rslot = 1 % NS;  // ring slot of stage j + 1 during step j
             const bool silu = p.flags & KDA_F_SILU;
             VConv vc;
-            load_vconv(p, slot, h, col, j0 == 0, vc);
+            if (!G::UW) load_vconv(p, slot, h, col, j0 == 0, vc);
             // A step's operands, read from the ring one step ahead: W (negated),
-            // Kd, gam (one row per lane, see decay_tile) and U0 (formed from the
-            // raw v rows of the stage).
+            // Kd, gam (one row per lane, see decay_tile) and, without a U0 wave,
+            // U0 (formed from the raw v rows of the stage).
             auto load = [&](const unsigned char *st, int64_t jabs, bf16x8 (&wn)[4], bf16x4 (&kd)[8], f32x4 &u0,
                             float (&gv)[2]) {
 #pragma unroll
@@ -1026,7 +1053,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                 for (int q = 0; q < 2; ++q)
                     gv[q] = *reinterpret_cast<const float *>(
                         st + R_GAM + (64 * q + 16 * (m16 >> 2) + 4 * g4 + (m16 & 3)) * 4);
-                u0 = u0_tile<G::kVOff, G::kVRow>(st, (tw * 16 + m16) * 2, lane, jabs == 0, vc, silu);
+                if (!G::UW) u0 = u0_tile<G::kVOff, G::kVRow>(st, (tw * 16 + m16) * 2, lane, jabs == 0, vc, silu);
             };
             // One step: operands of step j in the first set; the second set
             // receives step j + 1's (the loop alternates the two sets).
@@ -1035,6 +1062,10 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                             float (&gv_n)[2]) {
                 barrier_lds();  // B_j
                 __builtin_amdgcn_sched_barrier(0);
+                // with a U0 wave: this step's U0 from its exchange slot, added after
+                // the products so that the read hides under them
+                f32x4 u0w = {0.f, 0.f, 0.f, 0.f};
+                if (G::UW) u0w = *reinterpret_cast<const f32x4 *>(exch + G::kU0Off + (j & 1) * 1024 + lane * 16);
                 // (past the last step this reads a stale stage: harmless)
                 load(ring + rslot * G::kStage, j0 + j + 1, wn_n, kd_n, u0_n, gv_n);
                 rslot = rslot + 1 == NS ? 0 : rslot + 1;
@@ -1042,7 +1073,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
 #pragma unroll
                 for (int t = 0; t < 4; ++t) Sp[t] = join8(pack4(S[2 * t]), pack4(S[2 * t + 1]));
                 // two independent accumulation chains over the dk quarters
-                f32x4 Ua = u0;
+                f32x4 Ua = G::UW ? f32x4{0.f, 0.f, 0.f, 0.f} : u0;
                 f32x4 Uc = {0.f, 0.f, 0.f, 0.f};
                 Ua = mma_k32(wn[0], Sp[0], Ua);
                 Uc = mma_k32(wn[1], Sp[1], Uc);
@@ -1059,7 +1090,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                 decay_tile<5>(S[5], gv);
                 decay_tile<6>(S[6], gv);
                 decay_tile<7>(S[7], gv);
-                const bf16x4 Ub = pack4(Ua + Uc);
+                const bf16x4 Ub = pack4(G::UW ? (Ua + Uc) + u0w : Ua + Uc);
                 *reinterpret_cast<bf16x4 *>(ex + 4096 + lane * 8) = Ub;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) S[m] = mma_k16(kd[m], Ub, S[m]);
