@@ -38,8 +38,16 @@ __global__ void __launch_bounds__(256) state_copy_kernel(CopyParams p) {
     const int tid = threadIdx.x;
     const u32x4 *s = reinterpret_cast<const u32x4 *>(p.ssrc + ((size_t)src * H + h) * p.state_bytes);
     u32x4 *d = reinterpret_cast<u32x4 *>(p.sdst + ((size_t)dst * H + h) * p.state_bytes);
-    for (int c = tid; c < p.state_bytes / 16; c += 256)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
+    // four 16-byte pieces in flight per thread before their stores (the piece count,
+    // 4096 for fp32 or 2048 for bf16, is a multiple of 1024)
+    const int n = p.state_bytes / 16;
+    for (int c = tid; c < n; c += 1024) {
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = __builtin_nontemporal_load(s + c + k * 256);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(v[k], d + c + k * 256);
+    }
     if (!p.csrc) return;
     // conv state [slot][3 taps][CC]: this head's 128 channels of q, k and v per tap
     const int row = D * p.conv_elem, per = row / 16;  // bytes, 16-byte pieces per row

@@ -314,7 +314,8 @@ template <bool FU, class BeforeRec>
 __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, unsigned char *rec,
                                                 const SubTask &tk, int h, int lane, const EarlyRows &er,
                                                 LateRows &lr, const ConvW &cw, const float *cwl,
-                                                const SubTask *nx, EarlyRows &ner, BeforeRec &&before_rec) {
+                                                const SubTask *nx, EarlyRows &ner, BeforeRec &&before_rec,
+                                                float *gam) {
     constexpr int D = kHeadDim;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int p0 = 16 * tk.j;
@@ -367,10 +368,12 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
                 if (rr >= rem) { y[rr][0] = 0.f; y[rr][1] = 0.f; }
         }
     };
-    float bt[16];  // beta per row, wave-uniform
+    // beta of rows 4 g4 .. 4 g4 + 3 (the accumulator rows of this lane), from lanes
+    // 4 g4 + i of beta_r
+    float brl[4];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-        bt[rr] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(beta_r), rr));
+    for (int i = 0; i < 4; ++i)
+        brl[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * g4 + i), __float_as_int(beta_r)));
 
     // ---- gate: log2 decays as running products from the sub-chunk start
     //   run_r = 2^{b_r},  back_r = 2^{b_last - b_r},  fd = 2^{-b_last}
@@ -416,10 +419,10 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     before_rec();
     {
         f32x2 gm = {run[15][0], run[15][1]};
-        *reinterpret_cast<f32x2 *>(rec + R_GAM + 4 * c0) = gm;
+        *reinterpret_cast<f32x2 *>(gam + c0) = gm;
     }
 
-    // ---- k: KL = K.2^b, KI = K.2^-b (row-major), beta KL transposed, KD = K.2^(b_last-b)
+    // ---- k: KL = K.2^b, KI = K.2^-b (row-major), -KL transposed, KD = K.2^(b_last-b)
     {
         float wt[2][4], bs[2], y[16][2], rk[16];
         load_w(1, wt, bs);
@@ -444,8 +447,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int c = c0 + e, r = 4 * q4;
-                OPB::store4(sKGT + c * A_STR + r, bt[r] * kl[0][e], bt[r + 1] * kl[1][e],
-                            bt[r + 2] * kl[2][e], bt[r + 3] * kl[3][e]);
+                OPB::store4(sKGT + c * A_STR + r, -kl[0][e], -kl[1][e], -kl[2][e], -kl[3][e]);
                 // accumulator / A-fragment layouts for pass B: element (token r, channel c)
                 // of tile c / 16 sits in lane (r / 4) * 16 + c % 16, slot r % 4
                 const size_t fo = ((size_t)((c >> 4) * 64 + q4 * 16 + (c & 15)) * 4) * 2;
@@ -482,14 +484,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rl = 4 * g4 + i, sl = m16;
-            // beta of row rl (lanes 0..15 of beta_r hold rows 0..15), read as scalars and selected
-            const int bb = __float_as_int(beta_r);
-            const float b0 = __int_as_float(__builtin_amdgcn_readlane(bb, i));
-            const float b1 = __int_as_float(__builtin_amdgcn_readlane(bb, 4 + i));
-            const float b2 = __int_as_float(__builtin_amdgcn_readlane(bb, 8 + i));
-            const float b3 = __int_as_float(__builtin_amdgcn_readlane(bb, 12 + i));
-            const float brl = g4 < 2 ? (g4 == 0 ? b0 : b1) : (g4 == 2 ? b2 : b3);
-            nacc[i] = (sl < rl) ? a[i] * brl : 0.f;
+            nacc[i] = (sl < rl) ? a[i] * brl[i] : 0.f;
             sPS[rl * A_STR + sl] = (__bf16)((sl <= rl) ? pq[i] : 0.f);
         }
     }
@@ -504,7 +499,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     *reinterpret_cast<bf16x4 *>(rec + R_PP + (size_t)lane * 8) =
         *reinterpret_cast<const bf16x4 *>(sPS + m16 * A_STR + 4 * g4);
     if constexpr (FU) {
-        // ---- v: beta V transposed into the dead QL area
+        // ---- v: V transposed into the dead QL area
         __bf16 *sVT = reinterpret_cast<__bf16 *>(lds + A_VT);
         float wt[2][4], bs[2], y[16][2];
         load_w(2, wt, bs);
@@ -515,8 +510,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int r = 4 * q4;
-                OPB::store4(sVT + (c0 + e) * A_VTS + r, bt[r] * y[r][e], bt[r + 1] * y[r + 1][e],
-                            bt[r + 2] * y[r + 2][e], bt[r + 3] * y[r + 3][e]);
+                OPB::store4(sVT + (c0 + e) * A_VTS + r, y[r][e], y[r + 1][e], y[r + 2][e], y[r + 3][e]);
             }
     }
 
@@ -524,7 +518,10 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     // x (I + N) = e_r from the last column down, x_c = [c == r] - sum_{s > c} x_s N[s][c],
     // with N[s][c] read as a wave-uniform scalar from the register tile.  The
     // term with x_{c+1} comes last, so the dependent chain is one FMA per column.
-    bf16x4 xfr;  // row m16 of X, columns 4 g4 .. 4 g4 + 3 (A-operand fragment)
+    // row m16 of X diag(beta), columns 4 g4 .. 4 g4 + 3 (column 4 g4 + i carries beta of
+    // row 4 g4 + i): the A-operand fragment of U0 = X diag(beta) V and the B operand
+    // of W^T below
+    bf16x4 xb;
     {
         float x[16];
 #pragma unroll
@@ -544,48 +541,30 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         // turned into an indexed array access)
         const float m0 = g4 == 0 ? 1.f : 0.f, m1 = g4 == 1 ? 1.f : 0.f;
         const float m2 = g4 == 2 ? 1.f : 0.f, m3 = g4 == 3 ? 1.f : 0.f;
-        float xs[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xs[i] = fmaf(x[i], m0, fmaf(x[4 + i], m1, fmaf(x[8 + i], m2, x[12 + i] * m3)));
-            xfr[i] = (__bf16)xs[i];
-        }
-        if constexpr (!FU) {
-            // X diag(beta) for pass B's U0 = X diag(beta) V: column 4 g4 + i carries
-            // beta of row 4 g4 + i (read from lanes i, 4 + i, 8 + i, 12 + i of beta_r)
-            const int bb = __float_as_int(beta_r);
-            bf16x4 xb;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float b0 = __int_as_float(__builtin_amdgcn_readlane(bb, i));
-                const float b1 = __int_as_float(__builtin_amdgcn_readlane(bb, 4 + i));
-                const float b2 = __int_as_float(__builtin_amdgcn_readlane(bb, 8 + i));
-                const float b3 = __int_as_float(__builtin_amdgcn_readlane(bb, 12 + i));
-                const float bc = g4 < 2 ? (g4 == 0 ? b0 : b1) : (g4 == 2 ? b2 : b3);
-                xb[i] = (__bf16)(xs[i] * bc);
-            }
-            *reinterpret_cast<bf16x4 *>(rec + R_XB + (size_t)lane * 8) = xb;
-        }
+        for (int i = 0; i < 4; ++i)
+            xb[i] = (__bf16)(fmaf(x[i], m0, fmaf(x[4 + i], m1, fmaf(x[8 + i], m2, x[12 + i] * m3))) * brl[i]);
+        if constexpr (!FU) *reinterpret_cast<bf16x4 *>(rec + R_XB + (size_t)lane * 8) = xb;
     }
     wave_sync_lds();
 
-    // ---- W = X diag(beta) (K . 2^b), formed transposed: W^T = (diag(beta) K . 2^b)^T X^T
+    // ---- -W = -X diag(beta) (K . 2^b), formed transposed: -W^T = (-K . 2^b)^T (X diag(beta))^T
     // puts row r of W, channels 16 nt + 4 g4 .. + 3, in lane r + 16 g4 of tile nt,
     // which is the A-operand fragment pass B reads (tiles 2t and 2t + 1 give the two
     // halves of fragment t), so W goes to the record without an LDS round trip.
-    // With FU also U0 = X (diag(beta) V) to the record in accumulator layout.
+    // With FU also U0 = (X diag(beta)) V to the record in accumulator layout.
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const f32x4 w0 = mma_k16(OPB::load4raw(sKGT + (32 * t + m16) * A_STR + 4 * g4), xfr, z);
-        const f32x4 w1 = mma_k16(OPB::load4raw(sKGT + (32 * t + 16 + m16) * A_STR + 4 * g4), xfr, z);
-        *reinterpret_cast<bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16) = join8(pack4(-w0), pack4(-w1));
+        const f32x4 w0 = mma_k16(OPB::load4raw(sKGT + (32 * t + m16) * A_STR + 4 * g4), xb, z);
+        const f32x4 w1 = mma_k16(OPB::load4raw(sKGT + (32 * t + 16 + m16) * A_STR + 4 * g4), xb, z);
+        *reinterpret_cast<bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16) = join8(pack4(w0), pack4(w1));
     }
     if constexpr (FU) {
         const __bf16 *sVT = reinterpret_cast<const __bf16 *>(lds + A_VT);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
-            const f32x4 ur = mma_k16(xfr, OPB::load4raw(sVT + (16 * nt + m16) * A_VTS + 4 * g4), z);
+            const f32x4 ur = mma_k16(xb, OPB::load4raw(sVT + (16 * nt + m16) * A_VTS + 4 * g4), z);
             *reinterpret_cast<bf16x4 *>(rec + R_U0 + ((size_t)nt * 64 + lane) * 8) = pack4(ur);
         }
     }
@@ -652,10 +631,12 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     load_late(p, ta, h, lane, lr);
     const bool hb = next_task(p, ta.slot + stride, stride, tb);
     intra_sub_chunk<false>(p, lds, p.ws + ((size_t)h * p.nslots + ta.slot) * kRec, ta, h, lane, ra, lr, cw,
-                           nullptr, hb ? &tb : nullptr, rb, [] {});
+                           nullptr, hb ? &tb : nullptr, rb, [] {},
+                           reinterpret_cast<float *>(p.ws + ((size_t)h * p.nslots + ta.slot) * kRec + R_GAM));
     if (hb)
         intra_sub_chunk<false>(p, lds, p.ws + ((size_t)h * p.nslots + tb.slot) * kRec, tb, h, lane, rb, lr, cw,
-                               nullptr, nullptr, ra, [] {});
+                               nullptr, nullptr, ra, [] {},
+                               reinterpret_cast<float *>(p.ws + ((size_t)h * p.nslots + tb.slot) * kRec + R_GAM));
 }
 
 // Pass B geometry.  Per 16-column dv tile one recurrence wave (R: all 128 dk
@@ -1364,9 +1345,18 @@ struct FusedGeom {
     static constexpr int kThreads = 64 * (kAW + kRW);
     static constexpr int kAOff = NS * kRecFused;  // pass-A scratch, A_WAVE bytes per wave
     static constexpr int kConvOff = kAOff + kAW * A_WAVE;
-    static constexpr int kFlagOff = kConvOff + kConvLdsBytes;
+    // gam (2^b_last per dk channel, 128 fp32) of sub-chunk j sits in entry j mod
+    // kGamSlots of a ring of its own, read by the recurrence waves during step j.
+    // Pass A rewrites that entry (for sub-chunk j + kGamSlots) once every done[w]
+    // >= j + kGamSlots - NS + 1 = j + NS + 1, which a recurrence wave publishes at
+    // the end of step j + NS - 1, after step j.
+    static constexpr int kGamSlots = 2 * NS, kGamOff = kConvOff + kConvLdsBytes;
+    static constexpr int kFlagOff = kGamOff + kGamSlots * 512;
     static constexpr int kReady = kFlagOff, kDone = kFlagOff + 32, kAbort = kFlagOff + 60;
-    static constexpr int kLds = kFlagOff + 64;
+    // workgroup order (sequence lengths, then the chosen sequence), up to kOrderMax
+    // sequences
+    static constexpr int kOrderMax = 256, kOrderOff = kFlagOff + 64;
+    static constexpr int kLds = kOrderOff + 4 * (kOrderMax + 1);
     static_assert(NS >= kAW && NS <= 8, "every pass-A wave has a slot to fill; ready[] fits 32 bytes");
     static_assert(kRecFused % 16 == 0 && kLds <= 163840, "LDS");
     static_assert(2 * kRW * 16 == kHeadDim, "the recurrence waves cover every dv column");
@@ -1419,6 +1409,28 @@ __device__ __forceinline__ void wait_slot_free(unsigned char *lds, int64_t j) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Sequence of rank r when the sequences are ordered by length, longest first (ties
+// by index).  Workgroup b takes the sequence of rank b / H, so the longest
+// sequences start first and the short ones fill in at the end, which shortens the
+// tail of a launch whose workgroups run for very different times.  Every thread of
+// the workgroup calls this; the ranks of the N sequences are a permutation of
+// 0 .. N - 1, so exactly one thread writes the result.
+__device__ __forceinline__ int seq_of_rank(const int32_t *cu, int N, int r, int *lens) {
+    for (int i = threadIdx.x; i < N; i += FusedGeom::kThreads) lens[i] = cu[i + 1] - cu[i];
+    __syncthreads();
+    for (int t = threadIdx.x; t < N; t += FusedGeom::kThreads) {
+        const int lt = lens[t];
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int lm = lens[m];
+            rank += (lm > lt || (lm == lt && m < t)) ? 1 : 0;
+        }
+        if (rank == r) lens[FusedGeom::kOrderMax] = t;
+    }
+    __syncthreads();
+    return lens[FusedGeom::kOrderMax];
+}
+
 __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitParams p) {
     typedef FusedGeom G;
     constexpr int D = kHeadDim, NS = G::NS;
@@ -1428,7 +1440,10 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
     const int pr = blockIdx.x;
     if (pr >= p.pairs) return;  // whole workgroup
     const int H = p.H;
-    const int n = pr / H, h = pr - n * H;
+    const int rk = pr / H, h = pr - rk * H;
+    const int n = p.cu && p.num_seqs > 1 && p.num_seqs <= G::kOrderMax
+                      ? seq_of_rank(p.cu, p.num_seqs, rk, reinterpret_cast<int *>(smem_f + G::kOrderOff))
+                      : rk;
     const int slot = pool_slot(p.slots, p.num_slots, n);
     if (slot < 0) return;  // whole workgroup
     int64_t s0, L;
@@ -1464,7 +1479,8 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
             t1.j = j + G::kAW;
             const bool h1 = t1.j < J;
             intra_sub_chunk<true>(p, scratch, smem_f + (int)(j % NS) * kRecFused, t0, h, lane, r0, lr, unused,
-                                  cwl, h1 ? &t1 : nullptr, r1, [&] { wait_slot_free(smem_f, j); });
+                                  cwl, h1 ? &t1 : nullptr, r1, [&] { wait_slot_free(smem_f, j); },
+                                  reinterpret_cast<float *>(smem_f + G::kGamOff + (int)(j % G::kGamSlots) * 512));
             lds_word_set(smem_f, G::kReady + 4 * (int)(j % NS), (int)j + 1);
             t0.j = t1.j;
             r0 = r1;
@@ -1489,7 +1505,6 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
         struct Ops {
             bf16x8 wn[4], qg[4];
             bf16x4 kd[8], pp, u0[2];
-            float gv[2];
         };
         auto load = [&](int64_t jr, Ops &o) {
             wait_ready(smem_f, jr);
@@ -1502,10 +1517,6 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
 #pragma unroll
             for (int m = 0; m < 8; ++m)
                 o.kd[m] = *reinterpret_cast<const bf16x4 *>(st + R_KD + (m * 64 + lane) * 8);
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                o.gv[q] = *reinterpret_cast<const float *>(
-                    st + R_GAM + (64 * q + 16 * (m16 >> 2) + 4 * g4 + (m16 & 3)) * 4);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
                 o.u0[t] = *reinterpret_cast<const bf16x4 *>(st + R_U0 + ((2 * w + t) * 64 + lane) * 8);
@@ -1536,16 +1547,15 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) O[t] = mma_k32(c.qg[q], Sp[t][q], O[t]);
+            {
+                // gam of this lane's rows 16 m + 4 g4 .. + 3 from its ring entry
+                const unsigned char *gam = smem_f + G::kGamOff + (int)(j % G::kGamSlots) * 512 + 16 * g4;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                decay_tile<0>(S[t][0], c.gv);
-                decay_tile<1>(S[t][1], c.gv);
-                decay_tile<2>(S[t][2], c.gv);
-                decay_tile<3>(S[t][3], c.gv);
-                decay_tile<4>(S[t][4], c.gv);
-                decay_tile<5>(S[t][5], c.gv);
-                decay_tile<6>(S[t][6], c.gv);
-                decay_tile<7>(S[t][7], c.gv);
+                for (int m = 0; m < 8; ++m) {
+                    const f32x4 gm = *reinterpret_cast<const f32x4 *>(gam + 64 * m);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) S[t][m] *= gm;
+                }
             }
             bf16x4 Ub[2];
 #pragma unroll
