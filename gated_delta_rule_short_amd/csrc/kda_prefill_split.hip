@@ -870,6 +870,35 @@ struct PairWork {
     bool sin16, sout16;
     const unsigned char *rec0;
 };
+// Sequence of rank r when the sequences are ordered by length, longest first (ties
+// by index).  A pass-B or fused workgroup for (rank r, head) takes that sequence,
+// so the longest sequences start first and the short ones fill in at the end,
+// which shortens the tail of a launch whose workgroups run for very different
+// times.  Every thread of the workgroup calls this with the same arguments; lens
+// is LDS for kOrderMax + 1 ints.  The ranks of the N sequences are a permutation
+// of 0 .. N - 1, so exactly one thread writes the result.  Without cu_seqlens
+// (equal lengths) or with more than kOrderMax sequences the order is the index.
+constexpr int kOrderMax = 256;
+__device__ __forceinline__ bool order_by_length(const SplitParams &p) {
+    return p.cu && p.num_seqs > 1 && p.num_seqs <= kOrderMax;
+}
+template <int kThreads>
+__device__ __forceinline__ int seq_of_rank(const int32_t *cu, int N, int r, int *lens) {
+    for (int i = threadIdx.x; i < N; i += kThreads) lens[i] = cu[i + 1] - cu[i];
+    __syncthreads();
+    for (int t = threadIdx.x; t < N; t += kThreads) {
+        const int lt = lens[t];
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int lm = lens[m];
+            rank += (lm > lt || (lm == lt && m < t)) ? 1 : 0;
+        }
+        if (rank == r) lens[kOrderMax] = t;
+    }
+    __syncthreads();
+    return lens[kOrderMax];
+}
+
 __device__ __forceinline__ bool pair_work(const SplitParams &p, int n, int h, int slot, PairWork &w) {
     seq_bounds(p.cu, p.total, p.num_seqs, n, w.s0, w.L);
     const int64_t J = (w.L + 15) / 16;
@@ -960,7 +989,13 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
     const int tile = rem >> 3, pr = grp * 8 + (rem & 7);
     if (pr >= p.pairs) return;  // whole workgroup: no barrier is left waiting
     const int H = p.H;
-    const int n = pr / H, h = pr - n * H;
+    const int rk = pr / H, h = pr - rk * H;
+    int n = rk;
+    if (order_by_length(p)) {
+        // the ring's first bytes as scratch, before any wave writes the ring
+        n = seq_of_rank<G::kThreads>(p.cu, p.num_seqs, rk, reinterpret_cast<int *>(ring));
+        __syncthreads();
+    }
     const int slot = pool_slot(p.slots, p.num_slots, n);
     if (slot < 0) return;  // whole workgroup: no barrier is left waiting
     PairWork pw;
@@ -1183,7 +1218,13 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
     const int pr = blockIdx.x;
     if (pr >= p.pairs) return;  // whole workgroup: no barrier is left waiting
     const int H = p.H;
-    const int n = pr / H, h = pr - n * H;
+    const int rk = pr / H, h = pr - rk * H;
+    int n = rk;
+    if (order_by_length(p)) {
+        // the ring's first bytes as scratch, before any wave writes the ring
+        n = seq_of_rank<G::kThreads>(p.cu, p.num_seqs, rk, reinterpret_cast<int *>(ring));
+        __syncthreads();
+    }
     const int slot = pool_slot(p.slots, p.num_slots, n);
     if (slot < 0) return;  // whole workgroup: no barrier is left waiting
     PairWork pw;
@@ -1353,9 +1394,8 @@ struct FusedGeom {
     static constexpr int kGamSlots = 2 * NS, kGamOff = kConvOff + kConvLdsBytes;
     static constexpr int kFlagOff = kGamOff + kGamSlots * 512;
     static constexpr int kReady = kFlagOff, kDone = kFlagOff + 32, kAbort = kFlagOff + 60;
-    // workgroup order (sequence lengths, then the chosen sequence), up to kOrderMax
-    // sequences
-    static constexpr int kOrderMax = 256, kOrderOff = kFlagOff + 64;
+    // workgroup order (sequence lengths, then the chosen sequence)
+    static constexpr int kOrderOff = kFlagOff + 64;
     static constexpr int kLds = kOrderOff + 4 * (kOrderMax + 1);
     static_assert(NS >= kAW && NS <= 8, "every pass-A wave has a slot to fill; ready[] fits 32 bytes");
     static_assert(kRecFused % 16 == 0 && kLds <= 163840, "LDS");
@@ -1409,28 +1449,6 @@ __device__ __forceinline__ void wait_slot_free(unsigned char *lds, int64_t j) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Sequence of rank r when the sequences are ordered by length, longest first (ties
-// by index).  Workgroup b takes the sequence of rank b / H, so the longest
-// sequences start first and the short ones fill in at the end, which shortens the
-// tail of a launch whose workgroups run for very different times.  Every thread of
-// the workgroup calls this; the ranks of the N sequences are a permutation of
-// 0 .. N - 1, so exactly one thread writes the result.
-__device__ __forceinline__ int seq_of_rank(const int32_t *cu, int N, int r, int *lens) {
-    for (int i = threadIdx.x; i < N; i += FusedGeom::kThreads) lens[i] = cu[i + 1] - cu[i];
-    __syncthreads();
-    for (int t = threadIdx.x; t < N; t += FusedGeom::kThreads) {
-        const int lt = lens[t];
-        int rank = 0;
-        for (int m = 0; m < N; ++m) {
-            const int lm = lens[m];
-            rank += (lm > lt || (lm == lt && m < t)) ? 1 : 0;
-        }
-        if (rank == r) lens[FusedGeom::kOrderMax] = t;
-    }
-    __syncthreads();
-    return lens[FusedGeom::kOrderMax];
-}
-
 __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitParams p) {
     typedef FusedGeom G;
     constexpr int D = kHeadDim, NS = G::NS;
@@ -1441,8 +1459,8 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
     if (pr >= p.pairs) return;  // whole workgroup
     const int H = p.H;
     const int rk = pr / H, h = pr - rk * H;
-    const int n = p.cu && p.num_seqs > 1 && p.num_seqs <= G::kOrderMax
-                      ? seq_of_rank(p.cu, p.num_seqs, rk, reinterpret_cast<int *>(smem_f + G::kOrderOff))
+    const int n = order_by_length(p)
+                      ? seq_of_rank<G::kThreads>(p.cu, p.num_seqs, rk, reinterpret_cast<int *>(smem_f + G::kOrderOff))
                       : rk;
     const int slot = pool_slot(p.slots, p.num_slots, n);
     if (slot < 0) return;  // whole workgroup
