@@ -12,12 +12,13 @@
 //     A = strict_lower(K~ K^T . decay),  P = lower(Q~ K^T . decay),
 //     X = (I + diag(beta) A)^-1,  W = X diag(beta) (K . 2^b),
 // with b the log2-decay cumsum from the sub-chunk start (>= -115.4, so every
-// factor is a finite fp32/bf16 number), and writes them as matrix-core
+// factor is a finite fp32/bf16 number) and the output scale folded into the
+// query side (Q~ = scale Q . 2^b), and writes them as matrix-core
 // fragments to a workspace record, with X diag(beta) itself.  Pass B
 // (scan_kernel) runs one workgroup per (sequence, head, dv tile) over its
 // sub-chunks in order, forms U0 = X diag(beta) V from the conv of the raw v rows
 // of its columns, and carries the state:
-//     U = U0 - W S,  O = scale ((Q . 2^b) S + P U),
+//     U = U0 - W S,  O = Q~ S + P U,
 //     S = diag(2^b_last) S + (K . 2^(b_last - b))^T U.
 // Pass A does the conv / L2 / gate work of q and k once per token and head,
 // over the whole GPU; pass B keeps the fp32 state in registers (accumulator layout) for
@@ -49,7 +50,7 @@ constexpr float kLog2eS = 1.4426950408889634f;
 
 // Record of one (head, sub-chunk), byte offsets; bf16 unless noted.
 //   WN  [4][64][8]  -W, A-operand fragments (rows tokens, K = dk, permuted pairs)
-//   QG  [4][64][8]  Q . 2^b, same fragment layout
+//   QG  [4][64][8]  Q~ = scale Q . 2^b, same fragment layout
 //   KD  [8][64][4]  (K . 2^(b_last - b))^T, A-operand fragments (rows dk, K = tokens)
 //   PP  [64][4]     P, A-operand fragment (rows tokens, K = tokens)
 //   GAM [128] fp32  2^b_last per dk channel
@@ -137,12 +138,12 @@ __device__ __forceinline__ void conv16(const uint32_t (&x)[19], const float (&wt
         }
 }
 
-// Per-row 1 / sqrt(sum of squares + eps) over the 128 channels (two per lane; a
-// wave-uniform value per row), or 1 without the L2 step.
-__device__ __forceinline__ void l2_scale(const float (&y)[16][2], bool l2, int lane, float (&r)[16]) {
+// Per-row f / sqrt(sum of squares + eps) over the 128 channels (two per lane; a
+// wave-uniform value per row), or f without the L2 step.
+__device__ __forceinline__ void l2_scale(const float (&y)[16][2], bool l2, int lane, float f, float (&r)[16]) {
     if (!l2) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) r[rr] = 1.f;
+        for (int rr = 0; rr < 16; ++rr) r[rr] = f;
         return;
     }
     float p[16], s4[4];
@@ -150,7 +151,7 @@ __device__ __forceinline__ void l2_scale(const float (&y)[16][2], bool l2, int l
     for (int rr = 0; rr < 16; ++rr) p[rr] = fmaf(y[rr][0], y[rr][0], y[rr][1] * y[rr][1]);
     rows16_sum(p, s4, lane);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) s4[t] = __builtin_amdgcn_rsqf(s4[t] + 1e-6f);
+    for (int t = 0; t < 4; ++t) s4[t] = __builtin_amdgcn_rsqf(s4[t] + 1e-6f) * f;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) r[rr] = row_value(s4, rr);
 }
@@ -385,11 +386,16 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) g2v[e][rr] = fmaxf(bf_ch(xa[rr], e), p.lb) * kLog2eS;
     } else {
-        const float c = p.lb * kLog2eS;
+        // c sigma(a) = 1 / ((1 + 2^(-a log2 e)) / c), the division by c folded into
+        // one FMA with ic = 1 / c (kept finite, so that 2^(...) = 0 gives no 0 * inf)
+        const float ic = fmaxf(1.f / (p.lb * kLog2eS), -3.0e38f);
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) g2v[e][rr] = c * sigmoidf_dev(bf_ch(xa[rr], e));
+            for (int rr = 0; rr < 16; ++rr) {
+                const float ex = exp2_fast(-kLog2eS * bf_ch(xa[rr], e));
+                g2v[e][rr] = __builtin_amdgcn_rcpf(fmaf(ex, ic, ic));
+            }
     }
     if (edge) {
 #pragma unroll
@@ -428,7 +434,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         load_w(1, wt, bs);
         conv16(xk, wt, bs, y);
         finish(y);
-        l2_scale(y, l2, lane, rk);
+        l2_scale(y, l2, lane, 1.f, rk);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             float kl[4][2], kr[4][2];
@@ -459,14 +465,14 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     if (nx) load_early(p, *nx, h, lane, ner);
     uint32_t xv[FU ? 19 : 1];
     if constexpr (FU) load_v_rows(p, tk, h, lane, xv);
-    // ---- q: QL = Q.2^b (row-major)
+    // ---- q: QL = scale Q.2^b (row-major; the output scale rides on the query)
     {
         float wt[2][4], bs[2], y[16][2], rq[16];
         load_w(0, wt, bs);
         conv16(xq, wt, bs, y);
         if (nx) load_late(p, *nx, h, lane, lr);
         finish(y);
-        l2_scale(y, l2, lane, rq);
+        l2_scale(y, l2, lane, p.scale, rq);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
             Pair<__bf16>::store(sQL + rr * A_SRM + c0, y[rr][0] * rq[rr] * run[rr][0],
@@ -488,7 +494,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
             sPS[rl * A_STR + sl] = (__bf16)((sl <= rl) ? pq[i] : 0.f);
         }
     }
-    // Q . 2^b fragments (pairs of 16-channel blocks, matching pass B's state tiles)
+    // Q~ fragments (pairs of 16-channel blocks, matching pass B's state tiles)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const __bf16 *row = sQL + m16 * A_SRM + 32 * t + 4 * g4;
@@ -1129,7 +1135,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
         return;
     }
 
-    // ---------------- output: O = scale ((Q . 2^b) S + P U) of step j - 1
+    // ---------------- output: O = Q~ S + P U of step j - 1
     if (J == 0) return;
     const int64_t tokstride = (int64_t)H * D;
     // stores: a wave-uniform row base plus one 32-bit per-lane offset (column col
@@ -1162,12 +1168,12 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
             __bf16 *orow = ob + (size_t)(16 * ja) * tokstride;
             if (16 * ja + 16 <= L) {  // the whole sub-chunk lies in the sequence
 #pragma unroll
-                for (int i = 0; i < 4; ++i) (orow + (size_t)i * tokstride)[loff] = (__bf16)(p.scale * O[i]);
+                for (int i = 0; i < 4; ++i) (orow + (size_t)i * tokstride)[loff] = (__bf16)O[i];
             } else {
                 const int64_t r0 = 16 * ja + 4 * g4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (r0 + i < L) (orow + (size_t)i * tokstride)[loff] = (__bf16)(p.scale * O[i]);
+                    if (r0 + i < L) (orow + (size_t)i * tokstride)[loff] = (__bf16)O[i];
             }
         }
     }
@@ -1242,7 +1248,7 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
     }
 
     // ---------------- recurrence and output on tiles 2w, 2w + 1 (columns 32w ..)
-    //   U = U0 - W S,  O = scale (Q~ S + P U),  S = diag(gam) S + Kd^T U
+    //   U = U0 - W S,  O = Q~ S + P U,  S = diag(gam) S + Kd^T U
     // S[t][m] holds rows 16 m + 4 g4 + i of column col[t] (accumulator layout).
     int col[2];
     col[0] = 32 * w + m16;
@@ -1340,14 +1346,14 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)(p.scale * O[t][i]);
+                        (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)O[t][i];
             } else {
                 const int64_t r0 = 16 * ja + 4 * g4;
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (r0 + i < L) (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)(p.scale * O[t][i]);
+                        if (r0 + i < L) (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)O[t][i];
             }
         };
         Ops A, B;
@@ -1507,7 +1513,7 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
     }
 
     // ---------------- recurrence and output on tiles 2w, 2w + 1 (columns 32w ..)
-    //   U = U0 - W S,  O = scale (Q~ S + P U),  S = diag(gam) S + Kd^T U
+    //   U = U0 - W S,  O = Q~ S + P U,  S = diag(gam) S + Kd^T U
     int col[2];
     col[0] = 32 * w + m16;
     col[1] = 32 * w + 16 + m16;
@@ -1590,14 +1596,14 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)(p.scale * O[t][i]);
+                        (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)O[t][i];
             } else {
                 const int64_t r0 = 16 * j + 4 * g4;
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (r0 + i < L) (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)(p.scale * O[t][i]);
+                        if (r0 + i < L) (orow + (size_t)i * tokstride)[loff + 16 * t] = (__bf16)O[t][i];
             }
             // records 0 .. j + 1 are in registers (or past the end): their slots are free
             lds_word_set(smem_f, G::kDone + 4 * w, (int)j + 2);
