@@ -3,10 +3,9 @@
 One step runs every row of the hot path once, each on its workload, with all
 inputs already resident in HBM:
   prefill    : 16 packed sequences of 512..16,384 tokens (137,314 in all), 64
-               heads of 128, bf16, fp32 initial and final states, two-pass
-               schedule with the binding's default workspace
-               (kda_prefill: intra_kernel, then scan_kernel or scan_wide_kernel,
-               once per workspace window)
+               heads of 128, bf16, fp32 initial and final states, the automatic
+               schedule (1024 (sequence, head) pairs: the fused schedule,
+               kda_prefill -> fused_kernel, one workgroup per pair)
   decode     : 256 sequences x 1 token, 64 heads, fp32 state 256x64x128x128
                updated in place, bf16 tokens                  (kda_decode)
   short_conv : the prefill's q|k|v rows as one [137,314, 24,576] bf16 tensor,
@@ -271,8 +270,10 @@ def main():
             "tokens_per_s_per_layer": round(P["T"] / sec, 1),
             "us_per_call": round(ms[key] * 1e3, 2),
             "roofline": roofline(byts, sec, _profile_field(key, "hbm_bytes_per_launch"),
-                                 kernel="kda_prefill (one call: intra_kernel, then scan_kernel or "
-                                        "scan_wide_kernel, per workspace window)",
+                                 kernel=("kda_prefill, fused schedule (fused_kernel)"
+                                         if P["N"] * P["H"] >= kda.FUSED_MIN_PAIRS else
+                                         "kda_prefill, two-pass schedule (intra_kernel, then scan_kernel "
+                                         "or scan_wide_kernel, per workspace window)"),
                                  mfma_algorithmic_frac=round(units * fpth / sec / 1e12 /
                                                              BF16_PEAK_TFLOPS, 4),
                                  mfma_busy_frac=_profile_field(key, "mfma_busy_frac"),

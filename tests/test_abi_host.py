@@ -495,6 +495,12 @@ def test_fused_schedule_takes_whole_heads_only(lib):
     assert b"fused" in lib.kda_last_error() and b"dv_tile" in lib.kda_last_error()
 
 
+def test_fused_threshold_matches_the_header():
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "kda.h")).read()
+    m = re.search(r"#define KDA_FUSED_MIN_PAIRS (\d+)", hdr)
+    assert m and int(m.group(1)) == K.FUSED_MIN_PAIRS == pkg.FUSED_MIN_PAIRS
+
+
 def test_workspace_size_follows_the_schedule(lib):
     """The recommended workspace is the two-pass one only when the call will run
     two passes: not for an explicit one-pass or fused schedule, and not when the
@@ -506,8 +512,12 @@ def test_workspace_size_follows_the_schedule(lib):
         few.schedule = sched
         assert lib.kda_prefill_workspace_size(ctypes.byref(few)) == want
     many = _prefill_args(num_seqs=16, num_heads=64, total_tokens=16 * 256)
-    assert 16 * 64 >= 1024  # KDA_FUSED_MIN_PAIRS
+    assert 16 * 64 >= K.FUSED_MIN_PAIRS
     assert lib.kda_prefill_workspace_size(ctypes.byref(many)) == 0
+    # one pair fewer than the threshold: two passes again
+    below = _prefill_args(num_seqs=1, num_heads=K.FUSED_MIN_PAIRS - 1, total_tokens=256)
+    assert lib.kda_prefill_workspace_size(ctypes.byref(below)) == lib.kda_prefill_workspace_full_size(
+        ctypes.byref(below)) > 0
     many.schedule = 2
     assert lib.kda_prefill_workspace_size(ctypes.byref(many)) == lib.kda_prefill_workspace_full_size(
         ctypes.byref(many)) > 0
