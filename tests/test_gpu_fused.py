@@ -150,3 +150,24 @@ def test_many_pairs_choose_the_fused_schedule():
                          state_in=inp["state_in"][:, heads])
     for name, (o, st, _) in (("fused", fused), ("two-pass", two)):
         assert_bf16_close(o[:, heads], ref["o"], cu, len(heads), st[:, heads], ref["state"], name)
+
+
+def test_more_sequences_than_the_length_order_ranks():
+    """The fused and pass-B workgroups take sequences longest first when a call has
+    at most 256 of them, and in index order beyond; 300 ragged sequences (empty
+    ones among them) at 4 heads (1200 pairs: the fused schedule by default) take
+    the index order, and match the oracle on both schedules; 200 of them take the
+    length order and match as well."""
+    H = 4
+    for count, seed in ((300, 281), (200, 282)):
+        lengths = [(7 * i + 3) % 41 for i in range(count)]
+        inp = KI.make_prefill(H, lengths, seed=seed, device=DEV, state_std=0.1, conv_cache_std=1.0)
+        ref = _oracle(inp)
+        cu = inp["cu_seqlens"].cpu()
+        if count * H >= kda.FUSED_MIN_PAIRS:
+            assert kda.prefill_workspace_bytes(sum(lengths), H, count) == 0
+        for sched in ("fused", "two_pass"):
+            kw = {"workspace": True} if sched == "two_pass" else {}
+            o, st, cs = _fused(inp, schedule=sched, **kw)
+            assert_bf16_close(o, ref["o"], cu, H, st, ref["state"], "%d sequences, %s" % (count, sched))
+            np.testing.assert_array_equal(to_np(cs), ref["conv_state"])
