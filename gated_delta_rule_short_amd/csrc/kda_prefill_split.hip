@@ -57,10 +57,9 @@ constexpr float kLog2eS = 1.4426950408889634f;
 //   XB  [64][4]     X diag(beta), A-operand fragment (rows tokens, K = tokens)
 // Every part is shared by all dv columns.  In LDS a record takes kRecArea bytes
 // (whole DMA KiB; the tail past kRec receives duplicate bytes).  The fused
-// schedule keeps its records in LDS only and holds U0 = X diag(beta) V
-// ([8][64][4], accumulator layout) at R_U0 in place of XB.
+// schedule keeps its records in LDS only (kRec bytes a slot) and takes gam from a
+// ring of its own.
 constexpr int R_WN = 0, R_QG = 4096, R_KD = 8192, R_PP = 12288, R_GAM = 12800, R_XB = 13312;
-constexpr int R_U0 = 13312, kRecFused = R_U0 + 4096;
 constexpr size_t kRec = 13824;
 constexpr int kRecArea = 14336;
 constexpr int kRecInst = kRecArea / 1024;  // DMA instructions of a record
@@ -104,10 +103,6 @@ constexpr int A_SRM = 132, A_STR = 20;
 constexpr int A_KL = 0, A_QL = A_KL + 16 * A_SRM * 2, A_KI = A_QL + 16 * A_SRM * 2;
 constexpr int A_KGT = A_KI + 16 * A_SRM * 2, A_PS = A_KGT + 128 * A_STR * 2;
 constexpr int A_WAVE = A_PS + 16 * A_STR * 2;
-// beta V transposed (fused schedule): A_VTS bf16 per channel row, in the QL area
-// once QL is dead
-constexpr int A_VTS = 16, A_VT = A_QL;
-static_assert(128 * A_VTS * 2 <= 16 * A_SRM * 2, "VT fits in the QL area");
 static_assert(A_WAVE % 16 == 0, "wave region alignment");
 static_assert(8 * A_WAVE <= 163840, "two workgroups of four waves per CU");
 
@@ -283,19 +278,6 @@ __device__ __forceinline__ void load_late(const SplitParams &p, const SubTask &t
     if (tk.j == 0) load_history(p, tk, h, lane, 0, r.xq);
 }
 
-// Rows p0-3 .. p0+15 of v (fused schedule: loaded inside the sub-chunk, when its
-// q block starts, so they are not held across sub-chunks).
-__device__ __forceinline__ void load_v_rows(const SplitParams &p, const SubTask &tk, int h, int lane,
-                                            uint32_t (&xv)[19]) {
-    constexpr int D = kHeadDim;
-    const int64_t rowbytes = (int64_t)p.H * D * 2;
-    const RowWindow wr = row_window(tk, -3);
-    const __amdgpu_buffer_rsrc_t rv = row_rsrc(p.v, tk, h, wr, rowbytes);
-#pragma unroll
-    for (int i = 0; i < 19; ++i)
-        xv[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, 4 * lane, row_soff(wr, i - 3, rowbytes), 0);
-    if (tk.j == 0) load_history(p, tk, h, lane, 2, xv);
-}
 
 // Conv taps and bias of one head in LDS (fused schedule): taps [3][128][4] for
 // q, k, v, then biases [3][128]; fp32.
@@ -306,12 +288,11 @@ constexpr int kConvLdsBytes = 3 * 128 * 5 * 4;
 // of the next sub-chunk's rows as soon as their registers are free: the early
 // rows after the k block (into ner), the late rows after the last conv that
 // reads them (into lr), so that they land while this sub-chunk finishes.  All
-// scratch LDS traffic stays inside the wave's region.  FU (the fused schedule)
-// also convolves v and writes U0 = X diag(beta) V in place of X diag(beta); its
-// conv taps come from LDS (cwl) instead of registers (cw).  before_rec() runs
+// scratch LDS traffic stays inside the wave's region.  With LT (the fused
+// schedule) the conv taps come from LDS (cwl) instead of registers (cw).  before_rec() runs
 // right before the first write to rec (the fused schedule waits there for its
 // ring slot, after the gate, which needs no slot).
-template <bool FU, class BeforeRec>
+template <bool LT, class BeforeRec>
 __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, unsigned char *rec,
                                                 const SubTask &tk, int h, int lane, const EarlyRows &er,
                                                 LateRows &lr, const ConvW &cw, const float *cwl,
@@ -336,7 +317,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     const uint32_t(&xa)[16] = er.xa;
     const float beta_r = (lane < 16 && lane < rem) ? __uint_as_float(er.beta_bits << 16) : 0.f;
     auto load_w = [&](int t, float (&wt)[2][4], float (&bs)[2]) {
-        if constexpr (FU) {
+        if constexpr (LT) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const f32x4 a = *reinterpret_cast<const f32x4 *>(cwl + (t * 128 + c0 + e) * 4);
@@ -463,8 +444,6 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         }
     }
     if (nx) load_early(p, *nx, h, lane, ner);
-    uint32_t xv[FU ? 19 : 1];
-    if constexpr (FU) load_v_rows(p, tk, h, lane, xv);
     // ---- q: QL = scale Q.2^b (row-major; the output scale rides on the query)
     {
         float wt[2][4], bs[2], y[16][2], rq[16];
@@ -504,21 +483,6 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     wave_sync_lds();
     *reinterpret_cast<bf16x4 *>(rec + R_PP + (size_t)lane * 8) =
         *reinterpret_cast<const bf16x4 *>(sPS + m16 * A_STR + 4 * g4);
-    if constexpr (FU) {
-        // ---- v: V transposed into the dead QL area
-        __bf16 *sVT = reinterpret_cast<__bf16 *>(lds + A_VT);
-        float wt[2][4], bs[2], y[16][2];
-        load_w(2, wt, bs);
-        conv16(xv, wt, bs, y);
-        finish(y);
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int r = 4 * q4;
-                OPB::store4(sVT + (c0 + e) * A_VTS + r, y[r][e], y[r + 1][e], y[r + 2][e], y[r + 3][e]);
-            }
-    }
 
     // ---- X = (I + N)^-1, one row per lane: lane r (mod 16) solves
     // x (I + N) = e_r from the last column down, x_c = [c == r] - sum_{s > c} x_s N[s][c],
@@ -550,7 +514,7 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             xb[i] = (__bf16)(fmaf(x[i], m0, fmaf(x[4 + i], m1, fmaf(x[8 + i], m2, x[12 + i] * m3))) * brl[i]);
-        if constexpr (!FU) *reinterpret_cast<bf16x4 *>(rec + R_XB + (size_t)lane * 8) = xb;
+        *reinterpret_cast<bf16x4 *>(rec + R_XB + (size_t)lane * 8) = xb;
     }
     wave_sync_lds();
 
@@ -558,21 +522,12 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     // puts row r of W, channels 16 nt + 4 g4 .. + 3, in lane r + 16 g4 of tile nt,
     // which is the A-operand fragment pass B reads (tiles 2t and 2t + 1 give the two
     // halves of fragment t), so W goes to the record without an LDS round trip.
-    // With FU also U0 = (X diag(beta)) V to the record in accumulator layout.
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const f32x4 w0 = mma_k16(OPB::load4raw(sKGT + (32 * t + m16) * A_STR + 4 * g4), xb, z);
         const f32x4 w1 = mma_k16(OPB::load4raw(sKGT + (32 * t + 16 + m16) * A_STR + 4 * g4), xb, z);
         *reinterpret_cast<bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16) = join8(pack4(w0), pack4(w1));
-    }
-    if constexpr (FU) {
-        const __bf16 *sVT = reinterpret_cast<const __bf16 *>(lds + A_VT);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const f32x4 ur = mma_k16(xb, OPB::load4raw(sVT + (16 * nt + m16) * A_VTS + 4 * g4), z);
-            *reinterpret_cast<bf16x4 *>(rec + R_U0 + ((size_t)nt * 64 + lane) * 8) = pack4(ur);
-        }
     }
 }
 
@@ -1374,9 +1329,10 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
 // ---------------------------------------------------------------------------
 // Fused schedule for many (sequence, head) pairs: one workgroup per pair over
 // all 128 dv columns.  Four pass-A waves form the records of the pair's
-// sub-chunks (sub-chunks a, a + 4, ... for wave a; U0 included, from v) in an
+// sub-chunks (sub-chunks a, a + 4, ... for wave a; the two-pass record) in an
 // NS-slot ring in LDS, and four recurrence waves run pass B's steps on them
-// (two 16-column tiles each, output included), so no record leaves the CU.
+// (two 16-column tiles each, U0 from the raw v rows and the output included),
+// so no record leaves the CU.
 // Slot j mod NS holds sub-chunk j.  The waves hand slots over through LDS
 // words instead of barriers (a pass-A task spans several steps):
 //   ready[s]  = j + 1 once sub-chunk j's record is complete in slot s;
@@ -1387,10 +1343,11 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
 // which no wave of the workgroup waits again: a broken hand-over yields wrong
 // results and never a workgroup that does not end.
 struct FusedGeom {
-    static constexpr int NS = 4;                  // record slots
+    static constexpr int NS = 5;                  // record slots
     static constexpr int kAW = 4, kRW = 4;        // pass-A waves, recurrence waves
     static constexpr int kThreads = 64 * (kAW + kRW);
-    static constexpr int kAOff = NS * kRecFused;  // pass-A scratch, A_WAVE bytes per wave
+    static constexpr int kSlot = (int)kRec;       // a record slot: the two-pass record
+    static constexpr int kAOff = NS * kSlot;      // pass-A scratch, A_WAVE bytes per wave
     static constexpr int kConvOff = kAOff + kAW * A_WAVE;
     // gam (2^b_last per dk channel, 128 fp32) of sub-chunk j sits in entry j mod
     // kGamSlots of a ring of its own, read by the recurrence waves during step j.
@@ -1404,7 +1361,7 @@ struct FusedGeom {
     static constexpr int kOrderOff = kFlagOff + 64;
     static constexpr int kLds = kOrderOff + 4 * (kOrderMax + 1);
     static_assert(NS >= kAW && NS <= 8, "every pass-A wave has a slot to fill; ready[] fits 32 bytes");
-    static_assert(kRecFused % 16 == 0 && kLds <= 163840, "LDS");
+    static_assert(kSlot % 16 == 0 && kLds <= 163840, "LDS");
     static_assert(2 * kRW * 16 == kHeadDim, "the recurrence waves cover every dv column");
 };
 constexpr int kSpinLimit = 1 << 22;
@@ -1502,7 +1459,7 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
         for (int64_t j = a; j < J; j += G::kAW) {
             t1.j = j + G::kAW;
             const bool h1 = t1.j < J;
-            intra_sub_chunk<true>(p, scratch, smem_f + (int)(j % NS) * kRecFused, t0, h, lane, r0, lr, unused,
+            intra_sub_chunk<true>(p, scratch, smem_f + (int)(j % NS) * G::kSlot, t0, h, lane, r0, lr, unused,
                                   cwl, h1 ? &t1 : nullptr, r1, [&] { wait_slot_free(smem_f, j); },
                                   reinterpret_cast<float *>(smem_f + G::kGamOff + (int)(j % G::kGamSlots) * 512));
             lds_word_set(smem_f, G::kReady + 4 * (int)(j % NS), (int)j + 1);
@@ -1526,13 +1483,74 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
         const int64_t tokstride = (int64_t)H * D;
         __bf16 *ob = reinterpret_cast<__bf16 *>(p.o) + ((size_t)s0 * tokstride + (size_t)h * D);
         const uint32_t loff = (uint32_t)col[0] + 4u * (uint32_t)g4 * (uint32_t)tokstride;
+        // U0 = X diag(beta) V per tile, from the width-4 conv of the raw v rows
+        // 4 g4 - 3 .. 4 g4 + 3 of the sub-chunk in this lane's columns, loaded one
+        // step ahead (vx[t][k]: raw bf16 of row 4 g4 - 3 + k, column col[t]).  Past
+        // the sequence end the rows read as zeros (buffer range), before its start
+        // they come from the conv state (or are zeros); X diag(beta) has zero columns
+        // for the rows past the end.
+        const float *cwl = reinterpret_cast<const float *>(smem_f + G::kConvOff);
+        const int64_t rowbytes = (int64_t)H * D * 2;
+        const unsigned char *vseq = reinterpret_cast<const unsigned char *>(p.v) + ((size_t)s0 * H + h) * D * 2;
+        const int vlane = 4 * g4 * (int)rowbytes + 2 * col[0];
+        const bool silu = p.flags & KDA_F_SILU;
+        uint32_t vx[2][7];
+        auto load_v = [&](int64_t jr) {
+            if (jr == 0) {
+                const int CCH = 3 * H * D;
+                const __bf16 *cs = p.cs_in ? reinterpret_cast<const __bf16 *>(p.cs_in) + (size_t)slot * 3 * CCH : nullptr;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int k = 0; k < 7; ++k) {
+                        const int64_t r = 4 * g4 - 3 + k;
+                        const int64_t rr = r < L ? r : L - 1;
+                        if (r < 0)
+                            vx[t][k] = cs ? *reinterpret_cast<const unsigned short *>(
+                                                cs + (size_t)(r + 3) * CCH + 2 * H * D + h * D + col[t])
+                                          : 0u;
+                        else
+                            vx[t][k] = *reinterpret_cast<const unsigned short *>(vseq + rr * rowbytes + 2 * col[t]);
+                    }
+            } else {
+                // rows 16 jr - 3 .. (>= 13, inside the sequence since jr < J) onwards
+                const int64_t r0 = 16 * jr - 3;
+                const int64_t nb = (L - r0) * rowbytes;
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<unsigned char *>(vseq + r0 * rowbytes), 0, (int)(nb < 0x7ffff000 ? nb : 0x7ffff000),
+                    0x00020000);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int k = 0; k < 7; ++k)
+                        vx[t][k] = __builtin_amdgcn_raw_buffer_load_b16(rs, vlane + 32 * t, k * (int)rowbytes, 0);
+            }
+        };
+        auto u0_of = [&](int t, bf16x4 xb) {
+            const int c = col[t];
+            const f32x4 wv = *reinterpret_cast<const f32x4 *>(cwl + (2 * 128 + c) * 4);
+            const float bv = cwl[3 * 128 * 4 + 2 * 128 + c];
+            float x[7];
+#pragma unroll
+            for (int k = 0; k < 7; ++k) x[k] = __uint_as_float(vx[t][k] << 16);
+            f32x4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float a = fmaf(wv[0], x[i], bv);
+                a = fmaf(wv[1], x[i + 1], a);
+                a = fmaf(wv[2], x[i + 2], a);
+                a = fmaf(wv[3], x[i + 3], a);
+                y[i] = silu ? a * sigmoidf_dev(a) : a;
+            }
+            return mma_k16w(xb, pack4(y), f32x4{0.f, 0.f, 0.f, 0.f});
+        };
         struct Ops {
             bf16x8 wn[4], qg[4];
-            bf16x4 kd[8], pp, u0[2];
+            bf16x4 kd[8], pp, xb;
         };
         auto load = [&](int64_t jr, Ops &o) {
             wait_ready(smem_f, jr);
-            const unsigned char *st = smem_f + (int)(jr % NS) * kRecFused;
+            const unsigned char *st = smem_f + (int)(jr % NS) * G::kSlot;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 o.wn[t] = *reinterpret_cast<const bf16x8 *>(st + R_WN + (t * 64 + lane) * 16);
@@ -1541,9 +1559,7 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
 #pragma unroll
             for (int m = 0; m < 8; ++m)
                 o.kd[m] = *reinterpret_cast<const bf16x4 *>(st + R_KD + (m * 64 + lane) * 8);
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                o.u0[t] = *reinterpret_cast<const bf16x4 *>(st + R_U0 + ((2 * w + t) * 64 + lane) * 8);
+            o.xb = *reinterpret_cast<const bf16x4 *>(st + R_XB + lane * 8);
             o.pp = *reinterpret_cast<const bf16x4 *>(st + R_PP + lane * 8);
         };
         auto step = [&](int64_t j, const Ops &c, Ops &nx) {
@@ -1556,10 +1572,11 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
             f32x4 Ua[2], Uc[2], O[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                Ua[t] = f32x4{(float)c.u0[t].x, (float)c.u0[t].y, (float)c.u0[t].z, (float)c.u0[t].w};
+                Ua[t] = u0_of(t, c.xb);
                 Uc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+            if (j + 1 < J) load_v(j + 1);  // vx is free again
 #pragma unroll
             for (int q = 0; q < 4; q += 2)
 #pragma unroll
@@ -1610,6 +1627,7 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
         };
         Ops A, B;
         load(0, A);
+        load_v(0);
         int64_t j = 0;
         for (; j + 1 < J; j += 2) {
             step(j, A, B);
