@@ -11,7 +11,7 @@ import torch
 import kda_inputs as KI
 import oracle
 import gated_delta_rule_short_amd as kda
-from tests._gpu_common import assert_bf16_close, seeded, to_np
+from tests._gpu_common import BF16_REL, assert_bf16_close, seeded, state_rel_errors, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -171,3 +171,26 @@ def test_more_sequences_than_the_length_order_ranks():
             o, st, cs = _fused(inp, schedule=sched, **kw)
             assert_bf16_close(o, ref["o"], cu, H, st, ref["state"], "%d sequences, %s" % (count, sched))
             np.testing.assert_array_equal(to_np(cs), ref["conv_state"])
+
+
+def test_ninety_six_heads_on_every_schedule_and_decode():
+    """A head count above 64 and not a power of two (96: token rows of 48 KiB per
+    tensor, conv channels 3 x 96 x 128) through the three prefill schedules and one
+    decode step, against the oracle."""
+    H, lengths = 96, [5, 40, 130]
+    inp = KI.make_prefill(H, lengths, seed=291, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    ref = _oracle(inp)
+    cu = inp["cu_seqlens"].cpu()
+    for sched, kw in (("fused", {}), ("two_pass", {"workspace": True}), ("one_pass", {"workspace": None})):
+        o, st, cs = _fused(inp, schedule=sched, **kw)
+        assert_bf16_close(o, ref["o"], cu, H, st, ref["state"], "96 heads, " + sched)
+        np.testing.assert_array_equal(to_np(cs), ref["conv_state"])
+    d = KI.make_decode(5, H, seed=292, device=DEV)
+    refd = oracle.decode(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"], d["conv_state"], d["state"])
+    od = kda.kda_decode(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"], d["conv_state"], d["state"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(d["conv_state"]), refd["conv_state"])
+    e = np.linalg.norm((to_np(od) - refd["o"]).reshape(-1, 128), axis=1) / \
+        np.linalg.norm(refd["o"].reshape(-1, 128), axis=1)
+    assert e.max() <= BF16_REL
+    assert state_rel_errors(d["state"], refd["state"]).max() <= BF16_REL
