@@ -119,6 +119,36 @@ def test_slot_outside_pool_skips_the_sequence():
     assert _untouched(st, st0, [2]) and _untouched(cs, cs0, [2])
 
 
+@pytest.mark.parametrize("sched", ["fused", "two_pass", "one_pass"])
+def test_prefill_slot_outside_pool_skips_the_sequence(sched):
+    """Prefill on every schedule: sequences with slots -1 and num_slots write no
+    output, state or conv state; the valid one equals the same call with every slot
+    valid, bit for bit."""
+    H, P = 2, 4
+    inp = KI.make_prefill(H, [20, 33, 17], seed=101, device=DEV)
+    args = (inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["conv_w"])
+    kw = {"workspace": True} if sched == "two_pass" else {}
+    cu = [int(c) for c in inp["cu_seqlens"].cpu()]
+
+    def run(slots, st, cs):
+        o = torch.full_like(inp["v"], 7.0)
+        kda.kda_prefill(*args, cu_seqlens=inp["cu_seqlens"], state_in=st, state_out=st, conv_state_in=cs,
+                        conv_state_out=cs, state_slots=torch.tensor(slots, dtype=torch.int32, device=DEV),
+                        o=o, schedule=sched, **kw)
+        torch.cuda.synchronize()
+        return o
+
+    st, cs = _pool(P, H, torch.bfloat16, 102)
+    st0, cs0 = st.clone(), cs.clone()
+    o = run([2, -1, P], st, cs)
+    assert torch.all(o[cu[1]:] == 7.0) and not torch.all(o[:cu[1]] == 7.0)
+    assert _untouched(st, st0, [2]) and _untouched(cs, cs0, [2])
+    st_v, cs_v = st0.clone(), cs0.clone()
+    o_v = run([2, 0, 1], st_v, cs_v)
+    assert torch.equal(o[:cu[1]], o_v[:cu[1]])
+    assert torch.equal(st[2], st_v[2]) and torch.equal(cs[2], cs_v[2])
+
+
 @pytest.mark.parametrize("sdt", [torch.float32, torch.bfloat16])
 def test_state_copy(sdt):
     H, P = 3, 8
