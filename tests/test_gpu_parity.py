@@ -300,9 +300,13 @@ def test_chunk_sizes_agree():
         assert state_rel_errors(st, res[0][1]).max() <= 1e-2
 
 
-def test_empty_batch_and_zero_tokens():
-    inp = KI.make_prefill(1, [0, 0], seed=5, device=DEV, state_std=0.1, conv_cache_std=1.0)
-    o, st, cs = _gpu_prefill(inp)
+@pytest.mark.parametrize("sched,kw,H,N", [("one_pass", {}, 1, 2), ("two_pass", {"workspace": True}, 1, 2),
+                                         ("fused", {}, 1, 2), ("auto", {"workspace": True}, 64, 16)])
+def test_empty_batch_and_zero_tokens(sched, kw, H, N):
+    """No tokens at all: every schedule (the automatic one at 1024 pairs picks the
+    fused kernel) returns an empty o and passes the states through unchanged."""
+    inp = KI.make_prefill(H, [0] * N, seed=5, device=DEV, state_std=0.1, conv_cache_std=1.0)
+    o, st, cs = _gpu_prefill(inp, schedule=sched, **kw)
     assert o.numel() == 0
     assert torch.equal(st, inp["state_in"]) and torch.equal(cs, inp["conv_state_in"])
 
