@@ -46,6 +46,11 @@ PROFILE_OF = {  # committed rocprofv3 counter summaries holding HBM bytes per la
     "prefill_T4096": ("kda_prefill_split.hip", "prefill_T4096_H64.md"),
     "prefill_T65536": ("kda_prefill_split.hip", "prefill_T65536_H64.md"),
     "decode": ("kda_decode.hip", "decode_N256_H64.md"),
+    "decode_bf16_state": ("kda_decode.hip", "decode_bf16_state_N256_H64.md"),
+    "spec_decode": ("kda_decode.hip", "spec_decode_N256_T6_H64.md"),
+    "short_conv": ("kda_conv.hip", "short_conv_T137314_C24576.md"),
+    "state_copy": ("kda_pool.hip", "state_copy_128rows_H64.md"),
+    "gate_proj": ("kda_gate_proj.hip", "gate_proj_T4096_hid4096_H64.md"),
 }
 OPS = ["prefill_varlen", "prefill_T4096", "prefill_T65536", "decode", "short_conv",
        "decode_bf16_state", "spec_decode", "spec_commit", "gate_proj", "state_copy",
@@ -338,24 +343,28 @@ def main():
         "per_call_us": {nm: round(ms[nm] * 1e3, 2) for nm in names},
         "per_call_us_mean": {nm: round(ms_mean[nm] * 1e3, 2) for nm in names},
         "short_conv": {"us_per_call": round(ms["short_conv"] * 1e3, 2),
-                       "roofline": roofline(conv_bytes, ms["short_conv"] * 1e-3)},
+                       "roofline": roofline(conv_bytes, ms["short_conv"] * 1e-3,
+                                            _profile_field("short_conv", "hbm_bytes_per_launch"))},
         "gate_proj": {
             "workload": "gate and beta in-projections of 4096 tokens: hidden 4096, rank 128, "
                         "64 heads x 128 gate channels, bf16, log-decay epilogue",
             "us_per_call": round(ms["gate_proj"] * 1e3, 2),
             "TFLOPs": round(gp_flops / (ms["gate_proj"] * 1e-3) / 1e12, 1),
-            "roofline": roofline(gp_bytes, ms["gate_proj"] * 1e-3, flops_per_call=gp_flops),
+            "roofline": roofline(gp_bytes, ms["gate_proj"] * 1e-3,
+                                 _profile_field("gate_proj", "hbm_bytes_per_launch"), flops_per_call=gp_flops),
         },
         "state_copy": {
             "workload": "%d pool rows (fp32 state, 64 heads, and conv state) copied to %d other "
                         "rows of the decode workload's pool" % (n_cp, n_cp),
             "us_per_call": round(ms["state_copy"] * 1e3, 2),
-            "roofline": roofline(cp_bytes, ms["state_copy"] * 1e-3),
+            "roofline": roofline(cp_bytes, ms["state_copy"] * 1e-3,
+                                 _profile_field("state_copy", "hbm_bytes_per_launch")),
         },
         "decode_bf16_state": {
             "workload": "the decode workload with the state stored as bf16 (512 MiB)",
             "us_per_call": round(ms["decode_bf16_state"] * 1e3, 2),
-            "roofline": roofline(dec_state_bytes // 2 + dec_other, ms["decode_bf16_state"] * 1e-3),
+            "roofline": roofline(dec_state_bytes // 2 + dec_other, ms["decode_bf16_state"] * 1e-3,
+                                 _profile_field("decode_bf16_state", "hbm_bytes_per_launch")),
         },
         "spec_decode": {
             "workload": "256 sequences x 6 tokens (k=5 drafts + 1), H=64, bf16 tokens, fp32 "
@@ -365,7 +374,7 @@ def main():
             "verified_tokens_per_s": round(N_sp * T_sp / sp_s, 1),
             "accepted_tokens_per_s": round(sum(max(0, min(T_sp, a_)) for a_ in acc_l) / sp_s, 1),
             "mean_accepted": round(sum(acc_l) / len(acc_l), 3),
-            "roofline": roofline(sp_bytes, sp_s),
+            "roofline": roofline(sp_bytes, sp_s, _profile_field("spec_decode", "hbm_bytes_per_launch")),
         },
     }
 
