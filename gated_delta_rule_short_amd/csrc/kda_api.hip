@@ -4,6 +4,7 @@
 // return a status code and leave a message in a thread-local buffer.  The
 // library allocates nothing and never synchronises the stream.
 #include <cmath>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -162,11 +163,19 @@ void trace(const char *fmt, ...) {
     std::fprintf(stderr, "[kda] %s\n", line);
 }
 
+constexpr int kDefaultSpinLimit = 1 << 22;
+std::atomic<int> g_spin_limit{kDefaultSpinLimit};
+int spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+
 }  // namespace kda
 
 extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+int32_t kda_set_spin_limit(int32_t polls) {
+    return kda::g_spin_limit.exchange(polls > 0 ? polls : kda::kDefaultSpinLimit);
+}
 
 const char *kda_status_string(kda_status s) {
     switch (s) {

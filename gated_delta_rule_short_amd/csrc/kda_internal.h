@@ -14,6 +14,9 @@ namespace kda {
 bool trace_on();
 void trace(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
 
+// Polls of a fused-prefill hand-over wait before it gives up (kda_set_spin_limit).
+int spin_limit();
+
 // Conv over packed sequences; x, y: [T][channels].
 hipError_t launch_short_conv(kda_dtype dt, const void *x, void *y, int64_t T, int channels,
                              const float *w, const float *b, const void *cs_in,

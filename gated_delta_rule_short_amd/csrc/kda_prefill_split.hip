@@ -91,6 +91,7 @@ struct SplitParams {
     // waits in `carry` ([N][H][128][128]) from one window to the next.
     int64_t jw, win;
     float *carry;
+    int spin_limit;  // polls of a fused hand-over wait before it gives up
 };
 
 // Slot of sub-chunk j of sequence n (start s0): distinct for all (n, j) and
@@ -1339,9 +1340,9 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
 //   done[w]   = the number of records recurrence wave w has read into registers.
 // Pass-A wave a waits for min_w done[w] >= j - NS + 1 before writing sub-chunk j;
 // recurrence wave w waits for ready[j mod NS] >= j + 1 before reading it.  A
-// wait that polls kSpinLimit times without success sets the abort word, after
-// which no wave of the workgroup waits again: a broken hand-over yields wrong
-// results and never a workgroup that does not end.
+// wait that polls spin_limit times (kda_set_spin_limit; 2^22 by default) without
+// success sets the abort word, after which no wave of the workgroup waits again:
+// a broken hand-over yields wrong results and never a workgroup that does not end.
 struct FusedGeom {
     static constexpr int NS = 5;                  // record slots
     static constexpr int kAW = 4, kRW = 4;        // pass-A waves, recurrence waves
@@ -1364,7 +1365,6 @@ struct FusedGeom {
     static_assert(kSlot % 16 == 0 && kLds <= 163840, "LDS");
     static_assert(2 * kRW * 16 == kHeadDim, "the recurrence waves cover every dv column");
 };
-constexpr int kSpinLimit = 1 << 22;
 
 __device__ __forceinline__ int lds_word(const unsigned char *lds, int off) {
     return __builtin_amdgcn_readfirstlane(
@@ -1380,11 +1380,11 @@ __device__ __forceinline__ void give_up(unsigned char *lds) {
     __hip_atomic_store(reinterpret_cast<int *>(lds + FusedGeom::kAbort), 1, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void wait_ready(unsigned char *lds, int64_t j) {
+__device__ __forceinline__ void wait_ready(unsigned char *lds, int64_t j, int limit) {
     const int off = FusedGeom::kReady + 4 * (int)(j % FusedGeom::NS);
     for (int it = 0;; ++it) {
         if (lds_word(lds, off) >= (int)j + 1 || lds_word(lds, FusedGeom::kAbort)) break;
-        if (it == kSpinLimit) {
+        if (it >= limit) {
             give_up(lds);
             break;
         }
@@ -1392,7 +1392,7 @@ __device__ __forceinline__ void wait_ready(unsigned char *lds, int64_t j) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-__device__ __forceinline__ void wait_slot_free(unsigned char *lds, int64_t j) {
+__device__ __forceinline__ void wait_slot_free(unsigned char *lds, int64_t j, int limit) {
     const int want = (int)j - FusedGeom::NS + 1;
     if (want <= 0) return;
     for (int it = 0;; ++it) {
@@ -1403,7 +1403,7 @@ __device__ __forceinline__ void wait_slot_free(unsigned char *lds, int64_t j) {
             m = d < m ? d : m;
         }
         if (m >= want || lds_word(lds, FusedGeom::kAbort)) break;
-        if (it == kSpinLimit) {
+        if (it >= limit) {
             give_up(lds);
             break;
         }
@@ -1460,7 +1460,7 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
             t1.j = j + G::kAW;
             const bool h1 = t1.j < J;
             intra_sub_chunk<true>(p, scratch, smem_f + (int)(j % NS) * G::kSlot, t0, h, lane, r0, lr, unused,
-                                  cwl, h1 ? &t1 : nullptr, r1, [&] { wait_slot_free(smem_f, j); },
+                                  cwl, h1 ? &t1 : nullptr, r1, [&] { wait_slot_free(smem_f, j, p.spin_limit); },
                                   reinterpret_cast<float *>(smem_f + G::kGamOff + (int)(j % G::kGamSlots) * 512));
             lds_word_set(smem_f, G::kReady + 4 * (int)(j % NS), (int)j + 1);
             t0.j = t1.j;
@@ -1549,7 +1549,7 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
             bf16x4 kd[8], pp, xb;
         };
         auto load = [&](int64_t jr, Ops &o) {
-            wait_ready(smem_f, jr);
+            wait_ready(smem_f, jr, p.spin_limit);
             const unsigned char *st = smem_f + (int)(jr % NS) * G::kSlot;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -1720,6 +1720,7 @@ SplitParams common_params(const kda_prefill_args *a) {
     sp.carry = nullptr;
     sp.nslots = 0;
     sp.tiles = 1;
+    sp.spin_limit = spin_limit();
     return sp;
 }
 }  // namespace

@@ -22,7 +22,7 @@ PREFILL_WORKSPACE_CAP = 4 << 30  # KDA_PREFILL_WORKSPACE_CAP
 PREFILL_SCRATCH_BYTES = 256 << 20  # KDA_PREFILL_SCRATCH_BYTES (kda_prefill_noalloc)
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_error", "kda_short_conv",
+EXPORTS = ("kda_abi_version", "kda_set_spin_limit", "kda_status_string", "kda_last_error", "kda_short_conv",
            "kda_prefill", "kda_prefill_workspace_size", "kda_prefill_workspace_full_size",
            "kda_prefill_workspace_min_size", "kda_prefill_noalloc", "kda_decode", "kda_decode_multi",
            "kda_decode_commit", "kda_state_copy", "kda_gate_beta_proj",
@@ -133,6 +133,8 @@ def load_library(path: str = LIB_PATH):
                                "`python -c 'import __graft_entry__ as g; g.build()'`" % path)
         lib = ctypes.CDLL(path)
         lib.kda_abi_version.restype = ctypes.c_int
+        lib.kda_set_spin_limit.restype = _c_i32
+        lib.kda_set_spin_limit.argtypes = [_c_i32]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_status_string.argtypes = [ctypes.c_int]  # kda_status (an int-sized enum)
         lib.kda_last_error.restype = ctypes.c_char_p
@@ -252,6 +254,14 @@ def _pool_shape(t, name, rows_shape_tail):
 
 def abi_version():
     return load_library().kda_abi_version()
+
+
+def set_spin_limit(polls):
+    """Bound of the fused prefill's hand-over waits, for tests of its failure path
+    (kda_set_spin_limit): after `polls` unsuccessful polls a wait gives up and the
+    call ends with wrong results instead of hanging.  polls <= 0 restores the
+    default.  Returns the previous bound."""
+    return load_library().kda_set_spin_limit(int(polls))
 
 
 def kda_short_conv(x, weight, *, cu_seqlens=None, cu_seqlens_host=None, bias=None,

@@ -110,6 +110,17 @@ enum {
 /* Version of this ABI (KDA_ABI_VERSION). */
 int kda_abi_version(void);
 
+/*
+ * Bound of the fused prefill's hand-over waits (KDA_SCHEDULE_FUSED), for tests of
+ * its failure path.  A wave of the fused kernel waits for a ring slot or a record
+ * by polling a word in LDS; after `polls` unsuccessful polls it gives up and
+ * marks the workgroup, whose waves then wait no more: the call still ends, with
+ * wrong results, instead of hanging.  The default (2^22 polls, restored by any
+ * polls <= 0) is never reached by a correct hand-over.  Process-wide; takes
+ * effect for launches after the call; returns the previous bound.
+ */
+int32_t kda_set_spin_limit(int32_t polls);
+
 /* Static string naming a kda_status value ("KDA_UNKNOWN_STATUS" for any other value). */
 const char *kda_status_string(kda_status status);
 

@@ -194,3 +194,24 @@ def test_ninety_six_heads_on_every_schedule_and_decode():
         np.linalg.norm(refd["o"].reshape(-1, 128), axis=1)
     assert e.max() <= BF16_REL
     assert state_rel_errors(d["state"], refd["state"]).max() <= BF16_REL
+
+
+def test_hand_over_waits_give_up_instead_of_hanging():
+    """With the wait bound forced down to one poll from the host, the fused kernel's
+    hand-over waits give up at once and mark their workgroup, whose waves then wait
+    no more: the call ends (its results are not checked: a wave that gives up uses
+    a ring slot before its hand-over).  With the default bound restored the same
+    call equals its earlier result bit for bit."""
+    lengths = [40, 17, 64, 5] * 4
+    H = 64  # 1024 pairs: the fused schedule
+    inp = KI.make_prefill(H, lengths, seed=301, device=DEV, state_std=0.1)
+    ref = _fused(inp)
+    prev = kda.set_spin_limit(1)
+    try:
+        o, st, cs = _fused(inp)  # must return
+        assert o.shape == ref[0].shape
+    finally:
+        assert kda.set_spin_limit(0) == 1
+    assert prev == kda.set_spin_limit(0)  # 0 restored the default
+    again = _fused(inp)
+    assert torch.equal(again[0], ref[0]) and torch.equal(again[1], ref[1]) and torch.equal(again[2], ref[2])
