@@ -4,7 +4,8 @@ One step runs every row of the hot path once, each on its workload, with all
 inputs already resident in HBM:
   prefill    : 16 packed sequences of 512..16,384 tokens (137,314 in all), 64
                heads of 128, bf16, fp32 initial and final states, the automatic
-               schedule (1024 (sequence, head) pairs: the fused schedule,
+               schedule (1024 (sequence, head) pairs, above the 384 from which the
+               automatic choice is the fused schedule:
                kda_prefill -> fused_kernel, one workgroup per pair)
   decode     : 256 sequences x 1 token, 64 heads, fp32 state 256x64x128x128
                updated in place, bf16 tokens                  (kda_decode)

@@ -51,7 +51,7 @@ class KdaPrefillArgs(ctypes.Structure):
 # kda_schedule (include/kda.h); the automatic choice is the fused schedule from
 # FUSED_MIN_PAIRS (sequence, head) pairs on (KDA_FUSED_MIN_PAIRS)
 SCHEDULES = {"auto": 0, "one_pass": 1, "two_pass": 2, "fused": 3}
-FUSED_MIN_PAIRS = 1024
+FUSED_MIN_PAIRS = 384
 
 
 def _schedule_code(schedule):

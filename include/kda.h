@@ -208,8 +208,10 @@ typedef enum {
 } kda_schedule;
 
 /* The automatic choice takes the fused schedule from this many (sequence, head)
- * pairs on (bf16 I/O, chunk_size 0 or 16). */
-#define KDA_FUSED_MIN_PAIRS 1024
+ * pairs on (bf16 I/O, chunk_size 0 or 16): one and a half workgroups per compute
+ * unit of the 256 of gfx950.  Below about that many the two-pass schedule, whose
+ * first pass spreads over the whole GPU, was the faster one on ragged batches. */
+#define KDA_FUSED_MIN_PAIRS 384
 
 /*
  * Three schedules compute the same mixer (identical in exact arithmetic):
@@ -224,7 +226,8 @@ typedef enum {
  *   - fused (KDA_SCHEDULE_FUSED; bf16 I/O, chunk_size 0 or 16): one workgroup
  *     per (sequence, head) forms the same 16-token operands in its own LDS while
  *     it carries the state over them, so they never reach memory; no workspace.
- *     It needs enough pairs to fill the GPU (one workgroup per compute unit).
+ *     It needs enough pairs to fill the GPU (more than one workgroup per compute
+     unit).
  * KDA_SCHEDULE_AUTO takes the fused schedule when it applies and there are at
  * least KDA_FUSED_MIN_PAIRS pairs, else two passes when a workspace is given,
  * else one pass.  An explicit schedule that the dtype or chunk_size excludes

@@ -41,7 +41,7 @@ def _lib():
 
 def _schedules():
     # the three schedules: two passes (the default for few pairs), fused (the
-    # default from 1024 pairs on) and one pass with 64-token chunks
+    # default from FUSED_MIN_PAIRS pairs on) and one pass with 64-token chunks
     return {"two_pass": {"schedule": "two_pass"}, "fused": {"schedule": "fused"},
             "one_pass_chunk64": {"chunk_size": 64, "workspace": None, "schedule": "one_pass"}}
 

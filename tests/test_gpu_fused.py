@@ -128,7 +128,8 @@ def test_fused_bf16_state_and_pool_slots():
 
 
 def test_many_pairs_choose_the_fused_schedule():
-    """From 1024 (sequence, head) pairs the automatic choice is the fused schedule:
+    """With many (sequence, head) pairs (1024; the threshold is FUSED_MIN_PAIRS) the
+    automatic choice is the fused schedule:
     the recommended workspace is 0 and the default call equals an explicit fused
     call bit for bit; an explicit two-pass call of the same input stays within
     the bar of it."""
