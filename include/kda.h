@@ -227,10 +227,13 @@ typedef enum {
  *     per (sequence, head) forms the same 16-token operands in its own LDS while
  *     it carries the state over them, so they never reach memory; no workspace.
  *     It needs enough pairs to fill the GPU (more than one workgroup per compute
-     unit).
- * KDA_SCHEDULE_AUTO takes the fused schedule when it applies and there are at
- * least KDA_FUSED_MIN_PAIRS pairs, else two passes when a workspace is given,
- * else one pass.  An explicit schedule that the dtype or chunk_size excludes
+ *     unit), and a pair's sub-chunks run one after another in its workgroup.
+ * KDA_SCHEDULE_AUTO takes the fused schedule when it applies, there are at
+ * least KDA_FUSED_MIN_PAIRS pairs and, when cu_seqlens_host is given, the
+ * longest sequence holds at most 1.8 times the mean number of 16-token
+ * sub-chunks per compute unit (num_heads x the sum over sequences of their
+ * sub-chunks, over 256); else two passes when a workspace is given, else one
+ * pass.  An explicit schedule that the dtype or chunk_size excludes
  * returns KDA_ERR_UNSUPPORTED; KDA_SCHEDULE_TWO_PASS without a workspace returns
  * KDA_ERR_INVALID_ARG.  The fused and one-pass schedules ignore the workspace.
  * Workspace and windows.  A workspace of kda_prefill_workspace_full_size()
@@ -254,7 +257,7 @@ kda_status kda_prefill(const kda_prefill_args *args, hipStream_t stream);
  * will not run that schedule (fp32 I/O, an explicit chunk_size of 32 or 64, an
  * explicit one-pass or fused schedule, or the automatic choice of the fused
  * one).  Depends on num_seqs, num_heads, total_tokens, dtype, chunk_size,
- * schedule and, for the window count, cu_seqlens_host. */
+ * schedule and cu_seqlens_host (the automatic schedule and the window count). */
 #define KDA_PREFILL_WORKSPACE_CAP ((size_t)4 << 30)
 size_t kda_prefill_workspace_size(const kda_prefill_args *args);
 

@@ -523,6 +523,33 @@ def test_workspace_size_follows_the_schedule(lib):
         ctypes.byref(many)) > 0
 
 
+def test_automatic_schedule_weighs_the_longest_sequence(lib):
+    """With the host lengths, the automatic choice keeps two passes when one
+    sequence holds more than 1.8 times the mean sub-chunks per compute unit (the
+    fused workgroups of that sequence would run alone long after the rest), and
+    takes the fused schedule for the same pair count with balanced lengths or
+    without host lengths."""
+    H = 64
+
+    def rec(lengths, host=True):
+        cu = [0]
+        for L in lengths:
+            cu.append(cu[-1] + L)
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        a = _prefill_args(total_tokens=cu[-1], num_seqs=len(lengths), num_heads=H, cu_seqlens=FAKE,
+                          cu_seqlens_host=ctypes.cast(arr, ctypes.c_void_p) if host else None)
+        return lib.kda_prefill_workspace_size(ctypes.byref(a)), lib.kda_prefill_workspace_full_size(ctypes.byref(a))
+
+    skewed = [32768] + [512] * 7  # 512 pairs; longest 2048 sub-chunks, mean load 568
+    ws, full = rec(skewed)
+    assert ws == full > 0  # two passes
+    assert rec(skewed, host=False)[0] == 0  # lengths unknown: fused
+    assert rec([4096] * 8)[0] == 0  # balanced: fused
+    # the boundary: longest * 256 <= 1.8 * (sum of sub-chunks) * H
+    assert rec([16384] + [1024] * 15)[0] > 0  # ratio 2.06: two passes
+    assert rec([8192] + [2048] * 15)[0] == 0  # ratio 0.84: fused
+
+
 # Every buffer a prefill call writes (o, state_out, conv_state_out, workspace) is
 # checked against every other buffer of the call: these aliases would let one
 # wave overwrite what another still reads.

@@ -216,3 +216,18 @@ def test_hand_over_waits_give_up_instead_of_hanging():
     assert prev == kda.set_spin_limit(0)  # 0 restored the default
     again = _fused(inp)
     assert torch.equal(again[0], ref[0]) and torch.equal(again[1], ref[1]) and torch.equal(again[2], ref[2])
+
+
+def test_automatic_choice_weighs_the_longest_sequence():
+    """512 pairs: with one sequence much longer than the mean load per compute unit
+    the automatic choice (host lengths given) is the two-pass schedule, bit for bit;
+    with balanced lengths it is the fused schedule, bit for bit."""
+    H = 64
+    for lengths, want in (([2048] + [64] * 7, "two_pass"), ([256] * 8, "fused")):
+        inp = KI.make_prefill(H, lengths, seed=311, device=DEV, state_std=0.1)
+        cu_h = inp["cu_seqlens"].cpu()
+        auto = _fused(inp, schedule="auto", cu_seqlens_host=cu_h, workspace=True)
+        kw = {"workspace": True} if want == "two_pass" else {}
+        ref = _fused(inp, schedule=want, cu_seqlens_host=cu_h, **kw)
+        for a_, b_ in zip(auto, ref):
+            assert torch.equal(a_, b_), want
