@@ -192,7 +192,8 @@ typedef struct {
     const int32_t *state_slots;/* [N] device pool slots, or NULL (see "State pool") */
     int32_t num_slots;         /* pool rows when state_slots is given */
     int32_t dv_tile;           /* state columns per workgroup: 0 = chosen from the
-                                  number of (sequence, head) pairs; else 32, 64 or
+                                  number of (sequence, head) pairs (and, for two
+                                  passes, the host lengths); else 32, 64 or
                                   128 (and 16 for the two-pass schedule; the fused
                                   schedule takes 0 or 128).  Changes which
                                   workgroup computes a column, never the
