@@ -938,7 +938,11 @@ __device__ __forceinline__ void store_state_tile(const f32x4 (&S)[8], void *dst,
 // the R waves compute from registers read from stage j and read stage j + 1;
 // O reads stage j - 1 and the S and U fragments of step j - 1; after B_j the
 // producers refill the slot of stage j - 2 with stage j + NS - 2.
-template <int NTW>
+// SILU (KDA_F_SILU) is a template argument of the kernels that run the recurrence
+// (this one, scan_wide_kernel and fused_kernel): with a run-time flag the compiler
+// evaluates the activation of U0's conv in every step and selects the result
+// afterwards.
+template <int NTW, bool SILU>
 __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) scan_kernel(SplitParams p) {
     typedef ScanGeom<NTW> G;
     constexpr int D = kHeadDim, NS = G::NS;
@@ -988,7 +992,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
         // ---------------- U0 of step j + 1 during step j (stage j + 1 is in LDS at
         // B_j), into the exchange slot of its step's parity
         if (J == 0) return;
-        const bool silu = p.flags & KDA_F_SILU;
+        constexpr bool silu = SILU;
         VConv vc;
         load_vconv(p, slot, h, col, j0 == 0, vc);
         auto put_u0 = [&](int64_t js) {
@@ -1013,7 +1017,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
         load_state_tile(S, pw.sin, pw.sin_row, pw.sin16, col, g4);
         if (J > 0) {
             int rslot = 1 % NS;  // ring slot of stage j + 1 during step j
-            const bool silu = p.flags & KDA_F_SILU;
+            constexpr bool silu = SILU;
             VConv vc;
             if (!G::UW) load_vconv(p, slot, h, col, j0 == 0, vc);
             // A step's operands, read from the ring one step ahead: W (negated),
@@ -1171,6 +1175,7 @@ struct WideGeom {
 // is in LDS, and after it the producers refill the slot of stage j - 2).  During
 // step j the recurrence waves compute step j from registers read from stage j
 // and read stage j + 1.
+template <bool SILU>
 __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitParams p) {
     typedef WideGeom G;
     constexpr int D = kHeadDim, NS = G::NS;
@@ -1217,7 +1222,7 @@ __global__ void __launch_bounds__(WideGeom::kThreads, 1) scan_wide_kernel(SplitP
         __bf16 *ob = reinterpret_cast<__bf16 *>(p.o) + ((size_t)s0 * tokstride + (size_t)h * D);
         const uint32_t loff = (uint32_t)col[0] + 4u * (uint32_t)g4 * (uint32_t)tokstride;
         int rslot = 1 % NS;  // ring slot of stage j + 1 during step j
-        const bool silu = p.flags & KDA_F_SILU;
+        constexpr bool silu = SILU;
         VConv vc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) load_vconv(p, slot, h, col[t], j0 == 0, vc[t]);
@@ -1412,6 +1417,7 @@ __device__ __forceinline__ void wait_slot_free(unsigned char *lds, int64_t j, in
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+template <bool SILU>
 __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitParams p) {
     typedef FusedGeom G;
     constexpr int D = kHeadDim, NS = G::NS;
@@ -1493,7 +1499,7 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
         const int64_t rowbytes = (int64_t)H * D * 2;
         const unsigned char *vseq = reinterpret_cast<const unsigned char *>(p.v) + ((size_t)s0 * H + h) * D * 2;
         const int vlane = 4 * g4 * (int)rowbytes + 2 * col[0];
-        const bool silu = p.flags & KDA_F_SILU;
+        constexpr bool silu = SILU;
         uint32_t vx[2][7];
         auto load_v = [&](int64_t jr) {
             if (jr == 0) {
@@ -1644,12 +1650,18 @@ hipError_t launch_fused(const SplitParams &sp, hipStream_t s) {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel),
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel<false>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
+        if (attr == hipSuccess)
+            attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
     });
     if (attr != hipSuccess) return attr;
     const unsigned blocks = (unsigned)sp.pairs;
-    hipLaunchKernelGGL(fused_kernel, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
+    if (sp.flags & KDA_F_SILU)
+        hipLaunchKernelGGL(fused_kernel<true>, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
+    else
+        hipLaunchKernelGGL(fused_kernel<false>, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
     trace("fused_kernel grid=(%u) block=%d lds=%d slots=%d", blocks, G::kThreads, G::kLds, G::NS);
     return hipGetLastError();
 }
@@ -1659,12 +1671,18 @@ hipError_t launch_scan_wide(const SplitParams &sp, hipStream_t s) {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_wide_kernel),
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_wide_kernel<false>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
+        if (attr == hipSuccess)
+            attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_wide_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
     });
     if (attr != hipSuccess) return attr;
     const unsigned blocks = (unsigned)sp.pairs;
-    hipLaunchKernelGGL(scan_wide_kernel, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
+    if (sp.flags & KDA_F_SILU)
+        hipLaunchKernelGGL(scan_wide_kernel<true>, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
+    else
+        hipLaunchKernelGGL(scan_wide_kernel<false>, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
     trace("scan_wide_kernel grid=(%u) block=%d lds=%d ring=%d", blocks, G::kThreads, G::kLds, G::NS);
     return hipGetLastError();
 }
@@ -1675,12 +1693,18 @@ hipError_t launch_scan(const SplitParams &sp, hipStream_t s) {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_kernel<NTW>),
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_kernel<NTW, false>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
+        if (attr == hipSuccess)
+            attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_kernel<NTW, true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
     });
     if (attr != hipSuccess) return attr;
     const unsigned blocks = (unsigned)((sp.pairs + 7) / 8) * 8u * (unsigned)sp.tiles;
-    hipLaunchKernelGGL(scan_kernel<NTW>, dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
+    if (sp.flags & KDA_F_SILU)
+        hipLaunchKernelGGL((scan_kernel<NTW, true>), dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
+    else
+        hipLaunchKernelGGL((scan_kernel<NTW, false>), dim3(blocks), dim3(G::kThreads), G::kLds, s, sp);
     trace("scan_kernel<%d> grid=(%u) block=%d lds=%d ring=%d", NTW, blocks, G::kThreads, G::kLds, G::NS);
     return hipGetLastError();
 }

@@ -315,6 +315,16 @@ def test_empty_batch_and_zero_tokens(sched, kw, H, N):
 
 @pytest.mark.parametrize("flags", [0, kda.KDA_F_SILU, kda.KDA_F_NO_QK_L2NORM, kda.KDA_F_GATE_IS_LOG])
 def test_two_pass_ragged_matches_oracle(flags):
+    _two_pass_ragged(flags)
+
+
+@pytest.mark.parametrize("dv_tile", [16, 128])
+def test_two_pass_silu_on_every_pass_b_kernel(dv_tile):
+    """The SiLU instance of the narrow (16 columns) and the wide pass B."""
+    _two_pass_ragged(kda.KDA_F_SILU, dv_tile=dv_tile)
+
+
+def _two_pass_ragged(flags, dv_tile=0):
     lengths = [1, 2, 3, 15, 16, 17, 0, 63, 64, 65, 130, 200]
     inp = KI.make_prefill(3, lengths, seed=131, device=DEV, state_std=0.1, conv_cache_std=1.0)
     if flags & kda.KDA_F_GATE_IS_LOG:
@@ -325,7 +335,7 @@ def test_two_pass_ragged_matches_oracle(flags):
         inp["k"] = (0.5 * inp["k"].float()).to(torch.bfloat16)
     bias = 0.1 * seeded(inp["conv_w"].shape[0], 133)
     ref = _oracle_prefill(inp, conv_b=bias, flags=flags)
-    o, st, cs = _gpu_prefill(inp, conv_bias=bias, flags=flags, workspace=True)
+    o, st, cs = _gpu_prefill(inp, conv_bias=bias, flags=flags, workspace=True, dv_tile=dv_tile)
     assert_bf16_close(o, ref["o"], inp["cu_seqlens"], 3, st, ref["state"], "two-pass")
     np.testing.assert_array_equal(to_np(cs), ref["conv_state"])
 
