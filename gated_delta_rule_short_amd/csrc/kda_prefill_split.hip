@@ -233,6 +233,10 @@ __device__ __forceinline__ int row_soff(const RowWindow &w, int r, int rowbytes)
     return i * rowbytes;
 }
 
+// Every row p0 - 3 .. p0 + 15 of the task lies in its sequence: the row windows are
+// exact and need no clamping.
+__device__ __forceinline__ bool interior(const SubTask &tk) { return 16 * tk.j >= 3 && 16 * tk.j + 16 <= tk.L; }
+
 // The three rows before a sequence for tensor t (0 q, 1 k, 2 v): conv state or zeros.
 __device__ __forceinline__ void load_history(const SplitParams &p, const SubTask &tk, int h, int lane, int t,
                                              uint32_t (&x)[19]) {
@@ -247,6 +251,9 @@ __device__ __forceinline__ void load_history(const SplitParams &p, const SubTask
         x[i] = csn ? *reinterpret_cast<const uint32_t *>(csn + (size_t)i * CCH + ch) : 0u;
 }
 
+// HIST = false: tk is known not to be the first sub-chunk of its sequence (no
+// conv-state rows to fetch), which keeps the loads free of a conditional path.
+template <bool HIST = true>
 __device__ __forceinline__ void load_early(const SplitParams &p, const SubTask &tk, int h, int lane, EarlyRows &r) {
     constexpr int D = kHeadDim;
     typedef __bf16 T;
@@ -254,51 +261,119 @@ __device__ __forceinline__ void load_early(const SplitParams &p, const SubTask &
     const RowWindow wa = row_window(tk, 0), wk = row_window(tk, -3);
     const __amdgpu_buffer_rsrc_t ra = row_rsrc(p.gate, tk, h, wa, rowbytes);
     const __amdgpu_buffer_rsrc_t rk = row_rsrc(p.k, tk, h, wk, rowbytes);
+    if (interior(tk)) {
+        // no clamping: row i of a window at i rows from its start
+        const int rb = (int)rowbytes;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-        r.xa[rr] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * lane, row_soff(wa, rr, rowbytes), 0);
+        for (int rr = 0; rr < 16; ++rr) r.xa[rr] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * lane, rr * rb, 0);
 #pragma unroll
-    for (int i = 0; i < 19; ++i)
-        r.xk[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, row_soff(wk, i - 3, rowbytes), 0);
+        for (int i = 0; i < 19; ++i) r.xk[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, i * rb, 0);
+    } else {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            r.xa[rr] = __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * lane, row_soff(wa, rr, rowbytes), 0);
+#pragma unroll
+        for (int i = 0; i < 19; ++i)
+            r.xk[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, row_soff(wk, i - 3, rowbytes), 0);
+    }
     // unconditional load from a row inside the sequence; the conversion and the
     // mask wait for the use, so this load does not force a wait on the others
     int br = 16 * tk.j + (lane & 15);
     br = br < tk.L ? br : tk.L - 1;
     r.beta_bits = *reinterpret_cast<const unsigned short *>(reinterpret_cast<const T *>(p.beta) +
                                                             ((size_t)tk.s0 + br) * p.H + h);
-    if (tk.j == 0) load_history(p, tk, h, lane, 1, r.xk);
+    if (HIST && tk.j == 0) load_history(p, tk, h, lane, 1, r.xk);
 }
 
+template <bool HIST = true>
 __device__ __forceinline__ void load_late(const SplitParams &p, const SubTask &tk, int h, int lane, LateRows &r) {
     constexpr int D = kHeadDim;
     const int64_t rowbytes = (int64_t)p.H * D * 2;
     const RowWindow wr = row_window(tk, -3);
     const __amdgpu_buffer_rsrc_t rq = row_rsrc(p.q, tk, h, wr, rowbytes);
+    if (interior(tk)) {
+        const int rb = (int)rowbytes;
 #pragma unroll
-    for (int i = 0; i < 19; ++i) r.xq[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, row_soff(wr, i - 3, rowbytes), 0);
-    if (tk.j == 0) load_history(p, tk, h, lane, 0, r.xq);
+        for (int i = 0; i < 19; ++i) r.xq[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, i * rb, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 19; ++i)
+            r.xq[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, row_soff(wr, i - 3, rowbytes), 0);
+    }
+    if (HIST && tk.j == 0) load_history(p, tk, h, lane, 0, r.xq);
 }
 
+
+// Lane K of each 16-lane row, broadcast to the whole row (DPP row_newbcast;
+// every source lane exists, so bound_ctrl changes nothing but lets the
+// compiler fold the move into the consuming multiply).
+template <int K>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + K, 0xf, 0xf, true));
+}
+
+// acc += row_bcast<C>(nneg[s]) x[s] for s = S, S - 1, .., C + 1, in that order, one
+// v_fmac_f32 with a row_newbcast source per term (the compiler does not fold the DPP
+// move into a multiply-accumulate, whose addend is tied to the result).  Written
+// out, the DPP read is invisible to the hazard check, so each block starts with the
+// two wait states a DPP source needs after a VALU write of it.
+#define KDA_FMAC_BC(d, n, x) "v_fmac_f32_dpp " d ", " n ", " x " row_newbcast:%1 row_mask:0xf bank_mask:0xf\n\t"
+template <int C, int S>
+__device__ __forceinline__ void fmac_bcast_terms(float &acc, const float (&x)[16], const float (&nneg)[16]) {
+    constexpr int n = S - C >= 4 ? 4 : S - C;
+    if constexpr (n == 4)
+        asm("s_nop 1\n\t" KDA_FMAC_BC("%0", "%2", "%3") KDA_FMAC_BC("%0", "%4", "%5")
+                KDA_FMAC_BC("%0", "%6", "%7") KDA_FMAC_BC("%0", "%8", "%9")
+            : "+v"(acc)
+            : "i"(C), "v"(nneg[S]), "v"(x[S]), "v"(nneg[S - 1]), "v"(x[S - 1]), "v"(nneg[S - 2]), "v"(x[S - 2]),
+              "v"(nneg[S - 3]), "v"(x[S - 3]));
+    else if constexpr (n == 3)
+        asm("s_nop 1\n\t" KDA_FMAC_BC("%0", "%2", "%3") KDA_FMAC_BC("%0", "%4", "%5") KDA_FMAC_BC("%0", "%6", "%7")
+            : "+v"(acc)
+            : "i"(C), "v"(nneg[S]), "v"(x[S]), "v"(nneg[S - 1]), "v"(x[S - 1]), "v"(nneg[S - 2]), "v"(x[S - 2]));
+    else if constexpr (n == 2)
+        asm("s_nop 1\n\t" KDA_FMAC_BC("%0", "%2", "%3") KDA_FMAC_BC("%0", "%4", "%5")
+            : "+v"(acc)
+            : "i"(C), "v"(nneg[S]), "v"(x[S]), "v"(nneg[S - 1]), "v"(x[S - 1]));
+    else
+        asm("s_nop 1\n\t" KDA_FMAC_BC("%0", "%2", "%3") : "+v"(acc) : "i"(C), "v"(nneg[S]), "v"(x[S]));
+    if constexpr (S - n > C) fmac_bcast_terms<C, S - n>(acc, x, nneg);
+}
+#undef KDA_FMAC_BC
+
+// Columns C .. 0 of one row x of X = (I + N)^-1 for a strictly lower 16 x 16 N
+// (x starts as the unit row e_r and comes out as row r of X): x_c = x_c + sum_{s > c}
+// (-N[s][c]) x_s, from the last column down, the term with x_{c+1} last so that the
+// dependent chain is one FMA per column.  nneg[s] holds -N[s][c] in lane c of every
+// 16-lane row; a row broadcast hands it to the whole row.  The wave runs with every
+// lane active here.
+template <int C>
+__device__ __forceinline__ void unit_lower_inverse_row(float (&x)[16], const float (&nneg)[16]) {
+    fmac_bcast_terms<C, 15>(x[C], x, nneg);
+    if constexpr (C > 0) unit_lower_inverse_row<C - 1>(x, nneg);
+}
 
 // Conv taps and bias of one head in LDS (fused schedule): taps [3][128][4] for
 // q, k, v, then biases [3][128]; fp32.
 constexpr int kConvLdsBytes = 3 * 128 * 5 * 4;
 
-// One 16-token sub-chunk by one wave, from its early and late rows (loads
-// issued before), into the record at rec.  When nx is set it starts the loads
-// of the next sub-chunk's rows as soon as their registers are free: the early
-// rows after the k block (into ner), the late rows after the last conv that
-// reads them (into lr), so that they land while this sub-chunk finishes.  All
-// scratch LDS traffic stays inside the wave's region.  With LT (the fused
-// schedule) the conv taps come from LDS (cwl) instead of registers (cw).  before_rec() runs
-// right before the first write to rec (the fused schedule waits there for its
-// ring slot, after the gate, which needs no slot).
+// The head of one 16-token sub-chunk by one wave, from its early and late rows
+// (loads issued before): the gate (gam into its ring entry), k (KD into the record
+// at rec, KL, KI and -KL transposed into the wave's tiles) and q (QL into its
+// tile); brl receives beta of the lane's accumulator rows for the tail.  When nx is
+// set it starts the loads of the next task's rows as soon as their registers are
+// free: the early rows after the k block (into ner), the late rows after the last
+// conv that reads them (into nlr).  All scratch LDS traffic stays inside the wave's
+// region.  With LT (the fused schedule) the conv taps come from LDS (cwl) instead
+// of registers (cw).  before_rec() runs right before the first write to rec (the
+// fused schedule waits there for its ring slot, after the gate, which needs no
+// slot).
 template <bool LT, class BeforeRec>
-__device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, unsigned char *rec,
-                                                const SubTask &tk, int h, int lane, const EarlyRows &er,
-                                                LateRows &lr, const ConvW &cw, const float *cwl,
-                                                const SubTask *nx, EarlyRows &ner, BeforeRec &&before_rec,
-                                                float *gam) {
+__device__ __forceinline__ void intra_head(const SplitParams &p, unsigned char *lds, unsigned char *rec,
+                                           const SubTask &tk, int h, int lane, const EarlyRows &er,
+                                           const LateRows &lr, const ConvW &cw, const float *cwl,
+                                           const SubTask *nx, EarlyRows &ner, LateRows &nlr,
+                                           BeforeRec &&before_rec, float *gam, float (&brl)[4]) {
     constexpr int D = kHeadDim;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int p0 = 16 * tk.j;
@@ -353,7 +428,6 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
     };
     // beta of rows 4 g4 .. 4 g4 + 3 (the accumulator rows of this lane), from lanes
     // 4 g4 + i of beta_r
-    float brl[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         brl[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * g4 + i), __float_as_int(beta_r)));
@@ -444,13 +518,14 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
             }
         }
     }
-    if (nx) load_early(p, *nx, h, lane, ner);
+    // the fused schedule's next task is sub-chunk j + 4 of the same sequence
+    if (nx) load_early<!LT>(p, *nx, h, lane, ner);
     // ---- q: QL = scale Q.2^b (row-major; the output scale rides on the query)
     {
         float wt[2][4], bs[2], y[16][2], rq[16];
         load_w(0, wt, bs);
         conv16(xq, wt, bs, y);
-        if (nx) load_late(p, *nx, h, lane, lr);
+        if (nx) load_late<!LT>(p, *nx, h, lane, nlr);
         finish(y);
         l2_scale(y, l2, lane, p.scale, rq);
 #pragma unroll
@@ -458,21 +533,37 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
             Pair<__bf16>::store(sQL + rr * A_SRM + c0, y[rr][0] * rq[rr] * run[rr][0],
                                 y[rr][1] * rq[rr] * run[rr][1]);
     }
+}
+
+// The rest of a sub-chunk once its head has filled the wave's tiles (KL, KI, QL,
+// -KL transposed): the decayed Grams, the Q~ fragments and P, X diag(beta) and -W,
+// into the record at rec.  brl: beta of the lane's accumulator rows, from the head.
+__device__ __forceinline__ void intra_tail(unsigned char *lds, unsigned char *rec, int lane, const float (&brl)[4]) {
+    const int m16 = lane & 15, g4 = lane >> 4;
+    __bf16 *sKL = reinterpret_cast<__bf16 *>(lds + A_KL);
+    __bf16 *sQL = reinterpret_cast<__bf16 *>(lds + A_QL);
+    __bf16 *sKI = reinterpret_cast<__bf16 *>(lds + A_KI);
+    __bf16 *sKGT = reinterpret_cast<__bf16 *>(lds + A_KGT);
+    __bf16 *sPS = reinterpret_cast<__bf16 *>(lds + A_PS);
     wave_sync_lds();
 
     // ---- decayed Grams over the sub-chunk (one 16 x 16 tile each).  N = diag(beta)
-    // strict_lower(A) stays in registers in accumulator layout (row 4 g4 + i,
-    // column m16 in slot i) for the inverse; P goes to LDS for its transpose.
-    float nacc[4];
+    // strict_lower(A), negated, goes to LDS transposed (-N[s][c] at float 16 c + s,
+    // in the K tile, which the Grams have finished with) for the inverse; P goes
+    // to LDS for its transpose.
+    float *sNT = reinterpret_cast<float *>(lds + A_KL);
     {
         const f32x4 a = OPB::gram(sKL + m16 * A_SRM, sKI + m16 * A_SRM, nullptr, g4);
         const f32x4 pq = OPB::gram(sQL + m16 * A_SRM, sKI + m16 * A_SRM, nullptr, g4);
+        f32x4 nn;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rl = 4 * g4 + i, sl = m16;
-            nacc[i] = (sl < rl) ? a[i] * brl[i] : 0.f;
+            nn[i] = (sl < rl) ? -(a[i] * brl[i]) : 0.f;
             sPS[rl * A_STR + sl] = (__bf16)((sl <= rl) ? pq[i] : 0.f);
         }
+        // rows 4 g4 .. 4 g4 + 3 of column m16 (the accumulator layout)
+        *reinterpret_cast<f32x4 *>(sNT + 16 * m16 + 4 * g4) = nn;
     }
     // Q~ fragments (pairs of 16-channel blocks, matching pass B's state tiles)
 #pragma unroll
@@ -487,27 +578,23 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
 
     // ---- X = (I + N)^-1, one row per lane: lane r (mod 16) solves
     // x (I + N) = e_r from the last column down, x_c = [c == r] - sum_{s > c} x_s N[s][c],
-    // with N[s][c] read as a wave-uniform scalar from the register tile.  The
-    // term with x_{c+1} comes last, so the dependent chain is one FMA per column.
+    // with -N[:, c] from LDS in lane c of every row, broadcast along the row.
     // row m16 of X diag(beta), columns 4 g4 .. 4 g4 + 3 (column 4 g4 + i carries beta of
     // row 4 g4 + i): the A-operand fragment of U0 = X diag(beta) V and the B operand
     // of W^T below
     bf16x4 xb;
     {
+        float nneg[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(sNT + 16 * m16 + 4 * q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nneg[4 * q + i] = v[i];
+        }
         float x[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) x[c] = (c == m16) ? 1.f : 0.f;
-#pragma unroll
-        for (int c = 14; c >= 0; --c) {
-            float acc = x[c];
-#pragma unroll
-            for (int s = 15; s > c; --s) {
-                const float nsc = __int_as_float(
-                    __builtin_amdgcn_readlane(__float_as_int(nacc[s & 3]), 16 * (s >> 2) + c));
-                acc = fmaf(-nsc, x[s], acc);
-            }
-            x[c] = acc;
-        }
+        unit_lower_inverse_row<14>(x, nneg);
         // arithmetic selection by lane group (a select chain over x would be
         // turned into an indexed array access)
         const float m0 = g4 == 0 ? 1.f : 0.f, m1 = g4 == 1 ? 1.f : 0.f;
@@ -530,6 +617,18 @@ __device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned c
         const f32x4 w1 = mma_k16(OPB::load4raw(sKGT + (32 * t + 16 + m16) * A_STR + 4 * g4), xb, z);
         *reinterpret_cast<bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16) = join8(pack4(w0), pack4(w1));
     }
+}
+
+// One sub-chunk, head then tail (see intra_head and intra_tail).
+template <bool LT, class BeforeRec>
+__device__ __forceinline__ void intra_sub_chunk(const SplitParams &p, unsigned char *lds, unsigned char *rec,
+                                                const SubTask &tk, int h, int lane, const EarlyRows &er,
+                                                const LateRows &lr, const ConvW &cw, const float *cwl,
+                                                const SubTask *nx, EarlyRows &ner, LateRows &nlr,
+                                                BeforeRec &&before_rec, float *gam) {
+    float brl[4];
+    intra_head<LT>(p, lds, rec, tk, h, lane, er, lr, cw, cwl, nx, ner, nlr, before_rec, gam, brl);
+    intra_tail(lds, rec, lane, brl);
 }
 
 // Pass A.  The slots of sequence n start at base(n) = start_n / 16 + n
@@ -593,11 +692,11 @@ __global__ void __launch_bounds__(256, 2) intra_kernel(SplitParams p) {
     load_late(p, ta, h, lane, lr);
     const bool hb = next_task(p, ta.slot + stride, stride, tb);
     intra_sub_chunk<false>(p, lds, p.ws + ((size_t)h * p.nslots + ta.slot) * kRec, ta, h, lane, ra, lr, cw,
-                           nullptr, hb ? &tb : nullptr, rb, [] {},
+                           nullptr, hb ? &tb : nullptr, rb, lr, [] {},
                            reinterpret_cast<float *>(p.ws + ((size_t)h * p.nslots + ta.slot) * kRec + R_GAM));
     if (hb)
         intra_sub_chunk<false>(p, lds, p.ws + ((size_t)h * p.nslots + tb.slot) * kRec, tb, h, lane, rb, lr, cw,
-                               nullptr, nullptr, ra, [] {},
+                               nullptr, nullptr, ra, lr, [] {},
                                reinterpret_cast<float *>(p.ws + ((size_t)h * p.nslots + tb.slot) * kRec + R_GAM));
 }
 
@@ -704,14 +803,6 @@ __device__ __forceinline__ f32x4 u0_tile(const unsigned char *st, int colb, int 
     const bf16x4 xb = *reinterpret_cast<const bf16x4 *>(st + R_XB + lane * 8);
     // a K = 32 shape, as the U chain it starts
     return mma_k16w(xb, pack4(y), f32x4{0.f, 0.f, 0.f, 0.f});
-}
-
-// Lane K of each 16-lane row, broadcast to the whole row (DPP row_newbcast;
-// every source lane exists, so bound_ctrl changes nothing but lets the
-// compiler fold the move into the consuming multiply).
-template <int K>
-__device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + K, 0xf, 0xf, true));
 }
 
 // s (dk tile M of the state, rows 16 M + 4 g4 + i) *= gam of those rows.  gv[q]
@@ -1455,23 +1546,39 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
         unsigned char *scratch = smem_f + G::kAOff + a * A_WAVE;
         const float *cwl = reinterpret_cast<const float *>(smem_f + G::kConvOff);
         ConvW unused;  // the fused body reads its taps from LDS
-        SubTask t0, t1;
-        t0.slot = t1.slot = 0; t0.s0 = t1.s0 = s0; t0.L = t1.L = L; t0.n = t1.n = n;
-        EarlyRows r0, r1;
+        SubTask t0;
+        t0.slot = 0; t0.s0 = s0; t0.L = L; t0.n = n;
+        // Software-pipelined over the wave's sub-chunks j = a, a + 4, ..: the loads
+        // of sub-chunk j are issued first, the tail of sub-chunk j - 4 (from the
+        // wave's tiles) runs while they are in flight, then the head of j consumes
+        // them.  No row register lives across an iteration, so none is copied at
+        // the loop's end while its load is still in flight.
+        EarlyRows er;
         LateRows lr;
+        float brl[4];
         t0.j = a;
-        load_early(p, t0, h, lane, r0);
-        load_late(p, t0, h, lane, lr);
-        for (int64_t j = a; j < J; j += G::kAW) {
-            t1.j = j + G::kAW;
-            const bool h1 = t1.j < J;
-            intra_sub_chunk<true>(p, scratch, smem_f + (int)(j % NS) * G::kSlot, t0, h, lane, r0, lr, unused,
-                                  cwl, h1 ? &t1 : nullptr, r1, [&] { wait_slot_free(smem_f, j, p.spin_limit); },
-                                  reinterpret_cast<float *>(smem_f + G::kGamOff + (int)(j % G::kGamSlots) * 512));
+        auto head = [&](int64_t j) {
+            intra_head<true>(p, scratch, smem_f + (int)(j % NS) * G::kSlot, t0, h, lane, er, lr, unused, cwl,
+                             nullptr, er, lr, [&] { wait_slot_free(smem_f, j, p.spin_limit); },
+                             reinterpret_cast<float *>(smem_f + G::kGamOff + (int)(j % G::kGamSlots) * 512), brl);
+        };
+        auto tail = [&](int64_t j) {
+            intra_tail(scratch, smem_f + (int)(j % NS) * G::kSlot, lane, brl);
             lds_word_set(smem_f, G::kReady + 4 * (int)(j % NS), (int)j + 1);
-            t0.j = t1.j;
-            r0 = r1;
+        };
+        load_early(p, t0, h, lane, er);
+        load_late(p, t0, h, lane, lr);
+        head(a);
+        for (int64_t j = a + G::kAW; j < J; j += G::kAW) {
+            t0.j = j;  // j >= 4: not the sequence's first sub-chunk
+            load_early<false>(p, t0, h, lane, er);
+            load_late<false>(p, t0, h, lane, lr);
+            tail(j - G::kAW);
+            // the head waits for the loads: keep the whole tail in front of it
+            __builtin_amdgcn_sched_barrier(0);
+            head(j);
         }
+        tail(J - 1 - (J - 1 - a) % G::kAW);
         return;
     }
 
@@ -1491,10 +1598,10 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
         const uint32_t loff = (uint32_t)col[0] + 4u * (uint32_t)g4 * (uint32_t)tokstride;
         // U0 = X diag(beta) V per tile, from the width-4 conv of the raw v rows
         // 4 g4 - 3 .. 4 g4 + 3 of the sub-chunk in this lane's columns, loaded one
-        // step ahead (vx[t][k]: raw bf16 of row 4 g4 - 3 + k, column col[t]).  Past
-        // the sequence end the rows read as zeros (buffer range), before its start
-        // they come from the conv state (or are zeros); X diag(beta) has zero columns
-        // for the rows past the end.
+        // step ahead (vx[t][k]: raw bf16 of row 4 g4 - 3 + k, column col[t]).  In a
+        // sequence's first and last sub-chunks the rows are clamped into the
+        // sequence (X diag(beta) has zero columns for the rows past its end) and
+        // the rows before its start come from the conv state (or are zeros).
         const float *cwl = reinterpret_cast<const float *>(smem_f + G::kConvOff);
         const int64_t rowbytes = (int64_t)H * D * 2;
         const unsigned char *vseq = reinterpret_cast<const unsigned char *>(p.v) + ((size_t)s0 * H + h) * D * 2;
@@ -1502,14 +1609,14 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
         constexpr bool silu = SILU;
         uint32_t vx[2][7];
         auto load_v = [&](int64_t jr) {
-            if (jr == 0) {
+            if (jr == 0 || 16 * jr + 16 > L) {
                 const int CCH = 3 * H * D;
                 const __bf16 *cs = p.cs_in ? reinterpret_cast<const __bf16 *>(p.cs_in) + (size_t)slot * 3 * CCH : nullptr;
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int k = 0; k < 7; ++k) {
-                        const int64_t r = 4 * g4 - 3 + k;
+                        const int64_t r = 16 * jr + 4 * g4 - 3 + k;
                         const int64_t rr = r < L ? r : L - 1;
                         if (r < 0)
                             vx[t][k] = cs ? *reinterpret_cast<const unsigned short *>(
@@ -1519,12 +1626,10 @@ __global__ void __launch_bounds__(FusedGeom::kThreads, 1) fused_kernel(SplitPara
                             vx[t][k] = *reinterpret_cast<const unsigned short *>(vseq + rr * rowbytes + 2 * col[t]);
                     }
             } else {
-                // rows 16 jr - 3 .. (>= 13, inside the sequence since jr < J) onwards
+                // rows 16 jr - 3 .. 16 jr + 15, all inside the sequence
                 const int64_t r0 = 16 * jr - 3;
-                const int64_t nb = (L - r0) * rowbytes;
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<unsigned char *>(vseq + r0 * rowbytes), 0, (int)(nb < 0x7ffff000 ? nb : 0x7ffff000),
-                    0x00020000);
+                    const_cast<unsigned char *>(vseq + r0 * rowbytes), 0, (int)(19 * rowbytes), 0x00020000);
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
