@@ -93,13 +93,17 @@ __device__ __forceinline__ void norm_scales(const float (*red)[3], bool l2, floa
 // columns 4 (tid%32)..+3).  sa, sk, sq: the token's decay, conv-ed key and query
 // for all 128 rows, in LDS; with PRESCALED they already carry their L2 scales
 // (ik, iq unused), else the step applies them (the same products either way).
+// SCALED: the slice holds S~ = diag(c)^-1 S for the running decay product c of
+// the call's tokens (c including this token's decay): sk and sq then hold c k
+// and c q, and sa holds k / c, so that S'^T k = S~^T (c k), S'^T q = S~^T (c q)
+// and the write is S~ += (k / c) u^T; the decay costs no multiply per element.
 // vv: this thread's four v.  part: LDS for the cross-wave partial sums.  With
 // four waves every thread adds the partials itself (part must not be read by a
 // previous step that some thread may still be in); with eight, wave 0 adds them
 // once into `tot` behind a second barrier, and the two barriers make one buffer
 // of each enough for consecutive calls.  Returns u; ov receives the output
 // columns.
-template <bool PRESCALED, int NT>
+template <bool PRESCALED, int NT, bool SCALED = false>
 __device__ __forceinline__ f32x4 token_step(f32x4 (&st)[Lay<NT>::kRows], const float *sa, const float *sk,
                                             const float *sq, f32x4 vv, float ik, float iq, float kq,
                                             float beta, float scale, f32x4 (*part)[32][2],
@@ -114,8 +118,12 @@ __device__ __forceinline__ f32x4 token_step(f32x4 (&st)[Lay<NT>::kRows], const f
         const int r = rg + LY::kRowStep * m;
         const float kr = PRESCALED ? sk[r] : sk[r] * ik;
         const float qr = PRESCALED ? sq[r] : sq[r] * iq;
-        krow[m] = kr;
-        st[m] = st[m] * sa[r];
+        if constexpr (SCALED) {
+            krow[m] = sa[r];
+        } else {
+            krow[m] = kr;
+            st[m] = st[m] * sa[r];
+        }
         ak = fma4(st[m], kr, ak);
         aq = fma4(st[m], qr, aq);
     }
@@ -340,7 +348,10 @@ struct MultiParams {
     uint32_t flags;
 };
 
-template <typename T, typename SB>
+// SCALED (see token_step): the tokens run on S~ = diag(c)^-1 S.  The host picks it
+// only for the sigmoid gate with T (-lb) log2(e) <= 100, so that c >= 2^-100 and
+// neither c nor 1 / c leaves the normal fp32 range.
+template <typename T, typename SB, bool SCALED>
 __global__ void __launch_bounds__(kMultiThreads) multi_kernel(MultiParams p) {
 #pragma clang fp contract(off)
     constexpr int NTH = kMultiThreads, kThreads = NTH;
@@ -494,15 +505,25 @@ __global__ void __launch_bounds__(kMultiThreads) multi_kernel(MultiParams p) {
         store_state<NTH>(st, S, tid);
     }
     // L2-normalised q and k of the new tokens, in place; k also into row 1 of
-    // the records
+    // the records.  SCALED: c k, c q and k / c in place of k, q and the decay,
+    // c the running product of the decays of row c over the tokens
     if (qk) {
+        float cr = 1.f;
         for (int t = 0; t < NT; ++t) {
             float iq, ik, kq;
             norm_scales(s_red[t], l2, iq, ik, kq);
             const float kn = s_k[t][c] * ik;
-            s_k[t][c] = kn;
-            s_q[t][c] = s_q[t][c] * iq;
+            const float qn = s_q[t][c] * iq;
             rec[(size_t)t * kRec + D + c] = kn;
+            if constexpr (SCALED) {
+                cr = cr * s_alpha[t][c];
+                s_k[t][c] = cr * kn;
+                s_q[t][c] = cr * qn;
+                s_alpha[t][c] = kn * __builtin_amdgcn_rcpf(cr);
+            } else {
+                s_k[t][c] = kn;
+                s_q[t][c] = qn;
+            }
         }
     }
     barrier_lds();
@@ -514,7 +535,7 @@ __global__ void __launch_bounds__(kMultiThreads) multi_kernel(MultiParams p) {
         norm_scales(s_red[t], l2, iq, ik, kq);
         const f32x4 vv = *reinterpret_cast<const f32x4 *>(&s_v[t][4 * cg]);
         f32x4 ov;
-        const f32x4 u = token_step<true, NTH>(st, s_alpha[t], s_k[t], s_q[t], vv, ik, iq, kq, s_beta[t],
+        const f32x4 u = token_step<true, NTH, SCALED>(st, s_alpha[t], s_k[t], s_q[t], vv, ik, iq, kq, s_beta[t],
                                               p.scale, s_part[t & 1], nullptr, tid, ov);
         if (rg == 0) {
             T *o = ob + t * tstride;
@@ -643,8 +664,18 @@ hipError_t launch_decode_multi(const kda_decode_multi_args *a, hipStream_t s) {
     p.H = a->num_heads; p.T = a->num_tokens; p.pT = a->pending_updates ? a->pending_tokens : 0;
     p.scale = a->scale; p.lb = a->gate_lower_bound; p.flags = a->flags;
     const unsigned blocks = (unsigned)a->num_seqs * (unsigned)a->num_heads;
-    launch_typed<MultiParams>("multi_kernel", kMultiThreads, a->dtype, a->flags, blocks, p, s,
-                     multi_kernel<__bf16, __bf16>, multi_kernel<__bf16, float>, multi_kernel<float, __bf16>, multi_kernel<float, float>);
+    // the state in its scaled form when the decays of the T tokens keep their
+    // product at or above 2^-100 (sigmoid gate: each decay is at least 2^(lb log2 e))
+    const bool scaled = !(a->flags & KDA_F_GATE_IS_LOG) &&
+                        (double)a->num_tokens * (double)(-a->gate_lower_bound) * 1.4426950408889634 <= 100.0;
+    if (scaled)
+        launch_typed<MultiParams>("multi_kernel<scaled>", kMultiThreads, a->dtype, a->flags, blocks, p, s,
+                                  multi_kernel<__bf16, __bf16, true>, multi_kernel<__bf16, float, true>,
+                                  multi_kernel<float, __bf16, true>, multi_kernel<float, float, true>);
+    else
+        launch_typed<MultiParams>("multi_kernel", kMultiThreads, a->dtype, a->flags, blocks, p, s,
+                                  multi_kernel<__bf16, __bf16, false>, multi_kernel<__bf16, float, false>,
+                                  multi_kernel<float, __bf16, false>, multi_kernel<float, float, false>);
     return hipGetLastError();
 }
 
