@@ -104,6 +104,29 @@ def _close_to_rounding(x, ref, dtype, what):
         what, int(bad.sum()), float((x - ref).abs().max()))
 
 
+@pytest.mark.parametrize("lb", [-5.0, -8.6, -14.0])
+def test_multi_scaled_state_range(lb):
+    """The verify step runs on the state scaled by the running decay product when
+    T (-lb) log2(e) <= 100 (lb = -5 and, at the edge with c near 2^-99, -8.6) and
+    on the plain state otherwise (-14); decays pushed to the bound (gate inputs of
+    +8, sigmoid near 1) make c as small as the bound allows."""
+    N, H, T = 4, 3, 8
+    d = KI.make_spec_decode(N, T, H, dtype=torch.float32, seed=61, device=DEV)
+    d["gate"] = (8.0 + seeded(d["gate"].shape, 62)).to(torch.float32)
+    st0, cs0 = d["state"].clone(), d["conv_state"].clone()
+    o, upd = kda.kda_decode_multi(d["q"], d["k"], d["v"], d["gate"], d["beta"], d["conv_w"],
+                                  d["conv_state"], d["state"], gate_lower_bound=lb)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(upd).all()
+    ref = _oracle_prefix(d, [T] * N, st0.cpu(), cs0.cpu(), gate_lower_bound=lb)
+    _check(o, ref["o"].reshape(N, T, H, 128), torch.float32, "multi o, lb %g" % lb)
+    acc = torch.tensor([T, 5, 1, 0], dtype=torch.int32)
+    kda.kda_decode_commit(upd, acc.to(DEV), d["conv_state"], d["state"])
+    torch.cuda.synchronize()
+    refc = _oracle_prefix(d, acc.tolist(), st0.cpu(), cs0.cpu(), gate_lower_bound=lb)
+    _check_state(d["state"], refc["state"], torch.float32, "committed state, lb %g" % lb)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_multi_and_commit_equal_decode_steps(dtype):
     N, H, T = 5, 4, 6
