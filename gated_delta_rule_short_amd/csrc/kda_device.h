@@ -79,9 +79,11 @@ template <> struct Pair<__bf16> {
 
 // Sum over the 64 lanes of a wave; every lane receives the same value.  DPP
 // moves combine lanes inside each 16-lane row (xor 1, xor 2, half-row mirror,
-// row mirror), then the four row sums are read out as scalars.
+// row mirror), then the four row sums are read out as scalars.  Every lane has a
+// source lane in these patterns, so bound_ctrl changes no value; set, it lets the
+// compiler fold each move into the add that consumes it.
 #define KDA_DPP(x, ctrl) \
-    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (x)), (ctrl), 0xf, 0xf, false))
+    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (x)), (ctrl), 0xf, 0xf, true))
 __device__ __forceinline__ float wave_sum(float x) {
     x += KDA_DPP(x, 0xb1);   // quad_perm [1,0,3,2]
     x += KDA_DPP(x, 0x4e);   // quad_perm [2,3,0,1]

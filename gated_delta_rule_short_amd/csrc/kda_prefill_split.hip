@@ -359,7 +359,7 @@ constexpr int kConvLdsBytes = 3 * 128 * 5 * 4;
 
 // The head of one 16-token sub-chunk by one wave, from its early and late rows
 // (loads issued before): the gate (gam into its ring entry), k (KD into the record
-// at rec, KL, KI and -KL transposed into the wave's tiles) and q (QL into its
+// at rec, KL, KI and KL transposed into the wave's tiles) and q (QL into its
 // tile); brl receives beta of the lane's accumulator rows for the tail.  When nx is
 // set it starts the loads of the next task's rows as soon as their registers are
 // free: the early rows after the k block (into ner), the late rows after the last
@@ -484,7 +484,7 @@ __device__ __forceinline__ void intra_head(const SplitParams &p, unsigned char *
         *reinterpret_cast<f32x2 *>(gam + c0) = gm;
     }
 
-    // ---- k: KL = K.2^b, KI = K.2^-b (row-major), -KL transposed, KD = K.2^(b_last-b)
+    // ---- k: KL = K.2^b, KI = K.2^-b (row-major), KL transposed, KD = K.2^(b_last-b)
     {
         float wt[2][4], bs[2], y[16][2], rk[16];
         load_w(1, wt, bs);
@@ -509,7 +509,7 @@ __device__ __forceinline__ void intra_head(const SplitParams &p, unsigned char *
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int c = c0 + e, r = 4 * q4;
-                OPB::store4(sKGT + c * A_STR + r, -kl[0][e], -kl[1][e], -kl[2][e], -kl[3][e]);
+                OPB::store4(sKGT + c * A_STR + r, kl[0][e], kl[1][e], kl[2][e], kl[3][e]);
                 // accumulator / A-fragment layouts for pass B: element (token r, channel c)
                 // of tile c / 16 sits in lane (r / 4) * 16 + c % 16, slot r % 4
                 const size_t fo = ((size_t)((c >> 4) * 64 + q4 * 16 + (c & 15)) * 4) * 2;
@@ -536,7 +536,7 @@ __device__ __forceinline__ void intra_head(const SplitParams &p, unsigned char *
 }
 
 // The rest of a sub-chunk once its head has filled the wave's tiles (KL, KI, QL,
-// -KL transposed): the decayed Grams, the Q~ fragments and P, X diag(beta) and -W,
+// KL transposed): the decayed Grams, the Q~ fragments and P, X diag(beta) and -W,
 // into the record at rec.  brl: beta of the lane's accumulator rows, from the head.
 __device__ __forceinline__ void intra_tail(unsigned char *lds, unsigned char *rec, int lane, const float (&brl)[4]) {
     const int m16 = lane & 15, g4 = lane >> 4;
@@ -606,15 +606,18 @@ __device__ __forceinline__ void intra_tail(unsigned char *lds, unsigned char *re
     }
     wave_sync_lds();
 
-    // ---- -W = -X diag(beta) (K . 2^b), formed transposed: -W^T = (-K . 2^b)^T (X diag(beta))^T
+    // ---- -W = -X diag(beta) (K . 2^b), formed transposed: -W^T = (K . 2^b)^T (-X diag(beta))^T
     // puts row r of W, channels 16 nt + 4 g4 .. + 3, in lane r + 16 g4 of tile nt,
     // which is the A-operand fragment pass B reads (tiles 2t and 2t + 1 give the two
-    // halves of fragment t), so W goes to the record without an LDS round trip.
+    // halves of fragment t), so W goes to the record without an LDS round trip.  The
+    // sign rides on the four bf16 of X diag(beta) (an exact sign flip), not on K.
+    typedef uint32_t w2 __attribute__((ext_vector_type(2)));
+    const bf16x4 xbn = __builtin_bit_cast(bf16x4, __builtin_bit_cast(w2, xb) ^ w2{0x80008000u, 0x80008000u});
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const f32x4 w0 = mma_k16(OPB::load4raw(sKGT + (32 * t + m16) * A_STR + 4 * g4), xb, z);
-        const f32x4 w1 = mma_k16(OPB::load4raw(sKGT + (32 * t + 16 + m16) * A_STR + 4 * g4), xb, z);
+        const f32x4 w0 = mma_k16(OPB::load4raw(sKGT + (32 * t + m16) * A_STR + 4 * g4), xbn, z);
+        const f32x4 w1 = mma_k16(OPB::load4raw(sKGT + (32 * t + 16 + m16) * A_STR + 4 * g4), xbn, z);
         *reinterpret_cast<bf16x8 *>(rec + R_WN + ((size_t)t * 64 + lane) * 16) = join8(pack4(w0), pack4(w1));
     }
 }
