@@ -312,46 +312,67 @@ __device__ __forceinline__ float row_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + K, 0xf, 0xf, true));
 }
 
-// acc += row_bcast<C>(nneg[s]) x[s] for s = S, S - 1, .., C + 1, in that order, one
-// v_fmac_f32 with a row_newbcast source per term (the compiler does not fold the DPP
-// move into a multiply-accumulate, whose addend is tied to the result).  Written
-// out, the DPP read is invisible to the hazard check, so each block starts with the
-// two wait states a DPP source needs after a VALU write of it.
-#define KDA_FMAC_BC(d, n, x) "v_fmac_f32_dpp " d ", " n ", " x " row_newbcast:%1 row_mask:0xf bank_mask:0xf\n\t"
-template <int C, int S>
-__device__ __forceinline__ void fmac_bcast_terms(float &acc, const float (&x)[16], const float (&nneg)[16]) {
-    constexpr int n = S - C >= 4 ? 4 : S - C;
-    if constexpr (n == 4)
-        asm("s_nop 1\n\t" KDA_FMAC_BC("%0", "%2", "%3") KDA_FMAC_BC("%0", "%4", "%5")
-                KDA_FMAC_BC("%0", "%6", "%7") KDA_FMAC_BC("%0", "%8", "%9")
-            : "+v"(acc)
-            : "i"(C), "v"(nneg[S]), "v"(x[S]), "v"(nneg[S - 1]), "v"(x[S - 1]), "v"(nneg[S - 2]), "v"(x[S - 2]),
-              "v"(nneg[S - 3]), "v"(x[S - 3]));
-    else if constexpr (n == 3)
-        asm("s_nop 1\n\t" KDA_FMAC_BC("%0", "%2", "%3") KDA_FMAC_BC("%0", "%4", "%5") KDA_FMAC_BC("%0", "%6", "%7")
-            : "+v"(acc)
-            : "i"(C), "v"(nneg[S]), "v"(x[S]), "v"(nneg[S - 1]), "v"(x[S - 1]), "v"(nneg[S - 2]), "v"(x[S - 2]));
-    else if constexpr (n == 2)
-        asm("s_nop 1\n\t" KDA_FMAC_BC("%0", "%2", "%3") KDA_FMAC_BC("%0", "%4", "%5")
-            : "+v"(acc)
-            : "i"(C), "v"(nneg[S]), "v"(x[S]), "v"(nneg[S - 1]), "v"(x[S - 1]));
-    else
-        asm("s_nop 1\n\t" KDA_FMAC_BC("%0", "%2", "%3") : "+v"(acc) : "i"(C), "v"(nneg[S]), "v"(x[S]));
-    if constexpr (S - n > C) fmac_bcast_terms<C, S - n>(acc, x, nneg);
-}
-#undef KDA_FMAC_BC
-
-// Columns C .. 0 of one row x of X = (I + N)^-1 for a strictly lower 16 x 16 N
-// (x starts as the unit row e_r and comes out as row r of X): x_c = x_c + sum_{s > c}
-// (-N[s][c]) x_s, from the last column down, the term with x_{c+1} last so that the
-// dependent chain is one FMA per column.  nneg[s] holds -N[s][c] in lane c of every
-// 16-lane row; a row broadcast hands it to the whole row.  The wave runs with every
+// Rows of X = (I + N)^-1 for a strictly lower 16 x 16 N, one row x per lane (x
+// starts as the unit row e_r and comes out as row r of X): x_c = x_c + sum_{s > c}
+// (-N[s][c]) x_s for every c.  Step k adds the term s = 15 - k to every column c <
+// s at once; x_s is final by then (its last term came in step k - 1), and each
+// column takes its terms in the order s = 15, 14, .., c + 1.  nneg[s] holds
+// -N[s][c] in lane c of every 16-lane row, handed to the whole row by a DPP row
+// broadcast inside v_fmac_f32 (the compiler does not fold a DPP move into a
+// multiply-add, whose addend is tied to the result).  The FMAs of a step are
+// independent, so the chain is 15 steps deep instead of 120.  Written out, the DPP
+// read is invisible to the hazard check, so each step starts with the two wait
+// states a DPP source needs after a VALU write of it.  The wave runs with every
 // lane active here.
-template <int C>
-__device__ __forceinline__ void unit_lower_inverse_row(float (&x)[16], const float (&nneg)[16]) {
-    fmac_bcast_terms<C, 15>(x[C], x, nneg);
-    if constexpr (C > 0) unit_lower_inverse_row<C - 1>(x, nneg);
+#define KDA_FMBC(c) "v_fmac_f32_dpp %[x" #c "], %[n], %[xs] row_newbcast:" #c " row_mask:0xf bank_mask:0xf\n\t"
+__device__ __forceinline__ void unit_lower_inverse_rows(float (&x)[16], const float (&nneg)[16]) {
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5) KDA_FMBC(6) KDA_FMBC(7) KDA_FMBC(8) KDA_FMBC(9) KDA_FMBC(10) KDA_FMBC(11) KDA_FMBC(12) KDA_FMBC(13) KDA_FMBC(14)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8]), [x9] "+v"(x[9]), [x10] "+v"(x[10]), [x11] "+v"(x[11]), [x12] "+v"(x[12]), [x13] "+v"(x[13]), [x14] "+v"(x[14])
+        : [n] "v"(nneg[15]), [xs] "v"(x[15]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5) KDA_FMBC(6) KDA_FMBC(7) KDA_FMBC(8) KDA_FMBC(9) KDA_FMBC(10) KDA_FMBC(11) KDA_FMBC(12) KDA_FMBC(13)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8]), [x9] "+v"(x[9]), [x10] "+v"(x[10]), [x11] "+v"(x[11]), [x12] "+v"(x[12]), [x13] "+v"(x[13])
+        : [n] "v"(nneg[14]), [xs] "v"(x[14]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5) KDA_FMBC(6) KDA_FMBC(7) KDA_FMBC(8) KDA_FMBC(9) KDA_FMBC(10) KDA_FMBC(11) KDA_FMBC(12)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8]), [x9] "+v"(x[9]), [x10] "+v"(x[10]), [x11] "+v"(x[11]), [x12] "+v"(x[12])
+        : [n] "v"(nneg[13]), [xs] "v"(x[13]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5) KDA_FMBC(6) KDA_FMBC(7) KDA_FMBC(8) KDA_FMBC(9) KDA_FMBC(10) KDA_FMBC(11)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8]), [x9] "+v"(x[9]), [x10] "+v"(x[10]), [x11] "+v"(x[11])
+        : [n] "v"(nneg[12]), [xs] "v"(x[12]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5) KDA_FMBC(6) KDA_FMBC(7) KDA_FMBC(8) KDA_FMBC(9) KDA_FMBC(10)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8]), [x9] "+v"(x[9]), [x10] "+v"(x[10])
+        : [n] "v"(nneg[11]), [xs] "v"(x[11]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5) KDA_FMBC(6) KDA_FMBC(7) KDA_FMBC(8) KDA_FMBC(9)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8]), [x9] "+v"(x[9])
+        : [n] "v"(nneg[10]), [xs] "v"(x[10]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5) KDA_FMBC(6) KDA_FMBC(7) KDA_FMBC(8)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7]), [x8] "+v"(x[8])
+        : [n] "v"(nneg[9]), [xs] "v"(x[9]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5) KDA_FMBC(6) KDA_FMBC(7)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6]), [x7] "+v"(x[7])
+        : [n] "v"(nneg[8]), [xs] "v"(x[8]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5) KDA_FMBC(6)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5]), [x6] "+v"(x[6])
+        : [n] "v"(nneg[7]), [xs] "v"(x[7]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4) KDA_FMBC(5)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4]), [x5] "+v"(x[5])
+        : [n] "v"(nneg[6]), [xs] "v"(x[6]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3) KDA_FMBC(4)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [x4] "+v"(x[4])
+        : [n] "v"(nneg[5]), [xs] "v"(x[5]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2) KDA_FMBC(3)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3])
+        : [n] "v"(nneg[4]), [xs] "v"(x[4]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1) KDA_FMBC(2)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2])
+        : [n] "v"(nneg[3]), [xs] "v"(x[3]));
+    asm("s_nop 1\n\t" KDA_FMBC(0) KDA_FMBC(1)
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1])
+        : [n] "v"(nneg[2]), [xs] "v"(x[2]));
+    asm("s_nop 1\n\t" KDA_FMBC(0)
+        : [x0] "+v"(x[0])
+        : [n] "v"(nneg[1]), [xs] "v"(x[1]));
 }
+#undef KDA_FMBC
 
 // Conv taps and bias of one head in LDS (fused schedule): taps [3][128][4] for
 // q, k, v, then biases [3][128]; fp32.
@@ -594,7 +615,7 @@ __device__ __forceinline__ void intra_tail(unsigned char *lds, unsigned char *re
         float x[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) x[c] = (c == m16) ? 1.f : 0.f;
-        unit_lower_inverse_row<14>(x, nneg);
+        unit_lower_inverse_rows(x, nneg);
         // arithmetic selection by lane group (a select chain over x would be
         // turned into an indexed array access)
         const float m0 = g4 == 0 ? 1.f : 0.f, m1 = g4 == 1 ? 1.f : 0.f;
