@@ -539,14 +539,14 @@ __device__ __forceinline__ void intra_head(const SplitParams &p, unsigned char *
             }
         }
     }
-    // the fused schedule's next task is sub-chunk j + 4 of the same sequence
-    if (nx) load_early<!LT>(p, *nx, h, lane, ner);
+    // (only the two-pass schedule prefetches here; its next task may start a sequence)
+    if (nx) load_early(p, *nx, h, lane, ner);
     // ---- q: QL = scale Q.2^b (row-major; the output scale rides on the query)
     {
         float wt[2][4], bs[2], y[16][2], rq[16];
         load_w(0, wt, bs);
         conv16(xq, wt, bs, y);
-        if (nx) load_late<!LT>(p, *nx, h, lane, nlr);
+        if (nx) load_late(p, *nx, h, lane, nlr);
         finish(y);
         l2_scale(y, l2, lane, p.scale, rq);
 #pragma unroll
