@@ -1062,8 +1062,13 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
     typedef ScanGeom<NTW> G;
     constexpr int D = kHeadDim, NS = G::NS;
     extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
-    // the wave index is uniform: keep it scalar so that role branches stay scalar
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    // the wave index is uniform: keep it scalar so that role branches stay scalar.
+    // Roles by index: recurrence waves, output waves, U0 waves, producers.  With two
+    // tiles the U0 waves take hardware waves 6 and 7 and the first two producers
+    // waves 4 and 5, so that a U0 wave shares its SIMD with an output wave rather
+    // than with the MFMA-heavy recurrence wave (waves go round the four SIMDs).
+    const int wh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int w = (NTW == 2 && wh >= 4 && wh < 8) ? (wh ^ 2) : wh;
     const int m16 = lane & 15, g4 = lane >> 4;
     const int bid = blockIdx.x;
     const int grp = bid / (8 * p.tiles), rem = bid - grp * 8 * p.tiles;
@@ -1176,6 +1181,10 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                 Uc = mma_k32(wn[1], Sp[1], Uc);
                 Ua = mma_k32(wn[2], Sp[2], Ua);
                 Uc = mma_k32(wn[3], Sp[3], Uc);
+                // The decays run while the U products are in flight: left to the
+                // scheduler, most of them sat between U's pack and the state
+                // products, on the step's dependent chain.
+                __builtin_amdgcn_sched_barrier(0);
                 unsigned char *ex = exch + (j & 1) * G::kExSlot;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) *reinterpret_cast<bf16x8 *>(ex + t * 1024 + lane * 16) = Sp[t];
@@ -1187,6 +1196,7 @@ __global__ void __launch_bounds__(ScanGeom<NTW>::kThreads, NTW == 1 ? 2 : 1) sca
                 decay_tile<5>(S[5], gv);
                 decay_tile<6>(S[6], gv);
                 decay_tile<7>(S[7], gv);
+                __builtin_amdgcn_sched_barrier(0);
                 const bf16x4 Ub = pack4(G::UW ? (Ua + Uc) + u0w : Ua + Uc);
                 *reinterpret_cast<bf16x4 *>(ex + 4096 + lane * 8) = Ub;
 #pragma unroll
