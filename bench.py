@@ -59,13 +59,19 @@ OPS = ["prefill_varlen", "prefill_T4096", "prefill_T65536", "decode", "short_con
 
 
 def _source_sha(name):
+    """Hash of a kernel source's code: comments removed and whitespace runs folded,
+    so that an edit of a comment leaves the summaries of its kernels in force."""
     path = os.path.join(ROOT, "gated_delta_rule_short_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def _profile_field(key, field):
     """A number from a committed rocprofv3 summary, or None when the summary is
-    absent or was taken on a different version of the kernel source."""
+    absent or was taken on different code (comments and layout aside)."""
     src, fname = PROFILE_OF[key]
     path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):

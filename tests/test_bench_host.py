@@ -1,6 +1,7 @@
 """Host-side checks of bench.py: the refusal of several GPUs, the roofline record,
 and the table of counter summaries it reads (every entry names a committed
-summary of its own kernel source with a per-launch byte count)."""
+summary of its own kernel source with a per-launch byte count, taken on the code
+that source holds now)."""
 import os
 import re
 import subprocess
@@ -36,3 +37,24 @@ def test_every_profile_entry_names_its_summary():
         assert re.search(r"kernel_source_sha:\s*[0-9a-f]{16}", text), fname
         assert re.search(r"hbm_bytes_per_launch:\s*[0-9.eE+]+", text), fname
         assert "--only %s " % key in text, fname  # the command that made it times this entry
+
+
+def test_every_profile_summary_describes_the_current_code():
+    # a kernel edited after its summaries were taken leaves the bench line without
+    # counted traffic and busy fractions: take the summaries again (rocprofv3, the
+    # commands each summary names) when this fails
+    for key, (src, fname) in bench.PROFILE_OF.items():
+        assert bench._profile_field(key, "hbm_bytes_per_launch") is not None, (key, fname, src)
+
+
+def test_source_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
+    csrc = tmp_path / "gated_delta_rule_short_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    f = csrc / "k.hip"
+    f.write_text("// header\nint f(int a) {\n    return a + 1;  /* one */\n}\n")
+    h = bench._source_sha("k.hip")
+    f.write_text("// another header\n/* block\n comment */ int f(int a) { return a + 1; }\n")
+    assert bench._source_sha("k.hip") == h
+    f.write_text("int f(int a) { return a + 2; }\n")
+    assert bench._source_sha("k.hip") != h
